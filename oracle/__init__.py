@@ -1,0 +1,221 @@
+"""CPU oracle for MoE dispatch/combine -- TEST INFRASTRUCTURE ONLY.
+
+Only tests/, ``__graft_entry__.smoke()`` and bench.py's ``cpu_baseline`` leg may import this
+package.  The product path (``combine_quant_amd``) never does, and the two share no code.
+
+The arithmetic lives in ``moe_oracle.c`` (plain single-threaded C, one IEEE binary32
+operation per written float operation); this module only marshals numpy arrays through
+ctypes.  Function-level citations of the pages are in the C source.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from .build import LIB, build
+
+_lib = None
+
+
+class OracleCfg(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "W", "E", "BS", "H", "K", "quant_mode", "zero_expert_num", "copy_expert_num",
+        "expert_token_nums_type", "mask_kind")]
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            build()
+        lib = ctypes.CDLL(LIB)
+        P = ctypes.c_void_p
+        i32, i64, u8, u16, f32 = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint8,
+                                  ctypes.c_uint16, ctypes.c_float)
+        sig = {
+            "oracle_bf16_to_f32": (f32, [u16]),
+            "oracle_f32_to_bf16": (u16, [f32]),
+            "oracle_e4m3_from_f32": (u8, [f32]),
+            "oracle_e4m3_to_f32": (f32, [u8]),
+            "oracle_mx_scale_count": (i32, [i32]),
+            "oracle_quant_int8_row": (None, [P, P, i32, P, P]),
+            "oracle_quant_mx_row": (None, [P, i32, i32, P, P]),
+            "oracle_route": (i32, [P, P, P, P, P]),
+            "oracle_recv_counts": (i32, [P, P, P, P, P]),
+            "oracle_dest_row": (i64, [P, P, P, i32, i32, i32]),
+            "oracle_dispatch": (i32, [P] * 13),
+            "oracle_combine_token": (i32, [P] * 9 + [i32, i32, P, P]),
+            "oracle_combine": (i32, [P] * 11),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    """Contiguous array of the given dtype, or None."""
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def make_cfg(W, E, BS, H, K, quant_mode=0, zero_expert_num=0, copy_expert_num=0,
+             expert_token_nums_type=1, mask_kind=0):
+    return OracleCfg(W, E, BS, H, K, quant_mode, zero_expert_num, copy_expert_num,
+                     expert_token_nums_type, mask_kind)
+
+
+def _ref(cfg):
+    return ctypes.byref(cfg)
+
+
+# -- scalar helpers ------------------------------------------------------------------------
+
+def bf16_to_f32(b):
+    return _load().oracle_bf16_to_f32(int(b))
+
+
+def f32_to_bf16(f):
+    return _load().oracle_f32_to_bf16(float(f))
+
+
+def e4m3_from_f32(v):
+    return _load().oracle_e4m3_from_f32(float(v))
+
+
+def e4m3_to_f32(code):
+    return _load().oracle_e4m3_to_f32(int(code))
+
+
+def mx_scale_count(H):
+    return _load().oracle_mx_scale_count(int(H))
+
+
+# -- rows ----------------------------------------------------------------------------------
+
+def quant_int8_row(x_bf16, smooth=None):
+    x = _c(x_bf16, np.uint16)
+    sm = _c(smooth, np.float32)
+    H = x.shape[0]
+    q = np.empty(H, np.int8)
+    sc = np.empty(1, np.float32)
+    _load().oracle_quant_int8_row(_p(x), _p(sm), H, _p(q), _p(sc))
+    return q, sc[0]
+
+
+def quant_mx_row(x_bf16, clip):
+    x = _c(x_bf16, np.uint16)
+    H = x.shape[0]
+    codes = np.empty(H, np.uint8)
+    scales = np.empty(mx_scale_count(H), np.float32)
+    _load().oracle_quant_mx_row(_p(x), H, 1 if clip else 0, _p(codes), _p(scales))
+    return codes, scales
+
+
+# -- routing -------------------------------------------------------------------------------
+
+def route(cfg, expert_ids, mask=None):
+    ids = _c(expert_ids, np.int32)
+    m = _c(mask, np.uint8)
+    cnt = np.empty((cfg.W, cfg.E), np.int32)
+    eidx = np.empty((cfg.W, cfg.BS, cfg.K), np.int32)
+    rc = _load().oracle_route(_ref(cfg), _p(ids), _p(m), _p(cnt), _p(eidx))
+    if rc != 0:
+        raise ValueError(f"oracle_route rejected the input (rc={rc})")
+    return cnt, eidx
+
+
+def recv_counts(cfg, cnt):
+    L = cfg.E // cfg.W
+    cnt = _c(cnt, np.int32)
+    erc = np.empty((cfg.W, L * cfg.W), np.int32)
+    etn = np.empty((cfg.W, L), np.int64)
+    off = np.empty(cfg.W + 1, np.int64)
+    _load().oracle_recv_counts(_ref(cfg), _p(cnt), _p(erc), _p(etn), _p(off))
+    return erc, etn, off
+
+
+def dest_row(cfg, ep_recv_count, recv_offsets, s, e, ordinal):
+    erc = _c(ep_recv_count, np.int32)
+    off = _c(recv_offsets, np.int64)
+    return _load().oracle_dest_row(_ref(cfg), _p(erc), _p(off), int(s), int(e), int(ordinal))
+
+
+def dispatch(cfg, x, expert_ids, smooth=None, mask=None, cap=None):
+    """Whole dispatch.  Returns a dict of numpy arrays; rows of expand_x / dynamic_scales /
+    assist_info past recv_offsets[W] are left zero."""
+    W, BS, H, K, L = cfg.W, cfg.BS, cfg.H, cfg.K, cfg.E // cfg.W
+    x = _c(x, np.uint16)
+    ids = _c(expert_ids, np.int32)
+    sm = _c(smooth, np.float32)
+    m = _c(mask, np.uint8)
+    cap = W * BS * K if cap is None else cap
+    if cfg.quant_mode == 0:
+        ex = np.zeros((cap, H), np.uint16)
+        ds = np.zeros(1, np.float32)
+    elif cfg.quant_mode == 2:
+        ex = np.zeros((cap, H), np.int8)
+        ds = np.zeros(cap, np.float32)
+    else:
+        ex = np.zeros((cap, H), np.uint8)
+        ds = np.zeros((cap, mx_scale_count(H)), np.float32)
+    eidx = np.empty((W, BS, K), np.int32)
+    ai = np.zeros((cap, 3), np.int32)
+    erc = np.empty((W, L * W), np.int32)
+    etn = np.empty((W, L), np.int64)
+    off = np.empty(W + 1, np.int64)
+    cnt = np.empty((W, cfg.E), np.int32)
+    rc = _load().oracle_dispatch(_ref(cfg), _p(x), _p(ids), _p(sm), _p(m), _p(ex), _p(ds),
+                                 _p(eidx), _p(ai), _p(erc), _p(etn), _p(off), _p(cnt))
+    if rc != 0:
+        raise ValueError(f"oracle_dispatch rejected the input (rc={rc})")
+    out = dict(expand_x=ex, expand_idx=eidx, assist_info=ai, ep_recv_count=erc,
+               expert_token_nums=etn, recv_offsets=off, cnt=cnt)
+    if cfg.quant_mode != 0:
+        out["dynamic_scales"] = ds
+    return out
+
+
+def combine(cfg, expert_out, expert_ids, expand_idx, expert_scales, ep_recv_count,
+            recv_offsets, mask=None, ori_x=None):
+    eo = _c(expert_out, np.uint16)
+    ids = _c(expert_ids, np.int32)
+    eidx = _c(expand_idx, np.int32)
+    w = _c(expert_scales, np.float32)
+    erc = _c(ep_recv_count, np.int32)
+    off = _c(recv_offsets, np.int64)
+    m = _c(mask, np.uint8)
+    ox = _c(ori_x, np.uint16)
+    y = np.empty((cfg.W, cfg.BS, cfg.H), np.uint16)
+    acc = np.empty(cfg.H, np.float32)
+    rc = _load().oracle_combine(_ref(cfg), _p(eo), _p(ids), _p(eidx), _p(w), _p(erc),
+                                _p(off), _p(m), _p(ox), _p(y), _p(acc))
+    if rc != 0:
+        raise ValueError(f"oracle_combine rejected the input (rc={rc})")
+    return y
+
+
+def combine_token(cfg, expert_out, expert_ids, expand_idx, expert_scales, ep_recv_count,
+                  recv_offsets, s, i, mask=None, ori_x=None):
+    """Combine for one source token (s, i); the big arrays are passed without copying when
+    they are already contiguous in the right dtype."""
+    eo = _c(expert_out, np.uint16)
+    ids = _c(expert_ids, np.int32)
+    eidx = _c(expand_idx, np.int32)
+    w = _c(expert_scales, np.float32)
+    erc = _c(ep_recv_count, np.int32)
+    off = _c(recv_offsets, np.int64)
+    m = _c(mask, np.uint8)
+    ox = _c(ori_x, np.uint16)
+    y = np.empty(cfg.H, np.uint16)
+    acc = np.empty(cfg.H, np.float32)
+    rc = _load().oracle_combine_token(_ref(cfg), _p(eo), _p(ids), _p(eidx), _p(w), _p(erc),
+                                      _p(off), _p(m), _p(ox), int(s), int(i), _p(acc), _p(y))
+    if rc != 0:
+        raise ValueError(f"oracle_combine_token rejected the input (rc={rc})")
+    return y

@@ -1,0 +1,84 @@
+/*
+ * moe_oracle.h -- plain, slow, single-threaded CPU oracle for MoE dispatch/combine.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link or call
+ * this code: only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg use it.
+ * It shares no header, helper, table or constant with the HIP library.
+ *
+ * Pages cited (by title; sections as numbered on each page):
+ *   [DDD] "MoeDistributeDispatch和MoeDistributeCombine算子设计介绍" (gitcode design doc, Atlas A2)
+ *   [LLD] "low_latency_dispatch" (hiascend API doc), sections 计算公式 and 约束说明
+ *   [OPS] "CANN ops-transformer 算子解析：MoeDistributeDispatchV3 的 EP 域 Token 分发与动态量化通信实现"
+ *         (mwwr.cn article), sections 功能说明, 参数说明, 约束说明, 接口级量化模式扩展
+ *   [SMP] "CANN MoE Dispatch/Combine 通信算子性能优化实践：Kernel 直调与 ACL SHMEM 实现专家分发与聚合"
+ *         (lqnn.cn article), sections Dispatch 功能介绍, Combine 功能介绍, 通信前量化
+ *
+ * Conventions: all pointers are host pointers; bf16 values travel as uint16_t bit patterns;
+ * arrays are C-contiguous in the shapes stated at each function.  Return 0 on success,
+ * a negative value on a contract violation (the oracle refuses rather than guesses).
+ */
+#ifndef MOE_ORACLE_H
+#define MOE_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+    int32_t W;                      /* logical EP ranks                                   */
+    int32_t E;                      /* routed experts; L = E / W per rank                 */
+    int32_t BS;                     /* tokens per source rank                             */
+    int32_t H;                      /* hidden size                                        */
+    int32_t K;                      /* picks per token                                    */
+    int32_t quant_mode;             /* 0 none, 2 int8 per token, 4 MX, 5 MX clip          */
+    int32_t zero_expert_num;        /* ids [E, E+Z) are zero experts                      */
+    int32_t copy_expert_num;        /* ids [E+Z, E+Z+C) are copy experts                  */
+    int32_t expert_token_nums_type; /* 0 inclusive cumsum, 1 per-expert counts            */
+    int32_t mask_kind;              /* 0 none, 1 per token [W][BS], 2 per pair [W][BS][K] */
+} oracle_cfg;
+
+/* scalar helpers (each written from its definition) */
+float    oracle_bf16_to_f32(uint16_t b);
+uint16_t oracle_f32_to_bf16(float f);
+uint8_t  oracle_e4m3_from_f32(float v);
+float    oracle_e4m3_to_f32(uint8_t code);
+int32_t  oracle_mx_scale_count(int32_t H);
+
+/* per-row quantization */
+void oracle_quant_int8_row(const uint16_t* x, const float* smooth_or_null, int32_t H,
+                           int8_t* q, float* scale);
+void oracle_quant_mx_row(const uint16_t* x, int32_t H, int32_t clip, uint8_t* codes,
+                         float* scales);
+
+/* routing, receive counts, destination rows */
+int32_t oracle_route(const oracle_cfg* c, const int32_t* expert_ids, const uint8_t* mask,
+                     int32_t* cnt, int32_t* expand_idx);
+int32_t oracle_recv_counts(const oracle_cfg* c, const int32_t* cnt, int32_t* ep_recv_count,
+                           int64_t* expert_token_nums, int64_t* recv_offsets);
+int64_t oracle_dest_row(const oracle_cfg* c, const int32_t* ep_recv_count,
+                        const int64_t* recv_offsets, int32_t s, int32_t e, int32_t ordinal);
+
+/* whole dispatch and combine */
+int32_t oracle_dispatch(const oracle_cfg* c, const uint16_t* x, const int32_t* expert_ids,
+                        const float* smooth_or_null, const uint8_t* mask, void* expand_x,
+                        float* dynamic_scales, int32_t* expand_idx, int32_t* assist_info,
+                        int32_t* ep_recv_count, int64_t* expert_token_nums,
+                        int64_t* recv_offsets, int32_t* cnt_scratch);
+int32_t oracle_combine_token(const oracle_cfg* c, const uint16_t* expert_out,
+                             const int32_t* expert_ids, const int32_t* expand_idx,
+                             const float* expert_scales, const int32_t* ep_recv_count,
+                             const int64_t* recv_offsets, const uint8_t* mask,
+                             const uint16_t* ori_x, int32_t s, int32_t i, float* acc_scratch,
+                             uint16_t* y_row);
+int32_t oracle_combine(const oracle_cfg* c, const uint16_t* expert_out,
+                       const int32_t* expert_ids, const int32_t* expand_idx,
+                       const float* expert_scales, const int32_t* ep_recv_count,
+                       const int64_t* recv_offsets, const uint8_t* mask,
+                       const uint16_t* ori_x, uint16_t* y, float* acc_scratch);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

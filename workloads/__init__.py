@@ -1,0 +1,233 @@
+"""Seeded synthetic inputs for MoE dispatch/combine.
+
+This module is shared by the tests, the bench and the smoke check; it holds only input
+generation (random draws, bf16 rounding of the draws, softmax of the routing logits) and none
+of the dispatch/combine arithmetic, so neither the oracle nor the HIP path depends on the
+other through it.
+
+The pages measure only on random synthetic data (the sample's data generator draws random
+tokens and routing); there is no public dataset to stand in for.  Workloads below follow the
+shapes the pages work with: H up to 8192, BS <= 512 tokens per rank, K <= 16 and
+DeepSeek-V3-style 256-expert routing.
+
+Recipe (numpy PCG64, one spawned sub-stream per tensor, base seed 0 by default):
+  x              bf16 of N(0,1) fp32 samples (round to nearest even); optional outliers:
+                 each value independently x10 with the workload's probability
+  expert_ids     uniform: K distinct ids per token, in the order of a uniform random
+                 permutation; zipf: K distinct ids drawn one after another without
+                 replacement with probability proportional to 1/rank^s over a seeded
+                 permutation of the experts (drawn with the Gumbel top-K construction,
+                 which has exactly that sequential law); randint: K independent uniform ids
+                 (duplicates allowed)
+  smooth         fp32 U(0.5, 1.5), shape [E][H]
+  mask           none; per token [W][BS]; or per pick [W][BS][K] with a fixed number of
+                 tokens per rank fully inactive (seeded choice)
+  expert_scales  fp32 softmax of N(0,1) logits over each token's K picks
+  expert_out     bf16 of N(0,1) fp32 samples, one row per received row
+"""
+from __future__ import annotations
+
+import dataclasses
+from dataclasses import dataclass
+
+import numpy as np
+
+# sub-stream slots of SeedSequence(seed).spawn(N_STREAMS)
+_X, _IDS, _SMOOTH, _MASK, _WEIGHTS, _EXPERT_OUT, _OUTLIER, _SPARE = range(8)
+N_STREAMS = 8
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    W: int                      # logical EP ranks
+    E: int                      # routed experts
+    BS: int                     # tokens per rank
+    H: int                      # hidden size
+    K: int                      # picks per token
+    quant_mode: int             # 0, 2, 4, 5
+    zero_expert_num: int = 0
+    copy_expert_num: int = 0
+    expert_token_nums_type: int = 1
+    mask_kind: int = 0          # 0 none, 1 per token, 2 per pick
+    smooth: bool = False
+    routing: str = "uniform"    # uniform | zipf | randint
+    zipf_s: float = 1.2
+    outlier_prob: float = 0.0
+    inactive_tokens_per_rank: int = 0
+    description: str = ""
+
+    @property
+    def L(self) -> int:
+        return self.E // self.W
+
+    @property
+    def T(self) -> int:
+        return self.W * self.BS
+
+    @property
+    def n_ids(self) -> int:
+        return self.E + self.zero_expert_num + self.copy_expert_num
+
+    @property
+    def cap(self) -> int:
+        """Rows that always suffice for the packed expand_x (every pick routed)."""
+        return self.W * self.BS * self.K
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+C1_MODE0 = Workload(
+    "c1_tiny_mode0", W=2, E=8, BS=16, H=1024, K=2, quant_mode=0,
+    description="tiny: W=2, E=8 (L=4), BS=16, H=1024, K=2, bf16 N(0,1), uniform distinct "
+                "top-2, no quantization, softmax weights")
+C1_MODE2 = C1_MODE0.replace(
+    name="c1_tiny_mode2", quant_mode=2,
+    description="tiny: W=2, E=8 (L=4), BS=16, H=1024, K=2, int8 per-token quant without "
+                "smooth scales")
+C2 = Workload(
+    "c2_w8_smooth", W=8, E=256, BS=128, H=7168, K=8, quant_mode=2, smooth=True,
+    outlier_prob=0.01, expert_token_nums_type=0,
+    description="W=8, E=256 (L=32), BS=128, H=7168, K=8, bf16 N(0,1) with 1% of values x10, "
+                "int8 per-token quant with per-expert smooth scales U(0.5,1.5), uniform "
+                "distinct top-8")
+C3 = Workload(
+    "c3_w16_mxfp8_zipf", W=16, E=256, BS=512, H=7168, K=8, quant_mode=4, routing="zipf",
+    description="W=16, E=256 (L=16), BS=512, H=7168, K=8, bf16 N(0,1), MX E4M3 32-element "
+                "blocks, Zipf(1.2) routing over a seeded expert permutation")
+C4 = Workload(
+    "c4_w16_int8_roundtrip", W=16, E=256, BS=512, H=7168, K=8, quant_mode=2,
+    description="W=16, E=256 (L=16), BS=512, H=7168, K=8, bf16 N(0,1), int8 per-token quant "
+                "(no smooth), uniform distinct top-8; combine reads bf16 N(0,1) expert "
+                "outputs per received row")
+C5 = Workload(
+    "c5_w32_mxclip_special", W=32, E=512, BS=512, H=8192, K=16, quant_mode=5,
+    zero_expert_num=2, copy_expert_num=2, mask_kind=2, inactive_tokens_per_rank=51,
+    description="W=32, E=512 (L=16) + 2 zero + 2 copy experts, BS=512, H=8192, K=16, bf16 "
+                "N(0,1), MX clip E4M3, per-pick mask with 51 of 512 tokens per rank fully "
+                "inactive, uniform distinct top-16 over all 516 ids")
+
+WORKLOADS = {w.name: w for w in (C1_MODE0, C1_MODE2, C2, C3, C4, C5)}
+
+
+def _streams(seed: int):
+    return [np.random.Generator(np.random.PCG64(s))
+            for s in np.random.SeedSequence(seed).spawn(N_STREAMS)]
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 samples to bf16 bit patterns (nearest, ties to even); inputs are finite."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    rounded = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return (rounded >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(
+        np.float32)
+
+
+def _normal_bf16(rng, shape, chunk=1 << 24) -> np.ndarray:
+    n = int(np.prod(shape))
+    out = np.empty(n, np.uint16)
+    for lo in range(0, n, chunk):
+        hi = min(n, lo + chunk)
+        out[lo:hi] = f32_to_bf16_bits(rng.standard_normal(hi - lo, dtype=np.float32))
+    return out.reshape(shape)
+
+
+def _topk_keys(keys: np.ndarray, K: int) -> np.ndarray:
+    """Indices of the K largest keys per row, largest first."""
+    part = np.argpartition(-keys, K - 1, axis=1)[:, :K]
+    order = np.argsort(-np.take_along_axis(keys, part, axis=1), axis=1, kind="stable")
+    return np.take_along_axis(part, order, axis=1)
+
+
+def gen_expert_ids(wl: Workload, rng) -> np.ndarray:
+    T, K, n = wl.T, wl.K, wl.n_ids
+    if wl.routing == "randint":
+        ids = rng.integers(0, n, size=(T, K), dtype=np.int64)
+    elif wl.routing == "uniform":
+        ids = np.empty((T, K), np.int64)
+        step = max(1, (1 << 22) // n)
+        for lo in range(0, T, step):
+            hi = min(T, lo + step)
+            ids[lo:hi] = _topk_keys(rng.random((hi - lo, n)), K)
+    elif wl.routing == "zipf":
+        if wl.zero_expert_num or wl.copy_expert_num:
+            raise ValueError("zipf routing is defined over routed experts only")
+        perm = rng.permutation(wl.E)                 # perm[rank-1] = expert id
+        logw = np.empty(wl.E)
+        logw[perm] = -wl.zipf_s * np.log(np.arange(1, wl.E + 1, dtype=np.float64))
+        ids = np.empty((T, K), np.int64)
+        step = max(1, (1 << 22) // wl.E)
+        for lo in range(0, T, step):
+            hi = min(T, lo + step)
+            g = rng.gumbel(size=(hi - lo, wl.E))
+            ids[lo:hi] = _topk_keys(logw[None, :] + g, K)
+    else:
+        raise ValueError(f"unknown routing {wl.routing!r}")
+    return ids.astype(np.int32).reshape(wl.W, wl.BS, K)
+
+
+def gen_mask(wl: Workload, rng):
+    if wl.mask_kind == 0:
+        return None
+    if wl.mask_kind == 1:
+        # per token, trues before falses within each rank
+        m = np.ones((wl.W, wl.BS), np.uint8)
+        n_off = wl.inactive_tokens_per_rank
+        if n_off:
+            m[:, wl.BS - n_off:] = 0
+        return m
+    m = np.ones((wl.W, wl.BS, wl.K), np.uint8)
+    for s in range(wl.W):
+        off = rng.choice(wl.BS, size=wl.inactive_tokens_per_rank, replace=False)
+        m[s, off, :] = 0
+    return m
+
+
+def gen_expert_scales(wl: Workload, rng) -> np.ndarray:
+    logits = rng.standard_normal((wl.T, wl.K), dtype=np.float32)
+    z = np.exp(logits - logits.max(axis=1, keepdims=True))
+    w = (z / z.sum(axis=1, keepdims=True)).astype(np.float32)
+    return w.reshape(wl.W, wl.BS, wl.K)
+
+
+def generate(wl: Workload, seed: int = 0, expert_out_rows: int | None = None) -> dict:
+    """All host inputs of one dispatch+combine round trip.
+
+    expert_out is generated only when expert_out_rows is given (it can be large)."""
+    st = _streams(seed)
+    x = _normal_bf16(st[_X], (wl.W, wl.BS, wl.H))
+    if wl.outlier_prob > 0:
+        hit = st[_OUTLIER].random((wl.W, wl.BS, wl.H)) < wl.outlier_prob
+        xf = bf16_bits_to_f32(x)
+        xf[hit] *= np.float32(10.0)
+        x = f32_to_bf16_bits(xf)
+    out = dict(
+        x=x,
+        expert_ids=gen_expert_ids(wl, st[_IDS]),
+        mask=gen_mask(wl, st[_MASK]),
+        expert_scales=gen_expert_scales(wl, st[_WEIGHTS]),
+        smooth=(st[_SMOOTH].uniform(0.5, 1.5, (wl.E, wl.H)).astype(np.float32)
+                if wl.smooth else None),
+    )
+    if expert_out_rows is not None:
+        out["expert_out"] = _normal_bf16(st[_EXPERT_OUT], (expert_out_rows, wl.H))
+    return out
+
+
+def expert_out_torch(wl: Workload, rows: int, seed: int = 0, device="cuda"):
+    """bf16 N(0,1) expert outputs drawn on the device with torch's seeded generator.
+
+    Used where the numpy draw of a multi-GB buffer would dominate a run; the values are
+    still a pure function of (seed, rows, H), and the host copy of the same bytes is what
+    the oracle reads."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(np.random.SeedSequence(seed).spawn(N_STREAMS)[_EXPERT_OUT]
+                      .generate_state(1)[0]))
+    return torch.randn((rows, wl.H), generator=g, device=device,
+                       dtype=torch.float32).to(torch.bfloat16)
