@@ -1,0 +1,245 @@
+"""ctypes binding of libmoe_dc.so: argument marshalling only.
+
+Function names mirror the C ABI in include/moe_dc.h.  Every step of dispatch and combine runs
+in the library's HIP kernels; this module checks tensor dtypes/shapes/devices, passes raw
+device pointers and the current HIP stream, and turns a negative status into an exception.
+It never falls back to another implementation: if the library is missing, loading fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from .build import LIB
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = 0, -1, -2, -3, -4
+_STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
+           -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_DEVICE"}
+
+EXPORTS = ("moe_dc_validate", "moe_dc_scales_per_row", "moe_dc_dispatch_workspace_bytes",
+           "moe_dispatch", "moe_combine", "moe_dc_last_error", "moe_dc_version")
+
+
+class MoeDcConfig(ctypes.Structure):
+    """Mirror of moe_dc_config."""
+    _fields_ = [
+        ("ep_world_size", ctypes.c_int32),
+        ("moe_expert_num", ctypes.c_int32),
+        ("bs", ctypes.c_int32),
+        ("hidden", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("quant_mode", ctypes.c_int32),
+        ("zero_expert_num", ctypes.c_int32),
+        ("copy_expert_num", ctypes.c_int32),
+        ("const_expert_num", ctypes.c_int32),
+        ("expert_token_nums_type", ctypes.c_int32),
+        ("mask_kind", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("expand_rows_capacity", ctypes.c_int64),
+    ]
+
+    @property
+    def W(self):
+        return self.ep_world_size
+
+    @property
+    def E(self):
+        return self.moe_expert_num
+
+    @property
+    def L(self):
+        return self.moe_expert_num // self.ep_world_size
+
+
+class MoeDcError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB) -> ctypes.CDLL:
+    """Load libmoe_dc.so (raises OSError when it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise OSError(f"{path} is missing: build it with combine_quant_amd.build.build()")
+    lib = ctypes.CDLL(path)
+    P, cfgp = ctypes.c_void_p, ctypes.POINTER(MoeDcConfig)
+    lib.moe_dc_validate.restype = ctypes.c_int
+    lib.moe_dc_validate.argtypes = [cfgp]
+    lib.moe_dc_scales_per_row.restype = ctypes.c_int32
+    lib.moe_dc_scales_per_row.argtypes = [cfgp]
+    lib.moe_dc_dispatch_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_dc_dispatch_workspace_bytes.argtypes = [cfgp]
+    lib.moe_dispatch.restype = ctypes.c_int
+    lib.moe_dispatch.argtypes = [cfgp] + [P] * 11 + [P, ctypes.c_size_t, P]
+    lib.moe_combine.restype = ctypes.c_int
+    lib.moe_combine.argtypes = [cfgp] + [P] * 9 + [P]
+    lib.moe_dc_last_error.restype = ctypes.c_char_p
+    lib.moe_dc_last_error.argtypes = []
+    lib.moe_dc_version.restype = ctypes.c_char_p
+    lib.moe_dc_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def make_config(W, E, BS, H, K, quant_mode=0, zero_expert_num=0, copy_expert_num=0,
+                const_expert_num=0, expert_token_nums_type=1, mask_kind=0, cap=None):
+    cap = W * BS * K if cap is None else cap
+    return MoeDcConfig(W, E, BS, H, K, quant_mode, zero_expert_num, copy_expert_num,
+                       const_expert_num, expert_token_nums_type, mask_kind, 0, cap)
+
+
+def _check(status: int):
+    if status != MOE_OK:
+        raise MoeDcError(status, load_library().moe_dc_last_error().decode())
+
+
+def moe_dc_last_error() -> str:
+    return load_library().moe_dc_last_error().decode()
+
+
+def moe_dc_version() -> str:
+    return load_library().moe_dc_version().decode()
+
+
+def moe_dc_validate(cfg: MoeDcConfig) -> int:
+    return load_library().moe_dc_validate(ctypes.byref(cfg))
+
+
+def moe_dc_scales_per_row(cfg: MoeDcConfig) -> int:
+    return load_library().moe_dc_scales_per_row(ctypes.byref(cfg))
+
+
+def moe_dc_dispatch_workspace_bytes(cfg: MoeDcConfig) -> int:
+    return load_library().moe_dc_dispatch_workspace_bytes(ctypes.byref(cfg))
+
+
+def _ptr(t, dtype=None, shape=None, name="tensor", device=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device, stream):
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+_CODE_DTYPES = {0: torch.bfloat16, 2: torch.int8, 4: (torch.uint8, torch.float8_e4m3fn),
+                5: (torch.uint8, torch.float8_e4m3fn)}
+
+
+def moe_dispatch(cfg, x, expert_ids, smooth_scales, x_active_mask, expand_x, dynamic_scales,
+                 expand_idx, assist_info, ep_recv_count, expert_token_nums, recv_offsets,
+                 workspace, stream=None):
+    """Enqueue one dispatch on `stream` (default: the current stream of x's device)."""
+    W, BS, H, K, E, L, cap = (cfg.ep_world_size, cfg.bs, cfg.hidden, cfg.topk,
+                              cfg.moe_expert_num, cfg.L, cfg.expand_rows_capacity)
+    dev = x.device
+    ns = moe_dc_scales_per_row(cfg)
+    mshape = {1: (W, BS), 2: (W, BS, K)}.get(cfg.mask_kind)
+    args = [
+        _ptr(x, torch.bfloat16, (W, BS, H), "x", dev),
+        _ptr(expert_ids, torch.int32, (W, BS, K), "expert_ids", dev),
+        _ptr(smooth_scales, torch.float32, (E, H), "smooth_scales", dev),
+        _ptr(x_active_mask, (torch.uint8, torch.bool), mshape, "x_active_mask", dev),
+        _ptr(expand_x, _CODE_DTYPES.get(cfg.quant_mode), (cap, H), "expand_x", dev),
+        _ptr(dynamic_scales, torch.float32, None if ns <= 0 else
+             ((cap,) if ns == 1 else (cap, ns)), "dynamic_scales", dev),
+        _ptr(expand_idx, torch.int32, (W, BS, K), "expand_idx", dev),
+        _ptr(assist_info, torch.int32, (cap, 3), "assist_info", dev),
+        _ptr(ep_recv_count, torch.int32, (W, L * W), "ep_recv_count", dev),
+        _ptr(expert_token_nums, torch.int64, (W, L), "expert_token_nums", dev),
+        _ptr(recv_offsets, torch.int64, (W + 1,), "recv_offsets", dev),
+        _ptr(workspace, torch.uint8, None, "workspace", dev),
+    ]
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    lib = load_library()
+    _check(lib.moe_dispatch(ctypes.byref(cfg), *args, ctypes.c_size_t(ws_bytes),
+                            _stream(dev, stream)))
+
+
+def moe_combine(cfg, expert_out, expert_ids, expand_idx, expert_scales, ep_recv_count,
+                recv_offsets, x_active_mask, ori_x, y, stream=None):
+    """Enqueue one combine on `stream` (default: the current stream of y's device)."""
+    W, BS, H, K, L, cap = (cfg.ep_world_size, cfg.bs, cfg.hidden, cfg.topk, cfg.L,
+                           cfg.expand_rows_capacity)
+    dev = y.device
+    mshape = {1: (W, BS), 2: (W, BS, K)}.get(cfg.mask_kind)
+    args = [
+        _ptr(expert_out, torch.bfloat16, (cap, H), "expert_out", dev),
+        _ptr(expert_ids, torch.int32, (W, BS, K), "expert_ids", dev),
+        _ptr(expand_idx, torch.int32, (W, BS, K), "expand_idx", dev),
+        _ptr(expert_scales, torch.float32, (W, BS, K), "expert_scales", dev),
+        _ptr(ep_recv_count, torch.int32, (W, L * W), "ep_recv_count", dev),
+        _ptr(recv_offsets, torch.int64, (W + 1,), "recv_offsets", dev),
+        _ptr(x_active_mask, (torch.uint8, torch.bool), mshape, "x_active_mask", dev),
+        _ptr(ori_x, torch.bfloat16, (W, BS, H), "ori_x", dev),
+        _ptr(y, torch.bfloat16, (W, BS, H), "y", dev),
+    ]
+    lib = load_library()
+    _check(lib.moe_combine(ctypes.byref(cfg), *args, _stream(dev, stream)))
+
+
+# -- allocation helpers (torch owns the memory; the library never allocates) ----------------
+
+def alloc_dispatch_outputs(cfg, device="cuda"):
+    """Empty output tensors and a workspace sized for cfg."""
+    _check(moe_dc_validate(cfg))
+    W, BS, H, K, L, cap = (cfg.ep_world_size, cfg.bs, cfg.hidden, cfg.topk, cfg.L,
+                           cfg.expand_rows_capacity)
+    ns = moe_dc_scales_per_row(cfg)
+    code_dtype = {0: torch.bfloat16, 2: torch.int8}.get(cfg.quant_mode, torch.uint8)
+    return dict(
+        expand_x=torch.empty((cap, H), dtype=code_dtype, device=device),
+        dynamic_scales=(None if ns == 0 else
+                        torch.empty((cap,) if ns == 1 else (cap, ns), dtype=torch.float32,
+                                    device=device)),
+        expand_idx=torch.empty((W, BS, K), dtype=torch.int32, device=device),
+        assist_info=torch.empty((cap, 3), dtype=torch.int32, device=device),
+        ep_recv_count=torch.empty((W, L * W), dtype=torch.int32, device=device),
+        expert_token_nums=torch.empty((W, L), dtype=torch.int64, device=device),
+        recv_offsets=torch.empty((W + 1,), dtype=torch.int64, device=device),
+        workspace=torch.empty((moe_dc_dispatch_workspace_bytes(cfg),), dtype=torch.uint8,
+                              device=device),
+    )
+
+
+def dispatch(cfg, x, expert_ids, smooth_scales=None, x_active_mask=None, out=None,
+             stream=None):
+    """Allocate (or reuse `out`) and enqueue moe_dispatch; returns the output dict."""
+    o = alloc_dispatch_outputs(cfg, x.device) if out is None else out
+    moe_dispatch(cfg, x, expert_ids, smooth_scales, x_active_mask, o["expand_x"],
+                 o["dynamic_scales"], o["expand_idx"], o["assist_info"], o["ep_recv_count"],
+                 o["expert_token_nums"], o["recv_offsets"], o["workspace"], stream)
+    return o
+
+
+def combine(cfg, expert_out, expert_ids, expand_idx, expert_scales, ep_recv_count,
+            recv_offsets, x_active_mask=None, ori_x=None, y=None, stream=None):
+    """Allocate (or reuse `y`) and enqueue moe_combine; returns y."""
+    if y is None:
+        y = torch.empty((cfg.ep_world_size, cfg.bs, cfg.hidden), dtype=torch.bfloat16,
+                        device=expert_out.device)
+    moe_combine(cfg, expert_out, expert_ids, expand_idx, expert_scales, ep_recv_count,
+                recv_offsets, x_active_mask, ori_x, y, stream)
+    return y

@@ -1,0 +1,178 @@
+// combine.hip -- top-K weighted gather back to the source tokens.
+//
+// One workgroup per source token.  Lanes 0..K-1 first resolve each pick's source row with
+// the design doc's addressing rule (§3.4.2: the owner rank's window + the expert's offset
+// inside it + expand_idx), written here with the dispatch outputs: recv_offsets[r] + the
+// running total of ep_recv_count just before (local expert j, source s) + expand_idx.
+// Special experts follow the low_latency_dispatch formulas: a zero expert contributes
+// nothing, a copy expert contributes its weight times ori_x.
+//
+// Each lane then owns 16-byte column vectors of the token; for each it issues the K row
+// loads first (all in flight together) and only then accumulates in pick order, one fp32
+// multiply and one fp32 add per pick (the sample article's combine: weight each expert row,
+// accumulate in fp32, cast down), and stores the bf16 rounding of the sum.
+#include "dc_device.h"
+#include "dc_internal.h"
+
+namespace moe_dc {
+namespace {
+
+constexpr int kMaxThreads = 1024;
+constexpr int kVpt = 8;
+
+template <int VEC> struct Cio;
+
+template <> struct Cio<8> {
+    using Raw = uint4;
+    static __device__ __forceinline__ Raw load(const uint16_t* p, int v)
+    {
+        return reinterpret_cast<const uint4*>(p)[v];
+    }
+    static __device__ __forceinline__ void accumulate(Raw w, float wt, float (&acc)[8])
+    {
+        const float f[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
+                            bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] = acc[c] + wt * f[c];
+    }
+    static __device__ __forceinline__ void store(uint16_t* p, int v, const float (&acc)[8])
+    {
+        reinterpret_cast<uint4*>(p)[v] =
+            make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                       pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+    }
+};
+
+template <> struct Cio<1> {
+    using Raw = uint16_t;
+    static __device__ __forceinline__ Raw load(const uint16_t* p, int v) { return p[v]; }
+    static __device__ __forceinline__ void accumulate(Raw w, float wt, float (&acc)[1])
+    {
+        acc[0] = acc[0] + wt * __uint_as_float((uint32_t)w << 16);
+    }
+    static __device__ __forceinline__ void store(uint16_t* p, int v, const float (&acc)[1])
+    {
+        p[v] = (uint16_t)f32_to_bf16_rne(acc[0]);
+    }
+};
+
+constexpr long long kNone = -1;   // inactive pick, zero expert, or unresolvable
+constexpr long long kCopy = -2;   // copy expert: read ori_x
+
+template <int VEC, int KMAX>
+__global__ __launch_bounds__(kMaxThreads) void combine_kernel(
+    const uint16_t* __restrict__ expert_out, const int32_t* __restrict__ ids,
+    const int32_t* __restrict__ expand_idx, const float* __restrict__ weights,
+    const int32_t* __restrict__ ep_recv_count, const int64_t* __restrict__ recv_offsets,
+    const uint8_t* __restrict__ mask, int mask_kind, const uint16_t* __restrict__ ori_x,
+    uint16_t* __restrict__ y, int W, int E, int L, int BS, int H, int K, int zero_end,
+    int id_end, long long cap)
+{
+    using IO = Cio<VEC>;
+    __shared__ long long src_of[KMAX];
+    __shared__ float w_of[KMAX];
+
+    const size_t tok = blockIdx.x;
+    const int s = (int)(tok / BS);
+    const int t = threadIdx.x;
+    const int nt = blockDim.x;
+
+    if (t < K) {
+        const size_t p = tok * K + t;
+        const int32_t e = ids[p];
+        const bool on = mask_kind == 0 || (mask_kind == 1 ? mask[tok] != 0 : mask[p] != 0);
+        long long src = kNone;
+        if (on && e >= 0) {
+            if (e < E) {
+                const int32_t ord = expand_idx[p];
+                if (ord >= 0) {
+                    const int r = e / L;
+                    const int j = e - r * L;
+                    const long long flat = (long long)j * W + s;
+                    const long long base =
+                        flat == 0 ? 0 : (long long)ep_recv_count[(size_t)r * L * W + flat - 1];
+                    const long long row = (long long)recv_offsets[r] + base + ord;
+                    if (row >= 0 && row < cap) src = row * H;
+                }
+            } else if (e >= zero_end && e < id_end) {
+                src = kCopy;
+            }
+        }
+        src_of[t] = src;
+        w_of[t] = weights[p];
+    }
+    __syncthreads();
+
+    const int NV = H / VEC;
+    const uint16_t* self = ori_x ? ori_x + tok * (size_t)H : nullptr;
+    uint16_t* yr = y + tok * (size_t)H;
+#pragma unroll 1
+    for (int n = 0; n < kVpt; ++n) {
+        const int v = t + n * nt;
+        if (v >= NV) break;
+        typename IO::Raw buf[KMAX];
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            if (k < K) {
+                const long long src = src_of[k];
+                if (src >= 0) buf[k] = IO::load(expert_out + src, v);
+                else if (src == kCopy) buf[k] = IO::load(self, v);
+            }
+        }
+        float acc[VEC];
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) acc[c] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            if (k < K && src_of[k] != kNone) IO::accumulate(buf[k], w_of[k], acc);
+        IO::store(yr, v, acc);
+    }
+}
+
+template <int VEC, int KMAX>
+hipError_t launch_k(const Shape& sh, const void* expert_out, const int32_t* ids,
+                    const int32_t* expand_idx, const float* w, const int32_t* erc,
+                    const int64_t* roff, const uint8_t* mask, const void* ori_x, void* y,
+                    hipStream_t stream)
+{
+    // one vector per lane when the row fits in one workgroup, else up to kVpt per lane
+    // (H <= 8192 always fits: 1024 lanes x 8 elements)
+    const int NV = sh.H / VEC;
+    const int want = (NV + kWave - 1) / kWave * kWave;
+    const int threads = want < kMaxThreads ? want : kMaxThreads;
+    const size_t tokens = (size_t)sh.W * sh.BS;
+    hipLaunchKernelGGL((combine_kernel<VEC, KMAX>), dim3((unsigned)tokens), dim3(threads), 0,
+                       stream, static_cast<const uint16_t*>(expert_out), ids, expand_idx, w,
+                       erc, roff, mask, sh.mask_kind, static_cast<const uint16_t*>(ori_x),
+                       static_cast<uint16_t*>(y), sh.W, sh.E, sh.L, sh.BS, sh.H, sh.K,
+                       sh.zero_end, sh.id_end, (long long)sh.cap);
+    return hipGetLastError();
+}
+
+template <int VEC>
+hipError_t launch_vec(const Shape& sh, const void* eo, const int32_t* ids, const int32_t* ei,
+                      const float* w, const int32_t* erc, const int64_t* roff,
+                      const uint8_t* mask, const void* ori_x, void* y, hipStream_t stream)
+{
+    if (sh.K <= 2) return launch_k<VEC, 2>(sh, eo, ids, ei, w, erc, roff, mask, ori_x, y, stream);
+    if (sh.K <= 4) return launch_k<VEC, 4>(sh, eo, ids, ei, w, erc, roff, mask, ori_x, y, stream);
+    if (sh.K <= 8) return launch_k<VEC, 8>(sh, eo, ids, ei, w, erc, roff, mask, ori_x, y, stream);
+    return launch_k<VEC, 16>(sh, eo, ids, ei, w, erc, roff, mask, ori_x, y, stream);
+}
+
+}  // namespace
+
+hipError_t launch_combine(const Shape& sh, const void* expert_out, const int32_t* expert_ids,
+                          const int32_t* expand_idx, const float* expert_scales,
+                          const int32_t* ep_recv_count, const int64_t* recv_offsets,
+                          const uint8_t* mask, const void* ori_x, void* y, bool vectorized,
+                          hipStream_t stream)
+{
+    if (vectorized)
+        return launch_vec<8>(sh, expert_out, expert_ids, expand_idx, expert_scales,
+                             ep_recv_count, recv_offsets, mask, ori_x, y, stream);
+    return launch_vec<1>(sh, expert_out, expert_ids, expand_idx, expert_scales, ep_recv_count,
+                         recv_offsets, mask, ori_x, y, stream);
+}
+
+}  // namespace moe_dc

@@ -1,0 +1,91 @@
+// dc_device.h -- device helpers for the gfx950 dispatch/combine kernels.
+//
+// Everything here is written for CDNA4 wave64 execution.  Numerics follow the formulas of
+// the pages exactly as the library header states them: one binary32 operation per written
+// float operation (the library is built with -ffp-contract=off, so no FMA fusion), IEEE
+// division, subnormals kept.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe_dc {
+
+constexpr int kWave = 64;
+constexpr int kMaxK = 16;          // largest top-k the pages allow
+constexpr int kMxBlock = 32;       // MX block length (elements sharing one exponent)
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// binary32 -> bf16 bit pattern, round to nearest even, NaN kept quiet.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// E4M3 ("fn" variant: bias 7, no infinities, 448 largest) code of a finite binary32 value:
+// nearest, ties to even, magnitudes >= 448 saturate to 448, sign kept (also on zero).
+// Normal results: round the binary32 significand to 3 fraction bits at bit 20 and rebias
+// the exponent from 127 to 7.  Below 2^-6 the E4M3 grid is uniform with step 2^-9, so the
+// code is |v| * 2^9 rounded to an integer (8 lands exactly on the smallest normal, 0x08).
+__device__ __forceinline__ uint32_t e4m3_code(float v)
+{
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    if (a >= 0x43E00000u) return sign | 0x7Eu;                 // |v| >= 448
+    if (a < 0x3C800000u) {                                     // |v| < 2^-6
+        const float scaled = __uint_as_float(a) * 512.0f;      // exact power-of-two scaling
+        return sign | (uint32_t)__builtin_rintf(scaled);
+    }
+    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    return sign | ((((r >> 23) - 120u) << 3) | ((r >> 20) & 7u));
+}
+
+// Largest value across the 64 lanes of a wave (unsigned).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        uint32_t o = __shfl_xor(v, off, kWave);
+        v = v > o ? v : o;
+    }
+    return v;
+}
+
+// Largest value over groups of G adjacent lanes (G a power of two <= 64).
+template <int G>
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t v)
+{
+#pragma unroll
+    for (int off = G / 2; off >= 1; off >>= 1) {
+        uint32_t o = __shfl_xor(v, off, kWave);
+        v = v > o ? v : o;
+    }
+    return v;
+}
+
+// Block-wide unsigned max; `scratch` holds one word per wave.  Every thread gets the result.
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* scratch)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int nwaves = (blockDim.x + kWave - 1) / kWave;
+    v = wave_max_u32(v);
+    if (lane == 0) scratch[wave] = v;
+    __syncthreads();
+    uint32_t r = 0;
+    for (int w = 0; w < nwaves; ++w) r = r > scratch[w] ? r : scratch[w];
+    __syncthreads();
+    return r;
+}
+
+}  // namespace moe_dc

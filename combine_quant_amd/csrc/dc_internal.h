@@ -1,0 +1,52 @@
+// dc_internal.h -- launch interface between the C-ABI layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe_dc {
+
+// Validated shape of one dispatch/combine problem (see moe_dc_config in include/moe_dc.h).
+struct Shape {
+    int32_t W, E, L, BS, H, K;
+    int32_t quant_mode;
+    int32_t zero_end;        // E + zero_expert_num
+    int32_t id_end;          // E + zero_expert_num + copy_expert_num
+    int32_t etn_type;
+    int32_t mask_kind;
+    int32_t scales_per_row;  // 0, 1 or Align2(Ceil(H,32))
+    int64_t cap;
+};
+
+// Workspace layout of moe_dispatch: one int32 per (expert e, source rank s) at e*W + s.
+// The route kernel stores the pick counts there; the scan kernel overwrites each with the
+// exclusive running total, i.e. the first packed row of that (expert, source) segment.
+inline size_t workspace_bytes(const Shape& s)
+{
+    size_t b = (size_t)s.E * (size_t)s.W * sizeof(int32_t);
+    return (b + 255) & ~(size_t)255;
+}
+
+// Routing: counts per (expert, source) and the final expand_idx.
+hipError_t launch_route(const Shape& s, const int32_t* expert_ids, const uint8_t* mask,
+                        int32_t* expand_idx, int32_t* seg, hipStream_t stream);
+
+// Receive-side prefix sums: seg counts -> segment bases (in place) + the three outputs.
+hipError_t launch_scan(const Shape& s, int32_t* seg, int32_t* ep_recv_count,
+                       int64_t* expert_token_nums, int64_t* recv_offsets, hipStream_t stream);
+
+// Quantize and scatter every routed pick to its packed row, with scales and source triple.
+hipError_t launch_scatter(const Shape& s, const void* x, const int32_t* expert_ids,
+                          const int32_t* expand_idx, const int32_t* seg, const float* smooth,
+                          void* expand_x, float* dynamic_scales, int32_t* assist_info,
+                          bool vectorized, hipStream_t stream);
+
+// Weighted top-K gather.
+hipError_t launch_combine(const Shape& s, const void* expert_out, const int32_t* expert_ids,
+                          const int32_t* expand_idx, const float* expert_scales,
+                          const int32_t* ep_recv_count, const int64_t* recv_offsets,
+                          const uint8_t* mask, const void* ori_x, void* y, bool vectorized,
+                          hipStream_t stream);
+
+}  // namespace moe_dc

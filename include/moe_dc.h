@@ -1,0 +1,174 @@
+/*
+ * moe_dc.h -- MoE Dispatch/Combine for one AMD Instinct MI355X (gfx950), C ABI.
+ *
+ * The library implements the data path of the MoE dispatch and combine operators described
+ * by these pages (cited below by the tags in brackets):
+ *   [DDD] "MoeDistributeDispatch和MoeDistributeCombine算子设计介绍" (gitcode design doc)
+ *   [LLD] "low_latency_dispatch" (hiascend API doc): 计算公式, 约束说明
+ *   [OPS] "CANN ops-transformer 算子解析：MoeDistributeDispatchV3 的 EP 域 Token 分发与动态量化
+ *         通信实现" (mwwr.cn): 功能说明, 参数说明, 约束说明, 调用说明, 接口级量化模式扩展
+ *   [SMP] "CANN MoE Dispatch/Combine 通信算子性能优化实践：Kernel 直调与 ACL SHMEM 实现专家分发
+ *         与聚合" (lqnn.cn): Dispatch 功能介绍, Combine 功能介绍, 通信前量化
+ *
+ * All W logical expert-parallel (EP) ranks live in the HBM of one GPU.  The pages' all-to-all
+ * exchange therefore becomes a device-local permutation: dispatch writes every routed pick
+ * straight to its final row of the receivers' packed buffer, and combine gathers from there.
+ *
+ * Notation: W ranks, E routed experts (L = E / W per rank, rank r owns [r*L, (r+1)*L)),
+ * BS tokens per source rank, H hidden size, K picks per token.  A "pick" is (s, i, k):
+ * source rank s, token i, k-th choice, with expert e = expert_ids[s][i][k].
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor arguments are DEVICE pointers into the memory of the current HIP device;
+ *     arrays are dense, C-contiguous, in the shapes given.  bf16 is the 16-bit brain-float
+ *     bit pattern.  Device pointers should be 16-byte aligned for the vectorised kernels;
+ *     unaligned pointers (or H not a multiple of 8) select slower element-wise kernels.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the legacy default stream).  Every
+ *     call is asynchronous on that stream: it validates on the host, enqueues kernels and
+ *     returns; outputs are valid in stream order.  No call synchronises the host, and no
+ *     call allocates or frees memory: the caller owns every buffer and the stream.
+ *   - A negative status means nothing was enqueued; moe_dc_last_error() then describes the
+ *     problem (thread-local, valid until the next call on the same thread).
+ */
+#ifndef MOE_DC_H
+#define MOE_DC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1,   /* a range, divisibility, pointer or size rule is broken   */
+    MOE_ERR_UNSUPPORTED = -2,   /* allowed by the pages but not built (modes 1/3, const)   */
+    MOE_ERR_WORKSPACE = -3,     /* workspace missing or smaller than the query returned    */
+    MOE_ERR_DEVICE = -4         /* a HIP runtime call failed                               */
+} moe_status;
+
+/* Operator attributes ([OPS] 参数说明; [LLD] 约束说明).  One struct serves both calls; the
+ * pages require the same values on every rank and for dispatch and its combine
+ * ([OPS] 约束说明, cross-card consistency), which one struct gives for free. */
+typedef struct {
+    int32_t ep_world_size;          /* W, in [2, 768]                                        */
+    int32_t moe_expert_num;         /* E, in (0, 1024], E % W == 0; L*W <= 2048               */
+    int32_t bs;                     /* BS tokens per rank, in [1, 512]                        */
+    int32_t hidden;                 /* H, in [1024, 8192]                                     */
+    int32_t topk;                   /* K, in (0, 16], K <= E + zero + copy + const            */
+    int32_t quant_mode;             /* 0 none, 2 int8 per token, 4 MX E4M3, 5 MX clip E4M3;
+                                       1 and 3 -> MOE_ERR_UNSUPPORTED                          */
+    int32_t zero_expert_num;        /* >= 0; ids [E, E+Z) are zero experts                    */
+    int32_t copy_expert_num;        /* >= 0; ids [E+Z, E+Z+C) are copy experts               */
+    int32_t const_expert_num;       /* must be 0 (its parameters are not on the pages)        */
+    int32_t expert_token_nums_type; /* 0 = running sum over local experts, 1 = counts         */
+    int32_t mask_kind;              /* 0 none, 1 per token [W][BS], 2 per pick [W][BS][K]     */
+    int32_t reserved;               /* must be 0                                              */
+    int64_t expand_rows_capacity;   /* rows of expand_x / dynamic_scales / assist_info and of
+                                       expert_out; must be >= W*BS*K                           */
+} moe_dc_config;
+
+/* Host-only check of every rule the pages state for the attributes ([OPS] 约束说明 and the
+ * wrapper's checks under 调用说明; [LLD] 约束说明): the ranges above, E % W == 0,
+ * L*W <= 2048, K <= E+Z+C+const, E+Z+C+const < INT32_MAX, capacity >= W*BS*K and < 2^31.
+ * Returns MOE_OK, MOE_ERR_INVALID_ARG or MOE_ERR_UNSUPPORTED.  Touches no device. */
+moe_status moe_dc_validate(const moe_dc_config* cfg);
+
+/* fp32 scales per expand_x row for cfg->quant_mode: 0 for mode 0, 1 for mode 2, and
+ * Align2(Ceil(H, 32)) for modes 4/5 (the dynamic_scales shape rule of [LLD] 约束说明).
+ * Returns -1 for an invalid config. */
+int32_t moe_dc_scales_per_row(const moe_dc_config* cfg);
+
+/* Workspace bytes moe_dispatch needs for this config (the pages' two-phase pattern:
+ * query the workspace size, then execute; [OPS] 调用说明).  0 for an invalid config.
+ * The workspace is scratch: its contents need no initialisation and are meaningless after
+ * the call; one workspace must not be used by two dispatches that may run concurrently. */
+size_t moe_dc_dispatch_workspace_bytes(const moe_dc_config* cfg);
+
+/* moe_dispatch -- quantize, route and scatter every pick to its receiver's packed rows.
+ *
+ * Defined by: [DDD] §2.2 (index computation: per source rank, a pick's expand_idx is the
+ * count of that rank's earlier picks, in row-major (token, pick) order, that chose the same
+ * expert; the target rank is e / L rounded down and the local expert e % L); [DDD] §2.4
+ * (receive side: the W x L count matrix is transposed and prefix-summed row-major into
+ * ep_recv_count; expert_token_nums is its last column); [OPS] 功能说明 情形 1/2 and
+ * [LLD] 计算公式 (quantization formulas of modes 0, 2, 4, 5); [SMP] Dispatch 功能介绍
+ * (each row carries its source triple, output as assist_info_for_combine).
+ *
+ * Inputs:
+ *   x              bf16  [W][BS][H]   tokens of every source rank
+ *   expert_ids     int32 [W][BS][K]   picks; ids >= E are the special experts
+ *   smooth_scales  fp32  [E][H] or NULL; mode 2 only (the routed expert's row multiplies
+ *                  the token before quantization, so quantization is per pick)
+ *   x_active_mask  uint8 [W][BS] (mask_kind 1) or [W][BS][K] (mask_kind 2), or NULL when
+ *                  mask_kind is 0; nonzero = active.  An inactive pick is not dispatched.
+ * Outputs (row = a receiver row in the packed layout below; cap = expand_rows_capacity):
+ *   expand_x       [cap][H] bf16 (mode 0), int8 (mode 2) or E4M3 bytes (modes 4/5)
+ *   dynamic_scales fp32 [cap] (mode 2: 1/dyn, with dyn = 127/max|x_fp32|) or
+ *                  [cap][Align2(Ceil(H,32))] (modes 4/5: 2^shared_exp per 32-element block,
+ *                  0 in the pad slot); NULL allowed for mode 0
+ *   expand_idx     int32 [W][BS][K]   ordinal of each pick among its source rank's picks of
+ *                  the same expert; -1 for inactive picks and special experts
+ *   assist_info    int32 [cap][3]     (s, i, k) of the pick stored in each row
+ *   ep_recv_count  int32 [W][L*W]     receiver r, entry j*W+s: inclusive running total of
+ *                  the rows r receives, over (local expert j, source s) in that order
+ *   expert_token_nums int64 [W][L]    type 1: rows per local expert; type 0: running sum
+ *   recv_offsets   int64 [W+1]        first row of each receiver; [W] = total routed rows
+ * Packed layout: receiver r owns rows [recv_offsets[r], recv_offsets[r+1]); inside, rows go
+ * by local expert, then source rank, then expand_idx.  So the whole buffer is one stable sort
+ * of the routed picks by (expert, s, i, k).  Rows at or past recv_offsets[W] are not written.
+ * Numerics: every fp32 operation is a single IEEE binary32 operation rounded to nearest
+ * even, in the order of the formulas; int8 codes round half to even and saturate at +-127
+ * (NaN -> 0); E4M3 codes round to nearest even and saturate at +-448; fp32 subnormals are
+ * kept.  The results are deterministic: identical inputs give identical bytes.
+ * Errors: host validation first (MOE_ERR_INVALID_ARG / _UNSUPPORTED / _WORKSPACE); a HIP
+ * launch failure gives MOE_ERR_DEVICE.  Out-of-range expert ids are a contract violation:
+ * the kernels never access memory out of bounds for them and treat such picks as not
+ * dispatched.  A per-token mask needs no particular order (the pages ask for trues before
+ * falses; any order works here). */
+moe_status moe_dispatch(const moe_dc_config* cfg,
+                        const void* x, const int32_t* expert_ids,
+                        const float* smooth_scales, const uint8_t* x_active_mask,
+                        void* expand_x, float* dynamic_scales, int32_t* expand_idx,
+                        int32_t* assist_info, int32_t* ep_recv_count,
+                        int64_t* expert_token_nums, int64_t* recv_offsets,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* moe_combine -- gather each token's K expert outputs and form their weighted sum.
+ *
+ * Defined by: [DDD] §3.4 (a pick's expert output sits at its rank's window + the expert's
+ * offset + expand_idx; the K outputs are weighted and summed back to the token); [SMP]
+ * Combine 功能介绍 (each expert row times its expert scale, accumulated in fp32, then cast
+ * down); [LLD] 计算公式 特殊专家场景 (a zero expert outputs 0, a copy expert outputs ori_x).
+ *
+ * Inputs:
+ *   expert_out     bf16 [cap][H]      expert outputs, row-aligned with dispatch's expand_x
+ *   expert_ids, expand_idx, ep_recv_count, recv_offsets: as produced by moe_dispatch for
+ *                  this config (the addressing uses exactly these)
+ *   expert_scales  fp32 [W][BS][K]    weight of each pick
+ *   x_active_mask  as for moe_dispatch (inactive picks contribute nothing)
+ *   ori_x          bf16 [W][BS][H]    dispatch's x; required iff copy_expert_num > 0
+ * Output:
+ *   y              bf16 [W][BS][H]    y[s][i] = bf16_rne( sum over active picks in k order of
+ *                  w * expert_row ), accumulated in fp32 starting from +0 with one multiply
+ *                  and one add per pick (zero experts add nothing); all-inactive tokens -> +0
+ * Errors: as for moe_dispatch; ori_x NULL with copy experts is MOE_ERR_INVALID_ARG.
+ * Needs no workspace. */
+moe_status moe_combine(const moe_dc_config* cfg,
+                       const void* expert_out, const int32_t* expert_ids,
+                       const int32_t* expand_idx, const float* expert_scales,
+                       const int32_t* ep_recv_count, const int64_t* recv_offsets,
+                       const uint8_t* x_active_mask, const void* ori_x, void* y,
+                       void* stream);
+
+/* Text of the last non-OK status on this thread ("" if none). */
+const char* moe_dc_last_error(void);
+
+/* Library version string. */
+const char* moe_dc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_DC_H */

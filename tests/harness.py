@@ -1,0 +1,101 @@
+"""Test harness: runs the same seeded inputs through the HIP library and the CPU oracle.
+
+The GPU side only ever calls the C ABI through combine_quant_amd's binding; the oracle side
+only ever calls oracle/.  The two meet here, in the comparisons.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+import workloads
+
+
+def oracle_cfg(wl: workloads.Workload, etn_type=None):
+    return oracle.make_cfg(wl.W, wl.E, wl.BS, wl.H, wl.K, quant_mode=wl.quant_mode,
+                           zero_expert_num=wl.zero_expert_num,
+                           copy_expert_num=wl.copy_expert_num,
+                           expert_token_nums_type=wl.expert_token_nums_type if etn_type is None
+                           else etn_type,
+                           mask_kind=wl.mask_kind)
+
+
+def lib_cfg(wl: workloads.Workload, cap=None):
+    import combine_quant_amd as cq
+    return cq.make_config(wl.W, wl.E, wl.BS, wl.H, wl.K, wl.quant_mode,
+                          zero_expert_num=wl.zero_expert_num,
+                          copy_expert_num=wl.copy_expert_num,
+                          expert_token_nums_type=wl.expert_token_nums_type,
+                          mask_kind=wl.mask_kind, cap=cap)
+
+
+def to_dev(a, dtype=None, device="cuda"):
+    import torch
+    if a is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.to(device)
+
+
+def bf16_dev(a_u16, device="cuda"):
+    import torch
+    return to_dev(a_u16, torch.bfloat16, device)
+
+
+def host(t):
+    import torch
+    if t is None:
+        return None
+    t = t.detach()
+    if t.dtype == torch.bfloat16:
+        t = t.view(torch.int16)
+    if t.dtype == torch.float8_e4m3fn:
+        t = t.view(torch.uint8)
+    a = t.cpu().numpy()
+    return a.view(np.uint16) if a.dtype == np.int16 and t.dtype == torch.int16 else a
+
+
+def gpu_dispatch(wl, inp, cfg=None, device="cuda"):
+    import combine_quant_amd as cq
+    cfg = lib_cfg(wl) if cfg is None else cfg
+    x = bf16_dev(inp["x"], device)
+    ids = to_dev(inp["expert_ids"], device=device)
+    sm = to_dev(inp.get("smooth"), device=device)
+    mask = to_dev(inp.get("mask"), device=device)
+    out = cq.dispatch(cfg, x, ids, sm, mask)
+    return cfg, dict(x=x, ids=ids, mask=mask), out
+
+
+def compare_dispatch(wl, inp, out_dev, ref, rows=None):
+    """Bit-exact comparison of every dispatch output (rows: optional subset of rows to
+    compare for the per-row payload; default every routed row)."""
+    o = {k: host(v) for k, v in out_dev.items() if k != "workspace"}
+    np.testing.assert_array_equal(o["expand_idx"], ref["expand_idx"], err_msg="expand_idx")
+    np.testing.assert_array_equal(o["ep_recv_count"], ref["ep_recv_count"],
+                                  err_msg="ep_recv_count")
+    np.testing.assert_array_equal(o["expert_token_nums"], ref["expert_token_nums"],
+                                  err_msg="expert_token_nums")
+    np.testing.assert_array_equal(o["recv_offsets"], ref["recv_offsets"],
+                                  err_msg="recv_offsets")
+    P = int(ref["recv_offsets"][-1])
+    sel = np.arange(P) if rows is None else np.asarray(rows)
+    np.testing.assert_array_equal(o["assist_info"][sel], ref["assist_info"][sel],
+                                  err_msg="assist_info")
+    ex = o["expand_x"][sel]
+    rex = ref["expand_x"][sel]
+    np.testing.assert_array_equal(ex.view(np.uint8), rex.view(np.uint8), err_msg="expand_x")
+    if wl.quant_mode != 0:
+        np.testing.assert_array_equal(o["dynamic_scales"][sel].view(np.uint32),
+                                      ref["dynamic_scales"][sel].view(np.uint32),
+                                      err_msg="dynamic_scales")
+    return o
+
+
+def check_combine_tolerance(y_gpu_u16, y_ref_u16, rtol=1e-2, atol=1e-3):
+    a = workloads.bf16_bits_to_f32(y_gpu_u16).astype(np.float64)
+    b = workloads.bf16_bits_to_f32(y_ref_u16).astype(np.float64)
+    bad = np.abs(a - b) > atol + rtol * np.abs(b)
+    assert not bad.any(), f"{int(bad.sum())} of {bad.size} elements out of tolerance"
+    return int((y_gpu_u16 != y_ref_u16).sum())

@@ -1,0 +1,152 @@
+"""Host-side tests of the C ABI (no GPU needed): the library loads, exports every function
+include/moe_dc.h declares, and its host validation enforces the pages' attribute rules."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import combine_quant_amd as cq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_dc.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert _declared_functions() == sorted(cq.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = cq.load_library()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    # the exported symbols are plain C names (no C++ mangling)
+    raw = ctypes.CDLL(lib._name)
+    for name in _declared_functions():
+        getattr(raw, name)
+
+
+def test_config_struct_layout_matches_header():
+    # twelve int32 fields then one int64
+    assert ctypes.sizeof(cq.MoeDcConfig) == 12 * 4 + 8
+    assert cq.MoeDcConfig.expand_rows_capacity.offset == 48
+
+
+def _cfg(**kw):
+    base = dict(W=16, E=256, BS=512, H=7168, K=8, quant_mode=2)
+    base.update({k: v for k, v in kw.items() if k in base})
+    c = cq.make_config(base["W"], base["E"], base["BS"], base["H"], base["K"],
+                       base["quant_mode"])
+    for k, v in kw.items():
+        if k not in base:
+            setattr(c, k, v)
+    return c
+
+
+def test_valid_configs_of_the_workloads():
+    import workloads
+    for wl in workloads.WORKLOADS.values():
+        c = cq.make_config(wl.W, wl.E, wl.BS, wl.H, wl.K, wl.quant_mode,
+                           zero_expert_num=wl.zero_expert_num,
+                           copy_expert_num=wl.copy_expert_num, mask_kind=wl.mask_kind)
+        assert cq.moe_dc_validate(c) == cq.MOE_OK, (wl.name, cq.moe_dc_last_error())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(W=1), cq.MOE_ERR_INVALID_ARG),
+    (dict(W=769, E=769), cq.MOE_ERR_INVALID_ARG),
+    (dict(E=0), cq.MOE_ERR_INVALID_ARG),
+    (dict(E=1040, W=16), cq.MOE_ERR_INVALID_ARG),
+    (dict(E=250), cq.MOE_ERR_INVALID_ARG),            # not a multiple of W
+    (dict(BS=0), cq.MOE_ERR_INVALID_ARG),
+    (dict(BS=513), cq.MOE_ERR_INVALID_ARG),
+    (dict(H=1023), cq.MOE_ERR_INVALID_ARG),
+    (dict(H=8193), cq.MOE_ERR_INVALID_ARG),
+    (dict(K=0), cq.MOE_ERR_INVALID_ARG),
+    (dict(K=17), cq.MOE_ERR_INVALID_ARG),
+    (dict(W=2, E=2, K=3), cq.MOE_ERR_INVALID_ARG),    # K > number of experts
+    (dict(quant_mode=1), cq.MOE_ERR_UNSUPPORTED),
+    (dict(quant_mode=3), cq.MOE_ERR_UNSUPPORTED),
+    (dict(quant_mode=6), cq.MOE_ERR_INVALID_ARG),
+    (dict(const_expert_num=1), cq.MOE_ERR_UNSUPPORTED),
+    (dict(zero_expert_num=-1), cq.MOE_ERR_INVALID_ARG),
+    (dict(zero_expert_num=2 ** 31 - 100), cq.MOE_ERR_INVALID_ARG),   # id space >= INT32_MAX
+    (dict(expert_token_nums_type=2), cq.MOE_ERR_INVALID_ARG),
+    (dict(mask_kind=3), cq.MOE_ERR_INVALID_ARG),
+    (dict(reserved=1), cq.MOE_ERR_INVALID_ARG),
+    (dict(expand_rows_capacity=16 * 512 * 8 - 1), cq.MOE_ERR_INVALID_ARG),
+    (dict(expand_rows_capacity=2 ** 31), cq.MOE_ERR_INVALID_ARG),
+])
+def test_validation_rules(kw, status):
+    c = _cfg(**kw)
+    assert cq.moe_dc_validate(c) == status
+    assert cq.moe_dc_last_error() != ""
+    assert cq.moe_dc_dispatch_workspace_bytes(c) == 0
+    assert cq.moe_dc_scales_per_row(c) == -1
+
+
+def test_k_may_count_special_experts():
+    c = _cfg(W=2, E=2, K=4, zero_expert_num=1, copy_expert_num=1)
+    assert cq.moe_dc_validate(c) == cq.MOE_OK
+
+
+def test_scales_per_row_and_workspace():
+    assert cq.moe_dc_scales_per_row(_cfg(quant_mode=0)) == 0
+    assert cq.moe_dc_scales_per_row(_cfg(quant_mode=2)) == 1
+    assert cq.moe_dc_scales_per_row(_cfg(quant_mode=4)) == 224        # 7168/32, even
+    assert cq.moe_dc_scales_per_row(_cfg(quant_mode=5, H=1056)) == 34  # 33 blocks -> 34
+    assert cq.moe_dc_scales_per_row(_cfg(quant_mode=4, H=1030)) == 34  # ceil(1030/32)=33
+    ws = cq.moe_dc_dispatch_workspace_bytes(_cfg())
+    assert ws >= 256 * 16 * 4 and ws % 256 == 0
+
+
+def test_dispatch_rejects_bad_arguments_before_any_device_work():
+    """Argument errors return a status without touching the device (null pointers)."""
+    lib = cq.load_library()
+    c = _cfg()
+    rc = lib.moe_dispatch(ctypes.byref(c), *([None] * 11), None, ctypes.c_size_t(0), None)
+    assert rc == cq.MOE_ERR_INVALID_ARG
+    assert "NULL" in cq.moe_dc_last_error()
+    rc = lib.moe_combine(ctypes.byref(c), *([None] * 9), None)
+    assert rc == cq.MOE_ERR_INVALID_ARG
+    bad = _cfg(quant_mode=3)
+    rc = lib.moe_dispatch(ctypes.byref(bad), *([None] * 11), None, ctypes.c_size_t(0), None)
+    assert rc == cq.MOE_ERR_UNSUPPORTED
+
+
+def test_dispatch_workspace_and_mask_rules_on_host():
+    """With non-null dummy pointers the remaining host rules still fire before any launch."""
+    lib = cq.load_library()
+    p = ctypes.c_void_p(0x1000)
+    c = _cfg()
+    args = [p] * 11
+    # smooth scales with a mode that forbids them
+    c4 = _cfg(quant_mode=4)
+    rc = lib.moe_dispatch(ctypes.byref(c4), p, p, p, None, p, p, p, p, p, p, p, p,
+                          ctypes.c_size_t(1 << 20), None)
+    assert rc == cq.MOE_ERR_INVALID_ARG and "smooth" in cq.moe_dc_last_error()
+    # mask pointer without a mask kind
+    rc = lib.moe_dispatch(ctypes.byref(c), *args, p, ctypes.c_size_t(1 << 20), None)
+    assert rc == cq.MOE_ERR_INVALID_ARG and "mask" in cq.moe_dc_last_error()
+    # workspace too small
+    args_nomask = [p, p, None, None] + [p] * 7
+    rc = lib.moe_dispatch(ctypes.byref(c), *args_nomask, p, ctypes.c_size_t(8), None)
+    assert rc == cq.MOE_ERR_WORKSPACE
+    # combine: copy experts without ori_x
+    cc = _cfg(copy_expert_num=1)
+    rc = lib.moe_combine(ctypes.byref(cc), p, p, p, p, p, p, None, None, p, None)
+    assert rc == cq.MOE_ERR_INVALID_ARG and "ori_x" in cq.moe_dc_last_error()
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    c = _cfg(W=2, E=8, BS=16, H=1024, K=2)
+    x = torch.zeros((2, 16, 1024), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        cq.moe_dispatch(c, x, None, None, None, None, None, None, None, None, None, None, None)

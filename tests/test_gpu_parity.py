@@ -1,0 +1,243 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle, same seeded inputs.
+
+Dispatch outputs must match bit for bit (counts, indices, offsets, rows, codes, scales);
+combine must be within 1e-2 relative / 1e-3 absolute per bf16 element of the oracle (and
+is observed to be bit-identical, which a separate test records).
+"""
+import numpy as np
+import pytest
+
+import harness
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+W2 = workloads.C1_MODE0
+
+# small cases the oracle finishes in well under a second, covering several workgroups,
+# ragged tails (BS not a multiple of 32-token words, H not a multiple of 256 / 32 / 8),
+# masks, special experts and duplicate picks
+SMALL = {
+    "c1_mode0": workloads.C1_MODE0,
+    "c1_mode2": workloads.C1_MODE2,
+    "c1_mode4": workloads.C1_MODE0.replace(name="c1_mode4", quant_mode=4),
+    "c1_mode5": workloads.C1_MODE0.replace(name="c1_mode5", quant_mode=5),
+    "smooth_ragged": workloads.Workload("smooth_ragged", W=4, E=32, BS=100, H=1056, K=6,
+                                        quant_mode=2, smooth=True, outlier_prob=0.02,
+                                        expert_token_nums_type=0),
+    "mx_ragged_blocks": workloads.Workload("mx_ragged_blocks", W=3, E=12, BS=77, H=1032, K=5,
+                                           quant_mode=4, routing="zipf"),
+    "mxclip_masked_special": workloads.Workload(
+        "mxclip_masked_special", W=4, E=64, BS=70, H=2048, K=16, quant_mode=5,
+        zero_expert_num=2, copy_expert_num=2, mask_kind=2, inactive_tokens_per_rank=7),
+    "dup_picks_mask1d": workloads.Workload("dup_picks_mask1d", W=2, E=4, BS=65, H=1024, K=6,
+                                           quant_mode=2, routing="randint", zero_expert_num=1,
+                                           copy_expert_num=1, mask_kind=1,
+                                           inactive_tokens_per_rank=9),
+    "dup_picks_k16": workloads.Workload("dup_picks_k16", W=4, E=16, BS=140, H=1024, K=16,
+                                        quant_mode=4, routing="randint"),
+    "scalar_path_h1030": workloads.Workload("scalar_path_h1030", W=2, E=8, BS=33, H=1030, K=3,
+                                            quant_mode=5),
+    "scalar_path_mode2_h1030": workloads.Workload("scalar_path_mode2_h1030", W=2, E=8, BS=9,
+                                                  H=1030, K=3, quant_mode=2, smooth=True),
+    "scalar_path_mode0_h1030": workloads.Workload("scalar_path_mode0_h1030", W=3, E=9, BS=9,
+                                                  H=1030, K=2, quant_mode=0, copy_expert_num=1),
+    "l1_w8_k8": workloads.Workload("l1_w8_k8", W=8, E=8, BS=40, H=1024, K=8, quant_mode=4),
+    "bs1_h8192": workloads.Workload("bs1_h8192", W=2, E=2, BS=1, H=8192, K=2, quant_mode=2),
+    "w768_e768": workloads.Workload("w768_e768", W=768, E=768, BS=1, H=1024, K=2,
+                                    quant_mode=2),
+}
+
+
+def _oracle_dispatch(wl, inp, etn_type=None):
+    cfg = harness.oracle_cfg(wl, etn_type)
+    return cfg, oracle.dispatch(cfg, inp["x"], inp["expert_ids"], smooth=inp.get("smooth"),
+                                mask=inp.get("mask"))
+
+
+def _roundtrip(wl, seed=0):
+    import torch
+    inp = workloads.generate(wl, seed=seed)
+    ocfg, ref = _oracle_dispatch(wl, inp)
+    cfg, dev_in, out = harness.gpu_dispatch(wl, inp)
+    torch.cuda.synchronize()
+    harness.compare_dispatch(wl, inp, out, ref)
+    # combine on random expert outputs, one per packed row
+    rng = np.random.default_rng(seed + 77)
+    eo = workloads.f32_to_bf16_bits(rng.standard_normal((wl.cap, wl.H), dtype=np.float32))
+    y_ref = oracle.combine(ocfg, eo, inp["expert_ids"], ref["expand_idx"],
+                           inp["expert_scales"], ref["ep_recv_count"], ref["recv_offsets"],
+                           mask=inp.get("mask"), ori_x=inp["x"])
+    import combine_quant_amd as cq
+    y = cq.combine(cfg, harness.bf16_dev(eo), dev_in["ids"], out["expand_idx"],
+                   harness.to_dev(inp["expert_scales"]), out["ep_recv_count"],
+                   out["recv_offsets"], dev_in["mask"], dev_in["x"])
+    torch.cuda.synchronize()
+    y_gpu = harness.host(y)
+    ndiff = harness.check_combine_tolerance(y_gpu, y_ref)
+    return ndiff
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_roundtrip(name):
+    ndiff = _roundtrip(SMALL[name])
+    assert ndiff == 0, f"{ndiff} bf16 elements differ from the oracle (within tolerance)"
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3, 4])
+def test_c1_seeds(seed):
+    for wl in (workloads.C1_MODE0, workloads.C1_MODE2):
+        assert _roundtrip(wl, seed) == 0
+
+
+def test_c2_full_both_etn_types():
+    """W=8, BS=128, H=7168, K=8 with smooth scales and outliers: every output compared."""
+    import torch
+    import combine_quant_amd as cq
+    wl = workloads.C2
+    inp = workloads.generate(wl, seed=0)
+    for etn in (0, 1):
+        w = wl.replace(expert_token_nums_type=etn)
+        ocfg, ref = _oracle_dispatch(w, inp)
+        cfg, dev_in, out = harness.gpu_dispatch(w, inp)
+        torch.cuda.synchronize()
+        harness.compare_dispatch(w, inp, out, ref)
+    # identity-dequant FFN round trip: expert_out = bf16(q * scale) on both sides
+    P = int(ref["recv_offsets"][-1])
+    deq = ref["expand_x"].astype(np.float32) * ref["dynamic_scales"][:, None]
+    eo_ref = workloads.f32_to_bf16_bits(deq)
+    y_ref = oracle.combine(ocfg, eo_ref, inp["expert_ids"], ref["expand_idx"],
+                           inp["expert_scales"], ref["ep_recv_count"], ref["recv_offsets"])
+    eo = (out["expand_x"].float() * out["dynamic_scales"][:, None]).to(torch.bfloat16)
+    y = cq.combine(cfg, eo, dev_in["ids"], out["expand_idx"],
+                   harness.to_dev(inp["expert_scales"]), out["ep_recv_count"],
+                   out["recv_offsets"])
+    torch.cuda.synchronize()
+    assert P == wl.cap
+    assert harness.check_combine_tolerance(harness.host(y), y_ref) == 0
+
+
+def test_determinism_repeat():
+    import torch
+    wl = SMALL["mxclip_masked_special"]
+    inp = workloads.generate(wl, seed=5)
+    _, _, a = harness.gpu_dispatch(wl, inp)
+    _, _, b = harness.gpu_dispatch(wl, inp)
+    torch.cuda.synchronize()
+    for k in a:
+        if k == "workspace" or a[k] is None:
+            continue
+        P = int(a["recv_offsets"][-1].item())
+        ta, tb = (a[k][:P], b[k][:P]) if k in ("expand_x", "dynamic_scales",
+                                               "assist_info") else (a[k], b[k])
+        assert torch.equal(ta, tb), k
+
+
+def test_all_tokens_inactive():
+    import torch
+    import combine_quant_amd as cq
+    wl = workloads.Workload("all_off", W=2, E=8, BS=16, H=1024, K=2, quant_mode=2, mask_kind=2,
+                            inactive_tokens_per_rank=16, copy_expert_num=1)
+    inp = workloads.generate(wl, seed=0)
+    assert inp["mask"].sum() == 0
+    cfg, dev_in, out = harness.gpu_dispatch(wl, inp)
+    y = cq.combine(cfg, torch.zeros((wl.cap, wl.H), dtype=torch.bfloat16, device="cuda"),
+                   dev_in["ids"], out["expand_idx"], harness.to_dev(inp["expert_scales"]),
+                   out["ep_recv_count"], out["recv_offsets"], dev_in["mask"], dev_in["x"])
+    torch.cuda.synchronize()
+    assert (harness.host(out["expand_idx"]) == -1).all()
+    assert (harness.host(out["ep_recv_count"]) == 0).all()
+    assert (harness.host(out["recv_offsets"]) == 0).all()
+    assert (harness.host(y) == 0).all()
+
+
+def test_unaligned_pointers_take_the_scalar_path():
+    """x offset by one element: the library must fall back to element-wise kernels and
+    still match the oracle."""
+    import torch
+    import combine_quant_amd as cq
+    wl = workloads.C1_MODE2.replace(quant_mode=4)
+    inp = workloads.generate(wl, seed=3)
+    _, ref = _oracle_dispatch(wl, inp)
+    cfg = harness.lib_cfg(wl)
+    xbuf = torch.empty(inp["x"].size + 1, dtype=torch.bfloat16, device="cuda")
+    xbuf[1:] = harness.bf16_dev(inp["x"].ravel())
+    x = xbuf[1:].view(wl.W, wl.BS, wl.H)
+    assert x.data_ptr() % 16 != 0
+    out = cq.dispatch(cfg, x, harness.to_dev(inp["expert_ids"]))
+    torch.cuda.synchronize()
+    harness.compare_dispatch(wl, inp, out, ref)
+
+
+def test_exhaustive_int8_scale_via_rows():
+    """Every positive finite bf16 value as a token's absolute maximum (one token each):
+    dyn = 127/amax and scale = 1/dyn must round exactly like the oracle's."""
+    import torch
+    import combine_quant_amd as cq
+    amax_bits = np.arange(1, 0x7F80, dtype=np.uint16)
+    T = len(amax_bits)
+    W = 2
+    BS = 512
+    n_tok = W * BS
+    H = 1024
+    for lo in range(0, T, n_tok):
+        chunk = amax_bits[lo:lo + n_tok]
+        x = np.zeros((n_tok, H), np.uint16)
+        x[:len(chunk), 0] = chunk
+        x[:len(chunk), 1] = chunk | 0x8000          # a negative copy at the same magnitude
+        x[:len(chunk), 2] = np.where(chunk > 0x0100, chunk - 0x0100, 0)  # smaller values
+        x = x.reshape(W, BS, H)
+        ids = np.zeros((W, BS, 1), np.int32)
+        wl = workloads.Workload("amax_sweep", W=W, E=2, BS=BS, H=H, K=1, quant_mode=2)
+        inp = dict(x=x, expert_ids=ids)
+        _, ref = _oracle_dispatch(wl, inp)
+        cfg = harness.lib_cfg(wl)
+        out = cq.dispatch(cfg, harness.bf16_dev(x), harness.to_dev(ids))
+        torch.cuda.synchronize()
+        harness.compare_dispatch(wl, inp, out, ref)
+
+
+def test_exhaustive_e4m3_via_rows():
+    """All 65,536 bf16 patterns except NaN/inf, as MX elements under both MX modes, against
+    the oracle; blocks mix magnitudes so many shared exponents are exercised."""
+    import torch
+    import combine_quant_amd as cq
+    b = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    f = workloads.bf16_bits_to_f32(b)
+    b = b[np.isfinite(f)]
+    rng = np.random.default_rng(0)
+    b = rng.permutation(b)
+    H = 1024
+    n_tok = (len(b) + H - 1) // H
+    pad = np.zeros(n_tok * H - len(b), np.uint16)
+    x = np.concatenate([b, pad]).reshape(1, n_tok, H)
+    x = np.concatenate([x, x[:, ::-1]], axis=0)      # W=2
+    for mode in (4, 5):
+        wl = workloads.Workload("e4m3_sweep", W=2, E=2, BS=n_tok, H=H, K=1, quant_mode=mode)
+        ids = np.zeros((2, n_tok, 1), np.int32)
+        inp = dict(x=np.ascontiguousarray(x), expert_ids=ids)
+        _, ref = _oracle_dispatch(wl, inp)
+        out = cq.dispatch(harness.lib_cfg(wl), harness.bf16_dev(inp["x"]), harness.to_dev(ids))
+        torch.cuda.synchronize()
+        harness.compare_dispatch(wl, inp, out, ref)
+
+
+def test_invalid_arguments_raise_and_enqueue_nothing():
+    import torch
+    import combine_quant_amd as cq
+    wl = workloads.C1_MODE2
+    inp = workloads.generate(wl, seed=0)
+    cfg = harness.lib_cfg(wl)
+    x = harness.bf16_dev(inp["x"])
+    ids = harness.to_dev(inp["expert_ids"])
+    o = cq.alloc_dispatch_outputs(cfg)
+    o["expand_idx"].fill_(123)
+    small_ws = o["workspace"][:8]
+    with pytest.raises(cq.MoeDcError) as ei:
+        cq.moe_dispatch(cfg, x, ids, None, None, o["expand_x"], o["dynamic_scales"],
+                        o["expand_idx"], o["assist_info"], o["ep_recv_count"],
+                        o["expert_token_nums"], o["recv_offsets"], small_ws)
+    assert ei.value.status == cq.MOE_ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert (o["expand_idx"] == 123).all()
