@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE dispatch+combine hot path on one MI355X.
+
+One step = one moe_dispatch (routing ordinals, receive-count scan, quantize+scatter) followed
+by one moe_combine (top-K weighted gather) over the whole workload, with every input already
+resident in HBM.  The expert FFN between them is not part of the path: combine reads a
+pre-built bf16 expert-output buffer, one row per received row.
+
+Prints ONE JSON line.  `value` is whole-job tokens/s: W*BS source tokens per step divided
+by the measured time per step.  The `roofline` object is for the dominant kernel (the
+combine gather) with its algorithmic bytes per launch divided by its average duration from
+HIP events recorded on the launch stream; `traffic` is the measured HBM bytes per launch from
+the committed rocprofv3 counter summary when it still matches the kernel source.  The
+`cpu_baseline` object times the CPU oracle (single-threaded C) on the same inputs.
+
+Modes (`--mode`): bench (default), copy-calib (a plain device copy of known size, for
+scaling the HBM byte counters).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD's published peak
+METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (H=7168, K=8, 256 experts)"
+DEFAULT_WORKLOAD = "c4_w16_int8_roundtrip"
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "combine_kernel_c4_hbm_traffic.md")
+COMBINE_SOURCES = [os.path.join(ROOT, "combine_quant_amd", "csrc", f)
+                   for f in ("combine.hip", "dc_device.h")]
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--sets", type=int, default=2,
+                    help="input/output buffer sets rotated across steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-passes", type=int, default=3)
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy-calib"])
+    return ap.parse_args()
+
+
+# -- algorithmic bytes (what the method must move; no staging) -----------------------------
+
+def algorithmic_bytes(wl, inp, routed_rows, copy_picks, active_tokens):
+    """Bytes dispatch and combine must move for this input (see the design notes).
+
+    dispatch: read x of every token with a routed pick, ids (and mask, smooth table once),
+    write each routed row's codes + scales + source triple, expand_idx, ep_recv_count,
+    expert_token_nums, recv_offsets.
+    combine: read each routed expert-output row once, ids + expand_idx + weights, the
+    receive counts (and mask, and ori_x for copy picks), write y."""
+    W, E, H, K, T = wl.W, wl.E, wl.H, wl.K, wl.T
+    b = 2 if wl.quant_mode == 0 else 1
+    S = {0: 0, 2: 4}.get(wl.quant_mode, 4 * mx_scales_per_row(H))
+    m = 0 if inp.get("mask") is None else inp["mask"].nbytes
+    smooth = 0 if inp.get("smooth") is None else inp["smooth"].nbytes
+    P = routed_rows
+    dispatch = (2 * H * active_tokens + 4 * T * K + m + smooth + P * (b * H + S + 12)
+                + 4 * T * K + 4 * E * W + 8 * E + 8 * (W + 1))
+    combine = 2 * H * P + 12 * T * K + 4 * E * W + 8 * (W + 1) + m + 2 * H * copy_picks + 2 * H * T
+    return dispatch, combine
+
+
+def mx_scales_per_row(H):
+    nb = (H + 31) // 32
+    return nb + (nb & 1)
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic():
+    """HBM bytes per combine launch from the committed counter summary, or None when the
+    summary is missing or was taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    text = open(TRAFFIC_SUMMARY).read()
+    mh = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    mb = re.search(r"hbm_bytes_per_launch:\s*([0-9]+)", text)
+    if not mh or not mb or mh.group(1) != source_hash(COMBINE_SOURCES):
+        return None
+    return int(mb.group(1))
+
+
+# -- CPU baseline: the oracle, as it stands ---------------------------------------------
+
+def cpu_baseline(wl, inp, expert_out_host, passes):
+    import oracle
+    cfg = oracle.make_cfg(wl.W, wl.E, wl.BS, wl.H, wl.K, quant_mode=wl.quant_mode,
+                          zero_expert_num=wl.zero_expert_num,
+                          copy_expert_num=wl.copy_expert_num,
+                          expert_token_nums_type=wl.expert_token_nums_type,
+                          mask_kind=wl.mask_kind)
+    cpus = sorted(os.sched_getaffinity(0))
+    os.sched_setaffinity(0, {cpus[0]})          # the oracle is single-threaded; pin it
+    times = []
+    try:
+        for _ in range(passes):
+            t0 = time.perf_counter()
+            d = oracle.dispatch(cfg, inp["x"], inp["expert_ids"], smooth=inp.get("smooth"),
+                                mask=inp.get("mask"))
+            oracle.combine(cfg, expert_out_host, inp["expert_ids"], d["expand_idx"],
+                           inp["expert_scales"], d["ep_recv_count"], d["recv_offsets"],
+                           mask=inp.get("mask"), ori_x=inp["x"])
+            times.append(time.perf_counter() - t0)
+            del d
+    finally:
+        os.sched_setaffinity(0, set(cpus))
+    t = statistics.median(times)
+    return {"value": round(wl.T / t, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"the whole {wl.name} workload ({wl.T} source tokens, dispatch+combine), "
+                      f"{passes} passes, median {t:.2f} s; one core of {len(cpus)} available",
+            "seconds_per_pass": [round(x, 3) for x in times]}
+
+
+# -- modes --------------------------------------------------------------------------------
+
+def run_copy_calib(args):
+    """A plain device-to-device copy of known size (1 GiB), for scaling HBM counters."""
+    import torch
+    n = 1 << 30
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(max(1, args.steps)):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"mode": "copy-calib", "bytes_read_per_launch": n,
+                      "bytes_written_per_launch": n, "launches": max(1, args.steps)}))
+
+
+def run_bench(args):
+    import torch
+    import combine_quant_amd as cq
+
+    wl = workloads.WORKLOADS[args.workload]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {wl.name}", file=sys.stderr, flush=True)
+    inp = workloads.generate(wl, seed=args.seed)
+    cfg = cq.make_config(wl.W, wl.E, wl.BS, wl.H, wl.K, wl.quant_mode,
+                         zero_expert_num=wl.zero_expert_num, copy_expert_num=wl.copy_expert_num,
+                         expert_token_nums_type=wl.expert_token_nums_type,
+                         mask_kind=wl.mask_kind)
+
+    def dev_t(a, dtype=None):
+        if a is None:
+            return None
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(dtype) if dtype is not None else t).to(dev)
+
+    ids = dev_t(inp["expert_ids"])
+    mask = dev_t(inp.get("mask"))
+    smooth = dev_t(inp.get("smooth"))
+    w = dev_t(inp["expert_scales"])
+    sets = []
+    for k in range(args.sets):
+        x = dev_t(inp["x"], torch.bfloat16) if k == 0 else sets[0]["x"].clone()
+        eo = workloads.expert_out_torch(wl, wl.cap, seed=args.seed, device=dev)
+        sets.append(dict(x=x, eo=eo, out=cq.alloc_dispatch_outputs(cfg, dev),
+                         y=torch.empty((wl.W, wl.BS, wl.H), dtype=torch.bfloat16, device=dev)))
+    stream = torch.cuda.current_stream(dev)
+
+    def step(n):
+        st = sets[n % len(sets)]
+        o = st["out"]
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+              torch.cuda.Event(enable_timing=True))
+        ev[0].record(stream)
+        cq.moe_dispatch(cfg, st["x"], ids, smooth, mask, o["expand_x"], o["dynamic_scales"],
+                        o["expand_idx"], o["assist_info"], o["ep_recv_count"],
+                        o["expert_token_nums"], o["recv_offsets"], o["workspace"], stream)
+        ev[1].record(stream)
+        cq.moe_combine(cfg, st["eo"], ids, o["expand_idx"], w, o["ep_recv_count"],
+                       o["recv_offsets"], mask, st["x"], st["y"], stream)
+        ev[2].record(stream)
+        return ev
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for n in range(args.warmup):
+        step(n)
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    evs = [step(n) for n in range(args.steps)]
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    disp_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    comb_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    ms_per_step = total_ms / args.steps
+
+    # routed rows etc. of this input, read back from the library's own outputs
+    o = sets[0]["out"]
+    P = int(o["recv_offsets"][-1].item())
+    ids_np = inp["expert_ids"]
+    act = np.ones(ids_np.shape, bool) if inp.get("mask") is None else (
+        inp["mask"].astype(bool) if inp["mask"].ndim == 3 else
+        np.repeat(inp["mask"].astype(bool)[:, :, None], wl.K, axis=2))
+    copy_picks = int(((ids_np >= wl.E + wl.zero_expert_num) &
+                      (ids_np < wl.n_ids) & act).sum())
+    active_tokens = int(((o["expand_idx"] >= 0).any(dim=2)).sum().item())
+    d_bytes, c_bytes = algorithmic_bytes(wl, inp, P, copy_picks, active_tokens)
+    d_avg = statistics.mean(disp_ms)
+    c_avg = statistics.mean(comb_ms)
+    comb_gbps = c_bytes / (c_avg * 1e-3) / 1e9
+    disp_gbps = d_bytes / (d_avg * 1e-3) / 1e9
+    total_gbps = (d_bytes + c_bytes) / (ms_per_step * 1e-3) / 1e9
+    tokens_per_s = wl.T / (ms_per_step * 1e-3)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print(f"[bench] cpu baseline ({args.cpu_passes} oracle passes)", file=sys.stderr,
+              flush=True)
+        eo_host = sets[0]["eo"].view(torch.int16).cpu().numpy().view(np.uint16)
+        cpu = cpu_baseline(wl, inp, eo_host, args.cpu_passes)
+
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "W": wl.W, "E": wl.E, "BS_per_rank": wl.BS,
+                   "H": wl.H, "K": wl.K, "quant_mode": wl.quant_mode,
+                   "routing": wl.routing, "tokens_per_step": wl.T, "routed_rows": P,
+                   "description": wl.description},
+        "hbm_gbps": round(total_gbps, 1),
+        "hbm_frac": round(total_gbps / HBM_PEAK_GBPS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(comb_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(comb_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": committed_traffic(), "kernel": "combine_kernel",
+                     "algorithmic_bytes_per_launch": c_bytes,
+                     "avg_launch_us": round(c_avg * 1e3, 2)},
+        "dispatch": {"avg_us": round(d_avg * 1e3, 2), "algorithmic_bytes": d_bytes,
+                     "gbps": round(disp_gbps, 1), "frac": round(disp_gbps / HBM_PEAK_GBPS, 4)},
+        "combine": {"avg_us": round(c_avg * 1e3, 2), "algorithmic_bytes": c_bytes,
+                    "gbps": round(comb_gbps, 1)},
+        "wall_s_timed": round(wall, 4),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not "
+              "supported (how the path would shard across GPUs is described in the design "
+              "notes)", file=sys.stderr)
+        sys.exit(2)
+    if args.mode == "copy-calib":
+        run_copy_calib(args)
+    else:
+        run_bench(args)
+
+
+if __name__ == "__main__":
+    main()
