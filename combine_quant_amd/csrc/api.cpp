@@ -2,7 +2,7 @@
 //
 // Nothing here allocates device memory or synchronises the host; every launch goes to the
 // caller's stream in order (route -> scan -> scatter for dispatch, one kernel for combine).
-#include "../../include/moe_dc.h"
+#include "moe_dc.h"
 #include "dc_internal.h"
 
 #include <hip/hip_runtime_api.h>

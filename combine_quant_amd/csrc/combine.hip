@@ -11,6 +11,12 @@
 // loads first (all in flight together) and only then accumulates in pick order, one fp32
 // multiply and one fp32 add per pick (the sample article's combine: weight each expert row,
 // accumulate in fp32, cast down), and stores the bf16 rounding of the sum.
+//
+// Vectorized path (H % 8 == 0, 16-byte aligned): a token's row is cut into chunks of 128
+// 16-byte vectors, each handled by one independent wavefront, which resolves the token's
+// sources in lanes 0..K-1 and broadcasts them as wave-uniform values; expert rows are read
+// and y is written with the non-temporal policy; no workgroup barrier.  Element-wise
+// fallback: one workgroup per token.
 #include "dc_device.h"
 #include "dc_internal.h"
 
@@ -129,6 +135,125 @@ __global__ __launch_bounds__(kMaxThreads) void combine_kernel(
     }
 }
 
+
+constexpr int kWavesPerBlock = 4;
+constexpr int kSlotsPerTask = 2;   // 64-vector slots of one token per wave task
+
+// One wave task = one token x kSlotsPerTask slots of 64 16-byte vectors.  A token's row is
+// split across several independent waves (each resolves the token's K sources itself), so a
+// launch is many short tasks: the hardware keeps every SIMD busy to the end instead of
+// leaving a long, thinly occupied last round of whole-token waves.
+template <int KMAX, int SLOTS>
+__global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_wave_kernel(
+    const uint16_t* __restrict__ expert_out, const int32_t* __restrict__ ids,
+    const int32_t* __restrict__ expand_idx, const float* __restrict__ weights,
+    const int32_t* __restrict__ ep_recv_count, const int64_t* __restrict__ recv_offsets,
+    const uint8_t* __restrict__ mask, int mask_kind, const uint16_t* __restrict__ ori_x,
+    uint16_t* __restrict__ y, int W, int E, int L, int BS, int H, int K, int zero_end,
+    int id_end, long long cap, long long T, int tasks_per_token)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const long long task = (long long)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
+    const long long tok = task / tasks_per_token;
+    if (tok >= T) return;                                  // whole wave
+    const int slot0 = (int)(task - tok * tasks_per_token) * SLOTS;
+    const int s = (int)(tok / BS);
+    const int NV = H >> 3;
+
+    int src = -1;            // >= 0: expert_out row; -2: copy expert (ori_x); -1: nothing
+    float wk = 0.0f;
+    if (lane < K) {
+        const long long p = tok * K + lane;
+        const int32_t e = ids[p];
+        const bool on = mask_kind == 0 || (mask_kind == 1 ? mask[tok] != 0 : mask[p] != 0);
+        wk = weights[p];
+        if (on && e >= 0) {
+            if (e < E) {
+                const int32_t ord = expand_idx[p];
+                if (ord >= 0) {
+                    const int r = e / L;
+                    const int j = e - r * L;
+                    const long long flat = (long long)j * W + s;
+                    const long long base =
+                        flat == 0 ? 0 : (long long)ep_recv_count[(long long)r * L * W + flat - 1];
+                    const long long row = (long long)recv_offsets[r] + base + ord;
+                    if (row >= 0 && row < cap) src = (int)row;
+                }
+            } else if (e >= zero_end && e < id_end) {
+                src = -2;
+            }
+        }
+    }
+    int srcs[KMAX];
+    float ws[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        srcs[k] = k < K ? lane_value(src, k) : -1;
+        ws[k] = lane_value(wk, k);
+    }
+
+    const uint4* eo = reinterpret_cast<const uint4*>(expert_out);
+    const uint4* self = ori_x ? reinterpret_cast<const uint4*>(ori_x) + tok * NV : nullptr;
+    uint4* yr = reinterpret_cast<uint4*>(y) + tok * NV;
+    uint4 buf[SLOTS][KMAX];
+#pragma unroll
+    for (int n = 0; n < SLOTS; ++n) {
+        const int v = lane + (slot0 + n) * kWave;
+        if (v < NV) {
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) {
+                if (srcs[k] >= 0) buf[n][k] = load_stream(eo + (long long)srcs[k] * NV + v);
+                else if (srcs[k] == -2) buf[n][k] = self[v];
+            }
+        }
+    }
+#pragma unroll
+    for (int n = 0; n < SLOTS; ++n) {
+        const int v = lane + (slot0 + n) * kWave;
+        if (v < NV) {
+            float acc[8];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k)
+                if (srcs[k] != -1) Cio<8>::accumulate(buf[n][k], ws[k], acc);
+            store_stream(yr + v,
+                         make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                                    pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])));
+        }
+    }
+}
+
+template <int KMAX>
+hipError_t launch_wave_k(const Shape& sh, const void* expert_out, const int32_t* ids,
+                         const int32_t* expand_idx, const float* w, const int32_t* erc,
+                         const int64_t* roff, const uint8_t* mask, const void* ori_x, void* y,
+                         hipStream_t stream)
+{
+    const long long T = (long long)sh.W * sh.BS;
+    const int slots = ((sh.H >> 3) + kWave - 1) / kWave;
+    const int tasks_per_token = (slots + kSlotsPerTask - 1) / kSlotsPerTask;
+    const long long tasks = T * tasks_per_token;
+    const unsigned blocks = (unsigned)((tasks + kWavesPerBlock - 1) / kWavesPerBlock);
+    hipLaunchKernelGGL((combine_wave_kernel<KMAX, kSlotsPerTask>), dim3(blocks),
+                       dim3(kWave * kWavesPerBlock), 0, stream,
+                       static_cast<const uint16_t*>(expert_out), ids, expand_idx, w, erc, roff,
+                       mask, sh.mask_kind, static_cast<const uint16_t*>(ori_x),
+                       static_cast<uint16_t*>(y), sh.W, sh.E, sh.L, sh.BS, sh.H, sh.K,
+                       sh.zero_end, sh.id_end, (long long)sh.cap, T, tasks_per_token);
+    return hipGetLastError();
+}
+
+hipError_t launch_wave(const Shape& sh, const void* eo, const int32_t* ids, const int32_t* ei,
+                       const float* w, const int32_t* erc, const int64_t* roff,
+                       const uint8_t* mask, const void* ori_x, void* y, hipStream_t stream)
+{
+    if (sh.K <= 2) return launch_wave_k<2>(sh, eo, ids, ei, w, erc, roff, mask, ori_x, y, stream);
+    if (sh.K <= 4) return launch_wave_k<4>(sh, eo, ids, ei, w, erc, roff, mask, ori_x, y, stream);
+    if (sh.K <= 8) return launch_wave_k<8>(sh, eo, ids, ei, w, erc, roff, mask, ori_x, y, stream);
+    return launch_wave_k<16>(sh, eo, ids, ei, w, erc, roff, mask, ori_x, y, stream);
+}
+
 template <int VEC, int KMAX>
 hipError_t launch_k(const Shape& sh, const void* expert_out, const int32_t* ids,
                     const int32_t* expand_idx, const float* w, const int32_t* erc,
@@ -169,8 +294,8 @@ hipError_t launch_combine(const Shape& sh, const void* expert_out, const int32_t
                           hipStream_t stream)
 {
     if (vectorized)
-        return launch_vec<8>(sh, expert_out, expert_ids, expand_idx, expert_scales,
-                             ep_recv_count, recv_offsets, mask, ori_x, y, stream);
+        return launch_wave(sh, expert_out, expert_ids, expand_idx, expert_scales, ep_recv_count,
+                           recv_offsets, mask, ori_x, y, stream);
     return launch_vec<1>(sh, expert_out, expert_ids, expand_idx, expert_scales, ep_recv_count,
                          recv_offsets, mask, ori_x, y, stream);
 }

@@ -50,6 +50,41 @@ __device__ __forceinline__ uint32_t e4m3_code(float v)
     return sign | ((((r >> 23) - 120u) << 3) | ((r >> 20) & 7u));
 }
 
+// Streaming (non-temporal) 16- and 8-byte global accesses, for rows that are touched once.
+// They lower to global loads/stores with the non-temporal cache policy, which keeps the
+// once-read / once-written rows from displacing reusable lines in L2 and the Infinity Cache.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 load_stream(const uint4* p)
+{
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void store_stream(uint4* p, uint4 o)
+{
+    const u32x4_t v = {o.x, o.y, o.z, o.w};
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
+}
+
+__device__ __forceinline__ void store_stream(uint2* p, uint2 o)
+{
+    const u32x2_t v = {o.x, o.y};
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t*>(p));
+}
+
+// Value of `v` in lane `lane` (a compile-time or wave-uniform index), for every lane.
+__device__ __forceinline__ int lane_value(int v, int lane)
+{
+    return __builtin_amdgcn_readlane(v, lane);
+}
+
+__device__ __forceinline__ float lane_value(float v, int lane)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
 // Largest value across the 64 lanes of a wave (unsigned).
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 {

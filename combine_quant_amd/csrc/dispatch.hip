@@ -1,12 +1,18 @@
 // dispatch.hip -- quantize each source token once and write it to its K packed rows.
 //
-// One workgroup per source token (s, i).  The token's bf16 row is read once with 16-byte
-// loads (8 elements per lane; consecutive lanes take consecutive 16-byte vectors, so every
-// load instruction of a wave covers 1 KiB of contiguous memory), quantized in registers, and
-// stored to the final row of each routed pick.  Rows come from the pages' placement rule
-// (design doc §2.2.2 token reorder + §2.4 post-processing, merged into one address because
-// every receiver lives in this GPU's memory): the (expert, source) segment base left in the
-// workspace by the scan kernel plus the pick's expand_idx.
+// Vectorized path (H % 8 == 0, 16-byte aligned pointers): one workgroup per source token
+// (s, i); each wavefront owns two slots of 64 16-byte vectors (8 bf16 elements per lane, so
+// every load instruction covers 1 KiB of contiguous memory).  All waves issue their row
+// loads first; threads 0..K-1 resolve the token's K destination rows meanwhile; one barrier
+// publishes the rows (and, for mode 2, the per-wave maxima of the token).  Each wave then
+// quantizes its slots in registers and stores them to the final row of every routed pick.
+// Rows are read and written with the non-temporal cache policy (each is touched exactly
+// once).  Small workgroups, many of them, keep every SIMD busy until the end of the launch.
+//
+// Destination rows follow the pages' placement rule (design doc §2.2.2 token reorder and
+// §2.4 post-processing, merged into one address because every receiver lives in this GPU's
+// memory): the (expert, source) segment base left in the workspace by the scan kernel plus
+// the pick's expand_idx.
 //
 // Quantization (ops-transformer article, 功能说明 情形 2; low_latency_dispatch, 计算公式):
 //   mode 0  rows copied bit for bit
@@ -18,8 +24,8 @@
 //           codes = E4M3(x / 2^shared_exp); the stored scale is 2^shared_exp.
 // An MX block is 32 elements = 4 adjacent lanes of 8, reduced with two lane exchanges.
 //
-// VEC = 8 is the vectorized path (H % 8 == 0, 16-byte aligned pointers); VEC = 1 handles
-// any H and alignment one element per lane.
+// The element-wise fallback (any H, any alignment) uses one workgroup per token with one
+// element per lane (scatter_kernel with VEC = 1).
 #include "dc_device.h"
 #include "dc_internal.h"
 
@@ -278,6 +284,277 @@ __global__ __launch_bounds__(kMaxThreads) void scatter_kernel(
     }
 }
 
+
+// ---------------------------------------------------------------------------------------
+// vectorized path: one workgroup per token, kTileSlots 64-vector slots per wave
+// ---------------------------------------------------------------------------------------
+
+constexpr int kTileSlots = 2;        // 64-vector slots (1 KiB of bf16 each) per wave
+constexpr int kMaxTileWaves = 8;     // H <= 8192: at most 1024 vectors = 16 slots
+
+__device__ __forceinline__ void unpack8(uint4 w, float (&f)[8])
+{
+    f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
+    f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z); f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
+}
+
+__device__ __forceinline__ void smooth8(const float* sm, int v, float (&f)[8])
+{
+    const float4 a = reinterpret_cast<const float4*>(sm)[2 * v];
+    const float4 b = reinterpret_cast<const float4*>(sm)[2 * v + 1];
+    f[0] = f[0] * a.x; f[1] = f[1] * a.y; f[2] = f[2] * a.z; f[3] = f[3] * a.w;
+    f[4] = f[4] * b.x; f[5] = f[5] * b.y; f[6] = f[6] * b.z; f[7] = f[7] * b.w;
+}
+
+__device__ __forceinline__ uint32_t absmax8(const float (&f)[8], uint32_t amax)
+{
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const uint32_t bits = __float_as_uint(f[c]) & 0x7FFFFFFFu;
+        amax = amax > bits ? amax : bits;
+    }
+    return amax;
+}
+
+__device__ __forceinline__ uint2 pack_codes8(const uint32_t (&c)[8])
+{
+    return make_uint2((c[0] & 0xFF) | ((c[1] & 0xFF) << 8) | ((c[2] & 0xFF) << 16) | (c[3] << 24),
+                      (c[4] & 0xFF) | ((c[5] & 0xFF) << 8) | ((c[6] & 0xFF) << 16) | (c[7] << 24));
+}
+
+template <int MODE, bool SMOOTH>
+__global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
+    const int32_t* __restrict__ expand_idx, const int32_t* __restrict__ seg,
+    const float* __restrict__ smooth, void* __restrict__ expand_x,
+    float* __restrict__ dyn_scales, int32_t* __restrict__ assist, int W, int E, int BS,
+    int H, int K, int ns, long long cap)
+{
+    __shared__ int32_t rows_lds[kMaxK];
+    __shared__ int32_t exps_lds[kMaxK];
+    __shared__ uint32_t red[2][kMaxTileWaves];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int nw = blockDim.x / kWave;
+    const long long tok = blockIdx.x;
+    const int s = (int)(tok / BS);
+    const int i = (int)(tok - (long long)s * BS);
+    const int NV = H >> 3;
+
+    // 1. this wave's slots of the token row, in flight before anything waits
+    const uint4* xr = reinterpret_cast<const uint4*>(x) + tok * NV;
+    uint4 raw[kTileSlots];
+#pragma unroll
+    for (int n = 0; n < kTileSlots; ++n) {
+        const int v = lane + (wave * kTileSlots + n) * kWave;
+        if (v < NV) raw[n] = load_stream(xr + v);
+    }
+
+    // 2. destination rows, resolved by threads 0..K-1
+    if (threadIdx.x < K) {
+        const long long p = tok * K + threadIdx.x;
+        const int32_t ord = expand_idx[p];
+        const int32_t e = ids[p];
+        int32_t row = -1;
+        if (ord >= 0 && e >= 0 && e < E) {
+            const long long r = (long long)seg[(long long)e * W + s] + ord;
+            if (r < cap) row = (int32_t)r;
+        }
+        rows_lds[threadIdx.x] = row;
+        exps_lds[threadIdx.x] = e;
+        if (row >= 0) {
+            assist[(long long)row * 3 + 0] = s;
+            assist[(long long)row * 3 + 1] = i;
+            assist[(long long)row * 3 + 2] = threadIdx.x;
+        }
+    }
+
+    // 3. the token's absolute maximum (mode 2 without smooth scales), per wave first
+    if (MODE == 2 && !SMOOTH) {
+        uint32_t amax = 0;
+#pragma unroll
+        for (int n = 0; n < kTileSlots; ++n) {
+            const int v = lane + (wave * kTileSlots + n) * kWave;
+            if (v < NV) {
+                float f[8];
+                unpack8(raw[n], f);
+                amax = absmax8(f, amax);
+            }
+        }
+        amax = wave_max_u32(amax);
+        if (lane == 0) red[0][wave] = amax;
+    }
+    __syncthreads();
+
+    int rows[kMaxK];
+    bool any = false;
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k) {
+        rows[k] = k < K ? __builtin_amdgcn_readfirstlane(rows_lds[k]) : -1;
+        any |= rows[k] >= 0;
+    }
+    if (!any) return;                                      // uniform over the workgroup
+
+    if (MODE == 0) {
+        uint4* out = reinterpret_cast<uint4*>(expand_x);
+#pragma unroll
+        for (int n = 0; n < kTileSlots; ++n) {
+            const int v = lane + (wave * kTileSlots + n) * kWave;
+            if (v >= NV) continue;
+#pragma unroll
+            for (int k = 0; k < kMaxK; ++k)
+                if (rows[k] >= 0) store_stream(out + (long long)rows[k] * NV + v, raw[n]);
+        }
+        return;
+    }
+
+    uint2* out = reinterpret_cast<uint2*>(expand_x);     // 8 codes per vector
+
+    if (MODE == 2 && !SMOOTH) {
+        uint32_t amax = 0;
+        for (int w = 0; w < nw; ++w) amax = amax > red[0][w] ? amax : red[0][w];
+        const float dyn = 127.0f / __uint_as_float(amax);
+#pragma unroll
+        for (int n = 0; n < kTileSlots; ++n) {
+            const int v = lane + (wave * kTileSlots + n) * kWave;
+            if (v >= NV) continue;
+            float f[8];
+            unpack8(raw[n], f);
+            uint32_t c[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) c[q] = int8_code(f[q], dyn);
+            const uint2 packed = pack_codes8(c);
+#pragma unroll
+            for (int k = 0; k < kMaxK; ++k)
+                if (rows[k] >= 0) store_stream(out + (long long)rows[k] * NV + v, packed);
+        }
+        if (threadIdx.x == 0) {
+            const float scale = 1.0f / dyn;
+#pragma unroll
+            for (int k = 0; k < kMaxK; ++k)
+                if (rows[k] >= 0) dyn_scales[rows[k]] = scale;
+        }
+        return;
+    }
+
+    if (MODE == 2) {   // smooth scales: one quantization per pick, on its expert's row
+        for (int pk = 0; pk < K; ++pk) {
+            const int prow = rows_lds[pk];
+            if (prow < 0) continue;                        // uniform over the workgroup
+            const float* sm = smooth + (long long)exps_lds[pk] * H;
+            uint32_t amax = 0;
+#pragma unroll
+            for (int n = 0; n < kTileSlots; ++n) {
+                const int v = lane + (wave * kTileSlots + n) * kWave;
+                if (v < NV) {
+                    float f[8];
+                    unpack8(raw[n], f);
+                    smooth8(sm, v, f);
+                    amax = absmax8(f, amax);
+                }
+            }
+            amax = wave_max_u32(amax);
+            // alternating buffers: a wave can only write this buffer again two picks later,
+            // after the next barrier, by which time every wave has read it
+            if (lane == 0) red[pk & 1][wave] = amax;
+            __syncthreads();
+            amax = 0;
+            for (int w = 0; w < nw; ++w) amax = amax > red[pk & 1][w] ? amax : red[pk & 1][w];
+            const float dyn = 127.0f / __uint_as_float(amax);
+#pragma unroll
+            for (int n = 0; n < kTileSlots; ++n) {
+                const int v = lane + (wave * kTileSlots + n) * kWave;
+                if (v >= NV) continue;
+                float f[8];
+                unpack8(raw[n], f);
+                smooth8(sm, v, f);
+                uint32_t c[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) c[q] = int8_code(f[q], dyn);
+                store_stream(out + (long long)prow * NV + v, pack_codes8(c));
+            }
+            if (threadIdx.x == 0) dyn_scales[prow] = 1.0f / dyn;
+        }
+        return;
+    }
+
+    // MX modes 4 and 5: a 32-element block is 4 adjacent lanes of one wave
+    const int nb = (H + kMxBlock - 1) / kMxBlock;
+#pragma unroll
+    for (int n = 0; n < kTileSlots; ++n) {
+        const int v = lane + (wave * kTileSlots + n) * kWave;
+        float f[8];
+        uint32_t amax = 0;
+        if (v < NV) {
+            unpack8(raw[n], f);
+            amax = absmax8(f, 0u);
+        }
+        amax = group_max_u32<4>(amax);
+        if (v >= NV) continue;
+        const int se = mx_shared_exp<MODE>(amax);
+        const float inv = __uint_as_float((uint32_t)(127 - se) << 23);       // 2^-se, exact
+        uint32_t c[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) c[q] = e4m3_code(f[q] * inv);
+        const uint2 packed = pack_codes8(c);
+        const bool lead = (v & 3) == 0;
+        const float scale = pow2f(se);
+#pragma unroll
+        for (int k = 0; k < kMaxK; ++k) {
+            if (rows[k] < 0) continue;
+            store_stream(out + (long long)rows[k] * NV + v, packed);
+            if (lead) dyn_scales[(long long)rows[k] * ns + (v >> 2)] = scale;
+        }
+    }
+    if (threadIdx.x == 0 && ns > nb) {
+#pragma unroll
+        for (int k = 0; k < kMaxK; ++k)
+            if (rows[k] >= 0) dyn_scales[(long long)rows[k] * ns + nb] = 0.0f;
+    }
+}
+
+template <int MODE, bool SMOOTH>
+hipError_t launch_tile_mode(const Shape& sh, const void* x, const int32_t* ids,
+                            const int32_t* expand_idx, const int32_t* seg, const float* smooth,
+                            void* expand_x, float* dyn_scales, int32_t* assist,
+                            hipStream_t stream)
+{
+    const long long T = (long long)sh.W * sh.BS;
+    const int slots = ((sh.H >> 3) + kWave - 1) / kWave;
+    const int waves = (slots + kTileSlots - 1) / kTileSlots;        // <= kMaxTileWaves
+    hipLaunchKernelGGL((scatter_tile_kernel<MODE, SMOOTH>), dim3((unsigned)T),
+                       dim3(kWave * waves), 0, stream, static_cast<const uint16_t*>(x), ids,
+                       expand_idx, seg, smooth, expand_x, dyn_scales, assist, sh.W, sh.E, sh.BS,
+                       sh.H, sh.K, sh.scales_per_row, (long long)sh.cap);
+    return hipGetLastError();
+}
+
+hipError_t launch_tile(const Shape& sh, const void* x, const int32_t* ids,
+                       const int32_t* expand_idx, const int32_t* seg, const float* smooth,
+                       void* expand_x, float* dyn_scales, int32_t* assist, hipStream_t stream)
+{
+    switch (sh.quant_mode) {
+    case 0:
+        return launch_tile_mode<0, false>(sh, x, ids, expand_idx, seg, smooth, expand_x,
+                                          dyn_scales, assist, stream);
+    case 2:
+        if (smooth)
+            return launch_tile_mode<2, true>(sh, x, ids, expand_idx, seg, smooth, expand_x,
+                                             dyn_scales, assist, stream);
+        return launch_tile_mode<2, false>(sh, x, ids, expand_idx, seg, smooth, expand_x,
+                                          dyn_scales, assist, stream);
+    case 4:
+        return launch_tile_mode<4, false>(sh, x, ids, expand_idx, seg, smooth, expand_x,
+                                          dyn_scales, assist, stream);
+    case 5:
+        return launch_tile_mode<5, false>(sh, x, ids, expand_idx, seg, smooth, expand_x,
+                                          dyn_scales, assist, stream);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
 template <int MODE, int VEC, bool SMOOTH>
 hipError_t launch_mode(const Shape& sh, const void* x, const int32_t* ids,
                        const int32_t* expand_idx, const int32_t* seg, const float* smooth,
@@ -329,8 +606,8 @@ hipError_t launch_scatter(const Shape& sh, const void* x, const int32_t* expert_
                           bool vectorized, hipStream_t stream)
 {
     if (vectorized)
-        return launch_vec<8>(sh, x, expert_ids, expand_idx, seg, smooth, expand_x,
-                             dynamic_scales, assist_info, stream);
+        return launch_tile(sh, x, expert_ids, expand_idx, seg, smooth, expand_x,
+                           dynamic_scales, assist_info, stream);
     return launch_vec<1>(sh, x, expert_ids, expand_idx, seg, smooth, expand_x, dynamic_scales,
                          assist_info, stream);
 }
