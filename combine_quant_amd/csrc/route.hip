@@ -6,19 +6,19 @@
 // it is computed in parallel and deterministically, without relying on the order in which
 // atomics land:
 //
-//   * one workgroup per (source rank s, group of 32 experts), one lane per token, builds in
-//     LDS a bitmap hit[e][i/32] with bit i%32 set when token i picked e at least once, plus
-//     extra[e][i/32] = picks beyond the first made by the tokens of that 32-token word
-//     (duplicates inside a token; the pages' own example draws ids with replacement).  OR
-//     and ADD commute, so the LDS contents do not depend on thread timing.
+//   * one workgroup per (source rank s, group of experts; about one workgroup per CU), one
+//     lane per token, builds in LDS a bitmap hit[e][i/32] with bit i%32 set when token i
+//     picked e at least once, plus extra[e][i/32] = picks beyond the first made by the tokens
+//     of that 32-token word (duplicates inside a token; the pages' own example draws ids
+//     with replacement).  OR and ADD commute, so the LDS contents do not depend on thread
+//     timing; and because bit i belongs to token i alone, the old value returned by the OR
+//     tells the lane whether its token already picked that expert.
 //   * an exclusive running popcount over each expert's words turns this into
 //       ordinal(i, k) = #hits in earlier words + extras in earlier words
 //                     + #hits of earlier tokens in the same word (masked popcount)
-//                     + duplicates of e earlier in token i
-//                     + extras of earlier tokens in the same word (only if that word has any)
-//   * the per-(expert, source) totals go to the workspace at e*W + s;
-//   * a token whose picks are all different (the usual case) needs none of the duplicate
-//     bookkeeping; a token with a repeated expert takes the exact slower branch.
+//                     + (only in words with extras) this token's earlier picks of e and the
+//                       repeats of the earlier tokens of the word
+//   * the per-(expert, source) totals go to the workspace at e*W + s.
 //
 // The receive-side scan (design doc §2.4: transpose the W x L receive matrix, then a
 // row-major running sum) is one workgroup.  Because the workspace keeps the counts in the
@@ -31,7 +31,7 @@
 namespace moe_dc {
 namespace {
 
-constexpr int kRouteExperts = 32;     // experts per routing workgroup
+constexpr int kMaxRouteExperts = 256; // experts per routing workgroup, at most
 constexpr int kScanThreads = 1024;    // >= E (E <= 1024 is validated)
 constexpr int kScanLdsCounts = 16384; // counts staged in LDS by the scan (64 KiB)
 
@@ -55,16 +55,38 @@ __device__ __forceinline__ void routed_picks(const int32_t* __restrict__ ids,
     }
 }
 
+// Same, for K == KMAX with KMAX a multiple of 4 and 16-byte aligned ids: 16-byte loads.
+// An id is routed when its pick is active and 0 <= id < E (one unsigned compare).
 template <int KMAX>
+__device__ __forceinline__ void routed_picks_vec(const int32_t* __restrict__ ids,
+                                                 const uint8_t* __restrict__ mask, int mask_kind,
+                                                 int E, long long tok, int32_t (&e)[KMAX])
+{
+    const int4* p = reinterpret_cast<const int4*>(ids + tok * KMAX);
+    const bool tok_on = mask_kind != 1 || mask[tok] != 0;
+#pragma unroll
+    for (int q = 0; q < KMAX / 4; ++q) {
+        const int4 v = p[q];
+        const int32_t r[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int k = 4 * q + c;
+            const bool on = tok_on && (mask_kind != 2 || mask[tok * KMAX + k] != 0);
+            e[k] = (on && (uint32_t)r[c] < (uint32_t)E) ? r[c] : -1;
+        }
+    }
+}
+
+template <int KMAX, bool VEC_IDS>
 __global__ __launch_bounds__(512) void route_kernel(
     const int32_t* __restrict__ ids, const uint8_t* __restrict__ mask, int mask_kind, int W,
-    int E, int BS, int K, int nwords, int32_t* __restrict__ expand_idx,
+    int E, int BS, int K, int nwords, int group, int32_t* __restrict__ expand_idx,
     int32_t* __restrict__ seg)
 {
     extern __shared__ uint32_t lds[];
     const int s = blockIdx.x;
-    const int e_lo = blockIdx.y * kRouteExperts;
-    const int ne = min(kRouteExperts, E - e_lo);
+    const int e_lo = blockIdx.y * group;
+    const int ne = min(group, E - e_lo);
     const int n = ne * nwords;
     uint32_t* hit = lds;               // [ne][nwords]
     uint32_t* extra = hit + n;         // [ne][nwords]
@@ -75,18 +97,16 @@ __global__ __launch_bounds__(512) void route_kernel(
     const int i = threadIdx.x;
     const long long tok = (long long)s * BS + i;
     int32_t e[KMAX];
-    bool distinct = true;
     if (i < BS) {
-        routed_picks<KMAX>(ids, mask, mask_kind, K, E, tok, e);
-#pragma unroll
-        for (int a = 0; a < KMAX; ++a)
-#pragma unroll
-            for (int b = a + 1; b < KMAX; ++b)
-                if (e[a] >= 0 && e[a] == e[b]) distinct = false;
+        if (VEC_IDS) routed_picks_vec<KMAX>(ids, mask, mask_kind, E, tok, e);
+        else routed_picks<KMAX>(ids, mask, mask_kind, K, E, tok, e);
     }
     for (int w = threadIdx.x; w < 2 * n; w += blockDim.x) lds[w] = 0;
     __syncthreads();
 
+    // Bit i of a word belongs to token i alone and this lane walks its picks in k order, so
+    // the value atomicOr returns says whether this token already picked the expert: each
+    // repeat counts one extra pick for the word.
     const int wd = i >> 5;
     const uint32_t bit = 1u << (i & 31);
     if (i < BS) {
@@ -95,23 +115,7 @@ __global__ __launch_bounds__(512) void route_kernel(
             const int32_t ek = e[k];
             if (ek < e_lo || ek >= e_lo + ne) continue;
             const int word = (ek - e_lo) * nwords + wd;
-            if (distinct) {
-                atomicOr(&hit[word], bit);
-                continue;
-            }
-            bool first = true;
-            uint32_t mult = 1;
-#pragma unroll
-            for (int k2 = 0; k2 < KMAX; ++k2) {
-                if (k2 != k && e[k2] == ek) {
-                    ++mult;
-                    if (k2 < k) first = false;
-                }
-            }
-            if (first) {
-                atomicOr(&hit[word], bit);
-                if (mult > 1) atomicAdd(&extra[word], mult - 1);
-            }
+            if (atomicOr(&hit[word], bit) & bit) atomicAdd(&extra[word], 1u);
         }
     }
     __syncthreads();
@@ -146,13 +150,12 @@ __global__ __launch_bounds__(512) void route_kernel(
         if (ek < e_lo || ek >= e_lo + ne) continue;
         const int word = (ek - e_lo) * nwords + wd;
         uint32_t ord = hit_pre[word] + extra_pre[word] + __popc(hit[word] & below);
-        if (!distinct) {
+        if (extra[word] != 0) {
+            // some token of this 32-token word picked ek more than once: add this token's
+            // own earlier picks of ek, and the repeats of the earlier tokens of the word
 #pragma unroll
             for (int k2 = 0; k2 < KMAX; ++k2)
                 if (k2 < k && e[k2] == ek) ++ord;
-        }
-        if (extra[word] != 0) {
-            // earlier tokens of this 32-token word that picked ek more than once
             uint32_t bits = hit[word] & below;
             while (bits) {
                 const int b = __ffs(bits) - 1;
@@ -202,38 +205,57 @@ __global__ __launch_bounds__(kScanThreads) void scan_flat_kernel(
     int32_t* __restrict__ ep_recv_count, int64_t* __restrict__ expert_token_nums,
     int64_t* __restrict__ recv_offsets)
 {
-    extern __shared__ int32_t ex[];          // N + 1 entries
+    // entry f is kept at LDS word f + f/32: one pad word per 32 spreads each thread's run of
+    // consecutive entries over the banks (a plain layout puts a wave's runs on 4 banks)
+    extern __shared__ int32_t lds_ex[];      // padded N + 1 entries, then E rank bases
     __shared__ int32_t wave_tot[kScanThreads / kWave];
     const int N = E * W;
+    int32_t* rank_first = lds_ex + N + 1 + ((N + 1) >> 5) + 1;
     const int t = threadIdx.x;
-    for (int f = t; f < N; f += blockDim.x) ex[f] = seg[f];
+#define ex(f) lds_ex[(f) + ((f) >> 5)]
+    for (int f = t; f < N; f += blockDim.x) ex(f) = seg[f];
     __syncthreads();
     const int per = (N + blockDim.x - 1) / blockDim.x;
     const int lo = min(N, t * per);
     const int hi = min(N, lo + per);
     int32_t run = 0;
-    for (int f = lo; f < hi; ++f) run += ex[f];
+    for (int f = lo; f < hi; ++f) run += ex(f);
     const int32_t incl = block_inclusive_scan(run, wave_tot);
     int32_t acc = incl - run;
     for (int f = lo; f < hi; ++f) {
-        const int32_t c = ex[f];
-        ex[f] = acc;
+        const int32_t c = ex(f);
+        ex(f) = acc;
         acc += c;
     }
-    if (t == blockDim.x - 1) ex[N] = incl;
+    if (t == blockDim.x - 1) ex(N) = incl;
     __syncthreads();
-    for (int f = t; f < N; f += blockDim.x) {
-        const int e = f / W;
-        const int rank_first = (e / L) * L * W;
-        seg[f] = ex[f];
-        ep_recv_count[f] = ex[f + 1] - ex[rank_first];
-    }
+    // per expert: its rank's first entry, expert_token_nums; per rank: recv_offsets
     for (int e = t; e < E; e += blockDim.x) {
-        const int rank_first = (e / L) * L * W;
-        expert_token_nums[e] =
-            (int64_t)(ex[(e + 1) * W] - (etn_type == 0 ? ex[rank_first] : ex[e * W]));
+        const int first = (e / L) * L * W;
+        rank_first[e] = ex(first);
+        const int last = (e + 1) * W;
+        const int from = etn_type == 0 ? first : e * W;
+        expert_token_nums[e] = (int64_t)(ex(last) - ex(from));
     }
-    for (int r = t; r <= W; r += blockDim.x) recv_offsets[r] = ex[r * L * W];
+    for (int r = t; r <= W; r += blockDim.x) {
+        const int f = r * L * W;
+        recv_offsets[r] = ex(f);
+    }
+    __syncthreads();
+    // coalesced stores over (expert, source): thread t covers source t % W of experts
+    // e0 + t / W, e0 advancing by rows = blockDim / W per pass (one division per thread)
+    const int rows = blockDim.x / W;
+    const int te = t / W;
+    const int ts = t - te * W;
+    if (te < rows) {
+        for (int e = te; e < E; e += rows) {
+            const int f = e * W + ts;
+            const int f1 = f + 1;
+            seg[f] = ex(f);
+            ep_recv_count[f] = ex(f1) - rank_first[e];
+        }
+    }
+#undef ex
 }
 
 // Receive-side scan for shapes whose counts exceed the LDS budget: one thread per expert
@@ -276,19 +298,26 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
 hipError_t launch_route(const Shape& sh, const int32_t* expert_ids, const uint8_t* mask,
                         int32_t* expand_idx, int32_t* seg, hipStream_t stream)
 {
+    // about one workgroup per CU: (W source ranks) x (groups of experts)
     const int nwords = (sh.BS + 31) / 32;
-    const int groups = (sh.E + kRouteExperts - 1) / kRouteExperts;
-    const int ne = sh.E < kRouteExperts ? sh.E : kRouteExperts;
-    const size_t lds = (size_t)4 * ne * nwords * sizeof(uint32_t);
+    int groups = 256 / sh.W;
+    const int max_groups = (sh.E + 15) / 16;
+    groups = groups < 1 ? 1 : (groups > max_groups ? max_groups : groups);
+    int group = (sh.E + groups - 1) / groups;
+    if (group > kMaxRouteExperts) group = kMaxRouteExperts;
+    groups = (sh.E + group - 1) / group;
+    const size_t lds = (size_t)4 * group * nwords * sizeof(uint32_t);
     const int threads = (sh.BS + kWave - 1) / kWave * kWave;      // one lane per token
     const dim3 grid(sh.W, groups);
-#define MOE_DC_ROUTE(KM)                                                                        \
-    hipLaunchKernelGGL(route_kernel<KM>, grid, dim3(threads), lds, stream, expert_ids, mask,  \
-                       sh.mask_kind, sh.W, sh.E, sh.BS, sh.K, nwords, expand_idx, seg)
-    if (sh.K <= 2) MOE_DC_ROUTE(2);
-    else if (sh.K <= 4) MOE_DC_ROUTE(4);
-    else if (sh.K <= 8) MOE_DC_ROUTE(8);
-    else MOE_DC_ROUTE(16);
+    const bool vec = (sh.K % 4 == 0) && ((reinterpret_cast<uintptr_t>(expert_ids) & 15) == 0);
+#define MOE_DC_ROUTE(KM, V)                                                                      \
+    hipLaunchKernelGGL((route_kernel<KM, V>), grid, dim3(threads), lds, stream, expert_ids,     \
+                       mask, sh.mask_kind, sh.W, sh.E, sh.BS, sh.K, nwords, group, expand_idx, \
+                       seg)
+    if (sh.K <= 2) MOE_DC_ROUTE(2, false);
+    else if (sh.K <= 4) { if (vec && sh.K == 4) MOE_DC_ROUTE(4, true); else MOE_DC_ROUTE(4, false); }
+    else if (sh.K <= 8) { if (vec && sh.K == 8) MOE_DC_ROUTE(8, true); else MOE_DC_ROUTE(8, false); }
+    else { if (vec && sh.K == 16) MOE_DC_ROUTE(16, true); else MOE_DC_ROUTE(16, false); }
 #undef MOE_DC_ROUTE
     return hipGetLastError();
 }
@@ -298,8 +327,9 @@ hipError_t launch_scan(const Shape& sh, int32_t* seg, int32_t* ep_recv_count,
 {
     const long long n = (long long)sh.E * sh.W;
     if (n <= kScanLdsCounts) {
+        const size_t words = (size_t)n + 1 + (size_t)((n + 1) >> 5) + 1 + sh.E;
         hipLaunchKernelGGL(scan_flat_kernel, dim3(1), dim3(kScanThreads),
-                           (n + 1) * sizeof(int32_t), stream, sh.W, sh.E, sh.L, sh.etn_type, seg,
+                           words * sizeof(int32_t), stream, sh.W, sh.E, sh.L, sh.etn_type, seg,
                            ep_recv_count, expert_token_nums, recv_offsets);
     } else {
         const int threads = ((sh.E + kWave - 1) / kWave) * kWave;

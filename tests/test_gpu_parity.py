@@ -44,6 +44,14 @@ SMALL = {
     "scalar_path_mode0_h1030": workloads.Workload("scalar_path_mode0_h1030", W=3, E=9, BS=9,
                                                   H=1030, K=2, quant_mode=0, copy_expert_num=1),
     "l1_w8_k8": workloads.Workload("l1_w8_k8", W=8, E=8, BS=40, H=1024, K=8, quant_mode=4),
+    "vec_ids_k8_special": workloads.Workload("vec_ids_k8_special", W=4, E=32, BS=50, H=1024, K=8,
+                                             quant_mode=2, zero_expert_num=1,
+                                             copy_expert_num=1, mask_kind=1,
+                                             inactive_tokens_per_rank=5),
+    "vec_ids_k4_special": workloads.Workload("vec_ids_k4_special", W=2, E=16, BS=90, H=1024, K=4,
+                                             quant_mode=4, zero_expert_num=2,
+                                             copy_expert_num=1, mask_kind=2,
+                                             inactive_tokens_per_rank=4),
     "bs1_h8192": workloads.Workload("bs1_h8192", W=2, E=2, BS=1, H=8192, K=2, quant_mode=2),
     "w768_e768": workloads.Workload("w768_e768", W=768, E=768, BS=1, H=1024, K=2,
                                     quant_mode=2),
@@ -241,3 +249,43 @@ def test_invalid_arguments_raise_and_enqueue_nothing():
     assert ei.value.status == cq.MOE_ERR_WORKSPACE
     torch.cuda.synchronize()
     assert (o["expand_idx"] == 123).all()
+
+
+@pytest.mark.parametrize("K", [3, 4, 8, 16])
+def test_out_of_range_ids_are_not_dispatched(K):
+    """Ids outside [0, E+Z+C) break the contract; the library must treat such picks exactly
+    like masked-off picks (no row, expand_idx -1, no combine term) and never touch memory
+    out of bounds.  Reference: the oracle on the same input with those picks masked off."""
+    import torch
+    import combine_quant_amd as cq
+    wl = workloads.Workload("bad_ids", W=4, E=32, BS=60, H=1024, K=K, quant_mode=2,
+                            zero_expert_num=1, copy_expert_num=1, mask_kind=2)
+    inp = workloads.generate(wl, seed=11)
+    rng = np.random.default_rng(5)
+    bad = rng.random(inp["expert_ids"].shape) < 0.1
+    ids_bad = inp["expert_ids"].copy()
+    ids_bad[bad] = rng.choice([-7, -1, wl.n_ids, wl.n_ids + 3, 1 << 30], size=int(bad.sum()))
+    # reference: same routing with the bad picks masked off and given a harmless id
+    ref_mask = inp["mask"].copy()
+    ref_mask[bad] = 0
+    ref_ids = ids_bad.copy()
+    ref_ids[bad] = 0
+    ocfg = harness.oracle_cfg(wl)
+    ref = oracle.dispatch(ocfg, inp["x"], ref_ids, mask=ref_mask)
+    cfg = harness.lib_cfg(wl)
+    x = harness.bf16_dev(inp["x"])
+    ids_dev = harness.to_dev(ids_bad)
+    mask_dev = harness.to_dev(inp["mask"])
+    out = cq.dispatch(cfg, x, ids_dev, None, mask_dev)
+    torch.cuda.synchronize()
+    harness.compare_dispatch(wl, inp, out, ref)
+    rng2 = np.random.default_rng(6)
+    eo = workloads.f32_to_bf16_bits(rng2.standard_normal((wl.cap, wl.H), dtype=np.float32))
+    y_ref = oracle.combine(ocfg, eo, ref_ids, ref["expand_idx"], inp["expert_scales"],
+                           ref["ep_recv_count"], ref["recv_offsets"], mask=ref_mask,
+                           ori_x=inp["x"])
+    y = cq.combine(cfg, harness.bf16_dev(eo), ids_dev, out["expand_idx"],
+                   harness.to_dev(inp["expert_scales"]), out["ep_recv_count"],
+                   out["recv_offsets"], mask_dev, x)
+    torch.cuda.synchronize()
+    assert harness.check_combine_tolerance(harness.host(y), y_ref) == 0
