@@ -13,7 +13,7 @@
 // accumulate in fp32, cast down), and stores the bf16 rounding of the sum.
 //
 // Vectorized path (H % 8 == 0, 16-byte aligned): a token's row is cut into chunks of 128
-// 16-byte vectors, each handled by one independent wavefront, which resolves the token's
+// 16-byte vectors (64 for K > 8), each handled by one independent wavefront, which resolves the token's
 // sources in lanes 0..K-1 and broadcasts them as wave-uniform values; expert rows are read
 // and y is written with the non-temporal policy; no workgroup barrier.  Element-wise
 // fallback: one workgroup per token.
@@ -137,9 +137,12 @@ __global__ __launch_bounds__(kMaxThreads) void combine_kernel(
 
 
 constexpr int kWavesPerBlock = 4;
-constexpr int kSlotsPerTask = 2;   // 64-vector slots of one token per wave task
 
-// One wave task = one token x kSlotsPerTask slots of 64 16-byte vectors.  A token's row is
+// 64-vector slots of one token per wave task: two (16 row loads in flight per lane at K=8);
+// one for K > 8, where two would need 32 loads' worth of registers and halve occupancy.
+constexpr int slots_per_task(int kmax) { return kmax > 8 ? 1 : 2; }
+
+// One wave task = one token x SLOTS slots of 64 16-byte vectors.  A token's row is
 // split across several independent waves (each resolves the token's K sources itself), so a
 // launch is many short tasks: the hardware keeps every SIMD busy to the end instead of
 // leaving a long, thinly occupied last round of whole-token waves.
@@ -232,10 +235,11 @@ hipError_t launch_wave_k(const Shape& sh, const void* expert_out, const int32_t*
 {
     const long long T = (long long)sh.W * sh.BS;
     const int slots = ((sh.H >> 3) + kWave - 1) / kWave;
-    const int tasks_per_token = (slots + kSlotsPerTask - 1) / kSlotsPerTask;
+    constexpr int kSlots = slots_per_task(KMAX);
+    const int tasks_per_token = (slots + kSlots - 1) / kSlots;
     const long long tasks = T * tasks_per_token;
     const unsigned blocks = (unsigned)((tasks + kWavesPerBlock - 1) / kWavesPerBlock);
-    hipLaunchKernelGGL((combine_wave_kernel<KMAX, kSlotsPerTask>), dim3(blocks),
+    hipLaunchKernelGGL((combine_wave_kernel<KMAX, kSlots>), dim3(blocks),
                        dim3(kWave * kWavesPerBlock), 0, stream,
                        static_cast<const uint16_t*>(expert_out), ids, expand_idx, w, erc, roff,
                        mask, sh.mask_kind, static_cast<const uint16_t*>(ori_x),

@@ -298,14 +298,6 @@ __device__ __forceinline__ void unpack8(uint4 w, float (&f)[8])
     f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z); f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
 }
 
-__device__ __forceinline__ void smooth8(const float* sm, int v, float (&f)[8])
-{
-    const float4 a = reinterpret_cast<const float4*>(sm)[2 * v];
-    const float4 b = reinterpret_cast<const float4*>(sm)[2 * v + 1];
-    f[0] = f[0] * a.x; f[1] = f[1] * a.y; f[2] = f[2] * a.z; f[3] = f[3] * a.w;
-    f[4] = f[4] * b.x; f[5] = f[5] * b.y; f[6] = f[6] * b.z; f[7] = f[7] * b.w;
-}
-
 __device__ __forceinline__ uint32_t absmax8(const float (&f)[8], uint32_t amax)
 {
 #pragma unroll
@@ -314,6 +306,28 @@ __device__ __forceinline__ uint32_t absmax8(const float (&f)[8], uint32_t amax)
         amax = amax > bits ? amax : bits;
     }
     return amax;
+}
+
+// Eight int8 codes of f * dyn for a finite dyn (dyn = 127 / amax with amax > 0 and not tiny):
+// then |f * dyn| <= 127 * (1 + 2^-23), so no clamp is needed and no NaN can arise.  Adding
+// 1.5 * 2^23 to the binary32 product puts the sum in [2^23, 2^24), where binary32 spacing is 1:
+// the addition rounds the product to an integer, ties to even, and the low byte of the sum's
+// bit pattern is that integer in two's complement.  Byte permutes gather the four low bytes.
+__device__ __forceinline__ uint2 int8_codes8_finite(const float (&f)[8], float dyn)
+{
+    uint32_t b[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const float v = f[q] * dyn;
+        b[q] = __float_as_uint(v + 12582912.0f);
+    }
+    const uint32_t lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u),
+                                              __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u),
+                                              0x05040100u);
+    const uint32_t hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[7], b[6], 0x0c0c0400u),
+                                              __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u),
+                                              0x05040100u);
+    return make_uint2(lo, hi);
 }
 
 __device__ __forceinline__ uint2 pack_codes8(const uint32_t (&c)[8])
@@ -415,16 +429,22 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
         uint32_t amax = 0;
         for (int w = 0; w < nw; ++w) amax = amax > red[0][w] ? amax : red[0][w];
         const float dyn = 127.0f / __uint_as_float(amax);
+        const bool finite = __float_as_uint(dyn) < 0x7F800000u;          // dyn > 0 here
 #pragma unroll
         for (int n = 0; n < kTileSlots; ++n) {
             const int v = lane + (wave * kTileSlots + n) * kWave;
             if (v >= NV) continue;
             float f[8];
             unpack8(raw[n], f);
-            uint32_t c[8];
+            uint2 packed;
+            if (finite) {
+                packed = int8_codes8_finite(f, dyn);
+            } else {
+                uint32_t c[8];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) c[q] = int8_code(f[q], dyn);
-            const uint2 packed = pack_codes8(c);
+                for (int q = 0; q < 8; ++q) c[q] = int8_code(f[q], dyn);
+                packed = pack_codes8(c);
+            }
 #pragma unroll
             for (int k = 0; k < kMaxK; ++k)
                 if (rows[k] >= 0) store_stream(out + (long long)rows[k] * NV + v, packed);
@@ -439,42 +459,79 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
     }
 
     if (MODE == 2) {   // smooth scales: one quantization per pick, on its expert's row
-        for (int pk = 0; pk < K; ++pk) {
-            const int prow = rows_lds[pk];
-            if (prow < 0) continue;                        // uniform over the workgroup
-            const float* sm = smooth + (long long)exps_lds[pk] * H;
+        // The picks run one after another (each needs a workgroup-wide maximum); the smooth
+        // slice of the next routed pick is loaded into the other register buffer while the
+        // current pick reduces, synchronizes and stores, so its latency is hidden.
+        float4 sm_cur[kTileSlots][2], sm_nxt[kTileSlots][2];
+        auto load_smooth = [&](int pick, float4 (&dst)[kTileSlots][2]) {
+            const float4* sm =
+                reinterpret_cast<const float4*>(smooth + (long long)exps_lds[pick] * H);
+#pragma unroll
+            for (int n = 0; n < kTileSlots; ++n) {
+                const int v = lane + (wave * kTileSlots + n) * kWave;
+                if (v < NV) {
+                    dst[n][0] = sm[2 * v];
+                    dst[n][1] = sm[2 * v + 1];
+                }
+            }
+        };
+        int pk = 0;
+        while (pk < K && rows[pk] < 0) ++pk;                 // first routed pick (uniform)
+        if (pk < K) load_smooth(pk, sm_cur);
+        for (int round = 0; pk < K; ++round) {
+            const int cur = round & 1;
+            int nxt = pk + 1;
+            while (nxt < K && rows[nxt] < 0) ++nxt;
+            if (nxt < K) load_smooth(nxt, sm_nxt);
+            const int prow = rows[pk];
+            // x * smooth stays in registers between the maximum and the codes
+            float f[kTileSlots][8];
             uint32_t amax = 0;
 #pragma unroll
             for (int n = 0; n < kTileSlots; ++n) {
                 const int v = lane + (wave * kTileSlots + n) * kWave;
                 if (v < NV) {
-                    float f[8];
-                    unpack8(raw[n], f);
-                    smooth8(sm, v, f);
-                    amax = absmax8(f, amax);
+                    unpack8(raw[n], f[n]);
+                    const float4 a = sm_cur[n][0];
+                    const float4 b = sm_cur[n][1];
+                    f[n][0] = f[n][0] * a.x; f[n][1] = f[n][1] * a.y;
+                    f[n][2] = f[n][2] * a.z; f[n][3] = f[n][3] * a.w;
+                    f[n][4] = f[n][4] * b.x; f[n][5] = f[n][5] * b.y;
+                    f[n][6] = f[n][6] * b.z; f[n][7] = f[n][7] * b.w;
+                    amax = absmax8(f[n], amax);
                 }
             }
             amax = wave_max_u32(amax);
             // alternating buffers: a wave can only write this buffer again two picks later,
             // after the next barrier, by which time every wave has read it
-            if (lane == 0) red[pk & 1][wave] = amax;
+            if (lane == 0) red[cur][wave] = amax;
             __syncthreads();
             amax = 0;
-            for (int w = 0; w < nw; ++w) amax = amax > red[pk & 1][w] ? amax : red[pk & 1][w];
+            for (int w = 0; w < nw; ++w) amax = amax > red[cur][w] ? amax : red[cur][w];
             const float dyn = 127.0f / __uint_as_float(amax);
+            const bool finite = __float_as_uint(dyn) < 0x7F800000u;
 #pragma unroll
             for (int n = 0; n < kTileSlots; ++n) {
                 const int v = lane + (wave * kTileSlots + n) * kWave;
                 if (v >= NV) continue;
-                float f[8];
-                unpack8(raw[n], f);
-                smooth8(sm, v, f);
-                uint32_t c[8];
+                uint2 packed;
+                if (finite) {
+                    packed = int8_codes8_finite(f[n], dyn);
+                } else {
+                    uint32_t c[8];
 #pragma unroll
-                for (int q = 0; q < 8; ++q) c[q] = int8_code(f[q], dyn);
-                store_stream(out + (long long)prow * NV + v, pack_codes8(c));
+                    for (int q = 0; q < 8; ++q) c[q] = int8_code(f[n][q], dyn);
+                    packed = pack_codes8(c);
+                }
+                store_stream(out + (long long)prow * NV + v, packed);
             }
             if (threadIdx.x == 0) dyn_scales[prow] = 1.0f / dyn;
+#pragma unroll
+            for (int n = 0; n < kTileSlots; ++n) {
+                sm_cur[n][0] = sm_nxt[n][0];
+                sm_cur[n][1] = sm_nxt[n][1];
+            }
+            pk = nxt;
         }
         return;
     }
