@@ -13,128 +13,56 @@
 // accumulate in fp32, cast down), and stores the bf16 rounding of the sum.
 //
 // Vectorized path (H % 8 == 0, 16-byte aligned): a token's row is cut into chunks of 128
-// 16-byte vectors (64 for K > 8), each handled by one independent wavefront, which resolves the token's
-// sources in lanes 0..K-1 and broadcasts them as wave-uniform values; expert rows are read
-// and y is written with the non-temporal policy; no workgroup barrier.  Element-wise
-// fallback: one workgroup per token.
+// 16-byte vectors (64 for K > 8), each handled by one independent wavefront, which resolves
+// the token's sources in lanes 0..K-1 and broadcasts them as wave-uniform values; expert rows
+// are read and y is written with the non-temporal policy; no workgroup barrier.  Element-wise
+// fallback (any H, any alignment): one workgroup per token, one element per lane.
 #include "dc_device.h"
 #include "dc_internal.h"
 
 namespace moe_dc {
 namespace {
 
-constexpr int kMaxThreads = 1024;
-constexpr int kVpt = 8;
+constexpr int kNone = -1;   // inactive pick, zero expert, or unresolvable
+constexpr int kCopy = -2;   // copy expert: read ori_x
 
-template <int VEC> struct Cio;
-
-template <> struct Cio<8> {
-    using Raw = uint4;
-    static __device__ __forceinline__ Raw load(const uint16_t* p, int v)
-    {
-        return reinterpret_cast<const uint4*>(p)[v];
-    }
-    static __device__ __forceinline__ void accumulate(Raw w, float wt, float (&acc)[8])
-    {
-        const float f[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
-                            bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
-#pragma unroll
-        for (int c = 0; c < 8; ++c) acc[c] = acc[c] + wt * f[c];
-    }
-    static __device__ __forceinline__ void store(uint16_t* p, int v, const float (&acc)[8])
-    {
-        reinterpret_cast<uint4*>(p)[v] =
-            make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                       pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
-    }
-};
-
-template <> struct Cio<1> {
-    using Raw = uint16_t;
-    static __device__ __forceinline__ Raw load(const uint16_t* p, int v) { return p[v]; }
-    static __device__ __forceinline__ void accumulate(Raw w, float wt, float (&acc)[1])
-    {
-        acc[0] = acc[0] + wt * __uint_as_float((uint32_t)w << 16);
-    }
-    static __device__ __forceinline__ void store(uint16_t* p, int v, const float (&acc)[1])
-    {
-        p[v] = (uint16_t)f32_to_bf16_rne(acc[0]);
-    }
-};
-
-constexpr long long kNone = -1;   // inactive pick, zero expert, or unresolvable
-constexpr long long kCopy = -2;   // copy expert: read ori_x
-
-template <int VEC, int KMAX>
-__global__ __launch_bounds__(kMaxThreads) void combine_kernel(
-    const uint16_t* __restrict__ expert_out, const int32_t* __restrict__ ids,
-    const int32_t* __restrict__ expand_idx, const float* __restrict__ weights,
+// Source of pick k of token tok: its expert_out row (>= 0), kCopy for a copy expert, or
+// kNone.  The row follows the design doc's addressing (§3.4.2: the owner rank's window + the
+// expert's offset inside it + expand_idx), written with the dispatch outputs:
+// recv_offsets[r] + the running total of ep_recv_count just before (local expert j,
+// source s) + expand_idx.  Rows outside [0, cap) are treated as unresolvable.
+__device__ __forceinline__ int pick_source(
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ expand_idx,
     const int32_t* __restrict__ ep_recv_count, const int64_t* __restrict__ recv_offsets,
-    const uint8_t* __restrict__ mask, int mask_kind, const uint16_t* __restrict__ ori_x,
-    uint16_t* __restrict__ y, int W, int E, int L, int BS, int H, int K, int zero_end,
-    int id_end, long long cap)
+    const uint8_t* __restrict__ mask, int mask_kind, int W, int E, int L, int K, int zero_end,
+    int id_end, long long cap, long long tok, int s, int k)
 {
-    using IO = Cio<VEC>;
-    __shared__ long long src_of[KMAX];
-    __shared__ float w_of[KMAX];
-
-    const size_t tok = blockIdx.x;
-    const int s = (int)(tok / BS);
-    const int t = threadIdx.x;
-    const int nt = blockDim.x;
-
-    if (t < K) {
-        const size_t p = tok * K + t;
-        const int32_t e = ids[p];
-        const bool on = mask_kind == 0 || (mask_kind == 1 ? mask[tok] != 0 : mask[p] != 0);
-        long long src = kNone;
-        if (on && e >= 0) {
-            if (e < E) {
-                const int32_t ord = expand_idx[p];
-                if (ord >= 0) {
-                    const int r = e / L;
-                    const int j = e - r * L;
-                    const long long flat = (long long)j * W + s;
-                    const long long base =
-                        flat == 0 ? 0 : (long long)ep_recv_count[(size_t)r * L * W + flat - 1];
-                    const long long row = (long long)recv_offsets[r] + base + ord;
-                    if (row >= 0 && row < cap) src = row * H;
-                }
-            } else if (e >= zero_end && e < id_end) {
-                src = kCopy;
-            }
-        }
-        src_of[t] = src;
-        w_of[t] = weights[p];
+    const long long p = tok * K + k;
+    const int32_t e = ids[p];
+    const bool on = mask_kind == 0 || (mask_kind == 1 ? mask[tok] != 0 : mask[p] != 0);
+    if (!on || e < 0) return kNone;
+    if (e < E) {
+        const int32_t ord = expand_idx[p];
+        if (ord < 0) return kNone;
+        const int r = e / L;
+        const int j = e - r * L;
+        const long long flat = (long long)j * W + s;
+        const long long base =
+            flat == 0 ? 0 : (long long)ep_recv_count[(long long)r * L * W + flat - 1];
+        const long long row = (long long)recv_offsets[r] + base + ord;
+        return (row >= 0 && row < cap) ? (int)row : kNone;
     }
-    __syncthreads();
-
-    const int NV = H / VEC;
-    const uint16_t* self = ori_x ? ori_x + tok * (size_t)H : nullptr;
-    uint16_t* yr = y + tok * (size_t)H;
-#pragma unroll 1
-    for (int n = 0; n < kVpt; ++n) {
-        const int v = t + n * nt;
-        if (v >= NV) break;
-        typename IO::Raw buf[KMAX];
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k) {
-            if (k < K) {
-                const long long src = src_of[k];
-                if (src >= 0) buf[k] = IO::load(expert_out + src, v);
-                else if (src == kCopy) buf[k] = IO::load(self, v);
-            }
-        }
-        float acc[VEC];
-#pragma unroll
-        for (int c = 0; c < VEC; ++c) acc[c] = 0.0f;
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k)
-            if (k < K && src_of[k] != kNone) IO::accumulate(buf[k], w_of[k], acc);
-        IO::store(yr, v, acc);
-    }
+    return (e >= zero_end && e < id_end) ? kCopy : kNone;
 }
 
+// acc[c] = acc[c] + w * element c of eight bf16 values (one multiply, one add each)
+__device__ __forceinline__ void accumulate8(uint4 v, float w, float (&acc)[8])
+{
+    const float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                        bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = acc[c] + w * f[c];
+}
 
 constexpr int kWavesPerBlock = 4;
 
@@ -163,35 +91,18 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_wave_kernel(
     const int s = (int)(tok / BS);
     const int NV = H >> 3;
 
-    int src = -1;            // >= 0: expert_out row; -2: copy expert (ori_x); -1: nothing
+    int src = kNone;
     float wk = 0.0f;
     if (lane < K) {
-        const long long p = tok * K + lane;
-        const int32_t e = ids[p];
-        const bool on = mask_kind == 0 || (mask_kind == 1 ? mask[tok] != 0 : mask[p] != 0);
-        wk = weights[p];
-        if (on && e >= 0) {
-            if (e < E) {
-                const int32_t ord = expand_idx[p];
-                if (ord >= 0) {
-                    const int r = e / L;
-                    const int j = e - r * L;
-                    const long long flat = (long long)j * W + s;
-                    const long long base =
-                        flat == 0 ? 0 : (long long)ep_recv_count[(long long)r * L * W + flat - 1];
-                    const long long row = (long long)recv_offsets[r] + base + ord;
-                    if (row >= 0 && row < cap) src = (int)row;
-                }
-            } else if (e >= zero_end && e < id_end) {
-                src = -2;
-            }
-        }
+        src = pick_source(ids, expand_idx, ep_recv_count, recv_offsets, mask, mask_kind, W, E,
+                          L, K, zero_end, id_end, cap, tok, s, lane);
+        wk = weights[tok * K + lane];
     }
     int srcs[KMAX];
     float ws[KMAX];
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
-        srcs[k] = k < K ? lane_value(src, k) : -1;
+        srcs[k] = k < K ? lane_value(src, k) : kNone;
         ws[k] = lane_value(wk, k);
     }
 
@@ -206,7 +117,7 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_wave_kernel(
 #pragma unroll
             for (int k = 0; k < KMAX; ++k) {
                 if (srcs[k] >= 0) buf[n][k] = load_stream(eo + (long long)srcs[k] * NV + v);
-                else if (srcs[k] == -2) buf[n][k] = self[v];
+                else if (srcs[k] == kCopy) buf[n][k] = self[v];
             }
         }
     }
@@ -219,7 +130,7 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_wave_kernel(
             for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
 #pragma unroll
             for (int k = 0; k < KMAX; ++k)
-                if (srcs[k] != -1) Cio<8>::accumulate(buf[n][k], ws[k], acc);
+                if (srcs[k] != kNone) accumulate8(buf[n][k], ws[k], acc);
             store_stream(yr + v,
                          make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
                                     pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])));
@@ -258,19 +169,56 @@ hipError_t launch_wave(const Shape& sh, const void* eo, const int32_t* ids, cons
     return launch_wave_k<16>(sh, eo, ids, ei, w, erc, roff, mask, ori_x, y, stream);
 }
 
-template <int VEC, int KMAX>
-hipError_t launch_k(const Shape& sh, const void* expert_out, const int32_t* ids,
-                    const int32_t* expand_idx, const float* w, const int32_t* erc,
-                    const int64_t* roff, const uint8_t* mask, const void* ori_x, void* y,
-                    hipStream_t stream)
+constexpr int kElemThreads = 1024;
+constexpr int kElemPerLane = 8;      // H <= 8192 = 1024 lanes x 8
+
+template <int KMAX>
+__global__ __launch_bounds__(kElemThreads) void combine_elem_kernel(
+    const uint16_t* __restrict__ expert_out, const int32_t* __restrict__ ids,
+    const int32_t* __restrict__ expand_idx, const float* __restrict__ weights,
+    const int32_t* __restrict__ ep_recv_count, const int64_t* __restrict__ recv_offsets,
+    const uint8_t* __restrict__ mask, int mask_kind, const uint16_t* __restrict__ ori_x,
+    uint16_t* __restrict__ y, int W, int E, int L, int BS, int H, int K, int zero_end,
+    int id_end, long long cap)
 {
-    // one vector per lane when the row fits in one workgroup, else up to kVpt per lane
-    // (H <= 8192 always fits: 1024 lanes x 8 elements)
-    const int NV = sh.H / VEC;
-    const int want = (NV + kWave - 1) / kWave * kWave;
-    const int threads = want < kMaxThreads ? want : kMaxThreads;
-    const size_t tokens = (size_t)sh.W * sh.BS;
-    hipLaunchKernelGGL((combine_kernel<VEC, KMAX>), dim3((unsigned)tokens), dim3(threads), 0,
+    __shared__ int src_of[KMAX];
+    __shared__ float w_of[KMAX];
+    const long long tok = blockIdx.x;
+    const int s = (int)(tok / BS);
+    const int t = threadIdx.x;
+    if (t < K) {
+        src_of[t] = pick_source(ids, expand_idx, ep_recv_count, recv_offsets, mask, mask_kind,
+                                W, E, L, K, zero_end, id_end, cap, tok, s, t);
+        w_of[t] = weights[tok * K + t];
+    }
+    __syncthreads();
+    const uint16_t* self = ori_x ? ori_x + tok * H : nullptr;
+    uint16_t* yr = y + tok * H;
+#pragma unroll 1
+    for (int n = 0; n < kElemPerLane; ++n) {
+        const int h = t + n * blockDim.x;
+        if (h >= H) break;
+        float acc = 0.0f;
+        for (int k = 0; k < K; ++k) {
+            const int src = src_of[k];
+            if (src == kNone) continue;
+            const uint16_t b = src >= 0 ? expert_out[(long long)src * H + h] : self[h];
+            acc = acc + w_of[k] * bf16_lo(b);
+        }
+        yr[h] = (uint16_t)f32_to_bf16_rne(acc);
+    }
+}
+
+template <int KMAX>
+hipError_t launch_elem_k(const Shape& sh, const void* expert_out, const int32_t* ids,
+                         const int32_t* expand_idx, const float* w, const int32_t* erc,
+                         const int64_t* roff, const uint8_t* mask, const void* ori_x, void* y,
+                         hipStream_t stream)
+{
+    const int want = (sh.H + kWave - 1) / kWave * kWave;
+    const int threads = want < kElemThreads ? want : kElemThreads;
+    const long long T = (long long)sh.W * sh.BS;
+    hipLaunchKernelGGL((combine_elem_kernel<KMAX>), dim3((unsigned)T), dim3(threads), 0,
                        stream, static_cast<const uint16_t*>(expert_out), ids, expand_idx, w,
                        erc, roff, mask, sh.mask_kind, static_cast<const uint16_t*>(ori_x),
                        static_cast<uint16_t*>(y), sh.W, sh.E, sh.L, sh.BS, sh.H, sh.K,
@@ -278,15 +226,12 @@ hipError_t launch_k(const Shape& sh, const void* expert_out, const int32_t* ids,
     return hipGetLastError();
 }
 
-template <int VEC>
-hipError_t launch_vec(const Shape& sh, const void* eo, const int32_t* ids, const int32_t* ei,
-                      const float* w, const int32_t* erc, const int64_t* roff,
-                      const uint8_t* mask, const void* ori_x, void* y, hipStream_t stream)
+hipError_t launch_elem(const Shape& sh, const void* eo, const int32_t* ids, const int32_t* ei,
+                       const float* w, const int32_t* erc, const int64_t* roff,
+                       const uint8_t* mask, const void* ori_x, void* y, hipStream_t stream)
 {
-    if (sh.K <= 2) return launch_k<VEC, 2>(sh, eo, ids, ei, w, erc, roff, mask, ori_x, y, stream);
-    if (sh.K <= 4) return launch_k<VEC, 4>(sh, eo, ids, ei, w, erc, roff, mask, ori_x, y, stream);
-    if (sh.K <= 8) return launch_k<VEC, 8>(sh, eo, ids, ei, w, erc, roff, mask, ori_x, y, stream);
-    return launch_k<VEC, 16>(sh, eo, ids, ei, w, erc, roff, mask, ori_x, y, stream);
+    if (sh.K <= 4) return launch_elem_k<4>(sh, eo, ids, ei, w, erc, roff, mask, ori_x, y, stream);
+    return launch_elem_k<16>(sh, eo, ids, ei, w, erc, roff, mask, ori_x, y, stream);
 }
 
 }  // namespace
@@ -300,8 +245,8 @@ hipError_t launch_combine(const Shape& sh, const void* expert_out, const int32_t
     if (vectorized)
         return launch_wave(sh, expert_out, expert_ids, expand_idx, expert_scales, ep_recv_count,
                            recv_offsets, mask, ori_x, y, stream);
-    return launch_vec<1>(sh, expert_out, expert_ids, expand_idx, expert_scales, ep_recv_count,
-                         recv_offsets, mask, ori_x, y, stream);
+    return launch_elem(sh, expert_out, expert_ids, expand_idx, expert_scales, ep_recv_count,
+                       recv_offsets, mask, ori_x, y, stream);
 }
 
 }  // namespace moe_dc

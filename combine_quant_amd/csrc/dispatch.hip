@@ -22,73 +22,16 @@
 //   mode 4  per 32-element block: shared_exp = floor(log2 max|x|) - 8 (clamped at -127)
 //   mode 5  per block: shared_exp = ceil(log2(max(max|x|, 1e-4) / 448))
 //           codes = E4M3(x / 2^shared_exp); the stored scale is 2^shared_exp.
-// An MX block is 32 elements = 4 adjacent lanes of 8, reduced with two lane exchanges.
+// In the vectorized path an MX block is 32 elements = 4 adjacent lanes of 8, reduced with two
+// lane exchanges.
 //
 // The element-wise fallback (any H, any alignment) uses one workgroup per token with one
-// element per lane (scatter_kernel with VEC = 1).
+// element per lane (scatter_elem_kernel); an MX block is then 32 adjacent lanes.
 #include "dc_device.h"
 #include "dc_internal.h"
 
 namespace moe_dc {
 namespace {
-
-constexpr int kMaxThreads = 1024;
-constexpr int kVpt = 8;            // vectors per lane, upper bound
-
-template <int VEC> struct Io;
-
-template <> struct Io<8> {
-    using Raw = uint4;
-    using Codes = uint2;
-    static __device__ __forceinline__ Raw load(const uint16_t* p, int v)
-    {
-        return reinterpret_cast<const uint4*>(p)[v];
-    }
-    static __device__ __forceinline__ void store_raw(uint16_t* p, int v, Raw w)
-    {
-        reinterpret_cast<uint4*>(p)[v] = w;
-    }
-    static __device__ __forceinline__ void unpack(Raw w, float (&f)[8])
-    {
-        f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
-        f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z); f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
-    }
-    static __device__ __forceinline__ void smooth(const float* p, int v, float (&f)[8])
-    {
-        const float4 a = reinterpret_cast<const float4*>(p)[2 * v];
-        const float4 b = reinterpret_cast<const float4*>(p)[2 * v + 1];
-        f[0] = f[0] * a.x; f[1] = f[1] * a.y; f[2] = f[2] * a.z; f[3] = f[3] * a.w;
-        f[4] = f[4] * b.x; f[5] = f[5] * b.y; f[6] = f[6] * b.z; f[7] = f[7] * b.w;
-    }
-    static __device__ __forceinline__ Codes pack(const uint32_t (&c)[8])
-    {
-        return make_uint2((c[0] & 0xFF) | ((c[1] & 0xFF) << 8) | ((c[2] & 0xFF) << 16) |
-                              (c[3] << 24),
-                          (c[4] & 0xFF) | ((c[5] & 0xFF) << 8) | ((c[6] & 0xFF) << 16) |
-                              (c[7] << 24));
-    }
-    static __device__ __forceinline__ void store_codes(uint8_t* p, int v, Codes c)
-    {
-        reinterpret_cast<uint2*>(p)[v] = c;
-    }
-};
-
-template <> struct Io<1> {
-    using Raw = uint16_t;
-    using Codes = uint8_t;
-    static __device__ __forceinline__ Raw load(const uint16_t* p, int v) { return p[v]; }
-    static __device__ __forceinline__ void store_raw(uint16_t* p, int v, Raw w) { p[v] = w; }
-    static __device__ __forceinline__ void unpack(Raw w, float (&f)[1])
-    {
-        f[0] = __uint_as_float((uint32_t)w << 16);
-    }
-    static __device__ __forceinline__ void smooth(const float* p, int v, float (&f)[1])
-    {
-        f[0] = f[0] * p[v];
-    }
-    static __device__ __forceinline__ Codes pack(const uint32_t (&c)[1]) { return (uint8_t)c[0]; }
-    static __device__ __forceinline__ void store_codes(uint8_t* p, int v, Codes c) { p[v] = c; }
-};
 
 // int8 code of one element: round half to even, saturate to +-127, NaN (0 * inf) -> 0.
 __device__ __forceinline__ uint32_t int8_code(float f, float dyn)
@@ -120,170 +63,6 @@ __device__ __forceinline__ float pow2f(int e)
 {
     return e >= -126 ? __uint_as_float((uint32_t)(127 + e) << 23) : __uint_as_float(0x00400000u);
 }
-
-template <int MODE, int VEC, bool SMOOTH>
-__global__ __launch_bounds__(kMaxThreads) void scatter_kernel(
-    const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
-    const int32_t* __restrict__ expand_idx, const int32_t* __restrict__ seg,
-    const float* __restrict__ smooth, void* __restrict__ expand_x,
-    float* __restrict__ dyn_scales, int32_t* __restrict__ assist, int W, int E, int BS,
-    int H, int K, int ns, long long cap)
-{
-    using IO = Io<VEC>;
-    __shared__ long long row_of[kMaxK];
-    __shared__ int32_t exp_of[kMaxK];
-    __shared__ uint32_t red[kMaxThreads / kWave];
-
-    const size_t tok = blockIdx.x;
-    const int s = (int)(tok / BS);
-    const int i = (int)(tok - (size_t)s * BS);
-    const int t = threadIdx.x;
-    const int nt = blockDim.x;
-
-    if (t < K) {
-        const int32_t ord = expand_idx[tok * K + t];
-        const int32_t e = ids[tok * K + t];
-        long long row = -1;
-        if (ord >= 0 && e >= 0 && e < E) {
-            row = (long long)seg[(size_t)e * W + s] + ord;
-            if (row >= cap) row = -1;
-        }
-        row_of[t] = row;
-        exp_of[t] = e;
-        if (row >= 0) {
-            assist[row * 3 + 0] = s;
-            assist[row * 3 + 1] = i;
-            assist[row * 3 + 2] = t;
-        }
-    }
-    __syncthreads();
-    bool any = false;
-    for (int k = 0; k < K; ++k) any |= row_of[k] >= 0;
-    if (!any) return;
-
-    const int NV = H / VEC;
-    const uint16_t* xr = x + tok * (size_t)H;
-    typename IO::Raw raw[kVpt];
-#pragma unroll
-    for (int n = 0; n < kVpt; ++n) {
-        const int v = t + n * nt;
-        if (v < NV) raw[n] = IO::load(xr, v);
-    }
-
-    if (MODE == 0) {
-        uint16_t* out = reinterpret_cast<uint16_t*>(expand_x);
-        for (int k = 0; k < K; ++k) {
-            const long long row = row_of[k];
-            if (row < 0) continue;
-#pragma unroll
-            for (int n = 0; n < kVpt; ++n) {
-                const int v = t + n * nt;
-                if (v < NV) IO::store_raw(out + row * H, v, raw[n]);
-            }
-        }
-        return;
-    }
-
-    uint8_t* out = reinterpret_cast<uint8_t*>(expand_x);
-
-    if (MODE == 2) {
-        // Without smooth scales every pick carries the same codes, so one pass serves all K;
-        // with smooth scales each pick is quantized on its own expert's row.
-        const int passes = SMOOTH ? K : 1;
-        for (int pk = 0; pk < passes; ++pk) {
-            if (SMOOTH && row_of[pk] < 0) continue;
-            const float* sm = SMOOTH ? smooth + (size_t)exp_of[pk] * H : nullptr;
-            uint32_t amax = 0;
-#pragma unroll
-            for (int n = 0; n < kVpt; ++n) {
-                const int v = t + n * nt;
-                if (v < NV) {
-                    float f[VEC];
-                    IO::unpack(raw[n], f);
-                    if (SMOOTH) IO::smooth(sm, v, f);
-#pragma unroll
-                    for (int c = 0; c < VEC; ++c) {
-                        const uint32_t b = __float_as_uint(f[c]) & 0x7FFFFFFFu;
-                        amax = amax > b ? amax : b;
-                    }
-                }
-            }
-            amax = block_max_u32(amax, red);
-            const float dyn = 127.0f / __uint_as_float(amax);
-            const float scale = 1.0f / dyn;
-#pragma unroll
-            for (int n = 0; n < kVpt; ++n) {
-                const int v = t + n * nt;
-                if (v < NV) {
-                    float f[VEC];
-                    IO::unpack(raw[n], f);
-                    if (SMOOTH) IO::smooth(sm, v, f);
-                    uint32_t c[VEC];
-#pragma unroll
-                    for (int q = 0; q < VEC; ++q) c[q] = int8_code(f[q], dyn);
-                    const typename IO::Codes packed = IO::pack(c);
-                    if (SMOOTH) {
-                        IO::store_codes(out + row_of[pk] * H, v, packed);
-                    } else {
-                        for (int k = 0; k < K; ++k)
-                            if (row_of[k] >= 0) IO::store_codes(out + row_of[k] * H, v, packed);
-                    }
-                }
-            }
-            if (t == 0) {
-                if (SMOOTH) {
-                    dyn_scales[row_of[pk]] = scale;
-                } else {
-                    for (int k = 0; k < K; ++k)
-                        if (row_of[k] >= 0) dyn_scales[row_of[k]] = scale;
-                }
-            }
-        }
-        return;
-    }
-
-    // MX modes 4 and 5
-    constexpr int kLanesPerBlock = kMxBlock / VEC;
-    const int nb = (H + kMxBlock - 1) / kMxBlock;
-#pragma unroll
-    for (int n = 0; n < kVpt; ++n) {
-        const int v = t + n * nt;
-        if (n * nt >= NV) break;          // uniform across the workgroup
-        float f[VEC];
-        uint32_t amax = 0;
-        if (v < NV) {
-            IO::unpack(raw[n], f);
-#pragma unroll
-            for (int c = 0; c < VEC; ++c) {
-                const uint32_t b = __float_as_uint(f[c]) & 0x7FFFFFFFu;
-                amax = amax > b ? amax : b;
-            }
-        }
-        amax = group_max_u32<kLanesPerBlock>(amax);
-        if (v < NV) {
-            const int se = mx_shared_exp<MODE>(amax);
-            const float inv = __uint_as_float((uint32_t)(127 - se) << 23);   // 2^-se, exact
-            uint32_t c[VEC];
-#pragma unroll
-            for (int q = 0; q < VEC; ++q) c[q] = e4m3_code(f[q] * inv);
-            const typename IO::Codes packed = IO::pack(c);
-            const bool lead = (v % kLanesPerBlock) == 0;
-            const float scale = pow2f(se);
-            const int blk = v / kLanesPerBlock;
-            for (int k = 0; k < K; ++k) {
-                const long long row = row_of[k];
-                if (row < 0) continue;
-                IO::store_codes(out + row * H, v, packed);
-                if (lead) dyn_scales[row * ns + blk] = scale;
-            }
-        }
-    }
-    if (t == 0 && ns > nb) {
-        for (int k = 0; k < K; ++k)
-            if (row_of[k] >= 0) dyn_scales[row_of[k] * ns + nb] = 0.0f;
-    }
-}
-
 
 // ---------------------------------------------------------------------------------------
 // vectorized path: one workgroup per token, kTileSlots 64-vector slots per wave
@@ -612,43 +391,190 @@ hipError_t launch_tile(const Shape& sh, const void* x, const int32_t* ids,
     }
 }
 
-template <int MODE, int VEC, bool SMOOTH>
-hipError_t launch_mode(const Shape& sh, const void* x, const int32_t* ids,
-                       const int32_t* expand_idx, const int32_t* seg, const float* smooth,
-                       void* expand_x, float* dyn_scales, int32_t* assist, hipStream_t stream)
+// ---------------------------------------------------------------------------------------
+// element-wise fallback: one workgroup per token, one element per lane
+// ---------------------------------------------------------------------------------------
+
+constexpr int kElemThreads = 1024;
+constexpr int kElemPerLane = 8;      // H <= 8192 = 1024 lanes x 8
+
+template <int MODE, bool SMOOTH>
+__global__ __launch_bounds__(kElemThreads) void scatter_elem_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
+    const int32_t* __restrict__ expand_idx, const int32_t* __restrict__ seg,
+    const float* __restrict__ smooth, void* __restrict__ expand_x,
+    float* __restrict__ dyn_scales, int32_t* __restrict__ assist, int W, int E, int BS,
+    int H, int K, int ns, long long cap)
 {
-    const int NV = sh.H / VEC;
-    int waves = (NV + kWave * kVpt - 1) / (kWave * kVpt);
-    if (waves < 1) waves = 1;
-    const int threads = waves * kWave;
-    const size_t tokens = (size_t)sh.W * sh.BS;
-    hipLaunchKernelGGL((scatter_kernel<MODE, VEC, SMOOTH>), dim3((unsigned)tokens),
-                       dim3(threads), 0, stream, static_cast<const uint16_t*>(x), ids,
-                       expand_idx, seg, smooth, expand_x, dyn_scales, assist, sh.W, sh.E, sh.BS,
-                       sh.H, sh.K, sh.scales_per_row, (long long)sh.cap);
+    __shared__ long long row_of[kMaxK];
+    __shared__ int32_t exp_of[kMaxK];
+    __shared__ uint32_t red[kElemThreads / kWave];
+
+    const long long tok = blockIdx.x;
+    const int s = (int)(tok / BS);
+    const int i = (int)(tok - (long long)s * BS);
+    const int t = threadIdx.x;
+    const int nt = blockDim.x;
+
+    if (t < K) {
+        const int32_t ord = expand_idx[tok * K + t];
+        const int32_t e = ids[tok * K + t];
+        long long row = -1;
+        if (ord >= 0 && e >= 0 && e < E) {
+            row = (long long)seg[(long long)e * W + s] + ord;
+            if (row >= cap) row = -1;
+        }
+        row_of[t] = row;
+        exp_of[t] = e;
+        if (row >= 0) {
+            assist[row * 3 + 0] = s;
+            assist[row * 3 + 1] = i;
+            assist[row * 3 + 2] = t;
+        }
+    }
+    __syncthreads();
+    bool any = false;
+    for (int k = 0; k < K; ++k) any |= row_of[k] >= 0;
+    if (!any) return;
+
+    const uint16_t* xr = x + tok * H;
+    uint16_t raw[kElemPerLane];
+#pragma unroll
+    for (int n = 0; n < kElemPerLane; ++n) {
+        const int h = t + n * nt;
+        if (h < H) raw[n] = xr[h];
+    }
+
+    if (MODE == 0) {
+        uint16_t* out = reinterpret_cast<uint16_t*>(expand_x);
+        for (int k = 0; k < K; ++k) {
+            const long long row = row_of[k];
+            if (row < 0) continue;
+#pragma unroll
+            for (int n = 0; n < kElemPerLane; ++n) {
+                const int h = t + n * nt;
+                if (h < H) out[row * H + h] = raw[n];
+            }
+        }
+        return;
+    }
+
+    uint8_t* out = reinterpret_cast<uint8_t*>(expand_x);
+
+    if (MODE == 2) {
+        // Without smooth scales every pick carries the same codes, so one pass serves all K;
+        // with smooth scales each pick is quantized on its own expert's row.
+        const int passes = SMOOTH ? K : 1;
+        for (int pk = 0; pk < passes; ++pk) {
+            if (SMOOTH && row_of[pk] < 0) continue;        // uniform over the workgroup
+            const float* sm = SMOOTH ? smooth + (long long)exp_of[pk] * H : nullptr;
+            uint32_t amax = 0;
+#pragma unroll
+            for (int n = 0; n < kElemPerLane; ++n) {
+                const int h = t + n * nt;
+                if (h < H) {
+                    float f = bf16_lo(raw[n]);
+                    if (SMOOTH) f = f * sm[h];
+                    const uint32_t b = __float_as_uint(f) & 0x7FFFFFFFu;
+                    amax = amax > b ? amax : b;
+                }
+            }
+            amax = block_max_u32(amax, red);
+            const float dyn = 127.0f / __uint_as_float(amax);
+#pragma unroll
+            for (int n = 0; n < kElemPerLane; ++n) {
+                const int h = t + n * nt;
+                if (h >= H) continue;
+                float f = bf16_lo(raw[n]);
+                if (SMOOTH) f = f * sm[h];
+                const uint8_t c = (uint8_t)int8_code(f, dyn);
+                if (SMOOTH) {
+                    out[row_of[pk] * H + h] = c;
+                } else {
+                    for (int k = 0; k < K; ++k)
+                        if (row_of[k] >= 0) out[row_of[k] * H + h] = c;
+                }
+            }
+            if (t == 0) {
+                const float scale = 1.0f / dyn;
+                if (SMOOTH) {
+                    dyn_scales[row_of[pk]] = scale;
+                } else {
+                    for (int k = 0; k < K; ++k)
+                        if (row_of[k] >= 0) dyn_scales[row_of[k]] = scale;
+                }
+            }
+        }
+        return;
+    }
+
+    // MX modes 4 and 5: a 32-element block is 32 adjacent lanes
+    const int nb = (H + kMxBlock - 1) / kMxBlock;
+#pragma unroll
+    for (int n = 0; n < kElemPerLane; ++n) {
+        const int h = t + n * nt;
+        if (n * nt >= H) break;                            // uniform across the workgroup
+        float f = 0.0f;
+        uint32_t amax = 0;
+        if (h < H) {
+            f = bf16_lo(raw[n]);
+            amax = __float_as_uint(f) & 0x7FFFFFFFu;
+        }
+        amax = group_max_u32<kMxBlock>(amax);
+        if (h >= H) continue;
+        const int se = mx_shared_exp<MODE>(amax);
+        const float inv = __uint_as_float((uint32_t)(127 - se) << 23);       // 2^-se, exact
+        const uint8_t c = (uint8_t)e4m3_code(f * inv);
+        const bool lead = (h % kMxBlock) == 0;
+        const float scale = pow2f(se);
+        for (int k = 0; k < K; ++k) {
+            const long long row = row_of[k];
+            if (row < 0) continue;
+            out[row * H + h] = c;
+            if (lead) dyn_scales[row * ns + h / kMxBlock] = scale;
+        }
+    }
+    if (t == 0 && ns > nb) {
+        for (int k = 0; k < K; ++k)
+            if (row_of[k] >= 0) dyn_scales[row_of[k] * ns + nb] = 0.0f;
+    }
+}
+
+template <int MODE, bool SMOOTH>
+hipError_t launch_elem_mode(const Shape& sh, const void* x, const int32_t* ids,
+                            const int32_t* expand_idx, const int32_t* seg, const float* smooth,
+                            void* expand_x, float* dyn_scales, int32_t* assist,
+                            hipStream_t stream)
+{
+    const long long T = (long long)sh.W * sh.BS;
+    const int want = (sh.H + kWave - 1) / kWave * kWave;
+    const int threads = want < kElemThreads ? want : kElemThreads;
+    hipLaunchKernelGGL((scatter_elem_kernel<MODE, SMOOTH>), dim3((unsigned)T), dim3(threads),
+                       0, stream, static_cast<const uint16_t*>(x), ids, expand_idx, seg, smooth,
+                       expand_x, dyn_scales, assist, sh.W, sh.E, sh.BS, sh.H, sh.K,
+                       sh.scales_per_row, (long long)sh.cap);
     return hipGetLastError();
 }
 
-template <int VEC>
-hipError_t launch_vec(const Shape& sh, const void* x, const int32_t* ids,
-                      const int32_t* expand_idx, const int32_t* seg, const float* smooth,
-                      void* expand_x, float* dyn_scales, int32_t* assist, hipStream_t stream)
+hipError_t launch_elem(const Shape& sh, const void* x, const int32_t* ids,
+                       const int32_t* expand_idx, const int32_t* seg, const float* smooth,
+                       void* expand_x, float* dyn_scales, int32_t* assist, hipStream_t stream)
 {
     switch (sh.quant_mode) {
     case 0:
-        return launch_mode<0, VEC, false>(sh, x, ids, expand_idx, seg, smooth, expand_x,
+        return launch_elem_mode<0, false>(sh, x, ids, expand_idx, seg, smooth, expand_x,
                                           dyn_scales, assist, stream);
     case 2:
         if (smooth)
-            return launch_mode<2, VEC, true>(sh, x, ids, expand_idx, seg, smooth, expand_x,
+            return launch_elem_mode<2, true>(sh, x, ids, expand_idx, seg, smooth, expand_x,
                                              dyn_scales, assist, stream);
-        return launch_mode<2, VEC, false>(sh, x, ids, expand_idx, seg, smooth, expand_x,
+        return launch_elem_mode<2, false>(sh, x, ids, expand_idx, seg, smooth, expand_x,
                                           dyn_scales, assist, stream);
     case 4:
-        return launch_mode<4, VEC, false>(sh, x, ids, expand_idx, seg, smooth, expand_x,
+        return launch_elem_mode<4, false>(sh, x, ids, expand_idx, seg, smooth, expand_x,
                                           dyn_scales, assist, stream);
     case 5:
-        return launch_mode<5, VEC, false>(sh, x, ids, expand_idx, seg, smooth, expand_x,
+        return launch_elem_mode<5, false>(sh, x, ids, expand_idx, seg, smooth, expand_x,
                                           dyn_scales, assist, stream);
     default:
         return hipErrorInvalidValue;
@@ -665,8 +591,8 @@ hipError_t launch_scatter(const Shape& sh, const void* x, const int32_t* expert_
     if (vectorized)
         return launch_tile(sh, x, expert_ids, expand_idx, seg, smooth, expand_x,
                            dynamic_scales, assist_info, stream);
-    return launch_vec<1>(sh, x, expert_ids, expand_idx, seg, smooth, expand_x, dynamic_scales,
-                         assist_info, stream);
+    return launch_elem(sh, x, expert_ids, expand_idx, seg, smooth, expand_x, dynamic_scales,
+                       assist_info, stream);
 }
 
 }  // namespace moe_dc
