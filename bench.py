@@ -71,7 +71,7 @@ def algorithmic_bytes(wl, inp, routed_rows, copy_picks, active_tokens):
     b = 2 if wl.quant_mode == 0 else 1
     S = {0: 0, 2: 4}.get(wl.quant_mode, 4 * mx_scales_per_row(H))
     m = 0 if inp.get("mask") is None else inp["mask"].nbytes
-    smooth = 0 if inp.get("smooth") is None else inp["smooth"].nbytes
+    smooth = 0 if inp.get("scales") is None else inp["scales"].nbytes
     P = routed_rows
     dispatch = (2 * H * active_tokens + 4 * T * K + m + smooth + P * (b * H + S + 12)
                 + 4 * T * K + 4 * E * W + 8 * E + 8 * (W + 1))
@@ -120,7 +120,7 @@ def cpu_baseline(wl, inp, expert_out_host, passes):
     try:
         for _ in range(passes):
             t0 = time.perf_counter()
-            d = oracle.dispatch(cfg, inp["x"], inp["expert_ids"], smooth=inp.get("smooth"),
+            d = oracle.dispatch(cfg, inp["x"], inp["expert_ids"], scales=inp.get("scales"),
                                 mask=inp.get("mask"))
             oracle.combine(cfg, expert_out_host, inp["expert_ids"], d["expand_idx"],
                            inp["expert_scales"], d["ep_recv_count"], d["recv_offsets"],
@@ -173,7 +173,7 @@ def run_bench(args):
 
     ids = dev_t(inp["expert_ids"])
     mask = dev_t(inp.get("mask"))
-    smooth = dev_t(inp.get("smooth"))
+    smooth = dev_t(inp.get("scales"))
     w = dev_t(inp["expert_scales"])
     sets = []
     for k in range(args.sets):

@@ -20,7 +20,10 @@ _lib = None
 class OracleCfg(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "W", "E", "BS", "H", "K", "quant_mode", "zero_expert_num", "copy_expert_num",
-        "expert_token_nums_type", "mask_kind")]
+        "expert_token_nums_type", "mask_kind", "out_dtype", "scales_kind", "scale_format")]
+
+# element types of expand_x (out_dtype values; 0 selects the quant mode's default)
+CODE_BF16, CODE_INT8, CODE_E4M3, CODE_E5M2 = 0, 1, 2, 3
 
 
 def _load():
@@ -37,7 +40,14 @@ def _load():
             "oracle_f32_to_bf16": (u16, [f32]),
             "oracle_e4m3_from_f32": (u8, [f32]),
             "oracle_e4m3_to_f32": (f32, [u8]),
+            "oracle_e5m2_from_f32": (u8, [f32]),
+            "oracle_e5m2_to_f32": (f32, [u8]),
+            "oracle_int8_from_f32": (ctypes.c_int8, [f32]),
+            "oracle_e8m0_from_scale": (u8, [f32]),
             "oracle_mx_scale_count": (i32, [i32]),
+            "oracle_code_type": (i32, [i32, i32]),
+            "oracle_scale_count": (i32, [i32, i32]),
+            "oracle_quant_row": (i32, [i32, i32, P, P, i32, i32, P, P]),
             "oracle_quant_int8_row": (None, [P, P, i32, P, P]),
             "oracle_quant_mx_row": (None, [P, i32, i32, P, P]),
             "oracle_route": (i32, [P, P, P, P, P]),
@@ -65,9 +75,10 @@ def _c(a, dtype):
 
 
 def make_cfg(W, E, BS, H, K, quant_mode=0, zero_expert_num=0, copy_expert_num=0,
-             expert_token_nums_type=1, mask_kind=0):
+             expert_token_nums_type=1, mask_kind=0, out_dtype=0, scales_kind=0,
+             scale_format=0):
     return OracleCfg(W, E, BS, H, K, quant_mode, zero_expert_num, copy_expert_num,
-                     expert_token_nums_type, mask_kind)
+                     expert_token_nums_type, mask_kind, out_dtype, scales_kind, scale_format)
 
 
 def _ref(cfg):
@@ -92,8 +103,36 @@ def e4m3_to_f32(code):
     return _load().oracle_e4m3_to_f32(int(code))
 
 
+def e5m2_from_f32(v):
+    return _load().oracle_e5m2_from_f32(float(v))
+
+
+def e5m2_to_f32(code):
+    return _load().oracle_e5m2_to_f32(int(code))
+
+
+def int8_from_f32(v):
+    return _load().oracle_int8_from_f32(float(v))
+
+
+def e8m0_from_scale(s):
+    return _load().oracle_e8m0_from_scale(float(s))
+
+
 def mx_scale_count(H):
     return _load().oracle_mx_scale_count(int(H))
+
+
+def code_type(quant_mode, out_dtype=0):
+    return _load().oracle_code_type(int(quant_mode), int(out_dtype))
+
+
+def scale_count(quant_mode, H):
+    return _load().oracle_scale_count(int(quant_mode), int(H))
+
+
+def code_np_dtype(ct):
+    return {CODE_BF16: np.uint16, CODE_INT8: np.int8}.get(ct, np.uint8)
 
 
 # -- rows ----------------------------------------------------------------------------------
@@ -115,6 +154,22 @@ def quant_mx_row(x_bf16, clip):
     scales = np.empty(mx_scale_count(H), np.float32)
     _load().oracle_quant_mx_row(_p(x), H, 1 if clip else 0, _p(codes), _p(scales))
     return codes, scales
+
+
+def quant_row(quant_mode, x_bf16, pre=None, out_dtype=0):
+    """Quantize one row; pre is None, a 1-element array (scalar) or an H-element row.
+    Returns (codes, scales) with codes int8 for the int8 type, else uint8."""
+    x = _c(x_bf16, np.uint16)
+    H = x.shape[0]
+    ct = code_type(quant_mode, out_dtype)
+    pr = _c(pre, np.float32)
+    codes = np.empty(H, code_np_dtype(ct))
+    scales = np.empty(max(1, scale_count(quant_mode, H)), np.float32)
+    rc = _load().oracle_quant_row(int(quant_mode), ct, _p(x), _p(pr),
+                                  0 if pr is None else pr.shape[0], H, _p(codes), _p(scales))
+    if rc != 0:
+        raise ValueError(f"oracle_quant_row rejected the arguments (rc={rc})")
+    return codes, scales[:scale_count(quant_mode, H)]
 
 
 # -- routing -------------------------------------------------------------------------------
@@ -146,24 +201,23 @@ def dest_row(cfg, ep_recv_count, recv_offsets, s, e, ordinal):
     return _load().oracle_dest_row(_ref(cfg), _p(erc), _p(off), int(s), int(e), int(ordinal))
 
 
-def dispatch(cfg, x, expert_ids, smooth=None, mask=None, cap=None):
-    """Whole dispatch.  Returns a dict of numpy arrays; rows of expand_x / dynamic_scales /
-    assist_info past recv_offsets[W] are left zero."""
+def dispatch(cfg, x, expert_ids, scales=None, mask=None, cap=None):
+    """Whole dispatch.  `scales` is the quantization scales tensor of cfg.scales_kind (a
+    1-element array, an [H] row or an [E][H] table).  Returns a dict of numpy arrays; rows of
+    expand_x / dynamic_scales / assist_info past recv_offsets[W] are left zero."""
     W, BS, H, K, L = cfg.W, cfg.BS, cfg.H, cfg.K, cfg.E // cfg.W
     x = _c(x, np.uint16)
     ids = _c(expert_ids, np.int32)
-    sm = _c(smooth, np.float32)
+    sm = _c(scales, np.float32)
     m = _c(mask, np.uint8)
     cap = W * BS * K if cap is None else cap
-    if cfg.quant_mode == 0:
-        ex = np.zeros((cap, H), np.uint16)
-        ds = np.zeros(1, np.float32)
-    elif cfg.quant_mode == 2:
-        ex = np.zeros((cap, H), np.int8)
-        ds = np.zeros(cap, np.float32)
-    else:
-        ex = np.zeros((cap, H), np.uint8)
-        ds = np.zeros((cap, mx_scale_count(H)), np.float32)
+    ct = code_type(cfg.quant_mode, cfg.out_dtype)
+    if ct < 0:
+        raise ValueError("quant_mode and out_dtype do not go together")
+    ns = scale_count(cfg.quant_mode, H)
+    ex = np.zeros((cap, H), code_np_dtype(ct))
+    sdt = np.uint8 if cfg.scale_format == 1 else np.float32
+    ds = np.zeros(1, sdt) if ns == 0 else np.zeros((cap,) if ns == 1 else (cap, ns), sdt)
     eidx = np.empty((W, BS, K), np.int32)
     ai = np.zeros((cap, 3), np.int32)
     erc = np.empty((W, L * W), np.int32)
@@ -176,7 +230,7 @@ def dispatch(cfg, x, expert_ids, smooth=None, mask=None, cap=None):
         raise ValueError(f"oracle_dispatch rejected the input (rc={rc})")
     out = dict(expand_x=ex, expand_idx=eidx, assist_info=ai, ep_recv_count=erc,
                expert_token_nums=etn, recv_offsets=off, cnt=cnt)
-    if cfg.quant_mode != 0:
+    if ns != 0:
         out["dynamic_scales"] = ds
     return out
 

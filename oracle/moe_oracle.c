@@ -7,8 +7,8 @@
  * nearest-even, in the order written.
  *
  * Every function restates what the pages define, in the pages' order.  Where a page is
- * silent or garbled the reading taken is named inline (R1..R12) and listed with its reason
- * in the design notes of the repository.
+ * silent or garbled the reading taken is named inline (R1, R2, ...) and listed with its
+ * reason in the design notes of the repository.
  */
 #include "moe_oracle.h"
 
@@ -96,6 +96,80 @@ uint8_t oracle_e4m3_from_f32(float v)
     return (uint8_t)(sign | code);
 }
 
+/* OCP E5M2: 1 sign, 5 exponent (bias 15), 2 mantissa bits, laid out like an IEEE binary
+ * format: exponent field 31 holds the infinities (mantissa 0) and NaNs.  The largest finite
+ * magnitude is 1.75 * 2^15 = 57344, the smallest normal 2^-14, and the subnormals are
+ * m * 2^-16 for m = 1..3. */
+float oracle_e5m2_to_f32(uint8_t code)
+{
+    int sign = code & 0x80;
+    int ex = (code >> 2) & 0x1F;
+    int m = code & 0x3;
+    double v;
+    if (ex == 0x1F) {
+        if (m != 0) return NAN;
+        return sign ? -INFINITY : INFINITY;
+    }
+    if (ex == 0) v = ldexp((double)m, -16);
+    else v = ldexp(1.0 + m / 4.0, ex - 15);
+    return (float)(sign ? -v : v);
+}
+
+/* Round a binary32 value to the nearest E5M2 value, ties to the even code.  Magnitudes at
+ * or above 57344 saturate to 57344 (reading R6 again: a saturating cast, so no code is ever
+ * infinite); NaN gives the NaN code; the sign is kept.  Same method as the E4M3 encoder:
+ * the E5M2 spacing in the binade of |v| is 2^(floor(log2|v|) - 2), and 2^-16 all through
+ * the subnormal range below 2^-14. */
+uint8_t oracle_e5m2_from_f32(float v)
+{
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    if (isnan(v)) return (uint8_t)(sign | 0x7F);
+    double a = fabs((double)v);
+    if (a >= 57344.0) return (uint8_t)(sign | 0x7B);
+    double quantum;
+    if (a < ldexp(1.0, -14)) {
+        quantum = ldexp(1.0, -16);
+    } else {
+        int ex;
+        frexp(a, &ex);               /* floor(log2 a) = ex - 1 */
+        quantum = ldexp(1.0, (ex - 1) - 2);
+    }
+    double n = nearbyint(a / quantum);
+    double r = n * quantum;          /* representable, <= 57344 because a < 57344 */
+    uint8_t code;
+    if (r < ldexp(1.0, -14)) {
+        code = (uint8_t)(r / ldexp(1.0, -16));         /* 0..4; 4 is exactly 2^-14 = 0x04 */
+    } else {
+        int ex;
+        double m = frexp(r, &ex);
+        int e2 = ex - 1;
+        int mant = (int)((2.0 * m - 1.0) * 4.0);       /* exact: 2m has 2 fraction bits */
+        code = (uint8_t)(((e2 + 15) << 2) | mant);
+    }
+    return (uint8_t)(sign | code);
+}
+
+/* The int8 cast of every int8 mode (readings R4, R5; reading R22: the static mode 1 uses the
+ * same cast): round half to even, saturate to [-127, 127], NaN -> 0. */
+int8_t oracle_int8_from_f32(float v)
+{
+    if (isnan(v)) return 0;
+    float r = nearbyintf(v);
+    if (r > 127.0f) r = 127.0f;
+    if (r < -127.0f) r = -127.0f;
+    return (int8_t)r;
+}
+
+/* E8M0 byte of a power-of-two scale 2^e with e in [-127, 127]: the biased exponent e + 127
+ * (the MX scale format; [SMP] 通信前量化 stores the MX shared-exponent scale as an E8M0 value
+ * next to the fp8 codes).  frexpf handles the subnormal 2^-127 exactly: byte 0. */
+uint8_t oracle_e8m0_from_scale(float s)
+{
+    int ex;
+    frexpf(s, &ex);                  /* s = 0.5 * 2^ex */
+    return (uint8_t)((ex - 1) + 127);
+}
+
 /* MX scales per row: one per 32-element block, padded to an even count (Align2 of
  * Ceil(H, 32)) as the dynamic_scales shape rule for quant modes 4/5 states ([LLD] 约束说明). */
 int32_t oracle_mx_scale_count(int32_t H)
@@ -104,44 +178,88 @@ int32_t oracle_mx_scale_count(int32_t H)
     return nb + (nb & 1);
 }
 
+/* Element type of expand_x for a quant mode and a requested out_dtype (0 = the mode's
+ * default).  [LLD] 约束说明 lists the allowed output types per mode: mode 0 keeps the input
+ * type; mode 1 int8; mode 2 int8, E4M3 or E5M2; mode 3 E4M3 or E5M2; modes 4/5 E4M3 or
+ * E5M2 (also fp4 and hifloat8 types there, not covered).  -1 for any other pairing. */
+int32_t oracle_code_type(int32_t quant_mode, int32_t out_dtype)
+{
+    switch (quant_mode) {
+    case 0:
+        return out_dtype == 0 ? ORACLE_CODE_BF16 : -1;
+    case 1:
+        return (out_dtype == 0 || out_dtype == ORACLE_CODE_INT8) ? ORACLE_CODE_INT8 : -1;
+    case 2:
+        if (out_dtype == 0) return ORACLE_CODE_INT8;
+        return (out_dtype == ORACLE_CODE_INT8 || out_dtype == ORACLE_CODE_E4M3 ||
+                out_dtype == ORACLE_CODE_E5M2) ? out_dtype : -1;
+    case 3:
+    case 4:
+    case 5:
+        if (out_dtype == 0) return ORACLE_CODE_E4M3;
+        return (out_dtype == ORACLE_CODE_E4M3 || out_dtype == ORACLE_CODE_E5M2) ? out_dtype
+                                                                                : -1;
+    default:
+        return -1;
+    }
+}
+
+/* Scales per expand_x row ([LLD] 约束说明, dynamic_scales shapes): none for modes 0 and 1,
+ * one for mode 2, Ceil(H, 128) for mode 3, Align2(Ceil(H, 32)) for modes 4/5. */
+int32_t oracle_scale_count(int32_t quant_mode, int32_t H)
+{
+    switch (quant_mode) {
+    case 2: return 1;
+    case 3: return (H + 127) / 128;
+    case 4:
+    case 5: return oracle_mx_scale_count(H);
+    default: return 0;
+    }
+}
+
 /* ------------------------------------------------------------------------------------- */
 /* quantization                                                                          */
 /* ------------------------------------------------------------------------------------- */
 
-/* Per-token dynamic int8 quantization, quant_mode 2 ([OPS] 功能说明 情形 2; [LLD] 计算公式,
- * quant_mode=2):
- *   x_fp32 = CastToFp32(x), times the smooth-scale row if one is given
- *   dyn    = 127 / max|x_fp32|           (127 is int8's largest value)
- *   q      = CastToInt8(x_fp32 * dyn)
- *   scale  = 1.0 / dyn                   (sent with the row; dequant is q * scale)
- * Reading R4: the int8 cast rounds half to even.  Reading R5: the cast saturates to
- * [-127, 127] and maps NaN to 0; with an all-zero row dyn = 127/0 = +inf, every product is
- * 0*inf = NaN -> 0, and scale = 1/inf = 0. */
-void oracle_quant_int8_row(const uint16_t* x, const float* smooth_or_null, int32_t H,
-                           int8_t* q, float* scale)
+/* Largest finite magnitude of a code type: the dst_type_max of the dynamic formulas and the
+ * fp8_max of the clip variant. */
+static float code_max(int32_t ct)
 {
-    float* f = (float*)malloc((size_t)H * sizeof(float));
-    for (int32_t h = 0; h < H; ++h) {
-        f[h] = oracle_bf16_to_f32(x[h]);
-        if (smooth_or_null) f[h] = f[h] * smooth_or_null[h];
-    }
+    return ct == ORACLE_CODE_INT8 ? 127.0f : ct == ORACLE_CODE_E4M3 ? 448.0f : 57344.0f;
+}
+
+/* emax of an fp8 element type: the exponent of its largest power of two (E4M3 2^8 = 256,
+ * E5M2 2^15), used by the MX shared exponent. */
+static int code_emax(int32_t ct)
+{
+    return ct == ORACLE_CODE_E4M3 ? 8 : 15;
+}
+
+static uint8_t encode(int32_t ct, float v)
+{
+    if (ct == ORACLE_CODE_INT8) return (uint8_t)oracle_int8_from_f32(v);
+    if (ct == ORACLE_CODE_E4M3) return oracle_e4m3_from_f32(v);
+    return oracle_e5m2_from_f32(v);
+}
+
+/* One dynamic-scale segment [h0, h1) of the fp32 row f ([LLD] 计算公式, quant_mode 2 over the
+ * whole token and quant_mode 3 over each group; [OPS] 功能说明 情形 2):
+ *   dyn   = dst_type_max / max|f| over the segment
+ *   q     = Cast(f * dyn, dst type)
+ *   scale = 1.0 / dyn
+ * An all-zero segment gives dyn = +inf and products 0 * inf = NaN; every NaN product is
+ * encoded as 0 (reading R21: R5 taken for the fp8 types too), and its scale is 1/inf = 0. */
+static float quant_dynamic(int32_t ct, const float* f, int32_t h0, int32_t h1, uint8_t* q)
+{
     float amax = 0.0f;
-    for (int32_t h = 0; h < H; ++h)
+    for (int32_t h = h0; h < h1; ++h)
         if (fabsf(f[h]) > amax) amax = fabsf(f[h]);
-    float dyn = 127.0f / amax;
-    for (int32_t h = 0; h < H; ++h) {
+    float dyn = code_max(ct) / amax;
+    for (int32_t h = h0; h < h1; ++h) {
         float v = f[h] * dyn;
-        float r;
-        if (isnan(v)) r = 0.0f;
-        else {
-            r = nearbyintf(v);
-            if (r > 127.0f) r = 127.0f;
-            if (r < -127.0f) r = -127.0f;
-        }
-        q[h] = (int8_t)r;
+        q[h] = isnan(v) ? 0 : encode(ct, v);
     }
-    *scale = 1.0f / dyn;
-    free(f);
+    return 1.0f / dyn;
 }
 
 /* floor(log2(a)) for a finite a > 0, exactly: frexpf gives a = m * 2^ex with m in [0.5,1). */
@@ -152,51 +270,105 @@ static int ilog2_floor(float a)
     return ex - 1;
 }
 
-/* MX quantization of one row, in blocks of 32 elements (the last block may be short).
+/* One MX block [h0, h1) (32 elements, the last one may be short).
  * quant_mode 4 ([LLD] 计算公式, quant_mode=4; [OPS] 接口级量化模式扩展):
- *   shared_exp = floor(log2(max|x| over the block)) - emax,  emax = 8 for E4M3
- *   q = Cast(x / 2^shared_exp, e4m3)
+ *   shared_exp = floor(log2(max|x| over the block)) - emax   (emax 8 for E4M3, 15 for E5M2)
+ *   q = Cast(x / 2^shared_exp, fp8)
  * Reading R7: max(x) is the block's absolute maximum.  Reading R8: an all-zero block takes
  * shared_exp = -127, and shared_exp is clamped below at -127 (the E8M0 range).
  * quant_mode 5, the clip variant ([LLD] 计算公式, quant_mode=5):
- *   max_abs_clamp = max(max|x|, 1e-4);  shared_exp = ceil(log2(max_abs_clamp / 448))
- *   q = CastToFp8(x / 2^shared_exp)
- * Reading R9: max_abs_clamp / 448 is one fp32 division and its ceil(log2) is taken exactly.
- * Reading R10: the scale written for each block is 2^shared_exp, the dequant multiplier
- * (codes * scale ~ x).  Pad entries of the Align2 layout are 0. */
+ *   max_abs_clamp = max(max|x|, 1e-4);  shared_exp = ceil(log2(max_abs_clamp / fp8_max))
+ *   q = CastToFp8(x / 2^shared_exp)     (fp8_max 448 for E4M3, 57344 for E5M2)
+ * Reading R9: max_abs_clamp / fp8_max is one fp32 division and its ceil(log2) is exact.
+ * Reading R10: the block's scale is 2^shared_exp, the dequant multiplier (codes * scale ~ x). */
+static float quant_mx_block(int32_t ct, int32_t clip, const float* f, int32_t h0, int32_t h1,
+                            uint8_t* q)
+{
+    float amax = 0.0f;
+    for (int32_t h = h0; h < h1; ++h)
+        if (fabsf(f[h]) > amax) amax = fabsf(f[h]);
+    int se;
+    if (!clip) {
+        if (amax == 0.0f) se = -127;
+        else se = ilog2_floor(amax) - code_emax(ct);
+        if (se < -127) se = -127;
+    } else {
+        float c = amax > 1e-4f ? amax : 1e-4f;
+        float v = c / code_max(ct);
+        int ex;
+        float m = frexpf(v, &ex);    /* v = m * 2^ex; v is a power of two iff m == 0.5 */
+        se = (m == 0.5f) ? ex - 1 : ex;
+    }
+    float sc = ldexpf(1.0f, se);     /* 2^-127 is a binary32 subnormal: exact */
+    for (int32_t h = h0; h < h1; ++h) q[h] = encode(ct, f[h] / sc);
+    return sc;
+}
+
+/* Quantize one token row x (bf16 [H]) for a quant mode and code type, after multiplying it
+ * by `pre` when given: pre_len 1 = one scalar for every element, pre_len H = one value per
+ * element, 0 = no multiplier ([LLD] 计算公式: x_fp32 = CastToFp32(x) * scales; the scales
+ * tensor may be a scalar, a row shared by the experts or the routed expert's row, per
+ * 约束说明 of modes 1-3; reading R23: modes 2 and 3 take the same three shapes as mode 1).
+ *   mode 1: q = Cast(x_fp32, int8) with the static scales already applied; no scales out
+ *   mode 2: one dynamic segment over the whole row; one scale
+ *   mode 3: dynamic segments of 128 elements (the last may be short); Ceil(H,128) scales
+ *           (reading R20: the group length is the 128 of the scale shape (A, Ceil(H,128)))
+ *   mode 4/5: MX blocks of 32; Align2(Ceil(H,32)) scales, the pad entry 0
+ * codes: H bytes (int8 two's complement or fp8 codes).  Returns 0, or -1 when the code type,
+ * the multiplier or the mode do not go together. */
+int32_t oracle_quant_row(int32_t quant_mode, int32_t code_type, const uint16_t* x,
+                         const float* pre, int32_t pre_len, int32_t H, void* codes,
+                         float* scales)
+{
+    if (quant_mode < 1 || quant_mode > 5) return -1;
+    if (oracle_code_type(quant_mode, code_type) != code_type) return -1;
+    if (pre_len != 0 && pre_len != 1 && pre_len != H) return -1;
+    if ((pre_len != 0) != (pre != NULL)) return -1;
+    if (quant_mode >= 4 && pre_len != 0) return -1;
+    if (quant_mode == 1 && pre_len == 0) return -1;
+    uint8_t* q = (uint8_t*)codes;
+    float* f = (float*)malloc((size_t)H * sizeof(float));
+    for (int32_t h = 0; h < H; ++h) {
+        f[h] = oracle_bf16_to_f32(x[h]);
+        if (pre_len == 1) f[h] = f[h] * pre[0];
+        else if (pre_len == H) f[h] = f[h] * pre[h];
+    }
+    if (quant_mode == 1) {
+        for (int32_t h = 0; h < H; ++h) q[h] = encode(code_type, f[h]);
+    } else if (quant_mode == 2) {
+        scales[0] = quant_dynamic(code_type, f, 0, H, q);
+    } else if (quant_mode == 3) {
+        for (int32_t g = 0; g * 128 < H; ++g) {
+            int32_t h1 = g * 128 + 128 < H ? g * 128 + 128 : H;
+            scales[g] = quant_dynamic(code_type, f, g * 128, h1, q);
+        }
+    } else {
+        int32_t nb = (H + 31) / 32;
+        for (int32_t b = 0; b < nb; ++b) {
+            int32_t h1 = b * 32 + 32 < H ? b * 32 + 32 : H;
+            scales[b] = quant_mx_block(code_type, quant_mode == 5, f, b * 32, h1, q);
+        }
+        for (int32_t b = nb; b < oracle_mx_scale_count(H); ++b) scales[b] = 0.0f;
+    }
+    free(f);
+    return 0;
+}
+
+/* Per-token dynamic int8 quantization, quant_mode 2 ([OPS] 功能说明 情形 2; [LLD] 计算公式,
+ * quant_mode=2): dyn = 127 / max|x_fp32|, q = CastToInt8(x_fp32 * dyn), scale = 1.0 / dyn,
+ * with x_fp32 the token times the smooth-scale row when one is given. */
+void oracle_quant_int8_row(const uint16_t* x, const float* smooth_or_null, int32_t H,
+                           int8_t* q, float* scale)
+{
+    oracle_quant_row(2, ORACLE_CODE_INT8, x, smooth_or_null, smooth_or_null ? H : 0, H, q,
+                     scale);
+}
+
+/* MX E4M3 quantization of one row (quant_mode 4, or 5 when clip is set). */
 void oracle_quant_mx_row(const uint16_t* x, int32_t H, int32_t clip, uint8_t* codes,
                          float* scales)
 {
-    int32_t nb = (H + 31) / 32;
-    int32_t ns = oracle_mx_scale_count(H);
-    for (int32_t b = 0; b < nb; ++b) {
-        int32_t h0 = b * 32;
-        int32_t h1 = h0 + 32 < H ? h0 + 32 : H;
-        float amax = 0.0f;
-        for (int32_t h = h0; h < h1; ++h) {
-            float a = fabsf(oracle_bf16_to_f32(x[h]));
-            if (a > amax) amax = a;
-        }
-        int se;
-        if (!clip) {
-            if (amax == 0.0f) se = -127;
-            else se = ilog2_floor(amax) - 8;
-            if (se < -127) se = -127;
-        } else {
-            float c = amax > 1e-4f ? amax : 1e-4f;
-            float v = c / 448.0f;
-            int ex;
-            float m = frexpf(v, &ex);  /* v = m * 2^ex; v is a power of two iff m == 0.5 */
-            se = (m == 0.5f) ? ex - 1 : ex;
-        }
-        float sc = ldexpf(1.0f, se);   /* 2^-127 is a binary32 subnormal: exact */
-        for (int32_t h = h0; h < h1; ++h) {
-            float v = oracle_bf16_to_f32(x[h]) / sc;
-            codes[h] = oracle_e4m3_from_f32(v);
-        }
-        scales[b] = sc;
-    }
-    for (int32_t b = nb; b < ns; ++b) scales[b] = 0.0f;
+    oracle_quant_row(clip ? 5 : 4, ORACLE_CODE_E4M3, x, NULL, 0, H, codes, scales);
 }
 
 /* ------------------------------------------------------------------------------------- */
@@ -292,24 +464,35 @@ int64_t oracle_dest_row(const oracle_cfg* c, const int32_t* ep_recv_count,
  * row, with the source triple (s, i, k) ([SMP] Dispatch 功能介绍, 计算步骤: the triple
  * travels with the quantized token and comes out as assist_info_for_combine).
  *   mode 0 ([LLD] quant_mode=0): the bf16 row is moved unchanged; no scales.
- *   mode 2: int8 row + one fp32 scale; the smooth-scale row is the routed expert's
- *           ([LLD] quant_mode 约束: shape (num_experts, H)), so quantization is per pair.
- *   mode 4/5: E4M3 codes + Align2(Ceil(H,32)) fp32 scales per row.
+ *   modes 1-5: the row quantized by oracle_quant_row for the configured code type.  The
+ *   scales tensor ([LLD] 约束说明, modes 1-3) is a scalar (scales_kind 1), a row shared by
+ *   every expert (2) or the routed expert's row of an [E][H] table (3); with kind 3 the
+ *   quantization is per pair.
  *   expand_x [cap][H] (uint16 bf16 patterns for mode 0, else bytes);
- *   dynamic_scales [cap] or [cap][scale count]; assist_info [cap][3]. */
+ *   dynamic_scales [cap][scale count] fp32, or bytes when scale_format is 1: each MX scale
+ *   2^e as its E8M0 byte e + 127 ([SMP] 通信前量化), pad bytes 0 (reading R24);
+ *   assist_info [cap][3].
+ * Returns -2 for a mode / code type / scales kind / scale format that do not go together,
+ * -3 when the scales pointer disagrees with scales_kind, -1 for an out-of-range id. */
 int32_t oracle_dispatch(const oracle_cfg* c, const uint16_t* x, const int32_t* expert_ids,
-                        const float* smooth_or_null, const uint8_t* mask, void* expand_x,
-                        float* dynamic_scales, int32_t* expand_idx, int32_t* assist_info,
+                        const float* scales_or_null, const uint8_t* mask, void* expand_x,
+                        void* dynamic_scales, int32_t* expand_idx, int32_t* assist_info,
                         int32_t* ep_recv_count, int64_t* expert_token_nums,
                         int64_t* recv_offsets, int32_t* cnt_scratch)
 {
-    const int32_t H = c->H;
-    if (c->quant_mode != 0 && c->quant_mode != 2 && c->quant_mode != 4 && c->quant_mode != 5)
-        return -2;
-    if (smooth_or_null && c->quant_mode != 2) return -3;
+    const int32_t H = c->H, mode = c->quant_mode;
+    const int32_t ct = oracle_code_type(mode, c->out_dtype);
+    if (ct < 0) return -2;
+    if (c->scales_kind < 0 || c->scales_kind > 3) return -2;
+    if ((mode == 0 || mode >= 4) && c->scales_kind != 0) return -2;
+    if (mode == 1 && c->scales_kind == 0) return -2;
+    if (c->scale_format != 0 && !(c->scale_format == 1 && mode >= 4)) return -2;
+    if ((c->scales_kind != 0) != (scales_or_null != NULL)) return -3;
     if (oracle_route(c, expert_ids, mask, cnt_scratch, expand_idx) != 0) return -1;
     oracle_recv_counts(c, cnt_scratch, ep_recv_count, expert_token_nums, recv_offsets);
-    const int32_t ns = oracle_mx_scale_count(H);
+    const int32_t ns = oracle_scale_count(mode, H);
+    const int32_t nb = (H + 31) / 32;
+    float* rowsc = (float*)malloc((size_t)(ns > 0 ? ns : 1) * sizeof(float));
     for (int32_t s = 0; s < c->W; ++s)
         for (int32_t i = 0; i < c->BS; ++i)
             for (int32_t k = 0; k < c->K; ++k) {
@@ -319,21 +502,29 @@ int32_t oracle_dispatch(const oracle_cfg* c, const uint16_t* x, const int32_t* e
                 int32_t e = expert_ids[p];
                 int64_t row = oracle_dest_row(c, ep_recv_count, recv_offsets, s, e, ord);
                 const uint16_t* xr = x + ((size_t)s * c->BS + i) * H;
-                if (c->quant_mode == 0) {
+                if (mode == 0) {
                     memcpy((uint16_t*)expand_x + (size_t)row * H, xr, (size_t)H * 2);
-                } else if (c->quant_mode == 2) {
-                    const float* sm = smooth_or_null ? smooth_or_null + (size_t)e * H : NULL;
-                    oracle_quant_int8_row(xr, sm, H, (int8_t*)expand_x + (size_t)row * H,
-                                          &dynamic_scales[row]);
                 } else {
-                    oracle_quant_mx_row(xr, H, c->quant_mode == 5,
-                                        (uint8_t*)expand_x + (size_t)row * H,
-                                        dynamic_scales + (size_t)row * ns);
+                    const float* pre = NULL;
+                    int32_t pre_len = 0;
+                    if (c->scales_kind == 1) { pre = scales_or_null; pre_len = 1; }
+                    if (c->scales_kind == 2) { pre = scales_or_null; pre_len = H; }
+                    if (c->scales_kind == 3) { pre = scales_or_null + (size_t)e * H; pre_len = H; }
+                    oracle_quant_row(mode, ct, xr, pre, pre_len, H,
+                                     (uint8_t*)expand_x + (size_t)row * H, rowsc);
+                    for (int32_t b = 0; b < ns; ++b) {
+                        if (c->scale_format == 1)
+                            ((uint8_t*)dynamic_scales)[(size_t)row * ns + b] =
+                                b < nb ? oracle_e8m0_from_scale(rowsc[b]) : 0;
+                        else
+                            ((float*)dynamic_scales)[(size_t)row * ns + b] = rowsc[b];
+                    }
                 }
                 assist_info[(size_t)row * 3 + 0] = s;
                 assist_info[(size_t)row * 3 + 1] = i;
                 assist_info[(size_t)row * 3 + 2] = k;
             }
+    free(rowsc);
     return 0;
 }
 

@@ -32,24 +32,43 @@ typedef struct {
     int32_t BS;                     /* tokens per source rank                             */
     int32_t H;                      /* hidden size                                        */
     int32_t K;                      /* picks per token                                    */
-    int32_t quant_mode;             /* 0 none, 2 int8 per token, 4 MX, 5 MX clip          */
+    int32_t quant_mode;             /* 0 none, 1 static, 2 per token, 3 per 128-group,
+                                       4 MX, 5 MX clip                                      */
     int32_t zero_expert_num;        /* ids [E, E+Z) are zero experts                      */
     int32_t copy_expert_num;        /* ids [E+Z, E+Z+C) are copy experts                  */
     int32_t expert_token_nums_type; /* 0 inclusive cumsum, 1 per-expert counts            */
     int32_t mask_kind;              /* 0 none, 1 per token [W][BS], 2 per pair [W][BS][K] */
+    int32_t out_dtype;              /* 0 the mode's default, else one of ORACLE_CODE_*     */
+    int32_t scales_kind;            /* 0 none, 1 scalar (1,), 2 shared (H,), 3 per expert  */
+    int32_t scale_format;           /* 0 fp32 scales, 1 E8M0 bytes (modes 4/5 only)        */
 } oracle_cfg;
+
+/* element types of expand_x */
+#define ORACLE_CODE_BF16 0
+#define ORACLE_CODE_INT8 1
+#define ORACLE_CODE_E4M3 2
+#define ORACLE_CODE_E5M2 3
 
 /* scalar helpers (each written from its definition) */
 float    oracle_bf16_to_f32(uint16_t b);
 uint16_t oracle_f32_to_bf16(float f);
 uint8_t  oracle_e4m3_from_f32(float v);
 float    oracle_e4m3_to_f32(uint8_t code);
+uint8_t  oracle_e5m2_from_f32(float v);
+float    oracle_e5m2_to_f32(uint8_t code);
+int8_t   oracle_int8_from_f32(float v);
+uint8_t  oracle_e8m0_from_scale(float s);
 int32_t  oracle_mx_scale_count(int32_t H);
+int32_t  oracle_code_type(int32_t quant_mode, int32_t out_dtype);
+int32_t  oracle_scale_count(int32_t quant_mode, int32_t H);
 
 /* per-row quantization */
 void oracle_quant_int8_row(const uint16_t* x, const float* smooth_or_null, int32_t H,
                            int8_t* q, float* scale);
 void oracle_quant_mx_row(const uint16_t* x, int32_t H, int32_t clip, uint8_t* codes,
+                         float* scales);
+int32_t oracle_quant_row(int32_t quant_mode, int32_t code_type, const uint16_t* x,
+                         const float* pre, int32_t pre_len, int32_t H, void* codes,
                          float* scales);
 
 /* routing, receive counts, destination rows */
@@ -62,8 +81,8 @@ int64_t oracle_dest_row(const oracle_cfg* c, const int32_t* ep_recv_count,
 
 /* whole dispatch and combine */
 int32_t oracle_dispatch(const oracle_cfg* c, const uint16_t* x, const int32_t* expert_ids,
-                        const float* smooth_or_null, const uint8_t* mask, void* expand_x,
-                        float* dynamic_scales, int32_t* expand_idx, int32_t* assist_info,
+                        const float* scales_or_null, const uint8_t* mask, void* expand_x,
+                        void* dynamic_scales, int32_t* expand_idx, int32_t* assist_info,
                         int32_t* ep_recv_count, int64_t* expert_token_nums,
                         int64_t* recv_offsets, int32_t* cnt_scratch);
 int32_t oracle_combine_token(const oracle_cfg* c, const uint16_t* expert_out,

@@ -7,7 +7,8 @@ counts the oracle uses:
   * a pick's expand_idx is the number of earlier picks of the same source rank that chose
     the same expert;
   * the receive counts are plain counts over that list.
-E4M3 rounding is a nearest-value search over the 127 finite magnitudes.
+E4M3 and E5M2 rounding is a nearest-value search over the finite magnitudes of the format
+(127 for E4M3, 124 for E5M2), built from the formats' field definitions.
 """
 from fractions import Fraction
 
@@ -73,3 +74,32 @@ def e4m3_nearest(v: Fraction) -> int:
         return sign | 0x7E
     best = min(_E4M3, key=lambda cv: (abs(cv[1] - a), cv[0] & 1))
     return sign | best[0]
+
+
+def e5m2_values():
+    """(code, exact value) for the 124 finite non-negative E5M2 codes 0x00..0x7B."""
+    out = []
+    for code in range(0x7C):
+        ex, m = code >> 2, code & 3
+        v = Fraction(m, 4) * Fraction(2) ** -14 if ex == 0 else \
+            (1 + Fraction(m, 4)) * Fraction(2) ** (ex - 15)
+        out.append((code, v))
+    return out
+
+
+_E5M2 = e5m2_values()
+
+
+def e5m2_nearest(v: Fraction) -> int:
+    """Nearest finite E5M2 code to the exact value v (ties to the even code), with
+    magnitudes at or above 57344 clamped to 57344; the sign bit follows v's sign."""
+    sign = 0x80 if v < 0 else 0
+    a = abs(v)
+    if a >= 57344:
+        return sign | 0x7B
+    best = min(_E5M2, key=lambda cv: (abs(cv[1] - a), cv[0] & 1))
+    return sign | best[0]
+
+
+def fp8_nearest(kind: str, v: Fraction) -> int:
+    return e4m3_nearest(v) if kind == "e4m3" else e5m2_nearest(v)

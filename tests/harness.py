@@ -17,7 +17,8 @@ def oracle_cfg(wl: workloads.Workload, etn_type=None):
                            copy_expert_num=wl.copy_expert_num,
                            expert_token_nums_type=wl.expert_token_nums_type if etn_type is None
                            else etn_type,
-                           mask_kind=wl.mask_kind)
+                           mask_kind=wl.mask_kind, out_dtype=wl.out_dtype,
+                           scales_kind=wl.scales_kind, scale_format=wl.scale_format)
 
 
 def lib_cfg(wl: workloads.Workload, cap=None):
@@ -62,7 +63,7 @@ def gpu_dispatch(wl, inp, cfg=None, device="cuda"):
     cfg = lib_cfg(wl) if cfg is None else cfg
     x = bf16_dev(inp["x"], device)
     ids = to_dev(inp["expert_ids"], device=device)
-    sm = to_dev(inp.get("smooth"), device=device)
+    sm = to_dev(inp.get("scales"), device=device)
     mask = to_dev(inp.get("mask"), device=device)
     out = cq.dispatch(cfg, x, ids, sm, mask)
     return cfg, dict(x=x, ids=ids, mask=mask), out

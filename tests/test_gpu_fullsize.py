@@ -76,8 +76,8 @@ def test_fullsize_dispatch_and_combine(name):
     for n, (s, i, k, e, row) in enumerate(picks):
         xr = inp["x"][s, i]
         if wl.quant_mode == 2:
-            q, scale = oracle.quant_int8_row(xr, None if inp["smooth"] is None
-                                             else inp["smooth"][e])
+            q, scale = oracle.quant_int8_row(xr, None if inp["scales"] is None
+                                             else inp["scales"][e])
             assert (ex[n] == q).all(), (s, i, k)
             assert np.float32(sc[n]).view(np.uint32) == np.float32(scale).view(np.uint32)
         else:

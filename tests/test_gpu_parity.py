@@ -24,7 +24,7 @@ SMALL = {
     "c1_mode4": workloads.C1_MODE0.replace(name="c1_mode4", quant_mode=4),
     "c1_mode5": workloads.C1_MODE0.replace(name="c1_mode5", quant_mode=5),
     "smooth_ragged": workloads.Workload("smooth_ragged", W=4, E=32, BS=100, H=1056, K=6,
-                                        quant_mode=2, smooth=True, outlier_prob=0.02,
+                                        quant_mode=2, scales_kind=3, outlier_prob=0.02,
                                         expert_token_nums_type=0),
     "mx_ragged_blocks": workloads.Workload("mx_ragged_blocks", W=3, E=12, BS=77, H=1032, K=5,
                                            quant_mode=4, routing="zipf"),
@@ -40,7 +40,7 @@ SMALL = {
     "scalar_path_h1030": workloads.Workload("scalar_path_h1030", W=2, E=8, BS=33, H=1030, K=3,
                                             quant_mode=5),
     "scalar_path_mode2_h1030": workloads.Workload("scalar_path_mode2_h1030", W=2, E=8, BS=9,
-                                                  H=1030, K=3, quant_mode=2, smooth=True),
+                                                  H=1030, K=3, quant_mode=2, scales_kind=3),
     "scalar_path_mode0_h1030": workloads.Workload("scalar_path_mode0_h1030", W=3, E=9, BS=9,
                                                   H=1030, K=2, quant_mode=0, copy_expert_num=1),
     "l1_w8_k8": workloads.Workload("l1_w8_k8", W=8, E=8, BS=40, H=1024, K=8, quant_mode=4),
@@ -60,7 +60,7 @@ SMALL = {
 
 def _oracle_dispatch(wl, inp, etn_type=None):
     cfg = harness.oracle_cfg(wl, etn_type)
-    return cfg, oracle.dispatch(cfg, inp["x"], inp["expert_ids"], smooth=inp.get("smooth"),
+    return cfg, oracle.dispatch(cfg, inp["x"], inp["expert_ids"], scales=inp.get("scales"),
                                 mask=inp.get("mask"))
 
 

@@ -493,16 +493,24 @@ def test_combine_roundtrip_int8():
 # whole dispatch: payload placement against brute-force rows
 # ---------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("mode", [0, 2, 4, 5])
-def test_dispatch_payload_placement(mode):
+VARIANTS = [  # (quant_mode, out_dtype, scales_kind, scale_format)
+    (0, 0, 0, 0), (1, 0, 1, 0), (1, 1, 2, 0), (1, 0, 3, 0), (2, 0, 0, 0), (2, 0, 3, 0),
+    (2, 2, 2, 0), (2, 3, 1, 0), (3, 0, 0, 0), (3, 3, 3, 0), (4, 0, 0, 0), (4, 3, 0, 1),
+    (5, 0, 0, 0), (5, 2, 0, 1), (5, 3, 0, 0)]
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=lambda v: "m%d_t%d_s%d_f%d" % v)
+def test_dispatch_payload_placement(variant):
+    mode, odt, kind, fmt = variant
     wl = workloads.C1_MODE0.replace(quant_mode=mode, zero_expert_num=1, copy_expert_num=1,
-                                    mask_kind=2, inactive_tokens_per_rank=3, routing="randint")
+                                    mask_kind=2, inactive_tokens_per_rank=3, routing="randint",
+                                    out_dtype=odt, scales_kind=kind, scale_format=fmt)
     inp = workloads.generate(wl, seed=9)
-    sm = (np.random.default_rng(0).uniform(0.5, 1.5, (wl.E, wl.H)).astype(np.float32)
-          if mode == 2 else None)
+    sm = inp["scales"]
     cfg = oracle.make_cfg(wl.W, wl.E, wl.BS, wl.H, wl.K, quant_mode=mode,
-                          zero_expert_num=1, copy_expert_num=1, mask_kind=2)
-    d = oracle.dispatch(cfg, inp["x"], inp["expert_ids"], smooth=sm, mask=inp["mask"])
+                          zero_expert_num=1, copy_expert_num=1, mask_kind=2, out_dtype=odt,
+                          scales_kind=kind, scale_format=fmt)
+    d = oracle.dispatch(cfg, inp["x"], inp["expert_ids"], scales=sm, mask=inp["mask"])
     rows, beidx, *_ = brute.route(wl.W, wl.E, wl.BS, wl.K, inp["expert_ids"].tolist(),
                                   inp["mask"].tolist(), 2)
     assert d["expand_idx"].tolist() == beidx
@@ -512,9 +520,28 @@ def test_dispatch_payload_placement(mode):
         xr = inp["x"][s, i]
         if mode == 0:
             assert (d["expand_x"][row] == xr).all()
-        elif mode == 2:
-            q, sc = oracle.quant_int8_row(xr, sm[inp["expert_ids"][s, i, k]])
-            assert (d["expand_x"][row] == q).all() and d["dynamic_scales"][row] == sc
+            continue
+        pre = None if kind == 0 else sm[inp["expert_ids"][s, i, k]] if kind == 3 else sm
+        q, sc = oracle.quant_row(mode, xr, pre, odt)
+        assert (d["expand_x"][row] == q).all()
+        if mode == 1:
+            assert "dynamic_scales" not in d
+        elif fmt == 1:
+            nb = (wl.H + 31) // 32
+            want = [oracle.e8m0_from_scale(v) for v in sc[:nb]] + [0] * (len(sc) - nb)
+            assert d["dynamic_scales"][row].tolist() == want
         else:
-            c, sc = oracle.quant_mx_row(xr, mode == 5)
-            assert (d["expand_x"][row] == c).all() and (d["dynamic_scales"][row] == sc).all()
+            assert (d["dynamic_scales"][row] == sc).all()
+
+
+@pytest.mark.parametrize("variant", [(0, 2, 0, 0), (1, 0, 0, 0), (1, 2, 1, 0), (2, 0, 0, 1),
+                                     (3, 1, 0, 0), (4, 0, 1, 0), (5, 1, 0, 0), (3, 0, 4, 0)])
+def test_dispatch_rejects_invalid_variants(variant):
+    mode, odt, kind, fmt = variant
+    cfg = oracle.make_cfg(2, 8, 4, 1024, 2, quant_mode=mode, out_dtype=odt, scales_kind=kind,
+                          scale_format=fmt)
+    x = np.zeros((2, 4, 1024), np.uint16)
+    ids = np.zeros((2, 4, 2), np.int32)
+    sc = None if kind == 0 else np.ones(1024, np.float32)
+    with pytest.raises(ValueError):
+        oracle.dispatch(cfg, x, ids, scales=sc)

@@ -19,7 +19,10 @@ Recipe (numpy PCG64, one spawned sub-stream per tensor, base seed 0 by default):
                  permutation of the experts (drawn with the Gumbel top-K construction,
                  which has exactly that sequential law); randint: K independent uniform ids
                  (duplicates allowed)
-  smooth         fp32 U(0.5, 1.5), shape [E][H]
+  scales         the quantization scales tensor: shape (1,), (H,) or (E, H) for scales
+                 kinds 1, 2, 3; fp32 U(0.5, 1.5) as smooth scales (modes 2, 3), U(16, 48) as
+                 static int8 coefficients (mode 1: about 127 / max|x| of an N(0,1) row, so
+                 the largest elements of a row saturate)
   mask           none; per token [W][BS]; or per pick [W][BS][K] with a fixed number of
                  tokens per rank fully inactive (seeded choice)
   expert_scales  fp32 softmax of N(0,1) logits over each token's K picks
@@ -45,12 +48,14 @@ class Workload:
     BS: int                     # tokens per rank
     H: int                      # hidden size
     K: int                      # picks per token
-    quant_mode: int             # 0, 2, 4, 5
+    quant_mode: int             # 0..5
     zero_expert_num: int = 0
     copy_expert_num: int = 0
     expert_token_nums_type: int = 1
     mask_kind: int = 0          # 0 none, 1 per token, 2 per pick
-    smooth: bool = False
+    scales_kind: int = 0        # 0 none, 1 scalar, 2 shared row (H,), 3 per expert (E, H)
+    out_dtype: int = 0          # 0 the mode's default, 1 int8, 2 E4M3, 3 E5M2
+    scale_format: int = 0       # 0 fp32 scales, 1 E8M0 bytes (MX modes)
     routing: str = "uniform"    # uniform | zipf | randint
     zipf_s: float = 1.2
     outlier_prob: float = 0.0
@@ -87,7 +92,7 @@ C1_MODE2 = C1_MODE0.replace(
     description="tiny: W=2, E=8 (L=4), BS=16, H=1024, K=2, int8 per-token quant without "
                 "smooth scales")
 C2 = Workload(
-    "c2_w8_smooth", W=8, E=256, BS=128, H=7168, K=8, quant_mode=2, smooth=True,
+    "c2_w8_smooth", W=8, E=256, BS=128, H=7168, K=8, quant_mode=2, scales_kind=3,
     outlier_prob=0.01, expert_token_nums_type=0,
     description="W=8, E=256 (L=32), BS=128, H=7168, K=8, bf16 N(0,1) with 1% of values x10, "
                 "int8 per-token quant with per-expert smooth scales U(0.5,1.5), uniform "
@@ -195,6 +200,14 @@ def gen_expert_scales(wl: Workload, rng) -> np.ndarray:
     return w.reshape(wl.W, wl.BS, wl.K)
 
 
+def gen_scales(wl: Workload, rng):
+    if wl.scales_kind == 0:
+        return None
+    shape = {1: (1,), 2: (wl.H,), 3: (wl.E, wl.H)}[wl.scales_kind]
+    lo, hi = (16.0, 48.0) if wl.quant_mode == 1 else (0.5, 1.5)
+    return rng.uniform(lo, hi, shape).astype(np.float32)
+
+
 def generate(wl: Workload, seed: int = 0, expert_out_rows: int | None = None) -> dict:
     """All host inputs of one dispatch+combine round trip.
 
@@ -211,8 +224,7 @@ def generate(wl: Workload, seed: int = 0, expert_out_rows: int | None = None) ->
         expert_ids=gen_expert_ids(wl, st[_IDS]),
         mask=gen_mask(wl, st[_MASK]),
         expert_scales=gen_expert_scales(wl, st[_WEIGHTS]),
-        smooth=(st[_SMOOTH].uniform(0.5, 1.5, (wl.E, wl.H)).astype(np.float32)
-                if wl.smooth else None),
+        scales=gen_scales(wl, st[_SMOOTH]),
     )
     if expert_out_rows is not None:
         out["expert_out"] = _normal_bf16(st[_EXPERT_OUT], (expert_out_rows, wl.H))
