@@ -49,8 +49,9 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--sets", type=int, default=2,
-                    help="input/output buffer sets rotated across steps")
+    ap.add_argument("--sets", type=int, default=3,
+                    help="input/output buffer sets rotated across steps (each set is far "
+                         "larger than the 256 MB Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-passes", type=int, default=3)
     ap.add_argument("--mode", default="bench", choices=["bench", "copy-calib"])
@@ -69,7 +70,7 @@ def algorithmic_bytes(wl, inp, routed_rows, copy_picks, active_tokens):
     receive counts (and mask, and ori_x for copy picks), write y."""
     W, E, H, K, T = wl.W, wl.E, wl.H, wl.K, wl.T
     b = 2 if wl.quant_mode == 0 else 1
-    S = {0: 0, 2: 4}.get(wl.quant_mode, 4 * mx_scales_per_row(H))
+    S = scale_bytes_per_row(wl)
     m = 0 if inp.get("mask") is None else inp["mask"].nbytes
     smooth = 0 if inp.get("scales") is None else inp["scales"].nbytes
     P = routed_rows
@@ -82,6 +83,18 @@ def algorithmic_bytes(wl, inp, routed_rows, copy_picks, active_tokens):
 def mx_scales_per_row(H):
     nb = (H + 31) // 32
     return nb + (nb & 1)
+
+
+def scale_bytes_per_row(wl):
+    """dynamic_scales bytes per expand_x row: none (modes 0, 1), one fp32 (mode 2), one fp32
+    per 128-group (mode 3), one fp32 or E8M0 byte per 32-block, Align2 (modes 4, 5)."""
+    if wl.quant_mode <= 1:
+        return 0
+    if wl.quant_mode == 2:
+        return 4
+    if wl.quant_mode == 3:
+        return 4 * ((wl.H + 127) // 128)
+    return (1 if wl.scale_format == 1 else 4) * mx_scales_per_row(wl.H)
 
 
 def source_hash(paths):
@@ -113,7 +126,8 @@ def cpu_baseline(wl, inp, expert_out_host, passes):
                           zero_expert_num=wl.zero_expert_num,
                           copy_expert_num=wl.copy_expert_num,
                           expert_token_nums_type=wl.expert_token_nums_type,
-                          mask_kind=wl.mask_kind)
+                          mask_kind=wl.mask_kind, out_dtype=wl.out_dtype,
+                          scales_kind=wl.scales_kind, scale_format=wl.scale_format)
     cpus = sorted(os.sched_getaffinity(0))
     os.sched_setaffinity(0, {cpus[0]})          # the oracle is single-threaded; pin it
     times = []
@@ -163,7 +177,8 @@ def run_bench(args):
     cfg = cq.make_config(wl.W, wl.E, wl.BS, wl.H, wl.K, wl.quant_mode,
                          zero_expert_num=wl.zero_expert_num, copy_expert_num=wl.copy_expert_num,
                          expert_token_nums_type=wl.expert_token_nums_type,
-                         mask_kind=wl.mask_kind)
+                         mask_kind=wl.mask_kind, out_dtype=wl.out_dtype,
+                         scales_kind=wl.scales_kind, scale_format=wl.scale_format)
 
     def dev_t(a, dtype=None):
         if a is None:
@@ -230,6 +245,9 @@ def run_bench(args):
     d_bytes, c_bytes = algorithmic_bytes(wl, inp, P, copy_picks, active_tokens)
     d_avg = statistics.mean(disp_ms)
     c_avg = statistics.mean(comb_ms)
+
+    def pct(v, q):
+        return float(np.percentile(np.asarray(v), q)) * 1e3
     comb_gbps = c_bytes / (c_avg * 1e-3) / 1e9
     disp_gbps = d_bytes / (d_avg * 1e-3) / 1e9
     total_gbps = (d_bytes + c_bytes) / (ms_per_step * 1e-3) / 1e9
@@ -257,18 +275,22 @@ def run_bench(args):
         "data": "synthetic",
         "config": {"workload": wl.name, "W": wl.W, "E": wl.E, "BS_per_rank": wl.BS,
                    "H": wl.H, "K": wl.K, "quant_mode": wl.quant_mode,
+                   "out_dtype": wl.out_dtype, "scales_kind": wl.scales_kind,
+                   "scale_format": wl.scale_format,
                    "routing": wl.routing, "tokens_per_step": wl.T, "routed_rows": P,
                    "description": wl.description},
         "hbm_gbps": round(total_gbps, 1),
         "hbm_frac": round(total_gbps / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "achieved": round(comb_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(comb_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": committed_traffic(), "kernel": "combine_kernel",
+                     "traffic": committed_traffic(), "kernel": "combine_wave_kernel",
                      "algorithmic_bytes_per_launch": c_bytes,
                      "avg_launch_us": round(c_avg * 1e3, 2)},
-        "dispatch": {"avg_us": round(d_avg * 1e3, 2), "algorithmic_bytes": d_bytes,
+        "dispatch": {"avg_us": round(d_avg * 1e3, 2), "median_us": round(pct(disp_ms, 50), 2),
+                     "p90_us": round(pct(disp_ms, 90), 2), "algorithmic_bytes": d_bytes,
                      "gbps": round(disp_gbps, 1), "frac": round(disp_gbps / HBM_PEAK_GBPS, 4)},
-        "combine": {"avg_us": round(c_avg * 1e3, 2), "algorithmic_bytes": c_bytes,
+        "combine": {"avg_us": round(c_avg * 1e3, 2), "median_us": round(pct(comb_ms, 50), 2),
+                    "p90_us": round(pct(comb_ms, 90), 2), "algorithmic_bytes": c_bytes,
                     "gbps": round(comb_gbps, 1)},
         "wall_s_timed": round(wall, 4),
         "cpu_baseline": cpu,

@@ -15,6 +15,9 @@ import torch
 from .build import LIB
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = 0, -1, -2, -3, -4
+MOE_DTYPE_DEFAULT, MOE_DTYPE_INT8, MOE_DTYPE_E4M3, MOE_DTYPE_E5M2 = 0, 1, 2, 3
+MOE_SCALES_NONE, MOE_SCALES_SCALAR, MOE_SCALES_SHARED, MOE_SCALES_PER_EXPERT = 0, 1, 2, 3
+MOE_SCALE_FP32, MOE_SCALE_E8M0 = 0, 1
 _STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
            -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_DEVICE"}
 
@@ -36,7 +39,10 @@ class MoeDcConfig(ctypes.Structure):
         ("const_expert_num", ctypes.c_int32),
         ("expert_token_nums_type", ctypes.c_int32),
         ("mask_kind", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
+        ("scales_kind", ctypes.c_int32),
+        ("scale_format", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 2),
         ("expand_rows_capacity", ctypes.c_int64),
     ]
 
@@ -90,10 +96,22 @@ def load_library(path: str = LIB) -> ctypes.CDLL:
 
 
 def make_config(W, E, BS, H, K, quant_mode=0, zero_expert_num=0, copy_expert_num=0,
-                const_expert_num=0, expert_token_nums_type=1, mask_kind=0, cap=None):
+                const_expert_num=0, expert_token_nums_type=1, mask_kind=0, cap=None,
+                out_dtype=MOE_DTYPE_DEFAULT, scales_kind=MOE_SCALES_NONE,
+                scale_format=MOE_SCALE_FP32):
     cap = W * BS * K if cap is None else cap
     return MoeDcConfig(W, E, BS, H, K, quant_mode, zero_expert_num, copy_expert_num,
-                       const_expert_num, expert_token_nums_type, mask_kind, 0, cap)
+                       const_expert_num, expert_token_nums_type, mask_kind, out_dtype,
+                       scales_kind, scale_format, (ctypes.c_int32 * 2)(0, 0), cap)
+
+
+def code_type(cfg):
+    """Element type of expand_x: 0 bf16, 1 int8, 2 E4M3, 3 E5M2 (the moe_dtype values)."""
+    if cfg.quant_mode == 0:
+        return 0
+    if cfg.out_dtype != MOE_DTYPE_DEFAULT:
+        return cfg.out_dtype
+    return MOE_DTYPE_INT8 if cfg.quant_mode in (1, 2) else MOE_DTYPE_E4M3
 
 
 def _check(status: int):
@@ -144,27 +162,44 @@ def _stream(device, stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-_CODE_DTYPES = {0: torch.bfloat16, 2: torch.int8, 4: (torch.uint8, torch.float8_e4m3fn),
-                5: (torch.uint8, torch.float8_e4m3fn)}
+_CODE_DTYPES = {0: torch.bfloat16, 1: torch.int8, 2: (torch.uint8, torch.float8_e4m3fn),
+                3: (torch.uint8, torch.float8_e5m2)}
+_ALLOC_DTYPES = {0: torch.bfloat16, 1: torch.int8, 2: torch.uint8, 3: torch.uint8}
 
 
-def moe_dispatch(cfg, x, expert_ids, smooth_scales, x_active_mask, expand_x, dynamic_scales,
+def _scales_shape(cfg):
+    return {MOE_SCALES_SCALAR: (1,), MOE_SCALES_SHARED: (cfg.hidden,),
+            MOE_SCALES_PER_EXPERT: (cfg.moe_expert_num, cfg.hidden)}.get(cfg.scales_kind)
+
+
+def _dyn_scales_spec(cfg):
+    """(dtype, shape) of dynamic_scales, or None when the mode has no scales."""
+    ns = moe_dc_scales_per_row(cfg)
+    if ns <= 0:
+        return None
+    cap = cfg.expand_rows_capacity
+    dt = torch.uint8 if cfg.scale_format == MOE_SCALE_E8M0 else torch.float32
+    return dt, ((cap,) if ns == 1 else (cap, ns))
+
+
+def moe_dispatch(cfg, x, expert_ids, scales, x_active_mask, expand_x, dynamic_scales,
                  expand_idx, assist_info, ep_recv_count, expert_token_nums, recv_offsets,
                  workspace, stream=None):
-    """Enqueue one dispatch on `stream` (default: the current stream of x's device)."""
-    W, BS, H, K, E, L, cap = (cfg.ep_world_size, cfg.bs, cfg.hidden, cfg.topk,
-                              cfg.moe_expert_num, cfg.L, cfg.expand_rows_capacity)
+    """Enqueue one dispatch on `stream` (default: the current stream of x's device).
+    `scales` is the quantization scales tensor of cfg.scales_kind ([1], [H] or [E][H])."""
+    W, BS, H, K, L, cap = (cfg.ep_world_size, cfg.bs, cfg.hidden, cfg.topk, cfg.L,
+                           cfg.expand_rows_capacity)
     dev = x.device
-    ns = moe_dc_scales_per_row(cfg)
+    spec = _dyn_scales_spec(cfg)
     mshape = {1: (W, BS), 2: (W, BS, K)}.get(cfg.mask_kind)
     args = [
         _ptr(x, torch.bfloat16, (W, BS, H), "x", dev),
         _ptr(expert_ids, torch.int32, (W, BS, K), "expert_ids", dev),
-        _ptr(smooth_scales, torch.float32, (E, H), "smooth_scales", dev),
+        _ptr(scales, torch.float32, _scales_shape(cfg), "scales", dev),
         _ptr(x_active_mask, (torch.uint8, torch.bool), mshape, "x_active_mask", dev),
-        _ptr(expand_x, _CODE_DTYPES.get(cfg.quant_mode), (cap, H), "expand_x", dev),
-        _ptr(dynamic_scales, torch.float32, None if ns <= 0 else
-             ((cap,) if ns == 1 else (cap, ns)), "dynamic_scales", dev),
+        _ptr(expand_x, _CODE_DTYPES.get(code_type(cfg)), (cap, H), "expand_x", dev),
+        _ptr(dynamic_scales, None if spec is None else spec[0],
+             None if spec is None else spec[1], "dynamic_scales", dev),
         _ptr(expand_idx, torch.int32, (W, BS, K), "expand_idx", dev),
         _ptr(assist_info, torch.int32, (cap, 3), "assist_info", dev),
         _ptr(ep_recv_count, torch.int32, (W, L * W), "ep_recv_count", dev),
@@ -207,13 +242,11 @@ def alloc_dispatch_outputs(cfg, device="cuda"):
     _check(moe_dc_validate(cfg))
     W, BS, H, K, L, cap = (cfg.ep_world_size, cfg.bs, cfg.hidden, cfg.topk, cfg.L,
                            cfg.expand_rows_capacity)
-    ns = moe_dc_scales_per_row(cfg)
-    code_dtype = {0: torch.bfloat16, 2: torch.int8}.get(cfg.quant_mode, torch.uint8)
+    spec = _dyn_scales_spec(cfg)
     return dict(
-        expand_x=torch.empty((cap, H), dtype=code_dtype, device=device),
-        dynamic_scales=(None if ns == 0 else
-                        torch.empty((cap,) if ns == 1 else (cap, ns), dtype=torch.float32,
-                                    device=device)),
+        expand_x=torch.empty((cap, H), dtype=_ALLOC_DTYPES[code_type(cfg)], device=device),
+        dynamic_scales=(None if spec is None else
+                        torch.empty(spec[1], dtype=spec[0], device=device)),
         expand_idx=torch.empty((W, BS, K), dtype=torch.int32, device=device),
         assist_info=torch.empty((cap, 3), dtype=torch.int32, device=device),
         ep_recv_count=torch.empty((W, L * W), dtype=torch.int32, device=device),
@@ -224,11 +257,10 @@ def alloc_dispatch_outputs(cfg, device="cuda"):
     )
 
 
-def dispatch(cfg, x, expert_ids, smooth_scales=None, x_active_mask=None, out=None,
-             stream=None):
+def dispatch(cfg, x, expert_ids, scales=None, x_active_mask=None, out=None, stream=None):
     """Allocate (or reuse `out`) and enqueue moe_dispatch; returns the output dict."""
     o = alloc_dispatch_outputs(cfg, x.device) if out is None else out
-    moe_dispatch(cfg, x, expert_ids, smooth_scales, x_active_mask, o["expand_x"],
+    moe_dispatch(cfg, x, expert_ids, scales, x_active_mask, o["expand_x"],
                  o["dynamic_scales"], o["expand_idx"], o["assist_info"], o["ep_recv_count"],
                  o["expert_token_nums"], o["recv_offsets"], o["workspace"], stream)
     return o

@@ -34,12 +34,34 @@ moe_status ok()
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Element type of expand_x for a quant mode and requested out_dtype, or -1 when the pair is
+// not allowed ([LLD] 约束说明: mode 0 keeps the input type; mode 1 int8; mode 2 int8, E4M3
+// or E5M2; modes 3-5 E4M3 or E5M2).
+int32_t resolve_code_type(int32_t mode, int32_t out_dtype)
+{
+    switch (mode) {
+    case 0:
+        return out_dtype == MOE_DTYPE_DEFAULT ? moe_dc::kCodeBf16 : -1;
+    case 1:
+        return out_dtype == MOE_DTYPE_DEFAULT || out_dtype == MOE_DTYPE_INT8 ? moe_dc::kCodeInt8
+                                                                             : -1;
+    case 2:
+        if (out_dtype == MOE_DTYPE_DEFAULT || out_dtype == MOE_DTYPE_INT8) return moe_dc::kCodeInt8;
+        if (out_dtype == MOE_DTYPE_E4M3) return moe_dc::kCodeE4m3;
+        return out_dtype == MOE_DTYPE_E5M2 ? moe_dc::kCodeE5m2 : -1;
+    default:
+        if (out_dtype == MOE_DTYPE_DEFAULT || out_dtype == MOE_DTYPE_E4M3) return moe_dc::kCodeE4m3;
+        return out_dtype == MOE_DTYPE_E5M2 ? moe_dc::kCodeE5m2 : -1;
+    }
+}
+
 // Range and divisibility rules of the ops-transformer article (约束说明; the wrapper's
 // checks under 调用说明) and of low_latency_dispatch (约束说明).
 moe_status check(const moe_dc_config* c, moe_dc::Shape* out)
 {
     if (!c) return fail(MOE_ERR_INVALID_ARG, "config is NULL");
-    if (c->reserved != 0) return fail(MOE_ERR_INVALID_ARG, "reserved must be 0");
+    if (c->reserved[0] != 0 || c->reserved[1] != 0)
+        return fail(MOE_ERR_INVALID_ARG, "reserved must be 0");
     if (c->ep_world_size < 2 || c->ep_world_size > 768)
         return fail(MOE_ERR_INVALID_ARG, "ep_world_size %d outside [2, 768]", c->ep_world_size);
     if (c->moe_expert_num <= 0 || c->moe_expert_num > 1024)
@@ -65,10 +87,22 @@ moe_status check(const moe_dc_config* c, moe_dc::Shape* out)
         return fail(MOE_ERR_INVALID_ARG, "topk %d exceeds the number of experts", c->topk);
     if (c->const_expert_num != 0)
         return fail(MOE_ERR_UNSUPPORTED, "const experts are not supported");
-    if (c->quant_mode == 1 || c->quant_mode == 3)
-        return fail(MOE_ERR_UNSUPPORTED, "quant_mode %d is not supported", c->quant_mode);
-    if (c->quant_mode != 0 && c->quant_mode != 2 && c->quant_mode != 4 && c->quant_mode != 5)
+    if (c->quant_mode < 0 || c->quant_mode > 5)
         return fail(MOE_ERR_INVALID_ARG, "quant_mode %d is not one of 0..5", c->quant_mode);
+    const int32_t code_type = resolve_code_type(c->quant_mode, c->out_dtype);
+    if (code_type < 0)
+        return fail(MOE_ERR_INVALID_ARG, "out_dtype %d is not allowed with quant_mode %d",
+                    c->out_dtype, c->quant_mode);
+    if (c->scales_kind < MOE_SCALES_NONE || c->scales_kind > MOE_SCALES_PER_EXPERT)
+        return fail(MOE_ERR_INVALID_ARG, "scales_kind %d is not one of 0..3", c->scales_kind);
+    if ((c->quant_mode == 0 || c->quant_mode >= 4) && c->scales_kind != MOE_SCALES_NONE)
+        return fail(MOE_ERR_INVALID_ARG, "quant_mode %d takes no scales tensor", c->quant_mode);
+    if (c->quant_mode == 1 && c->scales_kind == MOE_SCALES_NONE)
+        return fail(MOE_ERR_INVALID_ARG, "quant_mode 1 needs a scales tensor");
+    if (c->scale_format != MOE_SCALE_FP32 &&
+        !(c->scale_format == MOE_SCALE_E8M0 && c->quant_mode >= 4))
+        return fail(MOE_ERR_INVALID_ARG, "scale_format %d is not allowed with quant_mode %d",
+                    c->scale_format, c->quant_mode);
     if (c->expert_token_nums_type != 0 && c->expert_token_nums_type != 1)
         return fail(MOE_ERR_INVALID_ARG, "expert_token_nums_type must be 0 or 1");
     if (c->mask_kind < 0 || c->mask_kind > 2)
@@ -87,12 +121,18 @@ moe_status check(const moe_dc_config* c, moe_dc::Shape* out)
         out->H = c->hidden;
         out->K = c->topk;
         out->quant_mode = c->quant_mode;
+        out->code_type = code_type;
+        out->scales_kind = c->scales_kind;
+        out->scale_e8m0 = c->scale_format == MOE_SCALE_E8M0 ? 1 : 0;
         out->zero_end = c->moe_expert_num + c->zero_expert_num;
         out->id_end = out->zero_end + c->copy_expert_num;
         out->etn_type = c->expert_token_nums_type;
         out->mask_kind = c->mask_kind;
         const int32_t nb = (c->hidden + 31) / 32;
-        out->scales_per_row = c->quant_mode == 0 ? 0 : c->quant_mode == 2 ? 1 : nb + (nb & 1);
+        out->scales_per_row = c->quant_mode <= 1   ? 0
+                              : c->quant_mode == 2 ? 1
+                              : c->quant_mode == 3 ? (c->hidden + 127) / 128
+                                                   : nb + (nb & 1);
         out->cap = c->expand_rows_capacity;
     }
     return MOE_OK;
@@ -129,8 +169,8 @@ size_t moe_dc_dispatch_workspace_bytes(const moe_dc_config* cfg)
 }
 
 moe_status moe_dispatch(const moe_dc_config* cfg, const void* x, const int32_t* expert_ids,
-                        const float* smooth_scales, const uint8_t* x_active_mask,
-                        void* expand_x, float* dynamic_scales, int32_t* expand_idx,
+                        const float* scales, const uint8_t* x_active_mask,
+                        void* expand_x, void* dynamic_scales, int32_t* expand_idx,
                         int32_t* assist_info, int32_t* ep_recv_count,
                         int64_t* expert_token_nums, int64_t* recv_offsets, void* workspace,
                         size_t workspace_bytes, void* stream)
@@ -141,11 +181,12 @@ moe_status moe_dispatch(const moe_dc_config* cfg, const void* x, const int32_t* 
     if (!x || !expert_ids || !expand_x || !expand_idx || !assist_info || !ep_recv_count ||
         !expert_token_nums || !recv_offsets)
         return fail(MOE_ERR_INVALID_ARG, "a required tensor pointer is NULL");
-    if (sh.quant_mode != 0 && !dynamic_scales)
+    if (sh.scales_per_row > 0 && !dynamic_scales)
         return fail(MOE_ERR_INVALID_ARG, "dynamic_scales is required for quant_mode %d",
                     sh.quant_mode);
-    if (smooth_scales && sh.quant_mode != 2)
-        return fail(MOE_ERR_INVALID_ARG, "smooth scales are only allowed with quant_mode 2");
+    if ((sh.scales_kind != MOE_SCALES_NONE) != (scales != nullptr))
+        return fail(MOE_ERR_INVALID_ARG,
+                    "scales must be given iff scales_kind is not MOE_SCALES_NONE");
     if ((sh.mask_kind != 0) != (x_active_mask != nullptr))
         return fail(MOE_ERR_INVALID_ARG, "x_active_mask must be given iff mask_kind != 0");
     const size_t need = moe_dc::workspace_bytes(sh);
@@ -154,8 +195,10 @@ moe_status moe_dispatch(const moe_dc_config* cfg, const void* x, const int32_t* 
                     workspace_bytes);
     hipStream_t s = static_cast<hipStream_t>(stream);
     int32_t* seg = static_cast<int32_t*>(workspace);
+    const bool row_scales =
+        sh.scales_kind == MOE_SCALES_SHARED || sh.scales_kind == MOE_SCALES_PER_EXPERT;
     const bool vec = sh.H % 8 == 0 && aligned16(x) && aligned16(expand_x) &&
-                     (!smooth_scales || aligned16(smooth_scales));
+                     (!row_scales || aligned16(scales));
 
     st = device_status(moe_dc::launch_route(sh, expert_ids, x_active_mask, expand_idx, seg, s),
                        "route kernel launch");
@@ -164,7 +207,7 @@ moe_status moe_dispatch(const moe_dc_config* cfg, const void* x, const int32_t* 
                                            recv_offsets, s),
                        "scan kernel launch");
     if (st != MOE_OK) return st;
-    st = device_status(moe_dc::launch_scatter(sh, x, expert_ids, expand_idx, seg, smooth_scales,
+    st = device_status(moe_dc::launch_scatter(sh, x, expert_ids, expand_idx, seg, scales,
                                               expand_x, dynamic_scales, assist_info, vec, s),
                        "scatter kernel launch");
     if (st != MOE_OK) return st;
@@ -200,6 +243,6 @@ moe_status moe_combine(const moe_dc_config* cfg, const void* expert_out,
 
 const char* moe_dc_last_error(void) { return g_last_error.c_str(); }
 
-const char* moe_dc_version(void) { return "moe_dc 0.1.0 (gfx950)"; }
+const char* moe_dc_version(void) { return "moe_dc 0.2.0 (gfx950)"; }
 
 }  // extern "C"

@@ -50,6 +50,25 @@ __device__ __forceinline__ uint32_t e4m3_code(float v)
     return sign | ((((r >> 23) - 120u) << 3) | ((r >> 20) & 7u));
 }
 
+// E5M2 (bias 15, largest finite 57344) code of a finite binary32 value: nearest, ties to
+// even, magnitudes >= 57344 saturate to 57344 (never the infinity code), sign kept.  Normal
+// results round the significand to 2 fraction bits at bit 21 and rebias from 127 to 15;
+// below 2^-14 the grid is uniform with step 2^-16.  A value below 57344 cannot round past
+// it, since 57344 itself is on the grid.
+__device__ __forceinline__ uint32_t e5m2_code(float v)
+{
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    if (a >= 0x47600000u) return sign | 0x7Bu;                 // |v| >= 57344
+    if (a < 0x38800000u) {                                     // |v| < 2^-14
+        const float scaled = __uint_as_float(a) * 65536.0f;    // exact power-of-two scaling
+        return sign | (uint32_t)__builtin_rintf(scaled);
+    }
+    const uint32_t r = a + 0xFFFFFu + ((a >> 21) & 1u);
+    return sign | ((((r >> 23) - 112u) << 2) | ((r >> 21) & 3u));
+}
+
 // Streaming (non-temporal) 16- and 8-byte global accesses, for rows that are touched once.
 // They lower to global loads/stores with the non-temporal cache policy, which keeps the
 // once-read / once-written rows from displacing reusable lines in L2 and the Infinity Cache.

@@ -7,15 +7,26 @@
 
 namespace moe_dc {
 
+// Element types of expand_x (the values of moe_dtype in the C ABI).
+enum CodeType : int32_t { kCodeBf16 = 0, kCodeInt8 = 1, kCodeE4m3 = 2, kCodeE5m2 = 3 };
+
+// Shapes of the quantization scales tensor (the values of moe_scales_kind).
+enum ScalesKind : int32_t {
+    kScalesNone = 0, kScalesScalar = 1, kScalesShared = 2, kScalesPerExpert = 3
+};
+
 // Validated shape of one dispatch/combine problem (see moe_dc_config in include/moe_dc.h).
 struct Shape {
     int32_t W, E, L, BS, H, K;
     int32_t quant_mode;
+    int32_t code_type;       // CodeType of expand_x
+    int32_t scales_kind;     // ScalesKind of the scales tensor
+    int32_t scale_e8m0;      // 1: MX scales stored as E8M0 bytes, 0: fp32
     int32_t zero_end;        // E + zero_expert_num
     int32_t id_end;          // E + zero_expert_num + copy_expert_num
     int32_t etn_type;
     int32_t mask_kind;
-    int32_t scales_per_row;  // 0, 1 or Align2(Ceil(H,32))
+    int32_t scales_per_row;  // 0, 1, Ceil(H,128) or Align2(Ceil(H,32))
     int64_t cap;
 };
 
@@ -38,8 +49,8 @@ hipError_t launch_scan(const Shape& s, int32_t* seg, int32_t* ep_recv_count,
 
 // Quantize and scatter every routed pick to its packed row, with scales and source triple.
 hipError_t launch_scatter(const Shape& s, const void* x, const int32_t* expert_ids,
-                          const int32_t* expand_idx, const int32_t* seg, const float* smooth,
-                          void* expand_x, float* dynamic_scales, int32_t* assist_info,
+                          const int32_t* expand_idx, const int32_t* seg, const float* scales,
+                          void* expand_x, void* dynamic_scales, int32_t* assist_info,
                           bool vectorized, hipStream_t stream);
 
 // Weighted top-K gather.

@@ -1,59 +1,83 @@
-// dispatch.hip -- quantize each source token once and write it to its K packed rows.
+// dispatch.hip -- quantize each source token and write it to its K packed rows.
 //
 // Vectorized path (H % 8 == 0, 16-byte aligned pointers): one workgroup per source token
 // (s, i); each wavefront owns two slots of 64 16-byte vectors (8 bf16 elements per lane, so
 // every load instruction covers 1 KiB of contiguous memory).  All waves issue their row
 // loads first; threads 0..K-1 resolve the token's K destination rows meanwhile; one barrier
-// publishes the rows (and, for mode 2, the per-wave maxima of the token).  Each wave then
-// quantizes its slots in registers and stores them to the final row of every routed pick.
-// Rows are read and written with the non-temporal cache policy (each is touched exactly
-// once).  Small workgroups, many of them, keep every SIMD busy until the end of the launch.
+// publishes the rows (and, for per-token scaling, the per-wave maxima of the token).  Each
+// wave then quantizes its slots in registers and stores them to the final row of every
+// routed pick.  Rows are read and written with the non-temporal cache policy (each is
+// touched exactly once).  Small workgroups, many of them, keep every SIMD busy until the end
+// of the launch.
 //
 // Destination rows follow the pages' placement rule (design doc §2.2.2 token reorder and
 // §2.4 post-processing, merged into one address because every receiver lives in this GPU's
 // memory): the (expert, source) segment base left in the workspace by the scan kernel plus
 // the pick's expand_idx.
 //
-// Quantization (ops-transformer article, 功能说明 情形 2; low_latency_dispatch, 计算公式):
+// Quantization (low_latency_dispatch, 计算公式 and 约束说明; ops-transformer article,
+// 功能说明 情形 2).  x_fp32 is the bf16 token widened, times the scales tensor when one is
+// given: a scalar, a row shared by every expert, or the routed expert's row of an [E][H]
+// table (then the codes differ per pick and each pick is quantized on its own).
 //   mode 0  rows copied bit for bit
-//   mode 2  dyn = 127 / max|x_fp32| over the token (x_fp32 times the pick's expert smooth
-//           row when smooth scales are given, which makes the work per pick), codes =
-//           x_fp32 * dyn rounded half to even, scale = 1 / dyn
-//   mode 4  per 32-element block: shared_exp = floor(log2 max|x|) - 8 (clamped at -127)
-//   mode 5  per block: shared_exp = ceil(log2(max(max|x|, 1e-4) / 448))
-//           codes = E4M3(x / 2^shared_exp); the stored scale is 2^shared_exp.
-// In the vectorized path an MX block is 32 elements = 4 adjacent lanes of 8, reduced with two
-// lane exchanges.
+//   mode 1  codes = int8(x_fp32): static scales, no scales out
+//   mode 2  dyn = type_max / max|x_fp32| over the token, codes = type(x_fp32 * dyn),
+//           scale = 1 / dyn (type int8, E4M3 or E5M2; max 127, 448, 57344)
+//   mode 3  as mode 2 over each group of 128 elements; Ceil(H, 128) scales per row
+//   mode 4  per 32-element block: shared_exp = floor(log2 max|x|) - emax (clamped at -127;
+//           emax 8 for E4M3, 15 for E5M2)
+//   mode 5  per block: shared_exp = ceil(log2(max(max|x|, 1e-4) / fp8_max))
+//           codes = fp8(x / 2^shared_exp); the scale written is 2^shared_exp, as fp32 or as
+//           its E8M0 byte shared_exp + 127 (the SMP article's stored format)
+// int8 rounds half to even and saturates at +-127 with NaN -> 0; fp8 rounds to nearest even
+// and saturates at the type's largest finite value; NaN products of a dynamic mode (only
+// 0 * inf of an all-zero segment) give code 0.  In the vectorized path an MX block is 4
+// adjacent lanes and a group of 128 is 16 adjacent lanes, reduced with lane exchanges.
 //
 // The element-wise fallback (any H, any alignment) uses one workgroup per token with one
-// element per lane (scatter_elem_kernel); an MX block is then 32 adjacent lanes.
+// element per lane (scatter_elem_kernel); the variant is a runtime argument there.
 #include "dc_device.h"
 #include "dc_internal.h"
 
 namespace moe_dc {
 namespace {
 
-// int8 code of one element: round half to even, saturate to +-127, NaN (0 * inf) -> 0.
-__device__ __forceinline__ uint32_t int8_code(float f, float dyn)
+constexpr int kGroup = 128;          // mode 3 group length
+
+// int8 code of one value: round half to even, saturate to +-127, NaN -> 0.
+__device__ __forceinline__ uint32_t int8_code(float v)
 {
-    const float v = f * dyn;
     if (v != v) return 0u;
     const float r = fminf(fmaxf(__builtin_rintf(v), -127.0f), 127.0f);
     return (uint32_t)(int32_t)r;
 }
 
+template <int CT>
+__device__ __forceinline__ uint32_t fp8_code(float v)
+{
+    return CT == kCodeE4m3 ? e4m3_code(v) : e5m2_code(v);
+}
+
+// Largest finite value of a code type (dst_type_max / fp8_max of the formulas).
+template <int CT>
+constexpr float type_max()
+{
+    return CT == kCodeInt8 ? 127.0f : CT == kCodeE4m3 ? 448.0f : 57344.0f;
+}
+
 // Shared exponent of an MX block from the bit pattern of its absolute maximum.
-template <int MODE>
+template <int MODE, int CT>
 __device__ __forceinline__ int mx_shared_exp(uint32_t amax_bits)
 {
+    constexpr int emax = CT == kCodeE4m3 ? 8 : 15;
     if (MODE == 4) {
         if (amax_bits == 0) return -127;
         const int ex = (int)(amax_bits >> 23);
         const int fl = ex != 0 ? ex - 127 : (31 - __clz(amax_bits)) - 149;   // floor(log2)
-        return fl - 8 > -127 ? fl - 8 : -127;
+        return fl - emax > -127 ? fl - emax : -127;
     } else {
         const float c = fmaxf(__uint_as_float(amax_bits), 1e-4f);
-        const uint32_t vb = __float_as_uint(c / 448.0f);                   // normal, > 0
+        const uint32_t vb = __float_as_uint(c / type_max<CT>());           // normal, > 0
         return (int)(vb >> 23) - 127 + ((vb & 0x7FFFFFu) != 0u ? 1 : 0);     // ceil(log2)
     }
 }
@@ -64,17 +88,16 @@ __device__ __forceinline__ float pow2f(int e)
     return e >= -126 ? __uint_as_float((uint32_t)(127 + e) << 23) : __uint_as_float(0x00400000u);
 }
 
-// ---------------------------------------------------------------------------------------
-// vectorized path: one workgroup per token, kTileSlots 64-vector slots per wave
-// ---------------------------------------------------------------------------------------
-
-constexpr int kTileSlots = 2;        // 64-vector slots (1 KiB of bf16 each) per wave
-constexpr int kMaxTileWaves = 8;     // H <= 8192: at most 1024 vectors = 16 slots
-
 __device__ __forceinline__ void unpack8(uint4 w, float (&f)[8])
 {
     f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
     f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z); f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
+}
+
+__device__ __forceinline__ void mul8(float (&f)[8], float4 a, float4 b)
+{
+    f[0] = f[0] * a.x; f[1] = f[1] * a.y; f[2] = f[2] * a.z; f[3] = f[3] * a.w;
+    f[4] = f[4] * b.x; f[5] = f[5] * b.y; f[6] = f[6] * b.z; f[7] = f[7] * b.w;
 }
 
 __device__ __forceinline__ uint32_t absmax8(const float (&f)[8], uint32_t amax)
@@ -85,6 +108,12 @@ __device__ __forceinline__ uint32_t absmax8(const float (&f)[8], uint32_t amax)
         amax = amax > bits ? amax : bits;
     }
     return amax;
+}
+
+__device__ __forceinline__ uint2 pack_codes8(const uint32_t (&c)[8])
+{
+    return make_uint2((c[0] & 0xFF) | ((c[1] & 0xFF) << 8) | ((c[2] & 0xFF) << 16) | (c[3] << 24),
+                      (c[4] & 0xFF) | ((c[5] & 0xFF) << 8) | ((c[6] & 0xFF) << 16) | (c[7] << 24));
 }
 
 // Eight int8 codes of f * dyn for a finite dyn (dyn = 127 / amax with amax > 0 and not tiny):
@@ -109,19 +138,46 @@ __device__ __forceinline__ uint2 int8_codes8_finite(const float (&f)[8], float d
     return make_uint2(lo, hi);
 }
 
-__device__ __forceinline__ uint2 pack_codes8(const uint32_t (&c)[8])
+// Eight codes of the dynamic modes: type(f * dyn), NaN products -> 0.
+template <int CT>
+__device__ __forceinline__ uint2 dynamic_codes8(const float (&f)[8], float dyn)
 {
-    return make_uint2((c[0] & 0xFF) | ((c[1] & 0xFF) << 8) | ((c[2] & 0xFF) << 16) | (c[3] << 24),
-                      (c[4] & 0xFF) | ((c[5] & 0xFF) << 8) | ((c[6] & 0xFF) << 16) | (c[7] << 24));
+    if (CT == kCodeInt8 && __float_as_uint(dyn) < 0x7F800000u)    // dyn > 0 here
+        return int8_codes8_finite(f, dyn);
+    uint32_t c[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const float v = f[q] * dyn;
+        if (CT == kCodeInt8) c[q] = int8_code(v);
+        else c[q] = v != v ? 0u : fp8_code<CT>(v);
+    }
+    return pack_codes8(c);
 }
 
-template <int MODE, bool SMOOTH>
+// Eight static int8 codes (mode 1): the scales are already applied.
+__device__ __forceinline__ uint2 static_codes8(const float (&f)[8])
+{
+    uint32_t c[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) c[q] = int8_code(f[q]);
+    return pack_codes8(c);
+}
+
+// ---------------------------------------------------------------------------------------
+// vectorized path: one workgroup per token, kTileSlots 64-vector slots per wave
+// ---------------------------------------------------------------------------------------
+
+constexpr int kTileSlots = 2;        // 64-vector slots (1 KiB of bf16 each) per wave
+constexpr int kMaxTileWaves = 8;     // H <= 8192: at most 1024 vectors = 16 slots
+
+// MODE 0..5, CT the code type, SK the scales kind.
+template <int MODE, int CT, int SK>
 __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
     const int32_t* __restrict__ expand_idx, const int32_t* __restrict__ seg,
-    const float* __restrict__ smooth, void* __restrict__ expand_x,
-    float* __restrict__ dyn_scales, int32_t* __restrict__ assist, int W, int E, int BS,
-    int H, int K, int ns, long long cap)
+    const float* __restrict__ scales, void* __restrict__ expand_x,
+    void* __restrict__ dyn_scales, int32_t* __restrict__ assist, int W, int E, int BS,
+    int H, int K, int ns, long long cap, int e8m0)
 {
     __shared__ int32_t rows_lds[kMaxK];
     __shared__ int32_t exps_lds[kMaxK];
@@ -134,15 +190,26 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
     const int s = (int)(tok / BS);
     const int i = (int)(tok - (long long)s * BS);
     const int NV = H >> 3;
+    float* fscales = static_cast<float*>(dyn_scales);
 
-    // 1. this wave's slots of the token row, in flight before anything waits
+    // 1. this wave's slots of the token row (and of a shared scales row), in flight before
+    //    anything waits
     const uint4* xr = reinterpret_cast<const uint4*>(x) + tok * NV;
     uint4 raw[kTileSlots];
+    float4 shared_pre[kTileSlots][2];
 #pragma unroll
     for (int n = 0; n < kTileSlots; ++n) {
         const int v = lane + (wave * kTileSlots + n) * kWave;
-        if (v < NV) raw[n] = load_stream(xr + v);
+        if (v < NV) {
+            raw[n] = load_stream(xr + v);
+            if (SK == kScalesShared) {
+                const float4* sm = reinterpret_cast<const float4*>(scales);
+                shared_pre[n][0] = sm[2 * v];
+                shared_pre[n][1] = sm[2 * v + 1];
+            }
+        }
     }
+    const float scalar_pre = SK == kScalesScalar ? scales[0] : 1.0f;
 
     // 2. destination rows, resolved by threads 0..K-1
     if (threadIdx.x < K) {
@@ -163,18 +230,31 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
         }
     }
 
-    // 3. the token's absolute maximum (mode 2 without smooth scales), per wave first
-    if (MODE == 2 && !SMOOTH) {
-        uint32_t amax = 0;
+    // x_fp32 of this wave's slots when the codes are shared by every pick
+    float f[kTileSlots][8];
+    if (MODE != 0 && SK != kScalesPerExpert) {
 #pragma unroll
         for (int n = 0; n < kTileSlots; ++n) {
             const int v = lane + (wave * kTileSlots + n) * kWave;
             if (v < NV) {
-                float f[8];
-                unpack8(raw[n], f);
-                amax = absmax8(f, amax);
+                unpack8(raw[n], f[n]);
+                if (SK == kScalesScalar) {
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) f[n][q] = f[n][q] * scalar_pre;
+                }
+                if (SK == kScalesShared) mul8(f[n], shared_pre[n][0], shared_pre[n][1]);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) f[n][q] = 0.0f;
             }
         }
+    }
+
+    // 3. the token's absolute maximum (mode 2 with shared codes), per wave first
+    if (MODE == 2 && SK != kScalesPerExpert) {
+        uint32_t amax = 0;
+#pragma unroll
+        for (int n = 0; n < kTileSlots; ++n) amax = absmax8(f[n], amax);
         amax = wave_max_u32(amax);
         if (lane == 0) red[0][wave] = amax;
     }
@@ -204,82 +284,118 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
 
     uint2* out = reinterpret_cast<uint2*>(expand_x);     // 8 codes per vector
 
-    if (MODE == 2 && !SMOOTH) {
-        uint32_t amax = 0;
-        for (int w = 0; w < nw; ++w) amax = amax > red[0][w] ? amax : red[0][w];
-        const float dyn = 127.0f / __uint_as_float(amax);
-        const bool finite = __float_as_uint(dyn) < 0x7F800000u;          // dyn > 0 here
+    if (SK != kScalesPerExpert) {
+        // codes shared by every pick: quantize once, store K times
+        float dyn_tok = 0.0f;
+        if (MODE == 2) {
+            uint32_t amax = 0;
+            for (int w = 0; w < nw; ++w) amax = amax > red[0][w] ? amax : red[0][w];
+            dyn_tok = type_max<CT>() / __uint_as_float(amax);
+        }
 #pragma unroll
         for (int n = 0; n < kTileSlots; ++n) {
             const int v = lane + (wave * kTileSlots + n) * kWave;
-            if (v >= NV) continue;
-            float f[8];
-            unpack8(raw[n], f);
             uint2 packed;
-            if (finite) {
-                packed = int8_codes8_finite(f, dyn);
+            float scale = 0.0f;             // per group (mode 3) or per block (modes 4/5)
+            int se = 0;
+            if (MODE == 1) {
+                packed = static_codes8(f[n]);
+            } else if (MODE == 2) {
+                packed = dynamic_codes8<CT>(f[n], dyn_tok);
+            } else if (MODE == 3) {
+                const uint32_t amax = group_max_u32<kGroup / 8>(absmax8(f[n], 0u));
+                const float dyn = type_max<CT>() / __uint_as_float(amax);
+                packed = dynamic_codes8<CT>(f[n], dyn);
+                scale = 1.0f / dyn;
             } else {
+                const uint32_t amax = group_max_u32<kMxBlock / 8>(absmax8(f[n], 0u));
+                se = mx_shared_exp<MODE, CT>(amax);
+                const float inv = __uint_as_float((uint32_t)(127 - se) << 23);   // 2^-se
                 uint32_t c[8];
 #pragma unroll
-                for (int q = 0; q < 8; ++q) c[q] = int8_code(f[q], dyn);
+                for (int q = 0; q < 8; ++q) c[q] = fp8_code<CT>(f[n][q] * inv);
                 packed = pack_codes8(c);
+                scale = pow2f(se);
             }
+            if (v >= NV) continue;
 #pragma unroll
-            for (int k = 0; k < kMaxK; ++k)
-                if (rows[k] >= 0) store_stream(out + (long long)rows[k] * NV + v, packed);
+            for (int k = 0; k < kMaxK; ++k) {
+                if (rows[k] < 0) continue;
+                store_stream(out + (long long)rows[k] * NV + v, packed);
+                if (MODE == 3 && (v & (kGroup / 8 - 1)) == 0)
+                    fscales[(long long)rows[k] * ns + (v >> 4)] = scale;
+                if (MODE >= 4 && (v & 3) == 0) {
+                    if (e8m0)
+                        static_cast<uint8_t*>(dyn_scales)[(long long)rows[k] * ns + (v >> 2)] =
+                            (uint8_t)(se + 127);
+                    else
+                        fscales[(long long)rows[k] * ns + (v >> 2)] = scale;
+                }
+            }
         }
-        if (threadIdx.x == 0) {
-            const float scale = 1.0f / dyn;
+        if (MODE == 2 && threadIdx.x == 0) {
+            const float scale = 1.0f / dyn_tok;
 #pragma unroll
             for (int k = 0; k < kMaxK; ++k)
-                if (rows[k] >= 0) dyn_scales[rows[k]] = scale;
+                if (rows[k] >= 0) fscales[rows[k]] = scale;
+        }
+        if (MODE >= 4 && threadIdx.x == 0) {
+            const int nb = (H + kMxBlock - 1) / kMxBlock;
+            if (ns > nb) {
+#pragma unroll
+                for (int k = 0; k < kMaxK; ++k) {
+                    if (rows[k] < 0) continue;
+                    if (e8m0) static_cast<uint8_t*>(dyn_scales)[(long long)rows[k] * ns + nb] = 0;
+                    else fscales[(long long)rows[k] * ns + nb] = 0.0f;
+                }
+            }
         }
         return;
     }
 
-    if (MODE == 2) {   // smooth scales: one quantization per pick, on its expert's row
-        // The picks run one after another (each needs a workgroup-wide maximum); the smooth
-        // slice of the next routed pick is loaded into the other register buffer while the
-        // current pick reduces, synchronizes and stores, so its latency is hidden.
-        float4 sm_cur[kTileSlots][2], sm_nxt[kTileSlots][2];
-        auto load_smooth = [&](int pick, float4 (&dst)[kTileSlots][2]) {
-            const float4* sm =
-                reinterpret_cast<const float4*>(smooth + (long long)exps_lds[pick] * H);
+    // Per-expert scales (modes 1-3): one quantization per pick, on its expert's row.  The
+    // picks run one after another; the scales slice of the next routed pick is loaded into
+    // the other register buffer while the current pick is quantized and stored, so its
+    // latency is hidden.  Mode 2 needs a workgroup-wide maximum per pick; modes 1 and 3 do
+    // not synchronize at all.
+    float4 sm_cur[kTileSlots][2], sm_nxt[kTileSlots][2];
+    auto load_pre = [&](int pick, float4 (&dst)[kTileSlots][2]) {
+        const float4* sm =
+            reinterpret_cast<const float4*>(scales + (long long)exps_lds[pick] * H);
 #pragma unroll
-            for (int n = 0; n < kTileSlots; ++n) {
-                const int v = lane + (wave * kTileSlots + n) * kWave;
-                if (v < NV) {
-                    dst[n][0] = sm[2 * v];
-                    dst[n][1] = sm[2 * v + 1];
-                }
+        for (int n = 0; n < kTileSlots; ++n) {
+            const int v = lane + (wave * kTileSlots + n) * kWave;
+            if (v < NV) {
+                dst[n][0] = sm[2 * v];
+                dst[n][1] = sm[2 * v + 1];
             }
-        };
-        int pk = 0;
-        while (pk < K && rows[pk] < 0) ++pk;                 // first routed pick (uniform)
-        if (pk < K) load_smooth(pk, sm_cur);
-        for (int round = 0; pk < K; ++round) {
-            const int cur = round & 1;
-            int nxt = pk + 1;
-            while (nxt < K && rows[nxt] < 0) ++nxt;
-            if (nxt < K) load_smooth(nxt, sm_nxt);
-            const int prow = rows[pk];
-            // x * smooth stays in registers between the maximum and the codes
-            float f[kTileSlots][8];
-            uint32_t amax = 0;
+        }
+    };
+    int pk = 0;
+    while (pk < K && rows[pk] < 0) ++pk;                 // first routed pick (uniform)
+    if (pk < K) load_pre(pk, sm_cur);
+    for (int round = 0; pk < K; ++round) {
+        const int cur = round & 1;
+        int nxt = pk + 1;
+        while (nxt < K && rows[nxt] < 0) ++nxt;
+        if (nxt < K) load_pre(nxt, sm_nxt);
+        const int prow = rows[pk];
+        // x * scales stays in registers between the maximum and the codes
+        uint32_t amax = 0;
 #pragma unroll
-            for (int n = 0; n < kTileSlots; ++n) {
-                const int v = lane + (wave * kTileSlots + n) * kWave;
-                if (v < NV) {
-                    unpack8(raw[n], f[n]);
-                    const float4 a = sm_cur[n][0];
-                    const float4 b = sm_cur[n][1];
-                    f[n][0] = f[n][0] * a.x; f[n][1] = f[n][1] * a.y;
-                    f[n][2] = f[n][2] * a.z; f[n][3] = f[n][3] * a.w;
-                    f[n][4] = f[n][4] * b.x; f[n][5] = f[n][5] * b.y;
-                    f[n][6] = f[n][6] * b.z; f[n][7] = f[n][7] * b.w;
-                    amax = absmax8(f[n], amax);
-                }
+        for (int n = 0; n < kTileSlots; ++n) {
+            const int v = lane + (wave * kTileSlots + n) * kWave;
+            if (v < NV) {
+                unpack8(raw[n], f[n]);
+                mul8(f[n], sm_cur[n][0], sm_cur[n][1]);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) f[n][q] = 0.0f;
             }
+            if (MODE == 2) amax = absmax8(f[n], amax);
+        }
+        float dyn = 0.0f;
+        if (MODE == 2) {
             amax = wave_max_u32(amax);
             // alternating buffers: a wave can only write this buffer again two picks later,
             // after the next barrier, by which time every wave has read it
@@ -287,108 +403,108 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
             __syncthreads();
             amax = 0;
             for (int w = 0; w < nw; ++w) amax = amax > red[cur][w] ? amax : red[cur][w];
-            const float dyn = 127.0f / __uint_as_float(amax);
-            const bool finite = __float_as_uint(dyn) < 0x7F800000u;
+            dyn = type_max<CT>() / __uint_as_float(amax);
+        }
 #pragma unroll
-            for (int n = 0; n < kTileSlots; ++n) {
-                const int v = lane + (wave * kTileSlots + n) * kWave;
-                if (v >= NV) continue;
-                uint2 packed;
-                if (finite) {
-                    packed = int8_codes8_finite(f[n], dyn);
-                } else {
-                    uint32_t c[8];
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) c[q] = int8_code(f[n][q], dyn);
-                    packed = pack_codes8(c);
-                }
-                store_stream(out + (long long)prow * NV + v, packed);
+        for (int n = 0; n < kTileSlots; ++n) {
+            const int v = lane + (wave * kTileSlots + n) * kWave;
+            uint2 packed;
+            float gscale = 0.0f;
+            if (MODE == 1) {
+                packed = static_codes8(f[n]);
+            } else if (MODE == 2) {
+                packed = dynamic_codes8<CT>(f[n], dyn);
+            } else {
+                const uint32_t gmax = group_max_u32<kGroup / 8>(absmax8(f[n], 0u));
+                const float gdyn = type_max<CT>() / __uint_as_float(gmax);
+                packed = dynamic_codes8<CT>(f[n], gdyn);
+                gscale = 1.0f / gdyn;
             }
-            if (threadIdx.x == 0) dyn_scales[prow] = 1.0f / dyn;
-#pragma unroll
-            for (int n = 0; n < kTileSlots; ++n) {
-                sm_cur[n][0] = sm_nxt[n][0];
-                sm_cur[n][1] = sm_nxt[n][1];
-            }
-            pk = nxt;
+            if (v >= NV) continue;
+            store_stream(out + (long long)prow * NV + v, packed);
+            if (MODE == 3 && (v & (kGroup / 8 - 1)) == 0)
+                fscales[(long long)prow * ns + (v >> 4)] = gscale;
         }
-        return;
-    }
-
-    // MX modes 4 and 5: a 32-element block is 4 adjacent lanes of one wave
-    const int nb = (H + kMxBlock - 1) / kMxBlock;
+        if (MODE == 2 && threadIdx.x == 0) fscales[prow] = 1.0f / dyn;
 #pragma unroll
-    for (int n = 0; n < kTileSlots; ++n) {
-        const int v = lane + (wave * kTileSlots + n) * kWave;
-        float f[8];
-        uint32_t amax = 0;
-        if (v < NV) {
-            unpack8(raw[n], f);
-            amax = absmax8(f, 0u);
+        for (int n = 0; n < kTileSlots; ++n) {
+            sm_cur[n][0] = sm_nxt[n][0];
+            sm_cur[n][1] = sm_nxt[n][1];
         }
-        amax = group_max_u32<4>(amax);
-        if (v >= NV) continue;
-        const int se = mx_shared_exp<MODE>(amax);
-        const float inv = __uint_as_float((uint32_t)(127 - se) << 23);       // 2^-se, exact
-        uint32_t c[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) c[q] = e4m3_code(f[q] * inv);
-        const uint2 packed = pack_codes8(c);
-        const bool lead = (v & 3) == 0;
-        const float scale = pow2f(se);
-#pragma unroll
-        for (int k = 0; k < kMaxK; ++k) {
-            if (rows[k] < 0) continue;
-            store_stream(out + (long long)rows[k] * NV + v, packed);
-            if (lead) dyn_scales[(long long)rows[k] * ns + (v >> 2)] = scale;
-        }
-    }
-    if (threadIdx.x == 0 && ns > nb) {
-#pragma unroll
-        for (int k = 0; k < kMaxK; ++k)
-            if (rows[k] >= 0) dyn_scales[(long long)rows[k] * ns + nb] = 0.0f;
+        pk = nxt;
     }
 }
 
-template <int MODE, bool SMOOTH>
-hipError_t launch_tile_mode(const Shape& sh, const void* x, const int32_t* ids,
-                            const int32_t* expand_idx, const int32_t* seg, const float* smooth,
-                            void* expand_x, float* dyn_scales, int32_t* assist,
-                            hipStream_t stream)
+template <int MODE, int CT, int SK>
+hipError_t launch_tile_variant(const Shape& sh, const void* x, const int32_t* ids,
+                               const int32_t* expand_idx, const int32_t* seg,
+                               const float* scales, void* expand_x, void* dyn_scales,
+                               int32_t* assist, hipStream_t stream)
 {
     const long long T = (long long)sh.W * sh.BS;
     const int slots = ((sh.H >> 3) + kWave - 1) / kWave;
     const int waves = (slots + kTileSlots - 1) / kTileSlots;        // <= kMaxTileWaves
-    hipLaunchKernelGGL((scatter_tile_kernel<MODE, SMOOTH>), dim3((unsigned)T),
+    hipLaunchKernelGGL((scatter_tile_kernel<MODE, CT, SK>), dim3((unsigned)T),
                        dim3(kWave * waves), 0, stream, static_cast<const uint16_t*>(x), ids,
-                       expand_idx, seg, smooth, expand_x, dyn_scales, assist, sh.W, sh.E, sh.BS,
-                       sh.H, sh.K, sh.scales_per_row, (long long)sh.cap);
+                       expand_idx, seg, scales, expand_x, dyn_scales, assist, sh.W, sh.E,
+                       sh.BS, sh.H, sh.K, sh.scales_per_row, (long long)sh.cap,
+                       sh.scale_e8m0);
     return hipGetLastError();
 }
 
-hipError_t launch_tile(const Shape& sh, const void* x, const int32_t* ids,
-                       const int32_t* expand_idx, const int32_t* seg, const float* smooth,
-                       void* expand_x, float* dyn_scales, int32_t* assist, hipStream_t stream)
+template <int MODE, int CT>
+hipError_t launch_tile_scales(const Shape& sh, const void* x, const int32_t* ids,
+                              const int32_t* expand_idx, const int32_t* seg,
+                              const float* scales, void* expand_x, void* dyn_scales,
+                              int32_t* assist, hipStream_t stream)
 {
-    switch (sh.quant_mode) {
-    case 0:
-        return launch_tile_mode<0, false>(sh, x, ids, expand_idx, seg, smooth, expand_x,
-                                          dyn_scales, assist, stream);
-    case 2:
-        if (smooth)
-            return launch_tile_mode<2, true>(sh, x, ids, expand_idx, seg, smooth, expand_x,
-                                             dyn_scales, assist, stream);
-        return launch_tile_mode<2, false>(sh, x, ids, expand_idx, seg, smooth, expand_x,
-                                          dyn_scales, assist, stream);
-    case 4:
-        return launch_tile_mode<4, false>(sh, x, ids, expand_idx, seg, smooth, expand_x,
-                                          dyn_scales, assist, stream);
-    case 5:
-        return launch_tile_mode<5, false>(sh, x, ids, expand_idx, seg, smooth, expand_x,
-                                          dyn_scales, assist, stream);
+#define MOE_DC_TILE(SK)                                                                    \
+    launch_tile_variant<MODE, CT, SK>(sh, x, ids, expand_idx, seg, scales, expand_x,      \
+                                      dyn_scales, assist, stream)
+    switch (sh.scales_kind) {
+    case kScalesNone:
+        if constexpr (MODE == 1) return hipErrorInvalidValue;    // mode 1 needs scales
+        else return MOE_DC_TILE(kScalesNone);
+    case kScalesScalar:
+        return MOE_DC_TILE(kScalesScalar);
+    case kScalesShared:
+        return MOE_DC_TILE(kScalesShared);
+    case kScalesPerExpert:
+        return MOE_DC_TILE(kScalesPerExpert);
     default:
         return hipErrorInvalidValue;
     }
+#undef MOE_DC_TILE
+}
+
+hipError_t launch_tile(const Shape& sh, const void* x, const int32_t* ids,
+                       const int32_t* expand_idx, const int32_t* seg, const float* scales,
+                       void* expand_x, void* dyn_scales, int32_t* assist, hipStream_t stream)
+{
+#define MOE_DC_ARGS sh, x, ids, expand_idx, seg, scales, expand_x, dyn_scales, assist, stream
+    const int ct = sh.code_type;
+    switch (sh.quant_mode) {
+    case 0:
+        return launch_tile_variant<0, kCodeBf16, kScalesNone>(MOE_DC_ARGS);
+    case 1:
+        return launch_tile_scales<1, kCodeInt8>(MOE_DC_ARGS);
+    case 2:
+        if (ct == kCodeInt8) return launch_tile_scales<2, kCodeInt8>(MOE_DC_ARGS);
+        if (ct == kCodeE4m3) return launch_tile_scales<2, kCodeE4m3>(MOE_DC_ARGS);
+        return launch_tile_scales<2, kCodeE5m2>(MOE_DC_ARGS);
+    case 3:
+        if (ct == kCodeE4m3) return launch_tile_scales<3, kCodeE4m3>(MOE_DC_ARGS);
+        return launch_tile_scales<3, kCodeE5m2>(MOE_DC_ARGS);
+    case 4:
+        if (ct == kCodeE4m3) return launch_tile_variant<4, kCodeE4m3, kScalesNone>(MOE_DC_ARGS);
+        return launch_tile_variant<4, kCodeE5m2, kScalesNone>(MOE_DC_ARGS);
+    case 5:
+        if (ct == kCodeE4m3) return launch_tile_variant<5, kCodeE4m3, kScalesNone>(MOE_DC_ARGS);
+        return launch_tile_variant<5, kCodeE5m2, kScalesNone>(MOE_DC_ARGS);
+    default:
+        return hipErrorInvalidValue;
+    }
+#undef MOE_DC_ARGS
 }
 
 // ---------------------------------------------------------------------------------------
@@ -397,24 +513,49 @@ hipError_t launch_tile(const Shape& sh, const void* x, const int32_t* ids,
 
 constexpr int kElemThreads = 1024;
 constexpr int kElemPerLane = 8;      // H <= 8192 = 1024 lanes x 8
+constexpr int kElemWaves = kElemThreads / kWave;
 
-template <int MODE, bool SMOOTH>
+__device__ __forceinline__ uint32_t fp8_code_rt(int ct, float v)
+{
+    return ct == kCodeE4m3 ? e4m3_code(v) : e5m2_code(v);
+}
+
+__device__ __forceinline__ uint32_t dynamic_code_rt(int ct, float v)
+{
+    if (ct == kCodeInt8) return int8_code(v);
+    return v != v ? 0u : fp8_code_rt(ct, v);
+}
+
+__device__ __forceinline__ float type_max_rt(int ct)
+{
+    return ct == kCodeInt8 ? 127.0f : ct == kCodeE4m3 ? 448.0f : 57344.0f;
+}
+
+// The variant (mode, code type, scales kind, E8M0 scales) is a runtime argument here: this
+// kernel serves odd sizes and alignments only, where clarity matters more than speed.
+// Requires blockDim.x == 1024 for mode 3 (so a 128-element group is two whole waves of one
+// pass), which holds for every valid H (>= 1024).
 __global__ __launch_bounds__(kElemThreads) void scatter_elem_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
     const int32_t* __restrict__ expand_idx, const int32_t* __restrict__ seg,
-    const float* __restrict__ smooth, void* __restrict__ expand_x,
-    float* __restrict__ dyn_scales, int32_t* __restrict__ assist, int W, int E, int BS,
-    int H, int K, int ns, long long cap)
+    const float* __restrict__ scales, void* __restrict__ expand_x,
+    void* __restrict__ dyn_scales, int32_t* __restrict__ assist, int W, int E, int BS,
+    int H, int K, int ns, long long cap, int mode, int ct, int sk, int e8m0)
 {
     __shared__ long long row_of[kMaxK];
     __shared__ int32_t exp_of[kMaxK];
-    __shared__ uint32_t red[kElemThreads / kWave];
+    __shared__ uint32_t red[kElemWaves];
+    __shared__ uint32_t gred[kElemPerLane][kElemWaves];
 
     const long long tok = blockIdx.x;
     const int s = (int)(tok / BS);
     const int i = (int)(tok - (long long)s * BS);
     const int t = threadIdx.x;
     const int nt = blockDim.x;
+    const int lane = t & (kWave - 1);
+    const int wave = t / kWave;
+    float* fscales = static_cast<float*>(dyn_scales);
+    uint8_t* bscales = static_cast<uint8_t*>(dyn_scales);
 
     if (t < K) {
         const int32_t ord = expand_idx[tok * K + t];
@@ -445,7 +586,7 @@ __global__ __launch_bounds__(kElemThreads) void scatter_elem_kernel(
         if (h < H) raw[n] = xr[h];
     }
 
-    if (MODE == 0) {
+    if (mode == 0) {
         uint16_t* out = reinterpret_cast<uint16_t*>(expand_x);
         for (int k = 0; k < K; ++k) {
             const long long row = row_of[k];
@@ -460,138 +601,133 @@ __global__ __launch_bounds__(kElemThreads) void scatter_elem_kernel(
     }
 
     uint8_t* out = reinterpret_cast<uint8_t*>(expand_x);
-
-    if (MODE == 2) {
-        // Without smooth scales every pick carries the same codes, so one pass serves all K;
-        // with smooth scales each pick is quantized on its own expert's row.
-        const int passes = SMOOTH ? K : 1;
-        for (int pk = 0; pk < passes; ++pk) {
-            if (SMOOTH && row_of[pk] < 0) continue;        // uniform over the workgroup
-            const float* sm = SMOOTH ? smooth + (long long)exp_of[pk] * H : nullptr;
-            uint32_t amax = 0;
-#pragma unroll
-            for (int n = 0; n < kElemPerLane; ++n) {
-                const int h = t + n * nt;
-                if (h < H) {
-                    float f = bf16_lo(raw[n]);
-                    if (SMOOTH) f = f * sm[h];
-                    const uint32_t b = __float_as_uint(f) & 0x7FFFFFFFu;
-                    amax = amax > b ? amax : b;
-                }
-            }
-            amax = block_max_u32(amax, red);
-            const float dyn = 127.0f / __uint_as_float(amax);
-#pragma unroll
-            for (int n = 0; n < kElemPerLane; ++n) {
-                const int h = t + n * nt;
-                if (h >= H) continue;
-                float f = bf16_lo(raw[n]);
-                if (SMOOTH) f = f * sm[h];
-                const uint8_t c = (uint8_t)int8_code(f, dyn);
-                if (SMOOTH) {
-                    out[row_of[pk] * H + h] = c;
-                } else {
-                    for (int k = 0; k < K; ++k)
-                        if (row_of[k] >= 0) out[row_of[k] * H + h] = c;
-                }
-            }
-            if (t == 0) {
-                const float scale = 1.0f / dyn;
-                if (SMOOTH) {
-                    dyn_scales[row_of[pk]] = scale;
-                } else {
-                    for (int k = 0; k < K; ++k)
-                        if (row_of[k] >= 0) dyn_scales[row_of[k]] = scale;
-                }
-            }
-        }
-        return;
-    }
-
-    // MX modes 4 and 5: a 32-element block is 32 adjacent lanes
     const int nb = (H + kMxBlock - 1) / kMxBlock;
-#pragma unroll
-    for (int n = 0; n < kElemPerLane; ++n) {
-        const int h = t + n * nt;
-        if (n * nt >= H) break;                            // uniform across the workgroup
-        float f = 0.0f;
+    const float tmax = type_max_rt(ct);
+
+    // Per-expert scales make the codes per pick; otherwise one pass serves all K picks.
+    const int passes = sk == kScalesPerExpert ? K : 1;
+    for (int pk = 0; pk < passes; ++pk) {
+        if (sk == kScalesPerExpert && row_of[pk] < 0) continue;   // uniform over the block
+        const float* pre = sk == kScalesPerExpert ? scales + (long long)exp_of[pk] * H : scales;
+        float f[kElemPerLane];
+        uint32_t a[kElemPerLane];
         uint32_t amax = 0;
-        if (h < H) {
-            f = bf16_lo(raw[n]);
-            amax = __float_as_uint(f) & 0x7FFFFFFFu;
+#pragma unroll
+        for (int n = 0; n < kElemPerLane; ++n) {
+            const int h = t + n * nt;
+            f[n] = 0.0f;
+            if (h < H) {
+                f[n] = bf16_lo(raw[n]);
+                if (sk == kScalesScalar) f[n] = f[n] * pre[0];
+                if (sk == kScalesShared || sk == kScalesPerExpert) f[n] = f[n] * pre[h];
+            }
+            a[n] = __float_as_uint(f[n]) & 0x7FFFFFFFu;
+            amax = amax > a[n] ? amax : a[n];
         }
-        amax = group_max_u32<kMxBlock>(amax);
-        if (h >= H) continue;
-        const int se = mx_shared_exp<MODE>(amax);
-        const float inv = __uint_as_float((uint32_t)(127 - se) << 23);       // 2^-se, exact
-        const uint8_t c = (uint8_t)e4m3_code(f * inv);
-        const bool lead = (h % kMxBlock) == 0;
-        const float scale = pow2f(se);
-        for (int k = 0; k < K; ++k) {
-            const long long row = row_of[k];
-            if (row < 0) continue;
-            out[row * H + h] = c;
-            if (lead) dyn_scales[row * ns + h / kMxBlock] = scale;
+        float dyn_tok = 0.0f;
+        if (mode == 2) {
+            amax = block_max_u32(amax, red);
+            dyn_tok = tmax / __uint_as_float(amax);
         }
-    }
-    if (t == 0 && ns > nb) {
-        for (int k = 0; k < K; ++k)
-            if (row_of[k] >= 0) dyn_scales[row_of[k] * ns + nb] = 0.0f;
+        if (mode == 3) {
+            // each 128-element group is the two waves 2j, 2j+1 of one pass
+#pragma unroll
+            for (int n = 0; n < kElemPerLane; ++n) {
+                const uint32_t w = wave_max_u32(a[n]);
+                if (lane == 0) gred[n][wave] = w;
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int n = 0; n < kElemPerLane; ++n) {
+            const int h = t + n * nt;
+            if (n * nt >= H) break;                        // uniform across the workgroup
+            uint32_t code = 0;
+            float scale = 0.0f;
+            uint32_t sbyte = 0;
+            bool lead = false;
+            int sidx = 0;
+            if (mode == 1) {
+                code = int8_code(f[n]);
+            } else if (mode == 2) {
+                code = dynamic_code_rt(ct, f[n] * dyn_tok);
+            } else if (mode == 3) {
+                const int w0 = wave & ~1;
+                const uint32_t g = gred[n][w0] > gred[n][w0 + 1] ? gred[n][w0] : gred[n][w0 + 1];
+                const float dyn = tmax / __uint_as_float(g);
+                code = dynamic_code_rt(ct, f[n] * dyn);
+                scale = 1.0f / dyn;
+                lead = (h % kGroup) == 0;
+                sidx = h / kGroup;
+            } else {
+                const uint32_t bm = group_max_u32<kMxBlock>(a[n]);
+                const int se = mode == 4
+                    ? (ct == kCodeE4m3 ? mx_shared_exp<4, kCodeE4m3>(bm)
+                                       : mx_shared_exp<4, kCodeE5m2>(bm))
+                    : (ct == kCodeE4m3 ? mx_shared_exp<5, kCodeE4m3>(bm)
+                                       : mx_shared_exp<5, kCodeE5m2>(bm));
+                const float inv = __uint_as_float((uint32_t)(127 - se) << 23);   // 2^-se
+                code = fp8_code_rt(ct, f[n] * inv);
+                scale = pow2f(se);
+                sbyte = (uint32_t)(se + 127);
+                lead = (h % kMxBlock) == 0;
+                sidx = h / kMxBlock;
+            }
+            if (h >= H) continue;
+            for (int k = 0; k < K; ++k) {
+                const long long row = sk == kScalesPerExpert ? (k == pk ? row_of[pk] : -1)
+                                                             : row_of[k];
+                if (row < 0) continue;
+                out[row * H + h] = (uint8_t)code;
+                if (lead) {
+                    if (e8m0) bscales[row * ns + sidx] = (uint8_t)sbyte;
+                    else fscales[row * ns + sidx] = scale;
+                }
+            }
+        }
+        if (t == 0) {
+            for (int k = 0; k < K; ++k) {
+                const long long row = sk == kScalesPerExpert ? (k == pk ? row_of[pk] : -1)
+                                                             : row_of[k];
+                if (row < 0) continue;
+                if (mode == 2) fscales[row] = 1.0f / dyn_tok;
+                if (mode >= 4 && ns > nb) {
+                    if (e8m0) bscales[row * ns + nb] = 0;
+                    else fscales[row * ns + nb] = 0.0f;
+                }
+            }
+        }
+        if (mode == 3) __syncthreads();                    // gred is reused by the next pick
     }
 }
 
-template <int MODE, bool SMOOTH>
-hipError_t launch_elem_mode(const Shape& sh, const void* x, const int32_t* ids,
-                            const int32_t* expand_idx, const int32_t* seg, const float* smooth,
-                            void* expand_x, float* dyn_scales, int32_t* assist,
-                            hipStream_t stream)
+hipError_t launch_elem(const Shape& sh, const void* x, const int32_t* ids,
+                       const int32_t* expand_idx, const int32_t* seg, const float* scales,
+                       void* expand_x, void* dyn_scales, int32_t* assist, hipStream_t stream)
 {
     const long long T = (long long)sh.W * sh.BS;
     const int want = (sh.H + kWave - 1) / kWave * kWave;
     const int threads = want < kElemThreads ? want : kElemThreads;
-    hipLaunchKernelGGL((scatter_elem_kernel<MODE, SMOOTH>), dim3((unsigned)T), dim3(threads),
-                       0, stream, static_cast<const uint16_t*>(x), ids, expand_idx, seg, smooth,
+    if (sh.quant_mode == 3 && threads != kElemThreads) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(scatter_elem_kernel, dim3((unsigned)T), dim3(threads), 0, stream,
+                       static_cast<const uint16_t*>(x), ids, expand_idx, seg, scales,
                        expand_x, dyn_scales, assist, sh.W, sh.E, sh.BS, sh.H, sh.K,
-                       sh.scales_per_row, (long long)sh.cap);
+                       sh.scales_per_row, (long long)sh.cap, sh.quant_mode, sh.code_type,
+                       sh.scales_kind, sh.scale_e8m0);
     return hipGetLastError();
-}
-
-hipError_t launch_elem(const Shape& sh, const void* x, const int32_t* ids,
-                       const int32_t* expand_idx, const int32_t* seg, const float* smooth,
-                       void* expand_x, float* dyn_scales, int32_t* assist, hipStream_t stream)
-{
-    switch (sh.quant_mode) {
-    case 0:
-        return launch_elem_mode<0, false>(sh, x, ids, expand_idx, seg, smooth, expand_x,
-                                          dyn_scales, assist, stream);
-    case 2:
-        if (smooth)
-            return launch_elem_mode<2, true>(sh, x, ids, expand_idx, seg, smooth, expand_x,
-                                             dyn_scales, assist, stream);
-        return launch_elem_mode<2, false>(sh, x, ids, expand_idx, seg, smooth, expand_x,
-                                          dyn_scales, assist, stream);
-    case 4:
-        return launch_elem_mode<4, false>(sh, x, ids, expand_idx, seg, smooth, expand_x,
-                                          dyn_scales, assist, stream);
-    case 5:
-        return launch_elem_mode<5, false>(sh, x, ids, expand_idx, seg, smooth, expand_x,
-                                          dyn_scales, assist, stream);
-    default:
-        return hipErrorInvalidValue;
-    }
 }
 
 }  // namespace
 
 hipError_t launch_scatter(const Shape& sh, const void* x, const int32_t* expert_ids,
-                          const int32_t* expand_idx, const int32_t* seg, const float* smooth,
-                          void* expand_x, float* dynamic_scales, int32_t* assist_info,
+                          const int32_t* expand_idx, const int32_t* seg, const float* scales,
+                          void* expand_x, void* dynamic_scales, int32_t* assist_info,
                           bool vectorized, hipStream_t stream)
 {
     if (vectorized)
-        return launch_tile(sh, x, expert_ids, expand_idx, seg, smooth, expand_x,
+        return launch_tile(sh, x, expert_ids, expand_idx, seg, scales, expand_x,
                            dynamic_scales, assist_info, stream);
-    return launch_elem(sh, x, expert_ids, expand_idx, seg, smooth, expand_x, dynamic_scales,
+    return launch_elem(sh, x, expert_ids, expand_idx, seg, scales, expand_x, dynamic_scales,
                        assist_info, stream);
 }
 

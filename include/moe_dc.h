@@ -43,41 +43,76 @@ extern "C" {
 typedef enum {
     MOE_OK = 0,
     MOE_ERR_INVALID_ARG = -1,   /* a range, divisibility, pointer or size rule is broken   */
-    MOE_ERR_UNSUPPORTED = -2,   /* allowed by the pages but not built (modes 1/3, const)   */
+    MOE_ERR_UNSUPPORTED = -2,   /* allowed by the pages but not built (const experts)      */
     MOE_ERR_WORKSPACE = -3,     /* workspace missing or smaller than the query returned    */
     MOE_ERR_DEVICE = -4         /* a HIP runtime call failed                               */
 } moe_status;
 
+/* Element type of expand_x ([LLD] 约束说明 lists the types each quant mode allows). */
+typedef enum {
+    MOE_DTYPE_DEFAULT = 0,      /* the mode's default: bf16 (mode 0), int8 (modes 1, 2),
+                                   E4M3 (modes 3, 4, 5)                                     */
+    MOE_DTYPE_INT8 = 1,         /* modes 1, 2                                              */
+    MOE_DTYPE_E4M3 = 2,         /* OCP E4M3 ("fn": bias 7, max 448); modes 2-5             */
+    MOE_DTYPE_E5M2 = 3          /* OCP E5M2 (bias 15, max 57344); modes 2-5                */
+} moe_dtype;
+
+/* Shape of the quantization scales tensor ([LLD] 约束说明: for mode 1 a scalar quant
+ * coefficient, a row shared by every expert, or one row per expert; modes 2 and 3 take the
+ * same shapes as smooth scales). */
+typedef enum {
+    MOE_SCALES_NONE = 0,        /* no scales tensor (modes 0, 2, 3, 4, 5)                  */
+    MOE_SCALES_SCALAR = 1,      /* fp32 [1]                                                */
+    MOE_SCALES_SHARED = 2,      /* fp32 [H], the same row for every expert                 */
+    MOE_SCALES_PER_EXPERT = 3   /* fp32 [E][H]; the routed expert's row, so quantization is
+                                   per pick                                                */
+} moe_scales_kind;
+
+/* Storage of the MX block scales (modes 4/5). */
+typedef enum {
+    MOE_SCALE_FP32 = 0,         /* fp32 2^shared_exp                                        */
+    MOE_SCALE_E8M0 = 1          /* one byte shared_exp + 127 ([SMP] 通信前量化 stores the MX
+                                   scale as an E8M0 value)                                  */
+} moe_scale_format;
+
 /* Operator attributes ([OPS] 参数说明; [LLD] 约束说明).  One struct serves both calls; the
  * pages require the same values on every rank and for dispatch and its combine
- * ([OPS] 约束说明, cross-card consistency), which one struct gives for free. */
+ * ([OPS] 约束说明, cross-card consistency), which one struct gives for free.
+ * Layout: sixteen int32 then one int64, 72 bytes, no padding. */
 typedef struct {
     int32_t ep_world_size;          /* W, in [2, 768]                                        */
     int32_t moe_expert_num;         /* E, in (0, 1024], E % W == 0; L*W <= 2048               */
     int32_t bs;                     /* BS tokens per rank, in [1, 512]                        */
     int32_t hidden;                 /* H, in [1024, 8192]                                     */
     int32_t topk;                   /* K, in (0, 16], K <= E + zero + copy + const            */
-    int32_t quant_mode;             /* 0 none, 2 int8 per token, 4 MX E4M3, 5 MX clip E4M3;
-                                       1 and 3 -> MOE_ERR_UNSUPPORTED                          */
+    int32_t quant_mode;             /* 0 none, 1 static int8, 2 dynamic per token,
+                                       3 dynamic per 128-element group, 4 MX, 5 MX clip       */
     int32_t zero_expert_num;        /* >= 0; ids [E, E+Z) are zero experts                    */
     int32_t copy_expert_num;        /* >= 0; ids [E+Z, E+Z+C) are copy experts               */
     int32_t const_expert_num;       /* must be 0 (its parameters are not on the pages)        */
     int32_t expert_token_nums_type; /* 0 = running sum over local experts, 1 = counts         */
     int32_t mask_kind;              /* 0 none, 1 per token [W][BS], 2 per pick [W][BS][K]     */
-    int32_t reserved;               /* must be 0                                              */
+    int32_t out_dtype;              /* moe_dtype: mode 0 DEFAULT only; mode 1 DEFAULT/INT8;
+                                       mode 2 any; modes 3-5 DEFAULT/E4M3/E5M2               */
+    int32_t scales_kind;            /* moe_scales_kind: mode 1 SCALAR/SHARED/PER_EXPERT;
+                                       modes 2, 3 any; modes 0, 4, 5 NONE                     */
+    int32_t scale_format;           /* moe_scale_format: E8M0 only with modes 4/5            */
+    int32_t reserved[2];            /* must be 0                                              */
     int64_t expand_rows_capacity;   /* rows of expand_x / dynamic_scales / assist_info and of
                                        expert_out; must be >= W*BS*K                           */
 } moe_dc_config;
 
 /* Host-only check of every rule the pages state for the attributes ([OPS] 约束说明 and the
  * wrapper's checks under 调用说明; [LLD] 约束说明): the ranges above, E % W == 0,
- * L*W <= 2048, K <= E+Z+C+const, E+Z+C+const < INT32_MAX, capacity >= W*BS*K and < 2^31.
+ * L*W <= 2048, K <= E+Z+C+const, E+Z+C+const < INT32_MAX, capacity >= W*BS*K and < 2^31,
+ * and the pairings of quant_mode with out_dtype, scales_kind and scale_format above.
  * Returns MOE_OK, MOE_ERR_INVALID_ARG or MOE_ERR_UNSUPPORTED.  Touches no device. */
 moe_status moe_dc_validate(const moe_dc_config* cfg);
 
-/* fp32 scales per expand_x row for cfg->quant_mode: 0 for mode 0, 1 for mode 2, and
- * Align2(Ceil(H, 32)) for modes 4/5 (the dynamic_scales shape rule of [LLD] 约束说明).
- * Returns -1 for an invalid config. */
+/* Scales per expand_x row for cfg->quant_mode (the dynamic_scales shape rule of [LLD]
+ * 约束说明): 0 for modes 0 and 1, 1 for mode 2, Ceil(H, 128) for mode 3 and
+ * Align2(Ceil(H, 32)) for modes 4/5.  Each scale is an fp32, or one byte with
+ * MOE_SCALE_E8M0.  Returns -1 for an invalid config. */
 int32_t moe_dc_scales_per_row(const moe_dc_config* cfg);
 
 /* Workspace bytes moe_dispatch needs for this config (the pages' two-phase pattern:
@@ -93,21 +128,32 @@ size_t moe_dc_dispatch_workspace_bytes(const moe_dc_config* cfg);
  * expert; the target rank is e / L rounded down and the local expert e % L); [DDD] §2.4
  * (receive side: the W x L count matrix is transposed and prefix-summed row-major into
  * ep_recv_count; expert_token_nums is its last column); [OPS] 功能说明 情形 1/2 and
- * [LLD] 计算公式 (quantization formulas of modes 0, 2, 4, 5); [SMP] Dispatch 功能介绍
+ * [LLD] 计算公式 (quantization formulas of modes 0-5); [SMP] Dispatch 功能介绍
  * (each row carries its source triple, output as assist_info_for_combine).
  *
+ * Quantization of a token x (x_fp32 = x widened to fp32, times the scales tensor if any):
+ *   mode 1  codes = int8(x_fp32)
+ *   mode 2  dyn = type_max / max|x_fp32| over the token; codes = type(x_fp32 * dyn);
+ *           scale = 1/dyn (type_max 127 int8, 448 E4M3, 57344 E5M2)
+ *   mode 3  as mode 2 for each group of 128 consecutive elements (the last may be short)
+ *   mode 4  per 32-element block: shared_exp = floor(log2 max|x|) - emax, at least -127
+ *           (emax 8 for E4M3, 15 for E5M2; an all-zero block takes -127)
+ *   mode 5  per block: shared_exp = ceil(log2(max(max|x|, 1e-4) / type_max))
+ *   modes 4/5: codes = fp8(x / 2^shared_exp); scale = 2^shared_exp (the dequant multiplier)
+ *
  * Inputs:
- *   x              bf16  [W][BS][H]   tokens of every source rank
+ *   x              bf16  [W][BS][H]   tokens of every source rank (finite values)
  *   expert_ids     int32 [W][BS][K]   picks; ids >= E are the special experts
- *   smooth_scales  fp32  [E][H] or NULL; mode 2 only (the routed expert's row multiplies
- *                  the token before quantization, so quantization is per pick)
+ *   scales         fp32, shaped by cfg->scales_kind ([1], [H] or [E][H]); NULL iff
+ *                  scales_kind is MOE_SCALES_NONE
  *   x_active_mask  uint8 [W][BS] (mask_kind 1) or [W][BS][K] (mask_kind 2), or NULL when
  *                  mask_kind is 0; nonzero = active.  An inactive pick is not dispatched.
  * Outputs (row = a receiver row in the packed layout below; cap = expand_rows_capacity):
- *   expand_x       [cap][H] bf16 (mode 0), int8 (mode 2) or E4M3 bytes (modes 4/5)
- *   dynamic_scales fp32 [cap] (mode 2: 1/dyn, with dyn = 127/max|x_fp32|) or
- *                  [cap][Align2(Ceil(H,32))] (modes 4/5: 2^shared_exp per 32-element block,
- *                  0 in the pad slot); NULL allowed for mode 0
+ *   expand_x       [cap][H] bf16 (mode 0), else one byte per element: int8 or fp8 codes
+ *   dynamic_scales [cap][moe_dc_scales_per_row(cfg)] fp32 (or bytes with MOE_SCALE_E8M0):
+ *                  mode 2 one 1/dyn per row; mode 3 one 1/dyn per group; modes 4/5 one scale
+ *                  per 32-element block and 0 in the Align2 pad slot.  NULL allowed for
+ *                  modes 0 and 1, which have no scales
  *   expand_idx     int32 [W][BS][K]   ordinal of each pick among its source rank's picks of
  *                  the same expert; -1 for inactive picks and special experts
  *   assist_info    int32 [cap][3]     (s, i, k) of the pick stored in each row
@@ -120,7 +166,8 @@ size_t moe_dc_dispatch_workspace_bytes(const moe_dc_config* cfg);
  * of the routed picks by (expert, s, i, k).  Rows at or past recv_offsets[W] are not written.
  * Numerics: every fp32 operation is a single IEEE binary32 operation rounded to nearest
  * even, in the order of the formulas; int8 codes round half to even and saturate at +-127
- * (NaN -> 0); E4M3 codes round to nearest even and saturate at +-448; fp32 subnormals are
+ * (NaN -> 0); fp8 codes round to nearest even and saturate at +-448 (E4M3) or +-57344
+ * (E5M2); in modes 2/3 an all-zero segment gives codes 0 and scale 0; fp32 subnormals are
  * kept.  The results are deterministic: identical inputs give identical bytes.
  * Errors: host validation first (MOE_ERR_INVALID_ARG / _UNSUPPORTED / _WORKSPACE); a HIP
  * launch failure gives MOE_ERR_DEVICE.  Out-of-range expert ids are a contract violation:
@@ -129,8 +176,8 @@ size_t moe_dc_dispatch_workspace_bytes(const moe_dc_config* cfg);
  * falses; any order works here). */
 moe_status moe_dispatch(const moe_dc_config* cfg,
                         const void* x, const int32_t* expert_ids,
-                        const float* smooth_scales, const uint8_t* x_active_mask,
-                        void* expand_x, float* dynamic_scales, int32_t* expand_idx,
+                        const float* scales, const uint8_t* x_active_mask,
+                        void* expand_x, void* dynamic_scales, int32_t* expand_idx,
                         int32_t* assist_info, int32_t* ep_recv_count,
                         int64_t* expert_token_nums, int64_t* recv_offsets,
                         void* workspace, size_t workspace_bytes, void* stream);

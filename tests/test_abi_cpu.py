@@ -33,9 +33,21 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_config_struct_layout_matches_header():
-    # twelve int32 fields then one int64
-    assert ctypes.sizeof(cq.MoeDcConfig) == 12 * 4 + 8
-    assert cq.MoeDcConfig.expand_rows_capacity.offset == 48
+    # sixteen int32 fields (the last two reserved) then one int64
+    assert ctypes.sizeof(cq.MoeDcConfig) == 16 * 4 + 8
+    assert cq.MoeDcConfig.out_dtype.offset == 44
+    assert cq.MoeDcConfig.scales_kind.offset == 48
+    assert cq.MoeDcConfig.scale_format.offset == 52
+    assert cq.MoeDcConfig.expand_rows_capacity.offset == 64
+
+
+def test_header_enum_values_match_the_binding():
+    text = open(HEADER).read()
+    for name in ("MOE_DTYPE_DEFAULT", "MOE_DTYPE_INT8", "MOE_DTYPE_E4M3", "MOE_DTYPE_E5M2",
+                 "MOE_SCALES_NONE", "MOE_SCALES_SCALAR", "MOE_SCALES_SHARED",
+                 "MOE_SCALES_PER_EXPERT", "MOE_SCALE_FP32", "MOE_SCALE_E8M0"):
+        m = re.search(r"\b" + name + r"\s*=\s*(\d+)", text)
+        assert m and int(m.group(1)) == getattr(cq, name), name
 
 
 def _cfg(**kw):
@@ -44,7 +56,9 @@ def _cfg(**kw):
     c = cq.make_config(base["W"], base["E"], base["BS"], base["H"], base["K"],
                        base["quant_mode"])
     for k, v in kw.items():
-        if k not in base:
+        if k == "reserved":
+            c.reserved[1] = v
+        elif k not in base:
             setattr(c, k, v)
     return c
 
@@ -54,7 +68,9 @@ def test_valid_configs_of_the_workloads():
     for wl in workloads.WORKLOADS.values():
         c = cq.make_config(wl.W, wl.E, wl.BS, wl.H, wl.K, wl.quant_mode,
                            zero_expert_num=wl.zero_expert_num,
-                           copy_expert_num=wl.copy_expert_num, mask_kind=wl.mask_kind)
+                           copy_expert_num=wl.copy_expert_num, mask_kind=wl.mask_kind,
+                           out_dtype=wl.out_dtype, scales_kind=wl.scales_kind,
+                           scale_format=wl.scale_format)
         assert cq.moe_dc_validate(c) == cq.MOE_OK, (wl.name, cq.moe_dc_last_error())
 
 
@@ -71,9 +87,19 @@ def test_valid_configs_of_the_workloads():
     (dict(K=0), cq.MOE_ERR_INVALID_ARG),
     (dict(K=17), cq.MOE_ERR_INVALID_ARG),
     (dict(W=2, E=2, K=3), cq.MOE_ERR_INVALID_ARG),    # K > number of experts
-    (dict(quant_mode=1), cq.MOE_ERR_UNSUPPORTED),
-    (dict(quant_mode=3), cq.MOE_ERR_UNSUPPORTED),
+    (dict(quant_mode=1), cq.MOE_ERR_INVALID_ARG),     # static quant without scales
     (dict(quant_mode=6), cq.MOE_ERR_INVALID_ARG),
+    (dict(quant_mode=-1), cq.MOE_ERR_INVALID_ARG),
+    (dict(quant_mode=0, out_dtype=1), cq.MOE_ERR_INVALID_ARG),
+    (dict(quant_mode=1, out_dtype=2, scales_kind=1), cq.MOE_ERR_INVALID_ARG),
+    (dict(quant_mode=3, out_dtype=1), cq.MOE_ERR_INVALID_ARG),
+    (dict(quant_mode=4, out_dtype=1), cq.MOE_ERR_INVALID_ARG),
+    (dict(quant_mode=2, out_dtype=4), cq.MOE_ERR_INVALID_ARG),
+    (dict(quant_mode=4, scales_kind=2), cq.MOE_ERR_INVALID_ARG),
+    (dict(quant_mode=0, scales_kind=1), cq.MOE_ERR_INVALID_ARG),
+    (dict(quant_mode=2, scales_kind=4), cq.MOE_ERR_INVALID_ARG),
+    (dict(quant_mode=2, scale_format=1), cq.MOE_ERR_INVALID_ARG),
+    (dict(quant_mode=5, scale_format=2), cq.MOE_ERR_INVALID_ARG),
     (dict(const_expert_num=1), cq.MOE_ERR_UNSUPPORTED),
     (dict(zero_expert_num=-1), cq.MOE_ERR_INVALID_ARG),
     (dict(zero_expert_num=2 ** 31 - 100), cq.MOE_ERR_INVALID_ARG),   # id space >= INT32_MAX
@@ -96,9 +122,22 @@ def test_k_may_count_special_experts():
     assert cq.moe_dc_validate(c) == cq.MOE_OK
 
 
+@pytest.mark.parametrize("kw", [
+    dict(quant_mode=1, scales_kind=1), dict(quant_mode=1, out_dtype=1, scales_kind=3),
+    dict(quant_mode=2, out_dtype=2, scales_kind=2), dict(quant_mode=2, out_dtype=3),
+    dict(quant_mode=3), dict(quant_mode=3, out_dtype=3, scales_kind=3),
+    dict(quant_mode=4, out_dtype=3, scale_format=1), dict(quant_mode=5, scale_format=1),
+])
+def test_quant_variants_validate(kw):
+    assert cq.moe_dc_validate(_cfg(**kw)) == cq.MOE_OK, cq.moe_dc_last_error()
+
+
 def test_scales_per_row_and_workspace():
     assert cq.moe_dc_scales_per_row(_cfg(quant_mode=0)) == 0
+    assert cq.moe_dc_scales_per_row(_cfg(quant_mode=1, scales_kind=1)) == 0
     assert cq.moe_dc_scales_per_row(_cfg(quant_mode=2)) == 1
+    assert cq.moe_dc_scales_per_row(_cfg(quant_mode=3)) == 56         # 7168/128
+    assert cq.moe_dc_scales_per_row(_cfg(quant_mode=3, H=1030)) == 9   # ceil(1030/128)
     assert cq.moe_dc_scales_per_row(_cfg(quant_mode=4)) == 224        # 7168/32, even
     assert cq.moe_dc_scales_per_row(_cfg(quant_mode=5, H=1056)) == 34  # 33 blocks -> 34
     assert cq.moe_dc_scales_per_row(_cfg(quant_mode=4, H=1030)) == 34  # ceil(1030/32)=33
@@ -115,7 +154,7 @@ def test_dispatch_rejects_bad_arguments_before_any_device_work():
     assert "NULL" in cq.moe_dc_last_error()
     rc = lib.moe_combine(ctypes.byref(c), *([None] * 9), None)
     assert rc == cq.MOE_ERR_INVALID_ARG
-    bad = _cfg(quant_mode=3)
+    bad = _cfg(const_expert_num=1)
     rc = lib.moe_dispatch(ctypes.byref(bad), *([None] * 11), None, ctypes.c_size_t(0), None)
     assert rc == cq.MOE_ERR_UNSUPPORTED
 
@@ -125,12 +164,21 @@ def test_dispatch_workspace_and_mask_rules_on_host():
     lib = cq.load_library()
     p = ctypes.c_void_p(0x1000)
     c = _cfg()
-    args = [p] * 11
-    # smooth scales with a mode that forbids them
+    args = [p, p, None] + [p] * 8          # no scales tensor: the config has none
+    # a scales tensor the config does not announce, and a missing one it does
     c4 = _cfg(quant_mode=4)
     rc = lib.moe_dispatch(ctypes.byref(c4), p, p, p, None, p, p, p, p, p, p, p, p,
                           ctypes.c_size_t(1 << 20), None)
-    assert rc == cq.MOE_ERR_INVALID_ARG and "smooth" in cq.moe_dc_last_error()
+    assert rc == cq.MOE_ERR_INVALID_ARG and "scales" in cq.moe_dc_last_error()
+    c1 = _cfg(quant_mode=1, scales_kind=2)
+    rc = lib.moe_dispatch(ctypes.byref(c1), p, p, None, None, p, None, p, p, p, p, p, p,
+                          ctypes.c_size_t(1 << 20), None)
+    assert rc == cq.MOE_ERR_INVALID_ARG and "scales" in cq.moe_dc_last_error()
+    # mode 3 needs dynamic_scales
+    c3 = _cfg(quant_mode=3)
+    rc = lib.moe_dispatch(ctypes.byref(c3), p, p, None, None, p, None, p, p, p, p, p, p,
+                          ctypes.c_size_t(1 << 20), None)
+    assert rc == cq.MOE_ERR_INVALID_ARG and "dynamic_scales" in cq.moe_dc_last_error()
     # mask pointer without a mask kind
     rc = lib.moe_dispatch(ctypes.byref(c), *args, p, ctypes.c_size_t(1 << 20), None)
     assert rc == cq.MOE_ERR_INVALID_ARG and "mask" in cq.moe_dc_last_error()

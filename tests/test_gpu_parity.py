@@ -58,33 +58,8 @@ SMALL = {
 }
 
 
-def _oracle_dispatch(wl, inp, etn_type=None):
-    cfg = harness.oracle_cfg(wl, etn_type)
-    return cfg, oracle.dispatch(cfg, inp["x"], inp["expert_ids"], scales=inp.get("scales"),
-                                mask=inp.get("mask"))
-
-
-def _roundtrip(wl, seed=0):
-    import torch
-    inp = workloads.generate(wl, seed=seed)
-    ocfg, ref = _oracle_dispatch(wl, inp)
-    cfg, dev_in, out = harness.gpu_dispatch(wl, inp)
-    torch.cuda.synchronize()
-    harness.compare_dispatch(wl, inp, out, ref)
-    # combine on random expert outputs, one per packed row
-    rng = np.random.default_rng(seed + 77)
-    eo = workloads.f32_to_bf16_bits(rng.standard_normal((wl.cap, wl.H), dtype=np.float32))
-    y_ref = oracle.combine(ocfg, eo, inp["expert_ids"], ref["expand_idx"],
-                           inp["expert_scales"], ref["ep_recv_count"], ref["recv_offsets"],
-                           mask=inp.get("mask"), ori_x=inp["x"])
-    import combine_quant_amd as cq
-    y = cq.combine(cfg, harness.bf16_dev(eo), dev_in["ids"], out["expand_idx"],
-                   harness.to_dev(inp["expert_scales"]), out["ep_recv_count"],
-                   out["recv_offsets"], dev_in["mask"], dev_in["x"])
-    torch.cuda.synchronize()
-    y_gpu = harness.host(y)
-    ndiff = harness.check_combine_tolerance(y_gpu, y_ref)
-    return ndiff
+_oracle_dispatch = harness.oracle_dispatch
+_roundtrip = harness.roundtrip
 
 
 @pytest.mark.parametrize("name", list(SMALL))

@@ -113,7 +113,27 @@ C5 = Workload(
                 "N(0,1), MX clip E4M3, per-pick mask with 51 of 512 tokens per rank fully "
                 "inactive, uniform distinct top-16 over all 516 ids")
 
-WORKLOADS = {w.name: w for w in (C1_MODE0, C1_MODE2, C2, C3, C4, C5)}
+# the further quantization variants at the C3/C4 shape (measurement of those variants)
+C3_E5M2_E8M0 = C3.replace(
+    name="c3v_w16_mx_e5m2_e8m0", out_dtype=3, scale_format=1,
+    description="C3 with MX E5M2 elements and E8M0 scale bytes (the SMP article's stored "
+                "format)")
+C4_STATIC = C4.replace(
+    name="c4v_w16_static_int8_shared", quant_mode=1, scales_kind=2,
+    description="C4 with static int8 quantization, one shared [H] coefficient row "
+                "U(16, 48)")
+C4_TOKEN_E4M3 = C4.replace(
+    name="c4v_w16_token_e4m3", out_dtype=2,
+    description="C4 with per-token dynamic E4M3 codes")
+C4_GROUP = C4.replace(
+    name="c4v_w16_group_e4m3", quant_mode=3,
+    description="C4 with per-128-group dynamic E4M3 codes (56 scales per row)")
+C2_GROUP_SMOOTH = C2.replace(
+    name="c2v_w8_group_e4m3_smooth", quant_mode=3,
+    description="C2 with per-128-group dynamic E4M3 codes and per-expert smooth scales")
+
+WORKLOADS = {w.name: w for w in (C1_MODE0, C1_MODE2, C2, C3, C4, C5, C3_E5M2_E8M0, C4_STATIC,
+                                 C4_TOKEN_E4M3, C4_GROUP, C2_GROUP_SMOOTH)}
 
 
 def _streams(seed: int):
