@@ -44,6 +44,14 @@ def _load():
             "oracle_e5m2_to_f32": (f32, [u8]),
             "oracle_int8_from_f32": (ctypes.c_int8, [f32]),
             "oracle_e8m0_from_scale": (u8, [f32]),
+            "oracle_f32_to_f16": (u16, [f32]),
+            "oracle_f16_to_f32": (f32, [u16]),
+            "oracle_int8_from_f16": (ctypes.c_int8, [u16]),
+            "oracle_combine_block_count": (i32, [i32]),
+            "oracle_combine_quant_row": (None, [P, i32, P, P]),
+            "oracle_combine_dequant_row": (None, [P, P, i32, P]),
+            "oracle_combine_quantize": (i32, [P] * 5),
+            "oracle_combine_int8": (i32, [P] * 13),
             "oracle_mx_scale_count": (i32, [i32]),
             "oracle_code_type": (i32, [i32, i32]),
             "oracle_scale_count": (i32, [i32, i32]),
@@ -117,6 +125,22 @@ def int8_from_f32(v):
 
 def e8m0_from_scale(s):
     return _load().oracle_e8m0_from_scale(float(s))
+
+
+def f32_to_f16(f):
+    return _load().oracle_f32_to_f16(float(f))
+
+
+def f16_to_f32(h):
+    return _load().oracle_f16_to_f32(int(h))
+
+
+def int8_from_f16(h):
+    return _load().oracle_int8_from_f16(int(h))
+
+
+def combine_block_count(H):
+    return _load().oracle_combine_block_count(int(H))
 
 
 def mx_scale_count(H):
@@ -272,4 +296,56 @@ def combine_token(cfg, expert_out, expert_ids, expand_idx, expert_scales, ep_rec
                                       _p(off), _p(m), _p(ox), int(s), int(i), _p(acc), _p(y))
     if rc != 0:
         raise ValueError(f"oracle_combine_token rejected the input (rc={rc})")
+    return y
+
+
+# -- combine-side int8 block quantization ------------------------------------------------------
+
+def combine_quant_row(row_bf16):
+    x = _c(row_bf16, np.uint16)
+    H = x.shape[0]
+    q = np.empty(H, np.int8)
+    sc = np.empty(combine_block_count(H), np.float32)
+    _load().oracle_combine_quant_row(_p(x), H, _p(q), _p(sc))
+    return q, sc
+
+
+def combine_dequant_row(q, scales):
+    q = _c(q, np.int8)
+    sc = _c(scales, np.float32)
+    out = np.empty(q.shape[0], np.float32)
+    _load().oracle_combine_dequant_row(_p(q), _p(sc), q.shape[0], _p(out))
+    return out
+
+
+def combine_quantize(cfg, expert_out, recv_offsets):
+    """Codes [cap][H] int8 and scales [cap][Ceil(H,8)] fp32 of the rows [0, recv_offsets[W]);
+    later rows are left zero."""
+    eo = _c(expert_out, np.uint16)
+    off = _c(recv_offsets, np.int64)
+    cap = eo.shape[0]
+    codes = np.zeros((cap, cfg.H), np.int8)
+    scales = np.zeros((cap, combine_block_count(cfg.H)), np.float32)
+    _load().oracle_combine_quantize(_ref(cfg), _p(eo), _p(off), _p(codes), _p(scales))
+    return codes, scales
+
+
+def combine_int8(cfg, codes, scales, expert_ids, expand_idx, expert_scales, ep_recv_count,
+                 recv_offsets, mask=None, ori_x=None):
+    q = _c(codes, np.int8)
+    sc = _c(scales, np.float32)
+    ids = _c(expert_ids, np.int32)
+    eidx = _c(expand_idx, np.int32)
+    w = _c(expert_scales, np.float32)
+    erc = _c(ep_recv_count, np.int32)
+    off = _c(recv_offsets, np.int64)
+    m = _c(mask, np.uint8)
+    ox = _c(ori_x, np.uint16)
+    y = np.empty((cfg.W, cfg.BS, cfg.H), np.uint16)
+    acc = np.empty(cfg.H, np.float32)
+    row = np.empty(cfg.H, np.float32)
+    rc = _load().oracle_combine_int8(_ref(cfg), _p(q), _p(sc), _p(ids), _p(eidx), _p(w),
+                                     _p(erc), _p(off), _p(m), _p(ox), _p(y), _p(acc), _p(row))
+    if rc != 0:
+        raise ValueError(f"oracle_combine_int8 rejected the input (rc={rc})")
     return y

@@ -44,6 +44,63 @@ uint16_t oracle_f32_to_bf16(float f)
     return (uint16_t)keep;
 }
 
+/* IEEE binary16: 1 sign, 5 exponent (bias 15), 10 mantissa bits; largest finite 65504,
+ * smallest normal 2^-14, subnormals m * 2^-24.  Widening is exact. */
+float oracle_f16_to_f32(uint16_t h)
+{
+    int sign = h & 0x8000;
+    int ex = (h >> 10) & 0x1F;
+    int m = h & 0x3FF;
+    double v;
+    if (ex == 0x1F) {
+        if (m != 0) return NAN;
+        return sign ? -INFINITY : INFINITY;
+    }
+    if (ex == 0) v = ldexp((double)m, -24);
+    else v = ldexp(1.0 + m / 1024.0, ex - 15);
+    return (float)(sign ? -v : v);
+}
+
+/* Narrowing binary32 -> binary16, round to nearest, ties to even (the IEEE default); values
+ * that round beyond 65504 become infinity; NaN stays NaN.  Same method as the fp8 encoders:
+ * the binary16 spacing in the binade of |v| is 2^(floor(log2|v|) - 10), and 2^-24 all
+ * through the subnormal range below 2^-14. */
+uint16_t oracle_f32_to_f16(float f)
+{
+    uint16_t sign = signbit(f) ? 0x8000 : 0x0000;
+    if (isnan(f)) return (uint16_t)(sign | 0x7E00);
+    double a = fabs((double)f);
+    if (isinf(f)) return (uint16_t)(sign | 0x7C00);
+    double quantum;
+    if (a < ldexp(1.0, -14)) {
+        quantum = ldexp(1.0, -24);
+    } else {
+        int ex;
+        frexp(a, &ex);
+        quantum = ldexp(1.0, (ex - 1) - 10);
+    }
+    double r = nearbyint(a / quantum) * quantum;
+    if (r >= 65536.0) return (uint16_t)(sign | 0x7C00);      /* rounded past 65504 */
+    uint16_t code;
+    if (r < ldexp(1.0, -14)) {
+        code = (uint16_t)(r / ldexp(1.0, -24));               /* 0..1024; 1024 = 2^-14 */
+    } else {
+        int ex;
+        double m = frexp(r, &ex);
+        int e2 = ex - 1;
+        int mant = (int)((2.0 * m - 1.0) * 1024.0);            /* exact: 10 fraction bits */
+        code = (uint16_t)(((e2 + 15) << 10) | mant);
+    }
+    return (uint16_t)(sign | code);
+}
+
+/* binary16 -> int8 (the second cast of the combine-side quantization chain float -> fp16 ->
+ * int8): round half to even, saturate to [-127, 127], NaN -> 0 (readings R4, R5, R27). */
+int8_t oracle_int8_from_f16(uint16_t h)
+{
+    return oracle_int8_from_f32(oracle_f16_to_f32(h));
+}
+
 /* OCP E4M3 ("e4m3fn"): 1 sign, 4 exponent (bias 7), 3 mantissa bits; no infinities; the
  * all-ones pattern S.1111.111 is NaN, so the largest finite magnitude is 1.75 * 2^8 = 448.
  * Subnormals are m * 2^-9 for m = 1..7. */
@@ -593,6 +650,112 @@ int32_t oracle_combine(const oracle_cfg* c, const uint16_t* expert_out,
                                               mask, ori_x, s, i, acc,
                                               y + ((size_t)s * c->BS + i) * c->H);
             if (rc != 0) return rc;
+        }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------- */
+/* combine-side int8 block quantization ([SMP] 通信前量化, Combine 的 INT8 block 量化)       */
+/* ------------------------------------------------------------------------------------- */
+
+/* Blocks of 8 elements: the page processes 32-byte blocks of 8 floats (reading R26), so a
+ * row has Ceil(H, 8) blocks, the last one short when 8 does not divide H. */
+int32_t oracle_combine_block_count(int32_t H)
+{
+    return (H + 7) / 8;
+}
+
+/* Expert-side quantization of one expert-output row, in the page's order: widen to float;
+ * per block: absolute maximum (Abs, BlockReduceMax); scale = amax * (1 / 127) (Muls by the
+ * reciprocal of SCALE_PARAM = 127.0, the reciprocal one fp32 division); q = x / scale (Div);
+ * then the casts float -> fp16 -> int8 (reading R27: each cast rounds to nearest even; the
+ * int8 cast saturates at +-127 and maps NaN to 0, so an all-zero block, 0 / 0, gives codes
+ * 0 with scale 0). */
+void oracle_combine_quant_row(const uint16_t* row, int32_t H, int8_t* q, float* scales)
+{
+    const float inv127 = 1.0f / 127.0f;
+    for (int32_t b = 0; b * 8 < H; ++b) {
+        int32_t h0 = b * 8;
+        int32_t h1 = h0 + 8 < H ? h0 + 8 : H;
+        float amax = 0.0f;
+        for (int32_t h = h0; h < h1; ++h) {
+            float a = fabsf(oracle_bf16_to_f32(row[h]));
+            if (a > amax) amax = a;
+        }
+        float scale = amax * inv127;
+        for (int32_t h = h0; h < h1; ++h) {
+            float v = oracle_bf16_to_f32(row[h]) / scale;
+            q[h] = oracle_int8_from_f16(oracle_f32_to_f16(v));
+        }
+        scales[b] = scale;
+    }
+}
+
+/* Source-side dequantization: int8 -> fp16 -> float (both exact), times the block's scale
+ * (one fp32 multiply). */
+void oracle_combine_dequant_row(const int8_t* q, const float* scales, int32_t H, float* out)
+{
+    for (int32_t h = 0; h < H; ++h) {
+        float v = oracle_f16_to_f32(oracle_f32_to_f16((float)q[h]));
+        out[h] = v * scales[h / 8];
+    }
+}
+
+/* Every packed expert-output row [0, recv_offsets[W]) quantized; codes [cap][H] int8,
+ * scales [cap][Ceil(H, 8)] fp32.  Rows past recv_offsets[W] are not touched. */
+int32_t oracle_combine_quantize(const oracle_cfg* c, const uint16_t* expert_out,
+                                const int64_t* recv_offsets, int8_t* codes, float* scales)
+{
+    const int32_t H = c->H, nb = oracle_combine_block_count(H);
+    for (int64_t r = 0; r < recv_offsets[c->W]; ++r)
+        oracle_combine_quant_row(expert_out + (size_t)r * H, H, codes + (size_t)r * H,
+                                 scales + (size_t)r * nb);
+    return 0;
+}
+
+/* The combine of oracle_combine_token with each routed pick's row dequantized first: the
+ * same addressing ([DDD] §3.4.2), the same fp32 sum in k order of w * row, zero experts
+ * adding nothing and copy experts adding w * ori_x (reading R28: ori_x stays on its source
+ * rank, so it is never quantized); the result rounded to bf16. */
+int32_t oracle_combine_int8(const oracle_cfg* c, const int8_t* codes, const float* scales,
+                            const int32_t* expert_ids, const int32_t* expand_idx,
+                            const float* expert_scales, const int32_t* ep_recv_count,
+                            const int64_t* recv_offsets, const uint8_t* mask,
+                            const uint16_t* ori_x, uint16_t* y, float* acc, float* rowbuf)
+{
+    const int32_t H = c->H, nb = oracle_combine_block_count(H);
+    const int32_t zero_end = c->E + c->zero_expert_num;
+    const int32_t copy_end = zero_end + c->copy_expert_num;
+    for (int32_t s = 0; s < c->W; ++s)
+        for (int32_t i = 0; i < c->BS; ++i) {
+            for (int32_t h = 0; h < H; ++h) acc[h] = 0.0f;
+            for (int32_t k = 0; k < c->K; ++k) {
+                size_t p = ((size_t)s * c->BS + i) * c->K + k;
+                if (!pair_active(c, mask, s, i, k)) continue;
+                int32_t e = expert_ids[p];
+                float w = expert_scales[p];
+                if (e < 0 || e >= copy_end) return -1;
+                if (e < c->E) {
+                    int32_t ord = expand_idx[p];
+                    if (ord < 0) return -1;
+                    int64_t row = oracle_dest_row(c, ep_recv_count, recv_offsets, s, e, ord);
+                    oracle_combine_dequant_row(codes + (size_t)row * H,
+                                               scales + (size_t)row * nb, H, rowbuf);
+                    for (int32_t h = 0; h < H; ++h) {
+                        float t = w * rowbuf[h];
+                        acc[h] = acc[h] + t;
+                    }
+                } else if (e >= zero_end) {
+                    if (ori_x == NULL) return -1;
+                    const uint16_t* src = ori_x + ((size_t)s * c->BS + i) * H;
+                    for (int32_t h = 0; h < H; ++h) {
+                        float t = w * oracle_bf16_to_f32(src[h]);
+                        acc[h] = acc[h] + t;
+                    }
+                }
+            }
+            uint16_t* yr = y + ((size_t)s * c->BS + i) * H;
+            for (int32_t h = 0; h < H; ++h) yr[h] = oracle_f32_to_bf16(acc[h]);
         }
     return 0;
 }

@@ -62,6 +62,11 @@ int32_t  oracle_mx_scale_count(int32_t H);
 int32_t  oracle_code_type(int32_t quant_mode, int32_t out_dtype);
 int32_t  oracle_scale_count(int32_t quant_mode, int32_t H);
 
+/* IEEE binary16 (fp16) conversions */
+uint16_t oracle_f32_to_f16(float f);
+float    oracle_f16_to_f32(uint16_t h);
+int8_t   oracle_int8_from_f16(uint16_t h);
+
 /* per-row quantization */
 void oracle_quant_int8_row(const uint16_t* x, const float* smooth_or_null, int32_t H,
                            int8_t* q, float* scale);
@@ -91,6 +96,18 @@ int32_t oracle_combine_token(const oracle_cfg* c, const uint16_t* expert_out,
                              const int64_t* recv_offsets, const uint8_t* mask,
                              const uint16_t* ori_x, int32_t s, int32_t i, float* acc_scratch,
                              uint16_t* y_row);
+/* combine-side int8 block quantization (expert side) and the int8 combine (source side) */
+int32_t oracle_combine_block_count(int32_t H);
+void oracle_combine_quant_row(const uint16_t* row, int32_t H, int8_t* q, float* scales);
+void oracle_combine_dequant_row(const int8_t* q, const float* scales, int32_t H, float* out);
+int32_t oracle_combine_quantize(const oracle_cfg* c, const uint16_t* expert_out,
+                                const int64_t* recv_offsets, int8_t* codes, float* scales);
+int32_t oracle_combine_int8(const oracle_cfg* c, const int8_t* codes, const float* scales,
+                            const int32_t* expert_ids, const int32_t* expand_idx,
+                            const float* expert_scales, const int32_t* ep_recv_count,
+                            const int64_t* recv_offsets, const uint8_t* mask,
+                            const uint16_t* ori_x, uint16_t* y, float* acc_scratch,
+                            float* row_scratch);
 int32_t oracle_combine(const oracle_cfg* c, const uint16_t* expert_out,
                        const int32_t* expert_ids, const int32_t* expand_idx,
                        const float* expert_scales, const int32_t* ep_recv_count,
