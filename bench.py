@@ -76,8 +76,16 @@ def algorithmic_bytes(wl, inp, routed_rows, copy_picks, active_tokens):
     P = routed_rows
     dispatch = (2 * H * active_tokens + 4 * T * K + m + smooth + P * (b * H + S + 12)
                 + 4 * T * K + 4 * E * W + 8 * E + 8 * (W + 1))
-    combine = 2 * H * P + 12 * T * K + 4 * E * W + 8 * (W + 1) + m + 2 * H * copy_picks + 2 * H * T
+    row = 2 * H if wl.combine_quant == 0 else H + 4 * ((H + 7) // 8)
+    combine = row * P + 12 * T * K + 4 * E * W + 8 * (W + 1) + m + 2 * H * copy_picks + 2 * H * T
     return dispatch, combine
+
+
+def quantize_bytes(wl, routed_rows):
+    """Expert-side int8 block quantization: read each routed bf16 row, write its codes and
+    Ceil(H, 8) fp32 scales, read recv_offsets."""
+    H = wl.H
+    return routed_rows * (2 * H + H + 4 * ((H + 7) // 8)) + 8 * (wl.W + 1)
 
 
 def mx_scales_per_row(H):
@@ -136,9 +144,16 @@ def cpu_baseline(wl, inp, expert_out_host, passes):
             t0 = time.perf_counter()
             d = oracle.dispatch(cfg, inp["x"], inp["expert_ids"], scales=inp.get("scales"),
                                 mask=inp.get("mask"))
-            oracle.combine(cfg, expert_out_host, inp["expert_ids"], d["expand_idx"],
-                           inp["expert_scales"], d["ep_recv_count"], d["recv_offsets"],
-                           mask=inp.get("mask"), ori_x=inp["x"])
+            if wl.combine_quant:
+                codes, bsc = oracle.combine_quantize(cfg, expert_out_host, d["recv_offsets"])
+                oracle.combine_int8(cfg, codes, bsc, inp["expert_ids"], d["expand_idx"],
+                                    inp["expert_scales"], d["ep_recv_count"],
+                                    d["recv_offsets"], mask=inp.get("mask"), ori_x=inp["x"])
+                del codes, bsc
+            else:
+                oracle.combine(cfg, expert_out_host, inp["expert_ids"], d["expand_idx"],
+                               inp["expert_scales"], d["ep_recv_count"], d["recv_offsets"],
+                               mask=inp.get("mask"), ori_x=inp["x"])
             times.append(time.perf_counter() - t0)
             del d
     finally:
@@ -196,21 +211,34 @@ def run_bench(args):
         eo = workloads.expert_out_torch(wl, wl.cap, seed=args.seed, device=dev)
         sets.append(dict(x=x, eo=eo, out=cq.alloc_dispatch_outputs(cfg, dev),
                          y=torch.empty((wl.W, wl.BS, wl.H), dtype=torch.bfloat16, device=dev)))
+        if wl.combine_quant:
+            sets[-1]["codes"] = torch.empty((wl.cap, wl.H), dtype=torch.int8, device=dev)
+            sets[-1]["bscales"] = torch.empty((wl.cap, (wl.H + 7) // 8), dtype=torch.float32,
+                                              device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step(n):
         st = sets[n % len(sets)]
         o = st["out"]
-        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-              torch.cuda.Event(enable_timing=True))
+        ev = tuple(torch.cuda.Event(enable_timing=True) for _ in range(4))
         ev[0].record(stream)
         cq.moe_dispatch(cfg, st["x"], ids, smooth, mask, o["expand_x"], o["dynamic_scales"],
                         o["expand_idx"], o["assist_info"], o["ep_recv_count"],
                         o["expert_token_nums"], o["recv_offsets"], o["workspace"], stream)
         ev[1].record(stream)
-        cq.moe_combine(cfg, st["eo"], ids, o["expand_idx"], w, o["ep_recv_count"],
-                       o["recv_offsets"], mask, st["x"], st["y"], stream)
-        ev[2].record(stream)
+        if wl.combine_quant == 0:
+            ev[2].record(stream)
+            cq.moe_combine(cfg, st["eo"], ids, o["expand_idx"], w, o["ep_recv_count"],
+                           o["recv_offsets"], mask, st["x"], st["y"], stream)
+            ev[3].record(stream)
+        else:
+            cq.moe_combine_quantize(cfg, st["eo"], o["recv_offsets"], st["codes"],
+                                    st["bscales"], stream)
+            ev[2].record(stream)
+            cq.moe_combine_int8(cfg, st["codes"], st["bscales"], ids, o["expand_idx"], w,
+                                o["ep_recv_count"], o["recv_offsets"], mask, st["x"], st["y"],
+                                stream)
+            ev[3].record(stream)
         return ev
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
@@ -229,7 +257,8 @@ def run_bench(args):
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
     disp_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    comb_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    quant_ms = [e[1].elapsed_time(e[2]) for e in evs]      # 0 without combine quantization
+    comb_ms = [e[2].elapsed_time(e[3]) for e in evs]
     ms_per_step = total_ms / args.steps
 
     # routed rows etc. of this input, read back from the library's own outputs
@@ -250,7 +279,8 @@ def run_bench(args):
         return float(np.percentile(np.asarray(v), q)) * 1e3
     comb_gbps = c_bytes / (c_avg * 1e-3) / 1e9
     disp_gbps = d_bytes / (d_avg * 1e-3) / 1e9
-    total_gbps = (d_bytes + c_bytes) / (ms_per_step * 1e-3) / 1e9
+    q_bytes = quantize_bytes(wl, P) if wl.combine_quant else 0
+    total_gbps = (d_bytes + q_bytes + c_bytes) / (ms_per_step * 1e-3) / 1e9
     tokens_per_s = wl.T / (ms_per_step * 1e-3)
 
     cpu = None
@@ -276,14 +306,15 @@ def run_bench(args):
         "config": {"workload": wl.name, "W": wl.W, "E": wl.E, "BS_per_rank": wl.BS,
                    "H": wl.H, "K": wl.K, "quant_mode": wl.quant_mode,
                    "out_dtype": wl.out_dtype, "scales_kind": wl.scales_kind,
-                   "scale_format": wl.scale_format,
+                   "scale_format": wl.scale_format, "combine_quant": wl.combine_quant,
                    "routing": wl.routing, "tokens_per_step": wl.T, "routed_rows": P,
                    "description": wl.description},
         "hbm_gbps": round(total_gbps, 1),
         "hbm_frac": round(total_gbps / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "achieved": round(comb_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(comb_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": committed_traffic(), "kernel": "combine_wave_kernel",
+                     "traffic": committed_traffic() if wl.name == DEFAULT_WORKLOAD else None,
+                     "kernel": "combine_wave_kernel",
                      "algorithmic_bytes_per_launch": c_bytes,
                      "avg_launch_us": round(c_avg * 1e3, 2)},
         "dispatch": {"avg_us": round(d_avg * 1e3, 2), "median_us": round(pct(disp_ms, 50), 2),
@@ -292,6 +323,10 @@ def run_bench(args):
         "combine": {"avg_us": round(c_avg * 1e3, 2), "median_us": round(pct(comb_ms, 50), 2),
                     "p90_us": round(pct(comb_ms, 90), 2), "algorithmic_bytes": c_bytes,
                     "gbps": round(comb_gbps, 1)},
+        "combine_quantize": None if not wl.combine_quant else {
+            "avg_us": round(statistics.mean(quant_ms) * 1e3, 2),
+            "algorithmic_bytes": q_bytes,
+            "gbps": round(q_bytes / (statistics.mean(quant_ms) * 1e-3) / 1e9, 1)},
         "wall_s_timed": round(wall, 4),
         "cpu_baseline": cpu,
     }

@@ -22,7 +22,8 @@ _STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
            -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_DEVICE"}
 
 EXPORTS = ("moe_dc_validate", "moe_dc_scales_per_row", "moe_dc_dispatch_workspace_bytes",
-           "moe_dispatch", "moe_combine", "moe_dc_last_error", "moe_dc_version")
+           "moe_dispatch", "moe_combine", "moe_combine_quantize", "moe_combine_int8",
+           "moe_dc_last_error", "moe_dc_version")
 
 
 class MoeDcConfig(ctypes.Structure):
@@ -87,6 +88,10 @@ def load_library(path: str = LIB) -> ctypes.CDLL:
     lib.moe_dispatch.argtypes = [cfgp] + [P] * 11 + [P, ctypes.c_size_t, P]
     lib.moe_combine.restype = ctypes.c_int
     lib.moe_combine.argtypes = [cfgp] + [P] * 9 + [P]
+    lib.moe_combine_quantize.restype = ctypes.c_int
+    lib.moe_combine_quantize.argtypes = [cfgp] + [P] * 4 + [P]
+    lib.moe_combine_int8.restype = ctypes.c_int
+    lib.moe_combine_int8.argtypes = [cfgp] + [P] * 10 + [P]
     lib.moe_dc_last_error.restype = ctypes.c_char_p
     lib.moe_dc_last_error.argtypes = []
     lib.moe_dc_version.restype = ctypes.c_char_p
@@ -235,6 +240,48 @@ def moe_combine(cfg, expert_out, expert_ids, expand_idx, expert_scales, ep_recv_
     _check(lib.moe_combine(ctypes.byref(cfg), *args, _stream(dev, stream)))
 
 
+def combine_block_count(cfg):
+    """fp32 block scales per row of the combine-side int8 quantization: Ceil(H, 8)."""
+    return (cfg.hidden + 7) // 8
+
+
+def moe_combine_quantize(cfg, expert_out, recv_offsets, codes, block_scales, stream=None):
+    """Enqueue the expert-side int8 block quantization of rows [0, recv_offsets[W])."""
+    W, H, cap = cfg.ep_world_size, cfg.hidden, cfg.expand_rows_capacity
+    dev = codes.device
+    args = [
+        _ptr(expert_out, torch.bfloat16, (cap, H), "expert_out", dev),
+        _ptr(recv_offsets, torch.int64, (W + 1,), "recv_offsets", dev),
+        _ptr(codes, torch.int8, (cap, H), "codes", dev),
+        _ptr(block_scales, torch.float32, (cap, combine_block_count(cfg)), "block_scales",
+             dev),
+    ]
+    _check(load_library().moe_combine_quantize(ctypes.byref(cfg), *args, _stream(dev, stream)))
+
+
+def moe_combine_int8(cfg, codes, block_scales, expert_ids, expand_idx, expert_scales,
+                     ep_recv_count, recv_offsets, x_active_mask, ori_x, y, stream=None):
+    """Enqueue one combine over int8 block-quantized expert rows."""
+    W, BS, H, K, L, cap = (cfg.ep_world_size, cfg.bs, cfg.hidden, cfg.topk, cfg.L,
+                           cfg.expand_rows_capacity)
+    dev = y.device
+    mshape = {1: (W, BS), 2: (W, BS, K)}.get(cfg.mask_kind)
+    args = [
+        _ptr(codes, torch.int8, (cap, H), "codes", dev),
+        _ptr(block_scales, torch.float32, (cap, combine_block_count(cfg)), "block_scales",
+             dev),
+        _ptr(expert_ids, torch.int32, (W, BS, K), "expert_ids", dev),
+        _ptr(expand_idx, torch.int32, (W, BS, K), "expand_idx", dev),
+        _ptr(expert_scales, torch.float32, (W, BS, K), "expert_scales", dev),
+        _ptr(ep_recv_count, torch.int32, (W, L * W), "ep_recv_count", dev),
+        _ptr(recv_offsets, torch.int64, (W + 1,), "recv_offsets", dev),
+        _ptr(x_active_mask, (torch.uint8, torch.bool), mshape, "x_active_mask", dev),
+        _ptr(ori_x, torch.bfloat16, (W, BS, H), "ori_x", dev),
+        _ptr(y, torch.bfloat16, (W, BS, H), "y", dev),
+    ]
+    _check(load_library().moe_combine_int8(ctypes.byref(cfg), *args, _stream(dev, stream)))
+
+
 # -- allocation helpers (torch owns the memory; the library never allocates) ----------------
 
 def alloc_dispatch_outputs(cfg, device="cuda"):
@@ -274,4 +321,27 @@ def combine(cfg, expert_out, expert_ids, expand_idx, expert_scales, ep_recv_coun
                         device=expert_out.device)
     moe_combine(cfg, expert_out, expert_ids, expand_idx, expert_scales, ep_recv_count,
                 recv_offsets, x_active_mask, ori_x, y, stream)
+    return y
+
+
+def combine_quantize(cfg, expert_out, recv_offsets, out=None, stream=None):
+    """Allocate (or reuse `out` = (codes, block_scales)) and enqueue moe_combine_quantize."""
+    cap, H = cfg.expand_rows_capacity, cfg.hidden
+    if out is None:
+        out = (torch.empty((cap, H), dtype=torch.int8, device=expert_out.device),
+               torch.empty((cap, combine_block_count(cfg)), dtype=torch.float32,
+                           device=expert_out.device))
+    moe_combine_quantize(cfg, expert_out, recv_offsets, out[0], out[1], stream)
+    return out
+
+
+def combine_int8(cfg, codes, block_scales, expert_ids, expand_idx, expert_scales,
+                 ep_recv_count, recv_offsets, x_active_mask=None, ori_x=None, y=None,
+                 stream=None):
+    """Allocate (or reuse `y`) and enqueue moe_combine_int8; returns y."""
+    if y is None:
+        y = torch.empty((cfg.ep_world_size, cfg.bs, cfg.hidden), dtype=torch.bfloat16,
+                        device=codes.device)
+    moe_combine_int8(cfg, codes, block_scales, expert_ids, expand_idx, expert_scales,
+                     ep_recv_count, recv_offsets, x_active_mask, ori_x, y, stream)
     return y

@@ -1,7 +1,8 @@
 // api.cpp -- C ABI of libmoe_dc: host validation, workspace sizing and launch sequencing.
 //
 // Nothing here allocates device memory or synchronises the host; every launch goes to the
-// caller's stream in order (route -> scan -> scatter for dispatch, one kernel for combine).
+// caller's stream in order (route -> scan -> scatter for dispatch, one kernel for each of
+// combine, combine quantize and int8 combine).
 #include "moe_dc.h"
 #include "dc_internal.h"
 
@@ -33,6 +34,7 @@ moe_status ok()
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
 
 // Element type of expand_x for a quant mode and requested out_dtype, or -1 when the pair is
 // not allowed ([LLD] 约束说明: mode 0 keeps the input type; mode 1 int8; mode 2 int8, E4M3
@@ -237,6 +239,52 @@ moe_status moe_combine(const moe_dc_config* cfg, const void* expert_out,
                                               x_active_mask, ori_x, y, vec,
                                               static_cast<hipStream_t>(stream)),
                        "combine kernel launch");
+    if (st != MOE_OK) return st;
+    return ok();
+}
+
+moe_status moe_combine_quantize(const moe_dc_config* cfg, const void* expert_out,
+                                const int64_t* recv_offsets, int8_t* codes,
+                                float* block_scales, void* stream)
+{
+    moe_dc::Shape sh;
+    moe_status st = check(cfg, &sh);
+    if (st != MOE_OK) return st;
+    if (!expert_out || !recv_offsets || !codes || !block_scales)
+        return fail(MOE_ERR_INVALID_ARG, "a required tensor pointer is NULL");
+    const bool vec = sh.H % 8 == 0 && aligned16(expert_out) && aligned8(codes);
+    st = device_status(moe_dc::launch_combine_quantize(sh, expert_out, recv_offsets, codes,
+                                                       block_scales, vec,
+                                                       static_cast<hipStream_t>(stream)),
+                       "combine quantize kernel launch");
+    if (st != MOE_OK) return st;
+    return ok();
+}
+
+moe_status moe_combine_int8(const moe_dc_config* cfg, const int8_t* codes,
+                            const float* block_scales, const int32_t* expert_ids,
+                            const int32_t* expand_idx, const float* expert_scales,
+                            const int32_t* ep_recv_count, const int64_t* recv_offsets,
+                            const uint8_t* x_active_mask, const void* ori_x, void* y,
+                            void* stream)
+{
+    moe_dc::Shape sh;
+    moe_status st = check(cfg, &sh);
+    if (st != MOE_OK) return st;
+    if (!codes || !block_scales || !expert_ids || !expand_idx || !expert_scales ||
+        !ep_recv_count || !recv_offsets || !y)
+        return fail(MOE_ERR_INVALID_ARG, "a required tensor pointer is NULL");
+    if ((sh.mask_kind != 0) != (x_active_mask != nullptr))
+        return fail(MOE_ERR_INVALID_ARG, "x_active_mask must be given iff mask_kind != 0");
+    if (cfg->copy_expert_num > 0 && !ori_x)
+        return fail(MOE_ERR_INVALID_ARG, "ori_x is required when copy experts exist");
+    const bool vec = sh.H % 8 == 0 && aligned8(codes) && aligned16(y) &&
+                     (!ori_x || aligned16(ori_x));
+    st = device_status(moe_dc::launch_combine_int8(sh, codes, block_scales, expert_ids,
+                                                   expand_idx, expert_scales, ep_recv_count,
+                                                   recv_offsets, x_active_mask, ori_x, y, vec,
+                                                   static_cast<hipStream_t>(stream)),
+                       "int8 combine kernel launch");
     if (st != MOE_OK) return st;
     return ok();
 }

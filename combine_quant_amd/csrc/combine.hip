@@ -17,6 +17,14 @@
 // the token's sources in lanes 0..K-1 and broadcasts them as wave-uniform values; expert rows
 // are read and y is written with the non-temporal policy; no workgroup barrier.  Element-wise
 // fallback (any H, any alignment): one workgroup per token, one element per lane.
+//
+// Combine-side int8 block quantization (the sample article's combine INT8 block
+// quantization, 通信前量化): the expert side compresses each expert-output row into int8
+// codes with one fp32 scale per 8 elements (scale = amax * (1/127), code = int8(fp16(x /
+// scale)), each cast rounding to nearest even); the combine then reads codes and scales
+// instead of bf16 rows and dequantizes each element (int8 -> fp16 -> float is exact, times
+// the scale) before weighting it.  One 8-element block is exactly one lane's vector, so the
+// block maximum needs no lane exchange, and a lane reads 12 bytes per pick instead of 16.
 #include "dc_device.h"
 #include "dc_internal.h"
 
@@ -64,6 +72,38 @@ __device__ __forceinline__ void accumulate8(uint4 v, float w, float (&acc)[8])
     for (int c = 0; c < 8; ++c) acc[c] = acc[c] + w * f[c];
 }
 
+// Element c (0..3) of four int8 codes packed in a word, as a float (exact).
+__device__ __forceinline__ float code_at(uint32_t w, int c)
+{
+    return (float)(int32_t)(int8_t)(uint8_t)(w >> (8 * c));
+}
+
+// acc[c] = acc[c] + w * (code_c * scale): dequantize eight int8 codes of one block (one
+// multiply), then weight and accumulate (one multiply, one add)
+__device__ __forceinline__ void accumulate8_int8(uint2 q, float scale, float w, float (&acc)[8])
+{
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const float t0 = code_at(q.x, c) * scale;
+        acc[c] = acc[c] + w * t0;
+        const float t1 = code_at(q.y, c) * scale;
+        acc[4 + c] = acc[4 + c] + w * t1;
+    }
+}
+
+typedef uint32_t u32x2_ld_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint2 load_stream8(const uint2* p)
+{
+    const u32x2_ld_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_ld_t*>(p));
+    return make_uint2(v.x, v.y);
+}
+
+__device__ __forceinline__ float load_stream4(const float* p)
+{
+    return __builtin_nontemporal_load(p);
+}
+
 constexpr int kWavesPerBlock = 4;
 
 // 64-vector slots of one token per wave task: two (16 row loads in flight per lane at K=8);
@@ -74,14 +114,17 @@ constexpr int slots_per_task(int kmax) { return kmax > 8 ? 1 : 2; }
 // split across several independent waves (each resolves the token's K sources itself), so a
 // launch is many short tasks: the hardware keeps every SIMD busy to the end instead of
 // leaving a long, thinly occupied last round of whole-token waves.
-template <int KMAX, int SLOTS>
+// Q = 0: bf16 expert rows.  Q = 1: int8 codes [cap][H] and fp32 block scales [cap][H/8]
+// (qscales), one block per lane vector; a routed pick's buffer entry then holds the two code
+// words and the scale's bits.
+template <int KMAX, int SLOTS, int Q>
 __global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_wave_kernel(
-    const uint16_t* __restrict__ expert_out, const int32_t* __restrict__ ids,
-    const int32_t* __restrict__ expand_idx, const float* __restrict__ weights,
-    const int32_t* __restrict__ ep_recv_count, const int64_t* __restrict__ recv_offsets,
-    const uint8_t* __restrict__ mask, int mask_kind, const uint16_t* __restrict__ ori_x,
-    uint16_t* __restrict__ y, int W, int E, int L, int BS, int H, int K, int zero_end,
-    int id_end, long long cap, long long T, int tasks_per_token)
+    const void* __restrict__ expert_out, const float* __restrict__ qscales,
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ expand_idx,
+    const float* __restrict__ weights, const int32_t* __restrict__ ep_recv_count,
+    const int64_t* __restrict__ recv_offsets, const uint8_t* __restrict__ mask, int mask_kind,
+    const uint16_t* __restrict__ ori_x, uint16_t* __restrict__ y, int W, int E, int L, int BS,
+    int H, int K, int zero_end, int id_end, long long cap, long long T, int tasks_per_token)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const long long task = (long long)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
@@ -107,6 +150,7 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_wave_kernel(
     }
 
     const uint4* eo = reinterpret_cast<const uint4*>(expert_out);
+    const uint2* eq = reinterpret_cast<const uint2*>(expert_out);
     const uint4* self = ori_x ? reinterpret_cast<const uint4*>(ori_x) + tok * NV : nullptr;
     uint4* yr = reinterpret_cast<uint4*>(y) + tok * NV;
     uint4 buf[SLOTS][KMAX];
@@ -116,8 +160,17 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_wave_kernel(
         if (v < NV) {
 #pragma unroll
             for (int k = 0; k < KMAX; ++k) {
-                if (srcs[k] >= 0) buf[n][k] = load_stream(eo + (long long)srcs[k] * NV + v);
-                else if (srcs[k] == kCopy) buf[n][k] = self[v];
+                if (srcs[k] >= 0) {
+                    if (Q == 0) {
+                        buf[n][k] = load_stream(eo + (long long)srcs[k] * NV + v);
+                    } else {
+                        const uint2 q = load_stream8(eq + (long long)srcs[k] * NV + v);
+                        const float sc = load_stream4(qscales + (long long)srcs[k] * NV + v);
+                        buf[n][k] = make_uint4(q.x, q.y, __float_as_uint(sc), 0u);
+                    }
+                } else if (srcs[k] == kCopy) {
+                    buf[n][k] = self[v];
+                }
             }
         }
     }
@@ -129,8 +182,14 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_wave_kernel(
 #pragma unroll
             for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
 #pragma unroll
-            for (int k = 0; k < KMAX; ++k)
-                if (srcs[k] != kNone) accumulate8(buf[n][k], ws[k], acc);
+            for (int k = 0; k < KMAX; ++k) {
+                if (srcs[k] == kNone) continue;
+                if (Q == 1 && srcs[k] >= 0)
+                    accumulate8_int8(make_uint2(buf[n][k].x, buf[n][k].y),
+                                     __uint_as_float(buf[n][k].z), ws[k], acc);
+                else
+                    accumulate8(buf[n][k], ws[k], acc);
+            }
             store_stream(yr + v,
                          make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
                                     pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])));
@@ -138,11 +197,11 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_wave_kernel(
     }
 }
 
-template <int KMAX>
-hipError_t launch_wave_k(const Shape& sh, const void* expert_out, const int32_t* ids,
-                         const int32_t* expand_idx, const float* w, const int32_t* erc,
-                         const int64_t* roff, const uint8_t* mask, const void* ori_x, void* y,
-                         hipStream_t stream)
+template <int KMAX, int Q>
+hipError_t launch_wave_k(const Shape& sh, const void* expert_out, const float* qscales,
+                         const int32_t* ids, const int32_t* expand_idx, const float* w,
+                         const int32_t* erc, const int64_t* roff, const uint8_t* mask,
+                         const void* ori_x, void* y, hipStream_t stream)
 {
     const long long T = (long long)sh.W * sh.BS;
     const int slots = ((sh.H >> 3) + kWave - 1) / kWave;
@@ -150,48 +209,56 @@ hipError_t launch_wave_k(const Shape& sh, const void* expert_out, const int32_t*
     const int tasks_per_token = (slots + kSlots - 1) / kSlots;
     const long long tasks = T * tasks_per_token;
     const unsigned blocks = (unsigned)((tasks + kWavesPerBlock - 1) / kWavesPerBlock);
-    hipLaunchKernelGGL((combine_wave_kernel<KMAX, kSlots>), dim3(blocks),
-                       dim3(kWave * kWavesPerBlock), 0, stream,
-                       static_cast<const uint16_t*>(expert_out), ids, expand_idx, w, erc, roff,
-                       mask, sh.mask_kind, static_cast<const uint16_t*>(ori_x),
-                       static_cast<uint16_t*>(y), sh.W, sh.E, sh.L, sh.BS, sh.H, sh.K,
-                       sh.zero_end, sh.id_end, (long long)sh.cap, T, tasks_per_token);
+    hipLaunchKernelGGL((combine_wave_kernel<KMAX, kSlots, Q>), dim3(blocks),
+                       dim3(kWave * kWavesPerBlock), 0, stream, expert_out, qscales, ids,
+                       expand_idx, w, erc, roff, mask, sh.mask_kind,
+                       static_cast<const uint16_t*>(ori_x), static_cast<uint16_t*>(y), sh.W,
+                       sh.E, sh.L, sh.BS, sh.H, sh.K, sh.zero_end, sh.id_end,
+                       (long long)sh.cap, T, tasks_per_token);
     return hipGetLastError();
 }
 
-hipError_t launch_wave(const Shape& sh, const void* eo, const int32_t* ids, const int32_t* ei,
-                       const float* w, const int32_t* erc, const int64_t* roff,
-                       const uint8_t* mask, const void* ori_x, void* y, hipStream_t stream)
+template <int Q>
+hipError_t launch_wave(const Shape& sh, const void* eo, const float* qs, const int32_t* ids,
+                       const int32_t* ei, const float* w, const int32_t* erc,
+                       const int64_t* roff, const uint8_t* mask, const void* ori_x, void* y,
+                       hipStream_t stream)
 {
-    if (sh.K <= 2) return launch_wave_k<2>(sh, eo, ids, ei, w, erc, roff, mask, ori_x, y, stream);
-    if (sh.K <= 4) return launch_wave_k<4>(sh, eo, ids, ei, w, erc, roff, mask, ori_x, y, stream);
-    if (sh.K <= 8) return launch_wave_k<8>(sh, eo, ids, ei, w, erc, roff, mask, ori_x, y, stream);
-    return launch_wave_k<16>(sh, eo, ids, ei, w, erc, roff, mask, ori_x, y, stream);
+#define MOE_DC_ARGS sh, eo, qs, ids, ei, w, erc, roff, mask, ori_x, y, stream
+    if (sh.K <= 2) return launch_wave_k<2, Q>(MOE_DC_ARGS);
+    if (sh.K <= 4) return launch_wave_k<4, Q>(MOE_DC_ARGS);
+    if (sh.K <= 8) return launch_wave_k<8, Q>(MOE_DC_ARGS);
+    return launch_wave_k<16, Q>(MOE_DC_ARGS);
+#undef MOE_DC_ARGS
 }
 
 constexpr int kElemThreads = 1024;
 constexpr int kElemPerLane = 8;      // H <= 8192 = 1024 lanes x 8
 
-template <int KMAX>
+// Element-wise combine; Q as for combine_wave_kernel (codes [cap][H], scales [cap][Ceil(H,8)]).
+template <int KMAX, int Q>
 __global__ __launch_bounds__(kElemThreads) void combine_elem_kernel(
-    const uint16_t* __restrict__ expert_out, const int32_t* __restrict__ ids,
-    const int32_t* __restrict__ expand_idx, const float* __restrict__ weights,
-    const int32_t* __restrict__ ep_recv_count, const int64_t* __restrict__ recv_offsets,
-    const uint8_t* __restrict__ mask, int mask_kind, const uint16_t* __restrict__ ori_x,
-    uint16_t* __restrict__ y, int W, int E, int L, int BS, int H, int K, int zero_end,
-    int id_end, long long cap)
+    const void* __restrict__ expert_out, const float* __restrict__ qscales,
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ expand_idx,
+    const float* __restrict__ weights, const int32_t* __restrict__ ep_recv_count,
+    const int64_t* __restrict__ recv_offsets, const uint8_t* __restrict__ mask, int mask_kind,
+    const uint16_t* __restrict__ ori_x, uint16_t* __restrict__ y, int W, int E, int L, int BS,
+    int H, int K, int zero_end, int id_end, long long cap)
 {
     __shared__ int src_of[KMAX];
     __shared__ float w_of[KMAX];
     const long long tok = blockIdx.x;
     const int s = (int)(tok / BS);
     const int t = threadIdx.x;
+    const int nb = (H + 7) / 8;
     if (t < K) {
         src_of[t] = pick_source(ids, expand_idx, ep_recv_count, recv_offsets, mask, mask_kind,
                                 W, E, L, K, zero_end, id_end, cap, tok, s, t);
         w_of[t] = weights[tok * K + t];
     }
     __syncthreads();
+    const uint16_t* eo = static_cast<const uint16_t*>(expert_out);
+    const int8_t* eq = static_cast<const int8_t*>(expert_out);
     const uint16_t* self = ori_x ? ori_x + tok * H : nullptr;
     uint16_t* yr = y + tok * H;
 #pragma unroll 1
@@ -202,36 +269,131 @@ __global__ __launch_bounds__(kElemThreads) void combine_elem_kernel(
         for (int k = 0; k < K; ++k) {
             const int src = src_of[k];
             if (src == kNone) continue;
-            const uint16_t b = src >= 0 ? expert_out[(long long)src * H + h] : self[h];
-            acc = acc + w_of[k] * bf16_lo(b);
+            float v;
+            if (src >= 0 && Q == 1) {
+                const float t0 = (float)eq[(long long)src * H + h];
+                v = t0 * qscales[(long long)src * nb + h / 8];
+            } else {
+                v = bf16_lo(src >= 0 ? eo[(long long)src * H + h] : self[h]);
+            }
+            acc = acc + w_of[k] * v;
         }
         yr[h] = (uint16_t)f32_to_bf16_rne(acc);
     }
 }
 
-template <int KMAX>
-hipError_t launch_elem_k(const Shape& sh, const void* expert_out, const int32_t* ids,
-                         const int32_t* expand_idx, const float* w, const int32_t* erc,
-                         const int64_t* roff, const uint8_t* mask, const void* ori_x, void* y,
-                         hipStream_t stream)
+template <int KMAX, int Q>
+hipError_t launch_elem_k(const Shape& sh, const void* expert_out, const float* qscales,
+                         const int32_t* ids, const int32_t* expand_idx, const float* w,
+                         const int32_t* erc, const int64_t* roff, const uint8_t* mask,
+                         const void* ori_x, void* y, hipStream_t stream)
 {
     const int want = (sh.H + kWave - 1) / kWave * kWave;
     const int threads = want < kElemThreads ? want : kElemThreads;
     const long long T = (long long)sh.W * sh.BS;
-    hipLaunchKernelGGL((combine_elem_kernel<KMAX>), dim3((unsigned)T), dim3(threads), 0,
-                       stream, static_cast<const uint16_t*>(expert_out), ids, expand_idx, w,
-                       erc, roff, mask, sh.mask_kind, static_cast<const uint16_t*>(ori_x),
+    hipLaunchKernelGGL((combine_elem_kernel<KMAX, Q>), dim3((unsigned)T), dim3(threads), 0,
+                       stream, expert_out, qscales, ids, expand_idx, w, erc, roff, mask,
+                       sh.mask_kind, static_cast<const uint16_t*>(ori_x),
                        static_cast<uint16_t*>(y), sh.W, sh.E, sh.L, sh.BS, sh.H, sh.K,
                        sh.zero_end, sh.id_end, (long long)sh.cap);
     return hipGetLastError();
 }
 
-hipError_t launch_elem(const Shape& sh, const void* eo, const int32_t* ids, const int32_t* ei,
-                       const float* w, const int32_t* erc, const int64_t* roff,
-                       const uint8_t* mask, const void* ori_x, void* y, hipStream_t stream)
+template <int Q>
+hipError_t launch_elem(const Shape& sh, const void* eo, const float* qs, const int32_t* ids,
+                       const int32_t* ei, const float* w, const int32_t* erc,
+                       const int64_t* roff, const uint8_t* mask, const void* ori_x, void* y,
+                       hipStream_t stream)
 {
-    if (sh.K <= 4) return launch_elem_k<4>(sh, eo, ids, ei, w, erc, roff, mask, ori_x, y, stream);
-    return launch_elem_k<16>(sh, eo, ids, ei, w, erc, roff, mask, ori_x, y, stream);
+    if (sh.K <= 4)
+        return launch_elem_k<4, Q>(sh, eo, qs, ids, ei, w, erc, roff, mask, ori_x, y, stream);
+    return launch_elem_k<16, Q>(sh, eo, qs, ids, ei, w, erc, roff, mask, ori_x, y, stream);
+}
+
+// ---------------------------------------------------------------------------------------
+// expert-side int8 block quantization of the packed expert-output rows [0, recv_offsets[W])
+// ---------------------------------------------------------------------------------------
+
+constexpr float kInv127 = 1.0f / 127.0f;   // the reciprocal of SCALE_PARAM, one fp32 rounding
+
+// int8 code of x / scale through fp16: each narrowing rounds to nearest even, the int8 step
+// saturates at +-127, and a NaN quotient (0 / 0 in an all-zero block) gives 0.
+__device__ __forceinline__ uint32_t block_code(float x, float scale)
+{
+    const float v = x / scale;
+    const float h = (float)(_Float16)v;
+    if (h != h) return 0u;
+    const float r = fminf(fmaxf(__builtin_rintf(h), -127.0f), 127.0f);
+    return (uint32_t)(int32_t)r & 0xFFu;
+}
+
+// One wave task = one row x 2 slots of 64 lanes; each lane owns one 8-element block.
+constexpr int kQuantSlots = 2;
+
+__global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_quantize_kernel(
+    const uint16_t* __restrict__ expert_out, const int64_t* __restrict__ recv_offsets,
+    int8_t* __restrict__ codes, float* __restrict__ qscales, int W, int H, long long cap,
+    int tasks_per_row)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const long long task = (long long)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
+    const long long row = task / tasks_per_row;
+    const long long rows = recv_offsets[W];
+    if (row >= cap || row >= rows) return;                 // whole wave
+    const int slot0 = (int)(task - row * tasks_per_row) * kQuantSlots;
+    const int NV = H >> 3;
+    const uint4* src = reinterpret_cast<const uint4*>(expert_out) + row * NV;
+    uint4 raw[kQuantSlots];
+#pragma unroll
+    for (int n = 0; n < kQuantSlots; ++n) {
+        const int v = lane + (slot0 + n) * kWave;
+        if (v < NV) raw[n] = load_stream(src + v);
+    }
+#pragma unroll
+    for (int n = 0; n < kQuantSlots; ++n) {
+        const int v = lane + (slot0 + n) * kWave;
+        if (v >= NV) continue;
+        const float f[8] = {bf16_lo(raw[n].x), bf16_hi(raw[n].x), bf16_lo(raw[n].y),
+                            bf16_hi(raw[n].y), bf16_lo(raw[n].z), bf16_hi(raw[n].z),
+                            bf16_lo(raw[n].w), bf16_hi(raw[n].w)};
+        uint32_t amax = 0;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const uint32_t b = __float_as_uint(f[c]) & 0x7FFFFFFFu;
+            amax = amax > b ? amax : b;
+        }
+        const float scale = __uint_as_float(amax) * kInv127;
+        uint32_t c8[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) c8[c] = block_code(f[c], scale);
+        const uint2 packed = make_uint2(c8[0] | (c8[1] << 8) | (c8[2] << 16) | (c8[3] << 24),
+                                        c8[4] | (c8[5] << 8) | (c8[6] << 16) | (c8[7] << 24));
+        store_stream(reinterpret_cast<uint2*>(codes) + row * NV + v, packed);
+        __builtin_nontemporal_store(scale, qscales + row * NV + v);
+    }
+}
+
+// Element-wise quantization: one workgroup per row, one element per lane; a block is 8
+// adjacent lanes (the last block of a row may be short).
+__global__ __launch_bounds__(kElemThreads) void combine_quantize_elem_kernel(
+    const uint16_t* __restrict__ expert_out, const int64_t* __restrict__ recv_offsets,
+    int8_t* __restrict__ codes, float* __restrict__ qscales, int W, int H)
+{
+    const long long row = blockIdx.x;
+    if (row >= recv_offsets[W]) return;                    // whole workgroup
+    const int t = threadIdx.x;
+    const int nb = (H + 7) / 8;
+#pragma unroll 1
+    for (int n = 0; n < kElemPerLane; ++n) {
+        const int h = t + n * blockDim.x;
+        if (n * (int)blockDim.x >= H) break;               // uniform across the workgroup
+        const float f = h < H ? bf16_lo(expert_out[row * H + h]) : 0.0f;
+        const uint32_t amax = group_max_u32<8>(__float_as_uint(f) & 0x7FFFFFFFu);
+        const float scale = __uint_as_float(amax) * kInv127;
+        if (h >= H) continue;
+        codes[row * H + h] = (int8_t)block_code(f, scale);
+        if ((h & 7) == 0) qscales[row * nb + h / 8] = scale;
+    }
 }
 
 }  // namespace
@@ -243,10 +405,45 @@ hipError_t launch_combine(const Shape& sh, const void* expert_out, const int32_t
                           hipStream_t stream)
 {
     if (vectorized)
-        return launch_wave(sh, expert_out, expert_ids, expand_idx, expert_scales, ep_recv_count,
-                           recv_offsets, mask, ori_x, y, stream);
-    return launch_elem(sh, expert_out, expert_ids, expand_idx, expert_scales, ep_recv_count,
-                       recv_offsets, mask, ori_x, y, stream);
+        return launch_wave<0>(sh, expert_out, nullptr, expert_ids, expand_idx, expert_scales,
+                              ep_recv_count, recv_offsets, mask, ori_x, y, stream);
+    return launch_elem<0>(sh, expert_out, nullptr, expert_ids, expand_idx, expert_scales,
+                          ep_recv_count, recv_offsets, mask, ori_x, y, stream);
+}
+
+hipError_t launch_combine_int8(const Shape& sh, const int8_t* codes, const float* qscales,
+                               const int32_t* expert_ids, const int32_t* expand_idx,
+                               const float* expert_scales, const int32_t* ep_recv_count,
+                               const int64_t* recv_offsets, const uint8_t* mask,
+                               const void* ori_x, void* y, bool vectorized, hipStream_t stream)
+{
+    if (vectorized)
+        return launch_wave<1>(sh, codes, qscales, expert_ids, expand_idx, expert_scales,
+                              ep_recv_count, recv_offsets, mask, ori_x, y, stream);
+    return launch_elem<1>(sh, codes, qscales, expert_ids, expand_idx, expert_scales,
+                          ep_recv_count, recv_offsets, mask, ori_x, y, stream);
+}
+
+hipError_t launch_combine_quantize(const Shape& sh, const void* expert_out,
+                                   const int64_t* recv_offsets, int8_t* codes, float* qscales,
+                                   bool vectorized, hipStream_t stream)
+{
+    if (vectorized) {
+        const int slots = ((sh.H >> 3) + kWave - 1) / kWave;
+        const int tasks_per_row = (slots + kQuantSlots - 1) / kQuantSlots;
+        const long long tasks = (long long)sh.cap * tasks_per_row;
+        const unsigned blocks = (unsigned)((tasks + kWavesPerBlock - 1) / kWavesPerBlock);
+        hipLaunchKernelGGL(combine_quantize_kernel, dim3(blocks), dim3(kWave * kWavesPerBlock),
+                           0, stream, static_cast<const uint16_t*>(expert_out), recv_offsets,
+                           codes, qscales, sh.W, sh.H, (long long)sh.cap, tasks_per_row);
+    } else {
+        const int want = (sh.H + kWave - 1) / kWave * kWave;
+        const int threads = want < kElemThreads ? want : kElemThreads;
+        hipLaunchKernelGGL(combine_quantize_elem_kernel, dim3((unsigned)sh.cap),
+                           dim3(threads), 0, stream, static_cast<const uint16_t*>(expert_out),
+                           recv_offsets, codes, qscales, sh.W, sh.H);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace moe_dc

@@ -60,4 +60,17 @@ hipError_t launch_combine(const Shape& s, const void* expert_out, const int32_t*
                           const uint8_t* mask, const void* ori_x, void* y, bool vectorized,
                           hipStream_t stream);
 
+// Weighted top-K gather over int8 block-quantized expert rows (codes [cap][H], fp32 scales
+// [cap][Ceil(H,8)]).
+hipError_t launch_combine_int8(const Shape& s, const int8_t* codes, const float* qscales,
+                               const int32_t* expert_ids, const int32_t* expand_idx,
+                               const float* expert_scales, const int32_t* ep_recv_count,
+                               const int64_t* recv_offsets, const uint8_t* mask,
+                               const void* ori_x, void* y, bool vectorized, hipStream_t stream);
+
+// Expert-side int8 block quantization of the rows [0, recv_offsets[W]).
+hipError_t launch_combine_quantize(const Shape& s, const void* expert_out,
+                                   const int64_t* recv_offsets, int8_t* codes, float* qscales,
+                                   bool vectorized, hipStream_t stream);
+
 }  // namespace moe_dc

@@ -209,6 +209,42 @@ moe_status moe_combine(const moe_dc_config* cfg,
                        const uint8_t* x_active_mask, const void* ori_x, void* y,
                        void* stream);
 
+/* moe_combine_quantize -- expert-side int8 block quantization of the expert outputs, the
+ * compression the pages apply before the combine's return transfer.
+ *
+ * Defined by: [SMP] 通信前量化 (Combine 的 INT8 block 量化): each expert-output row is cut into
+ * blocks of 8 elements (32 bytes of fp32); per block scale = amax * (1/127) (the reciprocal of
+ * 127 rounded once to fp32), and each code = int8(fp16(x / scale)), where the division is one
+ * IEEE fp32 division and each narrowing rounds to nearest even (int8 saturates at +-127; an
+ * all-zero block gives codes 0 and scale 0).
+ *
+ * Inputs:
+ *   expert_out     bf16 [cap][H]      as for moe_combine
+ *   recv_offsets   int64 [W+1]        from moe_dispatch; rows [0, recv_offsets[W]) are coded
+ * Outputs:
+ *   codes          int8 [cap][H]
+ *   block_scales   fp32 [cap][Ceil(H, 8)]
+ * Rows at or past recv_offsets[W] are not written.  Errors as for moe_combine. */
+moe_status moe_combine_quantize(const moe_dc_config* cfg, const void* expert_out,
+                                const int64_t* recv_offsets, int8_t* codes,
+                                float* block_scales, void* stream);
+
+/* moe_combine_int8 -- moe_combine over block-quantized expert outputs.
+ *
+ * Defined by: moe_combine's definition with each routed pick's row dequantized first
+ * ([SMP] 通信前量化: int8 -> fp16 -> float, both exact, times the block's scale, one fp32
+ * multiply); zero experts add nothing, copy experts add w * ori_x (ori_x is not quantized).
+ *
+ * Inputs: codes and block_scales as written by moe_combine_quantize; the other arguments as
+ * for moe_combine.  Output: y bf16 [W][BS][H] = bf16_rne( sum over active picks in k order
+ * of w * (code * scale) ), accumulated in fp32 from +0.  Errors as for moe_combine. */
+moe_status moe_combine_int8(const moe_dc_config* cfg, const int8_t* codes,
+                            const float* block_scales, const int32_t* expert_ids,
+                            const int32_t* expand_idx, const float* expert_scales,
+                            const int32_t* ep_recv_count, const int64_t* recv_offsets,
+                            const uint8_t* x_active_mask, const void* ori_x, void* y,
+                            void* stream);
+
 /* Text of the last non-OK status on this thread ("" if none). */
 const char* moe_dc_last_error(void);
 

@@ -56,6 +56,7 @@ class Workload:
     scales_kind: int = 0        # 0 none, 1 scalar, 2 shared row (H,), 3 per expert (E, H)
     out_dtype: int = 0          # 0 the mode's default, 1 int8, 2 E4M3, 3 E5M2
     scale_format: int = 0       # 0 fp32 scales, 1 E8M0 bytes (MX modes)
+    combine_quant: int = 0      # 0 bf16 expert rows, 1 int8 blocks of 8 on the return path
     routing: str = "uniform"    # uniform | zipf | randint
     zipf_s: float = 1.2
     outlier_prob: float = 0.0
@@ -132,8 +133,13 @@ C2_GROUP_SMOOTH = C2.replace(
     name="c2v_w8_group_e4m3_smooth", quant_mode=3,
     description="C2 with per-128-group dynamic E4M3 codes and per-expert smooth scales")
 
+C4_COMBINE_INT8 = C4.replace(
+    name="c4v_w16_combine_int8", combine_quant=1,
+    description="C4 with the combine-side int8 block quantization: the expert outputs are "
+                "coded as int8 with one fp32 scale per 8 elements, then combined")
+
 WORKLOADS = {w.name: w for w in (C1_MODE0, C1_MODE2, C2, C3, C4, C5, C3_E5M2_E8M0, C4_STATIC,
-                                 C4_TOKEN_E4M3, C4_GROUP, C2_GROUP_SMOOTH)}
+                                 C4_TOKEN_E4M3, C4_GROUP, C2_GROUP_SMOOTH, C4_COMBINE_INT8)}
 
 
 def _streams(seed: int):
