@@ -197,6 +197,101 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_wave_kernel(
     }
 }
 
+// Int8 combine with 16-element lanes (H % 16 == 0): per pick a lane reads one 16-byte code
+// vector and one 8-byte pair of block scales (two blocks) instead of 8 + 4 bytes, so every
+// load instruction moves twice the bytes.  One wave task = one token x 64 lanes x 16
+// elements.  A copy expert's ori_x half-rows are read when they are accumulated.
+template <int KMAX>
+__global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_int8_wide_kernel(
+    const int8_t* __restrict__ codes, const float* __restrict__ qscales,
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ expand_idx,
+    const float* __restrict__ weights, const int32_t* __restrict__ ep_recv_count,
+    const int64_t* __restrict__ recv_offsets, const uint8_t* __restrict__ mask, int mask_kind,
+    const uint16_t* __restrict__ ori_x, uint16_t* __restrict__ y, int W, int E, int L, int BS,
+    int H, int K, int zero_end, int id_end, long long cap, long long T, int tasks_per_token)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const long long task = (long long)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
+    const long long tok = task / tasks_per_token;
+    if (tok >= T) return;                                  // whole wave
+    const int u = lane + (int)(task - tok * tasks_per_token) * kWave;
+    const int s = (int)(tok / BS);
+    const int NU = H >> 4;                                 // 16-element units per row
+    const int NV = H >> 3;
+
+    int src = kNone;
+    float wk = 0.0f;
+    if (lane < K) {
+        src = pick_source(ids, expand_idx, ep_recv_count, recv_offsets, mask, mask_kind, W, E,
+                          L, K, zero_end, id_end, cap, tok, s, lane);
+        wk = weights[tok * K + lane];
+    }
+    int srcs[KMAX];
+    float ws[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        srcs[k] = k < K ? lane_value(src, k) : kNone;
+        ws[k] = lane_value(wk, k);
+    }
+    if (u >= NU) return;
+
+    const uint4* cq = reinterpret_cast<const uint4*>(codes);
+    const uint2* sq = reinterpret_cast<const uint2*>(qscales);
+    const uint4* self = ori_x ? reinterpret_cast<const uint4*>(ori_x) + tok * NV : nullptr;
+    uint4 cbuf[KMAX];
+    uint2 sbuf[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        if (srcs[k] >= 0) {
+            cbuf[k] = load_stream(cq + (long long)srcs[k] * NU + u);
+            sbuf[k] = load_stream8(sq + (long long)srcs[k] * NU + u);
+        }
+    }
+    float lo[8], hi[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        lo[c] = 0.0f;
+        hi[c] = 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        if (srcs[k] >= 0) {
+            accumulate8_int8(make_uint2(cbuf[k].x, cbuf[k].y), __uint_as_float(sbuf[k].x),
+                             ws[k], lo);
+            accumulate8_int8(make_uint2(cbuf[k].z, cbuf[k].w), __uint_as_float(sbuf[k].y),
+                             ws[k], hi);
+        } else if (srcs[k] == kCopy) {
+            accumulate8(self[2 * u], ws[k], lo);
+            accumulate8(self[2 * u + 1], ws[k], hi);
+        }
+    }
+    uint4* yr = reinterpret_cast<uint4*>(y) + tok * NV;
+    store_stream(yr + 2 * u, make_uint4(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]),
+                                        pack_bf16x2(lo[4], lo[5]), pack_bf16x2(lo[6], lo[7])));
+    store_stream(yr + 2 * u + 1,
+                 make_uint4(pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3]),
+                            pack_bf16x2(hi[4], hi[5]), pack_bf16x2(hi[6], hi[7])));
+}
+
+template <int KMAX>
+hipError_t launch_int8_wide_k(const Shape& sh, const int8_t* codes, const float* qscales,
+                              const int32_t* ids, const int32_t* expand_idx, const float* w,
+                              const int32_t* erc, const int64_t* roff, const uint8_t* mask,
+                              const void* ori_x, void* y, hipStream_t stream)
+{
+    const long long T = (long long)sh.W * sh.BS;
+    const int tasks_per_token = ((sh.H >> 4) + kWave - 1) / kWave;
+    const long long tasks = T * tasks_per_token;
+    const unsigned blocks = (unsigned)((tasks + kWavesPerBlock - 1) / kWavesPerBlock);
+    hipLaunchKernelGGL((combine_int8_wide_kernel<KMAX>), dim3(blocks),
+                       dim3(kWave * kWavesPerBlock), 0, stream, codes, qscales, ids,
+                       expand_idx, w, erc, roff, mask, sh.mask_kind,
+                       static_cast<const uint16_t*>(ori_x), static_cast<uint16_t*>(y), sh.W,
+                       sh.E, sh.L, sh.BS, sh.H, sh.K, sh.zero_end, sh.id_end,
+                       (long long)sh.cap, T, tasks_per_token);
+    return hipGetLastError();
+}
+
 template <int KMAX, int Q>
 hipError_t launch_wave_k(const Shape& sh, const void* expert_out, const float* qscales,
                          const int32_t* ids, const int32_t* expand_idx, const float* w,
@@ -417,6 +512,18 @@ hipError_t launch_combine_int8(const Shape& sh, const int8_t* codes, const float
                                const int64_t* recv_offsets, const uint8_t* mask,
                                const void* ori_x, void* y, bool vectorized, hipStream_t stream)
 {
+    // 16-element lanes need 16-byte aligned code rows and 8-byte aligned scale pairs
+    const bool wide = vectorized && sh.H % 16 == 0 && sh.K <= 8 &&
+                      (reinterpret_cast<uintptr_t>(codes) & 15u) == 0 &&
+                      (reinterpret_cast<uintptr_t>(qscales) & 7u) == 0;
+    if (wide) {
+#define MOE_DC_ARGS sh, codes, qscales, expert_ids, expand_idx, expert_scales, ep_recv_count, \
+                    recv_offsets, mask, ori_x, y, stream
+        if (sh.K <= 2) return launch_int8_wide_k<2>(MOE_DC_ARGS);
+        if (sh.K <= 4) return launch_int8_wide_k<4>(MOE_DC_ARGS);
+        return launch_int8_wide_k<8>(MOE_DC_ARGS);
+#undef MOE_DC_ARGS
+    }
     if (vectorized)
         return launch_wave<1>(sh, codes, qscales, expert_ids, expand_idx, expert_scales,
                               ep_recv_count, recv_offsets, mask, ori_x, y, stream);

@@ -25,6 +25,12 @@ CASES = {
                         inactive_tokens_per_rank=9),
     "elem_h1030": WL("cq_h1030", W=2, E=8, BS=33, H=1030, K=3, quant_mode=0,
                      copy_expert_num=1),
+    # H % 16 != 0 keeps 8-element lanes; K <= 8 with H % 16 == 0 takes 16-element lanes
+    "narrow_h1032_copy": WL("cq_h1032", W=3, E=12, BS=50, H=1032, K=5, quant_mode=2,
+                            copy_expert_num=2, zero_expert_num=1, routing="randint"),
+    "wide_copy_k4": WL("cq_wide_copy", W=2, E=16, BS=90, H=2048, K=4, quant_mode=2,
+                       copy_expert_num=1, zero_expert_num=1, mask_kind=2,
+                       inactive_tokens_per_rank=7),
 }
 
 
