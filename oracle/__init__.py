@@ -52,6 +52,8 @@ def _load():
             "oracle_combine_dequant_row": (None, [P, P, i32, P]),
             "oracle_combine_quantize": (i32, [P] * 5),
             "oracle_combine_int8": (i32, [P] * 13),
+            "oracle_expand_scales": (i32, [P] * 5),
+            "oracle_combine_scatter": (i32, [P] * 12),
             "oracle_mx_scale_count": (i32, [i32]),
             "oracle_code_type": (i32, [i32, i32]),
             "oracle_scale_count": (i32, [i32, i32]),
@@ -348,4 +350,37 @@ def combine_int8(cfg, codes, scales, expert_ids, expand_idx, expert_scales, ep_r
                                      _p(erc), _p(off), _p(m), _p(ox), _p(y), _p(acc), _p(row))
     if rc != 0:
         raise ValueError(f"oracle_combine_int8 rejected the input (rc={rc})")
+    return y
+
+
+# -- weights with the rows, scatter-back combine ---------------------------------------------
+
+def expand_scales(cfg, assist_info, recv_offsets, expert_scales, cap):
+    ai = _c(assist_info, np.int32)
+    off = _c(recv_offsets, np.int64)
+    w = _c(expert_scales, np.float32)
+    out = np.zeros(cap, np.float32)
+    rc = _load().oracle_expand_scales(_ref(cfg), _p(ai), _p(off), _p(w), _p(out))
+    if rc != 0:
+        raise ValueError(f"oracle_expand_scales rejected the input (rc={rc})")
+    return out
+
+
+def combine_scatter(cfg, expert_out, assist_info, recv_offsets, expert_ids, expert_scales,
+                    mask=None, ori_x=None, shared_x=None):
+    eo = _c(expert_out, np.uint16)
+    ai = _c(assist_info, np.int32)
+    off = _c(recv_offsets, np.int64)
+    ids = _c(expert_ids, np.int32)
+    w = _c(expert_scales, np.float32)
+    m = _c(mask, np.uint8)
+    ox = _c(ori_x, np.uint16)
+    sx = _c(shared_x, np.uint16)
+    y = np.empty((cfg.W, cfg.BS, cfg.H), np.uint16)
+    window = np.empty(cfg.W * cfg.BS * cfg.K * cfg.H, np.uint16)
+    acc = np.empty(cfg.H, np.float32)
+    rc = _load().oracle_combine_scatter(_ref(cfg), _p(eo), _p(ai), _p(off), _p(ids), _p(w),
+                                        _p(m), _p(ox), _p(sx), _p(y), _p(window), _p(acc))
+    if rc != 0:
+        raise ValueError(f"oracle_combine_scatter rejected the input (rc={rc})")
     return y

@@ -759,3 +759,80 @@ int32_t oracle_combine_int8(const oracle_cfg* c, const int8_t* codes, const floa
         }
     return 0;
 }
+
+/* ------------------------------------------------------------------------------------- */
+/* weights with the rows, and the scatter-back combine                                   */
+/* ------------------------------------------------------------------------------------- */
+
+/* Each dispatched row's pick weight, row-aligned with expand_x: the weight travels with the
+ * token ([OPS] 参数说明, expand_scales_out: the weights of the tokens this card outputs).  The
+ * row's pick is read from its source triple (s, i, k) in assist_info.  Rows at or past
+ * recv_offsets[W] are not written. */
+int32_t oracle_expand_scales(const oracle_cfg* c, const int32_t* assist_info,
+                             const int64_t* recv_offsets, const float* expert_scales,
+                             float* expand_scales)
+{
+    for (int64_t r = 0; r < recv_offsets[c->W]; ++r) {
+        int32_t s = assist_info[r * 3 + 0], i = assist_info[r * 3 + 1], k = assist_info[r * 3 + 2];
+        if (s < 0 || s >= c->W || i < 0 || i >= c->BS || k < 0 || k >= c->K) return -1;
+        expand_scales[r] = expert_scales[((size_t)s * c->BS + i) * c->K + k];
+    }
+    return 0;
+}
+
+/* The sample's scatter-back combine ([SMP] Combine 功能介绍 计算步骤 and 源码实现), in its
+ * order.  First every expert-side row r in [0, recv_offsets[W]) is sent back to its source:
+ * its triple (s, i, k) = assist_info[r] gives the slot epOffset = i * K + k of rank s's
+ * receive window, and the row is copied there.  Then each source token waits for its K
+ * slots and sums them in pick order, each times its expert scale (the source's own
+ * expert_scales, reading R30), in fp32; the shared expert's output, when given, is added
+ * after the K picks (reading R29); the sum is rounded to bf16.
+ * Picks that were never dispatched (inactive, special experts) have no slot: a zero expert
+ * or an inactive pick adds nothing, a copy expert adds w * ori_x, as in oracle_combine.
+ *   window_scratch [W][BS*K][H] bf16; acc_scratch [H] fp32. */
+int32_t oracle_combine_scatter(const oracle_cfg* c, const uint16_t* expert_out,
+                               const int32_t* assist_info, const int64_t* recv_offsets,
+                               const int32_t* expert_ids, const float* expert_scales,
+                               const uint8_t* mask, const uint16_t* ori_x,
+                               const uint16_t* shared_x, uint16_t* y, uint16_t* window,
+                               float* acc)
+{
+    const int32_t H = c->H, K = c->K;
+    const int32_t zero_end = c->E + c->zero_expert_num;
+    const int32_t copy_end = zero_end + c->copy_expert_num;
+    memset(window, 0, (size_t)c->W * c->BS * K * H * sizeof(uint16_t));
+    for (int64_t r = 0; r < recv_offsets[c->W]; ++r) {
+        int32_t s = assist_info[r * 3 + 0], i = assist_info[r * 3 + 1], k = assist_info[r * 3 + 2];
+        if (s < 0 || s >= c->W || i < 0 || i >= c->BS || k < 0 || k >= K) return -1;
+        size_t ep_offset = (size_t)i * K + k;
+        memcpy(window + ((size_t)s * c->BS * K + ep_offset) * H, expert_out + (size_t)r * H,
+               (size_t)H * sizeof(uint16_t));
+    }
+    for (int32_t s = 0; s < c->W; ++s)
+        for (int32_t i = 0; i < c->BS; ++i) {
+            for (int32_t h = 0; h < H; ++h) acc[h] = 0.0f;
+            for (int32_t k = 0; k < K; ++k) {
+                size_t p = ((size_t)s * c->BS + i) * K + k;
+                if (!pair_active(c, mask, s, i, k)) continue;
+                int32_t e = expert_ids[p];
+                float w = expert_scales[p];
+                if (e < 0 || e >= copy_end) return -1;
+                const uint16_t* src;
+                if (e < c->E) src = window + ((size_t)s * c->BS * K + (size_t)i * K + k) * H;
+                else if (e < zero_end) continue;
+                else if (ori_x == NULL) return -1;
+                else src = ori_x + ((size_t)s * c->BS + i) * H;
+                for (int32_t h = 0; h < H; ++h) {
+                    float t = w * oracle_bf16_to_f32(src[h]);
+                    acc[h] = acc[h] + t;
+                }
+            }
+            if (shared_x) {
+                const uint16_t* sh = shared_x + ((size_t)s * c->BS + i) * H;
+                for (int32_t h = 0; h < H; ++h) acc[h] = acc[h] + oracle_bf16_to_f32(sh[h]);
+            }
+            uint16_t* yr = y + ((size_t)s * c->BS + i) * H;
+            for (int32_t h = 0; h < H; ++h) yr[h] = oracle_f32_to_bf16(acc[h]);
+        }
+    return 0;
+}

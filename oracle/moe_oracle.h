@@ -108,6 +108,15 @@ int32_t oracle_combine_int8(const oracle_cfg* c, const int8_t* codes, const floa
                             const int64_t* recv_offsets, const uint8_t* mask,
                             const uint16_t* ori_x, uint16_t* y, float* acc_scratch,
                             float* row_scratch);
+int32_t oracle_expand_scales(const oracle_cfg* c, const int32_t* assist_info,
+                             const int64_t* recv_offsets, const float* expert_scales,
+                             float* expand_scales);
+int32_t oracle_combine_scatter(const oracle_cfg* c, const uint16_t* expert_out,
+                               const int32_t* assist_info, const int64_t* recv_offsets,
+                               const int32_t* expert_ids, const float* expert_scales,
+                               const uint8_t* mask, const uint16_t* ori_x,
+                               const uint16_t* shared_x, uint16_t* y,
+                               uint16_t* window_scratch, float* acc_scratch);
 int32_t oracle_combine(const oracle_cfg* c, const uint16_t* expert_out,
                        const int32_t* expert_ids, const int32_t* expand_idx,
                        const float* expert_scales, const int32_t* ep_recv_count,
