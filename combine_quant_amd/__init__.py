@@ -9,7 +9,8 @@ from .binding import (  # noqa: F401
     MOE_ERR_DEVICE, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_OK,
     MOE_SCALE_E8M0, MOE_SCALE_FP32, MOE_SCALES_NONE, MOE_SCALES_PER_EXPERT,
     MOE_SCALES_SCALAR, MOE_SCALES_SHARED, MoeDcConfig, MoeDcError, alloc_dispatch_outputs,
-    code_type, combine, combine_block_count, combine_int8, combine_quantize, dispatch,
-    load_library, make_config, moe_combine, moe_combine_int8, moe_combine_quantize,
+    code_type, combine, combine_block_count, combine_int8, combine_quantize, combine_scatter,
+    dispatch, load_library, make_config, moe_combine, moe_combine_int8, moe_combine_quantize,
+    moe_combine_scatter, moe_dc_combine_scatter_workspace_bytes,
     moe_dc_dispatch_workspace_bytes, moe_dc_last_error, moe_dc_scales_per_row,
     moe_dc_validate, moe_dc_version, moe_dispatch)

@@ -22,7 +22,8 @@ _STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
            -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_DEVICE"}
 
 EXPORTS = ("moe_dc_validate", "moe_dc_scales_per_row", "moe_dc_dispatch_workspace_bytes",
-           "moe_dispatch", "moe_combine", "moe_combine_quantize", "moe_combine_int8",
+           "moe_dc_combine_scatter_workspace_bytes", "moe_dispatch", "moe_combine",
+           "moe_combine_scatter", "moe_combine_quantize", "moe_combine_int8",
            "moe_dc_last_error", "moe_dc_version")
 
 
@@ -85,7 +86,11 @@ def load_library(path: str = LIB) -> ctypes.CDLL:
     lib.moe_dc_dispatch_workspace_bytes.restype = ctypes.c_size_t
     lib.moe_dc_dispatch_workspace_bytes.argtypes = [cfgp]
     lib.moe_dispatch.restype = ctypes.c_int
-    lib.moe_dispatch.argtypes = [cfgp] + [P] * 11 + [P, ctypes.c_size_t, P]
+    lib.moe_dispatch.argtypes = [cfgp] + [P] * 13 + [P, ctypes.c_size_t, P]
+    lib.moe_dc_combine_scatter_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_dc_combine_scatter_workspace_bytes.argtypes = [cfgp]
+    lib.moe_combine_scatter.restype = ctypes.c_int
+    lib.moe_combine_scatter.argtypes = [cfgp] + [P] * 9 + [P, ctypes.c_size_t, P]
     lib.moe_combine.restype = ctypes.c_int
     lib.moe_combine.argtypes = [cfgp] + [P] * 9 + [P]
     lib.moe_combine_quantize.restype = ctypes.c_int
@@ -189,9 +194,10 @@ def _dyn_scales_spec(cfg):
 
 def moe_dispatch(cfg, x, expert_ids, scales, x_active_mask, expand_x, dynamic_scales,
                  expand_idx, assist_info, ep_recv_count, expert_token_nums, recv_offsets,
-                 workspace, stream=None):
+                 workspace, stream=None, expert_scales=None, expand_scales=None):
     """Enqueue one dispatch on `stream` (default: the current stream of x's device).
-    `scales` is the quantization scales tensor of cfg.scales_kind ([1], [H] or [E][H])."""
+    `scales` is the quantization scales tensor of cfg.scales_kind ([1], [H] or [E][H]);
+    expert_scales [W][BS][K] and expand_scales [cap] (the rows' weights) go together."""
     W, BS, H, K, L, cap = (cfg.ep_world_size, cfg.bs, cfg.hidden, cfg.topk, cfg.L,
                            cfg.expand_rows_capacity)
     dev = x.device
@@ -202,6 +208,7 @@ def moe_dispatch(cfg, x, expert_ids, scales, x_active_mask, expand_x, dynamic_sc
         _ptr(expert_ids, torch.int32, (W, BS, K), "expert_ids", dev),
         _ptr(scales, torch.float32, _scales_shape(cfg), "scales", dev),
         _ptr(x_active_mask, (torch.uint8, torch.bool), mshape, "x_active_mask", dev),
+        _ptr(expert_scales, torch.float32, (W, BS, K), "expert_scales", dev),
         _ptr(expand_x, _CODE_DTYPES.get(code_type(cfg)), (cap, H), "expand_x", dev),
         _ptr(dynamic_scales, None if spec is None else spec[0],
              None if spec is None else spec[1], "dynamic_scales", dev),
@@ -210,6 +217,7 @@ def moe_dispatch(cfg, x, expert_ids, scales, x_active_mask, expand_x, dynamic_sc
         _ptr(ep_recv_count, torch.int32, (W, L * W), "ep_recv_count", dev),
         _ptr(expert_token_nums, torch.int64, (W, L), "expert_token_nums", dev),
         _ptr(recv_offsets, torch.int64, (W + 1,), "recv_offsets", dev),
+        _ptr(expand_scales, torch.float32, (cap,), "expand_scales", dev),
         _ptr(workspace, torch.uint8, None, "workspace", dev),
     ]
     ws_bytes = 0 if workspace is None else workspace.numel()
@@ -238,6 +246,34 @@ def moe_combine(cfg, expert_out, expert_ids, expand_idx, expert_scales, ep_recv_
     ]
     lib = load_library()
     _check(lib.moe_combine(ctypes.byref(cfg), *args, _stream(dev, stream)))
+
+
+def moe_dc_combine_scatter_workspace_bytes(cfg: MoeDcConfig) -> int:
+    return load_library().moe_dc_combine_scatter_workspace_bytes(ctypes.byref(cfg))
+
+
+def moe_combine_scatter(cfg, expert_out, assist_info, recv_offsets, expert_ids, expert_scales,
+                        x_active_mask, ori_x, shared_x, y, workspace, stream=None):
+    """Enqueue one scatter-back combine (rows return by their assist_info triples)."""
+    W, BS, H, K, cap = (cfg.ep_world_size, cfg.bs, cfg.hidden, cfg.topk,
+                        cfg.expand_rows_capacity)
+    dev = y.device
+    mshape = {1: (W, BS), 2: (W, BS, K)}.get(cfg.mask_kind)
+    args = [
+        _ptr(expert_out, torch.bfloat16, (cap, H), "expert_out", dev),
+        _ptr(assist_info, torch.int32, (cap, 3), "assist_info", dev),
+        _ptr(recv_offsets, torch.int64, (W + 1,), "recv_offsets", dev),
+        _ptr(expert_ids, torch.int32, (W, BS, K), "expert_ids", dev),
+        _ptr(expert_scales, torch.float32, (W, BS, K), "expert_scales", dev),
+        _ptr(x_active_mask, (torch.uint8, torch.bool), mshape, "x_active_mask", dev),
+        _ptr(ori_x, torch.bfloat16, (W, BS, H), "ori_x", dev),
+        _ptr(shared_x, torch.bfloat16, (W, BS, H), "shared_x", dev),
+        _ptr(y, torch.bfloat16, (W, BS, H), "y", dev),
+        _ptr(workspace, torch.uint8, None, "workspace", dev),
+    ]
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    _check(load_library().moe_combine_scatter(ctypes.byref(cfg), *args,
+                                              ctypes.c_size_t(ws_bytes), _stream(dev, stream)))
 
 
 def combine_block_count(cfg):
@@ -304,13 +340,36 @@ def alloc_dispatch_outputs(cfg, device="cuda"):
     )
 
 
-def dispatch(cfg, x, expert_ids, scales=None, x_active_mask=None, out=None, stream=None):
-    """Allocate (or reuse `out`) and enqueue moe_dispatch; returns the output dict."""
+def dispatch(cfg, x, expert_ids, scales=None, x_active_mask=None, out=None, stream=None,
+             expert_scales=None):
+    """Allocate (or reuse `out`) and enqueue moe_dispatch; returns the output dict (with
+    "expand_scales" when expert_scales is given)."""
     o = alloc_dispatch_outputs(cfg, x.device) if out is None else out
+    if expert_scales is not None and o.get("expand_scales") is None:
+        o["expand_scales"] = torch.empty((cfg.expand_rows_capacity,), dtype=torch.float32,
+                                         device=x.device)
     moe_dispatch(cfg, x, expert_ids, scales, x_active_mask, o["expand_x"],
                  o["dynamic_scales"], o["expand_idx"], o["assist_info"], o["ep_recv_count"],
-                 o["expert_token_nums"], o["recv_offsets"], o["workspace"], stream)
+                 o["expert_token_nums"], o["recv_offsets"], o["workspace"], stream,
+                 expert_scales=expert_scales,
+                 expand_scales=o.get("expand_scales") if expert_scales is not None else None)
     return o
+
+
+def combine_scatter(cfg, expert_out, assist_info, recv_offsets, expert_ids, expert_scales,
+                    x_active_mask=None, ori_x=None, shared_x=None, y=None, workspace=None,
+                    stream=None):
+    """Allocate (or reuse `y` / `workspace`) and enqueue moe_combine_scatter; returns y."""
+    dev = expert_out.device
+    if y is None:
+        y = torch.empty((cfg.ep_world_size, cfg.bs, cfg.hidden), dtype=torch.bfloat16,
+                        device=dev)
+    if workspace is None:
+        workspace = torch.empty((moe_dc_combine_scatter_workspace_bytes(cfg),),
+                                dtype=torch.uint8, device=dev)
+    moe_combine_scatter(cfg, expert_out, assist_info, recv_offsets, expert_ids, expert_scales,
+                        x_active_mask, ori_x, shared_x, y, workspace, stream)
+    return y
 
 
 def combine(cfg, expert_out, expert_ids, expand_idx, expert_scales, ep_recv_count,

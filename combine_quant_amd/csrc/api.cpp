@@ -1,8 +1,8 @@
 // api.cpp -- C ABI of libmoe_dc: host validation, workspace sizing and launch sequencing.
 //
 // Nothing here allocates device memory or synchronises the host; every launch goes to the
-// caller's stream in order (route -> scan -> scatter for dispatch, one kernel for each of
-// combine, combine quantize and int8 combine).
+// caller's stream in order (route -> scan -> scatter for dispatch; index then gather for the
+// scatter-back combine; one kernel for each of combine, combine quantize and int8 combine).
 #include "moe_dc.h"
 #include "dc_internal.h"
 
@@ -35,6 +35,7 @@ moe_status ok()
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 // Element type of expand_x for a quant mode and requested out_dtype, or -1 when the pair is
 // not allowed ([LLD] 约束说明: mode 0 keeps the input type; mode 1 int8; mode 2 int8, E4M3
@@ -172,10 +173,11 @@ size_t moe_dc_dispatch_workspace_bytes(const moe_dc_config* cfg)
 
 moe_status moe_dispatch(const moe_dc_config* cfg, const void* x, const int32_t* expert_ids,
                         const float* scales, const uint8_t* x_active_mask,
-                        void* expand_x, void* dynamic_scales, int32_t* expand_idx,
-                        int32_t* assist_info, int32_t* ep_recv_count,
-                        int64_t* expert_token_nums, int64_t* recv_offsets, void* workspace,
-                        size_t workspace_bytes, void* stream)
+                        const float* expert_scales, void* expand_x, void* dynamic_scales,
+                        int32_t* expand_idx, int32_t* assist_info, int32_t* ep_recv_count,
+                        int64_t* expert_token_nums, int64_t* recv_offsets,
+                        float* expand_scales, void* workspace, size_t workspace_bytes,
+                        void* stream)
 {
     moe_dc::Shape sh;
     moe_status st = check(cfg, &sh);
@@ -191,10 +193,14 @@ moe_status moe_dispatch(const moe_dc_config* cfg, const void* x, const int32_t* 
                     "scales must be given iff scales_kind is not MOE_SCALES_NONE");
     if ((sh.mask_kind != 0) != (x_active_mask != nullptr))
         return fail(MOE_ERR_INVALID_ARG, "x_active_mask must be given iff mask_kind != 0");
+    if ((expert_scales != nullptr) != (expand_scales != nullptr))
+        return fail(MOE_ERR_INVALID_ARG, "expert_scales and expand_scales go together");
     const size_t need = moe_dc::workspace_bytes(sh);
     if (!workspace || workspace_bytes < need)
         return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     workspace_bytes);
+    if (!aligned4(workspace))
+        return fail(MOE_ERR_INVALID_ARG, "workspace must be 4-byte aligned");
     hipStream_t s = static_cast<hipStream_t>(stream);
     int32_t* seg = static_cast<int32_t*>(workspace);
     const bool row_scales =
@@ -210,7 +216,8 @@ moe_status moe_dispatch(const moe_dc_config* cfg, const void* x, const int32_t* 
                        "scan kernel launch");
     if (st != MOE_OK) return st;
     st = device_status(moe_dc::launch_scatter(sh, x, expert_ids, expand_idx, seg, scales,
-                                              expand_x, dynamic_scales, assist_info, vec, s),
+                                              expert_scales, expand_x, dynamic_scales,
+                                              assist_info, expand_scales, vec, s),
                        "scatter kernel launch");
     if (st != MOE_OK) return st;
     return ok();
@@ -239,6 +246,47 @@ moe_status moe_combine(const moe_dc_config* cfg, const void* expert_out,
                                               x_active_mask, ori_x, y, vec,
                                               static_cast<hipStream_t>(stream)),
                        "combine kernel launch");
+    if (st != MOE_OK) return st;
+    return ok();
+}
+
+size_t moe_dc_combine_scatter_workspace_bytes(const moe_dc_config* cfg)
+{
+    moe_dc::Shape sh;
+    if (check(cfg, &sh) != MOE_OK) return 0;
+    return moe_dc::combine_scatter_workspace_bytes(sh);
+}
+
+moe_status moe_combine_scatter(const moe_dc_config* cfg, const void* expert_out,
+                               const int32_t* assist_info, const int64_t* recv_offsets,
+                               const int32_t* expert_ids, const float* expert_scales,
+                               const uint8_t* x_active_mask, const void* ori_x,
+                               const void* shared_x, void* y, void* workspace,
+                               size_t workspace_bytes, void* stream)
+{
+    moe_dc::Shape sh;
+    moe_status st = check(cfg, &sh);
+    if (st != MOE_OK) return st;
+    if (!expert_out || !assist_info || !recv_offsets || !expert_ids || !expert_scales || !y)
+        return fail(MOE_ERR_INVALID_ARG, "a required tensor pointer is NULL");
+    if ((sh.mask_kind != 0) != (x_active_mask != nullptr))
+        return fail(MOE_ERR_INVALID_ARG, "x_active_mask must be given iff mask_kind != 0");
+    if (cfg->copy_expert_num > 0 && !ori_x)
+        return fail(MOE_ERR_INVALID_ARG, "ori_x is required when copy experts exist");
+    const size_t need = moe_dc::combine_scatter_workspace_bytes(sh);
+    if (!workspace || workspace_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace_bytes);
+    if (!aligned4(workspace))
+        return fail(MOE_ERR_INVALID_ARG, "workspace must be 4-byte aligned");
+    const bool vec = sh.H % 8 == 0 && aligned16(expert_out) && aligned16(y) &&
+                     (!ori_x || aligned16(ori_x)) && (!shared_x || aligned16(shared_x));
+    st = device_status(moe_dc::launch_combine_scatter(sh, expert_out, assist_info,
+                                                      recv_offsets, expert_ids, expert_scales,
+                                                      x_active_mask, ori_x, shared_x, y,
+                                                      static_cast<int32_t*>(workspace), vec,
+                                                      static_cast<hipStream_t>(stream)),
+                       "scatter-back combine launch");
     if (st != MOE_OK) return st;
     return ok();
 }

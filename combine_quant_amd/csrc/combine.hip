@@ -35,12 +35,15 @@ constexpr int kNone = -1;   // inactive pick, zero expert, or unresolvable
 constexpr int kCopy = -2;   // copy expert: read ori_x
 
 // Source of pick k of token tok: its expert_out row (>= 0), kCopy for a copy expert, or
-// kNone.  The row follows the design doc's addressing (§3.4.2: the owner rank's window + the
-// expert's offset inside it + expand_idx), written with the dispatch outputs:
-// recv_offsets[r] + the running total of ep_recv_count just before (local expert j,
-// source s) + expand_idx.  Rows outside [0, cap) are treated as unresolvable.
+// kNone.  With INV = false the row follows the design doc's addressing (§3.4.2: the owner
+// rank's window + the expert's offset inside it + expand_idx), written with the dispatch
+// outputs: recv_offsets[r] + the running total of ep_recv_count just before (local expert
+// j, source s) + expand_idx.  With INV = true, `pick_rows` is the map written by the
+// scatter-back step (slot tok * K + k -> the row that was sent back to it).  Rows outside
+// [0, cap) are treated as unresolvable.
+template <bool INV>
 __device__ __forceinline__ int pick_source(
-    const int32_t* __restrict__ ids, const int32_t* __restrict__ expand_idx,
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ pick_rows,
     const int32_t* __restrict__ ep_recv_count, const int64_t* __restrict__ recv_offsets,
     const uint8_t* __restrict__ mask, int mask_kind, int W, int E, int L, int K, int zero_end,
     int id_end, long long cap, long long tok, int s, int k)
@@ -49,8 +52,12 @@ __device__ __forceinline__ int pick_source(
     const int32_t e = ids[p];
     const bool on = mask_kind == 0 || (mask_kind == 1 ? mask[tok] != 0 : mask[p] != 0);
     if (!on || e < 0) return kNone;
+    if (e < E && INV) {
+        const int32_t row = pick_rows[p];
+        return (row >= 0 && row < cap) ? (int)row : kNone;
+    }
     if (e < E) {
-        const int32_t ord = expand_idx[p];
+        const int32_t ord = pick_rows[p];
         if (ord < 0) return kNone;
         const int r = e / L;
         const int j = e - r * L;
@@ -117,14 +124,17 @@ constexpr int slots_per_task(int kmax) { return kmax > 8 ? 1 : 2; }
 // Q = 0: bf16 expert rows.  Q = 1: int8 codes [cap][H] and fp32 block scales [cap][H/8]
 // (qscales), one block per lane vector; a routed pick's buffer entry then holds the two code
 // words and the scale's bits.
-template <int KMAX, int SLOTS, int Q>
+// INV selects the scatter-back addressing (expand_idx then holds the slot -> row map) and
+// SHARED adds the shared expert's bf16 output after the K picks.
+template <int KMAX, int SLOTS, int Q, bool INV, bool SHARED>
 __global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_wave_kernel(
     const void* __restrict__ expert_out, const float* __restrict__ qscales,
     const int32_t* __restrict__ ids, const int32_t* __restrict__ expand_idx,
     const float* __restrict__ weights, const int32_t* __restrict__ ep_recv_count,
     const int64_t* __restrict__ recv_offsets, const uint8_t* __restrict__ mask, int mask_kind,
-    const uint16_t* __restrict__ ori_x, uint16_t* __restrict__ y, int W, int E, int L, int BS,
-    int H, int K, int zero_end, int id_end, long long cap, long long T, int tasks_per_token)
+    const uint16_t* __restrict__ ori_x, const uint16_t* __restrict__ shared_x,
+    uint16_t* __restrict__ y, int W, int E, int L, int BS, int H, int K, int zero_end,
+    int id_end, long long cap, long long T, int tasks_per_token)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const long long task = (long long)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
@@ -137,8 +147,8 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_wave_kernel(
     int src = kNone;
     float wk = 0.0f;
     if (lane < K) {
-        src = pick_source(ids, expand_idx, ep_recv_count, recv_offsets, mask, mask_kind, W, E,
-                          L, K, zero_end, id_end, cap, tok, s, lane);
+        src = pick_source<INV>(ids, expand_idx, ep_recv_count, recv_offsets, mask, mask_kind,
+                               W, E, L, K, zero_end, id_end, cap, tok, s, lane);
         wk = weights[tok * K + lane];
     }
     int srcs[KMAX];
@@ -154,10 +164,12 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_wave_kernel(
     const uint4* self = ori_x ? reinterpret_cast<const uint4*>(ori_x) + tok * NV : nullptr;
     uint4* yr = reinterpret_cast<uint4*>(y) + tok * NV;
     uint4 buf[SLOTS][KMAX];
+    uint4 shv[SLOTS];
 #pragma unroll
     for (int n = 0; n < SLOTS; ++n) {
         const int v = lane + (slot0 + n) * kWave;
         if (v < NV) {
+            if (SHARED) shv[n] = load_stream(reinterpret_cast<const uint4*>(shared_x) + tok * NV + v);
 #pragma unroll
             for (int k = 0; k < KMAX; ++k) {
                 if (srcs[k] >= 0) {
@@ -190,6 +202,7 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_wave_kernel(
                 else
                     accumulate8(buf[n][k], ws[k], acc);
             }
+            if (SHARED) accumulate8(shv[n], 1.0f, acc);    // 1 * bf16 value is exact
             store_stream(yr + v,
                          make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
                                     pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])));
@@ -222,8 +235,8 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_int8_wide_kern
     int src = kNone;
     float wk = 0.0f;
     if (lane < K) {
-        src = pick_source(ids, expand_idx, ep_recv_count, recv_offsets, mask, mask_kind, W, E,
-                          L, K, zero_end, id_end, cap, tok, s, lane);
+        src = pick_source<false>(ids, expand_idx, ep_recv_count, recv_offsets, mask, mask_kind,
+                               W, E, L, K, zero_end, id_end, cap, tok, s, lane);
         wk = weights[tok * K + lane];
     }
     int srcs[KMAX];
@@ -292,11 +305,11 @@ hipError_t launch_int8_wide_k(const Shape& sh, const int8_t* codes, const float*
     return hipGetLastError();
 }
 
-template <int KMAX, int Q>
+template <int KMAX, int Q, bool INV, bool SHARED>
 hipError_t launch_wave_k(const Shape& sh, const void* expert_out, const float* qscales,
                          const int32_t* ids, const int32_t* expand_idx, const float* w,
                          const int32_t* erc, const int64_t* roff, const uint8_t* mask,
-                         const void* ori_x, void* y, hipStream_t stream)
+                         const void* ori_x, const void* shared_x, void* y, hipStream_t stream)
 {
     const long long T = (long long)sh.W * sh.BS;
     const int slots = ((sh.H >> 3) + kWave - 1) / kWave;
@@ -304,26 +317,27 @@ hipError_t launch_wave_k(const Shape& sh, const void* expert_out, const float* q
     const int tasks_per_token = (slots + kSlots - 1) / kSlots;
     const long long tasks = T * tasks_per_token;
     const unsigned blocks = (unsigned)((tasks + kWavesPerBlock - 1) / kWavesPerBlock);
-    hipLaunchKernelGGL((combine_wave_kernel<KMAX, kSlots, Q>), dim3(blocks),
+    hipLaunchKernelGGL((combine_wave_kernel<KMAX, kSlots, Q, INV, SHARED>), dim3(blocks),
                        dim3(kWave * kWavesPerBlock), 0, stream, expert_out, qscales, ids,
                        expand_idx, w, erc, roff, mask, sh.mask_kind,
-                       static_cast<const uint16_t*>(ori_x), static_cast<uint16_t*>(y), sh.W,
-                       sh.E, sh.L, sh.BS, sh.H, sh.K, sh.zero_end, sh.id_end,
+                       static_cast<const uint16_t*>(ori_x),
+                       static_cast<const uint16_t*>(shared_x), static_cast<uint16_t*>(y),
+                       sh.W, sh.E, sh.L, sh.BS, sh.H, sh.K, sh.zero_end, sh.id_end,
                        (long long)sh.cap, T, tasks_per_token);
     return hipGetLastError();
 }
 
-template <int Q>
+template <int Q, bool INV, bool SHARED>
 hipError_t launch_wave(const Shape& sh, const void* eo, const float* qs, const int32_t* ids,
                        const int32_t* ei, const float* w, const int32_t* erc,
-                       const int64_t* roff, const uint8_t* mask, const void* ori_x, void* y,
-                       hipStream_t stream)
+                       const int64_t* roff, const uint8_t* mask, const void* ori_x,
+                       const void* shared_x, void* y, hipStream_t stream)
 {
-#define MOE_DC_ARGS sh, eo, qs, ids, ei, w, erc, roff, mask, ori_x, y, stream
-    if (sh.K <= 2) return launch_wave_k<2, Q>(MOE_DC_ARGS);
-    if (sh.K <= 4) return launch_wave_k<4, Q>(MOE_DC_ARGS);
-    if (sh.K <= 8) return launch_wave_k<8, Q>(MOE_DC_ARGS);
-    return launch_wave_k<16, Q>(MOE_DC_ARGS);
+#define MOE_DC_ARGS sh, eo, qs, ids, ei, w, erc, roff, mask, ori_x, shared_x, y, stream
+    if (sh.K <= 2) return launch_wave_k<2, Q, INV, SHARED>(MOE_DC_ARGS);
+    if (sh.K <= 4) return launch_wave_k<4, Q, INV, SHARED>(MOE_DC_ARGS);
+    if (sh.K <= 8) return launch_wave_k<8, Q, INV, SHARED>(MOE_DC_ARGS);
+    return launch_wave_k<16, Q, INV, SHARED>(MOE_DC_ARGS);
 #undef MOE_DC_ARGS
 }
 
@@ -331,14 +345,15 @@ constexpr int kElemThreads = 1024;
 constexpr int kElemPerLane = 8;      // H <= 8192 = 1024 lanes x 8
 
 // Element-wise combine; Q as for combine_wave_kernel (codes [cap][H], scales [cap][Ceil(H,8)]).
-template <int KMAX, int Q>
+template <int KMAX, int Q, bool INV>
 __global__ __launch_bounds__(kElemThreads) void combine_elem_kernel(
     const void* __restrict__ expert_out, const float* __restrict__ qscales,
     const int32_t* __restrict__ ids, const int32_t* __restrict__ expand_idx,
     const float* __restrict__ weights, const int32_t* __restrict__ ep_recv_count,
     const int64_t* __restrict__ recv_offsets, const uint8_t* __restrict__ mask, int mask_kind,
-    const uint16_t* __restrict__ ori_x, uint16_t* __restrict__ y, int W, int E, int L, int BS,
-    int H, int K, int zero_end, int id_end, long long cap)
+    const uint16_t* __restrict__ ori_x, const uint16_t* __restrict__ shared_x,
+    uint16_t* __restrict__ y, int W, int E, int L, int BS, int H, int K, int zero_end,
+    int id_end, long long cap)
 {
     __shared__ int src_of[KMAX];
     __shared__ float w_of[KMAX];
@@ -347,8 +362,8 @@ __global__ __launch_bounds__(kElemThreads) void combine_elem_kernel(
     const int t = threadIdx.x;
     const int nb = (H + 7) / 8;
     if (t < K) {
-        src_of[t] = pick_source(ids, expand_idx, ep_recv_count, recv_offsets, mask, mask_kind,
-                                W, E, L, K, zero_end, id_end, cap, tok, s, t);
+        src_of[t] = pick_source<INV>(ids, expand_idx, ep_recv_count, recv_offsets, mask,
+                                     mask_kind, W, E, L, K, zero_end, id_end, cap, tok, s, t);
         w_of[t] = weights[tok * K + t];
     }
     __syncthreads();
@@ -373,36 +388,61 @@ __global__ __launch_bounds__(kElemThreads) void combine_elem_kernel(
             }
             acc = acc + w_of[k] * v;
         }
+        if (shared_x) acc = acc + bf16_lo(shared_x[tok * H + h]);
         yr[h] = (uint16_t)f32_to_bf16_rne(acc);
     }
 }
 
-template <int KMAX, int Q>
+template <int KMAX, int Q, bool INV>
 hipError_t launch_elem_k(const Shape& sh, const void* expert_out, const float* qscales,
                          const int32_t* ids, const int32_t* expand_idx, const float* w,
                          const int32_t* erc, const int64_t* roff, const uint8_t* mask,
-                         const void* ori_x, void* y, hipStream_t stream)
+                         const void* ori_x, const void* shared_x, void* y, hipStream_t stream)
 {
     const int want = (sh.H + kWave - 1) / kWave * kWave;
     const int threads = want < kElemThreads ? want : kElemThreads;
     const long long T = (long long)sh.W * sh.BS;
-    hipLaunchKernelGGL((combine_elem_kernel<KMAX, Q>), dim3((unsigned)T), dim3(threads), 0,
-                       stream, expert_out, qscales, ids, expand_idx, w, erc, roff, mask,
+    hipLaunchKernelGGL((combine_elem_kernel<KMAX, Q, INV>), dim3((unsigned)T), dim3(threads),
+                       0, stream, expert_out, qscales, ids, expand_idx, w, erc, roff, mask,
                        sh.mask_kind, static_cast<const uint16_t*>(ori_x),
-                       static_cast<uint16_t*>(y), sh.W, sh.E, sh.L, sh.BS, sh.H, sh.K,
-                       sh.zero_end, sh.id_end, (long long)sh.cap);
+                       static_cast<const uint16_t*>(shared_x), static_cast<uint16_t*>(y),
+                       sh.W, sh.E, sh.L, sh.BS, sh.H, sh.K, sh.zero_end, sh.id_end,
+                       (long long)sh.cap);
     return hipGetLastError();
 }
 
-template <int Q>
+template <int Q, bool INV>
 hipError_t launch_elem(const Shape& sh, const void* eo, const float* qs, const int32_t* ids,
                        const int32_t* ei, const float* w, const int32_t* erc,
-                       const int64_t* roff, const uint8_t* mask, const void* ori_x, void* y,
-                       hipStream_t stream)
+                       const int64_t* roff, const uint8_t* mask, const void* ori_x,
+                       const void* shared_x, void* y, hipStream_t stream)
 {
-    if (sh.K <= 4)
-        return launch_elem_k<4, Q>(sh, eo, qs, ids, ei, w, erc, roff, mask, ori_x, y, stream);
-    return launch_elem_k<16, Q>(sh, eo, qs, ids, ei, w, erc, roff, mask, ori_x, y, stream);
+#define MOE_DC_ARGS sh, eo, qs, ids, ei, w, erc, roff, mask, ori_x, shared_x, y, stream
+    if (sh.K <= 4) return launch_elem_k<4, Q, INV>(MOE_DC_ARGS);
+    return launch_elem_k<16, Q, INV>(MOE_DC_ARGS);
+#undef MOE_DC_ARGS
+}
+
+// ---------------------------------------------------------------------------------------
+// scatter-back: each expert-side row r < recv_offsets[W] is sent back to slot i * K + k of
+// its source rank s, (s, i, k) = assist_info[r] (the sample article's combine: epOffset =
+// tokenId * K + topkId).  Every rank lives in this HBM, so the slot records the row's index
+// instead of a copy of its bytes; the gather then reads the row through it.
+// ---------------------------------------------------------------------------------------
+
+constexpr int kIndexThreads = 256;
+
+__global__ __launch_bounds__(kIndexThreads) void scatter_back_index_kernel(
+    const int32_t* __restrict__ assist, const int64_t* __restrict__ recv_offsets,
+    int32_t* __restrict__ slot_rows, int W, int BS, int K, long long cap)
+{
+    const long long r = (long long)blockIdx.x * kIndexThreads + threadIdx.x;
+    if (r >= cap || r >= recv_offsets[W]) return;
+    const int32_t s = assist[r * 3 + 0];
+    const int32_t i = assist[r * 3 + 1];
+    const int32_t k = assist[r * 3 + 2];
+    if (s < 0 || s >= W || i < 0 || i >= BS || k < 0 || k >= K) return;   // not a triple
+    slot_rows[((long long)s * BS + i) * K + k] = (int32_t)r;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -500,10 +540,12 @@ hipError_t launch_combine(const Shape& sh, const void* expert_out, const int32_t
                           hipStream_t stream)
 {
     if (vectorized)
-        return launch_wave<0>(sh, expert_out, nullptr, expert_ids, expand_idx, expert_scales,
-                              ep_recv_count, recv_offsets, mask, ori_x, y, stream);
-    return launch_elem<0>(sh, expert_out, nullptr, expert_ids, expand_idx, expert_scales,
-                          ep_recv_count, recv_offsets, mask, ori_x, y, stream);
+        return launch_wave<0, false, false>(sh, expert_out, nullptr, expert_ids, expand_idx,
+                                            expert_scales, ep_recv_count, recv_offsets, mask,
+                                            ori_x, nullptr, y, stream);
+    return launch_elem<0, false>(sh, expert_out, nullptr, expert_ids, expand_idx,
+                                 expert_scales, ep_recv_count, recv_offsets, mask, ori_x,
+                                 nullptr, y, stream);
 }
 
 hipError_t launch_combine_int8(const Shape& sh, const int8_t* codes, const float* qscales,
@@ -525,10 +567,32 @@ hipError_t launch_combine_int8(const Shape& sh, const int8_t* codes, const float
 #undef MOE_DC_ARGS
     }
     if (vectorized)
-        return launch_wave<1>(sh, codes, qscales, expert_ids, expand_idx, expert_scales,
-                              ep_recv_count, recv_offsets, mask, ori_x, y, stream);
-    return launch_elem<1>(sh, codes, qscales, expert_ids, expand_idx, expert_scales,
-                          ep_recv_count, recv_offsets, mask, ori_x, y, stream);
+        return launch_wave<1, false, false>(sh, codes, qscales, expert_ids, expand_idx,
+                                            expert_scales, ep_recv_count, recv_offsets, mask,
+                                            ori_x, nullptr, y, stream);
+    return launch_elem<1, false>(sh, codes, qscales, expert_ids, expand_idx, expert_scales,
+                                 ep_recv_count, recv_offsets, mask, ori_x, nullptr, y, stream);
+}
+
+hipError_t launch_combine_scatter(const Shape& sh, const void* expert_out,
+                                  const int32_t* assist_info, const int64_t* recv_offsets,
+                                  const int32_t* expert_ids, const float* expert_scales,
+                                  const uint8_t* mask, const void* ori_x, const void* shared_x,
+                                  void* y, int32_t* slot_rows, bool vectorized,
+                                  hipStream_t stream)
+{
+    const unsigned blocks = (unsigned)((sh.cap + kIndexThreads - 1) / kIndexThreads);
+    hipLaunchKernelGGL(scatter_back_index_kernel, dim3(blocks), dim3(kIndexThreads), 0, stream,
+                       assist_info, recv_offsets, slot_rows, sh.W, sh.BS, sh.K,
+                       (long long)sh.cap);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+#define MOE_DC_ARGS sh, expert_out, nullptr, expert_ids, slot_rows, expert_scales, nullptr, \
+                    recv_offsets, mask, ori_x, shared_x, y, stream
+    if (!vectorized) return launch_elem<0, true>(MOE_DC_ARGS);
+    if (shared_x) return launch_wave<0, true, true>(MOE_DC_ARGS);
+    return launch_wave<0, true, false>(MOE_DC_ARGS);
+#undef MOE_DC_ARGS
 }
 
 hipError_t launch_combine_quantize(const Shape& sh, const void* expert_out,

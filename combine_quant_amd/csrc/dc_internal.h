@@ -48,10 +48,12 @@ hipError_t launch_scan(const Shape& s, int32_t* seg, int32_t* ep_recv_count,
                        int64_t* expert_token_nums, int64_t* recv_offsets, hipStream_t stream);
 
 // Quantize and scatter every routed pick to its packed row, with scales and source triple.
+// expand_scales (nullable) receives each row's pick weight from expert_scales.
 hipError_t launch_scatter(const Shape& s, const void* x, const int32_t* expert_ids,
                           const int32_t* expand_idx, const int32_t* seg, const float* scales,
-                          void* expand_x, void* dynamic_scales, int32_t* assist_info,
-                          bool vectorized, hipStream_t stream);
+                          const float* expert_scales, void* expand_x, void* dynamic_scales,
+                          int32_t* assist_info, float* expand_scales, bool vectorized,
+                          hipStream_t stream);
 
 // Weighted top-K gather.
 hipError_t launch_combine(const Shape& s, const void* expert_out, const int32_t* expert_ids,
@@ -67,6 +69,22 @@ hipError_t launch_combine_int8(const Shape& s, const int8_t* codes, const float*
                                const float* expert_scales, const int32_t* ep_recv_count,
                                const int64_t* recv_offsets, const uint8_t* mask,
                                const void* ori_x, void* y, bool vectorized, hipStream_t stream);
+
+// Scatter-back combine: rows sent back to slots by their assist_info triples, then the
+// per-token K-sum (+ the shared expert's output when shared_x is not null).  slot_rows is
+// scratch of W*BS*K int32.
+hipError_t launch_combine_scatter(const Shape& s, const void* expert_out,
+                                  const int32_t* assist_info, const int64_t* recv_offsets,
+                                  const int32_t* expert_ids, const float* expert_scales,
+                                  const uint8_t* mask, const void* ori_x, const void* shared_x,
+                                  void* y, int32_t* slot_rows, bool vectorized,
+                                  hipStream_t stream);
+
+inline size_t combine_scatter_workspace_bytes(const Shape& s)
+{
+    size_t b = (size_t)s.W * (size_t)s.BS * (size_t)s.K * sizeof(int32_t);
+    return (b + 255) & ~(size_t)255;
+}
 
 // Expert-side int8 block quantization of the rows [0, recv_offsets[W]).
 hipError_t launch_combine_quantize(const Shape& s, const void* expert_out,

@@ -175,9 +175,10 @@ template <int MODE, int CT, int SK>
 __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
     const int32_t* __restrict__ expand_idx, const int32_t* __restrict__ seg,
-    const float* __restrict__ scales, void* __restrict__ expand_x,
-    void* __restrict__ dyn_scales, int32_t* __restrict__ assist, int W, int E, int BS,
-    int H, int K, int ns, long long cap, int e8m0)
+    const float* __restrict__ scales, const float* __restrict__ weights,
+    void* __restrict__ expand_x, void* __restrict__ dyn_scales, int32_t* __restrict__ assist,
+    float* __restrict__ expand_scales, int W, int E, int BS, int H, int K, int ns,
+    long long cap, int e8m0)
 {
     __shared__ int32_t rows_lds[kMaxK];
     __shared__ int32_t exps_lds[kMaxK];
@@ -227,6 +228,7 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
             assist[(long long)row * 3 + 0] = s;
             assist[(long long)row * 3 + 1] = i;
             assist[(long long)row * 3 + 2] = threadIdx.x;
+            if (expand_scales) expand_scales[row] = weights[p];
         }
     }
 
@@ -435,32 +437,38 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
     }
 }
 
+// Arguments of every scatter launch.
+struct ScatterArgs {
+    const void* x;
+    const int32_t* ids;
+    const int32_t* expand_idx;
+    const int32_t* seg;
+    const float* scales;
+    const float* weights;
+    void* expand_x;
+    void* dyn_scales;
+    int32_t* assist;
+    float* expand_scales;
+};
+
 template <int MODE, int CT, int SK>
-hipError_t launch_tile_variant(const Shape& sh, const void* x, const int32_t* ids,
-                               const int32_t* expand_idx, const int32_t* seg,
-                               const float* scales, void* expand_x, void* dyn_scales,
-                               int32_t* assist, hipStream_t stream)
+hipError_t launch_tile_variant(const Shape& sh, const ScatterArgs& a, hipStream_t stream)
 {
     const long long T = (long long)sh.W * sh.BS;
     const int slots = ((sh.H >> 3) + kWave - 1) / kWave;
     const int waves = (slots + kTileSlots - 1) / kTileSlots;        // <= kMaxTileWaves
     hipLaunchKernelGGL((scatter_tile_kernel<MODE, CT, SK>), dim3((unsigned)T),
-                       dim3(kWave * waves), 0, stream, static_cast<const uint16_t*>(x), ids,
-                       expand_idx, seg, scales, expand_x, dyn_scales, assist, sh.W, sh.E,
-                       sh.BS, sh.H, sh.K, sh.scales_per_row, (long long)sh.cap,
-                       sh.scale_e8m0);
+                       dim3(kWave * waves), 0, stream, static_cast<const uint16_t*>(a.x), a.ids,
+                       a.expand_idx, a.seg, a.scales, a.weights, a.expand_x, a.dyn_scales,
+                       a.assist, a.expand_scales, sh.W, sh.E, sh.BS, sh.H, sh.K,
+                       sh.scales_per_row, (long long)sh.cap, sh.scale_e8m0);
     return hipGetLastError();
 }
 
 template <int MODE, int CT>
-hipError_t launch_tile_scales(const Shape& sh, const void* x, const int32_t* ids,
-                              const int32_t* expand_idx, const int32_t* seg,
-                              const float* scales, void* expand_x, void* dyn_scales,
-                              int32_t* assist, hipStream_t stream)
+hipError_t launch_tile_scales(const Shape& sh, const ScatterArgs& a, hipStream_t stream)
 {
-#define MOE_DC_TILE(SK)                                                                    \
-    launch_tile_variant<MODE, CT, SK>(sh, x, ids, expand_idx, seg, scales, expand_x,      \
-                                      dyn_scales, assist, stream)
+#define MOE_DC_TILE(SK) launch_tile_variant<MODE, CT, SK>(sh, a, stream)
     switch (sh.scales_kind) {
     case kScalesNone:
         if constexpr (MODE == 1) return hipErrorInvalidValue;    // mode 1 needs scales
@@ -477,11 +485,9 @@ hipError_t launch_tile_scales(const Shape& sh, const void* x, const int32_t* ids
 #undef MOE_DC_TILE
 }
 
-hipError_t launch_tile(const Shape& sh, const void* x, const int32_t* ids,
-                       const int32_t* expand_idx, const int32_t* seg, const float* scales,
-                       void* expand_x, void* dyn_scales, int32_t* assist, hipStream_t stream)
+hipError_t launch_tile(const Shape& sh, const ScatterArgs& a, hipStream_t stream)
 {
-#define MOE_DC_ARGS sh, x, ids, expand_idx, seg, scales, expand_x, dyn_scales, assist, stream
+#define MOE_DC_ARGS sh, a, stream
     const int ct = sh.code_type;
     switch (sh.quant_mode) {
     case 0:
@@ -538,9 +544,10 @@ __device__ __forceinline__ float type_max_rt(int ct)
 __global__ __launch_bounds__(kElemThreads) void scatter_elem_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
     const int32_t* __restrict__ expand_idx, const int32_t* __restrict__ seg,
-    const float* __restrict__ scales, void* __restrict__ expand_x,
-    void* __restrict__ dyn_scales, int32_t* __restrict__ assist, int W, int E, int BS,
-    int H, int K, int ns, long long cap, int mode, int ct, int sk, int e8m0)
+    const float* __restrict__ scales, const float* __restrict__ weights,
+    void* __restrict__ expand_x, void* __restrict__ dyn_scales, int32_t* __restrict__ assist,
+    float* __restrict__ expand_scales, int W, int E, int BS, int H, int K, int ns,
+    long long cap, int mode, int ct, int sk, int e8m0)
 {
     __shared__ long long row_of[kMaxK];
     __shared__ int32_t exp_of[kMaxK];
@@ -571,6 +578,7 @@ __global__ __launch_bounds__(kElemThreads) void scatter_elem_kernel(
             assist[row * 3 + 0] = s;
             assist[row * 3 + 1] = i;
             assist[row * 3 + 2] = t;
+            if (expand_scales) expand_scales[row] = weights[tok * K + t];
         }
     }
     __syncthreads();
@@ -701,19 +709,17 @@ __global__ __launch_bounds__(kElemThreads) void scatter_elem_kernel(
     }
 }
 
-hipError_t launch_elem(const Shape& sh, const void* x, const int32_t* ids,
-                       const int32_t* expand_idx, const int32_t* seg, const float* scales,
-                       void* expand_x, void* dyn_scales, int32_t* assist, hipStream_t stream)
+hipError_t launch_elem(const Shape& sh, const ScatterArgs& a, hipStream_t stream)
 {
     const long long T = (long long)sh.W * sh.BS;
     const int want = (sh.H + kWave - 1) / kWave * kWave;
     const int threads = want < kElemThreads ? want : kElemThreads;
     if (sh.quant_mode == 3 && threads != kElemThreads) return hipErrorInvalidValue;
     hipLaunchKernelGGL(scatter_elem_kernel, dim3((unsigned)T), dim3(threads), 0, stream,
-                       static_cast<const uint16_t*>(x), ids, expand_idx, seg, scales,
-                       expand_x, dyn_scales, assist, sh.W, sh.E, sh.BS, sh.H, sh.K,
-                       sh.scales_per_row, (long long)sh.cap, sh.quant_mode, sh.code_type,
-                       sh.scales_kind, sh.scale_e8m0);
+                       static_cast<const uint16_t*>(a.x), a.ids, a.expand_idx, a.seg, a.scales,
+                       a.weights, a.expand_x, a.dyn_scales, a.assist, a.expand_scales, sh.W,
+                       sh.E, sh.BS, sh.H, sh.K, sh.scales_per_row, (long long)sh.cap,
+                       sh.quant_mode, sh.code_type, sh.scales_kind, sh.scale_e8m0);
     return hipGetLastError();
 }
 
@@ -721,14 +727,13 @@ hipError_t launch_elem(const Shape& sh, const void* x, const int32_t* ids,
 
 hipError_t launch_scatter(const Shape& sh, const void* x, const int32_t* expert_ids,
                           const int32_t* expand_idx, const int32_t* seg, const float* scales,
-                          void* expand_x, void* dynamic_scales, int32_t* assist_info,
-                          bool vectorized, hipStream_t stream)
+                          const float* expert_scales, void* expand_x, void* dynamic_scales,
+                          int32_t* assist_info, float* expand_scales, bool vectorized,
+                          hipStream_t stream)
 {
-    if (vectorized)
-        return launch_tile(sh, x, expert_ids, expand_idx, seg, scales, expand_x,
-                           dynamic_scales, assist_info, stream);
-    return launch_elem(sh, x, expert_ids, expand_idx, seg, scales, expand_x, dynamic_scales,
-                       assist_info, stream);
+    const ScatterArgs a{x,        expert_ids,     expand_idx,  seg,          scales,
+                        expert_scales, expand_x, dynamic_scales, assist_info, expand_scales};
+    return vectorized ? launch_tile(sh, a, stream) : launch_elem(sh, a, stream);
 }
 
 }  // namespace moe_dc

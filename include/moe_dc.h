@@ -148,6 +148,7 @@ size_t moe_dc_dispatch_workspace_bytes(const moe_dc_config* cfg);
  *                  scales_kind is MOE_SCALES_NONE
  *   x_active_mask  uint8 [W][BS] (mask_kind 1) or [W][BS][K] (mask_kind 2), or NULL when
  *                  mask_kind is 0; nonzero = active.  An inactive pick is not dispatched.
+ *   expert_scales  fp32 [W][BS][K] pick weights, or NULL; given iff expand_scales is
  * Outputs (row = a receiver row in the packed layout below; cap = expand_rows_capacity):
  *   expand_x       [cap][H] bf16 (mode 0), else one byte per element: int8 or fp8 codes
  *   dynamic_scales [cap][moe_dc_scales_per_row(cfg)] fp32 (or bytes with MOE_SCALE_E8M0):
@@ -161,6 +162,9 @@ size_t moe_dc_dispatch_workspace_bytes(const moe_dc_config* cfg);
  *                  the rows r receives, over (local expert j, source s) in that order
  *   expert_token_nums int64 [W][L]    type 1: rows per local expert; type 0: running sum
  *   recv_offsets   int64 [W+1]        first row of each receiver; [W] = total routed rows
+ *   expand_scales  fp32 [cap] or NULL: each row's pick weight ([OPS] 参数说明,
+ *                  expand_scales_out: the weight travels with its token)
+ *   workspace      moe_dc_dispatch_workspace_bytes(cfg) bytes, 4-byte aligned
  * Packed layout: receiver r owns rows [recv_offsets[r], recv_offsets[r+1]); inside, rows go
  * by local expert, then source rank, then expand_idx.  So the whole buffer is one stable sort
  * of the routed picks by (expert, s, i, k).  Rows at or past recv_offsets[W] are not written.
@@ -177,9 +181,11 @@ size_t moe_dc_dispatch_workspace_bytes(const moe_dc_config* cfg);
 moe_status moe_dispatch(const moe_dc_config* cfg,
                         const void* x, const int32_t* expert_ids,
                         const float* scales, const uint8_t* x_active_mask,
+                        const float* expert_scales,
                         void* expand_x, void* dynamic_scales, int32_t* expand_idx,
                         int32_t* assist_info, int32_t* ep_recv_count,
                         int64_t* expert_token_nums, int64_t* recv_offsets,
+                        float* expand_scales,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* moe_combine -- gather each token's K expert outputs and form their weighted sum.
@@ -208,6 +214,40 @@ moe_status moe_combine(const moe_dc_config* cfg,
                        const int32_t* ep_recv_count, const int64_t* recv_offsets,
                        const uint8_t* x_active_mask, const void* ori_x, void* y,
                        void* stream);
+
+/* Workspace bytes moe_combine_scatter needs: one int32 per pick slot (W*BS*K), rounded up
+ * to 256.  0 for an invalid config.  Scratch, as for dispatch. */
+size_t moe_dc_combine_scatter_workspace_bytes(const moe_dc_config* cfg);
+
+/* moe_combine_scatter -- the scatter-back combine: rows return to their sources by their
+ * source triples, then each token sums its K slots and adds the shared expert's output.
+ *
+ * Defined by: [SMP] Combine 功能介绍 计算步骤 and 源码实现: each expert-side row r is sent back
+ * using its triple (s, i, k) = assist_info[r] to offset epOffset = i * K + k of source rank s;
+ * the source then multiplies each of a token's K results by its expert scale, sums them in
+ * fp32 and adds the shared expert's result.  All ranks share this GPU's memory, so a slot
+ * stores the row's index (in the workspace) and the sum reads the row through it: the same
+ * values as copying the row, without moving its bytes twice.
+ *
+ * Inputs:
+ *   expert_out     bf16 [cap][H]      expert outputs, row-aligned with expand_x
+ *   assist_info    int32 [cap][3]     from moe_dispatch; rows [0, recv_offsets[W]) are sent
+ *   recv_offsets   int64 [W+1]        from moe_dispatch
+ *   expert_ids     int32 [W][BS][K]   which picks are routed, zero or copy experts
+ *   expert_scales  fp32 [W][BS][K]    the source's pick weights
+ *   x_active_mask  as for moe_dispatch
+ *   ori_x          bf16 [W][BS][H]    required iff copy_expert_num > 0
+ *   shared_x       bf16 [W][BS][H]    the shared expert's output per token, or NULL
+ * Output:
+ *   y              bf16 [W][BS][H] = bf16_rne( sum over active picks in k order of w * row,
+ *                  then + shared_x ), accumulated in fp32 from +0
+ * Errors: as for moe_combine; a workspace smaller than the query is MOE_ERR_WORKSPACE. */
+moe_status moe_combine_scatter(const moe_dc_config* cfg, const void* expert_out,
+                               const int32_t* assist_info, const int64_t* recv_offsets,
+                               const int32_t* expert_ids, const float* expert_scales,
+                               const uint8_t* x_active_mask, const void* ori_x,
+                               const void* shared_x, void* y, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /* moe_combine_quantize -- expert-side int8 block quantization of the expert outputs, the
  * compression the pages apply before the combine's return transfer.

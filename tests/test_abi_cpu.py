@@ -145,51 +145,67 @@ def test_scales_per_row_and_workspace():
     assert ws >= 256 * 16 * 4 and ws % 256 == 0
 
 
+def _dispatch_raw(lib, cfg, x=None, ids=None, scales=None, mask=None, weights=None,
+                  expand_x=None, dyn=None, eidx=None, assist=None, erc=None, etn=None,
+                  roff=None, expand_scales=None, ws=None, ws_bytes=0):
+    return lib.moe_dispatch(ctypes.byref(cfg), x, ids, scales, mask, weights, expand_x, dyn,
+                            eidx, assist, erc, etn, roff, expand_scales, ws,
+                            ctypes.c_size_t(ws_bytes), None)
+
+
 def test_dispatch_rejects_bad_arguments_before_any_device_work():
     """Argument errors return a status without touching the device (null pointers)."""
     lib = cq.load_library()
     c = _cfg()
-    rc = lib.moe_dispatch(ctypes.byref(c), *([None] * 11), None, ctypes.c_size_t(0), None)
-    assert rc == cq.MOE_ERR_INVALID_ARG
+    assert _dispatch_raw(lib, c) == cq.MOE_ERR_INVALID_ARG
     assert "NULL" in cq.moe_dc_last_error()
     rc = lib.moe_combine(ctypes.byref(c), *([None] * 9), None)
     assert rc == cq.MOE_ERR_INVALID_ARG
-    bad = _cfg(const_expert_num=1)
-    rc = lib.moe_dispatch(ctypes.byref(bad), *([None] * 11), None, ctypes.c_size_t(0), None)
-    assert rc == cq.MOE_ERR_UNSUPPORTED
+    rc = lib.moe_combine_scatter(ctypes.byref(c), *([None] * 10), ctypes.c_size_t(0), None)
+    assert rc == cq.MOE_ERR_INVALID_ARG
+    rc = lib.moe_combine_quantize(ctypes.byref(c), *([None] * 4), None)
+    assert rc == cq.MOE_ERR_INVALID_ARG
+    rc = lib.moe_combine_int8(ctypes.byref(c), *([None] * 10), None)
+    assert rc == cq.MOE_ERR_INVALID_ARG
+    assert _dispatch_raw(lib, _cfg(const_expert_num=1)) == cq.MOE_ERR_UNSUPPORTED
 
 
 def test_dispatch_workspace_and_mask_rules_on_host():
     """With non-null dummy pointers the remaining host rules still fire before any launch."""
     lib = cq.load_library()
     p = ctypes.c_void_p(0x1000)
+    full = dict(x=p, ids=p, expand_x=p, dyn=p, eidx=p, assist=p, erc=p, etn=p, roff=p, ws=p,
+                ws_bytes=1 << 20)
     c = _cfg()
-    args = [p, p, None] + [p] * 8          # no scales tensor: the config has none
     # a scales tensor the config does not announce, and a missing one it does
-    c4 = _cfg(quant_mode=4)
-    rc = lib.moe_dispatch(ctypes.byref(c4), p, p, p, None, p, p, p, p, p, p, p, p,
-                          ctypes.c_size_t(1 << 20), None)
+    rc = _dispatch_raw(lib, _cfg(quant_mode=4), scales=p, **full)
     assert rc == cq.MOE_ERR_INVALID_ARG and "scales" in cq.moe_dc_last_error()
-    c1 = _cfg(quant_mode=1, scales_kind=2)
-    rc = lib.moe_dispatch(ctypes.byref(c1), p, p, None, None, p, None, p, p, p, p, p, p,
-                          ctypes.c_size_t(1 << 20), None)
+    rc = _dispatch_raw(lib, _cfg(quant_mode=1, scales_kind=2), **dict(full, dyn=None))
     assert rc == cq.MOE_ERR_INVALID_ARG and "scales" in cq.moe_dc_last_error()
     # mode 3 needs dynamic_scales
-    c3 = _cfg(quant_mode=3)
-    rc = lib.moe_dispatch(ctypes.byref(c3), p, p, None, None, p, None, p, p, p, p, p, p,
-                          ctypes.c_size_t(1 << 20), None)
+    rc = _dispatch_raw(lib, _cfg(quant_mode=3), **dict(full, dyn=None))
     assert rc == cq.MOE_ERR_INVALID_ARG and "dynamic_scales" in cq.moe_dc_last_error()
     # mask pointer without a mask kind
-    rc = lib.moe_dispatch(ctypes.byref(c), *args, p, ctypes.c_size_t(1 << 20), None)
+    rc = _dispatch_raw(lib, c, mask=p, **full)
     assert rc == cq.MOE_ERR_INVALID_ARG and "mask" in cq.moe_dc_last_error()
-    # workspace too small
-    args_nomask = [p, p, None, None] + [p] * 7
-    rc = lib.moe_dispatch(ctypes.byref(c), *args_nomask, p, ctypes.c_size_t(8), None)
+    # expert_scales without expand_scales
+    rc = _dispatch_raw(lib, c, weights=p, **full)
+    assert rc == cq.MOE_ERR_INVALID_ARG and "expand_scales" in cq.moe_dc_last_error()
+    # workspace too small, and misaligned
+    rc = _dispatch_raw(lib, c, **dict(full, ws_bytes=8))
     assert rc == cq.MOE_ERR_WORKSPACE
+    rc = _dispatch_raw(lib, c, **dict(full, ws=ctypes.c_void_p(0x1002)))
+    assert rc == cq.MOE_ERR_INVALID_ARG and "aligned" in cq.moe_dc_last_error()
     # combine: copy experts without ori_x
     cc = _cfg(copy_expert_num=1)
     rc = lib.moe_combine(ctypes.byref(cc), p, p, p, p, p, p, None, None, p, None)
     assert rc == cq.MOE_ERR_INVALID_ARG and "ori_x" in cq.moe_dc_last_error()
+    # scatter-back combine: workspace rules
+    need = cq.moe_dc_combine_scatter_workspace_bytes(c)
+    assert need == 16 * 512 * 8 * 4
+    rc = lib.moe_combine_scatter(ctypes.byref(c), p, p, p, p, p, None, None, None, p, p,
+                                 ctypes.c_size_t(need - 1), None)
+    assert rc == cq.MOE_ERR_WORKSPACE
 
 
 def test_binding_refuses_cpu_tensors():
@@ -198,3 +214,5 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros((2, 16, 1024), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         cq.moe_dispatch(c, x, None, None, None, None, None, None, None, None, None, None, None)
+    with pytest.raises(ValueError):
+        cq.moe_combine_scatter(c, x, None, None, None, None, None, None, None, x, None)
