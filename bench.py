@@ -77,7 +77,13 @@ def algorithmic_bytes(wl, inp, routed_rows, copy_picks, active_tokens):
     dispatch = (2 * H * active_tokens + 4 * T * K + m + smooth + P * (b * H + S + 12)
                 + 4 * T * K + 4 * E * W + 8 * E + 8 * (W + 1))
     row = 2 * H if wl.combine_quant == 0 else H + 4 * ((H + 7) // 8)
-    combine = row * P + 12 * T * K + 4 * E * W + 8 * (W + 1) + m + 2 * H * copy_picks + 2 * H * T
+    if wl.combine_path == "scatter":
+        # each routed row and its source triple once, ids + weights, the shared output, y
+        combine = (2 * H + 12) * P + 8 * T * K + 8 * (W + 1) + m + 2 * H * copy_picks \
+            + 2 * H * T + 2 * H * T
+    else:
+        combine = row * P + 12 * T * K + 4 * E * W + 8 * (W + 1) + m + 2 * H * copy_picks \
+            + 2 * H * T
     return dispatch, combine
 
 
@@ -128,7 +134,7 @@ def committed_traffic():
 
 # -- CPU baseline: the oracle, as it stands ---------------------------------------------
 
-def cpu_baseline(wl, inp, expert_out_host, passes):
+def cpu_baseline(wl, inp, expert_out_host, passes, shared_host=None):
     import oracle
     cfg = oracle.make_cfg(wl.W, wl.E, wl.BS, wl.H, wl.K, quant_mode=wl.quant_mode,
                           zero_expert_num=wl.zero_expert_num,
@@ -144,7 +150,12 @@ def cpu_baseline(wl, inp, expert_out_host, passes):
             t0 = time.perf_counter()
             d = oracle.dispatch(cfg, inp["x"], inp["expert_ids"], scales=inp.get("scales"),
                                 mask=inp.get("mask"))
-            if wl.combine_quant:
+            if wl.combine_path == "scatter":
+                oracle.combine_scatter(cfg, expert_out_host, d["assist_info"],
+                                       d["recv_offsets"], inp["expert_ids"],
+                                       inp["expert_scales"], mask=inp.get("mask"),
+                                       ori_x=inp["x"], shared_x=shared_host)
+            elif wl.combine_quant:
                 codes, bsc = oracle.combine_quantize(cfg, expert_out_host, d["recv_offsets"])
                 oracle.combine_int8(cfg, codes, bsc, inp["expert_ids"], d["expand_idx"],
                                     inp["expert_scales"], d["ep_recv_count"],
@@ -211,6 +222,11 @@ def run_bench(args):
         eo = workloads.expert_out_torch(wl, wl.cap, seed=args.seed, device=dev)
         sets.append(dict(x=x, eo=eo, out=cq.alloc_dispatch_outputs(cfg, dev),
                          y=torch.empty((wl.W, wl.BS, wl.H), dtype=torch.bfloat16, device=dev)))
+        if wl.combine_path == "scatter":
+            sets[-1]["shared"] = workloads.expert_out_torch(wl, wl.T, seed=args.seed + 1,
+                                                            device=dev).view(wl.W, wl.BS, wl.H)
+            sets[-1]["sws"] = torch.empty((cq.moe_dc_combine_scatter_workspace_bytes(cfg),),
+                                          dtype=torch.uint8, device=dev)
         if wl.combine_quant:
             sets[-1]["codes"] = torch.empty((wl.cap, wl.H), dtype=torch.int8, device=dev)
             sets[-1]["bscales"] = torch.empty((wl.cap, (wl.H + 7) // 8), dtype=torch.float32,
@@ -226,7 +242,12 @@ def run_bench(args):
                         o["expand_idx"], o["assist_info"], o["ep_recv_count"],
                         o["expert_token_nums"], o["recv_offsets"], o["workspace"], stream)
         ev[1].record(stream)
-        if wl.combine_quant == 0:
+        if wl.combine_path == "scatter":
+            ev[2].record(stream)
+            cq.moe_combine_scatter(cfg, st["eo"], o["assist_info"], o["recv_offsets"], ids, w,
+                                   mask, st["x"], st["shared"], st["y"], st["sws"], stream)
+            ev[3].record(stream)
+        elif wl.combine_quant == 0:
             ev[2].record(stream)
             cq.moe_combine(cfg, st["eo"], ids, o["expand_idx"], w, o["ep_recv_count"],
                            o["recv_offsets"], mask, st["x"], st["y"], stream)
@@ -288,7 +309,9 @@ def run_bench(args):
         print(f"[bench] cpu baseline ({args.cpu_passes} oracle passes)", file=sys.stderr,
               flush=True)
         eo_host = sets[0]["eo"].view(torch.int16).cpu().numpy().view(np.uint16)
-        cpu = cpu_baseline(wl, inp, eo_host, args.cpu_passes)
+        shared_host = (sets[0]["shared"].view(torch.int16).cpu().numpy().view(np.uint16)
+                       if wl.combine_path == "scatter" else None)
+        cpu = cpu_baseline(wl, inp, eo_host, args.cpu_passes, shared_host)
 
     line = {
         "metric": METRIC,
@@ -307,6 +330,7 @@ def run_bench(args):
                    "H": wl.H, "K": wl.K, "quant_mode": wl.quant_mode,
                    "out_dtype": wl.out_dtype, "scales_kind": wl.scales_kind,
                    "scale_format": wl.scale_format, "combine_quant": wl.combine_quant,
+                   "combine_path": wl.combine_path,
                    "routing": wl.routing, "tokens_per_step": wl.T, "routed_rows": P,
                    "description": wl.description},
         "hbm_gbps": round(total_gbps, 1),

@@ -27,6 +27,8 @@ Recipe (numpy PCG64, one spawned sub-stream per tensor, base seed 0 by default):
                  tokens per rank fully inactive (seeded choice)
   expert_scales  fp32 softmax of N(0,1) logits over each token's K picks
   expert_out     bf16 of N(0,1) fp32 samples, one row per received row
+  shared_x       bf16 of N(0,1) fp32 samples [W][BS][H] (the shared expert's output, drawn
+                 on the device like expert_out)
 """
 from __future__ import annotations
 
@@ -57,6 +59,8 @@ class Workload:
     out_dtype: int = 0          # 0 the mode's default, 1 int8, 2 E4M3, 3 E5M2
     scale_format: int = 0       # 0 fp32 scales, 1 E8M0 bytes (MX modes)
     combine_quant: int = 0      # 0 bf16 expert rows, 1 int8 blocks of 8 on the return path
+    combine_path: str = "gather"  # gather (expand_idx addressing) | scatter (assist_info
+                                  # triples, with a shared expert's output added)
     routing: str = "uniform"    # uniform | zipf | randint
     zipf_s: float = 1.2
     outlier_prob: float = 0.0
@@ -138,8 +142,14 @@ C4_COMBINE_INT8 = C4.replace(
     description="C4 with the combine-side int8 block quantization: the expert outputs are "
                 "coded as int8 with one fp32 scale per 8 elements, then combined")
 
+C4_SCATTER_SHARED = C4.replace(
+    name="c4v_w16_scatter_back_shared", combine_path="scatter",
+    description="C4 with the scatter-back combine (rows return by their source triples) "
+                "and a shared expert's bf16 N(0,1) output added to every token")
+
 WORKLOADS = {w.name: w for w in (C1_MODE0, C1_MODE2, C2, C3, C4, C5, C3_E5M2_E8M0, C4_STATIC,
-                                 C4_TOKEN_E4M3, C4_GROUP, C2_GROUP_SMOOTH, C4_COMBINE_INT8)}
+                                 C4_TOKEN_E4M3, C4_GROUP, C2_GROUP_SMOOTH, C4_COMBINE_INT8,
+                                 C4_SCATTER_SHARED)}
 
 
 def _streams(seed: int):
