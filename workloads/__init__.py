@@ -137,6 +137,10 @@ C2_GROUP_SMOOTH = C2.replace(
     name="c2v_w8_group_e4m3_smooth", quant_mode=3,
     description="C2 with per-128-group dynamic E4M3 codes and per-expert smooth scales")
 
+C4_SMOOTH = C4.replace(
+    name="c4v_w16_smooth", scales_kind=3,
+    description="C4 with per-expert smooth scales U(0.5, 1.5) [256][7168] (per-pick int8 "
+                "quantization)")
 C4_COMBINE_INT8 = C4.replace(
     name="c4v_w16_combine_int8", combine_quant=1,
     description="C4 with the combine-side int8 block quantization: the expert outputs are "
@@ -149,7 +153,7 @@ C4_SCATTER_SHARED = C4.replace(
 
 WORKLOADS = {w.name: w for w in (C1_MODE0, C1_MODE2, C2, C3, C4, C5, C3_E5M2_E8M0, C4_STATIC,
                                  C4_TOKEN_E4M3, C4_GROUP, C2_GROUP_SMOOTH, C4_COMBINE_INT8,
-                                 C4_SCATTER_SHARED)}
+                                 C4_SCATTER_SHARED, C4_SMOOTH)}
 
 
 def _streams(seed: int):
