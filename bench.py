@@ -55,6 +55,9 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-passes", type=int, default=3)
     ap.add_argument("--mode", default="bench", choices=["bench", "copy-calib"])
+    ap.add_argument("--graph", action="store_true",
+                    help="also capture one step per buffer set into a HIP graph and report the "
+                         "replayed step time as the headline (launch gaps removed)")
     return ap.parse_args()
 
 
@@ -191,6 +194,13 @@ def run_copy_calib(args):
                       "bytes_written_per_launch": n, "launches": max(1, args.steps)}))
 
 
+class _NoEvent:
+    """Stands in for a timing event inside graph capture, where none is recorded."""
+
+    def record(self, stream=None):
+        pass
+
+
 def run_bench(args):
     import torch
     import combine_quant_amd as cq
@@ -233,10 +243,11 @@ def run_bench(args):
                                               device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step(n):
+    def step(n, stream=stream, timed=True):
         st = sets[n % len(sets)]
         o = st["out"]
-        ev = tuple(torch.cuda.Event(enable_timing=True) for _ in range(4))
+        ev = tuple(torch.cuda.Event(enable_timing=True) if timed else _NoEvent()
+                   for _ in range(4))
         ev[0].record(stream)
         cq.moe_dispatch(cfg, st["x"], ids, smooth, mask, o["expand_x"], o["dynamic_scales"],
                         o["expand_idx"], o["assist_info"], o["ep_recv_count"],
@@ -277,6 +288,30 @@ def run_bench(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
+    eager_ms_per_step = total_ms / args.steps
+
+    if args.graph:
+        # one graph per buffer set, each holding one whole step; the warm-up above ran every
+        # kernel once outside capture
+        graphs = []
+        for k in range(len(sets)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(k, torch.cuda.current_stream(dev), timed=False)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for n in range(args.warmup):
+            graphs[n % len(graphs)].replay()
+        torch.cuda.synchronize()
+        print(f"[bench] timing {args.steps} graph replays", file=sys.stderr, flush=True)
+        wall0 = time.perf_counter()
+        t_start.record(stream)
+        for n in range(args.steps):
+            graphs[n % len(graphs)].replay()
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        total_ms = t_start.elapsed_time(t_end)
     disp_ms = [e[0].elapsed_time(e[1]) for e in evs]
     quant_ms = [e[1].elapsed_time(e[2]) for e in evs]      # 0 without combine quantization
     comb_ms = [e[2].elapsed_time(e[3]) for e in evs]
@@ -351,6 +386,8 @@ def run_bench(args):
             "avg_us": round(statistics.mean(quant_ms) * 1e3, 2),
             "algorithmic_bytes": q_bytes,
             "gbps": round(q_bytes / (statistics.mean(quant_ms) * 1e-3) / 1e9, 1)},
+        "launch": "hip_graph" if args.graph else "eager",
+        "eager_ms_per_step": round(eager_ms_per_step, 4),
         "wall_s_timed": round(wall, 4),
         "cpu_baseline": cpu,
     }

@@ -151,9 +151,31 @@ C4_SCATTER_SHARED = C4.replace(
     description="C4 with the scatter-back combine (rows return by their source triples) "
                 "and a shared expert's bf16 N(0,1) output added to every token")
 
+# the shapes of the sample article's performance table (性能数据): 8 ranks with 4 experts each,
+# H=7168, K=8, BS 8 or 256; non-quantized, or MXFP8 (E5M2 codes, E8M0 scales) dispatch with the
+# int8 block-quantized combine.  Here all 8 ranks run on one GPU.
+SAMPLE_BS8 = Workload(
+    "sample_w8_bs8_bf16", W=8, E=32, BS=8, H=7168, K=8, quant_mode=0,
+    description="the sample table's low-latency shape: 8 ranks x 4 experts, BS=8, H=7168, "
+                "K=8, no quantization")
+SAMPLE_BS8_Q = SAMPLE_BS8.replace(
+    name="sample_w8_bs8_mxfp8_cint8", quant_mode=4, out_dtype=3, scale_format=1,
+    combine_quant=1,
+    description="the sample table's low-latency shape with MXFP8 (E5M2 + E8M0) dispatch and "
+                "the int8 block-quantized combine")
+SAMPLE_BS256 = SAMPLE_BS8.replace(
+    name="sample_w8_bs256_bf16", BS=256,
+    description="the sample table's throughput shape: 8 ranks x 4 experts, BS=256, H=7168, "
+                "K=8, no quantization")
+SAMPLE_BS256_Q = SAMPLE_BS8_Q.replace(
+    name="sample_w8_bs256_mxfp8_cint8", BS=256,
+    description="the sample table's throughput shape with MXFP8 (E5M2 + E8M0) dispatch and "
+                "the int8 block-quantized combine")
+
 WORKLOADS = {w.name: w for w in (C1_MODE0, C1_MODE2, C2, C3, C4, C5, C3_E5M2_E8M0, C4_STATIC,
                                  C4_TOKEN_E4M3, C4_GROUP, C2_GROUP_SMOOTH, C4_COMBINE_INT8,
-                                 C4_SCATTER_SHARED, C4_SMOOTH)}
+                                 C4_SCATTER_SHARED, C4_SMOOTH, SAMPLE_BS8, SAMPLE_BS8_Q,
+                                 SAMPLE_BS256, SAMPLE_BS256_Q)}
 
 
 def _streams(seed: int):
