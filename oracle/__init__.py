@@ -23,7 +23,7 @@ class OracleCfg(ctypes.Structure):
         "expert_token_nums_type", "mask_kind", "out_dtype", "scales_kind", "scale_format")]
 
 # element types of expand_x (out_dtype values; 0 selects the quant mode's default)
-CODE_BF16, CODE_INT8, CODE_E4M3, CODE_E5M2 = 0, 1, 2, 3
+CODE_BF16, CODE_INT8, CODE_E4M3, CODE_E5M2, CODE_E2M1 = 0, 1, 2, 3, 4
 
 
 def _load():
@@ -42,6 +42,9 @@ def _load():
             "oracle_e4m3_to_f32": (f32, [u8]),
             "oracle_e5m2_from_f32": (u8, [f32]),
             "oracle_e5m2_to_f32": (f32, [u8]),
+            "oracle_e2m1_from_f32": (u8, [f32]),
+            "oracle_e2m1_to_f32": (f32, [u8]),
+            "oracle_code_row_bytes": (i32, [i32, i32]),
             "oracle_int8_from_f32": (ctypes.c_int8, [f32]),
             "oracle_e8m0_from_scale": (u8, [f32]),
             "oracle_f32_to_f16": (u16, [f32]),
@@ -121,6 +124,18 @@ def e5m2_to_f32(code):
     return _load().oracle_e5m2_to_f32(int(code))
 
 
+def e2m1_from_f32(v):
+    return _load().oracle_e2m1_from_f32(float(v))
+
+
+def e2m1_to_f32(code):
+    return _load().oracle_e2m1_to_f32(int(code))
+
+
+def code_row_bytes(ct, H):
+    return _load().oracle_code_row_bytes(int(ct), int(H))
+
+
 def int8_from_f32(v):
     return _load().oracle_int8_from_f32(float(v))
 
@@ -189,7 +204,8 @@ def quant_row(quant_mode, x_bf16, pre=None, out_dtype=0):
     H = x.shape[0]
     ct = code_type(quant_mode, out_dtype)
     pr = _c(pre, np.float32)
-    codes = np.empty(H, code_np_dtype(ct))
+    codes = np.empty(code_row_bytes(ct, H) // np.dtype(code_np_dtype(ct)).itemsize,
+                     code_np_dtype(ct))
     scales = np.empty(max(1, scale_count(quant_mode, H)), np.float32)
     rc = _load().oracle_quant_row(int(quant_mode), ct, _p(x), _p(pr),
                                   0 if pr is None else pr.shape[0], H, _p(codes), _p(scales))
@@ -241,7 +257,8 @@ def dispatch(cfg, x, expert_ids, scales=None, mask=None, cap=None):
     if ct < 0:
         raise ValueError("quant_mode and out_dtype do not go together")
     ns = scale_count(cfg.quant_mode, H)
-    ex = np.zeros((cap, H), code_np_dtype(ct))
+    ex = np.zeros((cap, code_row_bytes(ct, H) // np.dtype(code_np_dtype(ct)).itemsize),
+                  code_np_dtype(ct))
     sdt = np.uint8 if cfg.scale_format == 1 else np.float32
     ds = np.zeros(1, sdt) if ns == 0 else np.zeros((cap,) if ns == 1 else (cap, ns), sdt)
     eidx = np.empty((W, BS, K), np.int32)

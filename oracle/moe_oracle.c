@@ -206,6 +206,48 @@ uint8_t oracle_e5m2_from_f32(float v)
     return (uint8_t)(sign | code);
 }
 
+/* OCP E2M1 (fp4): 1 sign, 2 exponent (bias 1), 1 mantissa bit, no infinities or NaN.  The
+ * eight magnitudes are 0, 0.5 (the one subnormal), 1, 1.5, 2, 3, 4 and 6; a code is 4 bits. */
+float oracle_e2m1_to_f32(uint8_t code)
+{
+    int sign = code & 0x8;
+    int ex = (code >> 1) & 0x3;
+    int m = code & 0x1;
+    double v = ex == 0 ? 0.5 * m : ldexp(1.0 + m / 2.0, ex - 1);
+    return (float)(sign ? -v : v);
+}
+
+/* Round a binary32 value to the nearest E2M1 value, ties to the even code, saturating
+ * magnitudes >= 6 to 6 (reading R6 again; E2M1 has no NaN, so a NaN input is taken as a
+ * contract violation and coded 6 with its sign, like any overflow).  Method of the fp8
+ * encoders: spacing 2^(floor(log2|v|) - 1) in the binade of |v|, 0.5 below 1. */
+uint8_t oracle_e2m1_from_f32(float v)
+{
+    uint8_t sign = signbit(v) ? 0x8 : 0x0;
+    double a = fabs((double)v);
+    if (isnan(v) || a >= 6.0) return (uint8_t)(sign | 0x7);
+    double quantum;
+    if (a < 1.0) {
+        quantum = 0.5;
+    } else {
+        int ex;
+        frexp(a, &ex);
+        quantum = ldexp(1.0, (ex - 1) - 1);
+    }
+    double r = nearbyint(a / quantum) * quantum;     /* <= 6 because a < 6 */
+    uint8_t code;
+    if (r < 1.0) {
+        code = (uint8_t)(r / 0.5);                    /* 0..2; 2 is exactly 1.0 = 0x2 */
+    } else {
+        int ex;
+        double m = frexp(r, &ex);
+        int e2 = ex - 1;
+        int mant = (int)((2.0 * m - 1.0) * 2.0);      /* exact: 1 fraction bit */
+        code = (uint8_t)(((e2 + 1) << 1) | mant);
+    }
+    return (uint8_t)(sign | code);
+}
+
 /* The int8 cast of every int8 mode (readings R4, R5; reading R22: the static mode 1 uses the
  * same cast): round half to even, saturate to [-127, 127], NaN -> 0. */
 int8_t oracle_int8_from_f32(float v)
@@ -238,7 +280,8 @@ int32_t oracle_mx_scale_count(int32_t H)
 /* Element type of expand_x for a quant mode and a requested out_dtype (0 = the mode's
  * default).  [LLD] 约束说明 lists the allowed output types per mode: mode 0 keeps the input
  * type; mode 1 int8; mode 2 int8, E4M3 or E5M2; mode 3 E4M3 or E5M2; modes 4/5 E4M3 or
- * E5M2 (also fp4 and hifloat8 types there, not covered).  -1 for any other pairing. */
+ * E5M2, modes 4/5 also E2M1 (the hifloat8 and E1M2 types there are not covered).  -1 for any
+ * other pairing. */
 int32_t oracle_code_type(int32_t quant_mode, int32_t out_dtype)
 {
     switch (quant_mode) {
@@ -251,14 +294,26 @@ int32_t oracle_code_type(int32_t quant_mode, int32_t out_dtype)
         return (out_dtype == ORACLE_CODE_INT8 || out_dtype == ORACLE_CODE_E4M3 ||
                 out_dtype == ORACLE_CODE_E5M2) ? out_dtype : -1;
     case 3:
-    case 4:
-    case 5:
         if (out_dtype == 0) return ORACLE_CODE_E4M3;
         return (out_dtype == ORACLE_CODE_E4M3 || out_dtype == ORACLE_CODE_E5M2) ? out_dtype
                                                                                 : -1;
+    case 4:
+    case 5:
+        if (out_dtype == 0) return ORACLE_CODE_E4M3;
+        return (out_dtype == ORACLE_CODE_E4M3 || out_dtype == ORACLE_CODE_E5M2 ||
+                out_dtype == ORACLE_CODE_E2M1) ? out_dtype : -1;
     default:
         return -1;
     }
+}
+
+/* Bytes of one expand_x row: 2H for bf16, H/2 for E2M1 (two codes per byte, the element of
+ * even index in the low nibble: reading R31), else H. */
+int32_t oracle_code_row_bytes(int32_t code_type, int32_t H)
+{
+    if (code_type == ORACLE_CODE_BF16) return 2 * H;
+    if (code_type == ORACLE_CODE_E2M1) return H / 2;
+    return H;
 }
 
 /* Scales per expand_x row ([LLD] 约束说明, dynamic_scales shapes): none for modes 0 and 1,
@@ -282,21 +337,27 @@ int32_t oracle_scale_count(int32_t quant_mode, int32_t H)
  * fp8_max of the clip variant. */
 static float code_max(int32_t ct)
 {
-    return ct == ORACLE_CODE_INT8 ? 127.0f : ct == ORACLE_CODE_E4M3 ? 448.0f : 57344.0f;
+    switch (ct) {
+    case ORACLE_CODE_INT8: return 127.0f;
+    case ORACLE_CODE_E4M3: return 448.0f;
+    case ORACLE_CODE_E5M2: return 57344.0f;
+    default: return 6.0f;                            /* E2M1 */
+    }
 }
 
-/* emax of an fp8 element type: the exponent of its largest power of two (E4M3 2^8 = 256,
- * E5M2 2^15), used by the MX shared exponent. */
+/* emax of an MX element type: the exponent of its largest power of two (E4M3 2^8 = 256,
+ * E5M2 2^15, E2M1 2^2 = 4), used by the MX shared exponent. */
 static int code_emax(int32_t ct)
 {
-    return ct == ORACLE_CODE_E4M3 ? 8 : 15;
+    return ct == ORACLE_CODE_E4M3 ? 8 : ct == ORACLE_CODE_E5M2 ? 15 : 2;
 }
 
 static uint8_t encode(int32_t ct, float v)
 {
     if (ct == ORACLE_CODE_INT8) return (uint8_t)oracle_int8_from_f32(v);
     if (ct == ORACLE_CODE_E4M3) return oracle_e4m3_from_f32(v);
-    return oracle_e5m2_from_f32(v);
+    if (ct == ORACLE_CODE_E5M2) return oracle_e5m2_from_f32(v);
+    return oracle_e2m1_from_f32(v);
 }
 
 /* One dynamic-scale segment [h0, h1) of the fp32 row f ([LLD] 计算公式, quant_mode 2 over the
@@ -371,14 +432,15 @@ static float quant_mx_block(int32_t ct, int32_t clip, const float* f, int32_t h0
  *   mode 3: dynamic segments of 128 elements (the last may be short); Ceil(H,128) scales
  *           (reading R20: the group length is the 128 of the scale shape (A, Ceil(H,128)))
  *   mode 4/5: MX blocks of 32; Align2(Ceil(H,32)) scales, the pad entry 0
- * codes: H bytes (int8 two's complement or fp8 codes).  Returns 0, or -1 when the code type,
- * the multiplier or the mode do not go together. */
+ * codes: oracle_code_row_bytes bytes (int8 two's complement, fp8 codes, or E2M1 codes two per
+ * byte).  Returns 0, or -1 when the code type, the multiplier or the mode do not go together. */
 int32_t oracle_quant_row(int32_t quant_mode, int32_t code_type, const uint16_t* x,
                          const float* pre, int32_t pre_len, int32_t H, void* codes,
                          float* scales)
 {
     if (quant_mode < 1 || quant_mode > 5) return -1;
     if (oracle_code_type(quant_mode, code_type) != code_type) return -1;
+    if (code_type == ORACLE_CODE_E2M1 && H % 2 != 0) return -1;   /* [LLD]: H even for fp4 */
     if (pre_len != 0 && pre_len != 1 && pre_len != H) return -1;
     if ((pre_len != 0) != (pre != NULL)) return -1;
     if (quant_mode >= 4 && pre_len != 0) return -1;
@@ -400,12 +462,18 @@ int32_t oracle_quant_row(int32_t quant_mode, int32_t code_type, const uint16_t* 
             scales[g] = quant_dynamic(code_type, f, g * 128, h1, q);
         }
     } else {
+        /* E2M1 codes are made one per byte first, then packed two per byte (R31) */
+        uint8_t* one = code_type == ORACLE_CODE_E2M1 ? (uint8_t*)malloc((size_t)H) : q;
         int32_t nb = (H + 31) / 32;
         for (int32_t b = 0; b < nb; ++b) {
             int32_t h1 = b * 32 + 32 < H ? b * 32 + 32 : H;
-            scales[b] = quant_mx_block(code_type, quant_mode == 5, f, b * 32, h1, q);
+            scales[b] = quant_mx_block(code_type, quant_mode == 5, f, b * 32, h1, one);
         }
         for (int32_t b = nb; b < oracle_mx_scale_count(H); ++b) scales[b] = 0.0f;
+        if (code_type == ORACLE_CODE_E2M1) {
+            for (int32_t h = 0; h < H; h += 2) q[h / 2] = (uint8_t)(one[h] | (one[h + 1] << 4));
+            free(one);
+        }
     }
     free(f);
     return 0;
@@ -525,7 +593,7 @@ int64_t oracle_dest_row(const oracle_cfg* c, const int32_t* ep_recv_count,
  *   scales tensor ([LLD] 约束说明, modes 1-3) is a scalar (scales_kind 1), a row shared by
  *   every expert (2) or the routed expert's row of an [E][H] table (3); with kind 3 the
  *   quantization is per pair.
- *   expand_x [cap][H] (uint16 bf16 patterns for mode 0, else bytes);
+ *   expand_x [cap][row bytes] (bf16 patterns for mode 0; E2M1 two codes per byte; else bytes);
  *   dynamic_scales [cap][scale count] fp32, or bytes when scale_format is 1: each MX scale
  *   2^e as its E8M0 byte e + 127 ([SMP] 通信前量化), pad bytes 0 (reading R24);
  *   assist_info [cap][3].
@@ -549,6 +617,8 @@ int32_t oracle_dispatch(const oracle_cfg* c, const uint16_t* x, const int32_t* e
     oracle_recv_counts(c, cnt_scratch, ep_recv_count, expert_token_nums, recv_offsets);
     const int32_t ns = oracle_scale_count(mode, H);
     const int32_t nb = (H + 31) / 32;
+    const size_t row_bytes = (size_t)oracle_code_row_bytes(ct, H);
+    if (ct == ORACLE_CODE_E2M1 && H % 2 != 0) return -2;
     float* rowsc = (float*)malloc((size_t)(ns > 0 ? ns : 1) * sizeof(float));
     for (int32_t s = 0; s < c->W; ++s)
         for (int32_t i = 0; i < c->BS; ++i)
@@ -568,7 +638,7 @@ int32_t oracle_dispatch(const oracle_cfg* c, const uint16_t* x, const int32_t* e
                     if (c->scales_kind == 2) { pre = scales_or_null; pre_len = H; }
                     if (c->scales_kind == 3) { pre = scales_or_null + (size_t)e * H; pre_len = H; }
                     oracle_quant_row(mode, ct, xr, pre, pre_len, H,
-                                     (uint8_t*)expand_x + (size_t)row * H, rowsc);
+                                     (uint8_t*)expand_x + (size_t)row * row_bytes, rowsc);
                     for (int32_t b = 0; b < ns; ++b) {
                         if (c->scale_format == 1)
                             ((uint8_t*)dynamic_scales)[(size_t)row * ns + b] =

@@ -48,6 +48,7 @@ typedef struct {
 #define ORACLE_CODE_INT8 1
 #define ORACLE_CODE_E4M3 2
 #define ORACLE_CODE_E5M2 3
+#define ORACLE_CODE_E2M1 4              /* fp4, two codes per byte (modes 4/5, even H) */
 
 /* scalar helpers (each written from its definition) */
 float    oracle_bf16_to_f32(uint16_t b);
@@ -56,6 +57,9 @@ uint8_t  oracle_e4m3_from_f32(float v);
 float    oracle_e4m3_to_f32(uint8_t code);
 uint8_t  oracle_e5m2_from_f32(float v);
 float    oracle_e5m2_to_f32(uint8_t code);
+uint8_t  oracle_e2m1_from_f32(float v);
+float    oracle_e2m1_to_f32(uint8_t code);
+int32_t  oracle_code_row_bytes(int32_t code_type, int32_t H);
 int8_t   oracle_int8_from_f32(float v);
 uint8_t  oracle_e8m0_from_scale(float s);
 int32_t  oracle_mx_scale_count(int32_t H);

@@ -496,7 +496,7 @@ def test_combine_roundtrip_int8():
 VARIANTS = [  # (quant_mode, out_dtype, scales_kind, scale_format)
     (0, 0, 0, 0), (1, 0, 1, 0), (1, 1, 2, 0), (1, 0, 3, 0), (2, 0, 0, 0), (2, 0, 3, 0),
     (2, 2, 2, 0), (2, 3, 1, 0), (3, 0, 0, 0), (3, 3, 3, 0), (4, 0, 0, 0), (4, 3, 0, 1),
-    (5, 0, 0, 0), (5, 2, 0, 1), (5, 3, 0, 0)]
+    (5, 0, 0, 0), (5, 2, 0, 1), (5, 3, 0, 0), (4, 4, 0, 0), (5, 4, 0, 1)]
 
 
 @pytest.mark.parametrize("variant", VARIANTS, ids=lambda v: "m%d_t%d_s%d_f%d" % v)

@@ -7,10 +7,11 @@ number formats fix, computed independently of the oracle's C code:
   * the int8 cast at its rounding ties and saturation points;
   * E8M0 bytes of every power of two the MX scales can take;
   * the per-mode code types and scale counts of the low_latency_dispatch constraints;
-  * static (mode 1), per-token fp8 (mode 2), per-128-group (mode 3) and MX E5M2 (modes 4/5)
-    rows, element by element from exact rational arithmetic rounded once per binary32
-    operation, plus closed-form examples and invariants (group boundaries, all-zero groups,
-    the ragged last group).
+  * static (mode 1), per-token fp8 (mode 2), per-128-group (mode 3) and MX E5M2 and E2M1
+    (modes 4/5) rows, element by element from exact rational arithmetic rounded once per
+    binary32 operation, plus closed-form examples and invariants (group boundaries, all-zero
+    groups, the ragged last group, the nibble order of packed E2M1 codes);
+  * E2M1 encoding against a nearest-value search over the eight OCP fp4 magnitudes.
 """
 import math
 from fractions import Fraction
@@ -23,7 +24,7 @@ import oracle
 import workloads
 from exact import f32_bits, round_half_even, to_f32
 
-E4M3, E5M2 = oracle.CODE_E4M3, oracle.CODE_E5M2
+E4M3, E5M2, E2M1 = oracle.CODE_E4M3, oracle.CODE_E5M2, oracle.CODE_E2M1
 FP8_KIND = {E4M3: "e4m3", E5M2: "e5m2"}
 FP8_MAX = {E4M3: 448, E5M2: 57344}
 FP8_MAX_CODE = {E4M3: 0x7E, E5M2: 0x7B}
@@ -127,9 +128,9 @@ def test_e8m0_of_every_mx_scale():
 def test_code_types_follow_the_mode_constraints():
     # default element type of each mode, then which explicit types each mode accepts
     assert [oracle.code_type(m) for m in range(6)] == [0, 1, 1, 2, 2, 2]
-    allowed = {0: [], 1: [1], 2: [1, 2, 3], 3: [2, 3], 4: [2, 3], 5: [2, 3]}
+    allowed = {0: [], 1: [1], 2: [1, 2, 3], 3: [2, 3], 4: [2, 3, 4], 5: [2, 3, 4]}
     for m in range(6):
-        for t in (1, 2, 3, 4):
+        for t in (1, 2, 3, 4, 5):
             assert (oracle.code_type(m, t) == t) == (t in allowed[m]), (m, t)
     assert oracle.code_type(6) == -1
 
@@ -320,3 +321,106 @@ def test_quant_row_rejects_mismatched_arguments():
         oracle.quant_row(4, x, np.ones(64, np.float32))  # MX takes no scales
     with pytest.raises(ValueError):
         oracle.quant_row(2, x, np.ones(10, np.float32))  # neither scalar nor a row
+
+
+# ---------------------------------------------------------------------------------------
+# E2M1 (fp4) MX elements, two codes per byte
+# ---------------------------------------------------------------------------------------
+
+E2M1_VALUES = [0, 0.5, 1, 1.5, 2, 3, 4, 6]          # the OCP fp4 magnitudes, codes 0..7
+
+
+def _e2m1_nearest(v):
+    """Nearest E2M1 code to the exact value v (ties to the even code), |v| >= 6 -> 6."""
+    sign = 0x8 if v < 0 else 0
+    a = abs(Fraction(v))
+    if a >= 6:
+        return sign | 0x7
+    best = min(range(8), key=lambda c: (abs(Fraction(E2M1_VALUES[c]) - a), c & 1))
+    return sign | best
+
+
+def test_e2m1_decode_table():
+    for code, v in enumerate(E2M1_VALUES):
+        assert oracle.e2m1_to_f32(code) == v
+        assert oracle.e2m1_to_f32(code | 0x8) == -v
+
+
+def test_e2m1_all_bf16_inputs():
+    b = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    f = workloads.bf16_bits_to_f32(b)
+    for v in f[np.isfinite(f)]:
+        want = _e2m1_nearest(float(v))
+        if v == 0:
+            want = 0x8 if math.copysign(1, float(v)) < 0 else 0
+        assert oracle.e2m1_from_f32(float(v)) == want, float(v)
+
+
+def test_e2m1_ties():
+    # midpoints go to the even code: 0.25 -> 0, 0.75 -> 1.0, 1.25 -> 1.0, 1.75 -> 2,
+    # 2.5 -> 2, 3.5 -> 4, 5 -> 4; 6.5 and up saturate to 6
+    for v, want in [(0.25, 0x0), (0.75, 0x2), (1.25, 0x2), (1.75, 0x4), (2.5, 0x4),
+                    (3.5, 0x6), (5.0, 0x6), (6.5, 0x7), (1e9, 0x7), (-5.0, 0xE)]:
+        assert oracle.e2m1_from_f32(v) == want, v
+
+
+def _unpack_e2m1(codes):
+    out = np.empty(codes.size * 2, np.uint8)
+    out[0::2] = codes & 0xF
+    out[1::2] = codes >> 4
+    return out
+
+
+def test_mx_e2m1_closed_forms_and_packing():
+    vals = [1.0] * 32
+    vals[0], vals[1] = -1.5, 0.5
+    codes, sc = oracle.quant_row(4, bf16(vals), None, E2M1)
+    # amax 1.5 -> floor(log2) 0 - emax 2 = -2: elements times 4: -6 (0xF), 2 (0x4), 4 (0x6)
+    assert len(codes) == 16 and sc.tolist() == [0.25, 0.0]
+    assert codes[0] == (0xF | (0x4 << 4))           # element 0 in the low nibble
+    assert (codes[1:] == (0x6 | (0x6 << 4))).all()
+    codes, sc = oracle.quant_row(5, bf16([6.0] * 32), None, E2M1)
+    assert sc[0] == 1.0 and (codes == 0x77).all()    # 6 / 6 = 1 -> exponent 0
+    codes, sc = oracle.quant_row(5, np.zeros(32, np.uint16), None, E2M1)
+    # 1e-4 / 6 = 1.67e-5: log2 = -15.87 -> ceil -15
+    assert sc[0] == 2.0 ** -15 and (codes == 0).all()
+
+
+@pytest.mark.parametrize("mode", [4, 5])
+def test_mx_e2m1_rows_exact(mode):
+    rng = np.random.default_rng(71 + mode)
+    H = 1056
+    xf = (rng.standard_normal(H) * rng.choice([1e-6, 1.0, 300.0], H)).astype(np.float32)
+    xb = workloads.f32_to_bf16_bits(xf)
+    xf = workloads.bf16_bits_to_f32(xb)
+    codes, sc = oracle.quant_row(mode, xb, None, E2M1)
+    assert len(codes) == H // 2
+    q = _unpack_e2m1(codes)
+    for b in range((H + 31) // 32):
+        blk = xf[b * 32:(b + 1) * 32]
+        amax = Fraction(float(np.abs(blk).max()))
+        if mode == 4:
+            se = -127 if amax == 0 else max(-127, math.floor(math.log2(amax)) - 2)
+            if amax != 0 and se > -127:
+                while Fraction(2) ** (se + 2) > amax:
+                    se -= 1
+                while Fraction(2) ** (se + 3) <= amax:
+                    se += 1
+        else:
+            c = to_f32(Fraction(max(amax, Fraction(float(np.float32(1e-4))))) / Fraction(6))
+            se = math.ceil(math.log2(c))
+            while Fraction(2) ** se < Fraction(c):
+                se += 1
+            while Fraction(2) ** (se - 1) >= Fraction(c):
+                se -= 1
+        assert Fraction(float(sc[b])) == Fraction(2) ** se
+        for v, code in zip(blk, q[b * 32:(b + 1) * 32]):
+            want = _e2m1_nearest(Fraction(float(v)) / Fraction(2) ** se)
+            if v == 0:
+                want = 0x8 if math.copysign(1, float(v)) < 0 else 0
+            assert code == want
+
+
+def test_e2m1_needs_even_hidden():
+    with pytest.raises(ValueError):
+        oracle.quant_row(4, bf16([1.0] * 33), None, E2M1)
