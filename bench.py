@@ -72,12 +72,12 @@ def algorithmic_bytes(wl, inp, routed_rows, copy_picks, active_tokens):
     combine: read each routed expert-output row once, ids + expand_idx + weights, the
     receive counts (and mask, and ori_x for copy picks), write y."""
     W, E, H, K, T = wl.W, wl.E, wl.H, wl.K, wl.T
-    b = 2 if wl.quant_mode == 0 else 1
+    b = 2 if wl.quant_mode == 0 else 0.5 if wl.out_dtype == 4 else 1
     S = scale_bytes_per_row(wl)
     m = 0 if inp.get("mask") is None else inp["mask"].nbytes
     smooth = 0 if inp.get("scales") is None else inp["scales"].nbytes
     P = routed_rows
-    dispatch = (2 * H * active_tokens + 4 * T * K + m + smooth + P * (b * H + S + 12)
+    dispatch = (2 * H * active_tokens + 4 * T * K + m + smooth + P * (int(b * H) + S + 12)
                 + 4 * T * K + 4 * E * W + 8 * E + 8 * (W + 1))
     row = 2 * H if wl.combine_quant == 0 else H + 4 * ((H + 7) // 8)
     if wl.combine_path == "scatter":

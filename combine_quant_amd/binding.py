@@ -15,7 +15,7 @@ import torch
 from .build import LIB
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = 0, -1, -2, -3, -4
-MOE_DTYPE_DEFAULT, MOE_DTYPE_INT8, MOE_DTYPE_E4M3, MOE_DTYPE_E5M2 = 0, 1, 2, 3
+MOE_DTYPE_DEFAULT, MOE_DTYPE_INT8, MOE_DTYPE_E4M3, MOE_DTYPE_E5M2, MOE_DTYPE_E2M1 = 0, 1, 2, 3, 4
 MOE_SCALES_NONE, MOE_SCALES_SCALAR, MOE_SCALES_SHARED, MOE_SCALES_PER_EXPERT = 0, 1, 2, 3
 MOE_SCALE_FP32, MOE_SCALE_E8M0 = 0, 1
 _STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
@@ -173,8 +173,14 @@ def _stream(device, stream):
 
 
 _CODE_DTYPES = {0: torch.bfloat16, 1: torch.int8, 2: (torch.uint8, torch.float8_e4m3fn),
-                3: (torch.uint8, torch.float8_e5m2)}
-_ALLOC_DTYPES = {0: torch.bfloat16, 1: torch.int8, 2: torch.uint8, 3: torch.uint8}
+                3: (torch.uint8, torch.float8_e5m2), 4: torch.uint8}
+_ALLOC_DTYPES = {0: torch.bfloat16, 1: torch.int8, 2: torch.uint8, 3: torch.uint8,
+                 4: torch.uint8}
+
+
+def code_row_elems(cfg):
+    """Elements of one expand_x row in its tensor dtype: H, or H / 2 bytes for E2M1."""
+    return cfg.hidden // 2 if code_type(cfg) == MOE_DTYPE_E2M1 else cfg.hidden
 
 
 def _scales_shape(cfg):
@@ -209,7 +215,8 @@ def moe_dispatch(cfg, x, expert_ids, scales, x_active_mask, expand_x, dynamic_sc
         _ptr(scales, torch.float32, _scales_shape(cfg), "scales", dev),
         _ptr(x_active_mask, (torch.uint8, torch.bool), mshape, "x_active_mask", dev),
         _ptr(expert_scales, torch.float32, (W, BS, K), "expert_scales", dev),
-        _ptr(expand_x, _CODE_DTYPES.get(code_type(cfg)), (cap, H), "expand_x", dev),
+        _ptr(expand_x, _CODE_DTYPES.get(code_type(cfg)), (cap, code_row_elems(cfg)), "expand_x",
+             dev),
         _ptr(dynamic_scales, None if spec is None else spec[0],
              None if spec is None else spec[1], "dynamic_scales", dev),
         _ptr(expand_idx, torch.int32, (W, BS, K), "expand_idx", dev),
@@ -327,7 +334,8 @@ def alloc_dispatch_outputs(cfg, device="cuda"):
                            cfg.expand_rows_capacity)
     spec = _dyn_scales_spec(cfg)
     return dict(
-        expand_x=torch.empty((cap, H), dtype=_ALLOC_DTYPES[code_type(cfg)], device=device),
+        expand_x=torch.empty((cap, code_row_elems(cfg)), dtype=_ALLOC_DTYPES[code_type(cfg)],
+                             device=device),
         dynamic_scales=(None if spec is None else
                         torch.empty(spec[1], dtype=spec[0], device=device)),
         expand_idx=torch.empty((W, BS, K), dtype=torch.int32, device=device),

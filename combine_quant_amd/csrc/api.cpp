@@ -39,7 +39,7 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 
 // Element type of expand_x for a quant mode and requested out_dtype, or -1 when the pair is
 // not allowed ([LLD] 约束说明: mode 0 keeps the input type; mode 1 int8; mode 2 int8, E4M3
-// or E5M2; modes 3-5 E4M3 or E5M2).
+// or E5M2; mode 3 E4M3 or E5M2; modes 4/5 E4M3, E5M2 or E2M1).
 int32_t resolve_code_type(int32_t mode, int32_t out_dtype)
 {
     switch (mode) {
@@ -54,7 +54,8 @@ int32_t resolve_code_type(int32_t mode, int32_t out_dtype)
         return out_dtype == MOE_DTYPE_E5M2 ? moe_dc::kCodeE5m2 : -1;
     default:
         if (out_dtype == MOE_DTYPE_DEFAULT || out_dtype == MOE_DTYPE_E4M3) return moe_dc::kCodeE4m3;
-        return out_dtype == MOE_DTYPE_E5M2 ? moe_dc::kCodeE5m2 : -1;
+        if (out_dtype == MOE_DTYPE_E5M2) return moe_dc::kCodeE5m2;
+        return out_dtype == MOE_DTYPE_E2M1 && mode >= 4 ? moe_dc::kCodeE2m1 : -1;
     }
 }
 
@@ -96,6 +97,8 @@ moe_status check(const moe_dc_config* c, moe_dc::Shape* out)
     if (code_type < 0)
         return fail(MOE_ERR_INVALID_ARG, "out_dtype %d is not allowed with quant_mode %d",
                     c->out_dtype, c->quant_mode);
+    if (code_type == moe_dc::kCodeE2m1 && c->hidden % 2 != 0)
+        return fail(MOE_ERR_INVALID_ARG, "E2M1 codes need an even hidden size");
     if (c->scales_kind < MOE_SCALES_NONE || c->scales_kind > MOE_SCALES_PER_EXPERT)
         return fail(MOE_ERR_INVALID_ARG, "scales_kind %d is not one of 0..3", c->scales_kind);
     if ((c->quant_mode == 0 || c->quant_mode >= 4) && c->scales_kind != MOE_SCALES_NONE)

@@ -69,6 +69,22 @@ __device__ __forceinline__ uint32_t e5m2_code(float v)
     return sign | ((((r >> 23) - 112u) << 2) | ((r >> 21) & 3u));
 }
 
+// E2M1 (fp4: bias 1, magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) 4-bit code of a finite binary32
+// value: nearest, ties to even, magnitudes >= 6 saturate to 6, sign in bit 3.  Below 1 the
+// grid is 0, 0.5, 1 (step 0.5: the code is |v| * 2 rounded); above, the significand is rounded
+// to 1 fraction bit at bit 22 and the exponent rebiased from 127 to 1.
+__device__ __forceinline__ uint32_t e2m1_code(float v)
+{
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t sign = (u >> 28) & 0x8u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    if (a >= 0x40C00000u) return sign | 0x7u;                  // |v| >= 6
+    if (a < 0x3F800000u)                                       // |v| < 1
+        return sign | (uint32_t)__builtin_rintf(__uint_as_float(a) * 2.0f);
+    const uint32_t r = a + 0x1FFFFFu + ((a >> 22) & 1u);
+    return sign | ((((r >> 23) - 126u) << 1) | ((r >> 22) & 1u));
+}
+
 // Streaming (non-temporal) 16- and 8-byte global accesses, for rows that are touched once.
 // They lower to global loads/stores with the non-temporal cache policy, which keeps the
 // once-read / once-written rows from displacing reusable lines in L2 and the Infinity Cache.

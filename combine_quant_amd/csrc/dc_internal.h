@@ -8,7 +8,9 @@
 namespace moe_dc {
 
 // Element types of expand_x (the values of moe_dtype in the C ABI).
-enum CodeType : int32_t { kCodeBf16 = 0, kCodeInt8 = 1, kCodeE4m3 = 2, kCodeE5m2 = 3 };
+enum CodeType : int32_t {
+    kCodeBf16 = 0, kCodeInt8 = 1, kCodeE4m3 = 2, kCodeE5m2 = 3, kCodeE2m1 = 4
+};
 
 // Shapes of the quantization scales tensor (the values of moe_scales_kind).
 enum ScalesKind : int32_t {

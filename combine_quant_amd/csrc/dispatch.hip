@@ -28,7 +28,9 @@
 //           emax 8 for E4M3, 15 for E5M2)
 //   mode 5  per block: shared_exp = ceil(log2(max(max|x|, 1e-4) / fp8_max))
 //           codes = fp8(x / 2^shared_exp); the scale written is 2^shared_exp, as fp32 or as
-//           its E8M0 byte shared_exp + 127 (the SMP article's stored format)
+//           its E8M0 byte shared_exp + 127 (the SMP article's stored format).  Modes 4/5
+//           also take E2M1 (fp4: emax 2, max 6) elements, two 4-bit codes per byte with the
+//           even element in the low nibble.
 // int8 rounds half to even and saturates at +-127 with NaN -> 0; fp8 rounds to nearest even
 // and saturates at the type's largest finite value; NaN products of a dynamic mode (only
 // 0 * inf of an all-zero segment) give code 0.  In the vectorized path an MX block is 4
@@ -55,21 +57,22 @@ __device__ __forceinline__ uint32_t int8_code(float v)
 template <int CT>
 __device__ __forceinline__ uint32_t fp8_code(float v)
 {
-    return CT == kCodeE4m3 ? e4m3_code(v) : e5m2_code(v);
+    return CT == kCodeE4m3 ? e4m3_code(v) : CT == kCodeE5m2 ? e5m2_code(v) : e2m1_code(v);
 }
 
 // Largest finite value of a code type (dst_type_max / fp8_max of the formulas).
 template <int CT>
 constexpr float type_max()
 {
-    return CT == kCodeInt8 ? 127.0f : CT == kCodeE4m3 ? 448.0f : 57344.0f;
+    return CT == kCodeInt8 ? 127.0f : CT == kCodeE4m3 ? 448.0f : CT == kCodeE5m2 ? 57344.0f
+                                                                                 : 6.0f;
 }
 
 // Shared exponent of an MX block from the bit pattern of its absolute maximum.
 template <int MODE, int CT>
 __device__ __forceinline__ int mx_shared_exp(uint32_t amax_bits)
 {
-    constexpr int emax = CT == kCodeE4m3 ? 8 : 15;
+    constexpr int emax = CT == kCodeE4m3 ? 8 : CT == kCodeE5m2 ? 15 : 2;
     if (MODE == 4) {
         if (amax_bits == 0) return -127;
         const int ex = (int)(amax_bits >> 23);
@@ -316,14 +319,25 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
                 uint32_t c[8];
 #pragma unroll
                 for (int q = 0; q < 8; ++q) c[q] = fp8_code<CT>(f[n][q] * inv);
-                packed = pack_codes8(c);
+                if (CT == kCodeE2m1) {            // eight 4-bit codes, element 0 lowest
+                    uint32_t w = 0;
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) w |= c[q] << (4 * q);
+                    packed = make_uint2(w, 0u);
+                } else {
+                    packed = pack_codes8(c);
+                }
                 scale = pow2f(se);
             }
             if (v >= NV) continue;
 #pragma unroll
             for (int k = 0; k < kMaxK; ++k) {
                 if (rows[k] < 0) continue;
-                store_stream(out + (long long)rows[k] * NV + v, packed);
+                if (CT == kCodeE2m1)
+                    __builtin_nontemporal_store(
+                        packed.x, reinterpret_cast<uint32_t*>(expand_x) + (long long)rows[k] * NV + v);
+                else
+                    store_stream(out + (long long)rows[k] * NV + v, packed);
                 if (MODE == 3 && (v & (kGroup / 8 - 1)) == 0)
                     fscales[(long long)rows[k] * ns + (v >> 4)] = scale;
                 if (MODE >= 4 && (v & 3) == 0) {
@@ -503,9 +517,11 @@ hipError_t launch_tile(const Shape& sh, const ScatterArgs& a, hipStream_t stream
         return launch_tile_scales<3, kCodeE5m2>(MOE_DC_ARGS);
     case 4:
         if (ct == kCodeE4m3) return launch_tile_variant<4, kCodeE4m3, kScalesNone>(MOE_DC_ARGS);
+        if (ct == kCodeE2m1) return launch_tile_variant<4, kCodeE2m1, kScalesNone>(MOE_DC_ARGS);
         return launch_tile_variant<4, kCodeE5m2, kScalesNone>(MOE_DC_ARGS);
     case 5:
         if (ct == kCodeE4m3) return launch_tile_variant<5, kCodeE4m3, kScalesNone>(MOE_DC_ARGS);
+        if (ct == kCodeE2m1) return launch_tile_variant<5, kCodeE2m1, kScalesNone>(MOE_DC_ARGS);
         return launch_tile_variant<5, kCodeE5m2, kScalesNone>(MOE_DC_ARGS);
     default:
         return hipErrorInvalidValue;
@@ -523,7 +539,7 @@ constexpr int kElemWaves = kElemThreads / kWave;
 
 __device__ __forceinline__ uint32_t fp8_code_rt(int ct, float v)
 {
-    return ct == kCodeE4m3 ? e4m3_code(v) : e5m2_code(v);
+    return ct == kCodeE4m3 ? e4m3_code(v) : ct == kCodeE5m2 ? e5m2_code(v) : e2m1_code(v);
 }
 
 __device__ __forceinline__ uint32_t dynamic_code_rt(int ct, float v)
@@ -670,10 +686,12 @@ __global__ __launch_bounds__(kElemThreads) void scatter_elem_kernel(
             } else {
                 const uint32_t bm = group_max_u32<kMxBlock>(a[n]);
                 const int se = mode == 4
-                    ? (ct == kCodeE4m3 ? mx_shared_exp<4, kCodeE4m3>(bm)
-                                       : mx_shared_exp<4, kCodeE5m2>(bm))
-                    : (ct == kCodeE4m3 ? mx_shared_exp<5, kCodeE4m3>(bm)
-                                       : mx_shared_exp<5, kCodeE5m2>(bm));
+                    ? (ct == kCodeE4m3   ? mx_shared_exp<4, kCodeE4m3>(bm)
+                       : ct == kCodeE5m2 ? mx_shared_exp<4, kCodeE5m2>(bm)
+                                         : mx_shared_exp<4, kCodeE2m1>(bm))
+                    : (ct == kCodeE4m3   ? mx_shared_exp<5, kCodeE4m3>(bm)
+                       : ct == kCodeE5m2 ? mx_shared_exp<5, kCodeE5m2>(bm)
+                                         : mx_shared_exp<5, kCodeE2m1>(bm));
                 const float inv = __uint_as_float((uint32_t)(127 - se) << 23);   // 2^-se
                 code = fp8_code_rt(ct, f[n] * inv);
                 scale = pow2f(se);
@@ -681,12 +699,16 @@ __global__ __launch_bounds__(kElemThreads) void scatter_elem_kernel(
                 lead = (h % kMxBlock) == 0;
                 sidx = h / kMxBlock;
             }
+            // E2M1: the even element of each pair writes both codes as one byte (H is even)
+            const uint32_t next = __shfl_down(code, 1, kWave);
             if (h >= H) continue;
+            const bool fp4 = ct == kCodeE2m1;
             for (int k = 0; k < K; ++k) {
                 const long long row = sk == kScalesPerExpert ? (k == pk ? row_of[pk] : -1)
                                                              : row_of[k];
                 if (row < 0) continue;
-                out[row * H + h] = (uint8_t)code;
+                if (!fp4) out[row * H + h] = (uint8_t)code;
+                else if ((h & 1) == 0) out[row * (H / 2) + h / 2] = (uint8_t)(code | (next << 4));
                 if (lead) {
                     if (e8m0) bscales[row * ns + sidx] = (uint8_t)sbyte;
                     else fscales[row * ns + sidx] = scale;

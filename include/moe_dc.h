@@ -54,7 +54,9 @@ typedef enum {
                                    E4M3 (modes 3, 4, 5)                                     */
     MOE_DTYPE_INT8 = 1,         /* modes 1, 2                                              */
     MOE_DTYPE_E4M3 = 2,         /* OCP E4M3 ("fn": bias 7, max 448); modes 2-5             */
-    MOE_DTYPE_E5M2 = 3          /* OCP E5M2 (bias 15, max 57344); modes 2-5                */
+    MOE_DTYPE_E5M2 = 3,         /* OCP E5M2 (bias 15, max 57344); modes 2-5                */
+    MOE_DTYPE_E2M1 = 4          /* OCP E2M1 fp4 (max 6), two codes per byte, the element of
+                                   even index in the low nibble; modes 4/5, H even          */
 } moe_dtype;
 
 /* Shape of the quantization scales tensor ([LLD] 约束说明: for mode 1 a scalar quant
@@ -93,7 +95,8 @@ typedef struct {
     int32_t expert_token_nums_type; /* 0 = running sum over local experts, 1 = counts         */
     int32_t mask_kind;              /* 0 none, 1 per token [W][BS], 2 per pick [W][BS][K]     */
     int32_t out_dtype;              /* moe_dtype: mode 0 DEFAULT only; mode 1 DEFAULT/INT8;
-                                       mode 2 any; modes 3-5 DEFAULT/E4M3/E5M2               */
+                                       mode 2 DEFAULT/INT8/E4M3/E5M2; mode 3 DEFAULT/E4M3/
+                                       E5M2; modes 4/5 DEFAULT/E4M3/E5M2/E2M1                */
     int32_t scales_kind;            /* moe_scales_kind: mode 1 SCALAR/SHARED/PER_EXPERT;
                                        modes 2, 3 any; modes 0, 4, 5 NONE                     */
     int32_t scale_format;           /* moe_scale_format: E8M0 only with modes 4/5            */
@@ -139,7 +142,8 @@ size_t moe_dc_dispatch_workspace_bytes(const moe_dc_config* cfg);
  *   mode 4  per 32-element block: shared_exp = floor(log2 max|x|) - emax, at least -127
  *           (emax 8 for E4M3, 15 for E5M2; an all-zero block takes -127)
  *   mode 5  per block: shared_exp = ceil(log2(max(max|x|, 1e-4) / type_max))
- *   modes 4/5: codes = fp8(x / 2^shared_exp); scale = 2^shared_exp (the dequant multiplier)
+ *   modes 4/5: codes = fp8(x / 2^shared_exp); scale = 2^shared_exp (the dequant multiplier);
+ *           E2M1 elements use emax 2 and type_max 6
  *
  * Inputs:
  *   x              bf16  [W][BS][H]   tokens of every source rank (finite values)
@@ -150,7 +154,8 @@ size_t moe_dc_dispatch_workspace_bytes(const moe_dc_config* cfg);
  *                  mask_kind is 0; nonzero = active.  An inactive pick is not dispatched.
  *   expert_scales  fp32 [W][BS][K] pick weights, or NULL; given iff expand_scales is
  * Outputs (row = a receiver row in the packed layout below; cap = expand_rows_capacity):
- *   expand_x       [cap][H] bf16 (mode 0), else one byte per element: int8 or fp8 codes
+ *   expand_x       [cap][H] bf16 (mode 0), [cap][H/2] bytes for E2M1 (two codes per byte),
+ *                  else [cap][H] bytes: int8 or fp8 codes
  *   dynamic_scales [cap][moe_dc_scales_per_row(cfg)] fp32 (or bytes with MOE_SCALE_E8M0):
  *                  mode 2 one 1/dyn per row; mode 3 one 1/dyn per group; modes 4/5 one scale
  *                  per 32-element block and 0 in the Align2 pad slot.  NULL allowed for

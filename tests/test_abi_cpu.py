@@ -44,6 +44,7 @@ def test_config_struct_layout_matches_header():
 def test_header_enum_values_match_the_binding():
     text = open(HEADER).read()
     for name in ("MOE_DTYPE_DEFAULT", "MOE_DTYPE_INT8", "MOE_DTYPE_E4M3", "MOE_DTYPE_E5M2",
+                 "MOE_DTYPE_E2M1",
                  "MOE_SCALES_NONE", "MOE_SCALES_SCALAR", "MOE_SCALES_SHARED",
                  "MOE_SCALES_PER_EXPERT", "MOE_SCALE_FP32", "MOE_SCALE_E8M0"):
         m = re.search(r"\b" + name + r"\s*=\s*(\d+)", text)
@@ -94,7 +95,10 @@ def test_valid_configs_of_the_workloads():
     (dict(quant_mode=1, out_dtype=2, scales_kind=1), cq.MOE_ERR_INVALID_ARG),
     (dict(quant_mode=3, out_dtype=1), cq.MOE_ERR_INVALID_ARG),
     (dict(quant_mode=4, out_dtype=1), cq.MOE_ERR_INVALID_ARG),
-    (dict(quant_mode=2, out_dtype=4), cq.MOE_ERR_INVALID_ARG),
+    (dict(quant_mode=2, out_dtype=4), cq.MOE_ERR_INVALID_ARG),      # fp4 only for MX
+    (dict(quant_mode=3, out_dtype=4), cq.MOE_ERR_INVALID_ARG),
+    (dict(quant_mode=4, out_dtype=4, H=1025), cq.MOE_ERR_INVALID_ARG),  # fp4 needs even H
+    (dict(quant_mode=5, out_dtype=5), cq.MOE_ERR_INVALID_ARG),
     (dict(quant_mode=4, scales_kind=2), cq.MOE_ERR_INVALID_ARG),
     (dict(quant_mode=0, scales_kind=1), cq.MOE_ERR_INVALID_ARG),
     (dict(quant_mode=2, scales_kind=4), cq.MOE_ERR_INVALID_ARG),
@@ -127,6 +131,7 @@ def test_k_may_count_special_experts():
     dict(quant_mode=2, out_dtype=2, scales_kind=2), dict(quant_mode=2, out_dtype=3),
     dict(quant_mode=3), dict(quant_mode=3, out_dtype=3, scales_kind=3),
     dict(quant_mode=4, out_dtype=3, scale_format=1), dict(quant_mode=5, scale_format=1),
+    dict(quant_mode=4, out_dtype=4), dict(quant_mode=5, out_dtype=4, scale_format=1, H=1030),
 ])
 def test_quant_variants_validate(kw):
     assert cq.moe_dc_validate(_cfg(**kw)) == cq.MOE_OK, cq.moe_dc_last_error()

@@ -68,6 +68,17 @@ VARIANTS = {
                         scale_format=1),
     "mxclip_e5m2_e8m0_h1030": WL("mxclip_e5m2_e8m0_h1030", W=2, E=8, BS=33, H=1030, K=3,
                                  quant_mode=5, out_dtype=3, scale_format=1),
+    # MX with E2M1 (fp4) elements, two codes per byte
+    "mx_e2m1": WL("mx_e2m1", W=3, E=12, BS=77, H=1032, K=5, quant_mode=4, out_dtype=4,
+                  routing="zipf"),
+    "mxclip_e2m1_e8m0_special": WL("mxclip_e2m1_e8m0_special", W=4, E=64, BS=70, H=2048,
+                                   K=16, quant_mode=5, out_dtype=4, scale_format=1,
+                                   zero_expert_num=2, copy_expert_num=2, mask_kind=2,
+                                   inactive_tokens_per_rank=7),
+    "mx_e2m1_h1030": WL("mx_e2m1_h1030", W=2, E=8, BS=33, H=1030, K=3, quant_mode=4,
+                        out_dtype=4),
+    "mxclip_e2m1_h1030": WL("mxclip_e2m1_h1030", W=2, E=8, BS=33, H=1030, K=3,
+                            quant_mode=5, out_dtype=4, scale_format=1),
 }
 
 
@@ -117,6 +128,28 @@ def test_exhaustive_e5m2_via_rows(mode):
     x = np.concatenate([b, np.zeros(n_tok * H - len(b), np.uint16)]).reshape(1, n_tok, H)
     x = np.ascontiguousarray(np.concatenate([x, x[:, ::-1]], axis=0))
     wl = WL("e5m2_sweep", W=2, E=2, BS=n_tok, H=H, K=1, quant_mode=mode, out_dtype=3)
+    ids = np.zeros((2, n_tok, 1), np.int32)
+    inp = dict(x=x, expert_ids=ids)
+    _, ref = harness.oracle_dispatch(wl, inp)
+    out = cq.dispatch(harness.lib_cfg(wl), harness.bf16_dev(x), harness.to_dev(ids))
+    torch.cuda.synchronize()
+    harness.compare_dispatch(wl, inp, out, ref)
+
+
+@pytest.mark.parametrize("mode", [4, 5])
+def test_exhaustive_e2m1_via_rows(mode):
+    """All finite bf16 patterns as token elements, coded as E2M1 under both MX modes."""
+    import torch
+    import combine_quant_amd as cq
+    b = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    f = workloads.bf16_bits_to_f32(b)
+    b = b[np.isfinite(f)]
+    b = np.random.default_rng(10 + mode).permutation(b)
+    H = 1024
+    n_tok = (len(b) + H - 1) // H
+    x = np.concatenate([b, np.zeros(n_tok * H - len(b), np.uint16)]).reshape(1, n_tok, H)
+    x = np.ascontiguousarray(np.concatenate([x, x[:, ::-1]], axis=0))
+    wl = WL("e2m1_sweep", W=2, E=2, BS=n_tok, H=H, K=1, quant_mode=mode, out_dtype=4)
     ids = np.zeros((2, n_tok, 1), np.int32)
     inp = dict(x=x, expert_ids=ids)
     _, ref = harness.oracle_dispatch(wl, inp)

@@ -123,6 +123,9 @@ C3_E5M2_E8M0 = C3.replace(
     name="c3v_w16_mx_e5m2_e8m0", out_dtype=3, scale_format=1,
     description="C3 with MX E5M2 elements and E8M0 scale bytes (the SMP article's stored "
                 "format)")
+C3_MXFP4 = C3.replace(
+    name="c3v_w16_mxfp4_e8m0", out_dtype=4, scale_format=1,
+    description="C3 with MX E2M1 (fp4) elements, two per byte, and E8M0 scale bytes")
 C4_STATIC = C4.replace(
     name="c4v_w16_static_int8_shared", quant_mode=1, scales_kind=2,
     description="C4 with static int8 quantization, one shared [H] coefficient row "
@@ -175,7 +178,7 @@ SAMPLE_BS256_Q = SAMPLE_BS8_Q.replace(
 WORKLOADS = {w.name: w for w in (C1_MODE0, C1_MODE2, C2, C3, C4, C5, C3_E5M2_E8M0, C4_STATIC,
                                  C4_TOKEN_E4M3, C4_GROUP, C2_GROUP_SMOOTH, C4_COMBINE_INT8,
                                  C4_SCATTER_SHARED, C4_SMOOTH, SAMPLE_BS8, SAMPLE_BS8_Q,
-                                 SAMPLE_BS256, SAMPLE_BS256_Q)}
+                                 SAMPLE_BS256, SAMPLE_BS256_Q, C3_MXFP4)}
 
 
 def _streams(seed: int):
