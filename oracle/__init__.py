@@ -55,6 +55,7 @@ def _load():
             "oracle_combine_dequant_row": (None, [P, P, i32, P]),
             "oracle_combine_quantize": (i32, [P] * 5),
             "oracle_combine_int8": (i32, [P] * 13),
+            "oracle_combine_int8_token": (i32, [P] * 10 + [i32, i32, P, P, P]),
             "oracle_expand_scales": (i32, [P] * 5),
             "oracle_combine_scatter": (i32, [P] * 12),
             "oracle_mx_scale_count": (i32, [i32]),
@@ -400,4 +401,27 @@ def combine_scatter(cfg, expert_out, assist_info, recv_offsets, expert_ids, expe
                                         _p(m), _p(ox), _p(sx), _p(y), _p(window), _p(acc))
     if rc != 0:
         raise ValueError(f"oracle_combine_scatter rejected the input (rc={rc})")
+    return y
+
+
+def combine_int8_token(cfg, codes, scales, expert_ids, expand_idx, expert_scales,
+                       ep_recv_count, recv_offsets, s, i, mask=None, ori_x=None):
+    """The int8 combine for one source token (s, i)."""
+    q = _c(codes, np.int8)
+    sc = _c(scales, np.float32)
+    ids = _c(expert_ids, np.int32)
+    eidx = _c(expand_idx, np.int32)
+    w = _c(expert_scales, np.float32)
+    erc = _c(ep_recv_count, np.int32)
+    off = _c(recv_offsets, np.int64)
+    m = _c(mask, np.uint8)
+    ox = _c(ori_x, np.uint16)
+    y = np.empty(cfg.H, np.uint16)
+    acc = np.empty(cfg.H, np.float32)
+    row = np.empty(cfg.H, np.float32)
+    rc = _load().oracle_combine_int8_token(_ref(cfg), _p(q), _p(sc), _p(ids), _p(eidx), _p(w),
+                                           _p(erc), _p(off), _p(m), _p(ox), int(s), int(i),
+                                           _p(acc), _p(row), _p(y))
+    if rc != 0:
+        raise ValueError(f"oracle_combine_int8_token rejected the input (rc={rc})")
     return y

@@ -783,49 +783,64 @@ int32_t oracle_combine_quantize(const oracle_cfg* c, const uint16_t* expert_out,
     return 0;
 }
 
+int32_t oracle_combine_int8_token(const oracle_cfg* c, const int8_t* codes, const float* scales,
+                                  const int32_t* expert_ids, const int32_t* expand_idx,
+                                  const float* expert_scales, const int32_t* ep_recv_count,
+                                  const int64_t* recv_offsets, const uint8_t* mask,
+                                  const uint16_t* ori_x, int32_t s, int32_t i, float* acc,
+                                  float* rowbuf, uint16_t* y_row)
+{
+    const int32_t H = c->H, nb = oracle_combine_block_count(H);
+    const int32_t zero_end = c->E + c->zero_expert_num;
+    const int32_t copy_end = zero_end + c->copy_expert_num;
+    for (int32_t h = 0; h < H; ++h) acc[h] = 0.0f;
+    for (int32_t k = 0; k < c->K; ++k) {
+        size_t p = ((size_t)s * c->BS + i) * c->K + k;
+        if (!pair_active(c, mask, s, i, k)) continue;
+        int32_t e = expert_ids[p];
+        float w = expert_scales[p];
+        if (e < 0 || e >= copy_end) return -1;
+        if (e < c->E) {
+            int32_t ord = expand_idx[p];
+            if (ord < 0) return -1;
+            int64_t row = oracle_dest_row(c, ep_recv_count, recv_offsets, s, e, ord);
+            oracle_combine_dequant_row(codes + (size_t)row * H, scales + (size_t)row * nb, H,
+                                       rowbuf);
+            for (int32_t h = 0; h < H; ++h) {
+                float t = w * rowbuf[h];
+                acc[h] = acc[h] + t;
+            }
+        } else if (e >= zero_end) {
+            if (ori_x == NULL) return -1;
+            const uint16_t* src = ori_x + ((size_t)s * c->BS + i) * H;
+            for (int32_t h = 0; h < H; ++h) {
+                float t = w * oracle_bf16_to_f32(src[h]);
+                acc[h] = acc[h] + t;
+            }
+        }
+    }
+    for (int32_t h = 0; h < H; ++h) y_row[h] = oracle_f32_to_bf16(acc[h]);
+    return 0;
+}
+
 /* The combine of oracle_combine_token with each routed pick's row dequantized first: the
  * same addressing ([DDD] §3.4.2), the same fp32 sum in k order of w * row, zero experts
  * adding nothing and copy experts adding w * ori_x (reading R28: ori_x stays on its source
- * rank, so it is never quantized); the result rounded to bf16. */
+ * rank, so it is never quantized); the result rounded to bf16.  Token by token through
+ * oracle_combine_int8_token. */
 int32_t oracle_combine_int8(const oracle_cfg* c, const int8_t* codes, const float* scales,
                             const int32_t* expert_ids, const int32_t* expand_idx,
                             const float* expert_scales, const int32_t* ep_recv_count,
                             const int64_t* recv_offsets, const uint8_t* mask,
                             const uint16_t* ori_x, uint16_t* y, float* acc, float* rowbuf)
 {
-    const int32_t H = c->H, nb = oracle_combine_block_count(H);
-    const int32_t zero_end = c->E + c->zero_expert_num;
-    const int32_t copy_end = zero_end + c->copy_expert_num;
     for (int32_t s = 0; s < c->W; ++s)
         for (int32_t i = 0; i < c->BS; ++i) {
-            for (int32_t h = 0; h < H; ++h) acc[h] = 0.0f;
-            for (int32_t k = 0; k < c->K; ++k) {
-                size_t p = ((size_t)s * c->BS + i) * c->K + k;
-                if (!pair_active(c, mask, s, i, k)) continue;
-                int32_t e = expert_ids[p];
-                float w = expert_scales[p];
-                if (e < 0 || e >= copy_end) return -1;
-                if (e < c->E) {
-                    int32_t ord = expand_idx[p];
-                    if (ord < 0) return -1;
-                    int64_t row = oracle_dest_row(c, ep_recv_count, recv_offsets, s, e, ord);
-                    oracle_combine_dequant_row(codes + (size_t)row * H,
-                                               scales + (size_t)row * nb, H, rowbuf);
-                    for (int32_t h = 0; h < H; ++h) {
-                        float t = w * rowbuf[h];
-                        acc[h] = acc[h] + t;
-                    }
-                } else if (e >= zero_end) {
-                    if (ori_x == NULL) return -1;
-                    const uint16_t* src = ori_x + ((size_t)s * c->BS + i) * H;
-                    for (int32_t h = 0; h < H; ++h) {
-                        float t = w * oracle_bf16_to_f32(src[h]);
-                        acc[h] = acc[h] + t;
-                    }
-                }
-            }
-            uint16_t* yr = y + ((size_t)s * c->BS + i) * H;
-            for (int32_t h = 0; h < H; ++h) yr[h] = oracle_f32_to_bf16(acc[h]);
+            int32_t rc = oracle_combine_int8_token(c, codes, scales, expert_ids, expand_idx,
+                                                   expert_scales, ep_recv_count, recv_offsets,
+                                                   mask, ori_x, s, i, acc, rowbuf,
+                                                   y + ((size_t)s * c->BS + i) * c->H);
+            if (rc != 0) return rc;
         }
     return 0;
 }

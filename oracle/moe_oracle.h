@@ -106,6 +106,12 @@ void oracle_combine_quant_row(const uint16_t* row, int32_t H, int8_t* q, float* 
 void oracle_combine_dequant_row(const int8_t* q, const float* scales, int32_t H, float* out);
 int32_t oracle_combine_quantize(const oracle_cfg* c, const uint16_t* expert_out,
                                 const int64_t* recv_offsets, int8_t* codes, float* scales);
+int32_t oracle_combine_int8_token(const oracle_cfg* c, const int8_t* codes, const float* scales,
+                                  const int32_t* expert_ids, const int32_t* expand_idx,
+                                  const float* expert_scales, const int32_t* ep_recv_count,
+                                  const int64_t* recv_offsets, const uint8_t* mask,
+                                  const uint16_t* ori_x, int32_t s, int32_t i,
+                                  float* acc_scratch, float* row_scratch, uint16_t* y_row);
 int32_t oracle_combine_int8(const oracle_cfg* c, const int8_t* codes, const float* scales,
                             const int32_t* expert_ids, const int32_t* expand_idx,
                             const float* expert_scales, const int32_t* ep_recv_count,

@@ -223,3 +223,19 @@ def test_int8_combine_close_to_the_bf16_combine():
                 bound[s, i] += abs(float(inp["expert_scales"][s, i, k])) * (0.5 + 2.0 ** -5) * step
     bf16_ulp = 2.0 ** -7 * np.maximum(np.abs(y16), np.abs(y8))
     assert (np.abs(y8 - y16) <= bound + 2 * bf16_ulp + 1e-30).all()
+
+
+def test_token_version_equals_the_whole_buffer_version():
+    wl, cfg, inp, d = _dispatch_tiny(6, zero_expert_num=1, copy_expert_num=1, mask_kind=2,
+                                     inactive_tokens_per_rank=2, routing="randint")
+    eo = workloads.f32_to_bf16_bits(np.random.default_rng(8).standard_normal(
+        (wl.cap, wl.H)).astype(np.float32))
+    codes, scales = oracle.combine_quantize(cfg, eo, d["recv_offsets"])
+    args = (inp["expert_ids"], d["expand_idx"], inp["expert_scales"], d["ep_recv_count"],
+            d["recv_offsets"])
+    y = oracle.combine_int8(cfg, codes, scales, *args, mask=inp["mask"], ori_x=inp["x"])
+    for s in range(wl.W):
+        for i in range(wl.BS):
+            yt = oracle.combine_int8_token(cfg, codes, scales, *args, s, i, mask=inp["mask"],
+                                           ori_x=inp["x"])
+            assert (yt == y[s, i]).all()
