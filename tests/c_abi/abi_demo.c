@@ -1,0 +1,193 @@
+/*
+ * abi_demo.c -- a plain C11 consumer of libmoe_dc (include/moe_dc.h), linked against the HIP
+ * runtime only: no Python, no C++.  It checks the library end to end with invariants that
+ * need no reference implementation, then times dispatch + combine launched from native code.
+ *
+ * usage: abi_demo W E BS H K iters
+ *
+ * Inputs: x[s][i][h] = small integers / 64 (exact in bf16); each token picks K distinct experts
+ * (a seeded linear congruential generator); weights 1/K with K a power of two.  Dispatch runs
+ * without quantization, so the identity "expert" is expand_x itself, and the combine of K
+ * copies of x weighted 1/K must return x bit for bit.
+ * Checks: every status is MOE_OK; recv_offsets[W] = W*BS*K (nothing masked, no special
+ * experts) = the sum of expert_token_nums (type 1); every expand_x row holds the bf16 row of
+ * the token its assist_info triple names, and every pick appears exactly once; y == x.
+ * Prints "ok routed=<rows> step_us=<mean>" and exits 0, or prints the failure and exits 1.
+ */
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "moe_dc.h"
+
+#define HIP_OK(call)                                                                      \
+    do {                                                                                  \
+        hipError_t e_ = (call);                                                           \
+        if (e_ != hipSuccess) {                                                           \
+            printf("hip error %s at line %d\n", hipGetErrorString(e_), __LINE__);        \
+            return 1;                                                                     \
+        }                                                                                 \
+    } while (0)
+
+#define MOE_OK_OR_FAIL(call)                                                              \
+    do {                                                                                  \
+        moe_status st_ = (call);                                                          \
+        if (st_ != MOE_OK) {                                                              \
+            printf("moe status %d at line %d: %s\n", (int)st_, __LINE__, moe_dc_last_error()); \
+            return 1;                                                                     \
+        }                                                                                 \
+    } while (0)
+
+static uint32_t lcg_state = 12345u;
+static uint32_t lcg(void)
+{
+    lcg_state = lcg_state * 1664525u + 1013904223u;
+    return lcg_state >> 8;
+}
+
+/* bf16 pattern of a float that bf16 holds exactly (the low 16 bits are zero) */
+static uint16_t bf16_of(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+int main(int argc, char** argv)
+{
+    if (argc != 7) {
+        printf("usage: abi_demo W E BS H K iters\n");
+        return 1;
+    }
+    const int W = atoi(argv[1]), E = atoi(argv[2]), BS = atoi(argv[3]), H = atoi(argv[4]);
+    const int K = atoi(argv[5]), iters = atoi(argv[6]);
+    if ((K & (K - 1)) != 0 || K > E) {
+        printf("K must be a power of two and at most E\n");
+        return 1;
+    }
+    moe_dc_config cfg;
+    memset(&cfg, 0, sizeof cfg);
+    cfg.ep_world_size = W;
+    cfg.moe_expert_num = E;
+    cfg.bs = BS;
+    cfg.hidden = H;
+    cfg.topk = K;
+    cfg.quant_mode = 0;
+    cfg.expert_token_nums_type = 1;
+    cfg.expand_rows_capacity = (int64_t)W * BS * K;
+    MOE_OK_OR_FAIL(moe_dc_validate(&cfg));
+    const size_t T = (size_t)W * BS, cap = (size_t)cfg.expand_rows_capacity, L = (size_t)E / W;
+    const size_t ws_bytes = moe_dc_dispatch_workspace_bytes(&cfg);
+    if (ws_bytes == 0 || moe_dc_scales_per_row(&cfg) != 0) {
+        printf("unexpected workspace or scale count\n");
+        return 1;
+    }
+
+    uint16_t* x = malloc(T * H * sizeof(uint16_t));
+    int32_t* ids = malloc(T * K * sizeof(int32_t));
+    float* w = malloc(T * K * sizeof(float));
+    for (size_t n = 0; n < T * H; ++n) x[n] = bf16_of((float)((int)(lcg() % 2001) - 1000) / 64.0f);
+    for (size_t t = 0; t < T; ++t)
+        for (int k = 0; k < K; ++k) {
+            int e, dup;
+            do {                                       /* K distinct experts per token */
+                e = (int)(lcg() % (uint32_t)E);
+                dup = 0;
+                for (int j = 0; j < k; ++j) dup |= ids[t * K + j] == e;
+            } while (dup);
+            ids[t * K + k] = e;
+            w[t * K + k] = 1.0f / (float)K;
+        }
+
+    void *dx, *dids, *dw, *dex, *deidx, *dai, *derc, *detn, *droff, *dws, *dy;
+    HIP_OK(hipMalloc(&dx, T * H * 2));
+    HIP_OK(hipMalloc(&dids, T * K * 4));
+    HIP_OK(hipMalloc(&dw, T * K * 4));
+    HIP_OK(hipMalloc(&dex, cap * H * 2));
+    HIP_OK(hipMalloc(&deidx, T * K * 4));
+    HIP_OK(hipMalloc(&dai, cap * 3 * 4));
+    HIP_OK(hipMalloc(&derc, (size_t)W * L * W * 4));
+    HIP_OK(hipMalloc(&detn, (size_t)W * L * 8));
+    HIP_OK(hipMalloc(&droff, (size_t)(W + 1) * 8));
+    HIP_OK(hipMalloc(&dws, ws_bytes));
+    HIP_OK(hipMalloc(&dy, T * H * 2));
+    HIP_OK(hipMemcpy(dx, x, T * H * 2, hipMemcpyHostToDevice));
+    HIP_OK(hipMemcpy(dids, ids, T * K * 4, hipMemcpyHostToDevice));
+    HIP_OK(hipMemcpy(dw, w, T * K * 4, hipMemcpyHostToDevice));
+    hipStream_t stream;
+    HIP_OK(hipStreamCreate(&stream));
+
+    /* one round trip, checked */
+    MOE_OK_OR_FAIL(moe_dispatch(&cfg, dx, dids, NULL, NULL, NULL, dex, NULL, deidx, dai, derc,
+                                detn, droff, NULL, dws, ws_bytes, stream));
+    MOE_OK_OR_FAIL(moe_combine(&cfg, dex, dids, deidx, dw, derc, droff, NULL, NULL, dy, stream));
+    HIP_OK(hipStreamSynchronize(stream));
+
+    int64_t* roff = malloc((size_t)(W + 1) * 8);
+    int64_t* etn = malloc((size_t)W * L * 8);
+    int32_t* ai = malloc(cap * 3 * 4);
+    uint16_t* ex = malloc(cap * H * 2);
+    uint16_t* y = malloc(T * H * 2);
+    HIP_OK(hipMemcpy(roff, droff, (size_t)(W + 1) * 8, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(etn, detn, (size_t)W * L * 8, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(ai, dai, cap * 3 * 4, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(ex, dex, cap * H * 2, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(y, dy, T * H * 2, hipMemcpyDeviceToHost));
+
+    const int64_t P = roff[W];
+    int64_t etn_sum = 0;
+    for (size_t n = 0; n < (size_t)W * L; ++n) etn_sum += etn[n];
+    if (P != (int64_t)(T * K) || etn_sum != P) {
+        printf("routed rows %lld, expert_token_nums sum %lld, want %zu\n", (long long)P,
+               (long long)etn_sum, T * K);
+        return 1;
+    }
+    unsigned char* seen = calloc(T * K, 1);
+    for (int64_t r = 0; r < P; ++r) {
+        const int s = ai[r * 3], i = ai[r * 3 + 1], k = ai[r * 3 + 2];
+        if (s < 0 || s >= W || i < 0 || i >= BS || k < 0 || k >= K) {
+            printf("row %lld: bad triple\n", (long long)r);
+            return 1;
+        }
+        const size_t p = ((size_t)s * BS + i) * K + k;
+        if (seen[p]++) {
+            printf("pick %zu stored twice\n", p);
+            return 1;
+        }
+        if (memcmp(ex + (size_t)r * H, x + ((size_t)s * BS + i) * H, (size_t)H * 2) != 0) {
+            printf("row %lld does not hold its token\n", (long long)r);
+            return 1;
+        }
+    }
+    if (memcmp(y, x, T * H * 2) != 0) {
+        printf("combine of K copies weighted 1/K is not x\n");
+        return 1;
+    }
+
+    /* native launch timing: dispatch + combine, eager, on one stream */
+    hipEvent_t a, b;
+    HIP_OK(hipEventCreate(&a));
+    HIP_OK(hipEventCreate(&b));
+    for (int n = 0; n < 3; ++n) {
+        MOE_OK_OR_FAIL(moe_dispatch(&cfg, dx, dids, NULL, NULL, NULL, dex, NULL, deidx, dai,
+                                    derc, detn, droff, NULL, dws, ws_bytes, stream));
+        MOE_OK_OR_FAIL(moe_combine(&cfg, dex, dids, deidx, dw, derc, droff, NULL, NULL, dy,
+                                   stream));
+    }
+    HIP_OK(hipEventRecord(a, stream));
+    for (int n = 0; n < iters; ++n) {
+        MOE_OK_OR_FAIL(moe_dispatch(&cfg, dx, dids, NULL, NULL, NULL, dex, NULL, deidx, dai,
+                                    derc, detn, droff, NULL, dws, ws_bytes, stream));
+        MOE_OK_OR_FAIL(moe_combine(&cfg, dex, dids, deidx, dw, derc, droff, NULL, NULL, dy,
+                                   stream));
+    }
+    HIP_OK(hipEventRecord(b, stream));
+    HIP_OK(hipEventSynchronize(b));
+    float ms = 0.0f;
+    HIP_OK(hipEventElapsedTime(&ms, a, b));
+    printf("ok routed=%lld step_us=%.2f version=%s\n", (long long)P, 1000.0f * ms / iters,
+           moe_dc_version());
+    return 0;
+}
