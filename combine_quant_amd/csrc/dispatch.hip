@@ -297,6 +297,7 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
             for (int w = 0; w < nw; ++w) amax = amax > red[0][w] ? amax : red[0][w];
             dyn_tok = type_max<CT>() / __uint_as_float(amax);
         }
+        uint32_t fp4_words[kTileSlots];     // E2M1: this lane's eight codes, per slot
 #pragma unroll
         for (int n = 0; n < kTileSlots; ++n) {
             const int v = lane + (wave * kTileSlots + n) * kWave;
@@ -323,6 +324,7 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
                     uint32_t w = 0;
 #pragma unroll
                     for (int q = 0; q < 8; ++q) w |= c[q] << (4 * q);
+                    fp4_words[n] = w;
                     packed = make_uint2(w, 0u);
                 } else {
                     packed = pack_codes8(c);
@@ -333,11 +335,14 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
 #pragma unroll
             for (int k = 0; k < kMaxK; ++k) {
                 if (rows[k] < 0) continue;
-                if (CT == kCodeE2m1)
-                    __builtin_nontemporal_store(
-                        packed.x, reinterpret_cast<uint32_t*>(expand_x) + (long long)rows[k] * NV + v);
-                else
+                if (CT == kCodeE2m1) {
+                    if (NV & 1)                   // odd vector count: 4-byte stores
+                        __builtin_nontemporal_store(
+                            packed.x,
+                            reinterpret_cast<uint32_t*>(expand_x) + (long long)rows[k] * NV + v);
+                } else {
                     store_stream(out + (long long)rows[k] * NV + v, packed);
+                }
                 if (MODE == 3 && (v & (kGroup / 8 - 1)) == 0)
                     fscales[(long long)rows[k] * ns + (v >> 4)] = scale;
                 if (MODE >= 4 && (v & 3) == 0) {
@@ -347,6 +352,24 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
                     else
                         fscales[(long long)rows[k] * ns + (v >> 2)] = scale;
                 }
+            }
+        }
+        if (CT == kCodeE2m1 && (NV & 1) == 0) {
+            // The wave's two slots hold vectors [wave * 128, wave * 128 + 128); lane l writes
+            // vectors 2l and 2l + 1 (from slot l / 32) as one 8-byte store, so each store
+            // instruction covers 512 contiguous bytes.
+            const int src = (2 * lane) & (kWave - 1);
+            const uint32_t a0 = __shfl(fp4_words[0], src, kWave);
+            const uint32_t b0 = __shfl(fp4_words[0], src + 1, kWave);
+            const uint32_t a1 = __shfl(fp4_words[1], src, kWave);
+            const uint32_t b1 = __shfl(fp4_words[1], src + 1, kWave);
+            const uint2 pair = lane < kWave / 2 ? make_uint2(a0, b0) : make_uint2(a1, b1);
+            const int vpair = wave * kTileSlots * kWave + 2 * lane;
+            if (vpair < NV) {
+#pragma unroll
+                for (int k = 0; k < kMaxK; ++k)
+                    if (rows[k] >= 0)
+                        store_stream(out + ((long long)rows[k] * NV + vpair) / 2, pair);
             }
         }
         if (MODE == 2 && threadIdx.x == 0) {

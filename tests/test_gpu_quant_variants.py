@@ -75,6 +75,9 @@ VARIANTS = {
                                    K=16, quant_mode=5, out_dtype=4, scale_format=1,
                                    zero_expert_num=2, copy_expert_num=2, mask_kind=2,
                                    inactive_tokens_per_rank=7),
+    # even vector count (8-byte paired stores) with a ragged last wave: 130 vectors
+    "mxclip_e2m1_e8m0_h1040": WL("mxclip_e2m1_e8m0_h1040", W=3, E=12, BS=45, H=1040, K=4,
+                                 quant_mode=5, out_dtype=4, scale_format=1),
     "mx_e2m1_h1030": WL("mx_e2m1_h1030", W=2, E=8, BS=33, H=1030, K=3, quant_mode=4,
                         out_dtype=4),
     "mxclip_e2m1_h1030": WL("mxclip_e2m1_h1030", W=2, E=8, BS=33, H=1030, K=3,
