@@ -18,6 +18,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEV
 MOE_DTYPE_DEFAULT, MOE_DTYPE_INT8, MOE_DTYPE_E4M3, MOE_DTYPE_E5M2, MOE_DTYPE_E2M1 = 0, 1, 2, 3, 4
 MOE_SCALES_NONE, MOE_SCALES_SCALAR, MOE_SCALES_SHARED, MOE_SCALES_PER_EXPERT = 0, 1, 2, 3
 MOE_SCALE_FP32, MOE_SCALE_E8M0 = 0, 1
+MOE_DC_FLAG_SEPARATE_ROUTE = 1
 _STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
            -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_DEVICE"}
 
@@ -44,7 +45,8 @@ class MoeDcConfig(ctypes.Structure):
         ("out_dtype", ctypes.c_int32),
         ("scales_kind", ctypes.c_int32),
         ("scale_format", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 2),
+        ("flags", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
         ("expand_rows_capacity", ctypes.c_int64),
     ]
 
@@ -108,11 +110,11 @@ def load_library(path: str = LIB) -> ctypes.CDLL:
 def make_config(W, E, BS, H, K, quant_mode=0, zero_expert_num=0, copy_expert_num=0,
                 const_expert_num=0, expert_token_nums_type=1, mask_kind=0, cap=None,
                 out_dtype=MOE_DTYPE_DEFAULT, scales_kind=MOE_SCALES_NONE,
-                scale_format=MOE_SCALE_FP32):
+                scale_format=MOE_SCALE_FP32, flags=0):
     cap = W * BS * K if cap is None else cap
     return MoeDcConfig(W, E, BS, H, K, quant_mode, zero_expert_num, copy_expert_num,
                        const_expert_num, expert_token_nums_type, mask_kind, out_dtype,
-                       scales_kind, scale_format, (ctypes.c_int32 * 2)(0, 0), cap)
+                       scales_kind, scale_format, flags, 0, cap)
 
 
 def code_type(cfg):

@@ -64,7 +64,9 @@ int32_t resolve_code_type(int32_t mode, int32_t out_dtype)
 moe_status check(const moe_dc_config* c, moe_dc::Shape* out)
 {
     if (!c) return fail(MOE_ERR_INVALID_ARG, "config is NULL");
-    if (c->reserved[0] != 0 || c->reserved[1] != 0)
+    if ((c->flags & ~MOE_DC_FLAG_SEPARATE_ROUTE) != 0)
+        return fail(MOE_ERR_INVALID_ARG, "flags has unknown bits (0x%x)", c->flags);
+    if (c->reserved != 0)
         return fail(MOE_ERR_INVALID_ARG, "reserved must be 0");
     if (c->ep_world_size < 2 || c->ep_world_size > 768)
         return fail(MOE_ERR_INVALID_ARG, "ep_world_size %d outside [2, 768]", c->ep_world_size);
@@ -211,16 +213,24 @@ moe_status moe_dispatch(const moe_dc_config* cfg, const void* x, const int32_t* 
     const bool vec = sh.H % 8 == 0 && aligned16(x) && aligned16(expand_x) &&
                      (!row_scales || aligned16(scales));
 
-    st = device_status(moe_dc::launch_route(sh, expert_ids, x_active_mask, expand_idx, seg, s),
-                       "route kernel launch");
-    if (st != MOE_OK) return st;
-    st = device_status(moe_dc::launch_scan(sh, seg, ep_recv_count, expert_token_nums,
-                                           recv_offsets, s),
-                       "scan kernel launch");
-    if (st != MOE_OK) return st;
+    // A small batch routes inside the scatter launch (one launch instead of three).
+    const bool fused = vec && (cfg->flags & MOE_DC_FLAG_SEPARATE_ROUTE) == 0 &&
+                       moe_dc::fused_route_fits(sh);
+    const moe_dc::FusedRoute fr{x_active_mask, ep_recv_count, expert_token_nums, recv_offsets};
+    if (!fused) {
+        st = device_status(
+            moe_dc::launch_route(sh, expert_ids, x_active_mask, expand_idx, seg, s),
+            "route kernel launch");
+        if (st != MOE_OK) return st;
+        st = device_status(moe_dc::launch_scan(sh, seg, ep_recv_count, expert_token_nums,
+                                               recv_offsets, s),
+                           "scan kernel launch");
+        if (st != MOE_OK) return st;
+    }
     st = device_status(moe_dc::launch_scatter(sh, x, expert_ids, expand_idx, seg, scales,
                                               expert_scales, expand_x, dynamic_scales,
-                                              assist_info, expand_scales, vec, s),
+                                              assist_info, expand_scales, vec,
+                                              fused ? &fr : nullptr, s),
                        "scatter kernel launch");
     if (st != MOE_OK) return st;
     return ok();
@@ -342,6 +352,6 @@ moe_status moe_combine_int8(const moe_dc_config* cfg, const int8_t* codes,
 
 const char* moe_dc_last_error(void) { return g_last_error.c_str(); }
 
-const char* moe_dc_version(void) { return "moe_dc 0.2.0 (gfx950)"; }
+const char* moe_dc_version(void) { return "moe_dc 0.3.0 (gfx950)"; }
 
 }  // extern "C"

@@ -49,13 +49,33 @@ hipError_t launch_route(const Shape& s, const int32_t* expert_ids, const uint8_t
 hipError_t launch_scan(const Shape& s, int32_t* seg, int32_t* ep_recv_count,
                        int64_t* expert_token_nums, int64_t* recv_offsets, hipStream_t stream);
 
+// Small batches route inside the scatter launch: every workgroup recomputes the counts and
+// their prefix sums in LDS (W*BS*K ids, E*W counters) instead of reading them from the route
+// and scan kernels.  The outputs those kernels would write are written by the scatter launch.
+struct FusedRoute {
+    const uint8_t* mask;
+    int32_t* ep_recv_count;
+    int64_t* expert_token_nums;
+    int64_t* recv_offsets;
+};
+constexpr long long kFusedMaxPicks = 1024;   // W*BS*K (measured crossover: 1024-2048)
+constexpr long long kFusedMaxCounts = 4096;  // E*W (LDS words)
+
+inline bool fused_route_fits(const Shape& s)
+{
+    return (long long)s.W * s.BS * s.K <= kFusedMaxPicks &&
+           (long long)s.E * s.W <= kFusedMaxCounts;
+}
+
 // Quantize and scatter every routed pick to its packed row, with scales and source triple.
-// expand_scales (nullable) receives each row's pick weight from expert_scales.
+// expand_scales (nullable) receives each row's pick weight from expert_scales.  With
+// `fused` (vectorized launches only) the launch also does the routing: expand_idx is then an
+// output and seg is not used.
 hipError_t launch_scatter(const Shape& s, const void* x, const int32_t* expert_ids,
-                          const int32_t* expand_idx, const int32_t* seg, const float* scales,
+                          int32_t* expand_idx, const int32_t* seg, const float* scales,
                           const float* expert_scales, void* expand_x, void* dynamic_scales,
                           int32_t* assist_info, float* expand_scales, bool vectorized,
-                          hipStream_t stream);
+                          const FusedRoute* fused, hipStream_t stream);
 
 // Weighted top-K gather.
 hipError_t launch_combine(const Shape& s, const void* expert_out, const int32_t* expert_ids,

@@ -172,29 +172,178 @@ __device__ __forceinline__ uint2 static_codes8(const float (&f)[8])
 
 constexpr int kTileSlots = 2;        // 64-vector slots (1 KiB of bf16 each) per wave
 constexpr int kMaxTileWaves = 8;     // H <= 8192: at most 1024 vectors = 16 slots
+constexpr int kFusedMinWaves = 4;    // workgroup size floor when the launch also routes
 
-// MODE 0..5, CT the code type, SK the scales kind.
-template <int MODE, int CT, int SK>
+// Small batches route inside the scatter launch (all picks fit in one pass of a workgroup).
+// Workgroup 0 produces the receive-side outputs; every other workgroup finds the packed rows
+// of its own token's picks by counting.  Counting commutes, so no result depends on the
+// order in which atomics land.
+
+// Workgroup 0: routed-pick counts per (expert e, source rank s') at ex[e*W + s'] in LDS,
+// their exclusive running total over that flat order (ex[E*W] = all routed rows), and from
+// it ep_recv_count, expert_token_nums and recv_offsets -- what the route and scan kernels
+// write for larger batches.
+__device__ void route_totals(const int32_t* __restrict__ ids, const FusedRoute& fr, int W,
+                             int E, int L, int BS, int K, int mask_kind, int etn_type,
+                             int32_t* ex, int32_t* wave_tot)
+{
+    const int t = threadIdx.x;
+    const int nt = blockDim.x;
+    const int N = E * W;
+    const int picks = W * BS * K;
+    for (int f = t; f < N; f += nt) ex[f] = 0;
+    __syncthreads();
+    for (int p = t; p < picks; p += nt) {
+        const int q = p / K;
+        const int32_t e = routed_expert(ids, fr.mask, mask_kind, K, E, q, p - q * K);
+        if (e >= 0) atomicAdd(&ex[e * W + q / BS], 1);
+    }
+    __syncthreads();
+    // exclusive running total in place: each thread scans one run of entries
+    const int per = (N + nt - 1) / nt;
+    const int lo = min(N, t * per);
+    const int hi = min(N, lo + per);
+    int32_t run = 0;
+    for (int f = lo; f < hi; ++f) run += ex[f];
+    const int32_t incl = block_inclusive_scan(run, wave_tot);
+    int32_t acc = incl - run;
+    for (int f = lo; f < hi; ++f) {
+        const int32_t cnt = ex[f];
+        ex[f] = acc;
+        acc += cnt;
+    }
+    if (t == nt - 1) ex[N] = incl;
+    __syncthreads();
+    // receiver r = e / L: ep_recv_count runs from the rank's first segment; recv_offsets[r]
+    // is the rank's first row; expert_token_nums counts per expert (type 1) or runs (type 0)
+    for (int f = t; f < N; f += nt) fr.ep_recv_count[f] = ex[f + 1] - ex[(f / W / L) * L * W];
+    for (int e = t; e < E; e += nt) {
+        const int first = (e / L) * L * W;
+        fr.expert_token_nums[e] = (int64_t)(ex[(e + 1) * W] - ex[etn_type == 0 ? first : e * W]);
+    }
+    for (int r = t; r <= W; r += nt) fr.recv_offsets[r] = ex[r * L * W];
+}
+
+// Picks each thread of a token workgroup counts: t, t + blockDim, ... (blockDim >= 256).
+constexpr int kFusedPicksPerThread = (int)(kFusedMaxPicks / (kWave * kFusedMinWaves));
+
+// The routed expert (or -1) of each pick this thread counts.  Called before the token row is
+// requested: loads complete in issue order, so using these values then does not wait for
+// the row.
+__device__ __forceinline__ void load_fused_picks(const int32_t* __restrict__ ids,
+                                                 const FusedRoute& fr, int E, int K,
+                                                 int mask_kind, int picks,
+                                                 int32_t (&pe)[kFusedPicksPerThread])
+{
+#pragma unroll
+    for (int j = 0; j < kFusedPicksPerThread; ++j) {
+        const int p2 = threadIdx.x + j * blockDim.x;
+        pe[j] = -1;
+        if (p2 < picks) {
+            const int q = p2 / K;
+            pe[j] = routed_expert(ids, fr.mask, mask_kind, K, E, q, p2 - q * K);
+        }
+    }
+}
+
+// Token workgroups: the packed row of pick k of token `tok` (source rank s) is its position in
+// the stable sort of all routed picks by (expert, source rank, token, pick), i.e. the number
+// of routed picks p2 with a smaller expert, or the same expert and p2 < tok*K + k in the
+// flat (rank, token, pick) order.  Its expand_idx counts only the same expert's picks of
+// rank s before it.  Threads k < K get the row of pick k (-1 when it is not routed, or past
+// `cap`) and write its expand_idx.
+__device__ int32_t route_own_rows(const int32_t* __restrict__ ids, const FusedRoute& fr,
+                                  int E, int BS, int K, int mask_kind, int tok, int s,
+                                  long long cap, const int32_t (&pe)[kFusedPicksPerThread],
+                                  int32_t* row_lds, int32_t* ord_lds,
+                                  int32_t* __restrict__ expand_idx)
+{
+    const int t = threadIdx.x;
+    const int nt = blockDim.x;
+    const int own = tok * K;
+    const int rank_lo = s * BS * K;
+    if (t < kMaxK) {
+        row_lds[t] = 0;
+        ord_lds[t] = 0;
+    }
+    int32_t mine[kMaxK];
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k)
+        mine[k] = k < K ? routed_expert(ids, fr.mask, mask_kind, K, E, tok, k) : -1;
+    uint32_t before[kMaxK], same[kMaxK];
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k) before[k] = same[k] = 0;
+#pragma unroll
+    for (int j = 0; j < kFusedPicksPerThread; ++j) {
+        const int p2 = t + j * nt;
+        const int32_t e2 = pe[j];
+        if (e2 < 0) continue;
+#pragma unroll
+        for (int k = 0; k < kMaxK; ++k) {
+            const bool earlier = e2 == mine[k] && p2 < own + k;
+            before[k] += (e2 < mine[k] || earlier) ? 1u : 0u;
+            same[k] += (earlier && p2 >= rank_lo) ? 1u : 0u;
+        }
+    }
+    __syncthreads();                                      // row_lds / ord_lds cleared
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k) {
+        if (k < K) {                                       // uniform
+            const uint32_t b = wave_sum_u32(before[k]);
+            const uint32_t o = wave_sum_u32(same[k]);
+            if ((t & (kWave - 1)) == 0) {
+                if (b != 0) atomicAdd(&row_lds[k], (int32_t)b);
+                if (o != 0) atomicAdd(&ord_lds[k], (int32_t)o);
+            }
+        }
+    }
+    __syncthreads();
+    int32_t row = -1;
+    if (t < K) {
+        const bool routed = routed_expert(ids, fr.mask, mask_kind, K, E, tok, t) >= 0;
+        expand_idx[own + t] = routed ? ord_lds[t] : -1;
+        if (routed && row_lds[t] < cap) row = row_lds[t];
+    }
+    return row;
+}
+
+// MODE 0..5, CT the code type, SK the scales kind.  FUSED: the launch also routes, with one
+// extra workgroup (0, route_totals; E*W + 1 words of dynamic LDS) before the token
+// workgroups (route_own_rows); a separate instantiation, so the large-batch kernels keep
+// their register budget.
+template <int MODE, int CT, int SK, bool FUSED>
 __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
-    const int32_t* __restrict__ expand_idx, const int32_t* __restrict__ seg,
+    int32_t* __restrict__ expand_idx, const int32_t* __restrict__ seg,
     const float* __restrict__ scales, const float* __restrict__ weights,
     void* __restrict__ expand_x, void* __restrict__ dyn_scales, int32_t* __restrict__ assist,
     float* __restrict__ expand_scales, int W, int E, int BS, int H, int K, int ns,
-    long long cap, int e8m0)
+    long long cap, int e8m0, FusedRoute fr, int L, int mask_kind, int etn_type)
 {
     __shared__ int32_t rows_lds[kMaxK];
     __shared__ int32_t exps_lds[kMaxK];
     __shared__ uint32_t red[2][kMaxTileWaves];
+    __shared__ int32_t ord_lds[kMaxK];
+    __shared__ int32_t fused_rows_lds[kMaxK];
+    __shared__ int32_t wave_tot[kMaxTileWaves];
+    extern __shared__ int32_t route_ex[];
+
+    if (FUSED && blockIdx.x == 0) {
+        route_totals(ids, fr, W, E, L, BS, K, mask_kind, etn_type, route_ex, wave_tot);
+        return;
+    }
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int nw = blockDim.x / kWave;
-    const long long tok = blockIdx.x;
+    const long long tok = FUSED ? blockIdx.x - 1 : blockIdx.x;
     const int s = (int)(tok / BS);
     const int i = (int)(tok - (long long)s * BS);
     const int NV = H >> 3;
     float* fscales = static_cast<float*>(dyn_scales);
+
+    int32_t fused_picks[kFusedPicksPerThread];
+    if (FUSED) load_fused_picks(ids, fr, E, K, mask_kind, W * BS * K, fused_picks);
 
     // 1. this wave's slots of the token row (and of a shared scales row), in flight before
     //    anything waits
@@ -215,15 +364,23 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
     }
     const float scalar_pre = SK == kScalesScalar ? scales[0] : 1.0f;
 
-    // 2. destination rows, resolved by threads 0..K-1
+    // 2. destination rows, resolved by threads 0..K-1 (small batches route here first)
+    int32_t fused_row = -1;
+    if (FUSED)
+        fused_row = route_own_rows(ids, fr, E, BS, K, mask_kind, (int)tok, s, cap,
+                                   fused_picks, fused_rows_lds, ord_lds, expand_idx);
     if (threadIdx.x < K) {
         const long long p = tok * K + threadIdx.x;
-        const int32_t ord = expand_idx[p];
         const int32_t e = ids[p];
         int32_t row = -1;
-        if (ord >= 0 && e >= 0 && e < E) {
-            const long long r = (long long)seg[(long long)e * W + s] + ord;
-            if (r < cap) row = (int32_t)r;
+        if (FUSED) {
+            row = fused_row;
+        } else {
+            const int32_t ord = expand_idx[p];
+            if (ord >= 0 && e >= 0 && e < E) {
+                const long long r = (long long)seg[(long long)e * W + s] + ord;
+                if (r < cap) row = (int32_t)r;
+            }
         }
         rows_lds[threadIdx.x] = row;
         exps_lds[threadIdx.x] = e;
@@ -478,7 +635,7 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
 struct ScatterArgs {
     const void* x;
     const int32_t* ids;
-    const int32_t* expand_idx;
+    int32_t* expand_idx;
     const int32_t* seg;
     const float* scales;
     const float* weights;
@@ -486,6 +643,7 @@ struct ScatterArgs {
     void* dyn_scales;
     int32_t* assist;
     float* expand_scales;
+    const FusedRoute* fused;    // null: routing comes from the route and scan kernels
 };
 
 template <int MODE, int CT, int SK>
@@ -493,12 +651,24 @@ hipError_t launch_tile_variant(const Shape& sh, const ScatterArgs& a, hipStream_
 {
     const long long T = (long long)sh.W * sh.BS;
     const int slots = ((sh.H >> 3) + kWave - 1) / kWave;
-    const int waves = (slots + kTileSlots - 1) / kTileSlots;        // <= kMaxTileWaves
-    hipLaunchKernelGGL((scatter_tile_kernel<MODE, CT, SK>), dim3((unsigned)T),
-                       dim3(kWave * waves), 0, stream, static_cast<const uint16_t*>(a.x), a.ids,
-                       a.expand_idx, a.seg, a.scales, a.weights, a.expand_x, a.dyn_scales,
-                       a.assist, a.expand_scales, sh.W, sh.E, sh.BS, sh.H, sh.K,
-                       sh.scales_per_row, (long long)sh.cap, sh.scale_e8m0);
+    int waves = (slots + kTileSlots - 1) / kTileSlots;              // <= kMaxTileWaves
+    size_t lds = 0;
+    FusedRoute fr{};
+    if (a.fused) {
+        fr = *a.fused;
+        if (waves < kFusedMinWaves) waves = kFusedMinWaves;
+        lds = ((size_t)sh.E * sh.W + 1) * sizeof(int32_t);
+    }
+#define MOE_DC_TILE_LAUNCH(F)                                                                   \
+    hipLaunchKernelGGL((scatter_tile_kernel<MODE, CT, SK, F>), dim3((unsigned)(T + (F ? 1 : 0))), \
+                       dim3(kWave * waves), lds, stream, static_cast<const uint16_t*>(a.x),     \
+                       a.ids, a.expand_idx, a.seg, a.scales, a.weights, a.expand_x,            \
+                       a.dyn_scales, a.assist, a.expand_scales, sh.W, sh.E, sh.BS, sh.H, sh.K, \
+                       sh.scales_per_row, (long long)sh.cap, sh.scale_e8m0, fr, sh.L,         \
+                       sh.mask_kind, sh.etn_type)
+    if (a.fused) MOE_DC_TILE_LAUNCH(true);
+    else MOE_DC_TILE_LAUNCH(false);
+#undef MOE_DC_TILE_LAUNCH
     return hipGetLastError();
 }
 
@@ -771,13 +941,15 @@ hipError_t launch_elem(const Shape& sh, const ScatterArgs& a, hipStream_t stream
 }  // namespace
 
 hipError_t launch_scatter(const Shape& sh, const void* x, const int32_t* expert_ids,
-                          const int32_t* expand_idx, const int32_t* seg, const float* scales,
+                          int32_t* expand_idx, const int32_t* seg, const float* scales,
                           const float* expert_scales, void* expand_x, void* dynamic_scales,
                           int32_t* assist_info, float* expand_scales, bool vectorized,
-                          hipStream_t stream)
+                          const FusedRoute* fused, hipStream_t stream)
 {
+    if (fused && (!vectorized || !fused_route_fits(sh))) return hipErrorInvalidValue;
     const ScatterArgs a{x,        expert_ids,     expand_idx,  seg,          scales,
-                        expert_scales, expand_x, dynamic_scales, assist_info, expand_scales};
+                        expert_scales, expand_x, dynamic_scales, assist_info, expand_scales,
+                        fused};
     return vectorized ? launch_tile(sh, a, stream) : launch_elem(sh, a, stream);
 }
 

@@ -174,23 +174,6 @@ __global__ __launch_bounds__(512) void route_kernel(
     }
 }
 
-// Inclusive scan of one int per thread across the workgroup (wave shuffles + LDS).
-__device__ __forceinline__ int32_t block_inclusive_scan(int32_t v, int32_t* wave_tot)
-{
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        int32_t o = __shfl_up(v, off, kWave);
-        if (lane >= off) v += o;
-    }
-    if (lane == kWave - 1) wave_tot[wave] = v;
-    __syncthreads();
-    int32_t before = 0;
-    for (int w = 0; w < wave; ++w) before += wave_tot[w];
-    return v + before;
-}
-
 // Receive-side scan when the W*E counts fit in LDS.  In the flat order f = e*W + s (expert
 // major, source minor) the exclusive running total ex[f] is exactly the first packed row of
 // segment (e, s), and every output is a difference of two entries of ex:

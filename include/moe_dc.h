@@ -77,6 +77,16 @@ typedef enum {
                                    scale as an E8M0 value)                                  */
 } moe_scale_format;
 
+/* Bits of moe_dc_config.flags. */
+typedef enum {
+    MOE_DC_FLAG_SEPARATE_ROUTE = 1  /* moe_dispatch always runs the routing and the prefix
+                                       sums as kernels of their own.  By default a small
+                                       batch (W*BS*K <= 1024 picks and E*W <= 4096, with the
+                                       vectorised scatter) computes them inside the scatter
+                                       launch instead, one launch in place of three; the
+                                       results are identical either way                    */
+} moe_dc_flag;
+
 /* Operator attributes ([OPS] 参数说明; [LLD] 约束说明).  One struct serves both calls; the
  * pages require the same values on every rank and for dispatch and its combine
  * ([OPS] 约束说明, cross-card consistency), which one struct gives for free.
@@ -100,7 +110,8 @@ typedef struct {
     int32_t scales_kind;            /* moe_scales_kind: mode 1 SCALAR/SHARED/PER_EXPERT;
                                        modes 2, 3 any; modes 0, 4, 5 NONE                     */
     int32_t scale_format;           /* moe_scale_format: E8M0 only with modes 4/5            */
-    int32_t reserved[2];            /* must be 0                                              */
+    int32_t flags;                  /* moe_dc_flag bits; 0 for the defaults                   */
+    int32_t reserved;               /* must be 0                                              */
     int64_t expand_rows_capacity;   /* rows of expand_x / dynamic_scales / assist_info and of
                                        expert_out; must be >= W*BS*K                           */
 } moe_dc_config;
@@ -152,7 +163,8 @@ size_t moe_dc_dispatch_workspace_bytes(const moe_dc_config* cfg);
  *                  scales_kind is MOE_SCALES_NONE
  *   x_active_mask  uint8 [W][BS] (mask_kind 1) or [W][BS][K] (mask_kind 2), or NULL when
  *                  mask_kind is 0; nonzero = active.  An inactive pick is not dispatched.
- *   expert_scales  fp32 [W][BS][K] pick weights, or NULL; given iff expand_scales is
+ *   expert_scales  fp32 [W][BS][K] pick weights, or NULL; given exactly when expand_scales
+ *                  is given (each routed row then carries its pick's weight)
  * Outputs (row = a receiver row in the packed layout below; cap = expand_rows_capacity):
  *   expand_x       [cap][H] bf16 (mode 0), [cap][H/2] bytes for E2M1 (two codes per byte),
  *                  else [cap][H] bytes: int8 or fp8 codes

@@ -21,14 +21,15 @@ def oracle_cfg(wl: workloads.Workload, etn_type=None):
                            scales_kind=wl.scales_kind, scale_format=wl.scale_format)
 
 
-def lib_cfg(wl: workloads.Workload, cap=None):
+def lib_cfg(wl: workloads.Workload, cap=None, flags=0):
     import combine_quant_amd as cq
     return cq.make_config(wl.W, wl.E, wl.BS, wl.H, wl.K, wl.quant_mode,
                           zero_expert_num=wl.zero_expert_num,
                           copy_expert_num=wl.copy_expert_num,
                           expert_token_nums_type=wl.expert_token_nums_type,
                           mask_kind=wl.mask_kind, cap=cap, out_dtype=wl.out_dtype,
-                          scales_kind=wl.scales_kind, scale_format=wl.scale_format)
+                          scales_kind=wl.scales_kind, scale_format=wl.scale_format,
+                          flags=flags)
 
 
 def to_dev(a, dtype=None, device="cuda"):
@@ -113,14 +114,14 @@ def oracle_dispatch(wl, inp, etn_type=None):
                                 mask=inp.get("mask"))
 
 
-def roundtrip(wl, seed=0):
+def roundtrip(wl, seed=0, flags=0):
     """Dispatch compared bit for bit, then combine over random bf16 expert outputs compared
     within tolerance; returns the number of bf16 elements that differ at all."""
     import torch
     import combine_quant_amd as cq
     inp = workloads.generate(wl, seed=seed)
     ocfg, ref = oracle_dispatch(wl, inp)
-    cfg, dev_in, out = gpu_dispatch(wl, inp)
+    cfg, dev_in, out = gpu_dispatch(wl, inp, cfg=lib_cfg(wl, flags=flags))
     torch.cuda.synchronize()
     compare_dispatch(wl, inp, out, ref)
     rng = np.random.default_rng(seed + 77)

@@ -33,11 +33,13 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_config_struct_layout_matches_header():
-    # sixteen int32 fields (the last two reserved) then one int64
+    # sixteen int32 fields (flags, then one reserved) then one int64
     assert ctypes.sizeof(cq.MoeDcConfig) == 16 * 4 + 8
     assert cq.MoeDcConfig.out_dtype.offset == 44
     assert cq.MoeDcConfig.scales_kind.offset == 48
     assert cq.MoeDcConfig.scale_format.offset == 52
+    assert cq.MoeDcConfig.flags.offset == 56
+    assert cq.MoeDcConfig.reserved.offset == 60
     assert cq.MoeDcConfig.expand_rows_capacity.offset == 64
 
 
@@ -46,7 +48,8 @@ def test_header_enum_values_match_the_binding():
     for name in ("MOE_DTYPE_DEFAULT", "MOE_DTYPE_INT8", "MOE_DTYPE_E4M3", "MOE_DTYPE_E5M2",
                  "MOE_DTYPE_E2M1",
                  "MOE_SCALES_NONE", "MOE_SCALES_SCALAR", "MOE_SCALES_SHARED",
-                 "MOE_SCALES_PER_EXPERT", "MOE_SCALE_FP32", "MOE_SCALE_E8M0"):
+                 "MOE_SCALES_PER_EXPERT", "MOE_SCALE_FP32", "MOE_SCALE_E8M0",
+                 "MOE_DC_FLAG_SEPARATE_ROUTE"):
         m = re.search(r"\b" + name + r"\s*=\s*(\d+)", text)
         assert m and int(m.group(1)) == getattr(cq, name), name
 
@@ -57,9 +60,7 @@ def _cfg(**kw):
     c = cq.make_config(base["W"], base["E"], base["BS"], base["H"], base["K"],
                        base["quant_mode"])
     for k, v in kw.items():
-        if k == "reserved":
-            c.reserved[1] = v
-        elif k not in base:
+        if k not in base:
             setattr(c, k, v)
     return c
 
@@ -110,6 +111,8 @@ def test_valid_configs_of_the_workloads():
     (dict(expert_token_nums_type=2), cq.MOE_ERR_INVALID_ARG),
     (dict(mask_kind=3), cq.MOE_ERR_INVALID_ARG),
     (dict(reserved=1), cq.MOE_ERR_INVALID_ARG),
+    (dict(flags=2), cq.MOE_ERR_INVALID_ARG),
+    (dict(flags=-1), cq.MOE_ERR_INVALID_ARG),
     (dict(expand_rows_capacity=16 * 512 * 8 - 1), cq.MOE_ERR_INVALID_ARG),
     (dict(expand_rows_capacity=2 ** 31), cq.MOE_ERR_INVALID_ARG),
 ])
@@ -119,6 +122,11 @@ def test_validation_rules(kw, status):
     assert cq.moe_dc_last_error() != ""
     assert cq.moe_dc_dispatch_workspace_bytes(c) == 0
     assert cq.moe_dc_scales_per_row(c) == -1
+
+
+def test_separate_route_flag_is_valid():
+    c = _cfg(flags=cq.MOE_DC_FLAG_SEPARATE_ROUTE)
+    assert cq.moe_dc_validate(c) == cq.MOE_OK, cq.moe_dc_last_error()
 
 
 def test_k_may_count_special_experts():
