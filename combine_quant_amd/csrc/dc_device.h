@@ -161,14 +161,6 @@ __device__ __forceinline__ int32_t block_inclusive_scan(int32_t v, int32_t* wave
     return v + before;
 }
 
-// Sum across the 64 lanes of a wave; every lane gets the result.
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v)
-{
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-    return v;
-}
-
 // Expert of pick k of token tok when the pick is routed -- active under the mask (kind 1:
 // mask[tok], kind 2: mask[tok*K + k], nonzero = active) and 0 <= id < E -- else -1.
 __device__ __forceinline__ int32_t routed_expert(const int32_t* __restrict__ ids,

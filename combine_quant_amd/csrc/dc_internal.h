@@ -58,7 +58,7 @@ struct FusedRoute {
     int64_t* expert_token_nums;
     int64_t* recv_offsets;
 };
-constexpr long long kFusedMaxPicks = 1024;   // W*BS*K (measured crossover: 1024-2048)
+constexpr long long kFusedMaxPicks = 2048;   // W*BS*K (measured crossover: 2048-4096)
 constexpr long long kFusedMaxCounts = 4096;  // E*W (LDS words)
 
 inline bool fused_route_fits(const Shape& s)

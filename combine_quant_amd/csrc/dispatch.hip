@@ -227,14 +227,16 @@ __device__ void route_totals(const int32_t* __restrict__ ids, const FusedRoute& 
 // Picks each thread of a token workgroup counts: t, t + blockDim, ... (blockDim >= 256).
 constexpr int kFusedPicksPerThread = (int)(kFusedMaxPicks / (kWave * kFusedMinWaves));
 
-// The routed expert (or -1) of each pick this thread counts.  Called before the token row is
-// requested: loads complete in issue order, so using these values then does not wait for
-// the row.
-__device__ __forceinline__ void load_fused_picks(const int32_t* __restrict__ ids,
-                                                 const FusedRoute& fr, int E, int K,
-                                                 int mask_kind, int picks,
-                                                 int32_t (&pe)[kFusedPicksPerThread])
+// The routed expert (or -1) of each pick this thread counts, and in lane k < K of every
+// wave that of the workgroup's own pick k.  Called before the token row is requested: loads
+// complete in issue order, so using these values then does not wait for the row.
+__device__ __forceinline__ int32_t load_fused_picks(const int32_t* __restrict__ ids,
+                                                    const FusedRoute& fr, int E, int K,
+                                                    int mask_kind, int picks, long long tok,
+                                                    int32_t (&pe)[kFusedPicksPerThread])
 {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int32_t own_e = lane < K ? routed_expert(ids, fr.mask, mask_kind, K, E, tok, lane) : -1;
 #pragma unroll
     for (int j = 0; j < kFusedPicksPerThread; ++j) {
         const int p2 = threadIdx.x + j * blockDim.x;
@@ -244,6 +246,7 @@ __device__ __forceinline__ void load_fused_picks(const int32_t* __restrict__ ids
             pe[j] = routed_expert(ids, fr.mask, mask_kind, K, E, q, p2 - q * K);
         }
     }
+    return own_e;
 }
 
 // Token workgroups: the packed row of pick k of token `tok` (source rank s) is its position in
@@ -251,10 +254,11 @@ __device__ __forceinline__ void load_fused_picks(const int32_t* __restrict__ ids
 // of routed picks p2 with a smaller expert, or the same expert and p2 < tok*K + k in the
 // flat (rank, token, pick) order.  Its expand_idx counts only the same expert's picks of
 // rank s before it.  Threads k < K get the row of pick k (-1 when it is not routed, or past
-// `cap`) and write its expand_idx.
-__device__ int32_t route_own_rows(const int32_t* __restrict__ ids, const FusedRoute& fr,
-                                  int E, int BS, int K, int mask_kind, int tok, int s,
-                                  long long cap, const int32_t (&pe)[kFusedPicksPerThread],
+// `cap`) and write its expand_idx.  Both counts of a pick share one word (16 bits each; a
+// batch has at most kFusedMaxPicks picks); the words are summed across each wave with the
+// device library's data-parallel-primitive reduction, then across waves by LDS atomics.
+__device__ int32_t route_own_rows(int K, int BS, int tok, int s, long long cap,
+                                  const int32_t (&pe)[kFusedPicksPerThread], int32_t own_e,
                                   int32_t* row_lds, int32_t* ord_lds,
                                   int32_t* __restrict__ expand_idx)
 {
@@ -268,11 +272,10 @@ __device__ int32_t route_own_rows(const int32_t* __restrict__ ids, const FusedRo
     }
     int32_t mine[kMaxK];
 #pragma unroll
-    for (int k = 0; k < kMaxK; ++k)
-        mine[k] = k < K ? routed_expert(ids, fr.mask, mask_kind, K, E, tok, k) : -1;
-    uint32_t before[kMaxK], same[kMaxK];
+    for (int k = 0; k < kMaxK; ++k) mine[k] = lane_value(own_e, k);   // -1 for k >= K
+    uint32_t cnt[kMaxK];                  // before | same << 16
 #pragma unroll
-    for (int k = 0; k < kMaxK; ++k) before[k] = same[k] = 0;
+    for (int k = 0; k < kMaxK; ++k) cnt[k] = 0;
 #pragma unroll
     for (int j = 0; j < kFusedPicksPerThread; ++j) {
         const int p2 = t + j * nt;
@@ -281,26 +284,26 @@ __device__ int32_t route_own_rows(const int32_t* __restrict__ ids, const FusedRo
 #pragma unroll
         for (int k = 0; k < kMaxK; ++k) {
             const bool earlier = e2 == mine[k] && p2 < own + k;
-            before[k] += (e2 < mine[k] || earlier) ? 1u : 0u;
-            same[k] += (earlier && p2 >= rank_lo) ? 1u : 0u;
+            cnt[k] += (e2 < mine[k] || earlier) ? 1u : 0u;
+            cnt[k] += (earlier && p2 >= rank_lo) ? 0x10000u : 0u;
         }
     }
-    __syncthreads();                                      // row_lds / ord_lds cleared
 #pragma unroll
-    for (int k = 0; k < kMaxK; ++k) {
-        if (k < K) {                                       // uniform
-            const uint32_t b = wave_sum_u32(before[k]);
-            const uint32_t o = wave_sum_u32(same[k]);
-            if ((t & (kWave - 1)) == 0) {
-                if (b != 0) atomicAdd(&row_lds[k], (int32_t)b);
-                if (o != 0) atomicAdd(&ord_lds[k], (int32_t)o);
-            }
+    for (int k = 0; k < kMaxK; ++k) cnt[k] = __ockl_wfred_add_u32(cnt[k]);   // wave sums (DPP)
+    __syncthreads();                                      // row_lds / ord_lds cleared
+    if ((t & (kWave - 1)) == 0) {
+#pragma unroll
+        for (int k = 0; k < kMaxK; ++k) {
+            const int32_t before = (int32_t)(cnt[k] & 0xFFFFu);
+            const int32_t same = (int32_t)(cnt[k] >> 16);
+            if (k < K && before != 0) atomicAdd(&row_lds[k], before);
+            if (k < K && same != 0) atomicAdd(&ord_lds[k], same);
         }
     }
     __syncthreads();
     int32_t row = -1;
     if (t < K) {
-        const bool routed = routed_expert(ids, fr.mask, mask_kind, K, E, tok, t) >= 0;
+        const bool routed = own_e >= 0;                   // lane t of wave 0: own pick t
         expand_idx[own + t] = routed ? ord_lds[t] : -1;
         if (routed && row_lds[t] < cap) row = row_lds[t];
     }
@@ -343,7 +346,8 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
     float* fscales = static_cast<float*>(dyn_scales);
 
     int32_t fused_picks[kFusedPicksPerThread];
-    if (FUSED) load_fused_picks(ids, fr, E, K, mask_kind, W * BS * K, fused_picks);
+    int32_t fused_own = -1;
+    if (FUSED) fused_own = load_fused_picks(ids, fr, E, K, mask_kind, W * BS * K, tok, fused_picks);
 
     // 1. this wave's slots of the token row (and of a shared scales row), in flight before
     //    anything waits
@@ -367,8 +371,8 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
     // 2. destination rows, resolved by threads 0..K-1 (small batches route here first)
     int32_t fused_row = -1;
     if (FUSED)
-        fused_row = route_own_rows(ids, fr, E, BS, K, mask_kind, (int)tok, s, cap,
-                                   fused_picks, fused_rows_lds, ord_lds, expand_idx);
+        fused_row = route_own_rows(K, BS, (int)tok, s, cap, fused_picks, fused_own,
+                                   fused_rows_lds, ord_lds, expand_idx);
     if (threadIdx.x < K) {
         const long long p = tok * K + threadIdx.x;
         const int32_t e = ids[p];

@@ -81,7 +81,7 @@ typedef enum {
 typedef enum {
     MOE_DC_FLAG_SEPARATE_ROUTE = 1  /* moe_dispatch always runs the routing and the prefix
                                        sums as kernels of their own.  By default a small
-                                       batch (W*BS*K <= 1024 picks and E*W <= 4096, with the
+                                       batch (W*BS*K <= 2048 picks and E*W <= 4096, with the
                                        vectorised scatter) computes them inside the scatter
                                        launch instead, one launch in place of three; the
                                        results are identical either way                    */

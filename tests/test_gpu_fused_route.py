@@ -1,6 +1,6 @@
 """GPU parity of the small-batch dispatch, which routes inside the scatter launch.
 
-For W*BS*K <= 1024 picks and E*W <= 4096 (vectorised path) moe_dispatch computes the
+For W*BS*K <= 2048 picks and E*W <= 4096 (vectorised path) moe_dispatch computes the
 counts, prefix sums and expand_idx in the scatter workgroups; MOE_DC_FLAG_SEPARATE_ROUTE
 forces the route and scan kernels.  Every case runs both ways: each is compared with the CPU
 oracle bit for bit, and the two with each other.  The fused launch never touches the
@@ -20,7 +20,7 @@ WL = workloads.Workload
 CASES = {
     "c1_mode0": workloads.C1_MODE0,
     "c1_mode2": workloads.C1_MODE2,
-    "randint_dups_mask2_special": WL("randint_dups_mask2_special", W=4, E=16, BS=30, H=1024,
+    "randint_dups_mask2_special": WL("randint_dups_mask2_special", W=4, E=16, BS=40, H=1024,
                                      K=8, quant_mode=2, routing="randint", mask_kind=2,
                                      inactive_tokens_per_rank=5, zero_expert_num=1,
                                      copy_expert_num=1),
@@ -30,7 +30,7 @@ CASES = {
                                 quant_mode=3, scales_kind=3, out_dtype=2),
     "sample_bs8_mx_e5m2_e8m0": WL("sample_bs8_mx_e5m2_e8m0", W=8, E=32, BS=8, H=7168, K=8,
                                   quant_mode=4, out_dtype=3, scale_format=1),
-    "picks_at_limit": WL("picks_at_limit", W=2, E=32, BS=64, H=1024, K=8, quant_mode=2),
+    "picks_at_limit": WL("picks_at_limit", W=2, E=32, BS=128, H=1024, K=8, quant_mode=2),
     "counts_at_limit_fp4": WL("counts_at_limit_fp4", W=4, E=1024, BS=8, H=1040, K=16,
                               quant_mode=5, out_dtype=4, scale_format=1),
     "one_token_per_rank": WL("one_token_per_rank", W=16, E=256, BS=1, H=7168, K=8,
@@ -38,7 +38,7 @@ CASES = {
 }
 # just past the limits: the separate kernels run whatever the flag says
 PAST_LIMIT = {
-    "picks_past_limit": WL("picks_past_limit", W=2, E=32, BS=65, H=1024, K=8, quant_mode=2),
+    "picks_past_limit": WL("picks_past_limit", W=2, E=32, BS=129, H=1024, K=8, quant_mode=2),
     "counts_past_limit": WL("counts_past_limit", W=8, E=1024, BS=4, H=1024, K=8,
                             quant_mode=2),
 }
