@@ -6,7 +6,7 @@ forces the route and scan kernels.  Every case runs both ways: each is compared 
 oracle bit for bit, and the two with each other.  The fused launch never touches the
 workspace (the separate route and scan keep their counts there), which shows which path ran.
 Cases cover masks of both kinds, zero/copy experts, duplicate picks inside a token, both
-expert_token_nums types, per-expert scales, fp4 codes and both limits exactly."""
+expert_token_nums types, every scales shape, fp4 codes and both limits exactly."""
 import numpy as np
 import pytest
 
@@ -35,6 +35,12 @@ CASES = {
                               quant_mode=5, out_dtype=4, scale_format=1),
     "one_token_per_rank": WL("one_token_per_rank", W=16, E=256, BS=1, H=7168, K=8,
                              quant_mode=2),
+    "smooth_per_expert_int8": WL("smooth_per_expert_int8", W=8, E=64, BS=16, H=7168, K=8,
+                                 quant_mode=2, scales_kind=3, outlier_prob=0.01),
+    "static_shared_row": WL("static_shared_row", W=4, E=32, BS=16, H=2048, K=6, quant_mode=1,
+                            scales_kind=2),
+    "mx_e2m1_fp32_ragged": WL("mx_e2m1_fp32_ragged", W=4, E=16, BS=32, H=2064, K=4,
+                              quant_mode=4, out_dtype=4),
 }
 # just past the limits: the separate kernels run whatever the flag says
 PAST_LIMIT = {
