@@ -216,10 +216,12 @@ __device__ void route_totals(const int32_t* __restrict__ ids, const FusedRoute& 
     __syncthreads();
     // receiver r = e / L: ep_recv_count runs from the rank's first segment; recv_offsets[r]
     // is the rank's first row; expert_token_nums counts per expert (type 1) or runs (type 0)
-    for (int f = t; f < N; f += nt) fr.ep_recv_count[f] = ex[f + 1] - ex[(f / W / L) * L * W];
+    for (int f = t; f < N; f += nt)
+        fr.ep_recv_count[f] = ex[f + 1] - ex[(f / W / L) * L * W];
     for (int e = t; e < E; e += nt) {
         const int first = (e / L) * L * W;
-        fr.expert_token_nums[e] = (int64_t)(ex[(e + 1) * W] - ex[etn_type == 0 ? first : e * W]);
+        const int from = etn_type == 0 ? first : e * W;
+        fr.expert_token_nums[e] = (int64_t)(ex[(e + 1) * W] - ex[from]);
     }
     for (int r = t; r <= W; r += nt) fr.recv_offsets[r] = ex[r * L * W];
 }
@@ -236,7 +238,8 @@ __device__ __forceinline__ int32_t load_fused_picks(const int32_t* __restrict__ 
                                                     int32_t (&pe)[kFusedPicksPerThread])
 {
     const int lane = threadIdx.x & (kWave - 1);
-    const int32_t own_e = lane < K ? routed_expert(ids, fr.mask, mask_kind, K, E, tok, lane) : -1;
+    const int32_t own_e =
+        lane < K ? routed_expert(ids, fr.mask, mask_kind, K, E, tok, lane) : -1;
 #pragma unroll
     for (int j = 0; j < kFusedPicksPerThread; ++j) {
         const int p2 = threadIdx.x + j * blockDim.x;
