@@ -1,8 +1,9 @@
 // api.cpp -- C ABI of libmoe_dc: host validation, workspace sizing and launch sequencing.
 //
 // Nothing here allocates device memory or synchronises the host; every launch goes to the
-// caller's stream in order (route -> scan -> scatter for dispatch; index then gather for the
-// scatter-back combine; one kernel for each of combine, combine quantize and int8 combine).
+// caller's stream in order (route -> scan -> scatter for dispatch, or the scatter alone for a
+// small batch, which routes in its own workgroups; index then gather for the scatter-back
+// combine; one kernel for each of combine, combine quantize and int8 combine).
 #include "moe_dc.h"
 #include "dc_internal.h"
 

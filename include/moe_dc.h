@@ -27,7 +27,9 @@
  *     call is asynchronous on that stream: it validates on the host, enqueues kernels and
  *     returns; outputs are valid in stream order.  No call synchronises the host, and no
  *     call allocates or frees memory: the caller owns every buffer and the stream.
- *   - A negative status means nothing was enqueued; moe_dc_last_error() then describes the
+ *   - A negative status other than MOE_ERR_DEVICE means nothing was enqueued (after
+ *     MOE_ERR_DEVICE, kernels enqueued before the failing launch may still run and the
+ *     outputs are undefined); moe_dc_last_error() then describes the
  *     problem (thread-local, valid until the next call on the same thread).
  */
 #ifndef MOE_DC_H
