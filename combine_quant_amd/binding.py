@@ -2,7 +2,8 @@
 
 Function names mirror the C ABI in include/moe_dc.h.  Every step of dispatch and combine runs
 in the library's HIP kernels; this module checks tensor dtypes/shapes/devices, passes raw
-device pointers and the current HIP stream, and turns a negative status into an exception.
+device pointers and the current HIP stream (with the tensors' device current, which the
+library launches on), and turns a negative status into an exception.
 It never falls back to another implementation: if the library is missing, loading fails.
 """
 from __future__ import annotations
@@ -231,8 +232,9 @@ def moe_dispatch(cfg, x, expert_ids, scales, x_active_mask, expand_x, dynamic_sc
     ]
     ws_bytes = 0 if workspace is None else workspace.numel()
     lib = load_library()
-    _check(lib.moe_dispatch(ctypes.byref(cfg), *args, ctypes.c_size_t(ws_bytes),
-                            _stream(dev, stream)))
+    with torch.cuda.device(dev):
+        _check(lib.moe_dispatch(ctypes.byref(cfg), *args, ctypes.c_size_t(ws_bytes),
+                                _stream(dev, stream)))
 
 
 def moe_combine(cfg, expert_out, expert_ids, expand_idx, expert_scales, ep_recv_count,
@@ -254,7 +256,8 @@ def moe_combine(cfg, expert_out, expert_ids, expand_idx, expert_scales, ep_recv_
         _ptr(y, torch.bfloat16, (W, BS, H), "y", dev),
     ]
     lib = load_library()
-    _check(lib.moe_combine(ctypes.byref(cfg), *args, _stream(dev, stream)))
+    with torch.cuda.device(dev):
+        _check(lib.moe_combine(ctypes.byref(cfg), *args, _stream(dev, stream)))
 
 
 def moe_dc_combine_scatter_workspace_bytes(cfg: MoeDcConfig) -> int:
@@ -281,8 +284,10 @@ def moe_combine_scatter(cfg, expert_out, assist_info, recv_offsets, expert_ids, 
         _ptr(workspace, torch.uint8, None, "workspace", dev),
     ]
     ws_bytes = 0 if workspace is None else workspace.numel()
-    _check(load_library().moe_combine_scatter(ctypes.byref(cfg), *args,
-                                              ctypes.c_size_t(ws_bytes), _stream(dev, stream)))
+    with torch.cuda.device(dev):
+        _check(load_library().moe_combine_scatter(ctypes.byref(cfg), *args,
+                                                  ctypes.c_size_t(ws_bytes),
+                                                  _stream(dev, stream)))
 
 
 def combine_block_count(cfg):
@@ -301,7 +306,9 @@ def moe_combine_quantize(cfg, expert_out, recv_offsets, codes, block_scales, str
         _ptr(block_scales, torch.float32, (cap, combine_block_count(cfg)), "block_scales",
              dev),
     ]
-    _check(load_library().moe_combine_quantize(ctypes.byref(cfg), *args, _stream(dev, stream)))
+    with torch.cuda.device(dev):
+        _check(load_library().moe_combine_quantize(ctypes.byref(cfg), *args,
+                                                   _stream(dev, stream)))
 
 
 def moe_combine_int8(cfg, codes, block_scales, expert_ids, expand_idx, expert_scales,
@@ -324,7 +331,8 @@ def moe_combine_int8(cfg, codes, block_scales, expert_ids, expand_idx, expert_sc
         _ptr(ori_x, torch.bfloat16, (W, BS, H), "ori_x", dev),
         _ptr(y, torch.bfloat16, (W, BS, H), "y", dev),
     ]
-    _check(load_library().moe_combine_int8(ctypes.byref(cfg), *args, _stream(dev, stream)))
+    with torch.cuda.device(dev):
+        _check(load_library().moe_combine_int8(ctypes.byref(cfg), *args, _stream(dev, stream)))
 
 
 # -- allocation helpers (torch owns the memory; the library never allocates) ----------------
