@@ -120,26 +120,40 @@ __device__ __forceinline__ float lane_value(float v, int lane)
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-// Largest value across the 64 lanes of a wave (unsigned).
+// Largest value across the 64 lanes of a wave (unsigned), in every lane: the device
+// library's wave reduction (DPP row operations, then two lane reads).
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        uint32_t o = __shfl_xor(v, off, kWave);
-        v = v > o ? v : o;
-    }
-    return v;
+    return __ockl_wfred_max_u32(v);
 }
 
-// Largest value over groups of G adjacent lanes (G a power of two <= 64).
+// DPP lane patterns (GFX9 encodings) used by group_max_u32; every lane of a row of 16 reads a
+// valid lane, so no bound control is involved.
+constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowHalfMirror = 0x141; // lane i <-> 7 - i within each half row of 8
+constexpr int kDppRowMirror = 0x140;     // lane i <-> 15 - i within each row of 16
+
+__device__ __forceinline__ uint32_t dpp_max(uint32_t v, uint32_t o) { return v > o ? v : o; }
+
+// Largest value over groups of G adjacent lanes (G a power of two <= 64), in every lane of
+// the group.  Within a row of 16 lanes the exchanges are DPP moves (ALU latency); beyond, lane
+// shuffles.  After the quad steps all four lanes of a quad hold its maximum, so mirroring the
+// half row pairs each quad with its neighbour, and mirroring the row pairs the two halves.
 template <int G>
 __device__ __forceinline__ uint32_t group_max_u32(uint32_t v)
 {
+    if (G >= 2)
+        v = dpp_max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppQuadXor1, 0xF, 0xF, false));
+    if (G >= 4)
+        v = dpp_max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppQuadXor2, 0xF, 0xF, false));
+    if (G >= 8)
+        v = dpp_max(v,
+                    (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppRowHalfMirror, 0xF, 0xF, false));
+    if (G >= 16)
+        v = dpp_max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppRowMirror, 0xF, 0xF, false));
 #pragma unroll
-    for (int off = G / 2; off >= 1; off >>= 1) {
-        uint32_t o = __shfl_xor(v, off, kWave);
-        v = v > o ? v : o;
-    }
+    for (int off = 16; off < G; off <<= 1) v = dpp_max(v, __shfl_xor(v, off, kWave));
     return v;
 }
 

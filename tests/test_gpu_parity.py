@@ -117,14 +117,15 @@ def test_determinism_repeat():
         assert torch.equal(ta, tb), k
 
 
-def test_all_tokens_inactive():
+@pytest.mark.parametrize("flags", [0, 1])     # 1: MOE_DC_FLAG_SEPARATE_ROUTE
+def test_all_tokens_inactive(flags):
     import torch
     import combine_quant_amd as cq
     wl = workloads.Workload("all_off", W=2, E=8, BS=16, H=1024, K=2, quant_mode=2, mask_kind=2,
                             inactive_tokens_per_rank=16, copy_expert_num=1)
     inp = workloads.generate(wl, seed=0)
     assert inp["mask"].sum() == 0
-    cfg, dev_in, out = harness.gpu_dispatch(wl, inp)
+    cfg, dev_in, out = harness.gpu_dispatch(wl, inp, cfg=harness.lib_cfg(wl, flags=flags))
     y = cq.combine(cfg, torch.zeros((wl.cap, wl.H), dtype=torch.bfloat16, device="cuda"),
                    dev_in["ids"], out["expand_idx"], harness.to_dev(inp["expert_scales"]),
                    out["ep_recv_count"], out["recv_offsets"], dev_in["mask"], dev_in["x"])
