@@ -62,9 +62,10 @@ _oracle_dispatch = harness.oracle_dispatch
 _roundtrip = harness.roundtrip
 
 
+@pytest.mark.parametrize("flags", [0, 1])     # 1: MOE_DC_FLAG_SEPARATE_ROUTE
 @pytest.mark.parametrize("name", list(SMALL))
-def test_small_roundtrip(name):
-    ndiff = _roundtrip(SMALL[name])
+def test_small_roundtrip(name, flags):
+    ndiff = _roundtrip(SMALL[name], flags=flags)
     assert ndiff == 0, f"{ndiff} bf16 elements differ from the oracle (within tolerance)"
 
 
@@ -227,8 +228,9 @@ def test_invalid_arguments_raise_and_enqueue_nothing():
     assert (o["expand_idx"] == 123).all()
 
 
+@pytest.mark.parametrize("flags", [0, 1])     # 1: MOE_DC_FLAG_SEPARATE_ROUTE
 @pytest.mark.parametrize("K", [3, 4, 8, 16])
-def test_out_of_range_ids_are_not_dispatched(K):
+def test_out_of_range_ids_are_not_dispatched(K, flags):
     """Ids outside [0, E+Z+C) break the contract; the library must treat such picks exactly
     like masked-off picks (no row, expand_idx -1, no combine term) and never touch memory
     out of bounds.  Reference: the oracle on the same input with those picks masked off."""
@@ -248,7 +250,7 @@ def test_out_of_range_ids_are_not_dispatched(K):
     ref_ids[bad] = 0
     ocfg = harness.oracle_cfg(wl)
     ref = oracle.dispatch(ocfg, inp["x"], ref_ids, mask=ref_mask)
-    cfg = harness.lib_cfg(wl)
+    cfg = harness.lib_cfg(wl, flags=flags)
     x = harness.bf16_dev(inp["x"])
     ids_dev = harness.to_dev(ids_bad)
     mask_dev = harness.to_dev(inp["mask"])
