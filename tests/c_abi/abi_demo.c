@@ -12,6 +12,10 @@
  * Checks: every status is MOE_OK; recv_offsets[W] = W*BS*K (nothing masked, no special
  * experts) = the sum of expert_token_nums (type 1); every expand_x row holds the bf16 row of
  * the token its assist_info triple names, and every pick appears exactly once; y == x.
+ * The other two combines run on the same rows: the scatter-back combine (moe_combine_scatter,
+ * rows returned by their triples) must also give x bit for bit, and the int8 block-quantized
+ * combine (moe_combine_quantize, then moe_combine_int8) x within its quantization bound:
+ * 0.6 * (the 8-element block's max |x|) / 127 plus the bf16 rounding of the result.
  * Prints "ok routed=<rows> step_us=<mean>" and exits 0, or prints the failure and exits 1.
  */
 #include <hip/hip_runtime_api.h>
@@ -53,6 +57,14 @@ static uint16_t bf16_of(float f)
     uint32_t u;
     memcpy(&u, &f, sizeof u);
     return (uint16_t)(u >> 16);
+}
+
+static float f32_of_bf16(uint16_t b)
+{
+    const uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
 }
 
 int main(int argc, char** argv)
@@ -165,6 +177,46 @@ int main(int argc, char** argv)
         printf("combine of K copies weighted 1/K is not x\n");
         return 1;
     }
+
+    /* scatter-back combine: the rows go back by their triples; the same sum in k order */
+    const size_t ws2_bytes = moe_dc_combine_scatter_workspace_bytes(&cfg);
+    void *dws2, *dy2, *dcodes, *dbs, *dy3;
+    const size_t nb = ((size_t)H + 7) / 8;
+    HIP_OK(hipMalloc(&dws2, ws2_bytes));
+    HIP_OK(hipMalloc(&dy2, T * H * 2));
+    HIP_OK(hipMalloc(&dcodes, cap * H));
+    HIP_OK(hipMalloc(&dbs, cap * nb * 4));
+    HIP_OK(hipMalloc(&dy3, T * H * 2));
+    MOE_OK_OR_FAIL(moe_combine_scatter(&cfg, dex, dai, droff, dids, dw, NULL, NULL, NULL, dy2,
+                                       dws2, ws2_bytes, stream));
+    /* int8 block-quantized combine over the same rows */
+    MOE_OK_OR_FAIL(moe_combine_quantize(&cfg, dex, droff, dcodes, dbs, stream));
+    MOE_OK_OR_FAIL(moe_combine_int8(&cfg, dcodes, dbs, dids, deidx, dw, derc, droff, NULL, NULL,
+                                    dy3, stream));
+    HIP_OK(hipStreamSynchronize(stream));
+    HIP_OK(hipMemcpy(y, dy2, T * H * 2, hipMemcpyDeviceToHost));
+    if (memcmp(y, x, T * H * 2) != 0) {
+        printf("scatter-back combine of K copies weighted 1/K is not x\n");
+        return 1;
+    }
+    HIP_OK(hipMemcpy(y, dy3, T * H * 2, hipMemcpyDeviceToHost));
+    for (size_t t = 0; t < T; ++t)
+        for (size_t b0 = 0; b0 < (size_t)H; b0 += 8) {
+            float amax = 0.0f;
+            for (size_t h = b0; h < b0 + 8 && h < (size_t)H; ++h) {
+                const float a = f32_of_bf16(x[t * H + h]);
+                amax = a > amax ? a : (-a > amax ? -a : amax);
+            }
+            for (size_t h = b0; h < b0 + 8 && h < (size_t)H; ++h) {
+                const float xv = f32_of_bf16(x[t * H + h]), yv = f32_of_bf16(y[t * H + h]);
+                const float d = yv > xv ? yv - xv : xv - yv;
+                const float ax = xv > 0.0f ? xv : -xv;
+                if (d > 0.6f * amax / 127.0f + ax / 256.0f + 1e-6f) {
+                    printf("int8 combine: token %zu element %zu: %g vs %g\n", t, h, yv, xv);
+                    return 1;
+                }
+            }
+        }
 
     /* native launch timing: dispatch + combine, eager, on one stream */
     hipEvent_t a, b;

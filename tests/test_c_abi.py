@@ -1,6 +1,7 @@
 """The C ABI from plain C: include/moe_dc.h compiles as strict C11, and (on a GPU) a C
-program linked only against libmoe_dc.so and the HIP runtime runs dispatch and combine and
-checks them with invariants (tests/c_abi/abi_demo.c)."""
+program linked only against libmoe_dc.so and the HIP runtime runs dispatch and all three
+combines (gather, scatter-back, int8 block-quantized) and checks them with invariants
+(tests/c_abi/abi_demo.c)."""
 import os
 import re
 import subprocess
