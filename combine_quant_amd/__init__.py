@@ -5,7 +5,7 @@ include/moe_dc.h; this package is the thin Python binding (``binding``) and the 
 build (``build``).  PyTorch supplies device memory and streams only.
 """
 from .binding import (  # noqa: F401
-    EXPORTS, MOE_DC_FLAG_SEPARATE_ROUTE, MOE_DTYPE_DEFAULT, MOE_DTYPE_E2M1, MOE_DTYPE_E4M3, MOE_DTYPE_E5M2, MOE_DTYPE_INT8,
+    EXPORTS, MOE_DC_FLAG_CHECK_IDS, MOE_DC_FLAG_SEPARATE_ROUTE, MOE_DTYPE_DEFAULT, MOE_DTYPE_E2M1, MOE_DTYPE_E4M3, MOE_DTYPE_E5M2, MOE_DTYPE_INT8,
     MOE_ERR_DEVICE, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_OK,
     MOE_SCALE_E8M0, MOE_SCALE_FP32, MOE_SCALES_NONE, MOE_SCALES_PER_EXPERT,
     MOE_SCALES_SCALAR, MOE_SCALES_SHARED, MoeDcConfig, MoeDcError, alloc_dispatch_outputs,

@@ -65,7 +65,7 @@ int32_t resolve_code_type(int32_t mode, int32_t out_dtype)
 moe_status check(const moe_dc_config* c, moe_dc::Shape* out)
 {
     if (!c) return fail(MOE_ERR_INVALID_ARG, "config is NULL");
-    if ((c->flags & ~MOE_DC_FLAG_SEPARATE_ROUTE) != 0)
+    if ((c->flags & ~(MOE_DC_FLAG_SEPARATE_ROUTE | MOE_DC_FLAG_CHECK_IDS)) != 0)
         return fail(MOE_ERR_INVALID_ARG, "flags has unknown bits (0x%x)", c->flags);
     if (c->reserved != 0)
         return fail(MOE_ERR_INVALID_ARG, "reserved must be 0");
@@ -208,7 +208,12 @@ moe_status moe_dispatch(const moe_dc_config* cfg, const void* x, const int32_t* 
     if (!aligned4(workspace))
         return fail(MOE_ERR_INVALID_ARG, "workspace must be 4-byte aligned");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    int32_t* seg = static_cast<int32_t*>(workspace);
+    char* ws = static_cast<char*>(workspace);
+    int32_t* seg = reinterpret_cast<int32_t*>(ws + moe_dc::kWsSegOffset);
+    const bool check_ids = (cfg->flags & MOE_DC_FLAG_CHECK_IDS) != 0;
+    int32_t* bad_word = check_ids ? reinterpret_cast<int32_t*>(ws) : nullptr;
+    int32_t* bad_counts =
+        check_ids ? reinterpret_cast<int32_t*>(ws + moe_dc::ws_bad_counts_offset(sh)) : nullptr;
     const bool row_scales =
         sh.scales_kind == MOE_SCALES_SHARED || sh.scales_kind == MOE_SCALES_PER_EXPERT;
     const bool vec = sh.H % 8 == 0 && aligned16(x) && aligned16(expand_x) &&
@@ -217,14 +222,15 @@ moe_status moe_dispatch(const moe_dc_config* cfg, const void* x, const int32_t* 
     // A small batch routes inside the scatter launch (one launch instead of three).
     const bool fused = vec && (cfg->flags & MOE_DC_FLAG_SEPARATE_ROUTE) == 0 &&
                        moe_dc::fused_route_fits(sh);
-    const moe_dc::FusedRoute fr{x_active_mask, ep_recv_count, expert_token_nums, recv_offsets};
+    const moe_dc::FusedRoute fr{x_active_mask, ep_recv_count, expert_token_nums, recv_offsets,
+                                bad_word, sh.id_end};
     if (!fused) {
         st = device_status(
-            moe_dc::launch_route(sh, expert_ids, x_active_mask, expand_idx, seg, s),
+            moe_dc::launch_route(sh, expert_ids, x_active_mask, expand_idx, seg, bad_counts, s),
             "route kernel launch");
         if (st != MOE_OK) return st;
         st = device_status(moe_dc::launch_scan(sh, seg, ep_recv_count, expert_token_nums,
-                                               recv_offsets, s),
+                                               recv_offsets, bad_counts, bad_word, s),
                            "scan kernel launch");
         if (st != MOE_OK) return st;
     }
@@ -353,6 +359,6 @@ moe_status moe_combine_int8(const moe_dc_config* cfg, const int8_t* codes,
 
 const char* moe_dc_last_error(void) { return g_last_error.c_str(); }
 
-const char* moe_dc_version(void) { return "moe_dc 0.3.0 (gfx950)"; }
+const char* moe_dc_version(void) { return "moe_dc 0.4.0 (gfx950)"; }
 
 }  // extern "C"

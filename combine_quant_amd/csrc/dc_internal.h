@@ -32,22 +32,34 @@ struct Shape {
     int64_t cap;
 };
 
-// Workspace layout of moe_dispatch: one int32 per (expert e, source rank s) at e*W + s.
-// The route kernel stores the pick counts there; the scan kernel overwrites each with the
-// exclusive running total, i.e. the first packed row of that (expert, source) segment.
+// Workspace layout of moe_dispatch, each part 256-byte aligned:
+//   [0, 256)      the checked-ids word (int32 at 0; written only with MOE_DC_FLAG_CHECK_IDS)
+//   seg           one int32 per (expert e, source rank s) at e*W + s: the route kernel stores
+//                 the pick counts there, the scan kernel overwrites each with the exclusive
+//                 running total, i.e. the first packed row of that (expert, source) segment
+//   bad counts    one int32 per source rank: its active picks with an id outside [0, E+Z+C)
+inline size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+constexpr size_t kWsSegOffset = 256;
+inline size_t ws_bad_counts_offset(const Shape& s)
+{
+    return kWsSegOffset + round256((size_t)s.E * (size_t)s.W * sizeof(int32_t));
+}
 inline size_t workspace_bytes(const Shape& s)
 {
-    size_t b = (size_t)s.E * (size_t)s.W * sizeof(int32_t);
-    return (b + 255) & ~(size_t)255;
+    return ws_bad_counts_offset(s) + round256((size_t)s.W * sizeof(int32_t));
 }
 
-// Routing: counts per (expert, source) and the final expand_idx.
+// Routing: counts per (expert, source) and the final expand_idx.  With bad_counts (else
+// null), each source rank's count of active picks whose id lies outside [0, id_end).
 hipError_t launch_route(const Shape& s, const int32_t* expert_ids, const uint8_t* mask,
-                        int32_t* expand_idx, int32_t* seg, hipStream_t stream);
+                        int32_t* expand_idx, int32_t* seg, int32_t* bad_counts,
+                        hipStream_t stream);
 
 // Receive-side prefix sums: seg counts -> segment bases (in place) + the three outputs.
+// With bad_word (else null), the sum of the W bad_counts.
 hipError_t launch_scan(const Shape& s, int32_t* seg, int32_t* ep_recv_count,
-                       int64_t* expert_token_nums, int64_t* recv_offsets, hipStream_t stream);
+                       int64_t* expert_token_nums, int64_t* recv_offsets,
+                       const int32_t* bad_counts, int32_t* bad_word, hipStream_t stream);
 
 // Small batches route inside the scatter launch: every workgroup recomputes the counts and
 // their prefix sums in LDS (W*BS*K ids, E*W counters) instead of reading them from the route
@@ -57,6 +69,8 @@ struct FusedRoute {
     int32_t* ep_recv_count;
     int64_t* expert_token_nums;
     int64_t* recv_offsets;
+    int32_t* bad_word;      // null, or the checked-ids word
+    int32_t id_end;         // E + zero + copy experts
 };
 constexpr long long kFusedMaxPicks = 2048;   // W*BS*K (measured crossover: 2048-4096)
 constexpr long long kFusedMaxCounts = 4096;  // E*W (LDS words)

@@ -39,6 +39,7 @@
 // The element-wise fallback (any H, any alignment) uses one workgroup per token with one
 // element per lane (scatter_elem_kernel); the variant is a runtime argument there.
 #include "dc_device.h"
+#include "route_device.h"
 #include "dc_internal.h"
 
 namespace moe_dc {
@@ -182,7 +183,8 @@ constexpr int kFusedMinWaves = 4;    // workgroup size floor when the launch als
 // Workgroup 0: routed-pick counts per (expert e, source rank s') at ex[e*W + s'] in LDS,
 // their exclusive running total over that flat order (ex[E*W] = all routed rows), and from
 // it ep_recv_count, expert_token_nums and recv_offsets -- what the route and scan kernels
-// write for larger batches.
+// write for larger batches.  With fr.bad_word, also the number of active picks whose id
+// lies outside [0, fr.id_end).
 __device__ void route_totals(const int32_t* __restrict__ ids, const FusedRoute& fr, int W,
                              int E, int L, int BS, int K, int mask_kind, int etn_type,
                              int32_t* ex, int32_t* wave_tot)
@@ -191,14 +193,20 @@ __device__ void route_totals(const int32_t* __restrict__ ids, const FusedRoute& 
     const int nt = blockDim.x;
     const int N = E * W;
     const int picks = W * BS * K;
+    __shared__ int32_t bad_lds;
     for (int f = t; f < N; f += nt) ex[f] = 0;
+    if (t == 0) bad_lds = 0;
     __syncthreads();
+    int32_t bad = 0;
     for (int p = t; p < picks; p += nt) {
         const int q = p / K;
         const int32_t e = routed_expert(ids, fr.mask, mask_kind, K, E, q, p - q * K);
         if (e >= 0) atomicAdd(&ex[e * W + q / BS], 1);
+        if (fr.bad_word) bad += bad_pick(ids, fr.mask, mask_kind, K, fr.id_end, q, p - q * K);
     }
+    if (bad != 0) atomicAdd(&bad_lds, bad);
     __syncthreads();
+    if (fr.bad_word && t == 0) *fr.bad_word = bad_lds;
     // exclusive running total in place: each thread scans one run of entries
     const int per = (N + nt - 1) / nt;
     const int lo = min(N, t * per);

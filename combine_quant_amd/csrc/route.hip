@@ -26,6 +26,7 @@
 // ep_recv_count laid end to end, one exclusive scan of that flat array yields every segment
 // base and, by differences, every output.
 #include "dc_device.h"
+#include "route_device.h"
 #include "dc_internal.h"
 
 namespace moe_dc {
@@ -77,13 +78,16 @@ __device__ __forceinline__ void routed_picks_vec(const int32_t* __restrict__ ids
     }
 }
 
+// bad_counts (null unless ids are checked): the workgroups of expert group 0 store their
+// source rank's number of active picks whose id lies outside [0, id_end).
 template <int KMAX, bool VEC_IDS>
 __global__ __launch_bounds__(512) void route_kernel(
     const int32_t* __restrict__ ids, const uint8_t* __restrict__ mask, int mask_kind, int W,
     int E, int BS, int K, int nwords, int group, int32_t* __restrict__ expand_idx,
-    int32_t* __restrict__ seg)
+    int32_t* __restrict__ seg, int32_t* __restrict__ bad_counts, int id_end)
 {
     extern __shared__ uint32_t lds[];
+    __shared__ int32_t bad_lds;
     const int s = blockIdx.x;
     const int e_lo = blockIdx.y * group;
     const int ne = min(group, E - e_lo);
@@ -102,7 +106,14 @@ __global__ __launch_bounds__(512) void route_kernel(
         else routed_picks<KMAX>(ids, mask, mask_kind, K, E, tok, e);
     }
     for (int w = threadIdx.x; w < 2 * n; w += blockDim.x) lds[w] = 0;
+    const bool check = bad_counts != nullptr && blockIdx.y == 0;     // uniform
+    if (threadIdx.x == 0) bad_lds = 0;
     __syncthreads();
+    if (check && i < BS) {
+        int32_t c = 0;
+        for (int k = 0; k < K; ++k) c += bad_pick(ids, mask, mask_kind, K, id_end, tok, k);
+        if (c != 0) atomicAdd(&bad_lds, c);
+    }
 
     // Bit i of a word belongs to token i alone and this lane walks its picks in k order, so
     // the value atomicOr returns says whether this token already picked the expert: each
@@ -136,6 +147,7 @@ __global__ __launch_bounds__(512) void route_kernel(
             seg[(long long)(e_lo + el) * W + s] = (int32_t)(rp + __popc(hit[q]) + rx + extra[q]);
     }
     __syncthreads();
+    if (check && threadIdx.x == 0) bad_counts[s] = bad_lds;
 
     if (i >= BS) return;
     const uint32_t below = bit - 1u;
@@ -181,13 +193,28 @@ __global__ __launch_bounds__(512) void route_kernel(
 //   recv_offsets[r]        = ex[r*L*W],   recv_offsets[W] = ex[W*E]
 //   expert_token_nums[e]   = ex[(e+1)*W] - ex[e*W]            (counts, type 1)
 //                          = ex[(e+1)*W] - ex[r*L*W]          (running sum, type 0)
+// One workgroup: *out = counts[0] + ... + counts[n-1].
+__device__ void block_sum_to(const int32_t* __restrict__ counts, int n, int32_t* __restrict__ out)
+{
+    __shared__ int32_t acc;
+    if (threadIdx.x == 0) acc = 0;
+    __syncthreads();
+    int32_t c = 0;
+    for (int q = threadIdx.x; q < n; q += blockDim.x) c += counts[q];
+    if (c != 0) atomicAdd(&acc, c);
+    __syncthreads();
+    if (threadIdx.x == 0) *out = acc;
+}
+
 // One block-wide scan (each thread a run of consecutive entries, wave shuffles, LDS across
-// waves), then coalesced stores.
+// waves), then coalesced stores.  With bad_word, also the total of the route's bad counts.
 __global__ __launch_bounds__(kScanThreads) void scan_flat_kernel(
     int W, int E, int L, int etn_type, int32_t* __restrict__ seg,
     int32_t* __restrict__ ep_recv_count, int64_t* __restrict__ expert_token_nums,
-    int64_t* __restrict__ recv_offsets)
+    int64_t* __restrict__ recv_offsets, const int32_t* __restrict__ bad_counts,
+    int32_t* __restrict__ bad_word)
 {
+    if (bad_word) block_sum_to(bad_counts, W, bad_word);
     // entry f is kept at LDS word f + f/32: one pad word per 32 spreads each thread's run of
     // consecutive entries over the banks (a plain layout puts a wave's runs on 4 banks)
     extern __shared__ int32_t lds_ex[];      // padded N + 1 entries, then E rank bases
@@ -247,8 +274,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_flat_kernel(
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     int W, int E, int L, int etn_type, int32_t* __restrict__ seg,
     int32_t* __restrict__ ep_recv_count, int64_t* __restrict__ expert_token_nums,
-    int64_t* __restrict__ recv_offsets)
+    int64_t* __restrict__ recv_offsets, const int32_t* __restrict__ bad_counts,
+    int32_t* __restrict__ bad_word)
 {
+    if (bad_word) block_sum_to(bad_counts, W, bad_word);
     __shared__ int32_t wave_tot[kScanThreads / kWave];
     __shared__ int32_t expert_excl[kScanThreads];
     const int e = threadIdx.x;
@@ -279,7 +308,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
 }  // namespace
 
 hipError_t launch_route(const Shape& sh, const int32_t* expert_ids, const uint8_t* mask,
-                        int32_t* expand_idx, int32_t* seg, hipStream_t stream)
+                        int32_t* expand_idx, int32_t* seg, int32_t* bad_counts,
+                        hipStream_t stream)
 {
     // about one workgroup per CU: (W source ranks) x (groups of experts)
     const int nwords = (sh.BS + 31) / 32;
@@ -296,7 +326,7 @@ hipError_t launch_route(const Shape& sh, const int32_t* expert_ids, const uint8_
 #define MOE_DC_ROUTE(KM, V)                                                                      \
     hipLaunchKernelGGL((route_kernel<KM, V>), grid, dim3(threads), lds, stream, expert_ids,     \
                        mask, sh.mask_kind, sh.W, sh.E, sh.BS, sh.K, nwords, group, expand_idx, \
-                       seg)
+                       seg, bad_counts, sh.id_end)
     if (sh.K <= 2) MOE_DC_ROUTE(2, false);
     else if (sh.K <= 4) { if (vec && sh.K == 4) MOE_DC_ROUTE(4, true); else MOE_DC_ROUTE(4, false); }
     else if (sh.K <= 8) { if (vec && sh.K == 8) MOE_DC_ROUTE(8, true); else MOE_DC_ROUTE(8, false); }
@@ -306,18 +336,20 @@ hipError_t launch_route(const Shape& sh, const int32_t* expert_ids, const uint8_
 }
 
 hipError_t launch_scan(const Shape& sh, int32_t* seg, int32_t* ep_recv_count,
-                       int64_t* expert_token_nums, int64_t* recv_offsets, hipStream_t stream)
+                       int64_t* expert_token_nums, int64_t* recv_offsets,
+                       const int32_t* bad_counts, int32_t* bad_word, hipStream_t stream)
 {
     const long long n = (long long)sh.E * sh.W;
     if (n <= kScanLdsCounts) {
         const size_t words = (size_t)n + 1 + (size_t)((n + 1) >> 5) + 1 + sh.E;
         hipLaunchKernelGGL(scan_flat_kernel, dim3(1), dim3(kScanThreads),
                            words * sizeof(int32_t), stream, sh.W, sh.E, sh.L, sh.etn_type, seg,
-                           ep_recv_count, expert_token_nums, recv_offsets);
+                           ep_recv_count, expert_token_nums, recv_offsets, bad_counts, bad_word);
     } else {
         const int threads = ((sh.E + kWave - 1) / kWave) * kWave;
         hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(threads), 0, stream, sh.W, sh.E, sh.L,
-                           sh.etn_type, seg, ep_recv_count, expert_token_nums, recv_offsets);
+                           sh.etn_type, seg, ep_recv_count, expert_token_nums, recv_offsets,
+                           bad_counts, bad_word);
     }
     return hipGetLastError();
 }

@@ -81,12 +81,16 @@ typedef enum {
 
 /* Bits of moe_dc_config.flags. */
 typedef enum {
-    MOE_DC_FLAG_SEPARATE_ROUTE = 1  /* moe_dispatch always runs the routing and the prefix
-                                       sums as kernels of their own.  By default a small
-                                       batch (W*BS*K <= 2048 picks and E*W <= 4096, with the
-                                       vectorised scatter) computes them inside the scatter
-                                       launch instead, one launch in place of three; the
-                                       results are identical either way                    */
+    /* moe_dispatch always runs the routing and the prefix sums as kernels of their own.  By
+     * default a small batch (W*BS*K <= 2048 picks and E*W <= 4096, with the vectorised
+     * scatter) computes them inside the scatter launch instead, one launch in place of
+     * three; the results are identical either way. */
+    MOE_DC_FLAG_SEPARATE_ROUTE = 1,
+    /* moe_dispatch also counts the active picks whose expert id lies outside
+     * [0, E + zero + copy) -- a contract violation the kernels otherwise skip silently -- and
+     * stores the count as the int32 at byte 0 of the workspace (valid in stream order, until
+     * the workspace is used again). */
+    MOE_DC_FLAG_CHECK_IDS = 2
 } moe_dc_flag;
 
 /* Operator attributes ([OPS] 参数说明; [LLD] 约束说明).  One struct serves both calls; the
@@ -134,7 +138,8 @@ int32_t moe_dc_scales_per_row(const moe_dc_config* cfg);
 /* Workspace bytes moe_dispatch needs for this config (the pages' two-phase pattern:
  * query the workspace size, then execute; [OPS] 调用说明).  0 for an invalid config.
  * The workspace is scratch: its contents need no initialisation and are meaningless after
- * the call; one workspace must not be used by two dispatches that may run concurrently. */
+ * the call (except the checked-ids count of MOE_DC_FLAG_CHECK_IDS at byte 0); one workspace
+ * must not be used by two dispatches that may run concurrently. */
 size_t moe_dc_dispatch_workspace_bytes(const moe_dc_config* cfg);
 
 /* moe_dispatch -- quantize, route and scatter every pick to its receiver's packed rows.
@@ -195,7 +200,7 @@ size_t moe_dc_dispatch_workspace_bytes(const moe_dc_config* cfg);
  * Errors: host validation first (MOE_ERR_INVALID_ARG / _UNSUPPORTED / _WORKSPACE); a HIP
  * launch failure gives MOE_ERR_DEVICE.  Out-of-range expert ids are a contract violation:
  * the kernels never access memory out of bounds for them and treat such picks as not
- * dispatched.  A per-token mask needs no particular order (the pages ask for trues before
+ * dispatched; MOE_DC_FLAG_CHECK_IDS counts them.  A per-token mask needs no particular order (the pages ask for trues before
  * falses; any order works here). */
 moe_status moe_dispatch(const moe_dc_config* cfg,
                         const void* x, const int32_t* expert_ids,

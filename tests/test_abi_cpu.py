@@ -49,7 +49,7 @@ def test_header_enum_values_match_the_binding():
                  "MOE_DTYPE_E2M1",
                  "MOE_SCALES_NONE", "MOE_SCALES_SCALAR", "MOE_SCALES_SHARED",
                  "MOE_SCALES_PER_EXPERT", "MOE_SCALE_FP32", "MOE_SCALE_E8M0",
-                 "MOE_DC_FLAG_SEPARATE_ROUTE"):
+                 "MOE_DC_FLAG_SEPARATE_ROUTE", "MOE_DC_FLAG_CHECK_IDS"):
         m = re.search(r"\b" + name + r"\s*=\s*(\d+)", text)
         assert m and int(m.group(1)) == getattr(cq, name), name
 
@@ -111,7 +111,7 @@ def test_valid_configs_of_the_workloads():
     (dict(expert_token_nums_type=2), cq.MOE_ERR_INVALID_ARG),
     (dict(mask_kind=3), cq.MOE_ERR_INVALID_ARG),
     (dict(reserved=1), cq.MOE_ERR_INVALID_ARG),
-    (dict(flags=2), cq.MOE_ERR_INVALID_ARG),
+    (dict(flags=4), cq.MOE_ERR_INVALID_ARG),
     (dict(flags=-1), cq.MOE_ERR_INVALID_ARG),
     (dict(expand_rows_capacity=16 * 512 * 8 - 1), cq.MOE_ERR_INVALID_ARG),
     (dict(expand_rows_capacity=2 ** 31), cq.MOE_ERR_INVALID_ARG),
@@ -124,9 +124,19 @@ def test_validation_rules(kw, status):
     assert cq.moe_dc_scales_per_row(c) == -1
 
 
-def test_separate_route_flag_is_valid():
-    c = _cfg(flags=cq.MOE_DC_FLAG_SEPARATE_ROUTE)
+@pytest.mark.parametrize("flags", [1, 2, 3])
+def test_known_flags_are_valid(flags):
+    c = _cfg(flags=flags)
     assert cq.moe_dc_validate(c) == cq.MOE_OK, cq.moe_dc_last_error()
+
+
+def test_workspace_holds_the_checked_ids_word_and_per_rank_counts():
+    # 256 bytes for the checked-ids word, then the (expert, source) counts and W per-rank
+    # counts, each rounded up to 256 bytes
+    c = _cfg(W=16, E=256)
+    assert cq.moe_dc_dispatch_workspace_bytes(c) == 256 + 256 * 16 * 4 + 256
+    c = _cfg(W=3, E=9, BS=5)
+    assert cq.moe_dc_dispatch_workspace_bytes(c) == 256 + 256 + 256
 
 
 def test_k_may_count_special_experts():

@@ -228,12 +228,14 @@ def test_invalid_arguments_raise_and_enqueue_nothing():
     assert (o["expand_idx"] == 123).all()
 
 
-@pytest.mark.parametrize("flags", [0, 1])     # 1: MOE_DC_FLAG_SEPARATE_ROUTE
+# 1: MOE_DC_FLAG_SEPARATE_ROUTE, 2: MOE_DC_FLAG_CHECK_IDS
+@pytest.mark.parametrize("flags", [0, 1, 2, 3])
 @pytest.mark.parametrize("K", [3, 4, 8, 16])
 def test_out_of_range_ids_are_not_dispatched(K, flags):
     """Ids outside [0, E+Z+C) break the contract; the library must treat such picks exactly
     like masked-off picks (no row, expand_idx -1, no combine term) and never touch memory
-    out of bounds.  Reference: the oracle on the same input with those picks masked off."""
+    out of bounds.  Reference: the oracle on the same input with those picks masked off.
+    With the id check, the workspace's first int32 holds the number of active bad picks."""
     import torch
     import combine_quant_amd as cq
     wl = workloads.Workload("bad_ids", W=4, E=32, BS=60, H=1024, K=K, quant_mode=2,
@@ -257,6 +259,10 @@ def test_out_of_range_ids_are_not_dispatched(K, flags):
     out = cq.dispatch(cfg, x, ids_dev, None, mask_dev)
     torch.cuda.synchronize()
     harness.compare_dispatch(wl, inp, out, ref)
+    if flags & cq.MOE_DC_FLAG_CHECK_IDS:
+        n_bad = int((bad & (inp["mask"] != 0)).sum())
+        assert n_bad > 0
+        assert int(out["workspace"][:4].view(torch.int32).item()) == n_bad
     rng2 = np.random.default_rng(6)
     eo = workloads.f32_to_bf16_bits(rng2.standard_normal((wl.cap, wl.H), dtype=np.float32))
     y_ref = oracle.combine(ocfg, eo, ref_ids, ref["expand_idx"], inp["expert_scales"],
@@ -267,3 +273,8 @@ def test_out_of_range_ids_are_not_dispatched(K, flags):
                    out["recv_offsets"], mask_dev, x)
     torch.cuda.synchronize()
     assert harness.check_combine_tolerance(harness.host(y), y_ref) == 0
+    if flags & cq.MOE_DC_FLAG_CHECK_IDS:
+        # a clean batch through the same workspace reports zero
+        cq.dispatch(cfg, x, harness.to_dev(ref_ids), None, mask_dev, out=out)
+        torch.cuda.synchronize()
+        assert int(out["workspace"][:4].view(torch.int32).item()) == 0
