@@ -201,12 +201,36 @@ def _dyn_scales_spec(cfg):
     return dt, ((cap,) if ns == 1 else (cap, ns))
 
 
-def moe_dispatch(cfg, x, expert_ids, scales, x_active_mask, expand_x, dynamic_scales,
-                 expand_idx, assist_info, ep_recv_count, expert_token_nums, recv_offsets,
-                 workspace, stream=None, expert_scales=None, expand_scales=None):
-    """Enqueue one dispatch on `stream` (default: the current stream of x's device).
-    `scales` is the quantization scales tensor of cfg.scales_kind ([1], [H] or [E][H]);
-    expert_scales [W][BS][K] and expand_scales [cap] (the rows' weights) go together."""
+class Launch:
+    """One C-ABI call whose arguments were checked and marshalled once.  Calling it enqueues
+    the same call again on `stream` (default: the current stream of its device), which costs
+    only the foreign call: a plan for serving loops.  It keeps the tensors it was built from
+    alive; write new inputs into them in place between calls (or capture calls in a graph)."""
+
+    __slots__ = ("_fn", "_args", "_dev", "_index", "_keep")
+
+    def __init__(self, fn, args, dev, keep):
+        self._fn, self._args, self._dev, self._keep = fn, args, dev, keep
+        self._index = dev.index if dev.index is not None else torch.cuda.current_device()
+
+    def __call__(self, stream=None):
+        if torch.cuda.current_device() != self._index:
+            _launch(self._fn, self._args, self._dev, stream)
+            return
+        s = torch.cuda.current_stream(self._dev) if stream is None else stream
+        status = self._fn(*self._args, ctypes.c_void_p(s.cuda_stream))
+        if status != MOE_OK:
+            _check(status)
+
+
+def _launch(fn, args, dev, stream):
+    with torch.cuda.device(dev):
+        _check(fn(*args, _stream(dev, stream)))
+
+
+def _dispatch_call(cfg, x, expert_ids, scales, x_active_mask, expand_x, dynamic_scales,
+                   expand_idx, assist_info, ep_recv_count, expert_token_nums, recv_offsets,
+                   workspace, expert_scales=None, expand_scales=None):
     W, BS, H, K, L, cap = (cfg.ep_world_size, cfg.bs, cfg.hidden, cfg.topk, cfg.L,
                            cfg.expand_rows_capacity)
     dev = x.device
@@ -231,15 +255,24 @@ def moe_dispatch(cfg, x, expert_ids, scales, x_active_mask, expand_x, dynamic_sc
         _ptr(workspace, torch.uint8, None, "workspace", dev),
     ]
     ws_bytes = 0 if workspace is None else workspace.numel()
-    lib = load_library()
-    with torch.cuda.device(dev):
-        _check(lib.moe_dispatch(ctypes.byref(cfg), *args, ctypes.c_size_t(ws_bytes),
-                                _stream(dev, stream)))
+    return (load_library().moe_dispatch,
+            (ctypes.byref(cfg), *args, ctypes.c_size_t(ws_bytes)), dev)
 
 
-def moe_combine(cfg, expert_out, expert_ids, expand_idx, expert_scales, ep_recv_count,
-                recv_offsets, x_active_mask, ori_x, y, stream=None):
-    """Enqueue one combine on `stream` (default: the current stream of y's device)."""
+def moe_dispatch(cfg, x, expert_ids, scales, x_active_mask, expand_x, dynamic_scales,
+                 expand_idx, assist_info, ep_recv_count, expert_token_nums, recv_offsets,
+                 workspace, stream=None, expert_scales=None, expand_scales=None):
+    """Enqueue one dispatch on `stream` (default: the current stream of x's device).
+    `scales` is the quantization scales tensor of cfg.scales_kind ([1], [H] or [E][H]);
+    expert_scales [W][BS][K] and expand_scales [cap] (the rows' weights) go together."""
+    _launch(*_dispatch_call(cfg, x, expert_ids, scales, x_active_mask, expand_x,
+                            dynamic_scales, expand_idx, assist_info, ep_recv_count,
+                            expert_token_nums, recv_offsets, workspace, expert_scales,
+                            expand_scales), stream)
+
+
+def _combine_call(cfg, expert_out, expert_ids, expand_idx, expert_scales, ep_recv_count,
+                  recv_offsets, x_active_mask, ori_x, y):
     W, BS, H, K, L, cap = (cfg.ep_world_size, cfg.bs, cfg.hidden, cfg.topk, cfg.L,
                            cfg.expand_rows_capacity)
     dev = y.device
@@ -255,18 +288,22 @@ def moe_combine(cfg, expert_out, expert_ids, expand_idx, expert_scales, ep_recv_
         _ptr(ori_x, torch.bfloat16, (W, BS, H), "ori_x", dev),
         _ptr(y, torch.bfloat16, (W, BS, H), "y", dev),
     ]
-    lib = load_library()
-    with torch.cuda.device(dev):
-        _check(lib.moe_combine(ctypes.byref(cfg), *args, _stream(dev, stream)))
+    return load_library().moe_combine, (ctypes.byref(cfg), *args), dev
+
+
+def moe_combine(cfg, expert_out, expert_ids, expand_idx, expert_scales, ep_recv_count,
+                recv_offsets, x_active_mask, ori_x, y, stream=None):
+    """Enqueue one combine on `stream` (default: the current stream of y's device)."""
+    _launch(*_combine_call(cfg, expert_out, expert_ids, expand_idx, expert_scales,
+                           ep_recv_count, recv_offsets, x_active_mask, ori_x, y), stream)
 
 
 def moe_dc_combine_scatter_workspace_bytes(cfg: MoeDcConfig) -> int:
     return load_library().moe_dc_combine_scatter_workspace_bytes(ctypes.byref(cfg))
 
 
-def moe_combine_scatter(cfg, expert_out, assist_info, recv_offsets, expert_ids, expert_scales,
-                        x_active_mask, ori_x, shared_x, y, workspace, stream=None):
-    """Enqueue one scatter-back combine (rows return by their assist_info triples)."""
+def _combine_scatter_call(cfg, expert_out, assist_info, recv_offsets, expert_ids,
+                          expert_scales, x_active_mask, ori_x, shared_x, y, workspace):
     W, BS, H, K, cap = (cfg.ep_world_size, cfg.bs, cfg.hidden, cfg.topk,
                         cfg.expand_rows_capacity)
     dev = y.device
@@ -284,10 +321,16 @@ def moe_combine_scatter(cfg, expert_out, assist_info, recv_offsets, expert_ids, 
         _ptr(workspace, torch.uint8, None, "workspace", dev),
     ]
     ws_bytes = 0 if workspace is None else workspace.numel()
-    with torch.cuda.device(dev):
-        _check(load_library().moe_combine_scatter(ctypes.byref(cfg), *args,
-                                                  ctypes.c_size_t(ws_bytes),
-                                                  _stream(dev, stream)))
+    return (load_library().moe_combine_scatter,
+            (ctypes.byref(cfg), *args, ctypes.c_size_t(ws_bytes)), dev)
+
+
+def moe_combine_scatter(cfg, expert_out, assist_info, recv_offsets, expert_ids, expert_scales,
+                        x_active_mask, ori_x, shared_x, y, workspace, stream=None):
+    """Enqueue one scatter-back combine (rows return by their assist_info triples)."""
+    _launch(*_combine_scatter_call(cfg, expert_out, assist_info, recv_offsets, expert_ids,
+                                   expert_scales, x_active_mask, ori_x, shared_x, y,
+                                   workspace), stream)
 
 
 def combine_block_count(cfg):
@@ -295,8 +338,7 @@ def combine_block_count(cfg):
     return (cfg.hidden + 7) // 8
 
 
-def moe_combine_quantize(cfg, expert_out, recv_offsets, codes, block_scales, stream=None):
-    """Enqueue the expert-side int8 block quantization of rows [0, recv_offsets[W])."""
+def _combine_quantize_call(cfg, expert_out, recv_offsets, codes, block_scales):
     W, H, cap = cfg.ep_world_size, cfg.hidden, cfg.expand_rows_capacity
     dev = codes.device
     args = [
@@ -306,14 +348,16 @@ def moe_combine_quantize(cfg, expert_out, recv_offsets, codes, block_scales, str
         _ptr(block_scales, torch.float32, (cap, combine_block_count(cfg)), "block_scales",
              dev),
     ]
-    with torch.cuda.device(dev):
-        _check(load_library().moe_combine_quantize(ctypes.byref(cfg), *args,
-                                                   _stream(dev, stream)))
+    return load_library().moe_combine_quantize, (ctypes.byref(cfg), *args), dev
 
 
-def moe_combine_int8(cfg, codes, block_scales, expert_ids, expand_idx, expert_scales,
-                     ep_recv_count, recv_offsets, x_active_mask, ori_x, y, stream=None):
-    """Enqueue one combine over int8 block-quantized expert rows."""
+def moe_combine_quantize(cfg, expert_out, recv_offsets, codes, block_scales, stream=None):
+    """Enqueue the expert-side int8 block quantization of rows [0, recv_offsets[W])."""
+    _launch(*_combine_quantize_call(cfg, expert_out, recv_offsets, codes, block_scales), stream)
+
+
+def _combine_int8_call(cfg, codes, block_scales, expert_ids, expand_idx, expert_scales,
+                       ep_recv_count, recv_offsets, x_active_mask, ori_x, y):
     W, BS, H, K, L, cap = (cfg.ep_world_size, cfg.bs, cfg.hidden, cfg.topk, cfg.L,
                            cfg.expand_rows_capacity)
     dev = y.device
@@ -331,8 +375,14 @@ def moe_combine_int8(cfg, codes, block_scales, expert_ids, expand_idx, expert_sc
         _ptr(ori_x, torch.bfloat16, (W, BS, H), "ori_x", dev),
         _ptr(y, torch.bfloat16, (W, BS, H), "y", dev),
     ]
-    with torch.cuda.device(dev):
-        _check(load_library().moe_combine_int8(ctypes.byref(cfg), *args, _stream(dev, stream)))
+    return load_library().moe_combine_int8, (ctypes.byref(cfg), *args), dev
+
+
+def moe_combine_int8(cfg, codes, block_scales, expert_ids, expand_idx, expert_scales,
+                     ep_recv_count, recv_offsets, x_active_mask, ori_x, y, stream=None):
+    """Enqueue one combine over int8 block-quantized expert rows."""
+    _launch(*_combine_int8_call(cfg, codes, block_scales, expert_ids, expand_idx, expert_scales,
+                                ep_recv_count, recv_offsets, x_active_mask, ori_x, y), stream)
 
 
 # -- allocation helpers (torch owns the memory; the library never allocates) ----------------
@@ -358,67 +408,125 @@ def alloc_dispatch_outputs(cfg, device="cuda"):
     )
 
 
-def dispatch(cfg, x, expert_ids, scales=None, x_active_mask=None, out=None, stream=None,
-             expert_scales=None):
-    """Allocate (or reuse `out`) and enqueue moe_dispatch; returns the output dict (with
-    "expand_scales" when expert_scales is given)."""
+def _new_y(cfg, like):
+    return torch.empty((cfg.ep_world_size, cfg.bs, cfg.hidden), dtype=torch.bfloat16,
+                       device=like.device)
+
+
+# Each prepare_* checks and marshals one call once and returns (launch, outputs): calling
+# `launch(stream=None)` enqueues the same call again with the same tensors, costing only the
+# foreign call.  The plain functions below prepare and launch once.
+
+def prepare_dispatch(cfg, x, expert_ids, scales=None, x_active_mask=None, out=None,
+                     expert_scales=None):
+    """Plan for moe_dispatch: (launch, output dict; "expand_scales" when expert_scales is
+    given).  Write new x / expert_ids / mask contents in place between launches."""
     o = alloc_dispatch_outputs(cfg, x.device) if out is None else out
     if expert_scales is not None and o.get("expand_scales") is None:
         o["expand_scales"] = torch.empty((cfg.expand_rows_capacity,), dtype=torch.float32,
                                          device=x.device)
-    moe_dispatch(cfg, x, expert_ids, scales, x_active_mask, o["expand_x"],
-                 o["dynamic_scales"], o["expand_idx"], o["assist_info"], o["ep_recv_count"],
-                 o["expert_token_nums"], o["recv_offsets"], o["workspace"], stream,
-                 expert_scales=expert_scales,
-                 expand_scales=o.get("expand_scales") if expert_scales is not None else None)
+    fn, args, dev = _dispatch_call(
+        cfg, x, expert_ids, scales, x_active_mask, o["expand_x"], o["dynamic_scales"],
+        o["expand_idx"], o["assist_info"], o["ep_recv_count"], o["expert_token_nums"],
+        o["recv_offsets"], o["workspace"], expert_scales,
+        o.get("expand_scales") if expert_scales is not None else None)
+    keep = (cfg, x, expert_ids, scales, x_active_mask, expert_scales, dict(o))
+    return Launch(fn, args, dev, keep), o
+
+
+def dispatch(cfg, x, expert_ids, scales=None, x_active_mask=None, out=None, stream=None,
+             expert_scales=None):
+    """Allocate (or reuse `out`) and enqueue moe_dispatch; returns the output dict (with
+    "expand_scales" when expert_scales is given)."""
+    launch, o = prepare_dispatch(cfg, x, expert_ids, scales, x_active_mask, out, expert_scales)
+    launch(stream)
     return o
+
+
+def prepare_combine(cfg, expert_out, expert_ids, expand_idx, expert_scales, ep_recv_count,
+                    recv_offsets, x_active_mask=None, ori_x=None, y=None):
+    """Plan for moe_combine: (launch, y)."""
+    y = _new_y(cfg, expert_out) if y is None else y
+    fn, args, dev = _combine_call(cfg, expert_out, expert_ids, expand_idx, expert_scales,
+                                  ep_recv_count, recv_offsets, x_active_mask, ori_x, y)
+    keep = (cfg, expert_out, expert_ids, expand_idx, expert_scales, ep_recv_count,
+            recv_offsets, x_active_mask, ori_x, y)
+    return Launch(fn, args, dev, keep), y
+
+
+def combine(cfg, expert_out, expert_ids, expand_idx, expert_scales, ep_recv_count,
+            recv_offsets, x_active_mask=None, ori_x=None, y=None, stream=None):
+    """Allocate (or reuse `y`) and enqueue moe_combine; returns y."""
+    launch, y = prepare_combine(cfg, expert_out, expert_ids, expand_idx, expert_scales,
+                                ep_recv_count, recv_offsets, x_active_mask, ori_x, y)
+    launch(stream)
+    return y
+
+
+def prepare_combine_scatter(cfg, expert_out, assist_info, recv_offsets, expert_ids,
+                            expert_scales, x_active_mask=None, ori_x=None, shared_x=None,
+                            y=None, workspace=None):
+    """Plan for moe_combine_scatter: (launch, y)."""
+    dev = expert_out.device
+    y = _new_y(cfg, expert_out) if y is None else y
+    if workspace is None:
+        workspace = torch.empty((moe_dc_combine_scatter_workspace_bytes(cfg),),
+                                dtype=torch.uint8, device=dev)
+    fn, args, d = _combine_scatter_call(cfg, expert_out, assist_info, recv_offsets,
+                                        expert_ids, expert_scales, x_active_mask, ori_x,
+                                        shared_x, y, workspace)
+    keep = (cfg, expert_out, assist_info, recv_offsets, expert_ids, expert_scales,
+            x_active_mask, ori_x, shared_x, y, workspace)
+    return Launch(fn, args, d, keep), y
 
 
 def combine_scatter(cfg, expert_out, assist_info, recv_offsets, expert_ids, expert_scales,
                     x_active_mask=None, ori_x=None, shared_x=None, y=None, workspace=None,
                     stream=None):
     """Allocate (or reuse `y` / `workspace`) and enqueue moe_combine_scatter; returns y."""
-    dev = expert_out.device
-    if y is None:
-        y = torch.empty((cfg.ep_world_size, cfg.bs, cfg.hidden), dtype=torch.bfloat16,
-                        device=dev)
-    if workspace is None:
-        workspace = torch.empty((moe_dc_combine_scatter_workspace_bytes(cfg),),
-                                dtype=torch.uint8, device=dev)
-    moe_combine_scatter(cfg, expert_out, assist_info, recv_offsets, expert_ids, expert_scales,
-                        x_active_mask, ori_x, shared_x, y, workspace, stream)
+    launch, y = prepare_combine_scatter(cfg, expert_out, assist_info, recv_offsets,
+                                        expert_ids, expert_scales, x_active_mask, ori_x,
+                                        shared_x, y, workspace)
+    launch(stream)
     return y
 
 
-def combine(cfg, expert_out, expert_ids, expand_idx, expert_scales, ep_recv_count,
-            recv_offsets, x_active_mask=None, ori_x=None, y=None, stream=None):
-    """Allocate (or reuse `y`) and enqueue moe_combine; returns y."""
-    if y is None:
-        y = torch.empty((cfg.ep_world_size, cfg.bs, cfg.hidden), dtype=torch.bfloat16,
-                        device=expert_out.device)
-    moe_combine(cfg, expert_out, expert_ids, expand_idx, expert_scales, ep_recv_count,
-                recv_offsets, x_active_mask, ori_x, y, stream)
-    return y
-
-
-def combine_quantize(cfg, expert_out, recv_offsets, out=None, stream=None):
-    """Allocate (or reuse `out` = (codes, block_scales)) and enqueue moe_combine_quantize."""
+def prepare_combine_quantize(cfg, expert_out, recv_offsets, out=None):
+    """Plan for moe_combine_quantize: (launch, (codes, block_scales))."""
     cap, H = cfg.expand_rows_capacity, cfg.hidden
     if out is None:
         out = (torch.empty((cap, H), dtype=torch.int8, device=expert_out.device),
                torch.empty((cap, combine_block_count(cfg)), dtype=torch.float32,
                            device=expert_out.device))
-    moe_combine_quantize(cfg, expert_out, recv_offsets, out[0], out[1], stream)
+    fn, args, dev = _combine_quantize_call(cfg, expert_out, recv_offsets, out[0], out[1])
+    return Launch(fn, args, dev, (cfg, expert_out, recv_offsets, out)), out
+
+
+def combine_quantize(cfg, expert_out, recv_offsets, out=None, stream=None):
+    """Allocate (or reuse `out` = (codes, block_scales)) and enqueue moe_combine_quantize."""
+    launch, out = prepare_combine_quantize(cfg, expert_out, recv_offsets, out)
+    launch(stream)
     return out
+
+
+def prepare_combine_int8(cfg, codes, block_scales, expert_ids, expand_idx, expert_scales,
+                         ep_recv_count, recv_offsets, x_active_mask=None, ori_x=None, y=None):
+    """Plan for moe_combine_int8: (launch, y)."""
+    y = _new_y(cfg, codes) if y is None else y
+    fn, args, dev = _combine_int8_call(cfg, codes, block_scales, expert_ids, expand_idx,
+                                       expert_scales, ep_recv_count, recv_offsets,
+                                       x_active_mask, ori_x, y)
+    keep = (cfg, codes, block_scales, expert_ids, expand_idx, expert_scales, ep_recv_count,
+            recv_offsets, x_active_mask, ori_x, y)
+    return Launch(fn, args, dev, keep), y
 
 
 def combine_int8(cfg, codes, block_scales, expert_ids, expand_idx, expert_scales,
                  ep_recv_count, recv_offsets, x_active_mask=None, ori_x=None, y=None,
                  stream=None):
     """Allocate (or reuse `y`) and enqueue moe_combine_int8; returns y."""
-    if y is None:
-        y = torch.empty((cfg.ep_world_size, cfg.bs, cfg.hidden), dtype=torch.bfloat16,
-                        device=codes.device)
-    moe_combine_int8(cfg, codes, block_scales, expert_ids, expand_idx, expert_scales,
-                     ep_recv_count, recv_offsets, x_active_mask, ori_x, y, stream)
+    launch, y = prepare_combine_int8(cfg, codes, block_scales, expert_ids, expand_idx,
+                                     expert_scales, ep_recv_count, recv_offsets,
+                                     x_active_mask, ori_x, y)
+    launch(stream)
     return y

@@ -1,0 +1,110 @@
+"""GPU checks of the launch plans (prepare_*): a plan checks and marshals one C-ABI call
+once; each launch enqueues it again with the same tensors.  Outputs must match the CPU oracle
+(dispatch bit for bit, combine within 1e-2 relative / 1e-3 absolute) after the inputs are
+rewritten in place, on a side stream, and when the launches are captured in a HIP graph and
+replayed with new inputs between replays."""
+import numpy as np
+import pytest
+
+import harness
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+WL = workloads.Workload
+
+CASES = {
+    "c1_mode2": workloads.C1_MODE2,
+    "mx_e5m2_e8m0_mask": WL("mx_e5m2_e8m0_mask", W=4, E=32, BS=60, H=2048, K=8, quant_mode=4,
+                            out_dtype=3, scale_format=1, mask_kind=1,
+                            inactive_tokens_per_rank=6, copy_expert_num=1),
+}
+
+
+def _expect(wl, inp, eo):
+    ocfg, ref = harness.oracle_dispatch(wl, inp)
+    y_ref = oracle.combine(ocfg, eo, inp["expert_ids"], ref["expand_idx"],
+                           inp["expert_scales"], ref["ep_recv_count"], ref["recv_offsets"],
+                           mask=inp.get("mask"), ori_x=inp["x"])
+    return ref, y_ref
+
+
+def _plans(wl, inp, eo_dev):
+    import combine_quant_amd as cq
+    cfg = harness.lib_cfg(wl)
+    x = harness.bf16_dev(inp["x"])
+    ids = harness.to_dev(inp["expert_ids"])
+    mask = harness.to_dev(inp.get("mask"))
+    w = harness.to_dev(inp["expert_scales"])
+    d, out = cq.prepare_dispatch(cfg, x, ids, None, mask)
+    c, y = cq.prepare_combine(cfg, eo_dev, ids, out["expand_idx"], w, out["ep_recv_count"],
+                              out["recv_offsets"], mask, x)
+    return dict(x=x, ids=ids, mask=mask, w=w), d, out, c, y
+
+
+def _refill(dev_in, inp):
+    import torch
+    dev_in["x"].copy_(harness.bf16_dev(inp["x"]))
+    dev_in["ids"].copy_(harness.to_dev(inp["expert_ids"]))
+    if dev_in["mask"] is not None:
+        dev_in["mask"].copy_(harness.to_dev(inp["mask"]))
+    dev_in["w"].copy_(harness.to_dev(inp["expert_scales"]))
+    torch.cuda.synchronize()
+
+
+def _eo(wl, seed):
+    rng = np.random.default_rng(seed)
+    return workloads.f32_to_bf16_bits(rng.standard_normal((wl.cap, wl.H), dtype=np.float32))
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_plan_relaunch_with_new_inputs(name):
+    import torch
+    wl = CASES[name]
+    eo = _eo(wl, 9)
+    eo_dev = harness.bf16_dev(eo)
+    inp0 = workloads.generate(wl, seed=0)
+    dev_in, d, out, c, y = _plans(wl, inp0, eo_dev)
+    side = torch.cuda.Stream()
+    for seed, stream in ((0, None), (1, None), (2, side)):
+        inp = workloads.generate(wl, seed=seed)
+        _refill(dev_in, inp)
+        if stream is not None:
+            stream.wait_stream(torch.cuda.current_stream())
+        d(stream)
+        c(stream)
+        torch.cuda.synchronize()
+        ref, y_ref = _expect(wl, inp, eo)
+        harness.compare_dispatch(wl, inp, out, ref)
+        harness.check_combine_tolerance(harness.host(y), y_ref)
+
+
+def test_plans_captured_in_a_graph():
+    """Capture dispatch + combine plan launches once; replay after rewriting the inputs in
+    place, with eager work and synchronizations between replays; every replay must match the
+    oracle on its own inputs."""
+    import torch
+    wl = CASES["mx_e5m2_e8m0_mask"]
+    eo = _eo(wl, 4)
+    eo_dev = harness.bf16_dev(eo)
+    dev_in, d, out, c, y = _plans(wl, workloads.generate(wl, seed=0), eo_dev)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):          # warm up on the capture stream
+        d()
+        c()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        d()
+        c()
+    for seed in (5, 6, 7):
+        inp = workloads.generate(wl, seed=seed)
+        _refill(dev_in, inp)
+        g.replay()
+        torch.cuda.synchronize()
+        ref, y_ref = _expect(wl, inp, eo)
+        harness.compare_dispatch(wl, inp, out, ref)
+        harness.check_combine_tolerance(harness.host(y), y_ref)
+        torch.zeros(1024, device="cuda").sum().item()     # eager work between replays
