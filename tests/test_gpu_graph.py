@@ -17,6 +17,11 @@ CASES = {
         copy_expert_num=1, mask_kind=2, inactive_tokens_per_rank=6, routing="randint"),
     "mx_e5m2_e8m0": workloads.Workload("graph_mx", W=4, E=32, BS=40, H=2048, K=6,
                                        quant_mode=5, out_dtype=3, scale_format=1),
+    # 6,400 picks: routing and prefix sums run as kernels of their own (the two cases above
+    # route inside the scatter launch)
+    "int8_three_launches": workloads.Workload("graph_int8_large", W=4, E=32, BS=200, H=1024,
+                                              K=8, quant_mode=2, mask_kind=1,
+                                              inactive_tokens_per_rank=9),
 }
 
 
