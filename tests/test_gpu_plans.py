@@ -2,7 +2,8 @@
 once; each launch enqueues it again with the same tensors.  Outputs must match the CPU oracle
 (dispatch bit for bit, combine within 1e-2 relative / 1e-3 absolute) after the inputs are
 rewritten in place, on a side stream, and when the launches are captured in a HIP graph and
-replayed with new inputs between replays."""
+replayed with new inputs between replays.  Repeated calls of every entry point leave the
+device's free memory unchanged (the library allocates nothing)."""
 import numpy as np
 import pytest
 
@@ -108,3 +109,32 @@ def test_plans_captured_in_a_graph():
         harness.compare_dispatch(wl, inp, out, ref)
         harness.check_combine_tolerance(harness.host(y), y_ref)
         torch.zeros(1024, device="cuda").sum().item()     # eager work between replays
+
+
+def test_library_calls_allocate_no_device_memory():
+    """The C ABI never allocates: with every buffer made up front, repeated calls of each
+    entry point leave the device's free memory unchanged."""
+    import torch
+    import combine_quant_amd as cq
+    wl = CASES["mx_e5m2_e8m0_mask"]
+    inp = workloads.generate(wl, seed=1)
+    eo_dev = harness.bf16_dev(_eo(wl, 2))
+    dev_in, d, out, c, y = _plans(wl, inp, eo_dev)
+    cfg = harness.lib_cfg(wl)
+    q, (codes, bscales) = cq.prepare_combine_quantize(cfg, eo_dev, out["recv_offsets"])
+    c8, _ = cq.prepare_combine_int8(cfg, codes, bscales, dev_in["ids"], out["expand_idx"],
+                                    dev_in["w"], out["ep_recv_count"], out["recv_offsets"],
+                                    dev_in["mask"], dev_in["x"])
+    ys, _ = cq.prepare_combine_scatter(cfg, eo_dev, out["assist_info"], out["recv_offsets"],
+                                       dev_in["ids"], dev_in["w"], dev_in["mask"], dev_in["x"])
+    calls = (d, c, q, c8, ys)
+    for f in calls:                      # first calls load the code objects
+        f()
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    for _ in range(20):
+        for f in calls:
+            f()
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert free1 == free0, (free0, free1)
