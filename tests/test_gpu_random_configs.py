@@ -1,0 +1,67 @@
+"""GPU parity over seeded random configurations: each case draws a valid attribute set
+(ranks, experts, special experts, batch, hidden size including ragged and element-wise
+sizes, top-k, every quant mode with every output type, scales shape and scale format it
+allows, both mask kinds, the three routings) and a seeded input, then compares the HIP
+library with the CPU oracle -- dispatch bit for bit, combine within 1e-2 relative / 1e-3
+absolute -- on both routing paths (inside the scatter launch where the batch is small, and
+as kernels of their own)."""
+import numpy as np
+import pytest
+
+import harness
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 100
+
+# (out_dtype, scales_kind, scale_format) choices per quant mode
+_VARIANTS = {
+    0: [(0, 0, 0)],
+    1: [(o, k, 0) for o in (0, 1) for k in (1, 2, 3)],
+    2: [(o, k, 0) for o in (0, 1, 2, 3) for k in (0, 1, 2, 3)],
+    3: [(o, k, 0) for o in (0, 2, 3) for k in (0, 1, 2, 3)],
+    4: [(o, 0, f) for o in (0, 2, 3, 4) for f in (0, 1)],
+    5: [(o, 0, f) for o in (0, 2, 3, 4) for f in (0, 1)],
+}
+_H = (1024, 1030, 1032, 1040, 1056, 1152, 1280, 2048, 2056)
+
+
+def random_workload(i):
+    rng = np.random.default_rng(1000 + i)
+    W = int(rng.choice([2, 3, 4, 8]))
+    E = W * int(rng.choice([1, 2, 4, 8]))
+    Z, C = int(rng.choice([0, 0, 1, 2])), int(rng.choice([0, 0, 1]))
+    routing = str(rng.choice(["uniform", "randint", "zipf"]))
+    if routing == "zipf":
+        Z = C = 0
+    n_ids = E + Z + C
+    kmax = min(16, E if routing == "zipf" else n_ids)
+    K = int(rng.integers(1, kmax + 1))
+    BS = int(rng.integers(1, 48))
+    H = int(rng.choice(_H))
+    mode = int(rng.integers(0, 6))
+    variants = [v for v in _VARIANTS[mode] if not (v[0] == 4 and H % 2)]
+    out_dtype, scales_kind, scale_format = variants[int(rng.integers(0, len(variants)))]
+    mask_kind = int(rng.choice([0, 1, 2]))
+    inactive = int(rng.integers(0, BS // 2 + 1)) if mask_kind else 0
+    return workloads.Workload(
+        f"rand{i}", W=W, E=E, BS=BS, H=H, K=K, quant_mode=mode, zero_expert_num=Z,
+        copy_expert_num=C, expert_token_nums_type=int(rng.integers(0, 2)),
+        mask_kind=mask_kind, scales_kind=scales_kind, out_dtype=out_dtype,
+        scale_format=scale_format, routing=routing, inactive_tokens_per_rank=inactive,
+        outlier_prob=float(rng.choice([0.0, 0.02])))
+
+
+def test_random_configs_are_valid():
+    import combine_quant_amd as cq
+    for i in range(N_CASES):
+        wl = random_workload(i)
+        assert cq.moe_dc_validate(harness.lib_cfg(wl)) == cq.MOE_OK, (wl, cq.moe_dc_last_error())
+
+
+@pytest.mark.parametrize("flags", [0, 1])     # 1: MOE_DC_FLAG_SEPARATE_ROUTE
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_config_roundtrip(i, flags):
+    wl = random_workload(i)
+    harness.roundtrip(wl, seed=i, flags=flags)
