@@ -4,7 +4,8 @@ sizes, top-k, every quant mode with every output type, scales shape and scale fo
 allows, both mask kinds, the three routings) and a seeded input, then compares the HIP
 library with the CPU oracle -- dispatch bit for bit, combine within 1e-2 relative / 1e-3
 absolute -- on both routing paths (inside the scatter launch where the batch is small, and
-as kernels of their own)."""
+as kernels of their own).  The int8 block-quantized and scatter-back combines run over the
+same configurations."""
 import numpy as np
 import pytest
 
@@ -65,3 +66,18 @@ def test_random_configs_are_valid():
 def test_random_config_roundtrip(i, flags):
     wl = random_workload(i)
     harness.roundtrip(wl, seed=i, flags=flags)
+
+
+# the other two combines over the same random configurations: the int8 block-quantized
+# combine (codes and block scales bit for bit, y within tolerance) on even cases, the
+# scatter-back combine (with a shared expert's output on every other one) on odd cases
+@pytest.mark.parametrize("i", range(0, N_CASES, 2))
+def test_random_config_int8_combine(i):
+    import test_gpu_combine_quant as combine_quant_tests
+    combine_quant_tests._run(random_workload(i), seed=i)
+
+
+@pytest.mark.parametrize("i", range(1, N_CASES, 2))
+def test_random_config_scatter_back(i):
+    import test_gpu_combine_scatter as combine_scatter_tests
+    combine_scatter_tests._run(random_workload(i), i, with_shared=(i % 4 == 1))
