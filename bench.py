@@ -284,20 +284,25 @@ def run_bench(args):
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for n in range(args.warmup):
-        step(n)
+        step(n, timed=False)
     torch.cuda.synchronize()
+    # 1. the step time: K steps with nothing but their launches between two events
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
-    evs = [step(n) for n in range(args.steps)]
+    for n in range(args.steps):
+        step(n, timed=False)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
     eager_ms_per_step = total_ms / args.steps
+    # 2. per-kernel times: the same K steps again, with events around every launch
+    evs = [step(n) for n in range(args.steps)]
+    torch.cuda.synchronize()
 
     if args.graph:
         # one graph per buffer set, each holding one whole step; the warm-up above ran every
