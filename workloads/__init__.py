@@ -12,7 +12,9 @@ DeepSeek-V3-style 256-expert routing.
 
 Recipe (numpy PCG64, one spawned sub-stream per tensor, base seed 0 by default):
   x              bf16 of N(0,1) fp32 samples (round to nearest even); optional outliers:
-                 each value independently x10 with the workload's probability
+                 each value independently x10 with the workload's probability.  At the
+                 largest sizes x is drawn on the device with torch's seeded generator
+                 instead (x_torch)
   expert_ids     uniform: K distinct ids per token, in the order of a uniform random
                  permutation; zipf: K distinct ids drawn one after another without
                  replacement with probability proportional to 1/rank^s over a seeded
@@ -284,16 +286,38 @@ def generate(wl: Workload, seed: int = 0, expert_out_rows: int | None = None) ->
         xf = bf16_bits_to_f32(x)
         xf[hit] *= np.float32(10.0)
         x = f32_to_bf16_bits(xf)
-    out = dict(
-        x=x,
+    out = dict(x=x, **generate_routing(wl, seed))
+    if expert_out_rows is not None:
+        out["expert_out"] = _normal_bf16(st[_EXPERT_OUT], (expert_out_rows, wl.H))
+    return out
+
+
+def generate_routing(wl: Workload, seed: int = 0) -> dict:
+    """Every host input of generate() except x (each tensor has its own sub-stream, so the
+    values are the same as generate()'s)."""
+    st = _streams(seed)
+    return dict(
         expert_ids=gen_expert_ids(wl, st[_IDS]),
         mask=gen_mask(wl, st[_MASK]),
         expert_scales=gen_expert_scales(wl, st[_WEIGHTS]),
         scales=gen_scales(wl, st[_SMOOTH]),
     )
-    if expert_out_rows is not None:
-        out["expert_out"] = _normal_bf16(st[_EXPERT_OUT], (expert_out_rows, wl.H))
-    return out
+
+
+def x_torch(wl: Workload, seed: int = 0, device="cuda"):
+    """bf16 N(0,1) tokens [W][BS][H] drawn on the device with torch's seeded generator, for
+    sizes where the numpy draw would take minutes (no outliers).  The oracle reads the host
+    copy of the same bytes."""
+    import torch
+    if wl.outlier_prob > 0:
+        raise ValueError("x_torch draws no outliers")
+    g = torch.Generator(device=device)
+    g.manual_seed(int(np.random.SeedSequence(seed).spawn(N_STREAMS)[_X].generate_state(1)[0]))
+    x = torch.empty((wl.W, wl.BS, wl.H), dtype=torch.bfloat16, device=device)
+    for s in range(wl.W):            # one rank at a time: a small fp32 temporary
+        x[s] = torch.randn((wl.BS, wl.H), generator=g, device=device,
+                           dtype=torch.float32).to(torch.bfloat16)
+    return x
 
 
 def expert_out_torch(wl: Workload, rows: int, seed: int = 0, device="cuda"):
