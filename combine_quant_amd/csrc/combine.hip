@@ -41,6 +41,10 @@ constexpr int kCopy = -2;   // copy expert: read ori_x
 // j, source s) + expand_idx.  With INV = true, `pick_rows` is the map written by the
 // scatter-back step (slot tok * K + k -> the row that was sent back to it).  Rows outside
 // [0, cap) are treated as unresolvable.
+// The loads that depend only on the pick (expert id, expand_idx or slot row, mask byte) are
+// issued together, then the two that depend on the expert (the rank's window start and the
+// running total), so a task waits two load round trips before its row loads, not one per
+// field.
 template <bool INV>
 __device__ __forceinline__ int pick_source(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ pick_rows,
@@ -50,21 +54,19 @@ __device__ __forceinline__ int pick_source(
 {
     const long long p = tok * K + k;
     const int32_t e = ids[p];
-    const bool on = mask_kind == 0 || (mask_kind == 1 ? mask[tok] != 0 : mask[p] != 0);
+    const int32_t ord = pick_rows[p];
+    const bool on = mask_kind == 0 || mask[mask_kind == 1 ? tok : p] != 0;
     if (!on || e < 0) return kNone;
-    if (e < E && INV) {
-        const int32_t row = pick_rows[p];
-        return (row >= 0 && row < cap) ? (int)row : kNone;
-    }
+    if (e < E && INV) return (ord >= 0 && ord < cap) ? (int)ord : kNone;
     if (e < E) {
-        const int32_t ord = pick_rows[p];
         if (ord < 0) return kNone;
         const int r = e / L;
         const int j = e - r * L;
         const long long flat = (long long)j * W + s;
+        const long long window = recv_offsets[r];
         const long long base =
             flat == 0 ? 0 : (long long)ep_recv_count[(long long)r * L * W + flat - 1];
-        const long long row = (long long)recv_offsets[r] + base + ord;
+        const long long row = window + base + ord;
         return (row >= 0 && row < cap) ? (int)row : kNone;
     }
     return (e >= zero_end && e < id_end) ? kCopy : kNone;
@@ -100,15 +102,34 @@ __device__ __forceinline__ void accumulate8_int8(uint2 q, float scale, float w, 
 
 typedef uint32_t u32x2_ld_t __attribute__((ext_vector_type(2)));
 
+// Non-temporal 16-byte load through a pointer marked as global memory: a row base picked
+// among several buffers at run time would otherwise be accessed with flat instructions.
+typedef const __attribute__((address_space(1))) u32x4_t* global_u32x4_ptr;
+
+typedef const __attribute__((address_space(1))) u32x2_ld_t* global_u32x2_ptr;
+typedef const __attribute__((address_space(1))) float* global_f32_ptr;
+
+__device__ __forceinline__ uint4 load_row(const uint4* p)
+{
+    const u32x4_t v = __builtin_nontemporal_load((global_u32x4_ptr)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint2 load_row8(const uint2* p)
+{
+    const u32x2_ld_t v = __builtin_nontemporal_load((global_u32x2_ptr)p);
+    return make_uint2(v.x, v.y);
+}
+
+__device__ __forceinline__ float load_row4(const float* p)
+{
+    return __builtin_nontemporal_load((global_f32_ptr)p);
+}
+
 __device__ __forceinline__ uint2 load_stream8(const uint2* p)
 {
     const u32x2_ld_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_ld_t*>(p));
     return make_uint2(v.x, v.y);
-}
-
-__device__ __forceinline__ float load_stream4(const float* p)
-{
-    return __builtin_nontemporal_load(p);
 }
 
 constexpr int kWavesPerBlock = 4;
@@ -137,7 +158,9 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_wave_kernel(
     int id_end, long long cap, long long T, int tasks_per_token)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    const long long task = (long long)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
+    // the wave's index, as a wave-uniform value (so the task's row bases stay scalar)
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    const long long task = (long long)blockIdx.x * kWavesPerBlock + wave;
     const long long tok = task / tasks_per_token;
     if (tok >= T) return;                                  // whole wave
     const int slot0 = (int)(task - tok * tasks_per_token) * SLOTS;
@@ -147,9 +170,9 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_wave_kernel(
     int src = kNone;
     float wk = 0.0f;
     if (lane < K) {
+        wk = weights[tok * K + lane];
         src = pick_source<INV>(ids, expand_idx, ep_recv_count, recv_offsets, mask, mask_kind,
                                W, E, L, K, zero_end, id_end, cap, tok, s, lane);
-        wk = weights[tok * K + lane];
     }
     int srcs[KMAX];
     float ws[KMAX];
@@ -159,10 +182,28 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_wave_kernel(
         ws[k] = lane_value(wk, k);
     }
 
+    // One load per pick and slot from a wave-uniform base: the pick's expert-output row, or
+    // ori_x for a copy expert (bf16 rows).  The K loads of a slot then go out back to back;
+    // loading alternatives into the same registers on two paths would make the compiler
+    // wait for every earlier load before each of them.
     const uint4* eo = reinterpret_cast<const uint4*>(expert_out);
     const uint2* eq = reinterpret_cast<const uint2*>(expert_out);
-    const uint4* self = ori_x ? reinterpret_cast<const uint4*>(ori_x) + tok * NV : nullptr;
+    // ori_x is only read for copy experts, which exist only when it is given
+    const uint4* self = reinterpret_cast<const uint4*>(ori_x ? ori_x : y) + tok * NV;
     uint4* yr = reinterpret_cast<uint4*>(y) + tok * NV;
+    const uint4* rowp[KMAX];       // valid where `loads` has bit k
+    uint32_t loads = 0;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        rowp[k] = eo;
+        if (srcs[k] >= 0) {
+            rowp[k] = eo + (long long)srcs[k] * NV;
+            loads |= 1u << k;
+        } else if (Q == 0 && srcs[k] == kCopy) {
+            rowp[k] = self;
+            loads |= 1u << k;
+        }
+    }
     uint4 buf[SLOTS][KMAX];
     uint4 shv[SLOTS];
 #pragma unroll
@@ -172,16 +213,14 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_wave_kernel(
             if (SHARED) shv[n] = load_stream(reinterpret_cast<const uint4*>(shared_x) + tok * NV + v);
 #pragma unroll
             for (int k = 0; k < KMAX; ++k) {
-                if (srcs[k] >= 0) {
-                    if (Q == 0) {
-                        buf[n][k] = load_stream(eo + (long long)srcs[k] * NV + v);
-                    } else {
-                        const uint2 q = load_stream8(eq + (long long)srcs[k] * NV + v);
-                        const float sc = load_stream4(qscales + (long long)srcs[k] * NV + v);
-                        buf[n][k] = make_uint4(q.x, q.y, __float_as_uint(sc), 0u);
-                    }
-                } else if (srcs[k] == kCopy) {
-                    buf[n][k] = self[v];
+                if (!(loads & (1u << k))) continue;
+                if (Q == 0) {
+                    buf[n][k] = load_row(rowp[k] + v);
+                } else {
+                    const long long r = srcs[k];               // a routed pick's row
+                    const uint2 q = load_row8(eq + r * NV + v);
+                    const float sc = load_row4(qscales + r * NV + v);
+                    buf[n][k] = make_uint4(q.x, q.y, __float_as_uint(sc), 0u);
                 }
             }
         }
@@ -199,6 +238,8 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_wave_kernel(
                 if (Q == 1 && srcs[k] >= 0)
                     accumulate8_int8(make_uint2(buf[n][k].x, buf[n][k].y),
                                      __uint_as_float(buf[n][k].z), ws[k], acc);
+                else if (Q == 1)                    // copy expert: its ori_x vector, read here
+                    accumulate8(self[v], ws[k], acc);
                 else
                     accumulate8(buf[n][k], ws[k], acc);
             }
@@ -235,9 +276,9 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_int8_wide_kern
     int src = kNone;
     float wk = 0.0f;
     if (lane < K) {
+        wk = weights[tok * K + lane];
         src = pick_source<false>(ids, expand_idx, ep_recv_count, recv_offsets, mask, mask_kind,
                                W, E, L, K, zero_end, id_end, cap, tok, s, lane);
-        wk = weights[tok * K + lane];
     }
     int srcs[KMAX];
     float ws[KMAX];
