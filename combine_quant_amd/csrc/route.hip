@@ -37,22 +37,26 @@ constexpr int kScanThreads = 1024;    // >= E (E <= 1024 is validated)
 constexpr int kScanLdsCounts = 16384; // counts staged in LDS by the scan (64 KiB)
 
 // Expert id of each pick of token `tok`, or -1 when the pick is not routed (inactive,
-// special expert, or an id outside [0, E)).
+// special expert, or an id outside [0, E)).  Every load of the token (ids, mask bytes) is
+// issued before any of them is used, so they are in flight together.
 template <int KMAX>
 __device__ __forceinline__ void routed_picks(const int32_t* __restrict__ ids,
                                              const uint8_t* __restrict__ mask, int mask_kind,
                                              int K, int E, long long tok, int32_t (&e)[KMAX])
 {
+    int32_t v[KMAX];
+    uint8_t m[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) v[k] = k < K ? ids[tok * K + k] : -1;
+    if (mask_kind == 2) {
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) m[k] = k < K ? mask[tok * K + k] : 0;
+    }
     const bool tok_on = mask_kind != 1 || mask[tok] != 0;
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
-        int32_t v = -1;
-        if (k < K) {
-            v = ids[tok * K + k];
-            const bool on = tok_on && (mask_kind != 2 || mask[tok * K + k] != 0);
-            if (!on || v < 0 || v >= E) v = -1;
-        }
-        e[k] = v;
+        const bool on = tok_on && (mask_kind != 2 || m[k] != 0);
+        e[k] = (k < K && on && (uint32_t)v[k] < (uint32_t)E) ? v[k] : -1;
     }
 }
 
@@ -64,15 +68,22 @@ __device__ __forceinline__ void routed_picks_vec(const int32_t* __restrict__ ids
                                                  int E, long long tok, int32_t (&e)[KMAX])
 {
     const int4* p = reinterpret_cast<const int4*>(ids + tok * KMAX);
+    int4 v[KMAX >= 4 ? KMAX / 4 : 1];
+    uint8_t m[KMAX];
+#pragma unroll
+    for (int q = 0; q < KMAX / 4; ++q) v[q] = p[q];
+    if (mask_kind == 2) {
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) m[k] = mask[tok * KMAX + k];
+    }
     const bool tok_on = mask_kind != 1 || mask[tok] != 0;
 #pragma unroll
     for (int q = 0; q < KMAX / 4; ++q) {
-        const int4 v = p[q];
-        const int32_t r[4] = {v.x, v.y, v.z, v.w};
+        const int32_t r[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int k = 4 * q + c;
-            const bool on = tok_on && (mask_kind != 2 || mask[tok * KMAX + k] != 0);
+            const bool on = tok_on && (mask_kind != 2 || m[k] != 0);
             e[k] = (on && (uint32_t)r[c] < (uint32_t)E) ? r[c] : -1;
         }
     }
@@ -223,7 +234,19 @@ __global__ __launch_bounds__(kScanThreads) void scan_flat_kernel(
     int32_t* rank_first = lds_ex + N + 1 + ((N + 1) >> 5) + 1;
     const int t = threadIdx.x;
 #define ex(f) lds_ex[(f) + ((f) >> 5)]
-    for (int f = t; f < N; f += blockDim.x) ex(f) = seg[f];
+    // all of this thread's counts are requested before the first is stored to LDS, so the
+    // loads are in flight together (the launch has kScanThreads threads and N fits in LDS)
+    int32_t staged[kScanLdsCounts / kScanThreads];
+#pragma unroll
+    for (int j = 0; j < kScanLdsCounts / kScanThreads; ++j) {
+        const int f = t + j * kScanThreads;
+        staged[j] = f < N ? seg[f] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kScanLdsCounts / kScanThreads; ++j) {
+        const int f = t + j * kScanThreads;
+        if (f < N) ex(f) = staged[j];
+    }
     __syncthreads();
     const int per = (N + blockDim.x - 1) / blockDim.x;
     const int lo = min(N, t * per);
