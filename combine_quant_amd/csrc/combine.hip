@@ -13,7 +13,7 @@
 // accumulate in fp32, cast down), and stores the bf16 rounding of the sum.
 //
 // Vectorized path (H % 8 == 0, 16-byte aligned): a token's row is cut into chunks of 128
-// 16-byte vectors (64 for K > 8), each handled by one independent wavefront, which resolves
+// 16-byte vectors, each handled by one independent wavefront, which resolves
 // the token's sources in lanes 0..K-1 and broadcasts them as wave-uniform values; expert rows
 // are read and y is written with the non-temporal policy; no workgroup barrier.  Element-wise
 // fallback (any H, any alignment): one workgroup per token, one element per lane.
@@ -134,9 +134,9 @@ __device__ __forceinline__ uint2 load_stream8(const uint2* p)
 
 constexpr int kWavesPerBlock = 4;
 
-// 64-vector slots of one token per wave task: two (16 row loads in flight per lane at K=8);
-// one for K > 8, where two would need 32 loads' worth of registers and halve occupancy.
-constexpr int slots_per_task(int kmax) { return kmax > 8 ? 1 : 2; }
+// 64-vector slots of one token per wave task: two, so a lane has 2K row loads in flight
+// (at K = 16 that halves the waves per SIMD, and is still faster than one slot).
+constexpr int slots_per_task(int) { return 2; }
 
 // One wave task = one token x SLOTS slots of 64 16-byte vectors.  A token's row is
 // split across several independent waves (each resolves the token's K sources itself), so a
