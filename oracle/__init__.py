@@ -20,7 +20,11 @@ _lib = None
 class OracleCfg(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "W", "E", "BS", "H", "K", "quant_mode", "zero_expert_num", "copy_expert_num",
-        "expert_token_nums_type", "mask_kind", "out_dtype", "scales_kind", "scale_format")]
+        "expert_token_nums_type", "mask_kind", "out_dtype", "scales_kind", "scale_format",
+        "token_dtype")]
+
+# token element types (x, ori_x, expert outputs, y)
+TOKEN_BF16, TOKEN_F16 = 0, 1
 
 # element types of expand_x (out_dtype values; 0 selects the quant mode's default)
 CODE_BF16, CODE_INT8, CODE_E4M3, CODE_E5M2, CODE_E2M1 = 0, 1, 2, 3, 4
@@ -52,6 +56,7 @@ def _load():
             "oracle_int8_from_f16": (ctypes.c_int8, [u16]),
             "oracle_combine_block_count": (i32, [i32]),
             "oracle_combine_quant_row": (None, [P, i32, P, P]),
+            "oracle_combine_quant_row_tok": (None, [i32, P, i32, P, P]),
             "oracle_combine_dequant_row": (None, [P, P, i32, P]),
             "oracle_combine_quantize": (i32, [P] * 5),
             "oracle_combine_int8": (i32, [P] * 13),
@@ -62,6 +67,7 @@ def _load():
             "oracle_code_type": (i32, [i32, i32]),
             "oracle_scale_count": (i32, [i32, i32]),
             "oracle_quant_row": (i32, [i32, i32, P, P, i32, i32, P, P]),
+            "oracle_quant_row_tok": (i32, [i32, i32, i32, P, P, i32, i32, P, P]),
             "oracle_quant_int8_row": (None, [P, P, i32, P, P]),
             "oracle_quant_mx_row": (None, [P, i32, i32, P, P]),
             "oracle_route": (i32, [P, P, P, P, P]),
@@ -90,9 +96,10 @@ def _c(a, dtype):
 
 def make_cfg(W, E, BS, H, K, quant_mode=0, zero_expert_num=0, copy_expert_num=0,
              expert_token_nums_type=1, mask_kind=0, out_dtype=0, scales_kind=0,
-             scale_format=0):
+             scale_format=0, token_dtype=TOKEN_BF16):
     return OracleCfg(W, E, BS, H, K, quant_mode, zero_expert_num, copy_expert_num,
-                     expert_token_nums_type, mask_kind, out_dtype, scales_kind, scale_format)
+                     expert_token_nums_type, mask_kind, out_dtype, scales_kind, scale_format,
+                     token_dtype)
 
 
 def _ref(cfg):
@@ -198,9 +205,10 @@ def quant_mx_row(x_bf16, clip):
     return codes, scales
 
 
-def quant_row(quant_mode, x_bf16, pre=None, out_dtype=0):
-    """Quantize one row; pre is None, a 1-element array (scalar) or an H-element row.
-    Returns (codes, scales) with codes int8 for the int8 type, else uint8."""
+def quant_row(quant_mode, x_bf16, pre=None, out_dtype=0, token_dtype=TOKEN_BF16):
+    """Quantize one row (bf16 bit patterns, or binary16 with token_dtype=TOKEN_F16); pre is
+    None, a 1-element array (scalar) or an H-element row.  Returns (codes, scales) with codes
+    int8 for the int8 type, else uint8."""
     x = _c(x_bf16, np.uint16)
     H = x.shape[0]
     ct = code_type(quant_mode, out_dtype)
@@ -208,8 +216,9 @@ def quant_row(quant_mode, x_bf16, pre=None, out_dtype=0):
     codes = np.empty(code_row_bytes(ct, H) // np.dtype(code_np_dtype(ct)).itemsize,
                      code_np_dtype(ct))
     scales = np.empty(max(1, scale_count(quant_mode, H)), np.float32)
-    rc = _load().oracle_quant_row(int(quant_mode), ct, _p(x), _p(pr),
-                                  0 if pr is None else pr.shape[0], H, _p(codes), _p(scales))
+    rc = _load().oracle_quant_row_tok(int(token_dtype), int(quant_mode), ct, _p(x), _p(pr),
+                                      0 if pr is None else pr.shape[0], H, _p(codes),
+                                      _p(scales))
     if rc != 0:
         raise ValueError(f"oracle_quant_row rejected the arguments (rc={rc})")
     return codes, scales[:scale_count(quant_mode, H)]
@@ -321,12 +330,12 @@ def combine_token(cfg, expert_out, expert_ids, expand_idx, expert_scales, ep_rec
 
 # -- combine-side int8 block quantization ------------------------------------------------------
 
-def combine_quant_row(row_bf16):
+def combine_quant_row(row_bf16, token_dtype=TOKEN_BF16):
     x = _c(row_bf16, np.uint16)
     H = x.shape[0]
     q = np.empty(H, np.int8)
     sc = np.empty(combine_block_count(H), np.float32)
-    _load().oracle_combine_quant_row(_p(x), H, _p(q), _p(sc))
+    _load().oracle_combine_quant_row_tok(int(token_dtype), _p(x), H, _p(q), _p(sc))
     return q, sc
 
 

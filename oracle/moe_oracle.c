@@ -367,6 +367,18 @@ static uint8_t encode(int32_t ct, float v)
  *   scale = 1.0 / dyn
  * An all-zero segment gives dyn = +inf and products 0 * inf = NaN; every NaN product is
  * encoded as 0 (reading R21: R5 taken for the fp8 types too), and its scale is 1/inf = 0. */
+/* Token elements (x, ori_x, expert outputs, y): bf16 (token_dtype 0) or IEEE binary16 (1).
+ * Widening is exact for both; narrowing rounds to nearest, ties to even. */
+static float tok_to_f32(int32_t token_dtype, uint16_t b)
+{
+    return token_dtype ? oracle_f16_to_f32(b) : oracle_bf16_to_f32(b);
+}
+
+static uint16_t f32_to_tok(int32_t token_dtype, float f)
+{
+    return token_dtype ? oracle_f32_to_f16(f) : oracle_f32_to_bf16(f);
+}
+
 static float quant_dynamic(int32_t ct, const float* f, int32_t h0, int32_t h1, uint8_t* q)
 {
     float amax = 0.0f;
@@ -422,7 +434,7 @@ static float quant_mx_block(int32_t ct, int32_t clip, const float* f, int32_t h0
     return sc;
 }
 
-/* Quantize one token row x (bf16 [H]) for a quant mode and code type, after multiplying it
+/* Quantize one token row x (bf16 [H]; binary16 through oracle_quant_row_tok) for a quant mode and code type, after multiplying it
  * by `pre` when given: pre_len 1 = one scalar for every element, pre_len H = one value per
  * element, 0 = no multiplier ([LLD] 计算公式: x_fp32 = CastToFp32(x) * scales; the scales
  * tensor may be a scalar, a row shared by the experts or the routed expert's row, per
@@ -438,6 +450,13 @@ int32_t oracle_quant_row(int32_t quant_mode, int32_t code_type, const uint16_t* 
                          const float* pre, int32_t pre_len, int32_t H, void* codes,
                          float* scales)
 {
+    return oracle_quant_row_tok(0, quant_mode, code_type, x, pre, pre_len, H, codes, scales);
+}
+
+int32_t oracle_quant_row_tok(int32_t token_dtype, int32_t quant_mode, int32_t code_type,
+                             const uint16_t* x, const float* pre, int32_t pre_len, int32_t H,
+                             void* codes, float* scales)
+{
     if (quant_mode < 1 || quant_mode > 5) return -1;
     if (oracle_code_type(quant_mode, code_type) != code_type) return -1;
     if (code_type == ORACLE_CODE_E2M1 && H % 2 != 0) return -1;   /* [LLD]: H even for fp4 */
@@ -448,7 +467,7 @@ int32_t oracle_quant_row(int32_t quant_mode, int32_t code_type, const uint16_t* 
     uint8_t* q = (uint8_t*)codes;
     float* f = (float*)malloc((size_t)H * sizeof(float));
     for (int32_t h = 0; h < H; ++h) {
-        f[h] = oracle_bf16_to_f32(x[h]);
+        f[h] = tok_to_f32(token_dtype, x[h]);
         if (pre_len == 1) f[h] = f[h] * pre[0];
         else if (pre_len == H) f[h] = f[h] * pre[h];
     }
@@ -588,7 +607,7 @@ int64_t oracle_dest_row(const oracle_cfg* c, const int32_t* ep_recv_count,
 /* Full dispatch: route, count, then write each routed pair's payload at its destination
  * row, with the source triple (s, i, k) ([SMP] Dispatch 功能介绍, 计算步骤: the triple
  * travels with the quantized token and comes out as assist_info_for_combine).
- *   mode 0 ([LLD] quant_mode=0): the bf16 row is moved unchanged; no scales.
+ *   mode 0 ([LLD] quant_mode=0): the token row (bf16 or binary16) is moved unchanged; no scales.
  *   modes 1-5: the row quantized by oracle_quant_row for the configured code type.  The
  *   scales tensor ([LLD] 约束说明, modes 1-3) is a scalar (scales_kind 1), a row shared by
  *   every expert (2) or the routed expert's row of an [E][H] table (3); with kind 3 the
@@ -637,8 +656,8 @@ int32_t oracle_dispatch(const oracle_cfg* c, const uint16_t* x, const int32_t* e
                     if (c->scales_kind == 1) { pre = scales_or_null; pre_len = 1; }
                     if (c->scales_kind == 2) { pre = scales_or_null; pre_len = H; }
                     if (c->scales_kind == 3) { pre = scales_or_null + (size_t)e * H; pre_len = H; }
-                    oracle_quant_row(mode, ct, xr, pre, pre_len, H,
-                                     (uint8_t*)expand_x + (size_t)row * row_bytes, rowsc);
+                    oracle_quant_row_tok(c->token_dtype, mode, ct, xr, pre, pre_len, H,
+                                         (uint8_t*)expand_x + (size_t)row * row_bytes, rowsc);
                     for (int32_t b = 0; b < ns; ++b) {
                         if (c->scale_format == 1)
                             ((uint8_t*)dynamic_scales)[(size_t)row * ns + b] =
@@ -665,7 +684,7 @@ int32_t oracle_dispatch(const oracle_cfg* c, const uint16_t* x, const int32_t* e
  * experts ([LLD] 特殊专家场景): a zero expert's output is 0, a copy expert's is ori_x.
  * Reading R11: picks are summed in k order, as one fp32 multiply then one fp32 add each
  * (zero experts and inactive picks add nothing), starting from +0; the result is rounded
- * to bf16.  A token with no active pick therefore gives +0. */
+ * to the token type (bf16 or binary16).  A token with no active pick therefore gives +0. */
 int32_t oracle_combine_token(const oracle_cfg* c, const uint16_t* expert_out,
                              const int32_t* expert_ids, const int32_t* expand_idx,
                              const float* expert_scales, const int32_t* ep_recv_count,
@@ -689,7 +708,7 @@ int32_t oracle_combine_token(const oracle_cfg* c, const uint16_t* expert_out,
             int64_t row = oracle_dest_row(c, ep_recv_count, recv_offsets, s, e, ord);
             const uint16_t* src = expert_out + (size_t)row * H;
             for (int32_t h = 0; h < H; ++h) {
-                float t = w * oracle_bf16_to_f32(src[h]);
+                float t = w * tok_to_f32(c->token_dtype, src[h]);
                 acc[h] = acc[h] + t;
             }
         } else if (e < zero_end) {
@@ -698,12 +717,12 @@ int32_t oracle_combine_token(const oracle_cfg* c, const uint16_t* expert_out,
             if (ori_x == NULL) return -1;
             const uint16_t* src = ori_x + ((size_t)s * c->BS + i) * H;
             for (int32_t h = 0; h < H; ++h) {
-                float t = w * oracle_bf16_to_f32(src[h]);
+                float t = w * tok_to_f32(c->token_dtype, src[h]);
                 acc[h] = acc[h] + t;
             }
         }
     }
-    for (int32_t h = 0; h < H; ++h) y_row[h] = oracle_f32_to_bf16(acc[h]);
+    for (int32_t h = 0; h < H; ++h) y_row[h] = f32_to_tok(c->token_dtype, acc[h]);
     return 0;
 }
 
@@ -743,18 +762,24 @@ int32_t oracle_combine_block_count(int32_t H)
  * 0 with scale 0). */
 void oracle_combine_quant_row(const uint16_t* row, int32_t H, int8_t* q, float* scales)
 {
+    oracle_combine_quant_row_tok(0, row, H, q, scales);
+}
+
+void oracle_combine_quant_row_tok(int32_t token_dtype, const uint16_t* row, int32_t H, int8_t* q,
+                                  float* scales)
+{
     const float inv127 = 1.0f / 127.0f;
     for (int32_t b = 0; b * 8 < H; ++b) {
         int32_t h0 = b * 8;
         int32_t h1 = h0 + 8 < H ? h0 + 8 : H;
         float amax = 0.0f;
         for (int32_t h = h0; h < h1; ++h) {
-            float a = fabsf(oracle_bf16_to_f32(row[h]));
+            float a = fabsf(tok_to_f32(token_dtype, row[h]));
             if (a > amax) amax = a;
         }
         float scale = amax * inv127;
         for (int32_t h = h0; h < h1; ++h) {
-            float v = oracle_bf16_to_f32(row[h]) / scale;
+            float v = tok_to_f32(token_dtype, row[h]) / scale;
             q[h] = oracle_int8_from_f16(oracle_f32_to_f16(v));
         }
         scales[b] = scale;
@@ -778,8 +803,8 @@ int32_t oracle_combine_quantize(const oracle_cfg* c, const uint16_t* expert_out,
 {
     const int32_t H = c->H, nb = oracle_combine_block_count(H);
     for (int64_t r = 0; r < recv_offsets[c->W]; ++r)
-        oracle_combine_quant_row(expert_out + (size_t)r * H, H, codes + (size_t)r * H,
-                                 scales + (size_t)r * nb);
+        oracle_combine_quant_row_tok(c->token_dtype, expert_out + (size_t)r * H, H,
+                                     codes + (size_t)r * H, scales + (size_t)r * nb);
     return 0;
 }
 
@@ -814,19 +839,19 @@ int32_t oracle_combine_int8_token(const oracle_cfg* c, const int8_t* codes, cons
             if (ori_x == NULL) return -1;
             const uint16_t* src = ori_x + ((size_t)s * c->BS + i) * H;
             for (int32_t h = 0; h < H; ++h) {
-                float t = w * oracle_bf16_to_f32(src[h]);
+                float t = w * tok_to_f32(c->token_dtype, src[h]);
                 acc[h] = acc[h] + t;
             }
         }
     }
-    for (int32_t h = 0; h < H; ++h) y_row[h] = oracle_f32_to_bf16(acc[h]);
+    for (int32_t h = 0; h < H; ++h) y_row[h] = f32_to_tok(c->token_dtype, acc[h]);
     return 0;
 }
 
 /* The combine of oracle_combine_token with each routed pick's row dequantized first: the
  * same addressing ([DDD] §3.4.2), the same fp32 sum in k order of w * row, zero experts
  * adding nothing and copy experts adding w * ori_x (reading R28: ori_x stays on its source
- * rank, so it is never quantized); the result rounded to bf16.  Token by token through
+ * rank, so it is never quantized); the result rounded to the token type.  Token by token through
  * oracle_combine_int8_token. */
 int32_t oracle_combine_int8(const oracle_cfg* c, const int8_t* codes, const float* scales,
                             const int32_t* expert_ids, const int32_t* expand_idx,
@@ -871,7 +896,7 @@ int32_t oracle_expand_scales(const oracle_cfg* c, const int32_t* assist_info,
  * receive window, and the row is copied there.  Then each source token waits for its K
  * slots and sums them in pick order, each times its expert scale (the source's own
  * expert_scales, reading R30), in fp32; the shared expert's output, when given, is added
- * after the K picks (reading R29); the sum is rounded to bf16.
+ * after the K picks (reading R29); the sum is rounded to the token type.
  * Picks that were never dispatched (inactive, special experts) have no slot: a zero expert
  * or an inactive pick adds nothing, a copy expert adds w * ori_x, as in oracle_combine.
  *   window_scratch [W][BS*K][H] bf16; acc_scratch [H] fp32. */
@@ -908,16 +933,16 @@ int32_t oracle_combine_scatter(const oracle_cfg* c, const uint16_t* expert_out,
                 else if (ori_x == NULL) return -1;
                 else src = ori_x + ((size_t)s * c->BS + i) * H;
                 for (int32_t h = 0; h < H; ++h) {
-                    float t = w * oracle_bf16_to_f32(src[h]);
+                    float t = w * tok_to_f32(c->token_dtype, src[h]);
                     acc[h] = acc[h] + t;
                 }
             }
             if (shared_x) {
                 const uint16_t* sh = shared_x + ((size_t)s * c->BS + i) * H;
-                for (int32_t h = 0; h < H; ++h) acc[h] = acc[h] + oracle_bf16_to_f32(sh[h]);
+                for (int32_t h = 0; h < H; ++h) acc[h] = acc[h] + tok_to_f32(c->token_dtype, sh[h]);
             }
             uint16_t* yr = y + ((size_t)s * c->BS + i) * H;
-            for (int32_t h = 0; h < H; ++h) yr[h] = oracle_f32_to_bf16(acc[h]);
+            for (int32_t h = 0; h < H; ++h) yr[h] = f32_to_tok(c->token_dtype, acc[h]);
         }
     return 0;
 }

@@ -13,7 +13,8 @@
  *   [SMP] "CANN MoE Dispatch/Combine 通信算子性能优化实践：Kernel 直调与 ACL SHMEM 实现专家分发与聚合"
  *         (lqnn.cn article), sections Dispatch 功能介绍, Combine 功能介绍, 通信前量化
  *
- * Conventions: all pointers are host pointers; bf16 values travel as uint16_t bit patterns;
+ * Conventions: all pointers are host pointers; token values (bf16 or binary16, by the
+ * config's token_dtype) travel as uint16_t bit patterns;
  * arrays are C-contiguous in the shapes stated at each function.  Return 0 on success,
  * a negative value on a contract violation (the oracle refuses rather than guesses).
  */
@@ -41,6 +42,8 @@ typedef struct {
     int32_t out_dtype;              /* 0 the mode's default, else one of ORACLE_CODE_*     */
     int32_t scales_kind;            /* 0 none, 1 scalar (1,), 2 shared (H,), 3 per expert  */
     int32_t scale_format;           /* 0 fp32 scales, 1 E8M0 bytes (modes 4/5 only)        */
+    int32_t token_dtype;            /* token elements (x, ori_x, expert outputs, y): 0 bf16,
+                                       1 IEEE binary16                                      */
 } oracle_cfg;
 
 /* element types of expand_x */
@@ -79,6 +82,10 @@ void oracle_quant_mx_row(const uint16_t* x, int32_t H, int32_t clip, uint8_t* co
 int32_t oracle_quant_row(int32_t quant_mode, int32_t code_type, const uint16_t* x,
                          const float* pre, int32_t pre_len, int32_t H, void* codes,
                          float* scales);
+/* Same, with the row's elements bf16 (token_dtype 0) or binary16 (1). */
+int32_t oracle_quant_row_tok(int32_t token_dtype, int32_t quant_mode, int32_t code_type, const uint16_t* x,
+                         const float* pre, int32_t pre_len, int32_t H, void* codes,
+                         float* scales);
 
 /* routing, receive counts, destination rows */
 int32_t oracle_route(const oracle_cfg* c, const int32_t* expert_ids, const uint8_t* mask,
@@ -103,6 +110,8 @@ int32_t oracle_combine_token(const oracle_cfg* c, const uint16_t* expert_out,
 /* combine-side int8 block quantization (expert side) and the int8 combine (source side) */
 int32_t oracle_combine_block_count(int32_t H);
 void oracle_combine_quant_row(const uint16_t* row, int32_t H, int8_t* q, float* scales);
+void oracle_combine_quant_row_tok(int32_t token_dtype, const uint16_t* row, int32_t H, int8_t* q,
+                                  float* scales);
 void oracle_combine_dequant_row(const int8_t* q, const float* scales, int32_t H, float* out);
 int32_t oracle_combine_quantize(const oracle_cfg* c, const uint16_t* expert_out,
                                 const int64_t* recv_offsets, int8_t* codes, float* scales);

@@ -11,7 +11,8 @@ shapes the pages work with: H up to 8192, BS <= 512 tokens per rank, K <= 16 and
 DeepSeek-V3-style 256-expert routing.
 
 Recipe (numpy PCG64, one spawned sub-stream per tensor, base seed 0 by default):
-  x              bf16 of N(0,1) fp32 samples (round to nearest even); optional outliers:
+  x              bf16 (or binary16 for a workload with token_dtype 1) of N(0,1) fp32
+                 samples (round to nearest even); optional outliers:
                  each value independently x10 with the workload's probability.  At the
                  largest sizes x is drawn on the device with torch's seeded generator
                  instead (x_torch)
@@ -28,7 +29,7 @@ Recipe (numpy PCG64, one spawned sub-stream per tensor, base seed 0 by default):
   mask           none; per token [W][BS]; or per pick [W][BS][K] with a fixed number of
                  tokens per rank fully inactive (seeded choice)
   expert_scales  fp32 softmax of N(0,1) logits over each token's K picks
-  expert_out     bf16 of N(0,1) fp32 samples, one row per received row
+  expert_out     bf16 (or binary16) of N(0,1) fp32 samples, one row per received row
   shared_x       bf16 of N(0,1) fp32 samples [W][BS][H] (the shared expert's output, drawn
                  on the device like expert_out)
 """
@@ -67,6 +68,7 @@ class Workload:
     zipf_s: float = 1.2
     outlier_prob: float = 0.0
     inactive_tokens_per_rank: int = 0
+    token_dtype: int = 0        # token elements: 0 bf16, 1 IEEE binary16
     description: str = ""
 
     @property
@@ -177,10 +179,14 @@ SAMPLE_BS256_Q = SAMPLE_BS8_Q.replace(
     description="the sample table's throughput shape with MXFP8 (E5M2 + E8M0) dispatch and "
                 "the int8 block-quantized combine")
 
+C4_F16 = C4.replace(
+    name="c4v_w16_f16_tokens", token_dtype=1,
+    description="C4 with IEEE binary16 tokens (x, expert outputs and y in fp16)")
+
 WORKLOADS = {w.name: w for w in (C1_MODE0, C1_MODE2, C2, C3, C4, C5, C3_E5M2_E8M0, C4_STATIC,
                                  C4_TOKEN_E4M3, C4_GROUP, C2_GROUP_SMOOTH, C4_COMBINE_INT8,
                                  C4_SCATTER_SHARED, C4_SMOOTH, SAMPLE_BS8, SAMPLE_BS8_Q,
-                                 SAMPLE_BS256, SAMPLE_BS256_Q, C3_MXFP4)}
+                                 SAMPLE_BS256, SAMPLE_BS256_Q, C3_MXFP4, C4_F16)}
 
 
 def _streams(seed: int):
@@ -198,6 +204,33 @@ def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(
         np.float32)
+
+
+def f32_to_f16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 samples to binary16 bit patterns (numpy's cast: nearest, ties to even)."""
+    return np.ascontiguousarray(a, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def f16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(b, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+def tok_bits_to_f32(b: np.ndarray, token_dtype: int) -> np.ndarray:
+    """Token bit patterns (bf16, or binary16 when token_dtype is 1) widened to fp32."""
+    return f16_bits_to_f32(b) if token_dtype == 1 else bf16_bits_to_f32(b)
+
+
+def f32_to_tok_bits(a: np.ndarray, token_dtype: int) -> np.ndarray:
+    return f32_to_f16_bits(a) if token_dtype == 1 else f32_to_bf16_bits(a)
+
+
+def _normal_tok(rng, shape, token_dtype, chunk=1 << 24) -> np.ndarray:
+    n = int(np.prod(shape))
+    out = np.empty(n, np.uint16)
+    for lo in range(0, n, chunk):
+        hi = min(n, lo + chunk)
+        out[lo:hi] = f32_to_tok_bits(rng.standard_normal(hi - lo, dtype=np.float32), token_dtype)
+    return out.reshape(shape)
 
 
 def _normal_bf16(rng, shape, chunk=1 << 24) -> np.ndarray:
@@ -280,15 +313,15 @@ def generate(wl: Workload, seed: int = 0, expert_out_rows: int | None = None) ->
 
     expert_out is generated only when expert_out_rows is given (it can be large)."""
     st = _streams(seed)
-    x = _normal_bf16(st[_X], (wl.W, wl.BS, wl.H))
+    x = _normal_tok(st[_X], (wl.W, wl.BS, wl.H), wl.token_dtype)
     if wl.outlier_prob > 0:
         hit = st[_OUTLIER].random((wl.W, wl.BS, wl.H)) < wl.outlier_prob
-        xf = bf16_bits_to_f32(x)
+        xf = tok_bits_to_f32(x, wl.token_dtype)
         xf[hit] *= np.float32(10.0)
-        x = f32_to_bf16_bits(xf)
+        x = f32_to_tok_bits(xf, wl.token_dtype)
     out = dict(x=x, **generate_routing(wl, seed))
     if expert_out_rows is not None:
-        out["expert_out"] = _normal_bf16(st[_EXPERT_OUT], (expert_out_rows, wl.H))
+        out["expert_out"] = _normal_tok(st[_EXPERT_OUT], (expert_out_rows, wl.H), wl.token_dtype)
     return out
 
 
@@ -304,6 +337,11 @@ def generate_routing(wl: Workload, seed: int = 0) -> dict:
     )
 
 
+def _torch_token_dtype(wl: Workload):
+    import torch
+    return torch.float16 if wl.token_dtype == 1 else torch.bfloat16
+
+
 def x_torch(wl: Workload, seed: int = 0, device="cuda"):
     """bf16 N(0,1) tokens [W][BS][H] drawn on the device with torch's seeded generator, for
     sizes where the numpy draw would take minutes (no outliers).  The oracle reads the host
@@ -313,10 +351,10 @@ def x_torch(wl: Workload, seed: int = 0, device="cuda"):
         raise ValueError("x_torch draws no outliers")
     g = torch.Generator(device=device)
     g.manual_seed(int(np.random.SeedSequence(seed).spawn(N_STREAMS)[_X].generate_state(1)[0]))
-    x = torch.empty((wl.W, wl.BS, wl.H), dtype=torch.bfloat16, device=device)
+    x = torch.empty((wl.W, wl.BS, wl.H), dtype=_torch_token_dtype(wl), device=device)
     for s in range(wl.W):            # one rank at a time: a small fp32 temporary
         x[s] = torch.randn((wl.BS, wl.H), generator=g, device=device,
-                           dtype=torch.float32).to(torch.bfloat16)
+                           dtype=torch.float32).to(_torch_token_dtype(wl))
     return x
 
 
@@ -331,4 +369,4 @@ def expert_out_torch(wl: Workload, rows: int, seed: int = 0, device="cuda"):
     g.manual_seed(int(np.random.SeedSequence(seed).spawn(N_STREAMS)[_EXPERT_OUT]
                       .generate_state(1)[0]))
     return torch.randn((rows, wl.H), generator=g, device=device,
-                       dtype=torch.float32).to(torch.bfloat16)
+                       dtype=torch.float32).to(_torch_token_dtype(wl))
