@@ -4,7 +4,8 @@
 One step = one moe_dispatch (routing ordinals, receive-count scan, quantize+scatter) followed
 by one moe_combine (top-K weighted gather) over the whole workload, with every input already
 resident in HBM.  The expert FFN between them is not part of the path: combine reads a
-pre-built bf16 expert-output buffer, one row per received row.
+pre-built expert-output buffer (bf16, or fp16 for a binary16-token workload), one row per
+received row.
 
 Prints ONE JSON line.  `value` is whole-job tokens/s: W*BS source tokens per step divided
 by the measured time per step.  The `roofline` object is for the dominant kernel (the
@@ -144,7 +145,8 @@ def cpu_baseline(wl, inp, expert_out_host, passes, shared_host=None):
                           copy_expert_num=wl.copy_expert_num,
                           expert_token_nums_type=wl.expert_token_nums_type,
                           mask_kind=wl.mask_kind, out_dtype=wl.out_dtype,
-                          scales_kind=wl.scales_kind, scale_format=wl.scale_format)
+                          scales_kind=wl.scales_kind, scale_format=wl.scale_format,
+                          token_dtype=wl.token_dtype)
     cpus = sorted(os.sched_getaffinity(0))
     os.sched_setaffinity(0, {cpus[0]})          # the oracle is single-threaded; pin it
     times = []
@@ -214,7 +216,9 @@ def run_bench(args):
                          zero_expert_num=wl.zero_expert_num, copy_expert_num=wl.copy_expert_num,
                          expert_token_nums_type=wl.expert_token_nums_type,
                          mask_kind=wl.mask_kind, out_dtype=wl.out_dtype,
-                         scales_kind=wl.scales_kind, scale_format=wl.scale_format)
+                         scales_kind=wl.scales_kind, scale_format=wl.scale_format,
+                         token_dtype=wl.token_dtype)
+    tok_dtype = cq.token_torch_dtype(cfg)
 
     def dev_t(a, dtype=None):
         if a is None:
@@ -228,10 +232,10 @@ def run_bench(args):
     w = dev_t(inp["expert_scales"])
     sets = []
     for k in range(args.sets):
-        x = dev_t(inp["x"], torch.bfloat16) if k == 0 else sets[0]["x"].clone()
+        x = dev_t(inp["x"], tok_dtype) if k == 0 else sets[0]["x"].clone()
         eo = workloads.expert_out_torch(wl, wl.cap, seed=args.seed, device=dev)
         sets.append(dict(x=x, eo=eo, out=cq.alloc_dispatch_outputs(cfg, dev),
-                         y=torch.empty((wl.W, wl.BS, wl.H), dtype=torch.bfloat16, device=dev)))
+                         y=torch.empty((wl.W, wl.BS, wl.H), dtype=tok_dtype, device=dev)))
         if wl.combine_path == "scatter":
             sets[-1]["shared"] = workloads.expert_out_torch(wl, wl.T, seed=args.seed + 1,
                                                             device=dev).view(wl.W, wl.BS, wl.H)
@@ -378,7 +382,8 @@ def run_bench(args):
         "config": {"workload": wl.name, "W": wl.W, "E": wl.E, "BS_per_rank": wl.BS,
                    "H": wl.H, "K": wl.K, "quant_mode": wl.quant_mode,
                    "out_dtype": wl.out_dtype, "scales_kind": wl.scales_kind,
-                   "scale_format": wl.scale_format, "combine_quant": wl.combine_quant,
+                   "scale_format": wl.scale_format, "token_dtype": wl.token_dtype,
+                   "combine_quant": wl.combine_quant,
                    "combine_path": wl.combine_path,
                    "routing": wl.routing, "tokens_per_step": wl.T, "routed_rows": P,
                    "description": wl.description},

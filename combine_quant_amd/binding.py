@@ -20,6 +20,7 @@ MOE_DTYPE_DEFAULT, MOE_DTYPE_INT8, MOE_DTYPE_E4M3, MOE_DTYPE_E5M2, MOE_DTYPE_E2M
 MOE_SCALES_NONE, MOE_SCALES_SCALAR, MOE_SCALES_SHARED, MOE_SCALES_PER_EXPERT = 0, 1, 2, 3
 MOE_SCALE_FP32, MOE_SCALE_E8M0 = 0, 1
 MOE_DC_FLAG_SEPARATE_ROUTE, MOE_DC_FLAG_CHECK_IDS = 1, 2
+MOE_TOKEN_BF16, MOE_TOKEN_F16 = 0, 1
 _STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
            -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_DEVICE"}
 
@@ -47,7 +48,7 @@ class MoeDcConfig(ctypes.Structure):
         ("scales_kind", ctypes.c_int32),
         ("scale_format", ctypes.c_int32),
         ("flags", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("token_dtype", ctypes.c_int32),
         ("expand_rows_capacity", ctypes.c_int64),
     ]
 
@@ -111,11 +112,17 @@ def load_library(path: str = LIB) -> ctypes.CDLL:
 def make_config(W, E, BS, H, K, quant_mode=0, zero_expert_num=0, copy_expert_num=0,
                 const_expert_num=0, expert_token_nums_type=1, mask_kind=0, cap=None,
                 out_dtype=MOE_DTYPE_DEFAULT, scales_kind=MOE_SCALES_NONE,
-                scale_format=MOE_SCALE_FP32, flags=0):
+                scale_format=MOE_SCALE_FP32, flags=0, token_dtype=MOE_TOKEN_BF16):
     cap = W * BS * K if cap is None else cap
     return MoeDcConfig(W, E, BS, H, K, quant_mode, zero_expert_num, copy_expert_num,
                        const_expert_num, expert_token_nums_type, mask_kind, out_dtype,
-                       scales_kind, scale_format, flags, 0, cap)
+                       scales_kind, scale_format, flags, token_dtype, cap)
+
+
+def token_torch_dtype(cfg):
+    """torch dtype of the token tensors (x, ori_x, shared_x, expert_out, y, mode-0
+    expand_x): bfloat16, or float16 when cfg.token_dtype is MOE_TOKEN_F16."""
+    return torch.float16 if cfg.token_dtype == MOE_TOKEN_F16 else torch.bfloat16
 
 
 def code_type(cfg):
@@ -237,12 +244,13 @@ def _dispatch_call(cfg, x, expert_ids, scales, x_active_mask, expand_x, dynamic_
     spec = _dyn_scales_spec(cfg)
     mshape = {1: (W, BS), 2: (W, BS, K)}.get(cfg.mask_kind)
     args = [
-        _ptr(x, torch.bfloat16, (W, BS, H), "x", dev),
+        _ptr(x, token_torch_dtype(cfg), (W, BS, H), "x", dev),
         _ptr(expert_ids, torch.int32, (W, BS, K), "expert_ids", dev),
         _ptr(scales, torch.float32, _scales_shape(cfg), "scales", dev),
         _ptr(x_active_mask, (torch.uint8, torch.bool), mshape, "x_active_mask", dev),
         _ptr(expert_scales, torch.float32, (W, BS, K), "expert_scales", dev),
-        _ptr(expand_x, _CODE_DTYPES.get(code_type(cfg)), (cap, code_row_elems(cfg)), "expand_x",
+        _ptr(expand_x, (token_torch_dtype(cfg) if code_type(cfg) == 0
+                        else _CODE_DTYPES.get(code_type(cfg))), (cap, code_row_elems(cfg)), "expand_x",
              dev),
         _ptr(dynamic_scales, None if spec is None else spec[0],
              None if spec is None else spec[1], "dynamic_scales", dev),
@@ -278,15 +286,15 @@ def _combine_call(cfg, expert_out, expert_ids, expand_idx, expert_scales, ep_rec
     dev = y.device
     mshape = {1: (W, BS), 2: (W, BS, K)}.get(cfg.mask_kind)
     args = [
-        _ptr(expert_out, torch.bfloat16, (cap, H), "expert_out", dev),
+        _ptr(expert_out, token_torch_dtype(cfg), (cap, H), "expert_out", dev),
         _ptr(expert_ids, torch.int32, (W, BS, K), "expert_ids", dev),
         _ptr(expand_idx, torch.int32, (W, BS, K), "expand_idx", dev),
         _ptr(expert_scales, torch.float32, (W, BS, K), "expert_scales", dev),
         _ptr(ep_recv_count, torch.int32, (W, L * W), "ep_recv_count", dev),
         _ptr(recv_offsets, torch.int64, (W + 1,), "recv_offsets", dev),
         _ptr(x_active_mask, (torch.uint8, torch.bool), mshape, "x_active_mask", dev),
-        _ptr(ori_x, torch.bfloat16, (W, BS, H), "ori_x", dev),
-        _ptr(y, torch.bfloat16, (W, BS, H), "y", dev),
+        _ptr(ori_x, token_torch_dtype(cfg), (W, BS, H), "ori_x", dev),
+        _ptr(y, token_torch_dtype(cfg), (W, BS, H), "y", dev),
     ]
     return load_library().moe_combine, (ctypes.byref(cfg), *args), dev
 
@@ -309,15 +317,15 @@ def _combine_scatter_call(cfg, expert_out, assist_info, recv_offsets, expert_ids
     dev = y.device
     mshape = {1: (W, BS), 2: (W, BS, K)}.get(cfg.mask_kind)
     args = [
-        _ptr(expert_out, torch.bfloat16, (cap, H), "expert_out", dev),
+        _ptr(expert_out, token_torch_dtype(cfg), (cap, H), "expert_out", dev),
         _ptr(assist_info, torch.int32, (cap, 3), "assist_info", dev),
         _ptr(recv_offsets, torch.int64, (W + 1,), "recv_offsets", dev),
         _ptr(expert_ids, torch.int32, (W, BS, K), "expert_ids", dev),
         _ptr(expert_scales, torch.float32, (W, BS, K), "expert_scales", dev),
         _ptr(x_active_mask, (torch.uint8, torch.bool), mshape, "x_active_mask", dev),
-        _ptr(ori_x, torch.bfloat16, (W, BS, H), "ori_x", dev),
-        _ptr(shared_x, torch.bfloat16, (W, BS, H), "shared_x", dev),
-        _ptr(y, torch.bfloat16, (W, BS, H), "y", dev),
+        _ptr(ori_x, token_torch_dtype(cfg), (W, BS, H), "ori_x", dev),
+        _ptr(shared_x, token_torch_dtype(cfg), (W, BS, H), "shared_x", dev),
+        _ptr(y, token_torch_dtype(cfg), (W, BS, H), "y", dev),
         _ptr(workspace, torch.uint8, None, "workspace", dev),
     ]
     ws_bytes = 0 if workspace is None else workspace.numel()
@@ -342,7 +350,7 @@ def _combine_quantize_call(cfg, expert_out, recv_offsets, codes, block_scales):
     W, H, cap = cfg.ep_world_size, cfg.hidden, cfg.expand_rows_capacity
     dev = codes.device
     args = [
-        _ptr(expert_out, torch.bfloat16, (cap, H), "expert_out", dev),
+        _ptr(expert_out, token_torch_dtype(cfg), (cap, H), "expert_out", dev),
         _ptr(recv_offsets, torch.int64, (W + 1,), "recv_offsets", dev),
         _ptr(codes, torch.int8, (cap, H), "codes", dev),
         _ptr(block_scales, torch.float32, (cap, combine_block_count(cfg)), "block_scales",
@@ -372,8 +380,8 @@ def _combine_int8_call(cfg, codes, block_scales, expert_ids, expand_idx, expert_
         _ptr(ep_recv_count, torch.int32, (W, L * W), "ep_recv_count", dev),
         _ptr(recv_offsets, torch.int64, (W + 1,), "recv_offsets", dev),
         _ptr(x_active_mask, (torch.uint8, torch.bool), mshape, "x_active_mask", dev),
-        _ptr(ori_x, torch.bfloat16, (W, BS, H), "ori_x", dev),
-        _ptr(y, torch.bfloat16, (W, BS, H), "y", dev),
+        _ptr(ori_x, token_torch_dtype(cfg), (W, BS, H), "ori_x", dev),
+        _ptr(y, token_torch_dtype(cfg), (W, BS, H), "y", dev),
     ]
     return load_library().moe_combine_int8, (ctypes.byref(cfg), *args), dev
 
@@ -394,7 +402,9 @@ def alloc_dispatch_outputs(cfg, device="cuda"):
                            cfg.expand_rows_capacity)
     spec = _dyn_scales_spec(cfg)
     return dict(
-        expand_x=torch.empty((cap, code_row_elems(cfg)), dtype=_ALLOC_DTYPES[code_type(cfg)],
+        expand_x=torch.empty((cap, code_row_elems(cfg)),
+                             dtype=(token_torch_dtype(cfg) if code_type(cfg) == 0
+                                    else _ALLOC_DTYPES[code_type(cfg)]),
                              device=device),
         dynamic_scales=(None if spec is None else
                         torch.empty(spec[1], dtype=spec[0], device=device)),
@@ -409,7 +419,7 @@ def alloc_dispatch_outputs(cfg, device="cuda"):
 
 
 def _new_y(cfg, like):
-    return torch.empty((cfg.ep_world_size, cfg.bs, cfg.hidden), dtype=torch.bfloat16,
+    return torch.empty((cfg.ep_world_size, cfg.bs, cfg.hidden), dtype=token_torch_dtype(cfg),
                        device=like.device)
 
 

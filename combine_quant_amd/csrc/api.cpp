@@ -67,8 +67,9 @@ moe_status check(const moe_dc_config* c, moe_dc::Shape* out)
     if (!c) return fail(MOE_ERR_INVALID_ARG, "config is NULL");
     if ((c->flags & ~(MOE_DC_FLAG_SEPARATE_ROUTE | MOE_DC_FLAG_CHECK_IDS)) != 0)
         return fail(MOE_ERR_INVALID_ARG, "flags has unknown bits (0x%x)", c->flags);
-    if (c->reserved != 0)
-        return fail(MOE_ERR_INVALID_ARG, "reserved must be 0");
+    if (c->token_dtype != MOE_TOKEN_BF16 && c->token_dtype != MOE_TOKEN_F16)
+        return fail(MOE_ERR_INVALID_ARG, "token_dtype %d is not one of 0 (bf16), 1 (fp16)",
+                    c->token_dtype);
     if (c->ep_world_size < 2 || c->ep_world_size > 768)
         return fail(MOE_ERR_INVALID_ARG, "ep_world_size %d outside [2, 768]", c->ep_world_size);
     if (c->moe_expert_num <= 0 || c->moe_expert_num > 1024)
@@ -143,6 +144,7 @@ moe_status check(const moe_dc_config* c, moe_dc::Shape* out)
                               : c->quant_mode == 3 ? (c->hidden + 127) / 128
                                                    : nb + (nb & 1);
         out->cap = c->expand_rows_capacity;
+        out->tok_f16 = c->token_dtype == MOE_TOKEN_F16 ? 1 : 0;
     }
     return MOE_OK;
 }

@@ -72,11 +72,13 @@ __device__ __forceinline__ int pick_source(
     return (e >= zero_end && e < id_end) ? kCopy : kNone;
 }
 
-// acc[c] = acc[c] + w * element c of eight bf16 values (one multiply, one add each)
+// acc[c] = acc[c] + w * element c of eight token values (bf16, or binary16 with F16; one
+// multiply, one add each)
+template <bool F16>
 __device__ __forceinline__ void accumulate8(uint4 v, float w, float (&acc)[8])
 {
-    const float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                        bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+    const float f[8] = {tok_lo<F16>(v.x), tok_hi<F16>(v.x), tok_lo<F16>(v.y), tok_hi<F16>(v.y),
+                        tok_lo<F16>(v.z), tok_hi<F16>(v.z), tok_lo<F16>(v.w), tok_hi<F16>(v.w)};
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[c] = acc[c] + w * f[c];
 }
@@ -147,7 +149,7 @@ constexpr int slots_per_task(int) { return 2; }
 // words and the scale's bits.
 // INV selects the scatter-back addressing (expand_idx then holds the slot -> row map) and
 // SHARED adds the shared expert's bf16 output after the K picks.
-template <int KMAX, int SLOTS, int Q, bool INV, bool SHARED>
+template <int KMAX, int SLOTS, int Q, bool INV, bool SHARED, bool F16>
 __global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_wave_kernel(
     const void* __restrict__ expert_out, const float* __restrict__ qscales,
     const int32_t* __restrict__ ids, const int32_t* __restrict__ expand_idx,
@@ -239,14 +241,14 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_wave_kernel(
                     accumulate8_int8(make_uint2(buf[n][k].x, buf[n][k].y),
                                      __uint_as_float(buf[n][k].z), ws[k], acc);
                 else if (Q == 1)                    // copy expert: its ori_x vector, read here
-                    accumulate8(self[v], ws[k], acc);
+                    accumulate8<F16>(self[v], ws[k], acc);
                 else
-                    accumulate8(buf[n][k], ws[k], acc);
+                    accumulate8<F16>(buf[n][k], ws[k], acc);
             }
-            if (SHARED) accumulate8(shv[n], 1.0f, acc);    // 1 * bf16 value is exact
+            if (SHARED) accumulate8<F16>(shv[n], 1.0f, acc);   // 1 * a token value is exact
             store_stream(yr + v,
-                         make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                                    pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])));
+                         make_uint4(pack_tok2<F16>(acc[0], acc[1]), pack_tok2<F16>(acc[2], acc[3]),
+                                    pack_tok2<F16>(acc[4], acc[5]), pack_tok2<F16>(acc[6], acc[7])));
         }
     }
 }
@@ -255,7 +257,7 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_wave_kernel(
 // vector and one 8-byte pair of block scales (two blocks) instead of 8 + 4 bytes, so every
 // load instruction moves twice the bytes.  One wave task = one token x 64 lanes x 16
 // elements.  A copy expert's ori_x half-rows are read when they are accumulated.
-template <int KMAX>
+template <int KMAX, bool F16>
 __global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_int8_wide_kernel(
     const int8_t* __restrict__ codes, const float* __restrict__ qscales,
     const int32_t* __restrict__ ids, const int32_t* __restrict__ expand_idx,
@@ -315,16 +317,17 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_int8_wide_kern
             accumulate8_int8(make_uint2(cbuf[k].z, cbuf[k].w), __uint_as_float(sbuf[k].y),
                              ws[k], hi);
         } else if (srcs[k] == kCopy) {
-            accumulate8(self[2 * u], ws[k], lo);
-            accumulate8(self[2 * u + 1], ws[k], hi);
+            accumulate8<F16>(self[2 * u], ws[k], lo);
+            accumulate8<F16>(self[2 * u + 1], ws[k], hi);
         }
     }
     uint4* yr = reinterpret_cast<uint4*>(y) + tok * NV;
-    store_stream(yr + 2 * u, make_uint4(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]),
-                                        pack_bf16x2(lo[4], lo[5]), pack_bf16x2(lo[6], lo[7])));
+    store_stream(yr + 2 * u,
+                 make_uint4(pack_tok2<F16>(lo[0], lo[1]), pack_tok2<F16>(lo[2], lo[3]),
+                            pack_tok2<F16>(lo[4], lo[5]), pack_tok2<F16>(lo[6], lo[7])));
     store_stream(yr + 2 * u + 1,
-                 make_uint4(pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3]),
-                            pack_bf16x2(hi[4], hi[5]), pack_bf16x2(hi[6], hi[7])));
+                 make_uint4(pack_tok2<F16>(hi[0], hi[1]), pack_tok2<F16>(hi[2], hi[3]),
+                            pack_tok2<F16>(hi[4], hi[5]), pack_tok2<F16>(hi[6], hi[7])));
 }
 
 template <int KMAX>
@@ -337,12 +340,16 @@ hipError_t launch_int8_wide_k(const Shape& sh, const int8_t* codes, const float*
     const int tasks_per_token = ((sh.H >> 4) + kWave - 1) / kWave;
     const long long tasks = T * tasks_per_token;
     const unsigned blocks = (unsigned)((tasks + kWavesPerBlock - 1) / kWavesPerBlock);
-    hipLaunchKernelGGL((combine_int8_wide_kernel<KMAX>), dim3(blocks),
-                       dim3(kWave * kWavesPerBlock), 0, stream, codes, qscales, ids,
-                       expand_idx, w, erc, roff, mask, sh.mask_kind,
-                       static_cast<const uint16_t*>(ori_x), static_cast<uint16_t*>(y), sh.W,
-                       sh.E, sh.L, sh.BS, sh.H, sh.K, sh.zero_end, sh.id_end,
-                       (long long)sh.cap, T, tasks_per_token);
+#define MOE_DC_INT8_WIDE(F)                                                                 \
+    hipLaunchKernelGGL((combine_int8_wide_kernel<KMAX, F>), dim3(blocks),                   \
+                       dim3(kWave * kWavesPerBlock), 0, stream, codes, qscales, ids,        \
+                       expand_idx, w, erc, roff, mask, sh.mask_kind,                        \
+                       static_cast<const uint16_t*>(ori_x), static_cast<uint16_t*>(y), sh.W, \
+                       sh.E, sh.L, sh.BS, sh.H, sh.K, sh.zero_end, sh.id_end,               \
+                       (long long)sh.cap, T, tasks_per_token)
+    if (sh.tok_f16) MOE_DC_INT8_WIDE(true);
+    else MOE_DC_INT8_WIDE(false);
+#undef MOE_DC_INT8_WIDE
     return hipGetLastError();
 }
 
@@ -358,13 +365,17 @@ hipError_t launch_wave_k(const Shape& sh, const void* expert_out, const float* q
     const int tasks_per_token = (slots + kSlots - 1) / kSlots;
     const long long tasks = T * tasks_per_token;
     const unsigned blocks = (unsigned)((tasks + kWavesPerBlock - 1) / kWavesPerBlock);
-    hipLaunchKernelGGL((combine_wave_kernel<KMAX, kSlots, Q, INV, SHARED>), dim3(blocks),
-                       dim3(kWave * kWavesPerBlock), 0, stream, expert_out, qscales, ids,
-                       expand_idx, w, erc, roff, mask, sh.mask_kind,
-                       static_cast<const uint16_t*>(ori_x),
-                       static_cast<const uint16_t*>(shared_x), static_cast<uint16_t*>(y),
-                       sh.W, sh.E, sh.L, sh.BS, sh.H, sh.K, sh.zero_end, sh.id_end,
-                       (long long)sh.cap, T, tasks_per_token);
+#define MOE_DC_WAVE(F)                                                                      \
+    hipLaunchKernelGGL((combine_wave_kernel<KMAX, kSlots, Q, INV, SHARED, F>), dim3(blocks), \
+                       dim3(kWave * kWavesPerBlock), 0, stream, expert_out, qscales, ids,   \
+                       expand_idx, w, erc, roff, mask, sh.mask_kind,                        \
+                       static_cast<const uint16_t*>(ori_x),                                 \
+                       static_cast<const uint16_t*>(shared_x), static_cast<uint16_t*>(y),   \
+                       sh.W, sh.E, sh.L, sh.BS, sh.H, sh.K, sh.zero_end, sh.id_end,         \
+                       (long long)sh.cap, T, tasks_per_token)
+    if (sh.tok_f16) MOE_DC_WAVE(true);
+    else MOE_DC_WAVE(false);
+#undef MOE_DC_WAVE
     return hipGetLastError();
 }
 
@@ -394,7 +405,7 @@ __global__ __launch_bounds__(kElemThreads) void combine_elem_kernel(
     const int64_t* __restrict__ recv_offsets, const uint8_t* __restrict__ mask, int mask_kind,
     const uint16_t* __restrict__ ori_x, const uint16_t* __restrict__ shared_x,
     uint16_t* __restrict__ y, int W, int E, int L, int BS, int H, int K, int zero_end,
-    int id_end, long long cap)
+    int id_end, long long cap, int tok_f16)
 {
     __shared__ int src_of[KMAX];
     __shared__ float w_of[KMAX];
@@ -425,12 +436,12 @@ __global__ __launch_bounds__(kElemThreads) void combine_elem_kernel(
                 const float t0 = (float)eq[(long long)src * H + h];
                 v = t0 * qscales[(long long)src * nb + h / 8];
             } else {
-                v = bf16_lo(src >= 0 ? eo[(long long)src * H + h] : self[h]);
+                v = tok_lo_rt(src >= 0 ? eo[(long long)src * H + h] : self[h], tok_f16 != 0);
             }
             acc = acc + w_of[k] * v;
         }
-        if (shared_x) acc = acc + bf16_lo(shared_x[tok * H + h]);
-        yr[h] = (uint16_t)f32_to_bf16_rne(acc);
+        if (shared_x) acc = acc + tok_lo_rt(shared_x[tok * H + h], tok_f16 != 0);
+        yr[h] = (uint16_t)f32_to_tok_rt(acc, tok_f16 != 0);
     }
 }
 
@@ -448,7 +459,7 @@ hipError_t launch_elem_k(const Shape& sh, const void* expert_out, const float* q
                        sh.mask_kind, static_cast<const uint16_t*>(ori_x),
                        static_cast<const uint16_t*>(shared_x), static_cast<uint16_t*>(y),
                        sh.W, sh.E, sh.L, sh.BS, sh.H, sh.K, sh.zero_end, sh.id_end,
-                       (long long)sh.cap);
+                       (long long)sh.cap, sh.tok_f16);
     return hipGetLastError();
 }
 
@@ -509,7 +520,7 @@ constexpr int kQuantSlots = 2;
 __global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_quantize_kernel(
     const uint16_t* __restrict__ expert_out, const int64_t* __restrict__ recv_offsets,
     int8_t* __restrict__ codes, float* __restrict__ qscales, int W, int H, long long cap,
-    int tasks_per_row)
+    int tasks_per_row, int tok_f16)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const long long task = (long long)blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
@@ -529,9 +540,16 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_quantize_kerne
     for (int n = 0; n < kQuantSlots; ++n) {
         const int v = lane + (slot0 + n) * kWave;
         if (v >= NV) continue;
-        const float f[8] = {bf16_lo(raw[n].x), bf16_hi(raw[n].x), bf16_lo(raw[n].y),
-                            bf16_hi(raw[n].y), bf16_lo(raw[n].z), bf16_hi(raw[n].z),
-                            bf16_lo(raw[n].w), bf16_hi(raw[n].w)};
+        float f[8];
+        if (tok_f16) {
+            f[0] = f16_lo(raw[n].x); f[1] = f16_hi(raw[n].x); f[2] = f16_lo(raw[n].y);
+            f[3] = f16_hi(raw[n].y); f[4] = f16_lo(raw[n].z); f[5] = f16_hi(raw[n].z);
+            f[6] = f16_lo(raw[n].w); f[7] = f16_hi(raw[n].w);
+        } else {
+            f[0] = bf16_lo(raw[n].x); f[1] = bf16_hi(raw[n].x); f[2] = bf16_lo(raw[n].y);
+            f[3] = bf16_hi(raw[n].y); f[4] = bf16_lo(raw[n].z); f[5] = bf16_hi(raw[n].z);
+            f[6] = bf16_lo(raw[n].w); f[7] = bf16_hi(raw[n].w);
+        }
         uint32_t amax = 0;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
@@ -553,7 +571,7 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_quantize_kerne
 // adjacent lanes (the last block of a row may be short).
 __global__ __launch_bounds__(kElemThreads) void combine_quantize_elem_kernel(
     const uint16_t* __restrict__ expert_out, const int64_t* __restrict__ recv_offsets,
-    int8_t* __restrict__ codes, float* __restrict__ qscales, int W, int H)
+    int8_t* __restrict__ codes, float* __restrict__ qscales, int W, int H, int tok_f16)
 {
     const long long row = blockIdx.x;
     if (row >= recv_offsets[W]) return;                    // whole workgroup
@@ -563,7 +581,7 @@ __global__ __launch_bounds__(kElemThreads) void combine_quantize_elem_kernel(
     for (int n = 0; n < kElemPerLane; ++n) {
         const int h = t + n * blockDim.x;
         if (n * (int)blockDim.x >= H) break;               // uniform across the workgroup
-        const float f = h < H ? bf16_lo(expert_out[row * H + h]) : 0.0f;
+        const float f = h < H ? tok_lo_rt(expert_out[row * H + h], tok_f16 != 0) : 0.0f;
         const uint32_t amax = group_max_u32<8>(__float_as_uint(f) & 0x7FFFFFFFu);
         const float scale = __uint_as_float(amax) * kInv127;
         if (h >= H) continue;
@@ -647,13 +665,14 @@ hipError_t launch_combine_quantize(const Shape& sh, const void* expert_out,
         const unsigned blocks = (unsigned)((tasks + kWavesPerBlock - 1) / kWavesPerBlock);
         hipLaunchKernelGGL(combine_quantize_kernel, dim3(blocks), dim3(kWave * kWavesPerBlock),
                            0, stream, static_cast<const uint16_t*>(expert_out), recv_offsets,
-                           codes, qscales, sh.W, sh.H, (long long)sh.cap, tasks_per_row);
+                           codes, qscales, sh.W, sh.H, (long long)sh.cap, tasks_per_row,
+                           sh.tok_f16);
     } else {
         const int want = (sh.H + kWave - 1) / kWave * kWave;
         const int threads = want < kElemThreads ? want : kElemThreads;
         hipLaunchKernelGGL(combine_quantize_elem_kernel, dim3((unsigned)sh.cap),
                            dim3(threads), 0, stream, static_cast<const uint16_t*>(expert_out),
-                           recv_offsets, codes, qscales, sh.W, sh.H);
+                           recv_offsets, codes, qscales, sh.W, sh.H, sh.tok_f16);
     }
     return hipGetLastError();
 }

@@ -31,6 +31,45 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
+// IEEE binary16 token elements: widening is exact; narrowing is the hardware conversion,
+// which rounds to nearest even (overflow to infinity, subnormals kept, NaN stays NaN).
+__device__ __forceinline__ float f16_lo(uint32_t w)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+__device__ __forceinline__ uint32_t f32_to_f16(float f)
+{
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi)
+{
+    return f32_to_f16(lo) | (f32_to_f16(hi) << 16);
+}
+
+// Token elements (x, ori_x, shared_x, expert outputs, y) of either type: F16 selects binary16,
+// else bf16.
+template <bool F16>
+__device__ __forceinline__ float tok_lo(uint32_t w) { return F16 ? f16_lo(w) : bf16_lo(w); }
+template <bool F16>
+__device__ __forceinline__ float tok_hi(uint32_t w) { return F16 ? f16_hi(w) : bf16_hi(w); }
+template <bool F16>
+__device__ __forceinline__ uint32_t pack_tok2(float lo, float hi)
+{
+    return F16 ? pack_f16x2(lo, hi) : pack_bf16x2(lo, hi);
+}
+__device__ __forceinline__ float tok_lo_rt(uint32_t w, bool f16)
+{
+    return f16 ? f16_lo(w) : bf16_lo(w);
+}
+__device__ __forceinline__ uint32_t f32_to_tok_rt(float f, bool f16)
+{
+    return f16 ? f32_to_f16(f) : f32_to_bf16_rne(f);
+}
+
 // E4M3 ("fn" variant: bias 7, no infinities, 448 largest) code of a finite binary32 value:
 // nearest, ties to even, magnitudes >= 448 saturate to 448, sign kept (also on zero).
 // Normal results: round the binary32 significand to 3 fraction bits at bit 20 and rebias

@@ -29,6 +29,7 @@ struct Shape {
     int32_t etn_type;
     int32_t mask_kind;
     int32_t scales_per_row;  // 0, 1, Ceil(H,128) or Align2(Ceil(H,32))
+    int32_t tok_f16;         // 1: token elements are IEEE binary16, 0: bf16
     int64_t cap;
 };
 

@@ -92,10 +92,17 @@ __device__ __forceinline__ float pow2f(int e)
     return e >= -126 ? __uint_as_float((uint32_t)(127 + e) << 23) : __uint_as_float(0x00400000u);
 }
 
-__device__ __forceinline__ void unpack8(uint4 w, float (&f)[8])
+// Eight token elements of one 16-byte vector, widened to binary32 (exact): bf16, or
+// binary16 when f16 is set (a wave-uniform flag).
+__device__ __forceinline__ void unpack8(uint4 w, float (&f)[8], bool f16)
 {
-    f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
-    f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z); f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
+    if (f16) {
+        f[0] = f16_lo(w.x); f[1] = f16_hi(w.x); f[2] = f16_lo(w.y); f[3] = f16_hi(w.y);
+        f[4] = f16_lo(w.z); f[5] = f16_hi(w.z); f[6] = f16_lo(w.w); f[7] = f16_hi(w.w);
+    } else {
+        f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
+        f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z); f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
+    }
 }
 
 __device__ __forceinline__ void mul8(float (&f)[8], float4 a, float4 b)
@@ -332,7 +339,7 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
     const float* __restrict__ scales, const float* __restrict__ weights,
     void* __restrict__ expand_x, void* __restrict__ dyn_scales, int32_t* __restrict__ assist,
     float* __restrict__ expand_scales, int W, int E, int BS, int H, int K, int ns,
-    long long cap, int e8m0, FusedRoute fr, int L, int mask_kind, int etn_type)
+    long long cap, int e8m0, FusedRoute fr, int L, int mask_kind, int etn_type, int tok_f16)
 {
     __shared__ int32_t rows_lds[kMaxK];
     __shared__ int32_t exps_lds[kMaxK];
@@ -414,7 +421,7 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
         for (int n = 0; n < kTileSlots; ++n) {
             const int v = lane + (wave * kTileSlots + n) * kWave;
             if (v < NV) {
-                unpack8(raw[n], f[n]);
+                unpack8(raw[n], f[n], tok_f16 != 0);
                 if (SK == kScalesScalar) {
 #pragma unroll
                     for (int q = 0; q < 8; ++q) f[n][q] = f[n][q] * scalar_pre;
@@ -597,7 +604,7 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
         for (int n = 0; n < kTileSlots; ++n) {
             const int v = lane + (wave * kTileSlots + n) * kWave;
             if (v < NV) {
-                unpack8(raw[n], f[n]);
+                unpack8(raw[n], f[n], tok_f16 != 0);
                 mul8(f[n], sm_cur[n][0], sm_cur[n][1]);
             } else {
 #pragma unroll
@@ -680,7 +687,7 @@ hipError_t launch_tile_variant(const Shape& sh, const ScatterArgs& a, hipStream_
                        a.ids, a.expand_idx, a.seg, a.scales, a.weights, a.expand_x,            \
                        a.dyn_scales, a.assist, a.expand_scales, sh.W, sh.E, sh.BS, sh.H, sh.K, \
                        sh.scales_per_row, (long long)sh.cap, sh.scale_e8m0, fr, sh.L,         \
-                       sh.mask_kind, sh.etn_type)
+                       sh.mask_kind, sh.etn_type, sh.tok_f16)
     if (a.fused) MOE_DC_TILE_LAUNCH(true);
     else MOE_DC_TILE_LAUNCH(false);
 #undef MOE_DC_TILE_LAUNCH
@@ -771,7 +778,7 @@ __global__ __launch_bounds__(kElemThreads) void scatter_elem_kernel(
     const float* __restrict__ scales, const float* __restrict__ weights,
     void* __restrict__ expand_x, void* __restrict__ dyn_scales, int32_t* __restrict__ assist,
     float* __restrict__ expand_scales, int W, int E, int BS, int H, int K, int ns,
-    long long cap, int mode, int ct, int sk, int e8m0)
+    long long cap, int mode, int ct, int sk, int e8m0, int tok_f16)
 {
     __shared__ long long row_of[kMaxK];
     __shared__ int32_t exp_of[kMaxK];
@@ -849,7 +856,7 @@ __global__ __launch_bounds__(kElemThreads) void scatter_elem_kernel(
             const int h = t + n * nt;
             f[n] = 0.0f;
             if (h < H) {
-                f[n] = bf16_lo(raw[n]);
+                f[n] = tok_lo_rt(raw[n], tok_f16 != 0);
                 if (sk == kScalesScalar) f[n] = f[n] * pre[0];
                 if (sk == kScalesShared || sk == kScalesPerExpert) f[n] = f[n] * pre[h];
             }
@@ -949,7 +956,7 @@ hipError_t launch_elem(const Shape& sh, const ScatterArgs& a, hipStream_t stream
                        static_cast<const uint16_t*>(a.x), a.ids, a.expand_idx, a.seg, a.scales,
                        a.weights, a.expand_x, a.dyn_scales, a.assist, a.expand_scales, sh.W,
                        sh.E, sh.BS, sh.H, sh.K, sh.scales_per_row, (long long)sh.cap,
-                       sh.quant_mode, sh.code_type, sh.scales_kind, sh.scale_e8m0);
+                       sh.quant_mode, sh.code_type, sh.scales_kind, sh.scale_e8m0, sh.tok_f16);
     return hipGetLastError();
 }
 

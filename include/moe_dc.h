@@ -21,7 +21,10 @@
  * Conventions shared by every entry point:
  *   - Tensor arguments are DEVICE pointers into the memory of the current HIP device;
  *     arrays are dense, C-contiguous, in the shapes given.  bf16 is the 16-bit brain-float
- *     bit pattern.  Device pointers should be 16-byte aligned for the vectorised kernels;
+ *     bit pattern; every token tensor below written "bf16" (x, ori_x, shared_x, expert_out,
+ *     y, mode-0 expand_x) holds IEEE binary16 instead when cfg->token_dtype is
+ *     MOE_TOKEN_F16, and y then rounds to binary16.  Device pointers should be 16-byte
+ *     aligned for the vectorised kernels;
  *     unaligned pointers (or H not a multiple of 8) select slower element-wise kernels.
  *   - `stream` is a hipStream_t passed as void* (NULL = the legacy default stream).  Every
  *     call is asynchronous on that stream: it validates on the host, enqueues kernels and
@@ -79,6 +82,13 @@ typedef enum {
                                    scale as an E8M0 value)                                  */
 } moe_scale_format;
 
+/* Element type of the tokens: x, ori_x, shared_x, expert_out, y and the mode-0 rows of
+ * expand_x ([LLD] and [OPS] 参数说明: the token dtype is float16 or bfloat16). */
+typedef enum {
+    MOE_TOKEN_BF16 = 0,         /* bfloat16                                                */
+    MOE_TOKEN_F16 = 1           /* IEEE binary16; y rounds to nearest even, overflow to inf */
+} moe_token_dtype;
+
 /* Bits of moe_dc_config.flags. */
 typedef enum {
     /* moe_dispatch always runs the routing and the prefix sums as kernels of their own.  By
@@ -117,7 +127,8 @@ typedef struct {
                                        modes 2, 3 any; modes 0, 4, 5 NONE                     */
     int32_t scale_format;           /* moe_scale_format: E8M0 only with modes 4/5            */
     int32_t flags;                  /* moe_dc_flag bits; 0 for the defaults                   */
-    int32_t reserved;               /* must be 0                                              */
+    int32_t token_dtype;            /* moe_token_dtype of x, ori_x, shared_x, expert_out, y
+                                       and mode-0 expand_x: BF16 (0, the default) or F16      */
     int64_t expand_rows_capacity;   /* rows of expand_x / dynamic_scales / assist_info and of
                                        expert_out; must be >= W*BS*K                           */
 } moe_dc_config;

@@ -18,7 +18,8 @@ def oracle_cfg(wl: workloads.Workload, etn_type=None):
                            expert_token_nums_type=wl.expert_token_nums_type if etn_type is None
                            else etn_type,
                            mask_kind=wl.mask_kind, out_dtype=wl.out_dtype,
-                           scales_kind=wl.scales_kind, scale_format=wl.scale_format)
+                           scales_kind=wl.scales_kind, scale_format=wl.scale_format,
+                           token_dtype=wl.token_dtype)
 
 
 def lib_cfg(wl: workloads.Workload, cap=None, flags=0):
@@ -29,7 +30,7 @@ def lib_cfg(wl: workloads.Workload, cap=None, flags=0):
                           expert_token_nums_type=wl.expert_token_nums_type,
                           mask_kind=wl.mask_kind, cap=cap, out_dtype=wl.out_dtype,
                           scales_kind=wl.scales_kind, scale_format=wl.scale_format,
-                          flags=flags)
+                          flags=flags, token_dtype=wl.token_dtype)
 
 
 def to_dev(a, dtype=None, device="cuda"):
@@ -47,12 +48,18 @@ def bf16_dev(a_u16, device="cuda"):
     return to_dev(a_u16, torch.bfloat16, device)
 
 
+def tok_dev(a_u16, token_dtype=0, device="cuda"):
+    """Token bit patterns as a device tensor: bfloat16, or float16 for token_dtype 1."""
+    import torch
+    return to_dev(a_u16, torch.float16 if token_dtype == 1 else torch.bfloat16, device)
+
+
 def host(t):
     import torch
     if t is None:
         return None
     t = t.detach()
-    if t.dtype == torch.bfloat16:
+    if t.dtype in (torch.bfloat16, torch.float16):
         t = t.view(torch.int16)
     if t.dtype in (torch.float8_e4m3fn, torch.float8_e5m2):
         t = t.view(torch.uint8)
@@ -63,7 +70,7 @@ def host(t):
 def gpu_dispatch(wl, inp, cfg=None, device="cuda"):
     import combine_quant_amd as cq
     cfg = lib_cfg(wl) if cfg is None else cfg
-    x = bf16_dev(inp["x"], device)
+    x = tok_dev(inp["x"], wl.token_dtype, device)
     ids = to_dev(inp["expert_ids"], device=device)
     sm = to_dev(inp.get("scales"), device=device)
     mask = to_dev(inp.get("mask"), device=device)
@@ -100,9 +107,9 @@ def compare_dispatch(wl, inp, out_dev, ref, rows=None):
     return o
 
 
-def check_combine_tolerance(y_gpu_u16, y_ref_u16, rtol=1e-2, atol=1e-3):
-    a = workloads.bf16_bits_to_f32(y_gpu_u16).astype(np.float64)
-    b = workloads.bf16_bits_to_f32(y_ref_u16).astype(np.float64)
+def check_combine_tolerance(y_gpu_u16, y_ref_u16, rtol=1e-2, atol=1e-3, token_dtype=0):
+    a = workloads.tok_bits_to_f32(y_gpu_u16, token_dtype).astype(np.float64)
+    b = workloads.tok_bits_to_f32(y_ref_u16, token_dtype).astype(np.float64)
     bad = np.abs(a - b) > atol + rtol * np.abs(b)
     assert not bad.any(), f"{int(bad.sum())} of {bad.size} elements out of tolerance"
     return int((y_gpu_u16 != y_ref_u16).sum())
@@ -115,8 +122,9 @@ def oracle_dispatch(wl, inp, etn_type=None):
 
 
 def roundtrip(wl, seed=0, flags=0):
-    """Dispatch compared bit for bit, then combine over random bf16 expert outputs compared
-    within tolerance; returns the number of bf16 elements that differ at all."""
+    """Dispatch compared bit for bit, then combine over random expert outputs (of the
+    workload's token type) compared within tolerance; returns the number of elements that
+    differ at all."""
     import torch
     import combine_quant_amd as cq
     inp = workloads.generate(wl, seed=seed)
@@ -125,12 +133,13 @@ def roundtrip(wl, seed=0, flags=0):
     torch.cuda.synchronize()
     compare_dispatch(wl, inp, out, ref)
     rng = np.random.default_rng(seed + 77)
-    eo = workloads.f32_to_bf16_bits(rng.standard_normal((wl.cap, wl.H), dtype=np.float32))
+    eo = workloads.f32_to_tok_bits(rng.standard_normal((wl.cap, wl.H), dtype=np.float32),
+                                   wl.token_dtype)
     y_ref = oracle.combine(ocfg, eo, inp["expert_ids"], ref["expand_idx"],
                            inp["expert_scales"], ref["ep_recv_count"], ref["recv_offsets"],
                            mask=inp.get("mask"), ori_x=inp["x"])
-    y = cq.combine(cfg, bf16_dev(eo), dev_in["ids"], out["expand_idx"],
+    y = cq.combine(cfg, tok_dev(eo, wl.token_dtype), dev_in["ids"], out["expand_idx"],
                    to_dev(inp["expert_scales"]), out["ep_recv_count"],
                    out["recv_offsets"], dev_in["mask"], dev_in["x"])
     torch.cuda.synchronize()
-    return check_combine_tolerance(host(y), y_ref)
+    return check_combine_tolerance(host(y), y_ref, token_dtype=wl.token_dtype)

@@ -33,13 +33,13 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_config_struct_layout_matches_header():
-    # sixteen int32 fields (flags, then one reserved) then one int64
+    # sixteen int32 fields (flags, then token_dtype) then one int64
     assert ctypes.sizeof(cq.MoeDcConfig) == 16 * 4 + 8
     assert cq.MoeDcConfig.out_dtype.offset == 44
     assert cq.MoeDcConfig.scales_kind.offset == 48
     assert cq.MoeDcConfig.scale_format.offset == 52
     assert cq.MoeDcConfig.flags.offset == 56
-    assert cq.MoeDcConfig.reserved.offset == 60
+    assert cq.MoeDcConfig.token_dtype.offset == 60
     assert cq.MoeDcConfig.expand_rows_capacity.offset == 64
 
 
@@ -49,7 +49,8 @@ def test_header_enum_values_match_the_binding():
                  "MOE_DTYPE_E2M1",
                  "MOE_SCALES_NONE", "MOE_SCALES_SCALAR", "MOE_SCALES_SHARED",
                  "MOE_SCALES_PER_EXPERT", "MOE_SCALE_FP32", "MOE_SCALE_E8M0",
-                 "MOE_DC_FLAG_SEPARATE_ROUTE", "MOE_DC_FLAG_CHECK_IDS"):
+                 "MOE_DC_FLAG_SEPARATE_ROUTE", "MOE_DC_FLAG_CHECK_IDS", "MOE_TOKEN_BF16",
+                 "MOE_TOKEN_F16"):
         m = re.search(r"\b" + name + r"\s*=\s*(\d+)", text)
         assert m and int(m.group(1)) == getattr(cq, name), name
 
@@ -110,7 +111,8 @@ def test_valid_configs_of_the_workloads():
     (dict(zero_expert_num=2 ** 31 - 100), cq.MOE_ERR_INVALID_ARG),   # id space >= INT32_MAX
     (dict(expert_token_nums_type=2), cq.MOE_ERR_INVALID_ARG),
     (dict(mask_kind=3), cq.MOE_ERR_INVALID_ARG),
-    (dict(reserved=1), cq.MOE_ERR_INVALID_ARG),
+    (dict(token_dtype=2), cq.MOE_ERR_INVALID_ARG),
+    (dict(token_dtype=-1), cq.MOE_ERR_INVALID_ARG),
     (dict(flags=4), cq.MOE_ERR_INVALID_ARG),
     (dict(flags=-1), cq.MOE_ERR_INVALID_ARG),
     (dict(expand_rows_capacity=16 * 512 * 8 - 1), cq.MOE_ERR_INVALID_ARG),
