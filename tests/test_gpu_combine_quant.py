@@ -40,7 +40,7 @@ def _expert_out(wl, seed, scale_mix=True):
     if scale_mix:                                   # rows and blocks of very different sizes
         v *= rng.choice(np.float32([1e-20, 1e-3, 1.0, 1e3]), (wl.cap, 1))
         v[:, 8:16] = 0.0                            # one all-zero block per row
-    return workloads.f32_to_bf16_bits(v)
+    return workloads.f32_to_tok_bits(v, wl.token_dtype)
 
 
 def _run(wl, seed=0, eo=None):
@@ -54,7 +54,8 @@ def _run(wl, seed=0, eo=None):
     y_ref = oracle.combine_int8(ocfg, codes_ref, sc_ref, inp["expert_ids"], ref["expand_idx"],
                                 inp["expert_scales"], ref["ep_recv_count"],
                                 ref["recv_offsets"], mask=inp.get("mask"), ori_x=inp["x"])
-    codes, scales = cq.combine_quantize(cfg, harness.bf16_dev(eo), out["recv_offsets"])
+    codes, scales = cq.combine_quantize(cfg, harness.tok_dev(eo, wl.token_dtype),
+                                        out["recv_offsets"])
     y = cq.combine_int8(cfg, codes, scales, dev_in["ids"], out["expand_idx"],
                         harness.to_dev(inp["expert_scales"]), out["ep_recv_count"],
                         out["recv_offsets"], dev_in["mask"], dev_in["x"])
@@ -63,7 +64,7 @@ def _run(wl, seed=0, eo=None):
     np.testing.assert_array_equal(harness.host(codes)[:P], codes_ref[:P], err_msg="codes")
     np.testing.assert_array_equal(harness.host(scales)[:P].view(np.uint32),
                                   sc_ref[:P].view(np.uint32), err_msg="block scales")
-    return harness.check_combine_tolerance(harness.host(y), y_ref)
+    return harness.check_combine_tolerance(harness.host(y), y_ref, token_dtype=wl.token_dtype)
 
 
 @pytest.mark.parametrize("name", list(CASES))

@@ -28,8 +28,8 @@ CASES = {
 
 
 def _shared(wl, seed):
-    return workloads.f32_to_bf16_bits(np.random.default_rng(seed).standard_normal(
-        (wl.W, wl.BS, wl.H)).astype(np.float32))
+    return workloads.f32_to_tok_bits(np.random.default_rng(seed).standard_normal(
+        (wl.W, wl.BS, wl.H)).astype(np.float32), wl.token_dtype)
 
 
 def _run(wl, seed, with_shared, workspace=None):
@@ -38,28 +38,29 @@ def _run(wl, seed, with_shared, workspace=None):
     inp = workloads.generate(wl, seed=seed)
     ocfg, ref = harness.oracle_dispatch(wl, inp)
     cfg = harness.lib_cfg(wl)
-    x = harness.bf16_dev(inp["x"])
+    tok = wl.token_dtype
+    x = harness.tok_dev(inp["x"], tok)
     ids = harness.to_dev(inp["expert_ids"])
     mask = harness.to_dev(inp.get("mask"))
     w = harness.to_dev(inp["expert_scales"])
     out = cq.dispatch(cfg, x, ids, harness.to_dev(inp.get("scales")), mask, expert_scales=w)
     es_ref = oracle.expand_scales(ocfg, ref["assist_info"], ref["recv_offsets"],
                                   inp["expert_scales"], wl.cap)
-    eo = workloads.f32_to_bf16_bits(np.random.default_rng(seed + 3).standard_normal(
-        (wl.cap, wl.H)).astype(np.float32))
+    eo = workloads.f32_to_tok_bits(np.random.default_rng(seed + 3).standard_normal(
+        (wl.cap, wl.H)).astype(np.float32), tok)
     shared = _shared(wl, seed + 4) if with_shared else None
     y_ref = oracle.combine_scatter(ocfg, eo, ref["assist_info"], ref["recv_offsets"],
                                    inp["expert_ids"], inp["expert_scales"],
                                    mask=inp.get("mask"), ori_x=inp["x"], shared_x=shared)
-    y = cq.combine_scatter(cfg, harness.bf16_dev(eo), out["assist_info"], out["recv_offsets"],
-                           ids, w, mask, x, harness.bf16_dev(shared) if with_shared else None,
+    y = cq.combine_scatter(cfg, harness.tok_dev(eo, tok), out["assist_info"], out["recv_offsets"],
+                           ids, w, mask, x, harness.tok_dev(shared, tok) if with_shared else None,
                            workspace=workspace)
     torch.cuda.synchronize()
     harness.compare_dispatch(wl, inp, out, ref)
     P = int(ref["recv_offsets"][-1])
     np.testing.assert_array_equal(harness.host(out["expand_scales"])[:P].view(np.uint32),
                                   es_ref[:P].view(np.uint32), err_msg="expand_scales")
-    return harness.check_combine_tolerance(harness.host(y), y_ref)
+    return harness.check_combine_tolerance(harness.host(y), y_ref, token_dtype=tok)
 
 
 @pytest.mark.parametrize("with_shared", [False, True])

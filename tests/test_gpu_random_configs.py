@@ -5,7 +5,7 @@ allows, both mask kinds, the three routings) and a seeded input, then compares t
 library with the CPU oracle -- dispatch bit for bit, combine within 1e-2 relative / 1e-3
 absolute -- on both routing paths (inside the scatter launch where the batch is small, and
 as kernels of their own).  The int8 block-quantized and scatter-back combines run over the
-same configurations."""
+same configurations.  A further set of draws carries IEEE binary16 tokens instead of bf16."""
 import numpy as np
 import pytest
 
@@ -81,3 +81,26 @@ def test_random_config_int8_combine(i):
 def test_random_config_scatter_back(i):
     import test_gpu_combine_scatter as combine_scatter_tests
     combine_scatter_tests._run(random_workload(i), i, with_shared=(i % 4 == 1))
+
+
+# binary16 tokens (x, expert outputs, shared output and y) over further draws of the same
+# law; the routing path alternates with the case number
+N_F16 = 40
+
+
+@pytest.mark.parametrize("i", range(N_CASES, N_CASES + N_F16))
+def test_random_config_roundtrip_f16(i):
+    harness.roundtrip(random_workload(i).replace(token_dtype=1), seed=i, flags=i % 2)
+
+
+@pytest.mark.parametrize("i", range(N_CASES, N_CASES + N_F16, 2))
+def test_random_config_int8_combine_f16(i):
+    import test_gpu_combine_quant as combine_quant_tests
+    combine_quant_tests._run(random_workload(i).replace(token_dtype=1), seed=i)
+
+
+@pytest.mark.parametrize("i", range(N_CASES + 1, N_CASES + N_F16, 2))
+def test_random_config_scatter_back_f16(i):
+    import test_gpu_combine_scatter as combine_scatter_tests
+    combine_scatter_tests._run(random_workload(i).replace(token_dtype=1), i,
+                               with_shared=(i % 4 == 1))
