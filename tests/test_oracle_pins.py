@@ -428,6 +428,51 @@ def test_combine_exact_closed_form():
             assert (workloads.bf16_bits_to_f32(y[s, i]) == want).all()
 
 
+def test_combine_sums_in_k_order():
+    """y = bf16 of the fp32 running sum over k = 0, 1, ..., K-1 of w_k * row_k ([DDD] §3.4.2):
+    numpy float32 arithmetic in that order, rows located by the brute-force router.  Each
+    token's first pick carries a large term that its last pick cancels exactly, with small
+    terms between them, so the small terms are absorbed at the large term's spacing and the
+    result depends on the order; the reverse order (a witness) gives a different y on the
+    same draw.  Weights are powers of two, so every product is exact."""
+    W, E, BS, H, K = 2, 8, 16, 1024, 6
+    rng = np.random.default_rng(17)
+    ids = np.stack([rng.permutation(E)[:K] for _ in range(W * BS)]).astype(np.int32)
+    ids = ids.reshape(W, BS, K)
+    cfg = oracle.make_cfg(W, E, BS, H, K)
+    cnt, eidx = oracle.route(cfg, ids)
+    erc, etn, off = oracle.recv_counts(cfg, cnt)
+    rows_of, *_ = brute.route(W, E, BS, K, ids)
+    P = int(off[-1])
+    w = rng.choice(np.float32([0.5, 1.0, 2.0]), (W, BS, K))
+    v = rng.standard_normal((P, H)).astype(np.float32)
+    big = np.float32(2.0 ** 16) * (1 + rng.random((W, BS, H))).astype(np.float32)
+    big = workloads.bf16_bits_to_f32(workloads.f32_to_bf16_bits(big))
+    for s in range(W):
+        for i in range(BS):
+            v[rows_of[(s, i, 0)]] = big[s, i]
+            v[rows_of[(s, i, K - 1)]] = -big[s, i] * (w[s, i, 0] / w[s, i, K - 1])
+    eo = workloads.f32_to_bf16_bits(v)
+    rows = workloads.bf16_bits_to_f32(eo)
+    assert (rows[[rows_of[(s, i, K - 1)] for s in range(W) for i in range(BS)]]
+            == -(big * (w[..., :1] / w[..., K - 1:])).reshape(W * BS, H)).all()
+    y = oracle.combine(cfg, eo, ids, eidx, w, erc, off)
+    differs = 0
+    for s in range(W):
+        for i in range(BS):
+            terms = [w[s, i, k] * rows[rows_of[(s, i, k)]] for k in range(K)]
+            fwd = np.zeros(H, np.float32)
+            for t in terms:
+                fwd = fwd + t
+            rev = np.zeros(H, np.float32)
+            for t in reversed(terms):
+                rev = rev + t
+            want = workloads.f32_to_bf16_bits(fwd)
+            assert (y[s, i] == want).all(), (s, i)
+            differs += int((workloads.f32_to_bf16_bits(rev) != want).sum())
+    assert differs > 1000, f"the draw should make the summation order visible ({differs})"
+
+
 def test_combine_special_experts_and_masks():
     W, E, BS, H, K = 2, 4, 3, 1024, 2
     Z, C = 1, 1
