@@ -25,8 +25,11 @@ PIN_FILES = ["tests/test_oracle_f16_tokens.py", "tests/test_oracle_combine_quant
              "tests/test_oracle_pins.py"]
 
 _T = "float t = w * tok_to_f32(c->token_dtype, src[h]);"
+_RQ = "double r = nearbyint(a / quantum) * quantum;"     # binary16, then E2M1
+_NQ = "double n = nearbyint(a / quantum);"                # E4M3, then E5M2
 
-# (name, text in moe_oracle.c, replacement, which occurrence of the text)
+# (name, text in moe_oracle.c, replacement, which occurrence of the text); every mutant
+# keeps its reads and writes inside the buffers, so it fails a pin rather than crashing
 MUTANTS = [
     ("bf16 ties away from zero",
      "if (drop > 0x8000u || (drop == 0x8000u && (keep & 1u))) keep += 1u;",
@@ -89,6 +92,28 @@ MUTANTS = [
     ("scatter-back slot transposed",
      "size_t ep_offset = (size_t)i * K + k;", "size_t ep_offset = (size_t)k * c->BS + i;", 0),
     ("shared expert's term dropped", "if (shared_x) {", "if (0 && shared_x) {", 0),
+    ("binary16 ties away from zero", _RQ, "double r = round(a / quantum) * quantum;", 0),
+    ("E2M1 ties away from zero", _RQ, "double r = round(a / quantum) * quantum;", 1),
+    ("E4M3 ties away from zero", _NQ, "double n = round(a / quantum);", 0),
+    ("E5M2 ties away from zero", _NQ, "double n = round(a / quantum);", 1),
+    ("int8 ties away from zero", "float r = nearbyintf(v);", "float r = roundf(v);", 0),
+    ("NaN products encoded", "q[h] = isnan(v) ? 0 : encode(ct, v);", "q[h] = encode(ct, v);", 0),
+    ("per-pick mask read per token",
+     "return mask[((size_t)s * c->BS + i) * c->K + k] != 0;",
+     "return mask[(size_t)s * c->BS + i] != 0;", 0),
+    ("ordinals counted pick-major instead of token-major",
+     "        for (int32_t i = 0; i < c->BS; ++i)\n"
+     "            for (int32_t k = 0; k < c->K; ++k) {\n"
+     "                size_t p = ((size_t)s * c->BS + i) * c->K + k;\n"
+     "                int32_t e = expert_ids[p];\n"
+     "                if (e < 0 || e >= id_end) return -1;",
+     "        for (int32_t k = 0; k < c->K; ++k)\n"
+     "            for (int32_t i = 0; i < c->BS; ++i) {\n"
+     "                size_t p = ((size_t)s * c->BS + i) * c->K + k;\n"
+     "                int32_t e = expert_ids[p];\n"
+     "                if (e < 0 || e >= id_end) return -1;", 0),
+    ("receiver windows not accumulated",
+     "recv_offsets[r + 1] = recv_offsets[r] + run;", "recv_offsets[r + 1] = run;", 0),
 ]
 
 
