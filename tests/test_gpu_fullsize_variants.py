@@ -21,6 +21,8 @@ DISPATCH_CASES = {
                                             scales_kind=3),
     # MX E5M2 + E8M0 at the Zipf-routed W=16 shape
     "c3_e5m2_e8m0": workloads.C3_E5M2_E8M0,
+    # int8 per token at the W=16, H=7168 shape with binary16 tokens
+    "c4_f16_tokens": workloads.C4_F16,
 }
 
 
@@ -56,7 +58,8 @@ def test_fullsize_variant_dispatch(name):
             row = int(oracle.dest_row(ocfg, erc, off, s, e, o))
             assert tuple(ai[row]) == (s, i, k)
             pre = None if wl.scales_kind == 0 else inp["scales"][e]
-            q, sc = oracle.quant_row(wl.quant_mode, inp["x"][s, i], pre, wl.out_dtype)
+            q, sc = oracle.quant_row(wl.quant_mode, inp["x"][s, i], pre, wl.out_dtype,
+                                     token_dtype=wl.token_dtype)
             got = harness.host(out["expand_x"][row])
             assert (got.view(np.uint8) == q.view(np.uint8)).all(), (s, i, k)
             ds = harness.host(out["dynamic_scales"][row])
@@ -106,3 +109,37 @@ def test_c5_int8_combine_sampled():
                                          inp["expert_scales"], erc, roff, s, i,
                                          mask=inp["mask"], ori_x=inp["x"])
         assert harness.check_combine_tolerance(y_h[s, i], want) == 0
+
+
+def test_c4_f16_combine_sampled():
+    """The W=16, H=7168, K=8 round trip with binary16 tokens at full size: the gather
+    combine's outputs for sampled tokens against the oracle, from the rows they read."""
+    import torch
+    import combine_quant_amd as cq
+    wl = workloads.C4_F16
+    inp = workloads.generate(wl, seed=0)
+    cfg, dev_in, out = harness.gpu_dispatch(wl, inp)
+    eo_dev = workloads.expert_out_torch(wl, wl.cap, seed=0)
+    assert eo_dev.dtype == torch.float16
+    y = cq.combine(cfg, eo_dev, dev_in["ids"], out["expand_idx"],
+                   harness.to_dev(inp["expert_scales"]), out["ep_recv_count"],
+                   out["recv_offsets"], dev_in["mask"], dev_in["x"])
+    torch.cuda.synchronize()
+    assert y.dtype == torch.float16
+    eidx = harness.host(out["expand_idx"])
+    erc = harness.host(out["ep_recv_count"])
+    roff = harness.host(out["recv_offsets"])
+    ocfg = harness.oracle_cfg(wl)
+    tokens = _sample(wl, 7)
+    rows = sorted({int(oracle.dest_row(ocfg, erc, roff, s, int(inp["expert_ids"][s, i, k]),
+                                       int(eidx[s, i, k])))
+                   for s, i in tokens for k in range(wl.K) if eidx[s, i, k] >= 0})
+    rows_t = torch.tensor(rows, dtype=torch.long, device="cuda")
+    eo_rows = harness.host(eo_dev.index_select(0, rows_t))
+    eo_h = np.zeros((wl.cap, wl.H), np.uint16)
+    eo_h[rows] = eo_rows
+    y_h = harness.host(y)
+    for s, i in tokens:
+        want = oracle.combine_token(ocfg, eo_h, inp["expert_ids"], eidx, inp["expert_scales"],
+                                    erc, roff, s, i, mask=inp.get("mask"), ori_x=inp["x"])
+        assert harness.check_combine_tolerance(y_h[s, i], want, token_dtype=1) == 0, (s, i)
