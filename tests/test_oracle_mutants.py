@@ -27,6 +27,8 @@ PIN_FILES = ["tests/test_oracle_f16_tokens.py", "tests/test_oracle_combine_quant
 _T = "float t = w * tok_to_f32(c->token_dtype, src[h]);"
 _RQ = "double r = nearbyint(a / quantum) * quantum;"     # binary16, then E2M1
 _NQ = "double n = nearbyint(a / quantum);"                # E4M3, then E5M2
+_EMAX = "return ct == ORACLE_CODE_E4M3 ? 8 : ct == ORACLE_CODE_E5M2 ? 15 : 2;"
+_ZE = "const int32_t zero_end = c->E + c->zero_expert_num;"   # the gather combine first
 
 # (name, text in moe_oracle.c, replacement, which occurrence of the text); every mutant
 # keeps its reads and writes inside the buffers, so it fails a pin rather than crashing
@@ -114,6 +116,12 @@ MUTANTS = [
      "                if (e < 0 || e >= id_end) return -1;", 0),
     ("receiver windows not accumulated",
      "recv_offsets[r + 1] = recv_offsets[r] + run;", "recv_offsets[r + 1] = run;", 0),
+    ("E5M2 emax 16", _EMAX, "return ct == ORACLE_CODE_E4M3 ? 8 : ct == ORACLE_CODE_E5M2 ? 16 : 2;", 0),
+    ("E2M1 emax 1", _EMAX, "return ct == ORACLE_CODE_E4M3 ? 8 : ct == ORACLE_CODE_E5M2 ? 15 : 1;", 0),
+    ("assist_info stores (s, k, i)",
+     "assist_info[(size_t)row * 3 + 1] = i;\n                assist_info[(size_t)row * 3 + 2] = k;",
+     "assist_info[(size_t)row * 3 + 1] = k;\n                assist_info[(size_t)row * 3 + 2] = i;", 0),
+    ("zero experts combined as copy experts", _ZE, "const int32_t zero_end = c->E;", 0),
 ]
 
 
