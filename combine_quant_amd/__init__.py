@@ -15,5 +15,5 @@ from .binding import (  # noqa: F401
     combine_scatter, dispatch, load_library, make_config, moe_combine, moe_combine_int8,
     moe_combine_quantize, moe_combine_scatter, moe_dc_combine_scatter_workspace_bytes,
     moe_dc_dispatch_workspace_bytes, moe_dc_last_error, moe_dc_scales_per_row,
-    moe_dc_validate, moe_dc_version, moe_dispatch, prepare_combine, prepare_combine_int8,
+    moe_dc_validate, moe_dc_version, moe_dispatch, moe_dispatch_no_workspace, prepare_combine, prepare_combine_int8,
     prepare_combine_quantize, prepare_combine_scatter, prepare_dispatch)

@@ -25,7 +25,8 @@ _STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
            -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_DEVICE"}
 
 EXPORTS = ("moe_dc_validate", "moe_dc_scales_per_row", "moe_dc_dispatch_workspace_bytes",
-           "moe_dc_combine_scatter_workspace_bytes", "moe_dispatch", "moe_combine",
+           "moe_dc_combine_scatter_workspace_bytes", "moe_dispatch",
+           "moe_dispatch_no_workspace", "moe_combine",
            "moe_combine_scatter", "moe_combine_quantize", "moe_combine_int8",
            "moe_dc_last_error", "moe_dc_version")
 
@@ -91,6 +92,8 @@ def load_library(path: str = LIB) -> ctypes.CDLL:
     lib.moe_dc_dispatch_workspace_bytes.argtypes = [cfgp]
     lib.moe_dispatch.restype = ctypes.c_int
     lib.moe_dispatch.argtypes = [cfgp] + [P] * 13 + [P, ctypes.c_size_t, P]
+    lib.moe_dispatch_no_workspace.restype = ctypes.c_int
+    lib.moe_dispatch_no_workspace.argtypes = [cfgp] + [P] * 13 + [P]
     lib.moe_dc_combine_scatter_workspace_bytes.restype = ctypes.c_size_t
     lib.moe_dc_combine_scatter_workspace_bytes.argtypes = [cfgp]
     lib.moe_combine_scatter.restype = ctypes.c_int
@@ -277,6 +280,20 @@ def moe_dispatch(cfg, x, expert_ids, scales, x_active_mask, expand_x, dynamic_sc
                             dynamic_scales, expand_idx, assist_info, ep_recv_count,
                             expert_token_nums, recv_offsets, workspace, expert_scales,
                             expand_scales), stream)
+
+
+def moe_dispatch_no_workspace(cfg, x, expert_ids, scales, x_active_mask, expand_x,
+                              dynamic_scales, expand_idx, assist_info, ep_recv_count,
+                              expert_token_nums, recv_offsets, stream=None, expert_scales=None,
+                              expand_scales=None):
+    """Enqueue one dispatch without a workspace (the library's own static scratch is used);
+    the arguments are moe_dispatch's, less the workspace."""
+    fn, args, dev = _dispatch_call(cfg, x, expert_ids, scales, x_active_mask, expand_x,
+                                   dynamic_scales, expand_idx, assist_info, ep_recv_count,
+                                   expert_token_nums, recv_offsets, None, expert_scales,
+                                   expand_scales)
+    # moe_dispatch's argument list without its last two (workspace, workspace_bytes)
+    _launch(load_library().moe_dispatch_no_workspace, args[:-2], dev, stream)
 
 
 def _combine_call(cfg, expert_out, expert_ids, expand_idx, expert_scales, ep_recv_count,

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_dc.so")
-SOURCES = ["api.cpp", "route.hip", "dispatch.hip", "combine.hip"]
+SOURCES = ["api.cpp", "route.hip", "dispatch.hip", "combine.hip", "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

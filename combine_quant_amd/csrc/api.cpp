@@ -149,6 +149,45 @@ moe_status check(const moe_dc_config* c, moe_dc::Shape* out)
     return MOE_OK;
 }
 
+}  // namespace
+
+moe_status moe_dc::set_error(moe_status st, const char* msg)
+{
+    return fail(st, "%s", msg);
+}
+
+moe_status moe_dc::check_dispatch_args(const moe_dc_config* cfg, const void* x,
+                                       const int32_t* expert_ids, const float* scales,
+                                       const uint8_t* x_active_mask, const float* expert_scales,
+                                       const void* expand_x, const void* dynamic_scales,
+                                       const int32_t* expand_idx, const int32_t* assist_info,
+                                       const int32_t* ep_recv_count,
+                                       const int64_t* expert_token_nums,
+                                       const int64_t* recv_offsets, const float* expand_scales,
+                                       Shape* out)
+{
+    moe_dc::Shape sh;
+    moe_status st = check(cfg, &sh);
+    if (st != MOE_OK) return st;
+    if (!x || !expert_ids || !expand_x || !expand_idx || !assist_info || !ep_recv_count ||
+        !expert_token_nums || !recv_offsets)
+        return fail(MOE_ERR_INVALID_ARG, "a required tensor pointer is NULL");
+    if (sh.scales_per_row > 0 && !dynamic_scales)
+        return fail(MOE_ERR_INVALID_ARG, "dynamic_scales is required for quant_mode %d",
+                    sh.quant_mode);
+    if ((sh.scales_kind != MOE_SCALES_NONE) != (scales != nullptr))
+        return fail(MOE_ERR_INVALID_ARG,
+                    "scales must be given iff scales_kind is not MOE_SCALES_NONE");
+    if ((sh.mask_kind != 0) != (x_active_mask != nullptr))
+        return fail(MOE_ERR_INVALID_ARG, "x_active_mask must be given iff mask_kind != 0");
+    if ((expert_scales != nullptr) != (expand_scales != nullptr))
+        return fail(MOE_ERR_INVALID_ARG, "expert_scales and expand_scales go together");
+    if (out) *out = sh;
+    return MOE_OK;
+}
+
+namespace {
+
 moe_status device_status(hipError_t e, const char* what)
 {
     if (e == hipSuccess) return MOE_OK;
@@ -188,21 +227,12 @@ moe_status moe_dispatch(const moe_dc_config* cfg, const void* x, const int32_t* 
                         void* stream)
 {
     moe_dc::Shape sh;
-    moe_status st = check(cfg, &sh);
+    moe_status st = moe_dc::check_dispatch_args(cfg, x, expert_ids, scales, x_active_mask,
+                                                expert_scales, expand_x, dynamic_scales,
+                                                expand_idx, assist_info, ep_recv_count,
+                                                expert_token_nums, recv_offsets,
+                                                expand_scales, &sh);
     if (st != MOE_OK) return st;
-    if (!x || !expert_ids || !expand_x || !expand_idx || !assist_info || !ep_recv_count ||
-        !expert_token_nums || !recv_offsets)
-        return fail(MOE_ERR_INVALID_ARG, "a required tensor pointer is NULL");
-    if (sh.scales_per_row > 0 && !dynamic_scales)
-        return fail(MOE_ERR_INVALID_ARG, "dynamic_scales is required for quant_mode %d",
-                    sh.quant_mode);
-    if ((sh.scales_kind != MOE_SCALES_NONE) != (scales != nullptr))
-        return fail(MOE_ERR_INVALID_ARG,
-                    "scales must be given iff scales_kind is not MOE_SCALES_NONE");
-    if ((sh.mask_kind != 0) != (x_active_mask != nullptr))
-        return fail(MOE_ERR_INVALID_ARG, "x_active_mask must be given iff mask_kind != 0");
-    if ((expert_scales != nullptr) != (expand_scales != nullptr))
-        return fail(MOE_ERR_INVALID_ARG, "expert_scales and expand_scales go together");
     const size_t need = moe_dc::workspace_bytes(sh);
     if (!workspace || workspace_bytes < need)
         return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,

@@ -5,7 +5,25 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "moe_dc.h"
+
 namespace moe_dc {
+
+// Records `msg` as the calling thread's moe_dc_last_error() text and returns `st`.
+moe_status set_error(moe_status st, const char* msg);
+
+struct Shape;
+
+// Every host-side rule of moe_dispatch except those on the workspace: the config, the
+// required pointers and the pairings of optional ones.  Fills *out (if not null) on success.
+moe_status check_dispatch_args(const moe_dc_config* cfg, const void* x,
+                               const int32_t* expert_ids, const float* scales,
+                               const uint8_t* x_active_mask, const float* expert_scales,
+                               const void* expand_x, const void* dynamic_scales,
+                               const int32_t* expand_idx, const int32_t* assist_info,
+                               const int32_t* ep_recv_count, const int64_t* expert_token_nums,
+                               const int64_t* recv_offsets, const float* expand_scales,
+                               Shape* out);
 
 // Element types of expand_x (the values of moe_dtype in the C ABI).
 enum CodeType : int32_t {

@@ -223,6 +223,29 @@ moe_status moe_dispatch(const moe_dc_config* cfg,
                         float* expand_scales,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* moe_dispatch_no_workspace -- moe_dispatch without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  It runs the same kernels and writes the same outputs as
+ * moe_dispatch; its workspace is a 1 MiB array in the library's own device memory, one per
+ * GPU, held from the library's load until the process ends.
+ *
+ * Arguments: as for moe_dispatch, less workspace and workspace_bytes.
+ * Limits and errors: a config whose moe_dc_dispatch_workspace_bytes exceeds 1 MiB
+ * (E * W above about 261,000 counts) returns MOE_ERR_WORKSPACE, and MOE_DC_FLAG_CHECK_IDS
+ * (whose count lands in the caller's workspace) returns MOE_ERR_INVALID_ARG; both are checked
+ * on the host before anything is enqueued.  The first call on a device looks up that device's
+ * copy of the array (MOE_ERR_DEVICE if the lookup fails).  Nothing is allocated or freed.
+ * Every call on one GPU uses the same array: calls that may run concurrently on one GPU
+ * (other streams, other threads) race and must be ordered by the caller. */
+moe_status moe_dispatch_no_workspace(const moe_dc_config* cfg,
+                                     const void* x, const int32_t* expert_ids,
+                                     const float* scales, const uint8_t* x_active_mask,
+                                     const float* expert_scales,
+                                     void* expand_x, void* dynamic_scales, int32_t* expand_idx,
+                                     int32_t* assist_info, int32_t* ep_recv_count,
+                                     int64_t* expert_token_nums, int64_t* recv_offsets,
+                                     float* expand_scales, void* stream);
+
 /* moe_combine -- gather each token's K expert outputs and form their weighted sum.
  *
  * Defined by: [DDD] §3.4 (a pick's expert output sits at its rank's window + the expert's
