@@ -261,8 +261,9 @@ moe_status moe_dispatch(const moe_dc_config* cfg, const void* x, const int32_t* 
             moe_dc::launch_route(sh, expert_ids, x_active_mask, expand_idx, seg, bad_counts, s),
             "route kernel launch");
         if (st != MOE_OK) return st;
+        int32_t* totals = reinterpret_cast<int32_t*>(ws + moe_dc::ws_scan_totals_offset(sh));
         st = device_status(moe_dc::launch_scan(sh, seg, ep_recv_count, expert_token_nums,
-                                               recv_offsets, bad_counts, bad_word, s),
+                                               recv_offsets, bad_counts, bad_word, totals, s),
                            "scan kernel launch");
         if (st != MOE_OK) return st;
     }

@@ -514,6 +514,51 @@ __device__ __forceinline__ uint32_t block_code(float x, float scale)
     return (uint32_t)(int32_t)r & 0xFFu;
 }
 
+// The eight codes of one block, each int8(fp16(x / scale)) exactly as block_code gives it,
+// with one IEEE division per block instead of one per element.  For a normal, finite scale,
+// r = 1 / scale is correctly rounded and q = x * r lies within 2.5 units in the last place
+// (binary32) of the correctly rounded quotient (two roundings of relative size 2^-24 each,
+// against a unit of at least 2^-24 of the value), so both round to the same binary16 value
+// unless a binary16 rounding midpoint lies between them.  In binary32 a midpoint between
+// neighbouring binary16 values has its low 13 fraction bits equal to 0x1000; a product whose
+// low 13 bits lie within 5 units of that pattern is recomputed with the exact division (near
+// a power of two the neighbouring midpoints are 2^12 units away, so no other pattern can be
+// crossed).  The binary16 value then rounds to an integer below 128 in magnitude: |x| <=
+// amax and scale = amax * fp32(1/127) give |x / scale| <= 127 * (1 + 2^-23), so no clamp and
+// no NaN arise on this path; adding 1.5 * 2^23 rounds it half to even and leaves the integer
+// in the low byte.  Any other scale (zero, subnormal, infinite or NaN) takes block_code.
+__device__ __forceinline__ uint2 block_codes8(const float (&f)[8], float scale)
+{
+    uint32_t c8[8];
+    const uint32_t sb = __float_as_uint(scale);
+    if (sb >= 0x00800000u && sb < 0x7F800000u) {
+        const float r = 1.0f / scale;
+        uint32_t near_mid = 0;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const float q = f[c] * r;
+            const float h = (float)(_Float16)q;
+            c8[c] = __float_as_uint(h + 12582912.0f);
+            near_mid |= ((__float_as_uint(q) & 0x1FFFu) - 0xFFBu) <= 10u ? 1u << c : 0u;
+        }
+        if (near_mid != 0) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                if (near_mid & (1u << c)) c8[c] = block_code(f[c], scale);
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) c8[c] = block_code(f[c], scale);
+    }
+    const uint32_t lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(c8[3], c8[2], 0x0c0c0400u),
+                                              __builtin_amdgcn_perm(c8[1], c8[0], 0x0c0c0400u),
+                                              0x05040100u);
+    const uint32_t hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(c8[7], c8[6], 0x0c0c0400u),
+                                              __builtin_amdgcn_perm(c8[5], c8[4], 0x0c0c0400u),
+                                              0x05040100u);
+    return make_uint2(lo, hi);
+}
+
 // One wave task = one row x 2 slots of 64 lanes; each lane owns one 8-element block.
 constexpr int kQuantSlots = 2;
 
@@ -557,11 +602,7 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_quantize_kerne
             amax = amax > b ? amax : b;
         }
         const float scale = __uint_as_float(amax) * kInv127;
-        uint32_t c8[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) c8[c] = block_code(f[c], scale);
-        const uint2 packed = make_uint2(c8[0] | (c8[1] << 8) | (c8[2] << 16) | (c8[3] << 24),
-                                        c8[4] | (c8[5] << 8) | (c8[6] << 16) | (c8[7] << 24));
+        const uint2 packed = block_codes8(f, scale);
         store_stream(reinterpret_cast<uint2*>(codes) + row * NV + v, packed);
         __builtin_nontemporal_store(scale, qscales + row * NV + v);
     }

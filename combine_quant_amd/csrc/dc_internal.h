@@ -57,15 +57,23 @@ struct Shape {
 //                 the pick counts there, the scan kernel overwrites each with the exclusive
 //                 running total, i.e. the first packed row of that (expert, source) segment
 //   bad counts    one int32 per source rank: its active picks with an id outside [0, E+Z+C)
+//   group totals  only when E*W > kScanMaxFlat: one int32 per group of ranks of the
+//                 two-launch scan (at most W groups)
 inline size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 constexpr size_t kWsSegOffset = 256;
+constexpr long long kScanMaxFlat = 16384;   // E*W the one-workgroup scan takes in one pass
 inline size_t ws_bad_counts_offset(const Shape& s)
 {
     return kWsSegOffset + round256((size_t)s.E * (size_t)s.W * sizeof(int32_t));
 }
-inline size_t workspace_bytes(const Shape& s)
+inline size_t ws_scan_totals_offset(const Shape& s)
 {
     return ws_bad_counts_offset(s) + round256((size_t)s.W * sizeof(int32_t));
+}
+inline size_t workspace_bytes(const Shape& s)
+{
+    const bool grouped = (long long)s.E * s.W > kScanMaxFlat;
+    return ws_scan_totals_offset(s) + (grouped ? round256((size_t)s.W * sizeof(int32_t)) : 0);
 }
 
 // Routing: counts per (expert, source) and the final expand_idx.  With bad_counts (else
@@ -75,10 +83,12 @@ hipError_t launch_route(const Shape& s, const int32_t* expert_ids, const uint8_t
                         hipStream_t stream);
 
 // Receive-side prefix sums: seg counts -> segment bases (in place) + the three outputs.
-// With bad_word (else null), the sum of the W bad_counts.
+// With bad_word (else null), the sum of the W bad_counts.  totals: the workspace's group
+// totals (used only when E*W > kScanMaxFlat).
 hipError_t launch_scan(const Shape& s, int32_t* seg, int32_t* ep_recv_count,
                        int64_t* expert_token_nums, int64_t* recv_offsets,
-                       const int32_t* bad_counts, int32_t* bad_word, hipStream_t stream);
+                       const int32_t* bad_counts, int32_t* bad_word, int32_t* totals,
+                       hipStream_t stream);
 
 // Small batches route inside the scatter launch: every workgroup recomputes the counts and
 // their prefix sums in LDS (W*BS*K ids, E*W counters) instead of reading them from the route

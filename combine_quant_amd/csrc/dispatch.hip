@@ -367,6 +367,14 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
     int32_t fused_own = -1;
     if (FUSED) fused_own = load_fused_picks(ids, fr, E, K, mask_kind, W * BS * K, tok, fused_picks);
 
+    // Under a mask a token may have no routed pick at all: then its row is never needed, so
+    // the token's expand_idx entries (written by the route kernel) are read first and such a
+    // token leaves before requesting its row.  Unmasked batches skip this wait.
+    if (!FUSED && mask_kind != 0) {
+        const int32_t ord = lane < K ? expand_idx[tok * K + lane] : -1;
+        if (__ballot(ord >= 0) == 0) return;              // uniform over the workgroup
+    }
+
     // 1. this wave's slots of the token row (and of a shared scales row), in flight before
     //    anything waits
     const uint4* xr = reinterpret_cast<const uint4*>(x) + tok * NV;

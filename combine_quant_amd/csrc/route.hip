@@ -35,6 +35,8 @@ namespace {
 constexpr int kMaxRouteExperts = 256; // experts per routing workgroup, at most
 constexpr int kScanThreads = 1024;    // >= E (E <= 1024 is validated)
 constexpr int kScanLdsCounts = 16384; // counts staged in LDS by the scan (64 KiB)
+constexpr int kGroupCounts = 15872;   // entries per group of ranks in the two-launch scan: with
+                                      // its padding, under 64 KiB of LDS
 
 // Expert id of each pick of token `tok`, or -1 when the pick is not routed (inactive,
 // special expert, or an id outside [0, E)).  Every load of the token (ids, mask bytes) is
@@ -291,41 +293,110 @@ __global__ __launch_bounds__(kScanThreads) void scan_flat_kernel(
 #undef ex
 }
 
-// Receive-side scan for shapes whose counts exceed the LDS budget: one thread per expert
-// walks its W sources in global memory (each thread reads and rewrites only its own
-// entries).
-__global__ __launch_bounds__(kScanThreads) void scan_kernel(
-    int W, int E, int L, int etn_type, int32_t* __restrict__ seg,
-    int32_t* __restrict__ ep_recv_count, int64_t* __restrict__ expert_token_nums,
-    int64_t* __restrict__ recv_offsets, const int32_t* __restrict__ bad_counts,
-    int32_t* __restrict__ bad_word)
+// One workgroup: *out = the sum of every thread's v.
+__device__ void block_sum_to_value(int32_t v, int32_t* __restrict__ out)
 {
-    if (bad_word) block_sum_to(bad_counts, W, bad_word);
-    __shared__ int32_t wave_tot[kScanThreads / kWave];
-    __shared__ int32_t expert_excl[kScanThreads];
-    const int e = threadIdx.x;
-    int32_t total = 0;
-    if (e < E)
-        for (int s = 0; s < W; ++s) total += seg[(long long)e * W + s];
-    const int32_t incl = block_inclusive_scan(total, wave_tot);
-    const int32_t excl = incl - total;
-    expert_excl[e] = excl;
+    __shared__ int32_t acc;
+    if (threadIdx.x == 0) acc = 0;
     __syncthreads();
-    if (e >= E) return;
-    const int r = e / L;
-    const int j = e - r * L;
-    const int32_t rank_base = expert_excl[r * L];
-    if (j == 0) recv_offsets[r] = rank_base;
-    if (e == E - 1) recv_offsets[W] = incl;
-    expert_token_nums[e] = etn_type == 0 ? (int64_t)(incl - rank_base) : (int64_t)total;
-    int32_t run = excl;
-    for (int s = 0; s < W; ++s) {
-        const long long f = (long long)e * W + s;   // = r*L*W + j*W + s
-        const int32_t c = seg[f];
-        seg[f] = run;
-        run += c;
-        ep_recv_count[f] = run - rank_base;
+    if (v != 0) atomicAdd(&acc, v);
+    __syncthreads();
+    if (threadIdx.x == 0) *out = acc;
+}
+
+// Receive-side scan for shapes whose counts exceed one workgroup's LDS budget (E*W >
+// kScanMaxFlat), in two launches over groups of whole receiver ranks.  Every output of a
+// rank r -- its ep_recv_count row, its experts' expert_token_nums, recv_offsets[r] -- is a
+// difference of running totals inside the rank's own entries [r*L*W, (r+1)*L*W), except for
+// one offset common to all of them: the number of rows of the ranks before it.  So the ranks
+// are cut into groups of R consecutive ranks (R*L*W <= kGroupCounts; one rank has
+// L*W <= 2048 entries, so R >= 7); scan_group_totals_kernel sums each group's counts, and
+// scan_groups_kernel adds up the totals of the groups before its own and then scans its
+// group in LDS exactly as scan_flat_kernel scans the whole array.
+__global__ __launch_bounds__(kScanThreads) void scan_group_totals_kernel(
+    int W, int L, int R, const int32_t* __restrict__ seg, int32_t* __restrict__ totals,
+    const int32_t* __restrict__ bad_counts, int32_t* __restrict__ bad_word)
+{
+    if (blockIdx.x == 0 && bad_word) block_sum_to(bad_counts, W, bad_word);
+    const int LW = L * W;
+    const int r0 = blockIdx.x * R;
+    const int r1 = min(W, r0 + R);
+    const int f0 = r0 * LW;
+    const int n = (r1 - r0) * LW;
+    int32_t c[kScanLdsCounts / kScanThreads];
+#pragma unroll
+    for (int j = 0; j < kScanLdsCounts / kScanThreads; ++j) {
+        const int f = threadIdx.x + j * kScanThreads;
+        c[j] = f < n ? seg[f0 + f] : 0;
     }
+    int32_t sum = 0;
+#pragma unroll
+    for (int j = 0; j < kScanLdsCounts / kScanThreads; ++j) sum += c[j];
+    block_sum_to_value(sum, &totals[blockIdx.x]);
+}
+
+__global__ __launch_bounds__(kScanThreads) void scan_groups_kernel(
+    int W, int E, int L, int R, int etn_type, int32_t* __restrict__ seg,
+    int32_t* __restrict__ ep_recv_count, int64_t* __restrict__ expert_token_nums,
+    int64_t* __restrict__ recv_offsets, const int32_t* __restrict__ totals)
+{
+    extern __shared__ int32_t lds_grp[];     // padded group entries + 1
+    __shared__ int32_t wave_tot[kScanThreads / kWave];
+    __shared__ int32_t before_lds;
+    const int LW = L * W;
+    const int g = blockIdx.x;
+    const int r0 = g * R;
+    const int r1 = min(W, r0 + R);
+    const int f0 = r0 * LW;
+    const int n = (r1 - r0) * LW;
+    const int t = threadIdx.x;
+    const int nt = blockDim.x;
+#define ex(f) lds_grp[(f) + ((f) >> 5)]
+    // this group's counts, requested together with the earlier groups' totals
+    int32_t staged[kScanLdsCounts / kScanThreads];
+#pragma unroll
+    for (int j = 0; j < kScanLdsCounts / kScanThreads; ++j) {
+        const int f = t + j * kScanThreads;
+        staged[j] = f < n ? seg[f0 + f] : 0;
+    }
+    int32_t prior = 0;
+    for (int q = t; q < g; q += nt) prior += totals[q];
+    if (t == 0) before_lds = 0;
+#pragma unroll
+    for (int j = 0; j < kScanLdsCounts / kScanThreads; ++j) {
+        const int f = t + j * kScanThreads;
+        if (f < n) ex(f) = staged[j];
+    }
+    __syncthreads();
+    if (prior != 0) atomicAdd(&before_lds, prior);
+    const int per = (n + nt - 1) / nt;
+    const int lo = min(n, t * per);
+    const int hi = min(n, lo + per);
+    int32_t run = 0;
+    for (int f = lo; f < hi; ++f) run += ex(f);
+    const int32_t incl = block_inclusive_scan(run, wave_tot);   // its barrier also publishes
+    const int32_t before = before_lds;                           // before_lds
+    int32_t acc = before + incl - run;
+    for (int f = lo; f < hi; ++f) {
+        const int32_t c = ex(f);
+        ex(f) = acc;
+        acc += c;
+    }
+    if (t == nt - 1) ex(n) = before + incl;
+    __syncthreads();
+    for (int f = t; f < n; f += nt) {
+        seg[f0 + f] = ex(f);
+        const int rank_first = (f / LW) * LW;
+        ep_recv_count[f0 + f] = ex(f + 1) - ex(rank_first);
+    }
+    for (int e = r0 * L + t; e < r1 * L; e += nt) {
+        const int rank_first = (e / L) * LW - f0;
+        const int from = etn_type == 0 ? rank_first : e * W - f0;
+        expert_token_nums[e] = (int64_t)(ex((e + 1) * W - f0) - ex(from));
+    }
+    for (int r = r0 + t; r < r1; r += nt) recv_offsets[r] = ex(r * LW - f0);
+    if (r1 == W && t == 0) recv_offsets[W] = ex(n);
+#undef ex
 }
 
 }  // namespace
@@ -360,19 +431,26 @@ hipError_t launch_route(const Shape& sh, const int32_t* expert_ids, const uint8_
 
 hipError_t launch_scan(const Shape& sh, int32_t* seg, int32_t* ep_recv_count,
                        int64_t* expert_token_nums, int64_t* recv_offsets,
-                       const int32_t* bad_counts, int32_t* bad_word, hipStream_t stream)
+                       const int32_t* bad_counts, int32_t* bad_word, int32_t* totals,
+                       hipStream_t stream)
 {
     const long long n = (long long)sh.E * sh.W;
-    if (n <= kScanLdsCounts) {
+    if (n <= kScanMaxFlat) {
         const size_t words = (size_t)n + 1 + (size_t)((n + 1) >> 5) + 1 + sh.E;
         hipLaunchKernelGGL(scan_flat_kernel, dim3(1), dim3(kScanThreads),
                            words * sizeof(int32_t), stream, sh.W, sh.E, sh.L, sh.etn_type, seg,
                            ep_recv_count, expert_token_nums, recv_offsets, bad_counts, bad_word);
     } else {
-        const int threads = ((sh.E + kWave - 1) / kWave) * kWave;
-        hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(threads), 0, stream, sh.W, sh.E, sh.L,
-                           sh.etn_type, seg, ep_recv_count, expert_token_nums, recv_offsets,
-                           bad_counts, bad_word);
+        // groups of R whole ranks, R * L * W <= kGroupCounts (L * W <= 2048 gives R >= 7)
+        const int LW = sh.L * sh.W;
+        const int R = kGroupCounts / LW;
+        const int G = (sh.W + R - 1) / R;
+        const size_t words = (size_t)R * LW + 1 + (((size_t)R * LW + 1) >> 5) + 1;
+        hipLaunchKernelGGL(scan_group_totals_kernel, dim3(G), dim3(kScanThreads), 0, stream,
+                           sh.W, sh.L, R, seg, totals, bad_counts, bad_word);
+        hipLaunchKernelGGL(scan_groups_kernel, dim3(G), dim3(kScanThreads),
+                           words * sizeof(int32_t), stream, sh.W, sh.E, sh.L, R, sh.etn_type,
+                           seg, ep_recv_count, expert_token_nums, recv_offsets, totals);
     }
     return hipGetLastError();
 }

@@ -231,7 +231,7 @@ moe_status moe_dispatch(const moe_dc_config* cfg,
  *
  * Arguments: as for moe_dispatch, less workspace and workspace_bytes.
  * Limits and errors: a config whose moe_dc_dispatch_workspace_bytes exceeds 1 MiB
- * (E * W above about 261,000 counts) returns MOE_ERR_WORKSPACE, and MOE_DC_FLAG_CHECK_IDS
+ * (E * W above about 260,000 counts) returns MOE_ERR_WORKSPACE, and MOE_DC_FLAG_CHECK_IDS
  * (whose count lands in the caller's workspace) returns MOE_ERR_INVALID_ARG; both are checked
  * on the host before anything is enqueued.  The first call on a device looks up that device's
  * copy of the array (MOE_ERR_DEVICE if the lookup fails).  Nothing is allocated or freed.

@@ -139,6 +139,10 @@ def test_workspace_holds_the_checked_ids_word_and_per_rank_counts():
     assert cq.moe_dc_dispatch_workspace_bytes(c) == 256 + 256 * 16 * 4 + 256
     c = _cfg(W=3, E=9, BS=5)
     assert cq.moe_dc_dispatch_workspace_bytes(c) == 256 + 256 + 256
+    # more than 16,384 counts: the two-launch scan also keeps one total per group of ranks
+    # (at most W of them)
+    c = _cfg(W=768, E=768, BS=4, H=1024, K=2)
+    assert cq.moe_dc_dispatch_workspace_bytes(c) == 256 + 768 * 768 * 4 + 3072 + 3072
 
 
 def test_k_may_count_special_experts():

@@ -55,6 +55,14 @@ SMALL = {
     "bs1_h8192": workloads.Workload("bs1_h8192", W=2, E=2, BS=1, H=8192, K=2, quant_mode=2),
     "w768_e768": workloads.Workload("w768_e768", W=768, E=768, BS=1, H=1024, K=2,
                                     quant_mode=2),
+    # more (expert, source) counts than one LDS pass of the scan holds: chunked scan, with a
+    # short last chunk (24,192 counts) and with whole chunks (65,536 counts)
+    "scan_chunks_w24_e1008": workloads.Workload("scan_chunks_w24_e1008", W=24, E=1008, BS=8,
+                                                H=1024, K=4, quant_mode=2,
+                                                expert_token_nums_type=0),
+    "scan_chunks_w64_e1024": workloads.Workload("scan_chunks_w64_e1024", W=64, E=1024, BS=4,
+                                                H=1024, K=8, quant_mode=4, zero_expert_num=1,
+                                                mask_kind=2, inactive_tokens_per_rank=1),
 }
 
 
@@ -228,17 +236,19 @@ def test_invalid_arguments_raise_and_enqueue_nothing():
     assert (o["expand_idx"] == 123).all()
 
 
-# 1: MOE_DC_FLAG_SEPARATE_ROUTE, 2: MOE_DC_FLAG_CHECK_IDS
+# 1: MOE_DC_FLAG_SEPARATE_ROUTE, 2: MOE_DC_FLAG_CHECK_IDS; the (W, E) pairs give 128 (expert,
+# source) counts, and 65,536 (the two-launch scan of wide count matrices)
 @pytest.mark.parametrize("flags", [0, 1, 2, 3])
 @pytest.mark.parametrize("K", [3, 4, 8, 16])
-def test_out_of_range_ids_are_not_dispatched(K, flags):
+@pytest.mark.parametrize("W,E,BS", [(4, 32, 60), (64, 1024, 6)])
+def test_out_of_range_ids_are_not_dispatched(W, E, BS, K, flags):
     """Ids outside [0, E+Z+C) break the contract; the library must treat such picks exactly
     like masked-off picks (no row, expand_idx -1, no combine term) and never touch memory
     out of bounds.  Reference: the oracle on the same input with those picks masked off.
     With the id check, the workspace's first int32 holds the number of active bad picks."""
     import torch
     import combine_quant_amd as cq
-    wl = workloads.Workload("bad_ids", W=4, E=32, BS=60, H=1024, K=K, quant_mode=2,
+    wl = workloads.Workload("bad_ids", W=W, E=E, BS=BS, H=1024, K=K, quant_mode=2,
                             zero_expert_num=1, copy_expert_num=1, mask_kind=2)
     inp = workloads.generate(wl, seed=11)
     rng = np.random.default_rng(5)

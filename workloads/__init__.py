@@ -183,10 +183,18 @@ C4_F16 = C4.replace(
     name="c4v_w16_f16_tokens", token_dtype=1,
     description="C4 with IEEE binary16 tokens (x, expert outputs and y in fp16)")
 
+# the widest count matrix the library accepts (768 ranks x 768 experts: 589,824 (expert,
+# source) counts, which the receive-side scan takes in chunks) with small rows, to time the
+# routing and scan steps at that width
+W768_SCAN = Workload(
+    "w768_e768_scan", W=768, E=768, BS=16, H=1024, K=4, quant_mode=2,
+    description="W=768 ranks, E=768 experts (one per rank), BS=16, H=1024, K=4, int8 per "
+                "token: the largest count matrix, for the routing and chunked scan steps")
+
 WORKLOADS = {w.name: w for w in (C1_MODE0, C1_MODE2, C2, C3, C4, C5, C3_E5M2_E8M0, C4_STATIC,
                                  C4_TOKEN_E4M3, C4_GROUP, C2_GROUP_SMOOTH, C4_COMBINE_INT8,
                                  C4_SCATTER_SHARED, C4_SMOOTH, SAMPLE_BS8, SAMPLE_BS8_Q,
-                                 SAMPLE_BS256, SAMPLE_BS256_Q, C3_MXFP4, C4_F16)}
+                                 SAMPLE_BS256, SAMPLE_BS256_Q, C3_MXFP4, C4_F16, W768_SCAN)}
 
 
 def _streams(seed: int):
