@@ -15,7 +15,9 @@ the committed rocprofv3 counter summary when it still matches the kernel source.
 `cpu_baseline` object times the CPU oracle (single-threaded C) on the same inputs.
 
 Modes (`--mode`): bench (default), copy-calib (a plain device copy of known size, for
-scaling the HBM byte counters).
+scaling the HBM byte counters), ceilings (the dispatch scatter's and the combine gather's
+access patterns with their arithmetic taken out, timed beside the library's own dispatch and
+combine on the same buffers: the rates those patterns allow on this chip).
 """
 from __future__ import annotations
 
@@ -55,7 +57,7 @@ def parse_args():
                          "larger than the 256 MB Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-passes", type=int, default=3)
-    ap.add_argument("--mode", default="bench", choices=["bench", "copy-calib"])
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy-calib", "ceilings"])
     ap.add_argument("--graph", action="store_true",
                     help="also capture one step per buffer set into a HIP graph and report the "
                          "replayed step time as the headline (launch gaps removed)")
@@ -194,6 +196,116 @@ def run_copy_calib(args):
     torch.cuda.synchronize()
     print(json.dumps({"mode": "copy-calib", "bytes_read_per_launch": n,
                       "bytes_written_per_launch": n, "launches": max(1, args.steps)}))
+
+
+def _median_us(fn, stream, steps, warmup):
+    """Median duration of fn() in microseconds, each call between two events on `stream`."""
+    import torch
+    for n in range(warmup):
+        fn(n)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for n in range(steps):
+        evs[n][0].record(stream)
+        fn(n)
+        evs[n][1].record(stream)
+    torch.cuda.synchronize()
+    return statistics.median(a.elapsed_time(b) * 1e3 for a, b in evs)
+
+
+def run_ceilings(args):
+    """The scatter's and the gather's access patterns without their arithmetic, from
+    libmoe_dc_ceiling.so, next to the library's dispatch and combine (same buffers, same
+    rotation of buffer sets).  Prints one JSON line."""
+    import ctypes
+    import torch
+    import combine_quant_amd as cq
+    from combine_quant_amd.build import CEILING_LIB
+
+    wl = workloads.WORKLOADS[args.workload]
+    if wl.H % 1024 != 0 or wl.quant_mode == 0 or wl.combine_path != "gather":
+        sys.exit("ceilings: needs a quantized gather workload with H a multiple of 1024")
+    lib = ctypes.CDLL(CEILING_LIB)
+    P_, i64, i32 = ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int
+    lib.ceiling_scatter_copy.argtypes = [P_, P_, P_, i64, i32, i32, P_]
+    lib.ceiling_write_rows.argtypes = [P_, P_, i64, i32, P_]
+    lib.ceiling_gather_sum.argtypes = [P_, P_, P_, i64, i32, i32, P_]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    inp = workloads.generate(wl, seed=args.seed)
+    cfg = cq.make_config(wl.W, wl.E, wl.BS, wl.H, wl.K, wl.quant_mode,
+                         zero_expert_num=wl.zero_expert_num, copy_expert_num=wl.copy_expert_num,
+                         expert_token_nums_type=wl.expert_token_nums_type,
+                         mask_kind=wl.mask_kind, out_dtype=wl.out_dtype,
+                         scales_kind=wl.scales_kind, scale_format=wl.scale_format,
+                         token_dtype=wl.token_dtype)
+    tdt = cq.token_torch_dtype(cfg)
+
+    def dev_t(a, dtype=None):
+        if a is None:
+            return None
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(dtype) if dtype is not None else t).to(dev)
+
+    ids, mask, smooth = dev_t(inp["expert_ids"]), dev_t(inp.get("mask")), dev_t(inp.get("scales"))
+    w = dev_t(inp["expert_scales"])
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    sets = []
+    for k in range(args.sets):
+        x = dev_t(inp["x"], tdt) if k == 0 else sets[0]["x"].clone()
+        st = dict(x=x, eo=workloads.expert_out_torch(wl, wl.cap, seed=args.seed, device=dev),
+                  y=torch.empty((wl.W, wl.BS, wl.H), dtype=tdt, device=dev),
+                  raw=torch.empty((wl.cap, wl.H), dtype=torch.uint8, device=dev))
+        st["dispatch"], st["out"] = cq.prepare_dispatch(cfg, x, ids, smooth, mask)
+        o = st["out"]
+        st["combine"], _ = cq.prepare_combine(cfg, st["eo"], ids, o["expand_idx"], w,
+                                              o["ep_recv_count"], o["recv_offsets"], mask, x,
+                                              st["y"])
+        sets.append(st)
+    for st in sets:
+        st["dispatch"]()
+    torch.cuda.synchronize()
+    o = sets[0]["out"]
+    P = int(o["recv_offsets"][-1].item())
+    ai = o["assist_info"][:P].long()
+    pick = (ai[:, 0] * wl.BS + ai[:, 1]) * wl.K + ai[:, 2]
+    dest = torch.full((wl.T * wl.K,), -1, dtype=torch.int32, device=dev)
+    dest[pick] = torch.arange(P, dtype=torch.int32, device=dev)       # row of each pick
+    order = dest[dest >= 0].contiguous()                              # rows, token-major
+    active = int((dest.view(wl.T, wl.K) >= 0).any(dim=1).sum().item())
+    ns = len(sets)
+    H, T, K = wl.H, wl.T, wl.K
+
+    def check(rc):
+        if rc != 0:
+            raise RuntimeError(f"ceiling kernel launch failed ({rc})")
+
+    runs = {
+        "library_dispatch": (lambda n: sets[n % ns]["dispatch"](), None),
+        "scatter_copy": (lambda n: check(lib.ceiling_scatter_copy(
+            sets[n % ns]["x"].data_ptr(), dest.data_ptr(), sets[n % ns]["raw"].data_ptr(), T, H,
+            K, sp)), 2 * H * active + H * P + 4 * T * K),
+        "write_rows_scatter_order": (lambda n: check(lib.ceiling_write_rows(
+            sets[n % ns]["raw"].data_ptr(), order.data_ptr(), P, H, sp)), H * P),
+        "write_rows_in_sequence": (lambda n: check(lib.ceiling_write_rows(
+            sets[n % ns]["raw"].data_ptr(), None, P, H, sp)), H * P),
+        "library_combine": (lambda n: sets[n % ns]["combine"](), None),
+        "gather_sum": (lambda n: check(lib.ceiling_gather_sum(
+            sets[n % ns]["eo"].data_ptr(), dest.data_ptr(), sets[n % ns]["y"].data_ptr(), T, H,
+            K, sp)), 2 * H * P + 2 * H * T + 4 * T * K),
+    }
+    res = {}
+    for name, (fn, nbytes) in runs.items():
+        us = _median_us(fn, stream, args.steps, args.warmup)
+        res[name] = {"median_us": round(us, 2)}
+        if nbytes is not None:
+            res[name]["bytes"] = nbytes
+            res[name]["gbps"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+    print(json.dumps({"mode": "ceilings", "workload": wl.name, "routed_rows": P,
+                      "active_tokens": active, "steps": args.steps, "sets": args.sets,
+                      "results": res}), flush=True)
 
 
 class _NoEvent:
@@ -422,6 +534,8 @@ def main():
         sys.exit(2)
     if args.mode == "copy-calib":
         run_copy_calib(args)
+    elif args.mode == "ceilings":
+        run_ceilings(args)
     else:
         run_bench(args)
 

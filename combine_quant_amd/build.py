@@ -14,6 +14,9 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_dc.so")
 SOURCES = ["api.cpp", "route.hip", "dispatch.hip", "combine.hip", "noalloc.hip"]
+# measurement kernels of bench.py's ceiling mode (the access patterns without the arithmetic)
+CEILING_LIB = os.path.join(HERE, "libmoe_dc_ceiling.so")
+CEILING_SOURCES = ["ceiling.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -42,17 +45,24 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libmoe_dc.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib, verbose):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source, link libmoe_dc.so and the ceiling-measurement library; returns
+    the path of libmoe_dc.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + CEILING_SOURCES
+    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    _link(objs[:len(SOURCES)], LIB, verbose)
+    _link(objs[len(SOURCES):], CEILING_LIB, verbose)
     return LIB
 
 

@@ -289,7 +289,8 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_int8_wide_kern
         srcs[k] = k < K ? lane_value(src, k) : kNone;
         ws[k] = lane_value(wk, k);
     }
-    if (u >= NU) return;
+    // lanes past the row's last unit still take part in the lane exchange before the stores
+    const bool live = u < NU;
 
     const uint4* cq = reinterpret_cast<const uint4*>(codes);
     const uint2* sq = reinterpret_cast<const uint2*>(qscales);
@@ -298,7 +299,7 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_int8_wide_kern
     uint2 sbuf[KMAX];
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
-        if (srcs[k] >= 0) {
+        if (live && srcs[k] >= 0) {
             cbuf[k] = load_stream(cq + (long long)srcs[k] * NU + u);
             sbuf[k] = load_stream8(sq + (long long)srcs[k] * NU + u);
         }
@@ -309,25 +310,43 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void combine_int8_wide_kern
         lo[c] = 0.0f;
         hi[c] = 0.0f;
     }
+    if (live) {
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-        if (srcs[k] >= 0) {
-            accumulate8_int8(make_uint2(cbuf[k].x, cbuf[k].y), __uint_as_float(sbuf[k].x),
-                             ws[k], lo);
-            accumulate8_int8(make_uint2(cbuf[k].z, cbuf[k].w), __uint_as_float(sbuf[k].y),
-                             ws[k], hi);
-        } else if (srcs[k] == kCopy) {
-            accumulate8<F16>(self[2 * u], ws[k], lo);
-            accumulate8<F16>(self[2 * u + 1], ws[k], hi);
+        for (int k = 0; k < KMAX; ++k) {
+            if (srcs[k] >= 0) {
+                accumulate8_int8(make_uint2(cbuf[k].x, cbuf[k].y), __uint_as_float(sbuf[k].x),
+                                 ws[k], lo);
+                accumulate8_int8(make_uint2(cbuf[k].z, cbuf[k].w), __uint_as_float(sbuf[k].y),
+                                 ws[k], hi);
+            } else if (srcs[k] == kCopy) {
+                accumulate8<F16>(self[2 * u], ws[k], lo);
+                accumulate8<F16>(self[2 * u + 1], ws[k], hi);
+            }
         }
     }
+    // Lane l holds output vectors 2u and 2u + 1 (u = u0 + l).  Stored as they are, each store
+    // instruction would cover every other 16 bytes of the wave's 2 KiB; instead lane j
+    // writes vector 2u0 + j, then 2u0 + 64 + j, taken from lane j / 2 (resp. 32 + j / 2) --
+    // its first vector when j is even, its second when j is odd -- so each store instruction
+    // covers 1 KiB contiguously.
+    const uint4 va = make_uint4(pack_tok2<F16>(lo[0], lo[1]), pack_tok2<F16>(lo[2], lo[3]),
+                                pack_tok2<F16>(lo[4], lo[5]), pack_tok2<F16>(lo[6], lo[7]));
+    const uint4 vb = make_uint4(pack_tok2<F16>(hi[0], hi[1]), pack_tok2<F16>(hi[2], hi[3]),
+                                pack_tok2<F16>(hi[4], hi[5]), pack_tok2<F16>(hi[6], hi[7]));
+    const bool odd = (lane & 1) != 0;
+    const int v0 = 2 * (u - lane);                         // the wave's first output vector
     uint4* yr = reinterpret_cast<uint4*>(y) + tok * NV;
-    store_stream(yr + 2 * u,
-                 make_uint4(pack_tok2<F16>(lo[0], lo[1]), pack_tok2<F16>(lo[2], lo[3]),
-                            pack_tok2<F16>(lo[4], lo[5]), pack_tok2<F16>(lo[6], lo[7])));
-    store_stream(yr + 2 * u + 1,
-                 make_uint4(pack_tok2<F16>(hi[0], hi[1]), pack_tok2<F16>(hi[2], hi[3]),
-                            pack_tok2<F16>(hi[4], hi[5]), pack_tok2<F16>(hi[6], hi[7])));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int from = h * (kWave / 2) + (lane >> 1);
+        const uint32_t ax = __shfl(va.x, from, kWave), bx = __shfl(vb.x, from, kWave);
+        const uint32_t ay = __shfl(va.y, from, kWave), by = __shfl(vb.y, from, kWave);
+        const uint32_t az = __shfl(va.z, from, kWave), bz = __shfl(vb.z, from, kWave);
+        const uint32_t aw = __shfl(va.w, from, kWave), bw = __shfl(vb.w, from, kWave);
+        const int v = v0 + h * kWave + lane;
+        if (v < NV)
+            store_stream(yr + v, odd ? make_uint4(bx, by, bz, bw) : make_uint4(ax, ay, az, aw));
+    }
 }
 
 template <int KMAX>

@@ -121,6 +121,18 @@ __device__ __forceinline__ uint32_t absmax8(const float (&f)[8], uint32_t amax)
     return amax;
 }
 
+// absmax8 for values that are products of a multiplication (canonical floats, never NaN for
+// finite inputs): a float maximum of absolute values, which the compiler forms from max3
+// instructions with absolute-value operand modifiers; for non-negative non-NaN floats the
+// float order is the order of the bit patterns, so the result is absmax8's.
+__device__ __forceinline__ uint32_t absmax8_products(const float (&f)[8], uint32_t amax)
+{
+    float m = __uint_as_float(amax);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) m = __builtin_fmaxf(m, __builtin_fabsf(f[c]));
+    return __float_as_uint(m);
+}
+
 __device__ __forceinline__ uint2 pack_codes8(const uint32_t (&c)[8])
 {
     return make_uint2((c[0] & 0xFF) | ((c[1] & 0xFF) << 8) | ((c[2] & 0xFF) << 16) | (c[3] << 24),
@@ -618,7 +630,7 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
 #pragma unroll
                 for (int q = 0; q < 8; ++q) f[n][q] = 0.0f;
             }
-            if (MODE == 2) amax = absmax8(f[n], amax);
+            if (MODE == 2) amax = absmax8_products(f[n], amax);
         }
         float dyn = 0.0f;
         if (MODE == 2) {
@@ -641,7 +653,7 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
             } else if (MODE == 2) {
                 packed = dynamic_codes8<CT>(f[n], dyn);
             } else {
-                const uint32_t gmax = group_max_u32<kGroup / 8>(absmax8(f[n], 0u));
+                const uint32_t gmax = group_max_u32<kGroup / 8>(absmax8_products(f[n], 0u));
                 const float gdyn = type_max<CT>() / __uint_as_float(gmax);
                 packed = dynamic_codes8<CT>(f[n], gdyn);
                 gscale = 1.0f / gdyn;
@@ -658,6 +670,129 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
             sm_cur[n][1] = sm_nxt[n][1];
         }
         pk = nxt;
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// per-expert scales: one workgroup of two waves per pick
+// ---------------------------------------------------------------------------------------
+//
+// With an [E][H] scales table each pick is quantized on its own expert's row, so a token's
+// K picks share nothing but the token row.  Each pick gets a workgroup of two waves, each
+// holding half of the row (and the same half of the expert's scales row) in registers: the
+// products x * scales, their maximum (mode 2: the two waves' maxima meet in LDS, one
+// barrier; mode 3: a 128-group is 16 adjacent lanes), the codes and the stores, with every
+// load of the pick in flight at once.  A token's K picks thus run side by side instead of
+// one after another.  Placement: workgroups are dealt to the eight XCDs in turn (workgroup
+// b to XCD b mod 8), so pick k of token t runs in workgroup (t / 8) * 8K + 8k + t mod 8 --
+// all K picks of a token on one XCD, one after another in its order -- and the token row,
+// read from HBM by the first, is an L2 hit for the others (these loads keep the default
+// cache policy).
+
+// Used up to kPickKernelMaxPicks picks.  Measured on MI355X: W=8, BS=128, K=8, H=7168
+// (8,192 picks) dispatch 41.3 us against 46.7 us with the token workgroups below; at W=16,
+// BS=512 (65,536 picks) 276 us against 265 us: there each pick's workgroup reads the token row
+// and its scales row with little else to overlap, while a token workgroup streams its K picks
+// behind a single read of the row.
+constexpr long long kPickKernelMaxPicks = 16384;
+
+// WAVES waves of SLOTS 64-vector slots each per pick (WAVES * SLOTS * 64 * 8 >= H)
+template <int MODE, int CT, int WAVES, int SLOTS>
+__global__ __launch_bounds__(kWave * WAVES) void scatter_pick_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
+    const int32_t* __restrict__ expand_idx, const int32_t* __restrict__ seg,
+    const float* __restrict__ scales, const float* __restrict__ weights,
+    void* __restrict__ expand_x, void* __restrict__ dyn_scales, int32_t* __restrict__ assist,
+    float* __restrict__ expand_scales, int W, int E, int BS, int H, int K, int ns,
+    long long cap, long long T, int tok_f16)
+{
+    __shared__ uint32_t red[WAVES];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const long long grp = (long long)blockIdx.x / (8LL * K);
+    const int rem = (int)((long long)blockIdx.x - grp * 8 * K);
+    const int k = rem >> 3;
+    const long long tok = grp * 8 + (rem & 7);
+    if (tok >= T) return;                                  // whole workgroup
+    const long long p = tok * K + k;
+    const int32_t e = ids[p];
+    const int32_t ord = expand_idx[p];
+    if (ord < 0 || e < 0 || e >= E) return;                // not routed: whole workgroup
+    const int s = (int)(tok / BS);
+    const long long row = (long long)seg[(long long)e * W + s] + ord;
+    if (row >= cap) return;
+
+    // this wave's vectors: [base, end) with base a multiple of 64 vectors, so a lane's
+    // vectors are base + lane + 64 n and every 128-group is 16 adjacent lanes
+    const int NV = H >> 3;
+    const int share = ((NV + WAVES - 1) / WAVES + kWave - 1) / kWave * kWave;
+    const int base = wave * share;
+    const int end = base + share < NV ? base + share : NV;
+    const uint4* xr = reinterpret_cast<const uint4*>(x) + tok * NV;
+    const float4* sm = reinterpret_cast<const float4*>(scales + (long long)e * H);
+    uint4 raw[SLOTS];
+    float4 sa[SLOTS], sb[SLOTS];
+#pragma unroll
+    for (int n = 0; n < SLOTS; ++n) {
+        const int v = base + lane + n * kWave;
+        if (v < end) {
+            raw[n] = xr[v];
+            sa[n] = sm[2 * v];
+            sb[n] = sm[2 * v + 1];
+        }
+    }
+    if (threadIdx.x == 0) {
+        const int i = (int)(tok - (long long)s * BS);
+        assist[row * 3 + 0] = s;
+        assist[row * 3 + 1] = i;
+        assist[row * 3 + 2] = k;
+        if (expand_scales) expand_scales[row] = weights[p];
+    }
+    float f[SLOTS][8];
+    uint32_t amax = 0;
+#pragma unroll
+    for (int n = 0; n < SLOTS; ++n) {
+        const int v = base + lane + n * kWave;
+        if (v < end) {
+            unpack8(raw[n], f[n], tok_f16 != 0);
+            mul8(f[n], sa[n], sb[n]);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) f[n][q] = 0.0f;
+        }
+        if (MODE == 2) amax = absmax8_products(f[n], amax);
+    }
+    float dyn = 0.0f;
+    if (MODE == 2) {
+        amax = wave_max_u32(amax);
+        if (lane == 0) red[wave] = amax;
+        __syncthreads();
+        amax = 0;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) amax = amax > red[w] ? amax : red[w];
+        dyn = type_max<CT>() / __uint_as_float(amax);
+        if (threadIdx.x == 0) static_cast<float*>(dyn_scales)[row] = 1.0f / dyn;
+    }
+    uint2* out = reinterpret_cast<uint2*>(expand_x) + row * NV;
+    float* fscales = static_cast<float*>(dyn_scales);
+#pragma unroll
+    for (int n = 0; n < SLOTS; ++n) {
+        const int v = base + lane + n * kWave;
+        uint2 packed;
+        float gscale = 0.0f;
+        if (MODE == 1) {
+            packed = static_codes8(f[n]);
+        } else if (MODE == 2) {
+            packed = dynamic_codes8<CT>(f[n], dyn);
+        } else {
+            const uint32_t gmax = group_max_u32<kGroup / 8>(absmax8_products(f[n], 0u));
+            const float gdyn = type_max<CT>() / __uint_as_float(gmax);
+            packed = dynamic_codes8<CT>(f[n], gdyn);
+            gscale = 1.0f / gdyn;
+        }
+        if (v >= end) continue;
+        store_stream(out + v, packed);
+        if (MODE == 3 && (v & (kGroup / 8 - 1)) == 0) fscales[row * ns + (v >> 4)] = gscale;
     }
 }
 
@@ -680,6 +815,22 @@ template <int MODE, int CT, int SK>
 hipError_t launch_tile_variant(const Shape& sh, const ScatterArgs& a, hipStream_t stream)
 {
     const long long T = (long long)sh.W * sh.BS;
+    if constexpr (SK == kScalesPerExpert) {
+        if (!a.fused && T * sh.K <= kPickKernelMaxPicks) {
+            // one workgroup per pick, the K picks of a token on one XCD
+            const long long blocks = (T + 7) / 8 * 8 * sh.K;
+#define MOE_DC_PICK(WV, SL)                                                                    \
+    hipLaunchKernelGGL((scatter_pick_kernel<MODE, CT, WV, SL>), dim3((unsigned)blocks),         \
+                       dim3(kWave * WV), 0, stream, static_cast<const uint16_t*>(a.x), a.ids,   \
+                       a.expand_idx, a.seg, a.scales, a.weights, a.expand_x, a.dyn_scales,     \
+                       a.assist, a.expand_scales, sh.W, sh.E, sh.BS, sh.H, sh.K,               \
+                       sh.scales_per_row, (long long)sh.cap, T, sh.tok_f16)
+            if (sh.H <= 2 * 7 * kWave * 8) MOE_DC_PICK(2, 7);
+            else MOE_DC_PICK(2, 8);
+#undef MOE_DC_PICK
+            return hipGetLastError();
+        }
+    }
     const int slots = ((sh.H >> 3) + kWave - 1) / kWave;
     int waves = (slots + kTileSlots - 1) / kTileSlots;              // <= kMaxTileWaves
     size_t lds = 0;
