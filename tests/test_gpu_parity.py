@@ -55,6 +55,16 @@ SMALL = {
     "bs1_h8192": workloads.Workload("bs1_h8192", W=2, E=2, BS=1, H=8192, K=2, quant_mode=2),
     "w768_e768": workloads.Workload("w768_e768", W=768, E=768, BS=1, H=1024, K=2,
                                     quant_mode=2),
+    # per-expert scales with the separate routing (flags 1): one workgroup per pick, a token
+    # count that is not a multiple of 8 (the XCD placement groups tokens by 8), K = 16, a ragged
+    # row (the second wave holds one vector) and the widest row (eight slots per wave)
+    "pick_group_k16_ragged": workloads.Workload("pick_group_k16_ragged", W=3, E=48, BS=37,
+                                                H=1032, K=16, quant_mode=3, scales_kind=3),
+    "pick_static_h8192": workloads.Workload("pick_static_h8192", W=2, E=8, BS=9, H=8192, K=4,
+                                            quant_mode=1, scales_kind=3),
+    "pick_token_e5m2_w8": workloads.Workload("pick_token_e5m2_w8", W=8, E=64, BS=65, H=7168,
+                                             K=8, quant_mode=2, out_dtype=3, scales_kind=3,
+                                             mask_kind=2, inactive_tokens_per_rank=5),
     # more (expert, source) counts than one LDS pass of the scan holds: chunked scan, with a
     # short last chunk (24,192 counts) and with whole chunks (65,536 counts)
     "scan_chunks_w24_e1008": workloads.Workload("scan_chunks_w24_e1008", W=24, E=1008, BS=8,
