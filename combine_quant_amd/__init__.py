@@ -8,8 +8,8 @@ from .binding import (  # noqa: F401
     EXPORTS, MOE_DC_FLAG_CHECK_IDS, MOE_DC_FLAG_SEPARATE_ROUTE, MOE_DTYPE_DEFAULT,
     MOE_DTYPE_E2M1, MOE_DTYPE_E4M3, MOE_DTYPE_E5M2, MOE_DTYPE_INT8, MOE_ERR_DEVICE,
     MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_OK, MOE_SCALE_E8M0,
-    MOE_SCALE_FP32, MOE_SCALES_NONE, MOE_SCALES_PER_EXPERT, MOE_SCALES_SCALAR,
-    MOE_SCALES_SHARED, MOE_TOKEN_BF16, MOE_TOKEN_F16, Launch, MoeDcConfig, MoeDcError,
+    MOE_SCALE_FP32, MOE_SCALE_FP32_RECIPROCAL, MOE_SCALES_NONE, MOE_SCALES_PER_EXPERT,
+    MOE_SCALES_SCALAR, MOE_SCALES_SHARED, MOE_TOKEN_BF16, MOE_TOKEN_F16, Launch, MoeDcConfig, MoeDcError,
     alloc_dispatch_outputs, token_torch_dtype,
     code_row_elems, code_type, combine, combine_block_count, combine_int8, combine_quantize,
     combine_scatter, dispatch, load_library, make_config, moe_combine, moe_combine_int8,

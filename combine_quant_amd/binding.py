@@ -18,7 +18,7 @@ from .build import LIB
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = 0, -1, -2, -3, -4
 MOE_DTYPE_DEFAULT, MOE_DTYPE_INT8, MOE_DTYPE_E4M3, MOE_DTYPE_E5M2, MOE_DTYPE_E2M1 = 0, 1, 2, 3, 4
 MOE_SCALES_NONE, MOE_SCALES_SCALAR, MOE_SCALES_SHARED, MOE_SCALES_PER_EXPERT = 0, 1, 2, 3
-MOE_SCALE_FP32, MOE_SCALE_E8M0 = 0, 1
+MOE_SCALE_FP32, MOE_SCALE_E8M0, MOE_SCALE_FP32_RECIPROCAL = 0, 1, 2
 MOE_DC_FLAG_SEPARATE_ROUTE, MOE_DC_FLAG_CHECK_IDS = 1, 2
 MOE_TOKEN_BF16, MOE_TOKEN_F16 = 0, 1
 _STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",

@@ -110,7 +110,8 @@ moe_status check(const moe_dc_config* c, moe_dc::Shape* out)
     if (c->quant_mode == 1 && c->scales_kind == MOE_SCALES_NONE)
         return fail(MOE_ERR_INVALID_ARG, "quant_mode 1 needs a scales tensor");
     if (c->scale_format != MOE_SCALE_FP32 &&
-        !(c->scale_format == MOE_SCALE_E8M0 && c->quant_mode >= 4))
+        !((c->scale_format == MOE_SCALE_E8M0 || c->scale_format == MOE_SCALE_FP32_RECIPROCAL) &&
+          c->quant_mode >= 4))
         return fail(MOE_ERR_INVALID_ARG, "scale_format %d is not allowed with quant_mode %d",
                     c->scale_format, c->quant_mode);
     if (c->expert_token_nums_type != 0 && c->expert_token_nums_type != 1)
@@ -133,7 +134,7 @@ moe_status check(const moe_dc_config* c, moe_dc::Shape* out)
         out->quant_mode = c->quant_mode;
         out->code_type = code_type;
         out->scales_kind = c->scales_kind;
-        out->scale_e8m0 = c->scale_format == MOE_SCALE_E8M0 ? 1 : 0;
+        out->scale_format = c->scale_format;
         out->zero_end = c->moe_expert_num + c->zero_expert_num;
         out->id_end = out->zero_end + c->copy_expert_num;
         out->etn_type = c->expert_token_nums_type;

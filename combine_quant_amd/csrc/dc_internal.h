@@ -41,7 +41,7 @@ struct Shape {
     int32_t quant_mode;
     int32_t code_type;       // CodeType of expand_x
     int32_t scales_kind;     // ScalesKind of the scales tensor
-    int32_t scale_e8m0;      // 1: MX scales stored as E8M0 bytes, 0: fp32
+    int32_t scale_format;    // MX scales: 0 fp32 2^se, 1 E8M0 bytes, 2 fp32 2^-se
     int32_t zero_end;        // E + zero_expert_num
     int32_t id_end;          // E + zero_expert_num + copy_expert_num
     int32_t etn_type;

@@ -351,7 +351,7 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
     const float* __restrict__ scales, const float* __restrict__ weights,
     void* __restrict__ expand_x, void* __restrict__ dyn_scales, int32_t* __restrict__ assist,
     float* __restrict__ expand_scales, int W, int E, int BS, int H, int K, int ns,
-    long long cap, int e8m0, FusedRoute fr, int L, int mask_kind, int etn_type, int tok_f16)
+    long long cap, int sfmt, FusedRoute fr, int L, int mask_kind, int etn_type, int tok_f16)
 {
     __shared__ int32_t rows_lds[kMaxK];
     __shared__ int32_t exps_lds[kMaxK];
@@ -528,7 +528,7 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
                 } else {
                     packed = pack_codes8(c);
                 }
-                scale = pow2f(se);
+                scale = sfmt == 2 ? inv : pow2f(se);      // 1 / 2^se, or 2^se
             }
             if (v >= NV) continue;
 #pragma unroll
@@ -545,7 +545,7 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
                 if (MODE == 3 && (v & (kGroup / 8 - 1)) == 0)
                     fscales[(long long)rows[k] * ns + (v >> 4)] = scale;
                 if (MODE >= 4 && (v & 3) == 0) {
-                    if (e8m0)
+                    if (sfmt == 1)
                         static_cast<uint8_t*>(dyn_scales)[(long long)rows[k] * ns + (v >> 2)] =
                             (uint8_t)(se + 127);
                     else
@@ -583,7 +583,7 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
 #pragma unroll
                 for (int k = 0; k < kMaxK; ++k) {
                     if (rows[k] < 0) continue;
-                    if (e8m0) static_cast<uint8_t*>(dyn_scales)[(long long)rows[k] * ns + nb] = 0;
+                    if (sfmt == 1) static_cast<uint8_t*>(dyn_scales)[(long long)rows[k] * ns + nb] = 0;
                     else fscales[(long long)rows[k] * ns + nb] = 0.0f;
                 }
             }
@@ -845,7 +845,7 @@ hipError_t launch_tile_variant(const Shape& sh, const ScatterArgs& a, hipStream_
                        dim3(kWave * waves), lds, stream, static_cast<const uint16_t*>(a.x),     \
                        a.ids, a.expand_idx, a.seg, a.scales, a.weights, a.expand_x,            \
                        a.dyn_scales, a.assist, a.expand_scales, sh.W, sh.E, sh.BS, sh.H, sh.K, \
-                       sh.scales_per_row, (long long)sh.cap, sh.scale_e8m0, fr, sh.L,         \
+                       sh.scales_per_row, (long long)sh.cap, sh.scale_format, fr, sh.L,         \
                        sh.mask_kind, sh.etn_type, sh.tok_f16)
     if (a.fused) MOE_DC_TILE_LAUNCH(true);
     else MOE_DC_TILE_LAUNCH(false);
@@ -937,7 +937,7 @@ __global__ __launch_bounds__(kElemThreads) void scatter_elem_kernel(
     const float* __restrict__ scales, const float* __restrict__ weights,
     void* __restrict__ expand_x, void* __restrict__ dyn_scales, int32_t* __restrict__ assist,
     float* __restrict__ expand_scales, int W, int E, int BS, int H, int K, int ns,
-    long long cap, int mode, int ct, int sk, int e8m0, int tok_f16)
+    long long cap, int mode, int ct, int sk, int sfmt, int tok_f16)
 {
     __shared__ long long row_of[kMaxK];
     __shared__ int32_t exp_of[kMaxK];
@@ -1068,7 +1068,7 @@ __global__ __launch_bounds__(kElemThreads) void scatter_elem_kernel(
                                          : mx_shared_exp<5, kCodeE2m1>(bm));
                 const float inv = __uint_as_float((uint32_t)(127 - se) << 23);   // 2^-se
                 code = fp8_code_rt(ct, f[n] * inv);
-                scale = pow2f(se);
+                scale = sfmt == 2 ? inv : pow2f(se);
                 sbyte = (uint32_t)(se + 127);
                 lead = (h % kMxBlock) == 0;
                 sidx = h / kMxBlock;
@@ -1084,7 +1084,7 @@ __global__ __launch_bounds__(kElemThreads) void scatter_elem_kernel(
                 if (!fp4) out[row * H + h] = (uint8_t)code;
                 else if ((h & 1) == 0) out[row * (H / 2) + h / 2] = (uint8_t)(code | (next << 4));
                 if (lead) {
-                    if (e8m0) bscales[row * ns + sidx] = (uint8_t)sbyte;
+                    if (sfmt == 1) bscales[row * ns + sidx] = (uint8_t)sbyte;
                     else fscales[row * ns + sidx] = scale;
                 }
             }
@@ -1096,7 +1096,7 @@ __global__ __launch_bounds__(kElemThreads) void scatter_elem_kernel(
                 if (row < 0) continue;
                 if (mode == 2) fscales[row] = 1.0f / dyn_tok;
                 if (mode >= 4 && ns > nb) {
-                    if (e8m0) bscales[row * ns + nb] = 0;
+                    if (sfmt == 1) bscales[row * ns + nb] = 0;
                     else fscales[row * ns + nb] = 0.0f;
                 }
             }
@@ -1115,7 +1115,7 @@ hipError_t launch_elem(const Shape& sh, const ScatterArgs& a, hipStream_t stream
                        static_cast<const uint16_t*>(a.x), a.ids, a.expand_idx, a.seg, a.scales,
                        a.weights, a.expand_x, a.dyn_scales, a.assist, a.expand_scales, sh.W,
                        sh.E, sh.BS, sh.H, sh.K, sh.scales_per_row, (long long)sh.cap,
-                       sh.quant_mode, sh.code_type, sh.scales_kind, sh.scale_e8m0, sh.tok_f16);
+                       sh.quant_mode, sh.code_type, sh.scales_kind, sh.scale_format, sh.tok_f16);
     return hipGetLastError();
 }
 

@@ -78,8 +78,11 @@ typedef enum {
 /* Storage of the MX block scales (modes 4/5). */
 typedef enum {
     MOE_SCALE_FP32 = 0,         /* fp32 2^shared_exp                                        */
-    MOE_SCALE_E8M0 = 1          /* one byte shared_exp + 127 ([SMP] 通信前量化 stores the MX
+    MOE_SCALE_E8M0 = 1,         /* one byte shared_exp + 127 ([SMP] 通信前量化 stores the MX
                                    scale as an E8M0 value)                                  */
+    MOE_SCALE_FP32_RECIPROCAL = 2 /* fp32 2^-shared_exp, exact: the value that the [LLD]
+                                   计算公式 of modes 4/5 writes out, 1.0 divided by the
+                                   block's 2^shared_exp; the pad entry 0                     */
 } moe_scale_format;
 
 /* Element type of the tokens: x, ori_x, shared_x, expert_out, y and the mode-0 rows of
@@ -125,7 +128,8 @@ typedef struct {
                                        E5M2; modes 4/5 DEFAULT/E4M3/E5M2/E2M1                */
     int32_t scales_kind;            /* moe_scales_kind: mode 1 SCALAR/SHARED/PER_EXPERT;
                                        modes 2, 3 any; modes 0, 4, 5 NONE                     */
-    int32_t scale_format;           /* moe_scale_format: E8M0 only with modes 4/5            */
+    int32_t scale_format;           /* moe_scale_format: E8M0 and FP32_RECIPROCAL only with
+                                       modes 4/5                                              */
     int32_t flags;                  /* moe_dc_flag bits; 0 for the defaults                   */
     int32_t token_dtype;            /* moe_token_dtype of x, ori_x, shared_x, expert_out, y
                                        and mode-0 expand_x: BF16 (0, the default) or F16      */
@@ -188,7 +192,8 @@ size_t moe_dc_dispatch_workspace_bytes(const moe_dc_config* cfg);
  *                  else [cap][H] bytes: int8 or fp8 codes
  *   dynamic_scales [cap][moe_dc_scales_per_row(cfg)] fp32 (or bytes with MOE_SCALE_E8M0):
  *                  mode 2 one 1/dyn per row; mode 3 one 1/dyn per group; modes 4/5 one scale
- *                  per 32-element block and 0 in the Align2 pad slot.  NULL allowed for
+ *                  per 32-element block (2^shared_exp, its E8M0 byte, or 2^-shared_exp, as
+ *                  scale_format says) and 0 in the Align2 pad slot.  NULL allowed for
  *                  modes 0 and 1, which have no scales
  *   expand_idx     int32 [W][BS][K]   ordinal of each pick among its source rank's picks of
  *                  the same expert; -1 for inactive picks and special experts

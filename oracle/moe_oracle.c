@@ -614,7 +614,9 @@ int64_t oracle_dest_row(const oracle_cfg* c, const int32_t* ep_recv_count,
  *   quantization is per pair.
  *   expand_x [cap][row bytes] (bf16 patterns for mode 0; E2M1 two codes per byte; else bytes);
  *   dynamic_scales [cap][scale count] fp32, or bytes when scale_format is 1: each MX scale
- *   2^e as its E8M0 byte e + 127 ([SMP] 通信前量化), pad bytes 0 (reading R24);
+ *   2^e as its E8M0 byte e + 127 ([SMP] 通信前量化), pad bytes 0 (reading R24); with
+ *   scale_format 2 each MX scale is the formula's literal transmitted value 1.0 / 2^e (one fp32
+ *   division, exact for a power of two), pad 0;
  *   assist_info [cap][3].
  * Returns -2 for a mode / code type / scales kind / scale format that do not go together,
  * -3 when the scales pointer disagrees with scales_kind, -1 for an out-of-range id. */
@@ -630,7 +632,8 @@ int32_t oracle_dispatch(const oracle_cfg* c, const uint16_t* x, const int32_t* e
     if (c->scales_kind < 0 || c->scales_kind > 3) return -2;
     if ((mode == 0 || mode >= 4) && c->scales_kind != 0) return -2;
     if (mode == 1 && c->scales_kind == 0) return -2;
-    if (c->scale_format != 0 && !(c->scale_format == 1 && mode >= 4)) return -2;
+    if (c->scale_format != 0 && !((c->scale_format == 1 || c->scale_format == 2) && mode >= 4))
+        return -2;
     if ((c->scales_kind != 0) != (scales_or_null != NULL)) return -3;
     if (oracle_route(c, expert_ids, mask, cnt_scratch, expand_idx) != 0) return -1;
     oracle_recv_counts(c, cnt_scratch, ep_recv_count, expert_token_nums, recv_offsets);
@@ -662,6 +665,9 @@ int32_t oracle_dispatch(const oracle_cfg* c, const uint16_t* x, const int32_t* e
                         if (c->scale_format == 1)
                             ((uint8_t*)dynamic_scales)[(size_t)row * ns + b] =
                                 b < nb ? oracle_e8m0_from_scale(rowsc[b]) : 0;
+                        else if (c->scale_format == 2)   /* [LLD] 计算公式: 1.0 / dynamic_scales_value */
+                            ((float*)dynamic_scales)[(size_t)row * ns + b] =
+                                b < nb ? 1.0f / rowsc[b] : 0.0f;
                         else
                             ((float*)dynamic_scales)[(size_t)row * ns + b] = rowsc[b];
                     }

@@ -41,7 +41,8 @@ typedef struct {
     int32_t mask_kind;              /* 0 none, 1 per token [W][BS], 2 per pair [W][BS][K] */
     int32_t out_dtype;              /* 0 the mode's default, else one of ORACLE_CODE_*     */
     int32_t scales_kind;            /* 0 none, 1 scalar (1,), 2 shared (H,), 3 per expert  */
-    int32_t scale_format;           /* 0 fp32 scales, 1 E8M0 bytes (modes 4/5 only)        */
+    int32_t scale_format;           /* 0 fp32 scales, 1 E8M0 bytes, 2 fp32 1/scale
+                                       (1 and 2: modes 4/5 only)                             */
     int32_t token_dtype;            /* token elements (x, ori_x, expert outputs, y): 0 bf16,
                                        1 IEEE binary16                                      */
 } oracle_cfg;

@@ -48,7 +48,7 @@ def test_header_enum_values_match_the_binding():
     for name in ("MOE_DTYPE_DEFAULT", "MOE_DTYPE_INT8", "MOE_DTYPE_E4M3", "MOE_DTYPE_E5M2",
                  "MOE_DTYPE_E2M1",
                  "MOE_SCALES_NONE", "MOE_SCALES_SCALAR", "MOE_SCALES_SHARED",
-                 "MOE_SCALES_PER_EXPERT", "MOE_SCALE_FP32", "MOE_SCALE_E8M0",
+                 "MOE_SCALES_PER_EXPERT", "MOE_SCALE_FP32", "MOE_SCALE_E8M0", "MOE_SCALE_FP32_RECIPROCAL",
                  "MOE_DC_FLAG_SEPARATE_ROUTE", "MOE_DC_FLAG_CHECK_IDS", "MOE_TOKEN_BF16",
                  "MOE_TOKEN_F16"):
         m = re.search(r"\b" + name + r"\s*=\s*(\d+)", text)
@@ -105,7 +105,8 @@ def test_valid_configs_of_the_workloads():
     (dict(quant_mode=0, scales_kind=1), cq.MOE_ERR_INVALID_ARG),
     (dict(quant_mode=2, scales_kind=4), cq.MOE_ERR_INVALID_ARG),
     (dict(quant_mode=2, scale_format=1), cq.MOE_ERR_INVALID_ARG),
-    (dict(quant_mode=5, scale_format=2), cq.MOE_ERR_INVALID_ARG),
+    (dict(quant_mode=5, scale_format=3), cq.MOE_ERR_INVALID_ARG),
+    (dict(quant_mode=3, scale_format=2), cq.MOE_ERR_INVALID_ARG),   # reciprocal: MX only
     (dict(const_expert_num=1), cq.MOE_ERR_UNSUPPORTED),
     (dict(zero_expert_num=-1), cq.MOE_ERR_INVALID_ARG),
     (dict(zero_expert_num=2 ** 31 - 100), cq.MOE_ERR_INVALID_ARG),   # id space >= INT32_MAX
@@ -156,6 +157,7 @@ def test_k_may_count_special_experts():
     dict(quant_mode=3), dict(quant_mode=3, out_dtype=3, scales_kind=3),
     dict(quant_mode=4, out_dtype=3, scale_format=1), dict(quant_mode=5, scale_format=1),
     dict(quant_mode=4, out_dtype=4), dict(quant_mode=5, out_dtype=4, scale_format=1, H=1030),
+    dict(quant_mode=4, scale_format=2), dict(quant_mode=5, out_dtype=4, scale_format=2),
 ])
 def test_quant_variants_validate(kw):
     assert cq.moe_dc_validate(_cfg(**kw)) == cq.MOE_OK, cq.moe_dc_last_error()

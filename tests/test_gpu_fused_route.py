@@ -41,6 +41,8 @@ CASES = {
                             scales_kind=2),
     "mx_e2m1_fp32_ragged": WL("mx_e2m1_fp32_ragged", W=4, E=16, BS=32, H=2064, K=4,
                               quant_mode=4, out_dtype=4),
+    "mxclip_e4m3_recip": WL("mxclip_e4m3_recip", W=8, E=32, BS=8, H=7200, K=8, quant_mode=5,
+                            scale_format=2, mask_kind=1, inactive_tokens_per_rank=2),
 }
 # just past the limits: the separate kernels run whatever the flag says
 PAST_LIMIT = {

@@ -1,6 +1,6 @@
 """GPU parity of the further quantization variants: static int8 (mode 1), per-token fp8
 (mode 2 with E4M3/E5M2 codes), per-128-group fp8 (mode 3), MX with E5M2 elements and E8M0
-scale bytes, each with every shape of the scales tensor it allows.  Dispatch outputs are
+scale bytes or reciprocal fp32 scales, each with every shape of the scales tensor it allows.  Dispatch outputs are
 compared with the CPU oracle bit for bit; combine within 1e-2 relative / 1e-3 absolute.
 Cases span several workgroups, ragged tails (H not a multiple of 128 or 32; H = 1030 takes
 the element-wise kernel), masks, special experts and duplicate picks."""
@@ -82,6 +82,16 @@ VARIANTS = {
                         out_dtype=4),
     "mxclip_e2m1_h1030": WL("mxclip_e2m1_h1030", W=2, E=8, BS=33, H=1030, K=3,
                             quant_mode=5, out_dtype=4, scale_format=1),
+    # MX with reciprocal fp32 scales (2^-shared_exp): tile kernel with a pad slot, special
+    # experts and per-pick masks, and the element-wise kernel
+    "mx_e4m3_recip": WL("mx_e4m3_recip", W=4, E=32, BS=60, H=1056, K=6, quant_mode=4,
+                        scale_format=2),
+    "mxclip_e2m1_recip_special": WL("mxclip_e2m1_recip_special", W=4, E=64, BS=70, H=2048,
+                                    K=16, quant_mode=5, out_dtype=4, scale_format=2,
+                                    zero_expert_num=2, copy_expert_num=2, mask_kind=2,
+                                    inactive_tokens_per_rank=7),
+    "mxclip_e5m2_recip_h1030": WL("mxclip_e5m2_recip_h1030", W=2, E=8, BS=33, H=1030, K=3,
+                                  quant_mode=5, out_dtype=3, scale_format=2),
 }
 
 
@@ -181,3 +191,22 @@ def test_e8m0_bytes_are_the_fp32_exponents():
     assert (s8[:, nb:] == 0).all()
     assert torch.equal(a["expand_x"][:P], b["expand_x"][:P])
     assert oracle.e8m0_from_scale(2.0 ** -127) == 0
+
+
+@pytest.mark.parametrize("name", ["mx_e4m3_recip", "mxclip_e5m2_recip_h1030"])
+def test_reciprocal_scales_invert_the_fp32_scales(name):
+    """Same input under fp32 2^shared_exp and reciprocal scale storage: the codes are the
+    same, each product of the two scales is exactly 1 (2^-127 * 2^127 included), pads 0."""
+    import torch
+    wl = VARIANTS[name]
+    inp = workloads.generate(wl, seed=3)
+    _, _, a = harness.gpu_dispatch(wl.replace(scale_format=0), inp)
+    _, _, b = harness.gpu_dispatch(wl, inp)
+    torch.cuda.synchronize()
+    P = int(a["recv_offsets"][-1].item())
+    nb = (wl.H + 31) // 32
+    sa = harness.host(a["dynamic_scales"])[:P].astype(np.float64)
+    sb = harness.host(b["dynamic_scales"])[:P].astype(np.float64)
+    assert (sa[:, :nb] * sb[:, :nb] == 1.0).all()
+    assert (sb[:, nb:] == 0).all()
+    assert torch.equal(a["expand_x"][:P], b["expand_x"][:P])

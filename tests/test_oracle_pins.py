@@ -541,7 +541,8 @@ def test_combine_roundtrip_int8():
 VARIANTS = [  # (quant_mode, out_dtype, scales_kind, scale_format)
     (0, 0, 0, 0), (1, 0, 1, 0), (1, 1, 2, 0), (1, 0, 3, 0), (2, 0, 0, 0), (2, 0, 3, 0),
     (2, 2, 2, 0), (2, 3, 1, 0), (3, 0, 0, 0), (3, 3, 3, 0), (4, 0, 0, 0), (4, 3, 0, 1),
-    (5, 0, 0, 0), (5, 2, 0, 1), (5, 3, 0, 0), (4, 4, 0, 0), (5, 4, 0, 1)]
+    (5, 0, 0, 0), (5, 2, 0, 1), (5, 3, 0, 0), (4, 4, 0, 0), (5, 4, 0, 1), (4, 0, 0, 2),
+    (5, 4, 0, 2)]
 
 
 @pytest.mark.parametrize("variant", VARIANTS, ids=lambda v: "m%d_t%d_s%d_f%d" % v)
@@ -575,12 +576,20 @@ def test_dispatch_payload_placement(variant):
             nb = (wl.H + 31) // 32
             want = [oracle.e8m0_from_scale(v) for v in sc[:nb]] + [0] * (len(sc) - nb)
             assert d["dynamic_scales"][row].tolist() == want
+        elif fmt == 2:
+            # the formula's literal transmitted value, 1.0 / dynamic_scales_value ([LLD]
+            # 计算公式, modes 4/5), of a power of two: exact in binary64 and in binary32
+            nb = (wl.H + 31) // 32
+            want = np.array([1.0 / float(v) for v in sc[:nb]] + [0.0] * (len(sc) - nb),
+                            np.float32)
+            assert (d["dynamic_scales"][row].view(np.uint32) == want.view(np.uint32)).all()
         else:
             assert (d["dynamic_scales"][row] == sc).all()
 
 
 @pytest.mark.parametrize("variant", [(0, 2, 0, 0), (1, 0, 0, 0), (1, 2, 1, 0), (2, 0, 0, 1),
-                                     (3, 1, 0, 0), (4, 0, 1, 0), (5, 1, 0, 0), (3, 0, 4, 0)])
+                                     (3, 1, 0, 0), (4, 0, 1, 0), (5, 1, 0, 0), (3, 0, 4, 0),
+                                     (2, 0, 0, 2), (3, 0, 0, 2), (4, 0, 0, 3)])
 def test_dispatch_rejects_invalid_variants(variant):
     mode, odt, kind, fmt = variant
     cfg = oracle.make_cfg(2, 8, 4, 1024, 2, quant_mode=mode, out_dtype=odt, scales_kind=kind,
@@ -590,3 +599,32 @@ def test_dispatch_rejects_invalid_variants(variant):
     sc = None if kind == 0 else np.ones(1024, np.float32)
     with pytest.raises(ValueError):
         oracle.dispatch(cfg, x, ids, scales=sc)
+
+
+@pytest.mark.parametrize("mode", [4, 5])
+def test_mx_reciprocal_scales_with_pad(mode):
+    """scale_format 2 on a row with an odd block count (H = 1056: 33 blocks, Align2 -> 34): each
+    block's entry is 1 / 2^shared_exp, i.e. the entry of scale_format 0 inverted (exact for a
+    power of two), codes unchanged, the pad entry 0; and x is the codes divided by the
+    transmitted value, within half an E4M3 step."""
+    wl = workloads.Workload("mx_recip", W=2, E=4, BS=5, H=1056, K=2, quant_mode=mode)
+    inp = workloads.generate(wl, seed=4)
+    out = {}
+    for fmt in (0, 2):
+        cfg = oracle.make_cfg(wl.W, wl.E, wl.BS, wl.H, wl.K, quant_mode=mode, scale_format=fmt)
+        out[fmt] = oracle.dispatch(cfg, inp["x"], inp["expert_ids"])
+    P = int(out[0]["recv_offsets"][-1])
+    a, b = out[0]["dynamic_scales"][:P], out[2]["dynamic_scales"][:P]
+    assert (out[0]["expand_x"][:P] == out[2]["expand_x"][:P]).all()
+    assert (b[:, 33] == 0).all() and (a[:, 33] == 0).all()
+    assert (a[:, :33].astype(np.float64) * b[:, :33].astype(np.float64) == 1.0).all()
+    for row in range(P):
+        s, i, _ = out[2]["assist_info"][row]
+        xf = workloads.bf16_bits_to_f32(inp["x"][s, i]).astype(np.float64)
+        codes = np.array([oracle.e4m3_to_f32(c) for c in out[2]["expand_x"][row]], np.float64)
+        recon = codes / np.repeat(b[row, :33].astype(np.float64), 32)[:wl.H]
+        step = np.repeat(1.0 / b[row, :33].astype(np.float64), 32)[:wl.H]
+        # E4M3 spacing relative to the element: at most 2^-3 of the value, or the subnormal step
+        tol = np.maximum(np.abs(xf) * 2.0 ** -4, step * 2.0 ** -10)
+        clip = np.abs(xf) >= 448 * step              # saturated elements (mode 4 overflow)
+        assert (np.abs(recon - xf)[~clip] <= tol[~clip]).all()

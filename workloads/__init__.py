@@ -60,7 +60,7 @@ class Workload:
     mask_kind: int = 0          # 0 none, 1 per token, 2 per pick
     scales_kind: int = 0        # 0 none, 1 scalar, 2 shared row (H,), 3 per expert (E, H)
     out_dtype: int = 0          # 0 the mode's default, 1 int8, 2 E4M3, 3 E5M2
-    scale_format: int = 0       # 0 fp32 scales, 1 E8M0 bytes (MX modes)
+    scale_format: int = 0       # MX modes: 0 fp32 2^se, 1 E8M0 bytes, 2 fp32 2^-se
     combine_quant: int = 0      # 0 bf16 expert rows, 1 int8 blocks of 8 on the return path
     combine_path: str = "gather"  # gather (expand_idx addressing) | scatter (assist_info
                                   # triples, with a shared expert's output added)
