@@ -148,6 +148,42 @@ __device__ __forceinline__ void store_stream(uint2* p, uint2 o)
     __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t*>(p));
 }
 
+// Buffer resource over the `bytes` bytes at `base` (a wave-uniform address).  Accesses
+// through it are range-checked by the hardware: a load past the end returns 0 and a store
+// past it is dropped.  Code that covers a ragged row end this way needs no branch around the
+// access, so the compiler can count outstanding memory operations exactly and wait only for
+// the ones a value depends on.  Every access here is 16, 8 or 4 bytes at a multiple of its
+// size, so it lies either wholly inside or wholly past the end.
+constexpr int32_t kRsrcWord3 = 0x00020000;       // gfx9 family: 32-bit data format, no swizzle
+constexpr uint32_t kRsrcPastEnd = 0x80000000u;    // an offset past the end of every resource
+constexpr int kRsrcNonTemporal = 2;              // aux bits: the nt cache policy
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
+}
+
+// `off` is the lane's whole byte offset, passed as the vector offset (the compiler may move
+// a constant part into the instruction's immediate offset, which the range check includes);
+// the scalar offset operand stays 0, since it is not part of the range check.
+__device__ __forceinline__ float4 rsrc_load_f4(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                       __uint_as_float(v.w));
+}
+
+__device__ __forceinline__ void rsrc_store_stream(__amdgpu_buffer_rsrc_t r, uint32_t off, uint2 o)
+{
+    const u32x2_t v = {o.x, o.y};
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, kRsrcNonTemporal);
+}
+
+__device__ __forceinline__ void rsrc_store_f32(__amdgpu_buffer_rsrc_t r, uint32_t off, float o)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), r, (int)off, 0, 0);
+}
+
 // Value of `v` in lane `lane` (a compile-time or wave-uniform index), for every lane.
 __device__ __forceinline__ int lane_value(int v, int lane)
 {

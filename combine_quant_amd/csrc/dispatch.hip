@@ -355,6 +355,8 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
 {
     __shared__ int32_t rows_lds[kMaxK];
     __shared__ int32_t exps_lds[kMaxK];
+    __shared__ int32_t pick_row_lds[kMaxK];   // per-expert scales: the routed picks' rows
+    __shared__ int32_t pick_exp_lds[kMaxK];   // and experts, in k order
     __shared__ uint32_t red[2][kMaxTileWaves];
     __shared__ int32_t ord_lds[kMaxK];
     __shared__ int32_t fused_rows_lds[kMaxK];
@@ -395,6 +397,7 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
 #pragma unroll
     for (int n = 0; n < kTileSlots; ++n) {
         const int v = lane + (wave * kTileSlots + n) * kWave;
+        raw[n] = make_uint4(0u, 0u, 0u, 0u);
         if (v < NV) {
             raw[n] = load_stream(xr + v);
             if (SK == kScalesShared) {
@@ -426,6 +429,16 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
         }
         rows_lds[threadIdx.x] = row;
         exps_lds[threadIdx.x] = e;
+        if (SK == kScalesPerExpert) {
+            // threads 0..K-1 are lanes of wave 0: a routed pick's place in the list is the
+            // number of routed picks before it
+            const uint64_t routed = __ballot(row >= 0);
+            if (row >= 0) {
+                const int j = __popcll(routed & ((1ull << threadIdx.x) - 1ull));
+                pick_row_lds[j] = row;
+                pick_exp_lds[j] = e;
+            }
+        }
         if (row >= 0) {
             assist[(long long)row * 3 + 0] = s;
             assist[(long long)row * 3 + 1] = i;
@@ -465,13 +478,13 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
     __syncthreads();
 
     int rows[kMaxK];
-    bool any = false;
+    int n_routed = 0;
 #pragma unroll
     for (int k = 0; k < kMaxK; ++k) {
         rows[k] = k < K ? __builtin_amdgcn_readfirstlane(rows_lds[k]) : -1;
-        any |= rows[k] >= 0;
+        n_routed += rows[k] >= 0 ? 1 : 0;
     }
-    if (!any) return;                                      // uniform over the workgroup
+    if (n_routed == 0) return;                             // uniform over the workgroup
 
     if (MODE == 0) {
         uint4* out = reinterpret_cast<uint4*>(expand_x);
@@ -592,44 +605,50 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
     }
 
     // Per-expert scales (modes 1-3): one quantization per pick, on its expert's row.  The
-    // picks run one after another; the scales slice of the next routed pick is loaded into
-    // the other register buffer while the current pick is quantized and stored, so its
-    // latency is hidden.  Mode 2 needs a workgroup-wide maximum per pick; modes 1 and 3 do
+    // routed picks (listed in k order in LDS) run one after another; the scales slice of the
+    // next one is loaded into the other register buffer while the current pick is quantized
+    // and stored, so its latency is hidden.  The loop is unrolled by two, so the two buffers
+    // alternate without copies.  The scales slices are read and the codes written through
+    // range-checked buffer resources over the pick's rows, with no branch around them, so
+    // waiting for a slice does not also wait for the stores issued after it; past the row's
+    // end the token values and the slices read 0, so the products there are 0 and no maximum
+    // needs a bounds test.  Mode 2 needs a workgroup-wide maximum per pick; modes 1 and 3 do
     // not synchronize at all.
-    float4 sm_cur[kTileSlots][2], sm_nxt[kTileSlots][2];
-    auto load_pre = [&](int pick, float4 (&dst)[kTileSlots][2]) {
-        const float4* sm =
-            reinterpret_cast<const float4*>(scales + (long long)exps_lds[pick] * H);
+    float xf[kTileSlots][8];
+#pragma unroll
+    for (int n = 0; n < kTileSlots; ++n) unpack8(raw[n], xf[n], tok_f16 != 0);
+    float4 sa[kTileSlots][2], sb[kTileSlots][2];
+    // vector v = lane + slot0 + 64 n of the row for slot n of this wave
+    const uint32_t slot0 = (uint32_t)__builtin_amdgcn_readfirstlane(wave * kTileSlots * kWave);
+    const uint32_t v0 = (uint32_t)lane + slot0;
+    // past the end of the list the resource is empty: the loads return 0 and read nothing
+    auto load_pre = [&](int j, float4 (&dst)[kTileSlots][2]) {
+        const bool in = j < n_routed;                      // uniform
+        const int e = __builtin_amdgcn_readfirstlane(pick_exp_lds[in ? j : 0]);
+        const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales + (long long)e * H, in ? 4u * H : 0u);
+        // an opaque copy of the lane offset, so the constant parts below stay with each load
+        // (and go to its immediate offset) instead of each becoming a register of its own
+        uint32_t off = 32u * v0;
+        asm volatile("" : "+v"(off));
 #pragma unroll
         for (int n = 0; n < kTileSlots; ++n) {
-            const int v = lane + (wave * kTileSlots + n) * kWave;
-            if (v < NV) {
-                dst[n][0] = sm[2 * v];
-                dst[n][1] = sm[2 * v + 1];
-            }
+            dst[n][0] = rsrc_load_f4(sr, off + 2048u * n);
+            dst[n][1] = rsrc_load_f4(sr, off + 2048u * n + 16u);
         }
     };
-    int pk = 0;
-    while (pk < K && rows[pk] < 0) ++pk;                 // first routed pick (uniform)
-    if (pk < K) load_pre(pk, sm_cur);
-    for (int round = 0; pk < K; ++round) {
-        const int cur = round & 1;
-        int nxt = pk + 1;
-        while (nxt < K && rows[nxt] < 0) ++nxt;
-        if (nxt < K) load_pre(nxt, sm_nxt);
-        const int prow = rows[pk];
+    auto quant_pick = [&](int j, const float4 (&sm)[kTileSlots][2], int buf) {
+        const int prow = __builtin_amdgcn_readfirstlane(pick_row_lds[j]);
+        const __amdgpu_buffer_rsrc_t orow = make_rsrc(out + (long long)prow * NV, 8u * NV);
+        const __amdgpu_buffer_rsrc_t srow =
+            make_rsrc(fscales + (long long)prow * ns, 4u * (uint32_t)ns);
         // x * scales stays in registers between the maximum and the codes
+        float f[kTileSlots][8];
         uint32_t amax = 0;
 #pragma unroll
         for (int n = 0; n < kTileSlots; ++n) {
-            const int v = lane + (wave * kTileSlots + n) * kWave;
-            if (v < NV) {
-                unpack8(raw[n], f[n], tok_f16 != 0);
-                mul8(f[n], sm_cur[n][0], sm_cur[n][1]);
-            } else {
 #pragma unroll
-                for (int q = 0; q < 8; ++q) f[n][q] = 0.0f;
-            }
+            for (int q = 0; q < 8; ++q) f[n][q] = xf[n][q];
+            mul8(f[n], sm[n][0], sm[n][1]);
             if (MODE == 2) amax = absmax8_products(f[n], amax);
         }
         float dyn = 0.0f;
@@ -637,10 +656,10 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
             amax = wave_max_u32(amax);
             // alternating buffers: a wave can only write this buffer again two picks later,
             // after the next barrier, by which time every wave has read it
-            if (lane == 0) red[cur][wave] = amax;
+            if (lane == 0) red[buf][wave] = amax;
             __syncthreads();
             amax = 0;
-            for (int w = 0; w < nw; ++w) amax = amax > red[cur][w] ? amax : red[cur][w];
+            for (int w = 0; w < nw; ++w) amax = amax > red[buf][w] ? amax : red[buf][w];
             dyn = type_max<CT>() / __uint_as_float(amax);
         }
 #pragma unroll
@@ -658,18 +677,22 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
                 packed = dynamic_codes8<CT>(f[n], gdyn);
                 gscale = 1.0f / gdyn;
             }
-            if (v >= NV) continue;
-            store_stream(out + (long long)prow * NV + v, packed);
-            if (MODE == 3 && (v & (kGroup / 8 - 1)) == 0)
-                fscales[(long long)prow * ns + (v >> 4)] = gscale;
+            rsrc_store_stream(orow, 8u * v0 + 512u * n, packed);
+            if (MODE == 3)       // the group's first lane; the others aim past the end
+                rsrc_store_f32(srow, (v & (kGroup / 8 - 1)) == 0 ? 4u * (v >> 4) : kRsrcPastEnd,
+                               gscale);
         }
-        if (MODE == 2 && threadIdx.x == 0) fscales[prow] = 1.0f / dyn;
-#pragma unroll
-        for (int n = 0; n < kTileSlots; ++n) {
-            sm_cur[n][0] = sm_nxt[n][0];
-            sm_cur[n][1] = sm_nxt[n][1];
-        }
-        pk = nxt;
+        if (MODE == 2 && slot0 == 0)                       // wave 0 (uniform): lane 0 stores
+            rsrc_store_f32(srow, lane == 0 ? 0u : kRsrcPastEnd, 1.0f / dyn);
+    };
+    load_pre(0, sa);                                       // n_routed >= 1 here
+    for (int j = 0;; j += 2) {
+        load_pre(j + 1, sb);
+        quant_pick(j, sa, 0);
+        if (j + 1 >= n_routed) break;
+        load_pre(j + 2, sa);
+        quant_pick(j + 1, sb, 1);
+        if (j + 2 >= n_routed) break;
     }
 }
 
