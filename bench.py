@@ -231,6 +231,7 @@ def run_ceilings(args):
     lib.ceiling_scatter_copy.argtypes = [P_, P_, P_, i64, i32, i32, P_]
     lib.ceiling_write_rows.argtypes = [P_, P_, i64, i32, P_]
     lib.ceiling_gather_sum.argtypes = [P_, P_, P_, i64, i32, i32, P_]
+    lib.ceiling_write_chunks.argtypes = [P_, i64, i32, P_]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     inp = workloads.generate(wl, seed=args.seed)
@@ -291,6 +292,11 @@ def run_ceilings(args):
             sets[n % ns]["raw"].data_ptr(), order.data_ptr(), P, H, sp)), H * P),
         "write_rows_in_sequence": (lambda n: check(lib.ceiling_write_rows(
             sets[n % ns]["raw"].data_ptr(), None, P, H, sp)), H * P),
+        # the same bytes in address order, one chunk per one-shot workgroup: 4 KiB is the
+        # fastest write shape on this chip; the other sizes show how much the shape matters
+        **{f"write_chunks_{c // 1024}k_in_sequence": (lambda n, c=c: check(lib.ceiling_write_chunks(
+            sets[n % ns]["raw"].data_ptr(), H * P, c, sp)), H * P)
+           for c in (2048, 4096, 7168, 8192, 16384)},
         "library_combine": (lambda n: sets[n % ns]["combine"](), None),
         "gather_sum": (lambda n: check(lib.ceiling_gather_sum(
             sets[n % ns]["eo"].data_ptr(), dest.data_ptr(), sets[n % ns]["y"].data_ptr(), T, H,

@@ -15,6 +15,11 @@
 //                         flight) and combined with one integer add per element word, then
 //                         the result stored -- the combine's reads and writes without its
 //                         fp32 arithmetic
+//   ceiling_write_chunks  the same number of bytes written in address order by one-shot
+//                         workgroups that each store one chunk (one 16-byte store per lane):
+//                         with 4 KiB chunks (four waves) the fastest write shape measured on
+//                         this chip, for scale; other chunk sizes show how much that shape
+//                         matters
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -127,6 +132,15 @@ __global__ __launch_bounds__(256) void ceiling_gather_sum_kernel(
     }
 }
 
+// workgroup b (blockDim lanes) writes the 16-byte units [b * blockDim, (b + 1) * blockDim) of
+// out, n16 units in all
+__global__ __launch_bounds__(1024) void ceiling_write_chunks_kernel(uint4* __restrict__ out,
+                                                                   long long n16)
+{
+    const long long u = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (u < n16) out[u] = make_uint4((uint32_t)u, (uint32_t)(u >> 32), 0u, 0u);
+}
+
 }  // namespace
 
 extern "C" {
@@ -168,6 +182,19 @@ int ceiling_gather_sum(const void* rows, const int32_t* src, void* y, long long 
     if (K <= 8) MOE_DC_GATHER(8);
     else MOE_DC_GATHER(16);
 #undef MOE_DC_GATHER
+    return (int)hipGetLastError();
+}
+
+// out: bytes (a multiple of 16) bytes, 16-byte aligned; chunk: bytes per workgroup, a multiple
+// of 1024 up to 16384 (one wave per KiB).
+int ceiling_write_chunks(void* out, long long bytes, int chunk, void* stream)
+{
+    if (bytes % 16 != 0 || bytes <= 0 || chunk % 1024 != 0 || chunk < 1024 || chunk > 16384)
+        return (int)hipErrorInvalidValue;
+    const long long n16 = bytes / 16;
+    const int lanes = chunk / 16;
+    hipLaunchKernelGGL(ceiling_write_chunks_kernel, dim3((unsigned)((n16 + lanes - 1) / lanes)),
+                       dim3(lanes), 0, (hipStream_t)stream, static_cast<uint4*>(out), n16);
     return (int)hipGetLastError();
 }
 

@@ -49,3 +49,14 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, cwd=ROOT, timeout=300)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_ceiling_library_exports_the_probes_bench_calls():
+    """bench.py --mode ceilings loads libmoe_dc_ceiling.so and calls these four probes."""
+    import ctypes
+    from combine_quant_amd.build import CEILING_LIB
+    lib = ctypes.CDLL(CEILING_LIB)
+    for name in ("ceiling_scatter_copy", "ceiling_write_rows", "ceiling_gather_sum",
+                 "ceiling_write_chunks"):
+        assert hasattr(lib, name), name
+        assert name in open(bench.__file__).read(), name
