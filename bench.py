@@ -232,6 +232,7 @@ def run_ceilings(args):
     lib.ceiling_write_rows.argtypes = [P_, P_, i64, i32, P_]
     lib.ceiling_gather_sum.argtypes = [P_, P_, P_, i64, i32, i32, P_]
     lib.ceiling_write_chunks.argtypes = [P_, i64, i32, P_]
+    lib.ceiling_read_chunks.argtypes = [P_, P_, i64, i32, P_]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     inp = workloads.generate(wl, seed=args.seed)
@@ -278,6 +279,7 @@ def run_ceilings(args):
     active = int((dest.view(wl.T, wl.K) >= 0).any(dim=1).sum().item())
     ns = len(sets)
     H, T, K = wl.H, wl.T, wl.K
+    sink = torch.zeros(1024, dtype=torch.int32, device=dev)
 
     def check(rc):
         if rc != 0:
@@ -298,6 +300,9 @@ def run_ceilings(args):
             sets[n % ns]["raw"].data_ptr(), H * P, c, sp)), H * P)
            for c in (2048, 4096, 7168, 8192, 16384)},
         "library_combine": (lambda n: sets[n % ns]["combine"](), None),
+        # the gather's row bytes read in address order, 16 KiB per one-shot workgroup
+        "read_chunks_16k_in_sequence": (lambda n: check(lib.ceiling_read_chunks(
+            sets[n % ns]["eo"].data_ptr(), sink.data_ptr(), 2 * H * P, 16384, sp)), 2 * H * P),
         "gather_sum": (lambda n: check(lib.ceiling_gather_sum(
             sets[n % ns]["eo"].data_ptr(), dest.data_ptr(), sets[n % ns]["y"].data_ptr(), T, H,
             K, sp)), 2 * H * P + 2 * H * T + 4 * T * K),

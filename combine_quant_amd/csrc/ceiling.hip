@@ -20,6 +20,9 @@
 //                         with 4 KiB chunks (four waves) the fastest write shape measured on
 //                         this chip, for scale; other chunk sizes show how much that shape
 //                         matters
+//   ceiling_read_chunks   the gather's read bytes read in address order by one-shot workgroups,
+//                         one chunk each (one 16-byte non-temporal load per lane): the chip's
+//                         sequential read rate, for scale
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -141,6 +144,21 @@ __global__ __launch_bounds__(1024) void ceiling_write_chunks_kernel(uint4* __res
     if (u < n16) out[u] = make_uint4((uint32_t)u, (uint32_t)(u >> 32), 0u, 0u);
 }
 
+// workgroup b reads the 16-byte units [b * blockDim, (b + 1) * blockDim) of in and folds them
+// into one word; a word is stored only when it equals a sentinel, which keeps the loads live
+__global__ __launch_bounds__(1024) void ceiling_read_chunks_kernel(const uint4* __restrict__ in,
+                                                                  uint32_t* __restrict__ sink,
+                                                                  long long n16)
+{
+    const long long u = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    uint32_t acc = 0;
+    if (u < n16) {
+        const uint4 v = load_nt(in + u);
+        acc = v.x ^ v.y ^ v.z ^ v.w;
+    }
+    if (acc == 0x9E3779B9u) sink[threadIdx.x] = acc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -195,6 +213,19 @@ int ceiling_write_chunks(void* out, long long bytes, int chunk, void* stream)
     const int lanes = chunk / 16;
     hipLaunchKernelGGL(ceiling_write_chunks_kernel, dim3((unsigned)((n16 + lanes - 1) / lanes)),
                        dim3(lanes), 0, (hipStream_t)stream, static_cast<uint4*>(out), n16);
+    return (int)hipGetLastError();
+}
+
+// in: bytes (a multiple of 16) bytes, 16-byte aligned; sink: 1024 words; chunk as above.
+int ceiling_read_chunks(const void* in, void* sink, long long bytes, int chunk, void* stream)
+{
+    if (bytes % 16 != 0 || bytes <= 0 || chunk % 1024 != 0 || chunk < 1024 || chunk > 16384)
+        return (int)hipErrorInvalidValue;
+    const long long n16 = bytes / 16;
+    const int lanes = chunk / 16;
+    hipLaunchKernelGGL(ceiling_read_chunks_kernel, dim3((unsigned)((n16 + lanes - 1) / lanes)),
+                       dim3(lanes), 0, (hipStream_t)stream, static_cast<const uint4*>(in),
+                       static_cast<uint32_t*>(sink), n16);
     return (int)hipGetLastError();
 }
 

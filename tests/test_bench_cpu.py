@@ -52,11 +52,11 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_ceiling_library_exports_the_probes_bench_calls():
-    """bench.py --mode ceilings loads libmoe_dc_ceiling.so and calls these four probes."""
+    """bench.py --mode ceilings loads libmoe_dc_ceiling.so and calls these probes."""
     import ctypes
     from combine_quant_amd.build import CEILING_LIB
     lib = ctypes.CDLL(CEILING_LIB)
     for name in ("ceiling_scatter_copy", "ceiling_write_rows", "ceiling_gather_sum",
-                 "ceiling_write_chunks"):
+                 "ceiling_write_chunks", "ceiling_read_chunks"):
         assert hasattr(lib, name), name
         assert name in open(bench.__file__).read(), name
