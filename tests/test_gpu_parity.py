@@ -73,6 +73,18 @@ SMALL = {
     "scan_chunks_w64_e1024": workloads.Workload("scan_chunks_w64_e1024", W=64, E=1024, BS=4,
                                                 H=1024, K=8, quant_mode=4, zero_expert_num=1,
                                                 mask_kind=2, inactive_tokens_per_rank=1),
+    # per-expert scales past the pick-kernel limit (32,768 picks: one workgroup per token, its
+    # picks one after another) with rows that end inside a wave's slots, so lanes past the end
+    # read zeros and drop their stores; every mode that takes per-expert scales
+    "tile_per_expert_token_ragged": workloads.Workload(
+        "tile_per_expert_token_ragged", W=4, E=32, BS=512, H=1056, K=16, quant_mode=2,
+        scales_kind=3, outlier_prob=0.02),
+    "tile_per_expert_group_ragged": workloads.Workload(
+        "tile_per_expert_group_ragged", W=4, E=32, BS=512, H=1160, K=16, quant_mode=3,
+        out_dtype=2, scales_kind=3, mask_kind=2, inactive_tokens_per_rank=9),
+    "tile_per_expert_static_ragged": workloads.Workload(
+        "tile_per_expert_static_ragged", W=4, E=32, BS=512, H=2056, K=16, quant_mode=1,
+        scales_kind=3),
 }
 
 
