@@ -22,8 +22,8 @@ _VARIANTS = {
     1: [(o, k, 0) for o in (0, 1) for k in (1, 2, 3)],
     2: [(o, k, 0) for o in (0, 1, 2, 3) for k in (0, 1, 2, 3)],
     3: [(o, k, 0) for o in (0, 2, 3) for k in (0, 1, 2, 3)],
-    4: [(o, 0, f) for o in (0, 2, 3, 4) for f in (0, 1)],
-    5: [(o, 0, f) for o in (0, 2, 3, 4) for f in (0, 1)],
+    4: [(o, 0, f) for o in (0, 2, 3, 4) for f in (0, 1, 2)],
+    5: [(o, 0, f) for o in (0, 2, 3, 4) for f in (0, 1, 2)],
 }
 _H = (1024, 1030, 1032, 1040, 1056, 1152, 1280, 2048, 2056)
 
