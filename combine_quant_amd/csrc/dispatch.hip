@@ -28,9 +28,11 @@
 //           emax 8 for E4M3, 15 for E5M2)
 //   mode 5  per block: shared_exp = ceil(log2(max(max|x|, 1e-4) / fp8_max))
 //           codes = fp8(x / 2^shared_exp); the scale written is 2^shared_exp, as fp32 or as
-//           its E8M0 byte shared_exp + 127 (the SMP article's stored format).  Modes 4/5
-//           also take E2M1 (fp4: emax 2, max 6) elements, two 4-bit codes per byte with the
-//           even element in the low nibble.
+//           its E8M0 byte shared_exp + 127 (the SMP article's stored format), or, as the
+//           low_latency_dispatch formula writes it, its reciprocal 2^-shared_exp in fp32
+//           (exact: shared_exp lies in [-127, 126]).  Modes 4/5 also take E2M1 (fp4: emax
+//           2, max 6) elements, two 4-bit codes per byte with the even element in the low
+//           nibble.
 // int8 rounds half to even and saturates at +-127 with NaN -> 0; fp8 rounds to nearest even
 // and saturates at the type's largest finite value; NaN products of a dynamic mode (only
 // 0 * inf of an all-zero segment) give code 0.  In the vectorized path an MX block is 4
@@ -713,10 +715,11 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
 // cache policy).
 
 // Used up to kPickKernelMaxPicks picks.  Measured on MI355X: W=8, BS=128, K=8, H=7168
-// (8,192 picks) dispatch 41.3 us against 46.7 us with the token workgroups below; at W=16,
-// BS=512 (65,536 picks) 276 us against 265 us: there each pick's workgroup reads the token row
-// and its scales row with little else to overlap, while a token workgroup streams its K picks
-// behind a single read of the row.
+// (8,192 picks) dispatch 41.3 us against 46.7 us with the token workgroups; at W=16, BS=512
+// (65,536 picks) 276 us against 265 us for the token workgroups of the time (224 us since
+// their pick loop was rebuilt): there each pick's workgroup reads the token row and its
+// scales row with little else to overlap, while a token workgroup streams its K picks behind
+// a single read of the row.
 constexpr long long kPickKernelMaxPicks = 16384;
 
 // WAVES waves of SLOTS 64-vector slots each per pick (WAVES * SLOTS * 64 * 8 >= H)
