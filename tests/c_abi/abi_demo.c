@@ -15,7 +15,9 @@
  * The other two combines run on the same rows: the scatter-back combine (moe_combine_scatter,
  * rows returned by their triples) must also give x bit for bit, and the int8 block-quantized
  * combine (moe_combine_quantize, then moe_combine_int8) x within its quantization bound:
- * 0.6 * (the 8-element block's max |x|) / 127 plus the bf16 rounding of the result.
+ * 0.6 * (the 8-element block's max |x|) / 127 plus the bf16 rounding of the result.  The
+ * dispatch for callers that cannot allocate (moe_dispatch_no_workspace) must give the same
+ * bytes as moe_dispatch in every output.
  * Prints "ok routed=<rows> step_us=<mean>" and exits 0, or prints the failure and exits 1.
  */
 #include <hip/hip_runtime_api.h>
@@ -217,6 +219,53 @@ int main(int argc, char** argv)
                 }
             }
         }
+
+    /* the dispatch for callers that cannot allocate (its workspace is the library's static
+     * device array): every output the same bytes as moe_dispatch's */
+    {
+        int32_t* eidx = malloc(T * K * 4);
+        int32_t* erc = malloc((size_t)W * L * W * 4);
+        int32_t* eidx2 = malloc(T * K * 4);
+        int32_t* erc2 = malloc((size_t)W * L * W * 4);
+        int64_t* etn2 = malloc((size_t)W * L * 8);
+        int64_t* roff2 = malloc((size_t)(W + 1) * 8);
+        int32_t* ai2 = malloc(cap * 3 * 4);
+        uint16_t* ex2 = malloc(cap * H * 2);
+        void *dex2, *deidx2, *dai2, *derc2, *detn2, *droff2;
+        HIP_OK(hipMemcpy(eidx, deidx, T * K * 4, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(erc, derc, (size_t)W * L * W * 4, hipMemcpyDeviceToHost));
+        HIP_OK(hipMalloc(&dex2, cap * H * 2));
+        HIP_OK(hipMalloc(&deidx2, T * K * 4));
+        HIP_OK(hipMalloc(&dai2, cap * 3 * 4));
+        HIP_OK(hipMalloc(&derc2, (size_t)W * L * W * 4));
+        HIP_OK(hipMalloc(&detn2, (size_t)W * L * 8));
+        HIP_OK(hipMalloc(&droff2, (size_t)(W + 1) * 8));
+        MOE_OK_OR_FAIL(moe_dispatch_no_workspace(&cfg, dx, dids, NULL, NULL, NULL, dex2, NULL,
+                                                 deidx2, dai2, derc2, detn2, droff2, NULL,
+                                                 stream));
+        HIP_OK(hipStreamSynchronize(stream));
+        HIP_OK(hipMemcpy(eidx2, deidx2, T * K * 4, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(erc2, derc2, (size_t)W * L * W * 4, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(etn2, detn2, (size_t)W * L * 8, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(roff2, droff2, (size_t)(W + 1) * 8, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(ai2, dai2, cap * 3 * 4, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(ex2, dex2, cap * H * 2, hipMemcpyDeviceToHost));
+        if (memcmp(eidx, eidx2, T * K * 4) != 0 || memcmp(erc, erc2, (size_t)W * L * W * 4) != 0 ||
+            memcmp(etn, etn2, (size_t)W * L * 8) != 0 ||
+            memcmp(roff, roff2, (size_t)(W + 1) * 8) != 0 ||
+            memcmp(ai, ai2, (size_t)P * 3 * 4) != 0 || memcmp(ex, ex2, (size_t)P * H * 2) != 0) {
+            printf("moe_dispatch_no_workspace differs from moe_dispatch\n");
+            return 1;
+        }
+        HIP_OK(hipFree(dex2));
+        HIP_OK(hipFree(deidx2));
+        HIP_OK(hipFree(dai2));
+        HIP_OK(hipFree(derc2));
+        HIP_OK(hipFree(detn2));
+        HIP_OK(hipFree(droff2));
+        free(eidx); free(erc); free(eidx2); free(erc2); free(etn2); free(roff2); free(ai2);
+        free(ex2);
+    }
 
     /* native launch timing: dispatch + combine, eager, on one stream */
     hipEvent_t a, b;
