@@ -38,6 +38,12 @@
 // 0 * inf of an all-zero segment) give code 0.  In the vectorized path an MX block is 4
 // adjacent lanes and a group of 128 is 16 adjacent lanes, reduced with lane exchanges.
 //
+// Per-expert scales ([E][H]: a pick's codes depend on its expert) have two more layouts in
+// the vectorized path, chosen by batch size: one small workgroup per pick for small batches
+// (scatter_pick_kernel), and for large ones one workgroup per (window of tokens, expert)
+// that keeps the expert's scales row in registers (scatter_window_kernel).  Batches that
+// route inside the scatter launch use the token workgroups.
+//
 // The element-wise fallback (any H, any alignment) uses one workgroup per token with one
 // element per lane (scatter_elem_kernel); the variant is a runtime argument there.
 #include "dc_device.h"
@@ -714,7 +720,9 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
 // read from HBM by the first, is an L2 hit for the others (these loads keep the default
 // cache policy).
 
-// Used up to kPickKernelMaxPicks picks.  Measured on MI355X: W=8, BS=128, K=8, H=7168
+// Used up to kPickKernelMaxPicks picks (larger batches go to the window kernel below, or to
+// the token workgroups where a window would hold too few picks per expert).  Measured on
+// MI355X: W=8, BS=128, K=8, H=7168
 // (8,192 picks) dispatch 41.3 us against 46.7 us with the token workgroups; at W=16, BS=512
 // (65,536 picks) 276 us against 265 us for the token workgroups of the time (224 us since
 // their pick loop was rebuilt): there each pick's workgroup reads the token row and its
@@ -822,6 +830,251 @@ __global__ __launch_bounds__(kWave * WAVES) void scatter_pick_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// per-expert scales, larger batches: one workgroup per (token window, expert)
+// ---------------------------------------------------------------------------------------
+//
+// A token workgroup reads the scales rows of its K experts (4H bytes each, twice its token
+// row) for every pick; with 256 experts at H=7168 the 7.3 MB table does not fit an XCD's 4 MB
+// L2, so about half of those reads go out to the Infinity Cache.  Here the roles are swapped:
+// a workgroup holds one expert's scales row in registers and quantizes that expert's picks
+// among a window of `win` consecutive tokens (source ranks in turn), reading their token rows.
+// The E workgroups of a window run on one XCD (workgroup b runs on XCD b mod 8: window w goes
+// to XCD w mod 8, and its E workgroups follow one another there), so a window's token rows
+// come from HBM for the first workgroup that needs them and are L2 hits for the others (their
+// loads keep the default cache policy), while each scales row is read once per window.  The
+// window's picks of one expert fill a run of consecutive packed rows per source rank
+// (segment (e, s) is in token order).
+// The workgroup finds its picks by scanning the window's ids and expand_idx (L2 hits after
+// the first workgroup of the window); a pick's row is its segment base plus its expand_idx,
+// and the thread that finds it writes its source triple and weight.  Then the picks run one
+// after another -- products, their maximum (mode 2: the waves' maxima meet in LDS, one
+// barrier per pick), codes, stores -- with the next pick's token row in flight meanwhile in
+// the other of two register buffers.
+constexpr int kWinMaxTokens = 512;
+constexpr int kWinMaxList = 4096;      // win * K: 32 KiB of LDS lists
+constexpr int kScanBatch = 4;          // pick loads in flight per lane in the window scan
+
+__device__ __forceinline__ uint4 rsrc_load_u4(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <int MODE, int CT>
+__global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_window_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
+    const int32_t* __restrict__ expand_idx, const int32_t* __restrict__ seg,
+    const float* __restrict__ scales, const float* __restrict__ weights,
+    void* __restrict__ expand_x, void* __restrict__ dyn_scales, int32_t* __restrict__ assist,
+    float* __restrict__ expand_scales, int W, int E, int BS, int H, int K, int ns,
+    long long cap, int win, int tok_f16)
+{
+    // the expert's picks in the window (at most win * K: a token may list an expert K times):
+    // token within the window, and packed row
+    extern __shared__ int32_t win_lists[];
+    int32_t* list_tok = win_lists;
+    int32_t* list_row = win_lists + win * K;
+    int32_t* seg_lds = win_lists + 2 * win * K;          // segment bases (e, s) of the window
+    __shared__ int32_t wave_cnt[kMaxTileWaves];
+    __shared__ uint32_t red[2][kMaxTileWaves];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int nw = blockDim.x / kWave;
+    // workgroup b = 8 (w / 8 * E + e) + w % 8 serves window w (tokens [w win, w win + win)
+    // of the flat (rank, token) order), expert e
+    const int xcd = blockIdx.x & 7;
+    const long long jb = blockIdx.x >> 3;
+    const int e = (int)(jb % E);
+    const long long w = (jb / E) * 8 + xcd;
+    const long long T = (long long)W * BS;
+    const long long tok0 = w * win;
+    if (tok0 >= T) return;                                 // whole workgroup
+    const int ntok = T - tok0 < win ? (int)(T - tok0) : win;
+    const long long p0 = tok0 * K;
+    const int np = ntok * K;
+    const int NV = H >> 3;
+    float* fscales = static_cast<float*>(dyn_scales);
+    uint2* out = reinterpret_cast<uint2*>(expand_x);       // 8 codes per vector
+
+    // the expert's scales slices of this wave's slots, vector v0 + 64 n in slot n (past the
+    // row end the range check returns 0)
+    const uint32_t slot0 = (uint32_t)__builtin_amdgcn_readfirstlane(wave * kTileSlots * kWave);
+    const uint32_t v0 = (uint32_t)lane + slot0;
+    float4 sm[kTileSlots][2];
+    {
+        const __amdgpu_buffer_rsrc_t sr = make_rsrc(scales + (long long)e * H, 4u * H);
+#pragma unroll
+        for (int n = 0; n < kTileSlots; ++n) {
+            sm[n][0] = rsrc_load_f4(sr, 32u * v0 + 2048u * n);
+            sm[n][1] = rsrc_load_f4(sr, 32u * v0 + 2048u * n + 16u);
+        }
+    }
+
+    // list the expert's routed picks in the window in flat (token, pick) order, so the
+    // workgroups that run side by side on an XCD walk through the window's token rows
+    // together.  Wave w scans the picks [w per_wave, (w + 1) per_wave) twice: first it counts
+    // its candidates (ids == e, expand_idx >= 0), then, once every wave's count is in LDS,
+    // it writes them behind those of the waves before it.  A row past `cap` is listed as -1
+    // (its stores go nowhere).  The segment bases of the ranks the window spans are staged in
+    // LDS meanwhile.
+    const long long s_lo = tok0 / BS;
+    const int span = (int)((tok0 + ntok - 1) / BS - s_lo) + 1;          // <= ntok <= win
+    for (int t = threadIdx.x; t < span; t += blockDim.x)
+        seg_lds[t] = seg[(long long)e * W + s_lo + t];
+    const int per_wave = (np + nw * kWave - 1) / (nw * kWave) * kWave;
+    const int q_lo = wave * per_wave;
+    const int q_hi = q_lo + per_wave < np ? q_lo + per_wave : np;
+    auto scan = [&](bool write, int place) -> int {
+        for (int q0 = q_lo; q0 < q_hi; q0 += kScanBatch * kWave) {     // uniform per wave
+            int32_t pe[kScanBatch], od[kScanBatch];
+#pragma unroll
+            for (int u = 0; u < kScanBatch; ++u) {                     // all loads in flight
+                const int q = q0 + u * kWave + lane;
+                pe[u] = -1;
+                od[u] = -1;
+                if (q < q_hi) {
+                    pe[u] = ids[p0 + q];
+                    od[u] = expand_idx[p0 + q];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kScanBatch; ++u) {
+                const bool hit = pe[u] == e && od[u] >= 0;
+                const uint64_t bal = __ballot(hit);
+                if (write && hit) {
+                    const int q = q0 + u * kWave + lane;
+                    const int idx = place + __popcll(bal & ((1ull << lane) - 1ull));
+                    const int tl = q / K;
+                    const int sr = (int)((tok0 + tl) / BS - s_lo);
+                    const long long row = (long long)seg_lds[sr] + od[u];
+                    list_tok[idx] = tl;
+                    list_row[idx] = row < cap ? (int32_t)row : -1;
+                    if (row < cap) {
+                        const int s = (int)s_lo + sr;
+                        assist[row * 3 + 0] = s;
+                        assist[row * 3 + 1] = (int)(tok0 + tl - (long long)s * BS);
+                        assist[row * 3 + 2] = q - tl * K;
+                        if (expand_scales) expand_scales[row] = weights[p0 + q];
+                    }
+                }
+                place += __popcll(bal);
+            }
+        }
+        return place;
+    };
+    const int mine = scan(false, 0);
+    if (lane == 0) wave_cnt[wave] = mine;
+    __syncthreads();
+    int place = 0, n_picks = 0;
+    for (int w2 = 0; w2 < nw; ++w2) {
+        const int c = wave_cnt[w2];
+        place += w2 < wave ? c : 0;
+        n_picks += c;
+    }
+    n_picks = __builtin_amdgcn_readfirstlane(n_picks);
+    if (n_picks == 0) return;                              // uniform over the workgroup
+    scan(true, place);
+    __syncthreads();
+
+    // the token row of list entry j, in flight while the previous entry is quantized; past
+    // the end of the list the resource is empty and the loads read nothing
+    uint4 ra[kTileSlots], rb[kTileSlots];
+    auto load_row = [&](int j, uint4 (&dst)[kTileSlots]) {
+        const bool in = j < n_picks;                       // uniform
+        const int tl = __builtin_amdgcn_readfirstlane(list_tok[in ? j : 0]);
+        const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + (tok0 + tl) * H, in ? 2u * H : 0u);
+        uint32_t off = 16u * v0;
+        asm volatile("" : "+v"(off));
+#pragma unroll
+        for (int n = 0; n < kTileSlots; ++n) dst[n] = rsrc_load_u4(xr, off + 1024u * n);
+    };
+    auto quant_pick = [&](int j, const uint4 (&raw)[kTileSlots], int buf) {
+        const int prow = __builtin_amdgcn_readfirstlane(list_row[j]);   // -1: past cap
+        const long long orow0 = prow < 0 ? 0 : prow;
+        const __amdgpu_buffer_rsrc_t orow =
+            make_rsrc(out + orow0 * NV, prow < 0 ? 0u : 8u * NV);
+        const __amdgpu_buffer_rsrc_t srow =
+            make_rsrc(fscales + orow0 * ns, prow < 0 ? 0u : 4u * (uint32_t)ns);
+        float f[kTileSlots][8];
+        uint32_t amax = 0;
+#pragma unroll
+        for (int n = 0; n < kTileSlots; ++n) {
+            unpack8(raw[n], f[n], tok_f16 != 0);
+            mul8(f[n], sm[n][0], sm[n][1]);
+            if (MODE == 2) amax = absmax8_products(f[n], amax);
+        }
+        float dyn = 0.0f;
+        if (MODE == 2) {
+            amax = wave_max_u32(amax);
+            // alternating buffers: a wave can only write this buffer again two picks later,
+            // after the next barrier, by which time every wave has read it
+            if (lane == 0) red[buf][wave] = amax;
+            __syncthreads();
+            amax = 0;
+            for (int w2 = 0; w2 < nw; ++w2) amax = amax > red[buf][w2] ? amax : red[buf][w2];
+            dyn = type_max<CT>() / __uint_as_float(amax);
+        }
+#pragma unroll
+        for (int n = 0; n < kTileSlots; ++n) {
+            const int v = (int)v0 + n * kWave;
+            uint2 packed;
+            float gscale = 0.0f;
+            if (MODE == 1) {
+                packed = static_codes8(f[n]);
+            } else if (MODE == 2) {
+                packed = dynamic_codes8<CT>(f[n], dyn);
+            } else {
+                const uint32_t gmax = group_max_u32<kGroup / 8>(absmax8_products(f[n], 0u));
+                const float gdyn = type_max<CT>() / __uint_as_float(gmax);
+                packed = dynamic_codes8<CT>(f[n], gdyn);
+                gscale = 1.0f / gdyn;
+            }
+            rsrc_store_stream(orow, 8u * v0 + 512u * n, packed);
+            if (MODE == 3)       // the group's first lane; the others aim past the end
+                rsrc_store_f32(srow, (v & (kGroup / 8 - 1)) == 0 ? 4u * (v >> 4) : kRsrcPastEnd,
+                               gscale);
+        }
+        if (MODE == 2 && slot0 == 0)                       // wave 0 (uniform): lane 0 stores
+            rsrc_store_f32(srow, lane == 0 ? 0u : kRsrcPastEnd, 1.0f / dyn);
+    };
+    load_row(0, ra);
+    for (int j = 0;; j += 2) {
+        load_row(j + 1, rb);
+        quant_pick(j, ra, 0);
+        if (j + 1 >= n_picks) break;
+        load_row(j + 2, ra);
+        quant_pick(j + 1, rb, 1);
+        if (j + 2 >= n_picks) break;
+    }
+}
+
+// Tokens per window for the window kernel, or 0 where it does not pay.  A window is at most
+// kWinTokens tokens (and win * K <= kWinMaxList); the batch is cut into a multiple of 8
+// windows of equal size, so every XCD gets the same number; and the workgroups must average
+// at least kWinMinPicks picks each (win * K >= kWinMinPicks * E), or the scan and the
+// scales row of each workgroup are spread over too little work.  Measured on MI355X at
+// W=16, BS=512, E=256, H=7168, K=8 (dispatch, int8 per token with per-expert scales):
+// windows of 512 tokens 209-223 us, 256 tokens 214-233 us, 128 tokens 226-237 us, against
+// 225-237 us for the token workgroups; the scales read past L2 fall from 1.03 GB to 0.63 GB
+// per launch.  Below kPickKernelMaxPicks picks the pick kernel stays faster (W=8, BS=128:
+// 41 us against 45 us with 128-token windows).
+constexpr int kWinTokens = 512;
+constexpr int kWinMinPicks = 2;
+static_assert(kWinTokens <= kWinMaxTokens, "window size");
+
+inline int window_tokens(const Shape& sh)
+{
+    const long long T = (long long)sh.W * sh.BS;
+    const int fit = kWinMaxList / sh.K;
+    const int most = kWinTokens < fit ? kWinTokens : fit;
+    const long long per_xcd = (T + 8LL * most - 1) / (8LL * most);   // windows per XCD
+    const int win = (int)((T + 8 * per_xcd - 1) / (8 * per_xcd));    // <= most
+    if ((long long)win * sh.K < (long long)kWinMinPicks * sh.E) return 0;
+    return win;
+}
+
 // Arguments of every scatter launch.
 struct ScatterArgs {
     const void* x;
@@ -842,6 +1095,21 @@ hipError_t launch_tile_variant(const Shape& sh, const ScatterArgs& a, hipStream_
 {
     const long long T = (long long)sh.W * sh.BS;
     if constexpr (SK == kScalesPerExpert) {
+        const int win = a.fused ? 0 : window_tokens(sh);
+        if (win > 0 && T * sh.K > kPickKernelMaxPicks) {
+            const long long windows = (T + win - 1) / win;
+            const long long blocks = (windows + 7) / 8 * 8 * sh.E;
+            const int slots = ((sh.H >> 3) + kWave - 1) / kWave;
+            const int waves = (slots + kTileSlots - 1) / kTileSlots;        // <= kMaxTileWaves
+            const size_t lds = sizeof(int32_t) * ((size_t)2 * win * sh.K + win);
+            hipLaunchKernelGGL((scatter_window_kernel<MODE, CT>), dim3((unsigned)blocks),
+                               dim3(kWave * waves), lds, stream,
+                               static_cast<const uint16_t*>(a.x), a.ids, a.expand_idx, a.seg,
+                               a.scales, a.weights, a.expand_x, a.dyn_scales, a.assist,
+                               a.expand_scales, sh.W, sh.E, sh.BS, sh.H, sh.K,
+                               sh.scales_per_row, (long long)sh.cap, win, sh.tok_f16);
+            return hipGetLastError();
+        }
         if (!a.fused && T * sh.K <= kPickKernelMaxPicks) {
             // one workgroup per pick, the K picks of a token on one XCD
             const long long blocks = (T + 7) / 8 * 8 * sh.K;

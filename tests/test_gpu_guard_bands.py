@@ -3,11 +3,11 @@
 Every row-indexed output (expand_x, dynamic_scales, assist_info, expand_scales) is allocated with
 spare rows past W*BS*K and filled with a sentinel byte before the call; afterwards rows
 [recv_offsets[W], capacity) must still hold the sentinel in every byte, and rows below it must
-match the oracle.  The cases cover each scatter kernel: token workgroups with per-expert scales
-on rows that end inside a wave's slots (their loads and stores go through range-checked buffer
-resources), MX rows with a pad scale, E2M1 pairs and reciprocal scales, masks and special experts
-(fewer routed rows than picks), one workgroup per pick, routing inside the scatter launch, and
-the element-wise kernel."""
+match the oracle.  The cases cover each scatter kernel: window workgroups with per-expert
+scales on rows that end inside a wave's slots (their loads and stores go through range-checked
+buffer resources), windows that span source ranks, MX rows with a pad scale, E2M1 pairs and
+reciprocal scales, masks and special experts (fewer routed rows than picks), one workgroup per
+pick, routing inside the scatter launch, and the element-wise kernel."""
 import numpy as np
 import pytest
 
@@ -26,6 +26,10 @@ CASES = {
     "tile_per_expert_group_masked": WL("guard_tile_group", W=4, E=32, BS=512, H=1160, K=16,
                                        quant_mode=3, out_dtype=2, scales_kind=3, mask_kind=2,
                                        inactive_tokens_per_rank=9),
+    "window_spans_ranks_masked": WL("guard_window", W=100, E=200, BS=23, H=1096, K=8,
+                                    quant_mode=2, scales_kind=3, mask_kind=2,
+                                    inactive_tokens_per_rank=3, zero_expert_num=1,
+                                    copy_expert_num=1),
     "mx_fp4_recip_special": WL("guard_mx_fp4", W=4, E=64, BS=70, H=2064, K=16, quant_mode=5,
                                out_dtype=4, scale_format=2, zero_expert_num=2,
                                copy_expert_num=2, mask_kind=2, inactive_tokens_per_rank=7),

@@ -73,9 +73,10 @@ SMALL = {
     "scan_chunks_w64_e1024": workloads.Workload("scan_chunks_w64_e1024", W=64, E=1024, BS=4,
                                                 H=1024, K=8, quant_mode=4, zero_expert_num=1,
                                                 mask_kind=2, inactive_tokens_per_rank=1),
-    # per-expert scales past the pick-kernel limit (32,768 picks: one workgroup per token, its
-    # picks one after another) with rows that end inside a wave's slots, so lanes past the end
-    # read zeros and drop their stores; every mode that takes per-expert scales
+    # per-expert scales past the pick-kernel limit (32,768 picks: a workgroup per window of 256
+    # tokens and expert, the window's picks of the expert one after another) with rows that
+    # end inside a wave's slots, so lanes past the end read zeros and drop their stores; every
+    # mode that takes per-expert scales
     "tile_per_expert_token_ragged": workloads.Workload(
         "tile_per_expert_token_ragged", W=4, E=32, BS=512, H=1056, K=16, quant_mode=2,
         scales_kind=3, outlier_prob=0.02),
@@ -84,6 +85,22 @@ SMALL = {
         out_dtype=2, scales_kind=3, mask_kind=2, inactive_tokens_per_rank=9),
     "tile_per_expert_static_ragged": workloads.Workload(
         "tile_per_expert_static_ragged", W=4, E=32, BS=512, H=2056, K=16, quant_mode=1,
+        scales_kind=3),
+    # windows that span source ranks (BS=23, 288-token windows, the last one shorter), masks
+    # and special experts
+    "window_spans_ranks_masked": workloads.Workload(
+        "window_spans_ranks_masked", W=100, E=200, BS=23, H=1096, K=8, quant_mode=2,
+        scales_kind=3, mask_kind=2, inactive_tokens_per_rank=3, zero_expert_num=1,
+        copy_expert_num=1),
+    # ids drawn with repetition over 16 experts: a token lists an expert several times, so a
+    # window's list holds up to K entries per token
+    "window_repeated_ids_group": workloads.Workload(
+        "window_repeated_ids_group", W=8, E=16, BS=512, H=1024, K=8, quant_mode=3,
+        out_dtype=3, scales_kind=3, routing="randint"),
+    # too many experts for the windows (512-token windows at K=2 would average one pick per
+    # expert): token workgroups, their picks one after another
+    "token_per_expert_e1024": workloads.Workload(
+        "token_per_expert_e1024", W=32, E=1024, BS=512, H=1024, K=2, quant_mode=2,
         scales_kind=3),
 }
 
