@@ -202,6 +202,24 @@ constexpr int kTileSlots = 2;        // 64-vector slots (1 KiB of bf16 each) per
 constexpr int kMaxTileWaves = 8;     // H <= 8192: at most 1024 vectors = 16 slots
 constexpr int kFusedMinWaves = 4;    // workgroup size floor when the launch also routes
 
+// Per-wave maxima meet in LDS slots, one per wave, read back as a fixed, unrolled set of
+// kMaxTileWaves slots (a loop over the workgroup's wave count waited for each read in turn).
+// The slots of waves the workgroup does not have are cleared first; no wave writes them.
+__device__ __forceinline__ void clear_spare_slots(uint32_t (&red)[2][kMaxTileWaves], int nw)
+{
+    const int t = threadIdx.x;
+    if (t < 2 * kMaxTileWaves && t % kMaxTileWaves >= nw)
+        red[t / kMaxTileWaves][t % kMaxTileWaves] = 0u;
+}
+
+__device__ __forceinline__ uint32_t slots_max(const uint32_t (&slots)[kMaxTileWaves])
+{
+    uint32_t m = 0;
+#pragma unroll
+    for (int w = 0; w < kMaxTileWaves; ++w) m = m > slots[w] ? m : slots[w];
+    return m;
+}
+
 // Small batches route inside the scatter launch (all picks fit in one pass of a workgroup).
 // Workgroup 0 produces the receive-side outputs; every other workgroup finds the packed rows
 // of its own token's picks by counting.  Counting commutes, so no result depends on the
@@ -380,6 +398,7 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
     const int wave = threadIdx.x / kWave;
     const int nw = blockDim.x / kWave;
     const long long tok = FUSED ? blockIdx.x - 1 : blockIdx.x;
+    clear_spare_slots(red, nw);
     const int s = (int)(tok / BS);
     const int i = (int)(tok - (long long)s * BS);
     const int NV = H >> 3;
@@ -513,9 +532,7 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
         // codes shared by every pick: quantize once, store K times
         float dyn_tok = 0.0f;
         if (MODE == 2) {
-            uint32_t amax = 0;
-            for (int w = 0; w < nw; ++w) amax = amax > red[0][w] ? amax : red[0][w];
-            dyn_tok = type_max<CT>() / __uint_as_float(amax);
+            dyn_tok = type_max<CT>() / __uint_as_float(slots_max(red[0]));
         }
         uint32_t fp4_words[kTileSlots];     // E2M1: this lane's eight codes, per slot
 #pragma unroll
@@ -666,8 +683,7 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
             // after the next barrier, by which time every wave has read it
             if (lane == 0) red[buf][wave] = amax;
             __syncthreads();
-            amax = 0;
-            for (int w = 0; w < nw; ++w) amax = amax > red[buf][w] ? amax : red[buf][w];
+            amax = slots_max(red[buf]);
             dyn = type_max<CT>() / __uint_as_float(amax);
         }
 #pragma unroll
@@ -893,6 +909,7 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_window_kernel(
     if (tok0 >= T) return;                                 // whole workgroup
     const int ntok = T - tok0 < win ? (int)(T - tok0) : win;
     const long long p0 = tok0 * K;
+    clear_spare_slots(red, nw);
     const int np = ntok * K;
     const int NV = H >> 3;
     float* fscales = static_cast<float*>(dyn_scales);
@@ -1012,8 +1029,7 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_window_kernel(
             // after the next barrier, by which time every wave has read it
             if (lane == 0) red[buf][wave] = amax;
             __syncthreads();
-            amax = 0;
-            for (int w2 = 0; w2 < nw; ++w2) amax = amax > red[buf][w2] ? amax : red[buf][w2];
+            amax = slots_max(red[buf]);
             dyn = type_max<CT>() / __uint_as_float(amax);
         }
 #pragma unroll
