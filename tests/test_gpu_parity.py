@@ -97,6 +97,13 @@ SMALL = {
     "window_repeated_ids_group": workloads.Workload(
         "window_repeated_ids_group", W=8, E=16, BS=512, H=1024, K=8, quant_mode=3,
         out_dtype=3, scales_kind=3, routing="randint"),
+    # the widest row in windows (eight waves, no spare maximum slots) with per-token E4M3
+    # codes, and static int8 codes on per-expert coefficients
+    "window_h8192_e4m3": workloads.Workload(
+        "window_h8192_e4m3", W=8, E=64, BS=512, H=8192, K=8, quant_mode=2, out_dtype=2,
+        scales_kind=3, outlier_prob=0.01),
+    "window_h8192_static": workloads.Workload(
+        "window_h8192_static", W=8, E=64, BS=512, H=8192, K=8, quant_mode=1, scales_kind=3),
     # too many experts for the windows (512-token windows at K=2 would average one pick per
     # expert): token workgroups, their picks one after another
     "token_per_expert_e1024": workloads.Workload(
