@@ -721,15 +721,15 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
-// per-expert scales: one workgroup of two waves per pick
+// per-expert scales: one small workgroup per pick
 // ---------------------------------------------------------------------------------------
 //
 // With an [E][H] scales table each pick is quantized on its own expert's row, so a token's
-// K picks share nothing but the token row.  Each pick gets a workgroup of two waves, each
-// holding half of the row (and the same half of the expert's scales row) in registers: the
-// products x * scales, their maximum (mode 2: the two waves' maxima meet in LDS, one
-// barrier; mode 3: a 128-group is 16 adjacent lanes), the codes and the stores, with every
-// load of the pick in flight at once.  A token's K picks thus run side by side instead of
+// K picks share nothing but the token row.  Each pick gets a workgroup of two waves (H up
+// to 4096) or four, each holding its share of the row (and the same share of the expert's
+// scales row) in registers: the products x * scales, their maximum (mode 2: the waves'
+// maxima meet in LDS, one barrier; mode 3: a 128-group is 16 adjacent lanes), the codes and
+// the stores, with every load of the pick in flight at once.  A token's K picks thus run side by side instead of
 // one after another.  Placement: workgroups are dealt to the eight XCDs in turn (workgroup
 // b to XCD b mod 8), so pick k of token t runs in workgroup (t / 8) * 8K + 8k + t mod 8 --
 // all K picks of a token on one XCD, one after another in its order -- and the token row,
@@ -738,8 +738,9 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
 
 // Used up to kPickKernelMaxPicks picks (larger batches go to the window kernel below, or to
 // the token workgroups where a window would hold too few picks per expert).  Measured on
-// MI355X: W=8, BS=128, K=8, H=7168
-// (8,192 picks) dispatch 41.3 us against 46.7 us with the token workgroups; at W=16, BS=512
+// MI355X: W=8, BS=128, K=8, H=7168 (8,192 picks) dispatch 41.3 us against 46.7 us with the
+// token workgroups (and four waves of four slots per pick against two of seven: 41.3-41.6
+// against 41.6-42.0 us, per-128-group E4M3 codes 58.3 against 63.6 us); at W=16, BS=512
 // (65,536 picks) 276 us against 265 us for the token workgroups of the time (224 us since
 // their pick loop was rebuilt): there each pick's workgroup reads the token row and its
 // scales row with little else to overlap, while a token workgroup streams its K picks behind
@@ -1135,8 +1136,8 @@ hipError_t launch_tile_variant(const Shape& sh, const ScatterArgs& a, hipStream_
                        a.expand_idx, a.seg, a.scales, a.weights, a.expand_x, a.dyn_scales,     \
                        a.assist, a.expand_scales, sh.W, sh.E, sh.BS, sh.H, sh.K,               \
                        sh.scales_per_row, (long long)sh.cap, T, sh.tok_f16)
-            if (sh.H <= 2 * 7 * kWave * 8) MOE_DC_PICK(2, 7);
-            else MOE_DC_PICK(2, 8);
+            if (sh.H <= 2 * 4 * kWave * 8) MOE_DC_PICK(2, 4);
+            else MOE_DC_PICK(4, 4);
 #undef MOE_DC_PICK
             return hipGetLastError();
         }

@@ -57,7 +57,8 @@ SMALL = {
                                     quant_mode=2),
     # per-expert scales with the separate routing (flags 1): one workgroup per pick, a token
     # count that is not a multiple of 8 (the XCD placement groups tokens by 8), K = 16, a ragged
-    # row (the second wave holds one vector) and the widest row (eight slots per wave)
+    # row (the second of two waves holds one vector) and the widest row (four waves of four
+    # slots)
     "pick_group_k16_ragged": workloads.Workload("pick_group_k16_ragged", W=3, E=48, BS=37,
                                                 H=1032, K=16, quant_mode=3, scales_kind=3),
     "pick_static_h8192": workloads.Workload("pick_static_h8192", W=2, E=8, BS=9, H=8192, K=4,
