@@ -729,12 +729,12 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
 // to 4096) or four, each holding its share of the row (and the same share of the expert's
 // scales row) in registers: the products x * scales, their maximum (mode 2: the waves'
 // maxima meet in LDS, one barrier; mode 3: a 128-group is 16 adjacent lanes), the codes and
-// the stores, with every load of the pick in flight at once.  A token's K picks thus run side by side instead of
-// one after another.  Placement: workgroups are dealt to the eight XCDs in turn (workgroup
-// b to XCD b mod 8), so pick k of token t runs in workgroup (t / 8) * 8K + 8k + t mod 8 --
-// all K picks of a token on one XCD, one after another in its order -- and the token row,
-// read from HBM by the first, is an L2 hit for the others (these loads keep the default
-// cache policy).
+// the stores, with every load of the pick in flight at once.  A token's K picks thus run side
+// by side instead of one after another.  Placement: workgroups are dealt to the eight XCDs in
+// turn (workgroup b to XCD b mod 8), so pick k of token t runs in workgroup
+// (t / 8) * 8K + 8k + t mod 8 -- all K picks of a token on one XCD, one after another in its
+// order -- and the token row, read from HBM by the first, is an L2 hit for the others (these
+// loads keep the default cache policy).
 
 // Used up to kPickKernelMaxPicks picks (larger batches go to the window kernel below, or to
 // the token workgroups where a window would hold too few picks per expert).  Measured on
