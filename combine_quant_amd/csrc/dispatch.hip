@@ -941,6 +941,7 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_window_kernel(
     const int span = (int)((tok0 + ntok - 1) / BS - s_lo) + 1;          // <= ntok <= win
     for (int t = threadIdx.x; t < span; t += blockDim.x)
         seg_lds[t] = seg[(long long)e * W + s_lo + t];
+    if (threadIdx.x < kMaxTileWaves && (int)threadIdx.x >= nw) wave_cnt[threadIdx.x] = 0;
     const int per_wave = (np + nw * kWave - 1) / (nw * kWave) * kWave;
     const int q_lo = wave * per_wave;
     const int q_hi = q_lo + per_wave < np ? q_lo + per_wave : np;
@@ -986,7 +987,8 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_window_kernel(
     if (lane == 0) wave_cnt[wave] = mine;
     __syncthreads();
     int place = 0, n_picks = 0;
-    for (int w2 = 0; w2 < nw; ++w2) {
+#pragma unroll
+    for (int w2 = 0; w2 < kMaxTileWaves; ++w2) {          // absent waves' counts are 0
         const int c = wave_cnt[w2];
         place += w2 < wave ? c : 0;
         n_picks += c;
