@@ -104,3 +104,45 @@ def test_random_config_scatter_back_f16(i):
     import test_gpu_combine_scatter as combine_scatter_tests
     combine_scatter_tests._run(random_workload(i).replace(token_dtype=1), i,
                                with_shared=(i % 4 == 1))
+
+
+# per-expert scales past the pick kernel's 16,384 picks, where the windowed kernel (one
+# workgroup per window of tokens and expert) takes over: ranks, experts, special experts,
+# top-k, batch, row length (ragged ones included), the three per-expert modes with their
+# output types, masks and the three routings (repeated ids under randint)
+N_WINDOW = 24
+_H_WINDOW = (1024, 1032, 1056, 1160, 2048, 2056, 3080)
+
+
+def random_window_workload(i):
+    rng = np.random.default_rng(5000 + i)
+    while True:
+        W = int(rng.choice([2, 4, 8, 16, 32]))
+        E = min(1024, W * int(rng.choice([1, 2, 4, 8, 16, 32])))
+        Z, C = int(rng.choice([0, 0, 1, 2])), int(rng.choice([0, 0, 1]))
+        routing = str(rng.choice(["uniform", "randint", "zipf"]))
+        if routing == "zipf":
+            Z = C = 0
+        kmax = min(16, E if routing == "zipf" else E + Z + C)
+        K = int(rng.integers(1, kmax + 1))
+        bs_min = 16384 // (W * K) + 1                  # W * BS * K > 16,384
+        if bs_min <= 512:
+            break
+    BS = int(rng.integers(bs_min, min(512, bs_min + 96) + 1))
+    H = int(rng.choice(_H_WINDOW))
+    mode = int(rng.choice([1, 2, 3]))
+    out_dtype = int(rng.choice({1: [0, 1], 2: [0, 1, 2, 3], 3: [0, 2, 3]}[mode]))
+    mask_kind = int(rng.choice([0, 1, 2]))
+    inactive = int(rng.integers(0, BS // 4 + 1)) if mask_kind else 0
+    return workloads.Workload(
+        f"randwin{i}", W=W, E=E, BS=BS, H=H, K=K, quant_mode=mode, zero_expert_num=Z,
+        copy_expert_num=C, expert_token_nums_type=int(rng.integers(0, 2)),
+        mask_kind=mask_kind, scales_kind=3, out_dtype=out_dtype, routing=routing,
+        inactive_tokens_per_rank=inactive, outlier_prob=float(rng.choice([0.0, 0.02])))
+
+
+@pytest.mark.parametrize("i", range(N_WINDOW))
+def test_random_window_config_roundtrip(i):
+    wl = random_window_workload(i)
+    assert wl.W * wl.BS * wl.K > 16384
+    harness.roundtrip(wl, seed=i, flags=i % 2)
