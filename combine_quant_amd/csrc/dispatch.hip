@@ -737,7 +737,10 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
 // loads keep the default cache policy).
 
 // Used up to kPickKernelMaxPicks picks (larger batches go to the window kernel below, or to
-// the token workgroups where a window would hold too few picks per expert).  Measured on
+// the token workgroups where a window would hold too few picks per expert).  The crossover
+// with the window kernel, measured at H=7168, K=8, 256 experts: 6,144 picks 34.4 against
+// 39.0 us, 8,192 picks 41.0-42.0 against 43.7-44.1 us, 10,240 picks 48.0 against 46.7 us,
+// 16,384 picks 68.0 against 60.5 us.  Measured on
 // MI355X: W=8, BS=128, K=8, H=7168 (8,192 picks) dispatch 41.3 us against 46.7 us with the
 // token workgroups (and four waves of four slots per pick against two of seven: 41.3-41.6
 // against 41.6-42.0 us, per-128-group E4M3 codes 58.3 against 63.6 us); at W=16, BS=512
@@ -745,7 +748,7 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
 // their pick loop was rebuilt): there each pick's workgroup reads the token row and its
 // scales row with little else to overlap, while a token workgroup streams its K picks behind
 // a single read of the row.
-constexpr long long kPickKernelMaxPicks = 16384;
+constexpr long long kPickKernelMaxPicks = 8192;
 
 // WAVES waves of SLOTS 64-vector slots each per pick (WAVES * SLOTS * 64 * 8 >= H)
 template <int MODE, int CT, int WAVES, int SLOTS>

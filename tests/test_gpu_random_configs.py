@@ -106,8 +106,8 @@ def test_random_config_scatter_back_f16(i):
                                with_shared=(i % 4 == 1))
 
 
-# per-expert scales past the pick kernel's 16,384 picks, where the windowed kernel (one
-# workgroup per window of tokens and expert) takes over: ranks, experts, special experts,
+# per-expert scales past 16,384 picks (the pick kernel's limit is 8,192), where the windowed
+# kernel (one workgroup per window of tokens and expert) runs: ranks, experts, special experts,
 # top-k, batch, row length (ragged ones included), the three per-expert modes with their
 # output types, masks and the three routings (repeated ids under randint)
 N_WINDOW = 24
