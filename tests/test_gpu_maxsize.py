@@ -10,8 +10,9 @@ In the library's normal launch configuration:
     assist_info visits every routed pick exactly once, in strictly increasing (expert,
     source rank, token, pick) order -- the stable sort that defines the packed order;
   * payload rows of sampled tokens (including the picks that land in the first and the last
-    row) against the oracle, one row at a time: unquantized copies, int8 per-token codes and
-    MXFP4 clip codes with E8M0 scales;
+    row) against the oracle, one row at a time: unquantized copies, int8 per-token codes,
+    int8 codes with per-expert smooth scales [768][8192] (one workgroup per window of tokens
+    and expert) and MXFP4 clip codes with E8M0 scales;
   * combine over the unquantized packed rows (an identity expert): sampled tokens against
     the oracle, and every token against the k-ordered fp32 weighted sum of its own row
     within the combine tolerance.
@@ -83,11 +84,11 @@ def _picks(c):
     return out
 
 
-def _dispatch_and_check_routing(c, wl):
+def _dispatch_and_check_routing(c, wl, scales=None):
     import torch
     import combine_quant_amd as cq
     cfg = harness.lib_cfg(wl)
-    out = cq.dispatch(cfg, c["x"], c["ids_dev"])
+    out = cq.dispatch(cfg, c["x"], c["ids_dev"], scales)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(harness.host(out["expand_idx"]), c["eidx"])
     np.testing.assert_array_equal(harness.host(out["ep_recv_count"]), c["erc"])
@@ -154,14 +155,23 @@ def test_max_dispatch_layout_and_unquantized_rows(max_case, tmp_path):
         assert bool((err <= 1e-3 + 1e-2 * ref.abs()).all()), lo
 
 
-@pytest.mark.parametrize("variant", ["int8_per_token", "mxfp4_clip_e8m0"])
+@pytest.mark.parametrize("variant", ["int8_per_token", "mxfp4_clip_e8m0",
+                                     "int8_per_expert_scales"])
 def test_max_dispatch_quantized_rows(max_case, variant):
     import torch
     c = max_case
     wl = {"int8_per_token": c["wl"].replace(quant_mode=2),
           "mxfp4_clip_e8m0": c["wl"].replace(quant_mode=5, out_dtype=4,
-                                             scale_format=1)}[variant]
-    cfg, out = _dispatch_and_check_routing(c, wl)
+                                             scale_format=1),
+          # per-expert smooth scales [768][8192]: 1,536 windows of 256 tokens, one workgroup
+          # per (window, expert)
+          "int8_per_expert_scales": c["wl"].replace(quant_mode=2, scales_kind=3)}[variant]
+    sm = None
+    if wl.scales_kind == 3:
+        r = workloads.generate_routing(wl, seed=0)
+        assert (r["expert_ids"] == c["ids"]).all()
+        sm = r["scales"]
+    cfg, out = _dispatch_and_check_routing(c, wl, harness.to_dev(sm))
     picks = _picks(c)
     rows_t = torch.tensor([p[5] for p in picks], dtype=torch.long, device="cuda")
     ex = harness.host(out["expand_x"].index_select(0, rows_t))
@@ -170,7 +180,8 @@ def test_max_dispatch_quantized_rows(max_case, variant):
     nb = (wl.H + 31) // 32
     for m, (n, s, i, k, e, row) in enumerate(picks):
         assert tuple(ai[m]) == (s, i, k)
-        q, sc = oracle.quant_row(wl.quant_mode, c["x_rows"][n], None, wl.out_dtype)
+        q, sc = oracle.quant_row(wl.quant_mode, c["x_rows"][n], None if sm is None else sm[e],
+                                 wl.out_dtype)
         assert (ex[m].view(np.uint8) == q.view(np.uint8)).all(), (s, i, k, row)
         if wl.scale_format == 1:
             want = [oracle.e8m0_from_scale(v) for v in sc[:nb]] + [0] * (len(sc) - nb)
