@@ -106,16 +106,22 @@ def test_random_config_scatter_back_f16(i):
                                with_shared=(i % 4 == 1))
 
 
-# per-expert scales past 16,384 picks (the pick kernel's limit is 8,192), where the windowed
-# kernel (one workgroup per window of tokens and expert) runs: ranks, experts, special experts,
-# top-k, batch, row length (ragged ones included), the three per-expert modes with their
-# output types, masks and the three routings (repeated ids under randint)
-N_WINDOW = 24
+# per-expert scales past the pick kernel's limit of 8,192 picks, where the windowed kernel (one
+# workgroup per window of tokens and expert) runs: odd cases just past that limit (up to about
+# 16,384 picks), even cases past 16,384; ranks, experts, special experts, top-k, batch, row
+# length (ragged ones included), the three per-expert modes with their output types, masks and
+# the three routings (repeated ids under randint)
+N_WINDOW = 32
 _H_WINDOW = (1024, 1032, 1056, 1160, 2048, 2056, 3080)
+
+
+def _window_floor(i):
+    return 8192 if i % 2 else 16384
 
 
 def random_window_workload(i):
     rng = np.random.default_rng(5000 + i)
+    floor = _window_floor(i)
     while True:
         W = int(rng.choice([2, 4, 8, 16, 32]))
         E = min(1024, W * int(rng.choice([1, 2, 4, 8, 16, 32])))
@@ -125,7 +131,7 @@ def random_window_workload(i):
             Z = C = 0
         kmax = min(16, E if routing == "zipf" else E + Z + C)
         K = int(rng.integers(1, kmax + 1))
-        bs_min = 16384 // (W * K) + 1                  # W * BS * K > 16,384
+        bs_min = floor // (W * K) + 1                  # W * BS * K > floor
         if bs_min <= 512:
             break
     BS = int(rng.integers(bs_min, min(512, bs_min + 96) + 1))
@@ -144,5 +150,5 @@ def random_window_workload(i):
 @pytest.mark.parametrize("i", range(N_WINDOW))
 def test_random_window_config_roundtrip(i):
     wl = random_window_workload(i)
-    assert wl.W * wl.BS * wl.K > 16384
+    assert wl.W * wl.BS * wl.K > _window_floor(i)
     harness.roundtrip(wl, seed=i, flags=i % 2)
