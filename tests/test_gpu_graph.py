@@ -22,6 +22,14 @@ CASES = {
     "int8_three_launches": workloads.Workload("graph_int8_large", W=4, E=32, BS=200, H=1024,
                                               K=8, quant_mode=2, mask_kind=1,
                                               inactive_tokens_per_rank=9),
+    # per-expert scales: 3,200 picks (one workgroup per pick) and 10,240 picks (one workgroup
+    # per window of tokens and expert)
+    "smooth_pick_kernel": workloads.Workload("graph_smooth_pick", W=4, E=32, BS=100, H=2048,
+                                             K=8, quant_mode=2, scales_kind=3, mask_kind=2,
+                                             inactive_tokens_per_rank=5),
+    "smooth_window_kernel": workloads.Workload("graph_smooth_window", W=8, E=32, BS=160,
+                                               H=1024, K=8, quant_mode=3, out_dtype=2,
+                                               scales_kind=3),
 }
 
 
@@ -45,11 +53,11 @@ def test_graph_replays_match_eager(name):
 
     def load(inp, eo):
         return dict(x=harness.bf16_dev(inp["x"]), ids=harness.to_dev(inp["expert_ids"]),
-                    mask=harness.to_dev(inp.get("mask")),
+                    scales=harness.to_dev(inp.get("scales")), mask=harness.to_dev(inp.get("mask")),
                     w=harness.to_dev(inp["expert_scales"]), eo=harness.bf16_dev(eo))
 
     def run(t, out, y, stream=None):
-        cq.dispatch(cfg, t["x"], t["ids"], None, t["mask"], out=out, stream=stream)
+        cq.dispatch(cfg, t["x"], t["ids"], t["scales"], t["mask"], out=out, stream=stream)
         cq.combine(cfg, t["eo"], t["ids"], out["expand_idx"], t["w"], out["ep_recv_count"],
                    out["recv_offsets"], t["mask"], t["x"], y, stream=stream)
 

@@ -1,7 +1,7 @@
 """Independent calls on different streams: the library keeps no device state of its own
 between calls (every scratch word lives in the caller's workspace), so dispatch -> combine
 round trips of different configurations, each on its own stream with its own buffers, can
-run at the same time.  Their launches are interleaved across three streams and every
+run at the same time.  Their launches are interleaved across four streams and every
 result must match the CPU oracle exactly as it does alone (dispatch bit for bit, combine
 within 1e-2 relative / 1e-3 absolute)."""
 import numpy as np
@@ -13,19 +13,22 @@ import workloads
 
 pytestmark = pytest.mark.gpu
 
-# one small batch that routes inside the scatter launch, and two that use the route and scan
-# kernels (one with per-expert scales, one MX with special experts and a per-pick mask)
+# one small batch that routes inside the scatter launch, and three that use the route and
+# scan kernels (per-expert scales through one workgroup per pick, and through windows of tokens;
+# MX with special experts and a per-pick mask)
 CASES = [
     workloads.Workload("streams_small", W=4, E=16, BS=24, H=1024, K=4, quant_mode=2),
     workloads.Workload("streams_smooth", W=4, E=32, BS=160, H=2048, K=8, quant_mode=2,
                        scales_kind=3),
+    workloads.Workload("streams_smooth_windows", W=8, E=32, BS=192, H=1056, K=8, quant_mode=2,
+                       scales_kind=3, mask_kind=1, inactive_tokens_per_rank=11),
     workloads.Workload("streams_mx", W=8, E=32, BS=96, H=1024, K=6, quant_mode=5,
                        zero_expert_num=1, copy_expert_num=1, mask_kind=2,
                        inactive_tokens_per_rank=8, routing="randint"),
 ]
 
 
-def test_round_trips_on_three_streams_at_once():
+def test_round_trips_on_several_streams_at_once():
     import torch
     import combine_quant_amd as cq
     dev = torch.device("cuda")
@@ -45,7 +48,7 @@ def test_round_trips_on_three_streams_at_once():
             stream=torch.cuda.Stream()))
     torch.cuda.synchronize()          # every buffer is ready before the side streams start
 
-    # dispatches first on all three streams, then the combines, so the kernels of different
+    # dispatches first on all the streams, then the combines, so the kernels of different
     # calls are in flight together
     for j in jobs:
         cq.dispatch(j["cfg"], j["x"], j["ids"], j["scales"], j["mask"], out=j["out"],
