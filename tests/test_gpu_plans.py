@@ -20,6 +20,9 @@ CASES = {
     "mx_e5m2_e8m0_mask": WL("mx_e5m2_e8m0_mask", W=4, E=32, BS=60, H=2048, K=8, quant_mode=4,
                             out_dtype=3, scale_format=1, mask_kind=1,
                             inactive_tokens_per_rank=6, copy_expert_num=1),
+    # per-expert scales past the pick kernel's limit (10,240 picks: windows of tokens)
+    "smooth_windows": WL("plan_smooth_windows", W=8, E=32, BS=160, H=2048, K=8, quant_mode=2,
+                         scales_kind=3, zero_expert_num=1),
 }
 
 
@@ -37,11 +40,12 @@ def _plans(wl, inp, eo_dev):
     x = harness.bf16_dev(inp["x"])
     ids = harness.to_dev(inp["expert_ids"])
     mask = harness.to_dev(inp.get("mask"))
+    sm = harness.to_dev(inp.get("scales"))
     w = harness.to_dev(inp["expert_scales"])
-    d, out = cq.prepare_dispatch(cfg, x, ids, None, mask)
+    d, out = cq.prepare_dispatch(cfg, x, ids, sm, mask)
     c, y = cq.prepare_combine(cfg, eo_dev, ids, out["expand_idx"], w, out["ep_recv_count"],
                               out["recv_offsets"], mask, x)
-    return dict(x=x, ids=ids, mask=mask, w=w), d, out, c, y
+    return dict(x=x, ids=ids, mask=mask, scales=sm, w=w), d, out, c, y
 
 
 def _refill(dev_in, inp):
@@ -50,6 +54,8 @@ def _refill(dev_in, inp):
     dev_in["ids"].copy_(harness.to_dev(inp["expert_ids"]))
     if dev_in["mask"] is not None:
         dev_in["mask"].copy_(harness.to_dev(inp["mask"]))
+    if dev_in["scales"] is not None:
+        dev_in["scales"].copy_(harness.to_dev(inp["scales"]))
     dev_in["w"].copy_(harness.to_dev(inp["expert_scales"]))
     torch.cuda.synchronize()
 
