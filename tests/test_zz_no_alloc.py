@@ -1,8 +1,9 @@
 """moe_dispatch_no_workspace: moe_dispatch for callers that cannot allocate device memory.
 
-On the GPU, two calls in a row (a W=16, H=7168 batch, then a smaller masked MX batch with a
+On the GPU, calls in a row (a W=16, H=7168 batch, then a smaller masked MX batch with a
 different routing, so the second call runs over the first one's leftovers in the shared
-scratch) must give exactly the bytes moe_dispatch gives with a workspace of its own, and
+scratch, then a batch with per-expert scales that takes the window kernel) must give exactly
+the bytes moe_dispatch gives with a workspace of its own, and
 repeated calls must leave the device's free memory unchanged.  On the host, the configs the
 1 MiB scratch cannot hold and the id check are refused before any device work.
 """
@@ -18,6 +19,9 @@ SMALL = workloads.Workload(name="no_alloc_small", W=8, E=64, BS=128, H=2048, K=8
                            quant_mode=4, zero_expert_num=1, copy_expert_num=1, mask_kind=2,
                            inactive_tokens_per_rank=13, routing="uniform",
                            description="a smaller masked MX batch with special experts")
+SMOOTH = workloads.Workload(name="no_alloc_smooth", W=8, E=64, BS=256, H=2048, K=8,
+                            quant_mode=2, scales_kind=3, routing="zipf",
+                            description="per-expert scales past the pick kernel's limit")
 
 
 def _compare(wl, a, b):
@@ -48,7 +52,7 @@ def _no_workspace(cfg, dev_in, sm, out):
 def test_no_workspace_dispatch_matches_dispatch_on_two_calls():
     import torch
     import combine_quant_amd as cq
-    for wl in (workloads.C4, SMALL):                 # the second call is the smaller one
+    for wl in (workloads.C4, SMALL, SMOOTH):         # the second call is the smaller one
         inp = workloads.generate(wl, seed=3)
         cfg, dev_in, ref = harness.gpu_dispatch(wl, inp)
         sm = harness.to_dev(inp.get("scales"))
