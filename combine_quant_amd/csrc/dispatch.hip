@@ -731,10 +731,17 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
 // maxima meet in LDS, one barrier; mode 3: a 128-group is 16 adjacent lanes), the codes and
 // the stores, with every load of the pick in flight at once.  A token's K picks thus run side
 // by side instead of one after another.  Placement: workgroups are dealt to the eight XCDs in
-// turn (workgroup b to XCD b mod 8), so pick k of token t runs in workgroup
-// (t / 8) * 8K + 8k + t mod 8 -- all K picks of a token on one XCD, one after another in its
-// order -- and the token row, read from HBM by the first, is an L2 hit for the others (these
-// loads keep the default cache policy).
+// turn (workgroup b to XCD b mod 8).  The experts are cut into kPickExpertGroups contiguous
+// groups, group g served by XCDs [4g, 4g + 4), so each XCD's L2 holds the scales rows of half
+// the experts (3.7 MB at 256 experts and H=7168, instead of a 7.3 MB table that does not fit
+// its 4 MB).  Every pick has one candidate workgroup per group, and only the one whose group
+// holds the pick's expert goes on: pick k of token t, group g, is workgroup
+// 8 (K (t / 4) + k) + 4g + t mod 4, so a token's picks of one group run on one XCD one after
+// another, and the token row, read past L2 by the first of them, is an L2 hit for the others
+// (these loads keep the default cache policy).  Measured on MI355X at W=8, BS=128, K=8,
+// H=7168 (8,192 picks): dispatch 37.0-37.1 us against 41.5-41.9 us with every token's picks on
+// one XCD; with four or eight groups 44.0-44.4 and 55.5-55.8 us (more workgroups that only
+// read an id, and each token row fetched by more XCDs).
 
 // Used up to kPickKernelMaxPicks picks (larger batches go to the window kernel below, or to
 // the token workgroups where a window would hold too few picks per expert).  The crossover
@@ -749,6 +756,8 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
 // scales row with little else to overlap, while a token workgroup streams its K picks behind
 // a single read of the row.
 constexpr long long kPickKernelMaxPicks = 8192;
+constexpr int kPickExpertGroups = 2;                 // divides 8
+constexpr int kPickGroupXcds = 8 / kPickExpertGroups;
 
 // WAVES waves of SLOTS 64-vector slots each per pick (WAVES * SLOTS * 64 * 8 >= H)
 template <int MODE, int CT, int WAVES, int SLOTS>
@@ -763,15 +772,17 @@ __global__ __launch_bounds__(kWave * WAVES) void scatter_pick_kernel(
     __shared__ uint32_t red[WAVES];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const long long grp = (long long)blockIdx.x / (8LL * K);
-    const int rem = (int)((long long)blockIdx.x - grp * 8 * K);
-    const int k = rem >> 3;
-    const long long tok = grp * 8 + (rem & 7);
+    const int xcd = blockIdx.x & 7;
+    const int g = xcd / kPickGroupXcds;                    // expert group this workgroup serves
+    const long long jb = (long long)blockIdx.x >> 3;
+    const int k = (int)(jb % K);
+    const long long tok = (jb / K) * kPickGroupXcds + xcd % kPickGroupXcds;
     if (tok >= T) return;                                  // whole workgroup
     const long long p = tok * K + k;
     const int32_t e = ids[p];
     const int32_t ord = expand_idx[p];
     if (ord < 0 || e < 0 || e >= E) return;                // not routed: whole workgroup
+    if ((int)((long long)e * kPickExpertGroups / E) != g) return;   // another group's pick
     const int s = (int)(tok / BS);
     const long long row = (long long)seg[(long long)e * W + s] + ord;
     if (row >= cap) return;
@@ -1136,8 +1147,9 @@ hipError_t launch_tile_variant(const Shape& sh, const ScatterArgs& a, hipStream_
             return hipGetLastError();
         }
         if (!a.fused && T * sh.K <= kPickKernelMaxPicks) {
-            // one workgroup per pick, the K picks of a token on one XCD
-            const long long blocks = (T + 7) / 8 * 8 * sh.K;
+            // one workgroup per (pick, expert group): the matching one quantizes the pick
+            const long long blocks =
+                (T + kPickGroupXcds - 1) / kPickGroupXcds * 8 * sh.K;
 #define MOE_DC_PICK(WV, SL)                                                                    \
     hipLaunchKernelGGL((scatter_pick_kernel<MODE, CT, WV, SL>), dim3((unsigned)blocks),         \
                        dim3(kWave * WV), 0, stream, static_cast<const uint16_t*>(a.x), a.ids,   \
