@@ -745,9 +745,11 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
 
 // Used up to kPickKernelMaxPicks picks (larger batches go to the window kernel below, or to
 // the token workgroups where a window would hold too few picks per expert).  The crossover
-// with the window kernel, measured at H=7168, K=8, 256 experts: 6,144 picks 34.4 against
-// 39.0 us, 8,192 picks 41.0-42.0 against 43.7-44.1 us, 10,240 picks 48.0 against 46.7 us,
-// 16,384 picks 68.0 against 60.5 us.  Measured on
+// with the window kernel, measured at H=7168, K=8, 256 experts (dispatch, two expert groups):
+// 8,192 picks 36.7-37.0 against 43.7-44.1 us, 10,240 picks 42.1 against 46.3-47.0 us,
+// 12,288 picks 46.9-47.0 against 51.0-52.1 us, 16,384 picks 58.6 against 60.7-62.0 us
+// (with every token's picks on one XCD the window kernel had been faster from about 9,000
+// picks).  Measured on
 // MI355X: W=8, BS=128, K=8, H=7168 (8,192 picks) dispatch 41.3 us against 46.7 us with the
 // token workgroups (and four waves of four slots per pick against two of seven: 41.3-41.6
 // against 41.6-42.0 us, per-128-group E4M3 codes 58.3 against 63.6 us); at W=16, BS=512
@@ -755,7 +757,7 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
 // their pick loop was rebuilt): there each pick's workgroup reads the token row and its
 // scales row with little else to overlap, while a token workgroup streams its K picks behind
 // a single read of the row.
-constexpr long long kPickKernelMaxPicks = 8192;
+constexpr long long kPickKernelMaxPicks = 16384;
 constexpr int kPickExpertGroups = 2;                 // divides 8
 constexpr int kPickGroupXcds = 8 / kPickExpertGroups;
 
@@ -1094,8 +1096,9 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_window_kernel(
 // W=16, BS=512, E=256, H=7168, K=8 (dispatch, int8 per token with per-expert scales):
 // windows of 512 tokens 209-223 us, 256 tokens 214-233 us, 128 tokens 226-237 us, against
 // 225-237 us for the token workgroups; the scales read past L2 fall from 1.03 GB to 0.63 GB
-// per launch.  Below kPickKernelMaxPicks picks the pick kernel stays faster (W=8, BS=128:
-// 41 us against 45 us with 128-token windows).
+// per launch.  Up to kPickKernelMaxPicks picks the pick kernel is faster (W=8, BS=128:
+// 41 us against 45 us with 128-token windows, before its expert groups; W=16, BS=128:
+// 58.6 against 60.7-62.0 us).
 constexpr int kWinTokens = 512;
 constexpr int kWinMinPicks = 2;
 static_assert(kWinTokens <= kWinMaxTokens, "window size");

@@ -23,9 +23,9 @@ CASES = {
     "smooth_per_expert": WL("f16_smooth", W=4, E=32, BS=70, H=2048, K=8, quant_mode=2,
                             scales_kind=3, outlier_prob=0.02, token_dtype=1),
     # past the pick kernel's limit: one workgroup per (window of tokens, expert)
-    "smooth_windows": WL("f16_smooth_windows", W=8, E=64, BS=256, H=1032, K=8, quant_mode=2,
+    "smooth_windows": WL("f16_smooth_windows", W=8, E=64, BS=272, H=1032, K=8, quant_mode=2,
                          scales_kind=3, outlier_prob=0.02, token_dtype=1),
-    "group_smooth_windows": WL("f16_group_windows", W=4, E=32, BS=512, H=1160, K=6,
+    "group_smooth_windows": WL("f16_group_windows", W=8, E=32, BS=352, H=1160, K=6,
                                quant_mode=3, out_dtype=2, scales_kind=3, mask_kind=2,
                                inactive_tokens_per_rank=20, token_dtype=1),
     "group_e5m2_ragged": WL("f16_group", W=4, E=32, BS=50, H=1056, K=6, quant_mode=3,

@@ -22,12 +22,12 @@ CASES = {
     "int8_three_launches": workloads.Workload("graph_int8_large", W=4, E=32, BS=200, H=1024,
                                               K=8, quant_mode=2, mask_kind=1,
                                               inactive_tokens_per_rank=9),
-    # per-expert scales: 3,200 picks (one workgroup per pick) and 10,240 picks (one workgroup
+    # per-expert scales: 3,200 picks (one workgroup per pick) and 17,408 picks (one workgroup
     # per window of tokens and expert)
     "smooth_pick_kernel": workloads.Workload("graph_smooth_pick", W=4, E=32, BS=100, H=2048,
                                              K=8, quant_mode=2, scales_kind=3, mask_kind=2,
                                              inactive_tokens_per_rank=5),
-    "smooth_window_kernel": workloads.Workload("graph_smooth_window", W=8, E=32, BS=160,
+    "smooth_window_kernel": workloads.Workload("graph_smooth_window", W=8, E=32, BS=272,
                                                H=1024, K=8, quant_mode=3, out_dtype=2,
                                                scales_kind=3),
 }

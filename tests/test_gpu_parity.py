@@ -87,9 +87,13 @@ SMALL = {
     "tile_per_expert_static_ragged": workloads.Workload(
         "tile_per_expert_static_ragged", W=4, E=32, BS=512, H=2056, K=16, quant_mode=1,
         scales_kind=3),
-    # just past the pick kernel's limit (12,288 picks): 192-token windows at the c2 row shape
-    "window_12k_picks_h7168": workloads.Workload(
-        "window_12k_picks_h7168", W=8, E=256, BS=192, H=7168, K=8, quant_mode=2,
+    # 12,288 picks at the c2 row shape: one workgroup per pick and expert group
+    "pick_12k_picks_h7168": workloads.Workload(
+        "pick_12k_picks_h7168", W=8, E=256, BS=192, H=7168, K=8, quant_mode=2,
+        scales_kind=3, outlier_prob=0.01),
+    # just past the pick kernel's limit (17,408 picks): 272-token windows at the c2 row shape
+    "window_17k_picks_h7168": workloads.Workload(
+        "window_17k_picks_h7168", W=8, E=256, BS=272, H=7168, K=8, quant_mode=2,
         scales_kind=3, outlier_prob=0.01),
     # windows that span source ranks (BS=23, 288-token windows, the last one shorter), masks
     # and special experts

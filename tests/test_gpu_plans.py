@@ -20,8 +20,8 @@ CASES = {
     "mx_e5m2_e8m0_mask": WL("mx_e5m2_e8m0_mask", W=4, E=32, BS=60, H=2048, K=8, quant_mode=4,
                             out_dtype=3, scale_format=1, mask_kind=1,
                             inactive_tokens_per_rank=6, copy_expert_num=1),
-    # per-expert scales past the pick kernel's limit (10,240 picks: windows of tokens)
-    "smooth_windows": WL("plan_smooth_windows", W=8, E=32, BS=160, H=2048, K=8, quant_mode=2,
+    # per-expert scales past the pick kernel's limit (17,408 picks: windows of tokens)
+    "smooth_windows": WL("plan_smooth_windows", W=8, E=32, BS=272, H=2048, K=8, quant_mode=2,
                          scales_kind=3, zero_expert_num=1),
 }
 

@@ -106,22 +106,19 @@ def test_random_config_scatter_back_f16(i):
                                with_shared=(i % 4 == 1))
 
 
-# per-expert scales past the pick kernel's limit of 8,192 picks, where the windowed kernel (one
-# workgroup per window of tokens and expert) runs: odd cases just past that limit (up to about
-# 16,384 picks), even cases past 16,384; ranks, experts, special experts, top-k, batch, row
-# length (ragged ones included), the three per-expert modes with their output types, masks and
-# the three routings (repeated ids under randint)
-N_WINDOW = 32
+# per-expert scales in the two batch ranges of their kernels: past 16,384 picks, where the
+# windowed kernel (one workgroup per window of tokens and expert) runs, and from 8,193 to 16,384
+# picks, the upper half of the pick kernel's range (one workgroup per pick and expert group);
+# ranks, experts, special experts, top-k, batch, row length (ragged ones included), the three
+# per-expert modes with their output types, masks and the three routings (repeated ids under
+# randint)
+N_WINDOW = 24
+N_PICK_BAND = 16
 _H_WINDOW = (1024, 1032, 1056, 1160, 2048, 2056, 3080)
 
 
-def _window_floor(i):
-    return 8192 if i % 2 else 16384
-
-
-def random_window_workload(i):
-    rng = np.random.default_rng(5000 + i)
-    floor = _window_floor(i)
+def _per_expert_workload(name, rng, lo, hi):
+    """A per-expert-scales workload with lo < W * BS * K <= hi picks."""
     while True:
         W = int(rng.choice([2, 4, 8, 16, 32]))
         E = min(1024, W * int(rng.choice([1, 2, 4, 8, 16, 32])))
@@ -131,24 +128,40 @@ def random_window_workload(i):
             Z = C = 0
         kmax = min(16, E if routing == "zipf" else E + Z + C)
         K = int(rng.integers(1, kmax + 1))
-        bs_min = floor // (W * K) + 1                  # W * BS * K > floor
-        if bs_min <= 512:
+        bs_min = lo // (W * K) + 1                     # W * BS * K > lo
+        bs_max = min(512, bs_min + 96, hi // (W * K))  # W * BS * K <= hi
+        if bs_min <= bs_max:
             break
-    BS = int(rng.integers(bs_min, min(512, bs_min + 96) + 1))
+    BS = int(rng.integers(bs_min, bs_max + 1))
     H = int(rng.choice(_H_WINDOW))
     mode = int(rng.choice([1, 2, 3]))
     out_dtype = int(rng.choice({1: [0, 1], 2: [0, 1, 2, 3], 3: [0, 2, 3]}[mode]))
     mask_kind = int(rng.choice([0, 1, 2]))
     inactive = int(rng.integers(0, BS // 4 + 1)) if mask_kind else 0
     return workloads.Workload(
-        f"randwin{i}", W=W, E=E, BS=BS, H=H, K=K, quant_mode=mode, zero_expert_num=Z,
+        name, W=W, E=E, BS=BS, H=H, K=K, quant_mode=mode, zero_expert_num=Z,
         copy_expert_num=C, expert_token_nums_type=int(rng.integers(0, 2)),
         mask_kind=mask_kind, scales_kind=3, out_dtype=out_dtype, routing=routing,
         inactive_tokens_per_rank=inactive, outlier_prob=float(rng.choice([0.0, 0.02])))
 
 
+def random_window_workload(i):
+    return _per_expert_workload(f"randwin{i}", np.random.default_rng(5000 + i), 16384, 1 << 30)
+
+
+def random_pick_band_workload(i):
+    return _per_expert_workload(f"randpick{i}", np.random.default_rng(6000 + i), 8192, 16384)
+
+
 @pytest.mark.parametrize("i", range(N_WINDOW))
 def test_random_window_config_roundtrip(i):
     wl = random_window_workload(i)
-    assert wl.W * wl.BS * wl.K > _window_floor(i)
+    assert wl.W * wl.BS * wl.K > 16384
+    harness.roundtrip(wl, seed=i, flags=i % 2)
+
+
+@pytest.mark.parametrize("i", range(N_PICK_BAND))
+def test_random_pick_band_config_roundtrip(i):
+    wl = random_pick_band_workload(i)
+    assert 8192 < wl.W * wl.BS * wl.K <= 16384
     harness.roundtrip(wl, seed=i, flags=i % 2)

@@ -20,7 +20,7 @@ CASES = [
     workloads.Workload("streams_small", W=4, E=16, BS=24, H=1024, K=4, quant_mode=2),
     workloads.Workload("streams_smooth", W=4, E=32, BS=160, H=2048, K=8, quant_mode=2,
                        scales_kind=3),
-    workloads.Workload("streams_smooth_windows", W=8, E=32, BS=192, H=1056, K=8, quant_mode=2,
+    workloads.Workload("streams_smooth_windows", W=8, E=32, BS=272, H=1056, K=8, quant_mode=2,
                        scales_kind=3, mask_kind=1, inactive_tokens_per_rank=11),
     workloads.Workload("streams_mx", W=8, E=32, BS=96, H=1024, K=6, quant_mode=5,
                        zero_expert_num=1, copy_expert_num=1, mask_kind=2,

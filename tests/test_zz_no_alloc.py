@@ -19,7 +19,7 @@ SMALL = workloads.Workload(name="no_alloc_small", W=8, E=64, BS=128, H=2048, K=8
                            quant_mode=4, zero_expert_num=1, copy_expert_num=1, mask_kind=2,
                            inactive_tokens_per_rank=13, routing="uniform",
                            description="a smaller masked MX batch with special experts")
-SMOOTH = workloads.Workload(name="no_alloc_smooth", W=8, E=64, BS=256, H=2048, K=8,
+SMOOTH = workloads.Workload(name="no_alloc_smooth", W=8, E=64, BS=272, H=2048, K=8,
                             quant_mode=2, scales_kind=3, routing="zipf",
                             description="per-expert scales past the pick kernel's limit")
 
