@@ -768,19 +768,19 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
 // maxima meet in LDS, one barrier; mode 3: a 128-group is 16 adjacent lanes), the codes and
 // the stores, with every load of the pick in flight at once.  A token's K picks thus run side
 // by side instead of one after another.  Placement: workgroups are dealt to the eight XCDs in
-// turn (workgroup b to XCD b mod 8).  In modes 1 and 2 the experts are cut into two contiguous
+// turn (workgroup b to XCD b mod 8).  The experts are cut into kPickExpertGroups contiguous
 // groups, group g served by XCDs [4g, 4g + 4), so each XCD's L2 holds the scales rows of half
 // the experts (3.7 MB at 256 experts and H=7168, instead of a 7.3 MB table that does not fit
-// its 4 MB).  Every pick then has one candidate workgroup per group, and only the one whose
-// group holds the pick's expert goes on: with G groups, pick k of token t, group g, is
-// workgroup 8 (K (t / (8/G)) + k) + (8/G) g + t mod (8/G), so a token's picks of one group run
-// on one XCD one after another, and the token row, read past L2 by the first of them, is an L2
-// hit for the others (these loads keep the default cache policy).  Measured on MI355X at W=8,
-// BS=128, K=8, H=7168 (8,192 picks), dispatch: mode 2 36.0-36.6 us with two groups against
-// 41.0-41.1 us with one, mode 1 38.3-38.5 against 41.4 us; four and eight groups (mode 2)
-// 44.0-44.4 and 55.5-55.8 us (more workgroups that only read an id, each token row fetched by
-// more XCDs); but per-128-group E4M3 codes (mode 3) 65.4-66.4 us with two groups against 58.2
-// with one, so mode 3 keeps one group: all K picks of a token on one XCD.
+// its 4 MB).  Every pick has one candidate workgroup per group, and only the one whose group
+// holds the pick's expert goes on: pick k of token t, group g, is workgroup
+// 8 (K (t / 4) + k) + 4g + t mod 4, so a token's picks of one group run on one XCD one after
+// another, and the token row, read past L2 by the first of them, is an L2 hit for the others
+// (these loads keep the default cache policy).  Measured on MI355X at W=8, BS=128, K=8,
+// H=7168 (8,192 picks), dispatch with two groups against one (every token's picks on one XCD):
+// mode 2 36.0-36.6 against 41.0-41.1 us, mode 1 38.3-38.5 against 41.4 us, per-128-group E4M3
+// (mode 3) 42.4-43.2 against 42.2 us and at 12,288 picks 54.6-54.7 against 55.5 us; four and
+// eight groups (mode 2) 44.0-44.4 and 55.5-55.8 us (more workgroups that only read an id, each
+// token row fetched by more XCDs).
 
 // Used up to kPickKernelMaxPicks picks (larger batches go to the window kernel below, or to
 // the token workgroups where a window would hold too few picks per expert).  The crossover
@@ -797,8 +797,8 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
 // scales row with little else to overlap, while a token workgroup streams its K picks behind
 // a single read of the row.
 constexpr long long kPickKernelMaxPicks = 16384;
-// expert groups of the pick kernel in quant mode `mode` (divides 8)
-constexpr int pick_expert_groups(int mode) { return mode == 3 ? 1 : 2; }
+constexpr int kPickExpertGroups = 2;                 // divides 8
+constexpr int kPickGroupXcds = 8 / kPickExpertGroups;
 
 // WAVES waves of SLOTS 64-vector slots each per pick (WAVES * SLOTS * 64 * 8 >= H)
 template <int MODE, int CT, int WAVES, int SLOTS>
@@ -813,19 +813,17 @@ __global__ __launch_bounds__(kWave * WAVES) void scatter_pick_kernel(
     __shared__ uint32_t red[WAVES];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    constexpr int kGroups = pick_expert_groups(MODE);
-    constexpr int kGroupXcds = 8 / kGroups;
     const int xcd = blockIdx.x & 7;
-    const int g = xcd / kGroupXcds;                        // expert group this workgroup serves
+    const int g = xcd / kPickGroupXcds;                    // expert group this workgroup serves
     const long long jb = (long long)blockIdx.x >> 3;
     const int k = (int)(jb % K);
-    const long long tok = (jb / K) * kGroupXcds + xcd % kGroupXcds;
+    const long long tok = (jb / K) * kPickGroupXcds + xcd % kPickGroupXcds;
     if (tok >= T) return;                                  // whole workgroup
     const long long p = tok * K + k;
     const int32_t e = ids[p];
     const int32_t ord = expand_idx[p];
     if (ord < 0 || e < 0 || e >= E) return;                // not routed: whole workgroup
-    if ((int)((long long)e * kGroups / E) != g) return;   // another group's pick
+    if ((int)((long long)e * kPickExpertGroups / E) != g) return;   // another group's pick
     const int s = (int)(tok / BS);
     const long long row = (long long)seg[(long long)e * W + s] + ord;
     if (row >= cap) return;
@@ -1192,8 +1190,8 @@ hipError_t launch_tile_variant(const Shape& sh, const ScatterArgs& a, hipStream_
         }
         if (!a.fused && T * sh.K <= kPickKernelMaxPicks) {
             // one workgroup per (pick, expert group): the matching one quantizes the pick
-            constexpr int gx = 8 / pick_expert_groups(MODE);
-            const long long blocks = (T + gx - 1) / gx * 8 * sh.K;
+            const long long blocks =
+                (T + kPickGroupXcds - 1) / kPickGroupXcds * 8 * sh.K;
 #define MOE_DC_PICK(WV, SL)                                                                    \
     hipLaunchKernelGGL((scatter_pick_kernel<MODE, CT, WV, SL>), dim3((unsigned)blocks),         \
                        dim3(kWave * WV), 0, stream, static_cast<const uint16_t*>(a.x), a.ids,   \
