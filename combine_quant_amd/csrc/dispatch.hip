@@ -197,6 +197,22 @@ __device__ __forceinline__ uint2 fp8_codes8_hw(const float (&v)[8])
     return make_uint2(lo, hi);
 }
 
+// Eight E2M1 codes of finite or infinite values as one word, element 0 in the lowest nibble,
+// by gfx950's scaled fp4 conversion with scale 1 (two values per instruction, one byte each).
+// After a clamp to +-6 it gives e2m1_code's code for every finite binary32 value (checked on
+// the GPU); a NaN input is not allowed.
+__device__ __forceinline__ uint32_t fp4_word_hw(const float (&v)[8])
+{
+    float c[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) c[q] = __builtin_amdgcn_fmed3f(v[q], -6.0f, 6.0f);
+    uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, c[0], c[1], 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c[2], c[3], 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c[4], c[5], 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c[6], c[7], 1.0f, 3);
+    return w;
+}
+
 // Eight codes of the dynamic modes: type(f * dyn), NaN products -> 0.
 template <int CT>
 __device__ __forceinline__ uint2 dynamic_codes8(const float (&f)[8], float dyn)
@@ -591,17 +607,19 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
                 const uint32_t amax = group_max_u32<kMxBlock / 8>(absmax8(f[n], 0u));
                 se = mx_shared_exp<MODE, CT>(amax);
                 const float inv = __uint_as_float((uint32_t)(127 - se) << 23);   // 2^-se
-                uint32_t c[8];
+                // a NaN element saturates with its sign, as fp8_code gives it
+                float e[8];
 #pragma unroll
-                for (int q = 0; q < 8; ++q) c[q] = fp8_code<CT>(f[n][q] * inv);
+                for (int q = 0; q < 8; ++q) {
+                    const float p = f[n][q] * inv;
+                    e[q] = p != p ? __builtin_copysignf(type_max<CT>(), p) : p;
+                }
                 if (CT == kCodeE2m1) {            // eight 4-bit codes, element 0 lowest
-                    uint32_t w = 0;
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) w |= c[q] << (4 * q);
+                    const uint32_t w = fp4_word_hw(e);
                     fp4_words[n] = w;
                     packed = make_uint2(w, 0u);
                 } else {
-                    packed = pack_codes8(c);
+                    packed = fp8_codes8_hw<CT>(e);
                 }
                 scale = sfmt == 2 ? inv : pow2f(se);      // 1 / 2^se, or 2^se
             }
