@@ -125,6 +125,16 @@ def source_hash(paths):
     return h.hexdigest()[:16]
 
 
+def combine_kernel_name(wl):
+    """The kernel(s) the combine timing of workload `wl` covers."""
+    if wl.combine_quant:
+        return ("combine_int8_wide_kernel" if wl.H % 16 == 0 and wl.K <= 8
+                else "combine_wave_kernel")
+    if wl.combine_path == "scatter":
+        return "scatter_back_index_kernel + combine_wave_kernel"
+    return "combine_wave_kernel"
+
+
 def committed_traffic():
     """HBM bytes per combine launch from the committed counter summary, or None when the
     summary is missing or was taken on a different kernel source."""
@@ -515,7 +525,7 @@ def run_bench(args):
         "roofline": {"bound": "hbm", "achieved": round(comb_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(comb_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": committed_traffic() if wl.name == DEFAULT_WORKLOAD else None,
-                     "kernel": "combine_wave_kernel",
+                     "kernel": combine_kernel_name(wl),
                      "algorithmic_bytes_per_launch": c_bytes,
                      "avg_launch_us": round(c_avg * 1e3, 2)},
         "dispatch": {"avg_us": round(d_avg * 1e3, 2), "median_us": round(pct(disp_ms, 50), 2),

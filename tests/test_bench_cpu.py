@@ -60,3 +60,11 @@ def test_ceiling_library_exports_the_probes_bench_calls():
                  "ceiling_write_chunks", "ceiling_read_chunks"):
         assert hasattr(lib, name), name
         assert name in open(bench.__file__).read(), name
+
+
+def test_roofline_names_the_timed_combine_kernel():
+    w = workloads.WORKLOADS
+    assert bench.combine_kernel_name(w[bench.DEFAULT_WORKLOAD]) == "combine_wave_kernel"
+    assert bench.combine_kernel_name(w["c4v_w16_combine_int8"]) == "combine_int8_wide_kernel"
+    assert bench.combine_kernel_name(w["c4v_w16_scatter_back_shared"]).endswith(
+        "combine_wave_kernel")
