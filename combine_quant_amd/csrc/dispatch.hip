@@ -77,6 +77,38 @@ constexpr float type_max()
                                                                                  : 6.0f;
 }
 
+// a / b, correctly rounded, for a constant a > 0 and any b >= 0 (zero, infinite and NaN
+// included): where b's exponent field lies in [LO, 252], a reciprocal estimate and two fused
+// multiply-adds; elsewhere the correctly rounded division.  An exhaustive GPU check over every
+// binary32 b found the short sequence equal to the correctly rounded quotient for a = 448 with
+// exponent fields 8..252, a = 57344 with 15..252 and a = 1 with 1..252, and not outside those
+// ranges (tiny b, whose quotient overflows, and huge b); so each LO below is the one checked
+// for its a.
+template <int LO>
+__device__ __forceinline__ float div_rn(float a, float b)
+{
+    const uint32_t ex = __float_as_uint(b) >> 23;
+    if (ex >= (uint32_t)LO && ex <= 252u) {
+        const float y = __builtin_amdgcn_rcpf(b);
+        const float q0 = a * y;
+        const float r = __builtin_fmaf(-q0, b, a);
+        return __builtin_fmaf(r, y, q0);
+    }
+    return a / b;
+}
+
+// A per-128-group dynamic scale pair (mode 3): dyn = type_max / amax and scale = 1 / dyn, both
+// correctly rounded, as the per-element division gives them.
+template <int CT>
+__device__ __forceinline__ void group_dyn(uint32_t amax_bits, float& dyn, float& scale)
+{
+    const float amax = __uint_as_float(amax_bits);
+    if (CT == kCodeE4m3) dyn = div_rn<8>(448.0f, amax);
+    else if (CT == kCodeE5m2) dyn = div_rn<15>(57344.0f, amax);
+    else dyn = type_max<CT>() / amax;
+    scale = div_rn<1>(1.0f, dyn);
+}
+
 // Shared exponent of an MX block from the bit pattern of its absolute maximum.
 template <int MODE, int CT>
 __device__ __forceinline__ int mx_shared_exp(uint32_t amax_bits)
@@ -600,9 +632,9 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
                 packed = dynamic_codes8<CT>(f[n], dyn_tok);
             } else if (MODE == 3) {
                 const uint32_t amax = group_max_u32<kGroup / 8>(absmax8(f[n], 0u));
-                const float dyn = type_max<CT>() / __uint_as_float(amax);
+                float dyn;
+                group_dyn<CT>(amax, dyn, scale);
                 packed = dynamic_codes8<CT>(f[n], dyn);
-                scale = 1.0f / dyn;
             } else {
                 const uint32_t amax = group_max_u32<kMxBlock / 8>(absmax8(f[n], 0u));
                 se = mx_shared_exp<MODE, CT>(amax);
@@ -752,9 +784,9 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_tile_kernel(
                 packed = dynamic_codes8<CT>(f[n], dyn);
             } else {
                 const uint32_t gmax = group_max_u32<kGroup / 8>(absmax8_products(f[n], 0u));
-                const float gdyn = type_max<CT>() / __uint_as_float(gmax);
+                float gdyn;
+                group_dyn<CT>(gmax, gdyn, gscale);
                 packed = dynamic_codes8<CT>(f[n], gdyn);
-                gscale = 1.0f / gdyn;
             }
             rsrc_store_stream(orow, 8u * v0 + 512u * n, packed);
             if (MODE == 3)       // the group's first lane; the others aim past the end
@@ -910,9 +942,9 @@ __global__ __launch_bounds__(kWave * WAVES) void scatter_pick_kernel(
             packed = dynamic_codes8<CT>(f[n], dyn);
         } else {
             const uint32_t gmax = group_max_u32<kGroup / 8>(absmax8_products(f[n], 0u));
-            const float gdyn = type_max<CT>() / __uint_as_float(gmax);
+            float gdyn;
+            group_dyn<CT>(gmax, gdyn, gscale);
             packed = dynamic_codes8<CT>(f[n], gdyn);
-            gscale = 1.0f / gdyn;
         }
         if (v >= end) continue;
         store_stream(out + v, packed);
@@ -1122,9 +1154,9 @@ __global__ __launch_bounds__(kWave * kMaxTileWaves) void scatter_window_kernel(
                 packed = dynamic_codes8<CT>(f[n], dyn);
             } else {
                 const uint32_t gmax = group_max_u32<kGroup / 8>(absmax8_products(f[n], 0u));
-                const float gdyn = type_max<CT>() / __uint_as_float(gmax);
+                float gdyn;
+                group_dyn<CT>(gmax, gdyn, gscale);
                 packed = dynamic_codes8<CT>(f[n], gdyn);
-                gscale = 1.0f / gdyn;
             }
             rsrc_store_stream(orow, 8u * v0 + 512u * n, packed);
             if (MODE == 3)       // the group's first lane; the others aim past the end
