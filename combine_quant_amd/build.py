@@ -17,6 +17,9 @@ SOURCES = ["api.cpp", "route.hip", "dispatch.hip", "combine.hip", "noalloc.hip"]
 # measurement kernels of bench.py's ceiling mode (the access patterns without the arithmetic)
 CEILING_LIB = os.path.join(HERE, "libmoe_dc_ceiling.so")
 CEILING_SOURCES = ["ceiling.hip"]
+# exhaustive GPU checks of the instruction-level conversions, for the tests
+SELFCHECK_LIB = os.path.join(HERE, "libmoe_dc_selfcheck.so")
+SELFCHECK_SOURCES = ["selfcheck.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -55,14 +58,16 @@ def _link(objs, lib, verbose):
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source, link libmoe_dc.so and the ceiling-measurement library; returns
-    the path of libmoe_dc.so."""
+    """Compile every source, link libmoe_dc.so, the ceiling-measurement library and the
+    conversion self-check library; returns the path of libmoe_dc.so."""
     os.makedirs(BUILD, exist_ok=True)
-    srcs = SOURCES + CEILING_SOURCES
+    srcs = SOURCES + CEILING_SOURCES + SELFCHECK_SOURCES
     with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    _link(objs[:len(SOURCES)], LIB, verbose)
-    _link(objs[len(SOURCES):], CEILING_LIB, verbose)
+    n, c = len(SOURCES), len(CEILING_SOURCES)
+    _link(objs[:n], LIB, verbose)
+    _link(objs[n:n + c], CEILING_LIB, verbose)
+    _link(objs[n + c:], SELFCHECK_LIB, verbose)
     return LIB
 
 

@@ -47,6 +47,7 @@
 // The element-wise fallback (any H, any alignment) uses one workgroup per token with one
 // element per lane (scatter_elem_kernel); the variant is a runtime argument there.
 #include "dc_device.h"
+#include "dc_convert.h"
 #include "route_device.h"
 #include "dc_internal.h"
 
@@ -75,26 +76,6 @@ constexpr float type_max()
 {
     return CT == kCodeInt8 ? 127.0f : CT == kCodeE4m3 ? 448.0f : CT == kCodeE5m2 ? 57344.0f
                                                                                  : 6.0f;
-}
-
-// a / b, correctly rounded, for a constant a > 0 and any b >= 0 (zero, infinite and NaN
-// included): where b's exponent field lies in [LO, 252], a reciprocal estimate and two fused
-// multiply-adds; elsewhere the correctly rounded division.  An exhaustive GPU check over every
-// binary32 b found the short sequence equal to the correctly rounded quotient for a = 448 with
-// exponent fields 8..252, a = 57344 with 15..252 and a = 1 with 1..252, and not outside those
-// ranges (tiny b, whose quotient overflows, and huge b); so each LO below is the one checked
-// for its a.
-template <int LO>
-__device__ __forceinline__ float div_rn(float a, float b)
-{
-    const uint32_t ex = __float_as_uint(b) >> 23;
-    if (ex >= (uint32_t)LO && ex <= 252u) {
-        const float y = __builtin_amdgcn_rcpf(b);
-        const float q0 = a * y;
-        const float r = __builtin_fmaf(-q0, b, a);
-        return __builtin_fmaf(r, y, q0);
-    }
-    return a / b;
 }
 
 // A per-128-group dynamic scale pair (mode 3): dyn = type_max / amax and scale = 1 / dyn, both
@@ -199,50 +180,6 @@ __device__ __forceinline__ uint2 int8_codes8_finite(const float (&f)[8], float d
                                               __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u),
                                               0x05040100u);
     return make_uint2(lo, hi);
-}
-
-// Eight E4M3 or E5M2 codes of finite or infinite values, by the conversion instructions of
-// gfx950 (two values per instruction).  They round to nearest, ties to even, keep the sign of
-// zero and give the subnormal codes, exactly as e4m3_code / e5m2_code do -- checked on the GPU
-// against those encoders for every finite binary32 value -- but past the largest finite value
-// they give the NaN code, so each value is first clamped to +-type_max (one med3), where the
-// software codes saturate.  A NaN input is not allowed (med3 would turn it into -type_max).
-template <int CT>
-__device__ __forceinline__ uint2 fp8_codes8_hw(const float (&v)[8])
-{
-    constexpr float m = type_max<CT>();
-    float c[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) c[q] = __builtin_amdgcn_fmed3f(v[q], -m, m);
-    uint32_t lo, hi;
-    if (CT == kCodeE4m3) {
-        lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
-        lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], (int)lo, true);
-        hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[4], c[5], 0, false);
-        hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[6], c[7], (int)hi, true);
-    } else {
-        lo = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c[0], c[1], 0, false);
-        lo = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c[2], c[3], (int)lo, true);
-        hi = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c[4], c[5], 0, false);
-        hi = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c[6], c[7], (int)hi, true);
-    }
-    return make_uint2(lo, hi);
-}
-
-// Eight E2M1 codes of finite or infinite values as one word, element 0 in the lowest nibble,
-// by gfx950's scaled fp4 conversion with scale 1 (two values per instruction, one byte each).
-// After a clamp to +-6 it gives e2m1_code's code for every finite binary32 value (checked on
-// the GPU); a NaN input is not allowed.
-__device__ __forceinline__ uint32_t fp4_word_hw(const float (&v)[8])
-{
-    float c[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) c[q] = __builtin_amdgcn_fmed3f(v[q], -6.0f, 6.0f);
-    uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, c[0], c[1], 1.0f, 0);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c[2], c[3], 1.0f, 1);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c[4], c[5], 1.0f, 2);
-    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, c[6], c[7], 1.0f, 3);
-    return w;
 }
 
 // Eight codes of the dynamic modes: type(f * dyn), NaN products -> 0.
