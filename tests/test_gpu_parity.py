@@ -66,6 +66,14 @@ SMALL = {
     "pick_token_e5m2_w8": workloads.Workload("pick_token_e5m2_w8", W=8, E=64, BS=65, H=7168,
                                              K=8, quant_mode=2, out_dtype=3, scales_kind=3,
                                              mask_kind=2, inactive_tokens_per_rank=5),
+    # the pick kernel's two expert groups with very few experts: one expert per group (and a
+    # zero expert), and groups of two and one (and a copy expert)
+    "pick_groups_two_experts": workloads.Workload(
+        "pick_groups_two_experts", W=2, E=2, BS=512, H=1056, K=3, quant_mode=3, out_dtype=3,
+        scales_kind=3, zero_expert_num=1, routing="randint"),
+    "pick_groups_three_experts": workloads.Workload(
+        "pick_groups_three_experts", W=3, E=3, BS=400, H=2048, K=3, quant_mode=2,
+        scales_kind=3, copy_expert_num=1, mask_kind=1, inactive_tokens_per_rank=17),
     # more (expert, source) counts than one LDS pass of the scan holds: chunked scan, with a
     # short last chunk (24,192 counts) and with whole chunks (65,536 counts)
     "scan_chunks_w24_e1008": workloads.Workload("scan_chunks_w24_e1008", W=24, E=1008, BS=8,
