@@ -1,5 +1,6 @@
 // dc_convert.h -- the conversions of the dispatch kernels that use gfx950 instructions in
-// place of bit-level code: fp8 and fp4 element codes, and a short correctly rounded division.
+// place of bit-level code: static int8, fp8 and fp4 element codes, and a short correctly
+// rounded division.
 // Each is exact only where an exhaustive check over every binary32 input says so;
 // selfcheck.hip runs those checks on the GPU against the bit-level encoders of dc_device.h and
 // the correctly rounded division.
@@ -8,6 +9,36 @@
 #include "dc_internal.h"
 
 namespace moe_dc {
+
+// int8 code of one value: round half to even, saturate to +-127, NaN -> 0 (the two's complement
+// byte is the code).
+__device__ __forceinline__ uint32_t int8_code(float v)
+{
+    if (v != v) return 0u;
+    const float r = fminf(fmaxf(__builtin_rintf(v), -127.0f), 127.0f);
+    return (uint32_t)(int32_t)r;
+}
+
+// Eight int8 codes of v as int8_code gives them, packed element 0 lowest: a NaN becomes 0, one
+// med3 clamps to +-127, and adding 1.5 * 2^23 puts the value in [2^23, 2^24), where binary32
+// spacing is 1, so the addition rounds it to an integer (ties to even) whose two's complement is
+// the low byte of the sum's bit pattern; byte permutes gather the eight low bytes.
+__device__ __forceinline__ uint2 static_int8_codes8(const float (&v)[8])
+{
+    uint32_t b[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const float c = v[q] != v[q] ? 0.0f : __builtin_amdgcn_fmed3f(v[q], -127.0f, 127.0f);
+        b[q] = __float_as_uint(c + 12582912.0f);
+    }
+    const uint32_t lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u),
+                                              __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u),
+                                              0x05040100u);
+    const uint32_t hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[7], b[6], 0x0c0c0400u),
+                                              __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u),
+                                              0x05040100u);
+    return make_uint2(lo, hi);
+}
 
 // Eight E4M3 or E5M2 codes of finite or infinite values, by the conversion instructions of
 // gfx950 (two values per instruction).  They round to nearest, ties to even, keep the sign of

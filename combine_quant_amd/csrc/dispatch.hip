@@ -56,13 +56,6 @@ namespace {
 
 constexpr int kGroup = 128;          // mode 3 group length
 
-// int8 code of one value: round half to even, saturate to +-127, NaN -> 0.
-__device__ __forceinline__ uint32_t int8_code(float v)
-{
-    if (v != v) return 0u;
-    const float r = fminf(fmaxf(__builtin_rintf(v), -127.0f), 127.0f);
-    return (uint32_t)(int32_t)r;
-}
 
 template <int CT>
 __device__ __forceinline__ uint32_t fp8_code(float v)
@@ -210,10 +203,7 @@ __device__ __forceinline__ uint2 dynamic_codes8(const float (&f)[8], float dyn)
 // Eight static int8 codes (mode 1): the scales are already applied.
 __device__ __forceinline__ uint2 static_codes8(const float (&f)[8])
 {
-    uint32_t c[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) c[q] = int8_code(f[q]);
-    return pack_codes8(c);
+    return static_int8_codes8(f);
 }
 
 // ---------------------------------------------------------------------------------------

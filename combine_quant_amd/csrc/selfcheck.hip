@@ -5,7 +5,8 @@
 //
 //   codes: every binary32 bit pattern that is not a NaN (infinities included), eight
 //          consecutive patterns per call of fp8_codes8_hw<E4M3>, fp8_codes8_hw<E5M2> and
-//          fp4_word_hw, each code compared with e4m3_code, e5m2_code and e2m1_code
+//          fp4_word_hw, each code compared with e4m3_code, e5m2_code and e2m1_code; and every
+//          bit pattern (NaNs included) through static_int8_codes8 against int8_code
 //   division: every binary32 b with the sign bit clear (zero, subnormals, infinity and NaNs
 //          included), div_rn<8>(448, b), div_rn<15>(57344, b) and div_rn<1>(1, b) compared bit
 //          for bit with the correctly rounded quotient
@@ -19,14 +20,24 @@ using namespace moe_dc;
 
 constexpr int kPer = 256;                 // bit patterns per thread
 constexpr int kThreads = 256;
+constexpr int kCounts = 7;
 
-// mismatch counters: 0 E4M3, 1 E5M2, 2 E2M1, 3 448 / b, 4 57344 / b, 5 1 / b
+// mismatch counters: 0 E4M3, 1 E5M2, 2 E2M1, 3 448 / b, 4 57344 / b, 5 1 / b, 6 int8
 __global__ __launch_bounds__(kThreads) void check_codes_kernel(unsigned long long* bad)
 {
     const unsigned long long t = (unsigned long long)blockIdx.x * blockDim.x + threadIdx.x;
     const unsigned long long first = t * kPer;            // the grid covers 2^32 patterns
-    unsigned long long n4 = 0, n5 = 0, n2 = 0;
+    unsigned long long n4 = 0, n5 = 0, n2 = 0, n8 = 0;
     for (int j = 0; j < kPer; j += 8) {
+        float all[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) all[q] = __uint_as_float((uint32_t)(first + j + q));
+        const uint2 c8 = static_int8_codes8(all);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const uint32_t w8 = q < 4 ? c8.x : c8.y;
+            n8 += ((w8 >> (8 * (q & 3))) & 0xFFu) != (int8_code(all[q]) & 0xFFu);
+        }
         float v[8];
         bool cmp[8];
 #pragma unroll
@@ -51,6 +62,7 @@ __global__ __launch_bounds__(kThreads) void check_codes_kernel(unsigned long lon
     if (n4) atomicAdd(&bad[0], n4);
     if (n5) atomicAdd(&bad[1], n5);
     if (n2) atomicAdd(&bad[2], n2);
+    if (n8) atomicAdd(&bad[6], n8);
 }
 
 __global__ __launch_bounds__(kThreads) void check_division_kernel(unsigned long long* bad)
@@ -73,17 +85,17 @@ __global__ __launch_bounds__(kThreads) void check_division_kernel(unsigned long 
 
 extern "C" {
 
-// Runs both checks on the current device and copies the six mismatch counts (E4M3, E5M2,
-// E2M1 codes; 448 / b, 57344 / b, 1 / b) to the host array `counts`.  Allocates 48 bytes of
-// device memory for the counters and frees them; synchronizes the device.  Returns a
-// hipError_t value (0 on success).
+// Runs both checks on the current device and copies the seven mismatch counts (E4M3, E5M2,
+// E2M1 codes; 448 / b, 57344 / b, 1 / b; static int8 codes) to the host array `counts`.
+// Allocates 56 bytes of device memory for the counters and frees them; synchronizes the
+// device.  Returns a hipError_t value (0 on success).
 int moe_dc_selfcheck_conversions(unsigned long long* counts)
 {
     if (!counts) return (int)hipErrorInvalidValue;
     unsigned long long* bad = nullptr;
-    hipError_t e = hipMalloc(&bad, 6 * sizeof(unsigned long long));
+    hipError_t e = hipMalloc(&bad, kCounts * sizeof(unsigned long long));
     if (e != hipSuccess) return (int)e;
-    e = hipMemset(bad, 0, 6 * sizeof(unsigned long long));
+    e = hipMemset(bad, 0, kCounts * sizeof(unsigned long long));
     if (e == hipSuccess) {
         hipLaunchKernelGGL(check_codes_kernel, dim3((unsigned)((1ull << 32) / kPer / kThreads)),
                            dim3(kThreads), 0, 0, bad);
@@ -94,7 +106,7 @@ int moe_dc_selfcheck_conversions(unsigned long long* counts)
     }
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e == hipSuccess)
-        e = hipMemcpy(counts, bad, 6 * sizeof(unsigned long long), hipMemcpyDeviceToHost);
+        e = hipMemcpy(counts, bad, kCounts * sizeof(unsigned long long), hipMemcpyDeviceToHost);
     const hipError_t f = hipFree(bad);
     return (int)(e != hipSuccess ? e : f);
 }

@@ -1,7 +1,8 @@
 """The instruction-level conversions of the dispatch kernels (csrc/dc_convert.h) against what
 they replace, over every binary32 input: the fp8 (E4M3, E5M2) and fp4 (E2M1) element codes of
 gfx950's conversion instructions against the bit-level encoders of csrc/dc_device.h (every value
-but the NaNs), and the short division of the per-128-group scales against the correctly rounded
+but the NaNs), the static int8 codes by magic-number addition against the rounding and clamping
+of int8_code (every value), and the short division of the per-128-group scales against the correctly rounded
 quotient (every b with the sign bit clear).  The parity tests compare the kernels with the oracle
 on realistic inputs; this check covers the inputs they do not reach."""
 import ctypes
@@ -11,7 +12,8 @@ import pytest
 
 from combine_quant_amd import build as B
 
-NAMES = ("E4M3 codes", "E5M2 codes", "E2M1 codes", "448 / b", "57344 / b", "1 / b")
+NAMES = ("E4M3 codes", "E5M2 codes", "E2M1 codes", "448 / b", "57344 / b", "1 / b",
+         "static int8 codes")
 
 
 def _lib():
@@ -31,8 +33,8 @@ def test_selfcheck_library_exports_its_entry_point():
 def test_conversions_equal_the_bit_level_results_everywhere():
     import torch
     torch.cuda.init()
-    counts = (ctypes.c_ulonglong * 6)()
+    counts = (ctypes.c_ulonglong * len(NAMES))()
     print("[conversions] exhaustive check of codes and divisions", flush=True)
     rc = _lib().moe_dc_selfcheck_conversions(counts)
     assert rc == 0, f"hipError {rc}"
-    assert list(counts) == [0] * 6, dict(zip(NAMES, list(counts)))
+    assert list(counts) == [0] * len(NAMES), dict(zip(NAMES, list(counts)))
